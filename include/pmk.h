@@ -1,0 +1,278 @@
+/*
+ * pmk.h — C ABI of the persistent batch-1 decode megakernel library for MI355X (gfx950).
+ *
+ * The library runs single-stream (batch 1) greedy decode of a dense Llama-style decoder as
+ * ONE persistent, CU-resident kernel per decode call: every CU executes a static queue of
+ * tasks (GEMV tiles, attention splits, LM-head tiles) that the host lowers from the model
+ * into a task DAG synchronised by monotonic counters or epoch flags, after a static
+ * validator has proved the schedule deadlock- and race-free.
+ *
+ * Sources of the design (pages, by title and section):
+ *  - "AutoMegaKernel: A Statically-Checked Agent Harness for Self-Retargeting Megakernel
+ *    Synthesis" (explainer), Method: Layer 0 (one cooperative block per compute unit running
+ *    a local wait -> dispatch -> signal queue on monotonic counters), Layer 1 (GEMV, attention
+ *    and RMSNorm instructions), Layer 2 (Schedule IR task DAG and ScheduleConfig), and the
+ *    Safety Gate (acyclicity, satisfiable thresholds 1 <= t <= #producers, per-queue order,
+ *    joined multi-producer counters, happens-before on memory, output reachability, reject
+ *    before any launch).  Problem statement: the batch-1 latency floor is weight bytes over
+ *    HBM bandwidth; per-op launches and graph replay keep op boundaries.
+ *  - "Kog AI MI300X monokernel tutorial": the monokernel keeps the whole decode loop,
+ *    including LM-head sampling and the EOS check, in one resident kernel with no host
+ *    re-entry; batch-1 projections are GEMV on vector ALUs with dot2, not matrix cores;
+ *    work is partitioned at compile time over a fixed CU grid; sentinel polling replaced
+ *    atomic arrival counters.
+ *  - "Netra Kernel" summary, details: a C-ABI runtime binds persistent and boundary buffers
+ *    and launches on a caller-owned stream; kernels are chosen by an exact operation
+ *    contract and anything outside it is rejected, not approximated; FP8 E4M3 block-scale
+ *    weights and GQA attention over an FP8 KV cache.
+ *
+ * Conventions
+ *  - Every call returns pmk_status (PMK_OK = 0).  No C++ exception crosses the ABI.
+ *    pmk_last_error(ctx) gives a human-readable reason for the last failure on ctx.
+ *  - Device work is asynchronous on the caller's stream (a hipStream_t passed as void*;
+ *    NULL is the default stream).  Device-side failures (watchdog time-outs, NaN logits)
+ *    surface through pmk_poll_error() after the caller has synchronised the stream.
+ *  - The CALLER allocates all device memory (for example as torch uint8 tensors) with the
+ *    sizes pmk_buffer_sizes() reports, and keeps it alive until pmk_destroy().  The library
+ *    allocates only small host-side tables and a few-KB device copy of the schedule.
+ *  - One thread at a time per context.  Contexts are independent.
+ */
+#ifndef PMK_H_
+#define PMK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PMK_ABI_VERSION 1
+
+typedef enum {
+  PMK_OK = 0,
+  PMK_ERR_INVALID_ARG = 1,      /* NULL pointer, bad size, misaligned buffer, bad enum */
+  PMK_ERR_UNSUPPORTED = 2,      /* model outside the contract (biases, head_dim, GQA ratio, dtype) */
+  PMK_ERR_SCHEDULE_INVALID = 3, /* the static validator rejected the schedule; see pmk_last_error */
+  PMK_ERR_CAPACITY = 4,         /* position + steps would exceed max_seq */
+  PMK_ERR_NOT_BOUND = 5,        /* buffers not bound, or weights / KV not loaded yet */
+  PMK_ERR_HIP = 6,              /* a HIP runtime call failed; see pmk_last_error */
+  PMK_ERR_TIMEOUT = 7,          /* a device wait exceeded its spin limit (pmk_poll_error) */
+  PMK_ERR_NAN = 8,              /* NaN logits reached the greedy choice (pmk_poll_error) */
+  PMK_ERR_DEVICE = 9            /* the device cannot co-schedule the grid, or is not gfx950 */
+} pmk_status;
+
+typedef enum { PMK_DT_F16 = 0, PMK_DT_BF16 = 1, PMK_DT_FP8_E4M3 = 2 } pmk_dtype;
+
+typedef enum {
+  PMK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per decode call */
+  PMK_MODE_GRAPH = 1,      /* one captured hipGraph of per-op kernels, replayed once per step */
+  PMK_MODE_PER_OP = 2      /* the same per-op kernels launched directly (no graph) */
+} pmk_mode;
+
+typedef enum {
+  PMK_SYNC_FLAGS = 0,   /* each producer stores its epoch into its own flag word; waiters poll them */
+  PMK_SYNC_COUNTERS = 1 /* producers add 1 to a shared monotonic counter; waiters poll it */
+} pmk_sync_mode;
+
+/* The operation contract.  Supported: no biases, untied embeddings, head_dim in {64, 128},
+ * n_q_heads % n_kv_heads == 0, hidden, ffn, n_q_heads*head_dim multiples of 8 (16 for FP8),
+ * weight_dtype in {F16, BF16, FP8_E4M3} and kv_dtype in {F16, BF16, FP8_E4M3};
+ * FP8 weights use 128x128 fp32 block scales, and their embedding and norm gains are BF16. */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  int32_t max_seq;        /* KV capacity in positions */
+  float rms_eps;
+  float rope_theta;
+  int32_t weight_dtype;   /* pmk_dtype */
+  int32_t kv_dtype;       /* pmk_dtype */
+  int32_t has_bias;       /* must be 0 */
+  int32_t tie_embeddings; /* must be 0 */
+} pmk_model_config;
+
+/* Structural knobs of the schedule (the ScheduleConfig of the pages).  Zero means default. */
+typedef struct {
+  int32_t n_cus;        /* grid size = number of queues (default: all CUs of the device) */
+  int32_t sync_mode;    /* pmk_sync_mode (default FLAGS) */
+  int32_t attn_splits;  /* split-KV chunks per KV head (default: n_cus / n_kv_heads, capped by max_seq/16) */
+  int32_t prefetch;     /* 1 (default): issue a task's first weight loads before its wait; -1: off */
+  int32_t trace_steps;  /* steps kept in the per-task trace ring (default 0 = no trace buffer) */
+  int64_t spin_limit;   /* polls before a wait gives up and aborts the launch (default 1<<22) */
+} pmk_schedule_config;
+
+typedef struct {
+  uint64_t arena_bytes;     /* packed weights, gains, scales, RoPE table */
+  uint64_t kv_bytes;        /* K and V caches: 2 * L * n_kv * max_seq * head_dim * elem */
+  uint64_t workspace_bytes; /* activations, partials, flags, counters, trace */
+} pmk_sizes;
+
+/* Device pointers to the canonical tensors (row-major [out][in] for every linear weight):
+ *   embed[V][H], final_norm[H], lm_head[V][H] (+ lm_head_scale[ceil(V/128)][ceil(H/128)] for FP8),
+ *   layers: n_layers * 9 pointers, per layer in order
+ *     wq[nq*hd][H], wk[nkv*hd][H], wv[nkv*hd][H], wo[H][nq*hd], w_gate[F][H], w_up[F][H],
+ *     w_down[H][F], attn_norm[H], ffn_norm[H]
+ *   layer_scales (FP8 weights only, else NULL): n_layers * 7 pointers, the block scales of the
+ *     7 linear tensors, each [ceil(out/128)][ceil(in/128)] fp32.
+ * 16-bit tensors are raw F16/BF16 bits; FP8 tensors are E4M3FN bytes.  The host arrays of
+ * pointers are read during the call only. */
+typedef struct {
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+  const float* lm_head_scale;
+  const void* const* layers;
+  const float* const* layer_scales;
+} pmk_weight_ptrs;
+
+/* Watchdog / device error record (pmk_poll_error). */
+typedef struct {
+  int32_t code;     /* pmk_status of the device failure, PMK_OK if none */
+  int32_t cu;       /* queue that failed */
+  int32_t task;     /* task index */
+  int32_t counter;  /* counter it waited on */
+  uint32_t expected;
+  uint32_t seen;
+} pmk_device_error;
+
+typedef struct {
+  int32_t n_tasks;
+  int32_t n_counters;
+  int32_t n_cus;
+  int32_t attn_splits;
+  int32_t max_tasks_per_cu;
+  int32_t sync_mode;
+  uint64_t hash;        /* FNV-1a of the serialized schedule (deterministic across runs) */
+} pmk_schedule_info;
+
+typedef struct pmk_ctx pmk_ctx;
+
+int pmk_abi_version(void);
+const char* pmk_status_str(pmk_status s);
+/* Text of the last failure on ctx (never NULL; empty when none).  Valid until the next call. */
+const char* pmk_last_error(const pmk_ctx* ctx);
+/* Text of the last failure of a call that could not return a context (pmk_create). */
+const char* pmk_last_global_error(void);
+
+/* Host only.  Checks the contract, builds the schedule for the device's CU count and runs
+ * the static validator; returns PMK_ERR_UNSUPPORTED / PMK_ERR_SCHEDULE_INVALID with the
+ * reason in pmk_last_global_error().  hip_device < 0 builds a device-less context (for
+ * schedule inspection; every device call then returns PMK_ERR_NOT_BOUND). */
+pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sched, int hip_device,
+                      pmk_ctx** out);
+void pmk_destroy(pmk_ctx* ctx);
+
+pmk_status pmk_buffer_sizes(const pmk_ctx* ctx, pmk_sizes* out);
+/* Non-owning.  arena, kv and workspace must be 256-byte aligned device pointers of at
+ * least the reported sizes. */
+pmk_status pmk_bind(pmk_ctx* ctx, void* d_arena, void* d_kv, void* d_workspace);
+
+/* Repack the canonical tensors into the arena (QKV rows concatenated with each RoPE pair
+ * made adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table).
+ * Asynchronous on `stream`; the sources may be freed once the stream has synchronised. */
+pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stream);
+
+/* Teacher-forced prefill: runs positions 0..P-1 from d_tokens[P] (device), writing the KV
+ * cache; the greedy choice after the last position becomes the next input token (and is
+ * also stored to d_first_token if not NULL).  For an FP8 KV cache, d_kv_scales
+ * [n_layers][n_kv][2] (K, V) fp32 gives the static scales; it is required.
+ * Resets the position and the synchronisation state.  PMK_ERR_CAPACITY if P > max_seq. */
+pmk_status pmk_prefill_kv(pmk_ctx* ctx, const int32_t* d_tokens, int32_t P, const float* d_kv_scales,
+                          int32_t* d_first_token, void* stream);
+
+/* Resume from saved state: copies KV contents d_k, d_v [n_layers][n_kv][P][head_dim] (cache
+ * element format) into positions 0..P-1, sets the position to P and the next input token to
+ * `next_token`.  d_kv_scales as for pmk_prefill_kv. */
+pmk_status pmk_load_kv(pmk_ctx* ctx, const void* d_k, const void* d_v, int32_t P, int32_t next_token,
+                       const float* d_kv_scales, void* stream);
+
+/* Rewind to position `pos` (0 < pos <= current position) with next input token read from
+ * d_token (device int32).  KV entries at positions >= pos are overwritten by later steps. */
+pmk_status pmk_rewind(pmk_ctx* ctx, int32_t pos, const int32_t* d_token, void* stream);
+
+/* n greedy decode steps from the next-token slot at the current position.  Step i consumes
+ * the current input token at position pos+i, appends its K and V, and writes the greedy
+ * next token to d_out_tokens[i]; with d_out_logits != NULL the fp32 logits go to
+ * d_out_logits[i*vocab ...].  eos_id >= 0 stops after the step that emits it; the number of
+ * steps run goes to *d_n_done (device, may be NULL).  MEGAKERNEL mode is ONE kernel launch.
+ * The host advances its position by n (an upper bound when eos stops early; the device
+ * keeps the exact position).  PMK_ERR_CAPACITY if position + n > max_seq. */
+pmk_status pmk_decode_n_tokens(pmk_ctx* ctx, int32_t n, int32_t* d_out_tokens, float* d_out_logits,
+                               int32_t eos_id, int32_t* d_n_done, void* stream);
+
+pmk_status pmk_set_mode(pmk_ctx* ctx, int32_t mode);
+pmk_status pmk_get_position(const pmk_ctx* ctx, int32_t* pos);
+
+/* After the caller synchronised the stream: reads the device error word. */
+pmk_status pmk_poll_error(pmk_ctx* ctx, pmk_device_error* err);
+
+/* Trace: with trace_steps > 0 and pmk_set_trace(ctx, 1), each task of the first trace_steps
+ * steps of the next decode call records (wait begin, start, end) from the constant 100 MHz
+ * clock.  pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats
+ * gives the mean share of queue time spent waiting. */
+pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
+pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);
+pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
+
+/* Schedule inspection (host only, also for device-less contexts). */
+pmk_status pmk_schedule_get_info(const pmk_ctx* ctx, pmk_schedule_info* info);
+
+/* ---- Schedule IR, exposed for the validator's tests and the validator CLI ---- */
+typedef enum {
+  PMK_OP_QKV = 1,     /* RMSNorm prologue + packed QKV GEMV rows [a0,a1) + RoPE + KV append */
+  PMK_OP_ATTN = 2,    /* split-KV attention partial for kv head a0, split a1 (+ last-arriver combine) */
+  PMK_OP_OPROJ = 3,   /* O GEMV rows [a0,a1) + residual */
+  PMK_OP_GATEUP = 4,  /* RMSNorm prologue + interleaved gate/up GEMV rows [a0,a1) + SwiGLU */
+  PMK_OP_DOWN = 5,    /* down GEMV rows [a0,a1) + residual */
+  PMK_OP_LMHEAD = 6,  /* final RMSNorm + LM-head rows [a0,a1) + tile argmax into the step key */
+  PMK_OP_TOKEN = 7    /* reads the step key, writes the output token and the next-input slot */
+} pmk_op;
+
+typedef struct {
+  int32_t op;          /* pmk_op */
+  int32_t layer;
+  int32_t a0, a1;
+  int32_t wait_ctr;    /* counter index, or -1 */
+  int32_t wait_count;  /* threshold within one step: 1 <= t <= producers(wait_ctr) */
+  int32_t wait_lag;    /* 0: producers of the same step; 1: of the previous step.  At global step e
+                          the wait needs counter >= (e - lag) * producers + wait_count (flags mode:
+                          at least wait_count producer flags >= e - lag + 1). */
+  int32_t signal_ctr;  /* counter index, or -1 (ATTN: signalled by the last arriver's combine) */
+  int32_t signal_slot; /* this producer's flag slot in signal_ctr */
+} pmk_task;
+
+typedef struct pmk_schedule pmk_schedule;
+
+/* Build the schedule for `n_cus` queues without a device. */
+pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
+                              pmk_schedule** out);
+void pmk_schedule_free(pmk_schedule* s);
+int32_t pmk_schedule_num_tasks(const pmk_schedule* s);
+int32_t pmk_schedule_num_counters(const pmk_schedule* s);
+int32_t pmk_schedule_num_queues(const pmk_schedule* s);
+pmk_status pmk_schedule_get_task(const pmk_schedule* s, int32_t i, pmk_task* t);
+pmk_status pmk_schedule_set_task(pmk_schedule* s, int32_t i, const pmk_task* t);
+/* queue q's task list; *len receives its length; returns a pointer into the schedule */
+const int32_t* pmk_schedule_queue(const pmk_schedule* s, int32_t q, int32_t* len);
+pmk_status pmk_schedule_set_queue(pmk_schedule* s, int32_t q, const int32_t* tasks, int32_t len);
+int32_t pmk_schedule_counter_producers(const pmk_schedule* s, int32_t c);
+pmk_status pmk_schedule_set_counter_producers(pmk_schedule* s, int32_t c, int32_t producers);
+/* Static validator: returns PMK_OK or PMK_ERR_SCHEDULE_INVALID with the first failed check
+ * (one line, "<check>: <detail>") copied into report[0..cap). */
+pmk_status pmk_schedule_validate(const pmk_schedule* s, char* report, size_t cap);
+/* CPU simulator: executes the queues for `steps` steps with one host thread per queue
+ * and randomised yields, treating each task as reading/writing its declared regions in
+ * NaN-poisoned buffers.  Returns PMK_OK, PMK_ERR_TIMEOUT (a queue stuck: deadlock) or
+ * PMK_ERR_SCHEDULE_INVALID (a read observed a poisoned or stale value: race). */
+pmk_status pmk_schedule_simulate(const pmk_schedule* s, int32_t steps, uint64_t seed, char* report, size_t cap);
+uint64_t pmk_schedule_hash(const pmk_schedule* s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PMK_H_ */

@@ -1,0 +1,1121 @@
+// gfx950 (CDNA4) kernels of the persistent batch-1 decode path.
+//
+// One workgroup of 512 threads (8 wave64s) per CU executes that CU's static task queue for n
+// decode steps (the persistent kernel), or one task per workgroup (the per-op kernels that the
+// hipGraph baseline captures).  Both run the same task functions below.
+//
+// Pages: "AutoMegaKernel" explainer, Method: Layer 0 (one cooperative block per compute unit
+// running wait -> dispatch -> signal over a local queue with monotonic counters) and Layer 1
+// (GEMV, attention and RMSNorm instructions).  "Kog AI MI300X monokernel tutorial": batch-1
+// projections are GEMV on the vector ALUs (not matrix cores), the decode loop with LM-head
+// sampling and the EOS check stays inside one resident kernel, and sync moved from atomic
+// arrival counters to polling of the producers' own words.  "Netra Kernel" summary, details:
+// FP8 E4M3 block-scale weights and GQA attention over an FP8 KV cache.
+//
+// Memory ordering.  Data exchanged between CUs (activations, q, attention partials, the current
+// K/V row, flags) is written with agent-scope coherent stores (sc1) and read with agent-scope
+// coherent loads, so no L2 write-back or invalidate is needed.  A producer drains its stores
+// (s_waitcnt vmcnt(0) in every wave, then a workgroup barrier) before one thread publishes the
+// flag or counter; a consumer polls that word and only then issues its coherent data loads.
+// Weights and KV rows of past steps are read with plain non-temporal loads: they were written
+// before this launch or, for KV rows, before their first read in this launch, and every KV row
+// covers whole 128-byte lines (head_dim * element size >= 128 is part of the contract).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pmk_device.h"
+
+namespace pmk {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum { WF16 = 0, WBF16 = 1, WFP8 = 2 };
+
+// ------------------------------------------------------------------------------------------------
+// coherent (agent scope) accesses
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ldc(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ldc(const unsigned long long* p) {
+  return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ldc2(const float* p) {  // 8-byte aligned pair
+  unsigned long long u = ldc(reinterpret_cast<const unsigned long long*>(p));
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ void stc(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(uint8_t* p, uint8_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until every memory access this wave issued has completed
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ u32x4 ld_nt(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ------------------------------------------------------------------------------------------------
+// reductions
+// ------------------------------------------------------------------------------------------------
+// Sum over the 64 lanes with DPP row operations; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));  // row_bcast15 -> rows 1,3
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));  // row_bcast31 -> rows 2,3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_shfl(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// block sum (all threads get the result); `red` holds >= kWaves floats of LDS
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum_shfl(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += red[i];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// ------------------------------------------------------------------------------------------------
+// storage formats
+// ------------------------------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float dec16(uint16_t b) {
+  if (DT == WBF16) return __uint_as_float((uint32_t)b << 16);
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t enc16(float v) {
+  if (DT == WBF16) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  }
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
+}
+// OCP E4M3FN: nearest even, saturating to +-448
+__device__ __forceinline__ uint8_t enc_e4m3(float v) {
+  if (v != v) return 0x7f;
+  const uint8_t sign = (__float_as_uint(v) >> 24) & 0x80;
+  const float a = fabsf(v);
+  if (a >= 448.f) return sign | 0x7e;
+  if (a < 0.015625f) return sign | (uint8_t)rintf(a * 512.f);  // subnormal grid 2^-9
+  int ex;
+  const float m = frexpf(a, &ex);               // a = m * 2^ex, m in [0.5, 1)
+  float q = rintf(ldexpf(m, 4));                 // significand in [8, 16]
+  int e = ex - 1;
+  if (q == 16.f) { q = 8.f; e += 1; }
+  int code = ((e + 7) << 3) | ((int)q - 8);
+  return sign | (uint8_t)(code > 0x7e ? 0x7e : code);
+}
+__device__ __forceinline__ float dec_e4m3(uint32_t word, int byte) {
+  // hardware OCP E4M3 -> f32 (gfx950)
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+  return byte == 0 ? lo.x : byte == 1 ? lo.y : byte == 2 ? hi.x : hi.y;
+}
+
+// ------------------------------------------------------------------------------------------------
+// synchronisation: waits (wave 0 polls, then a workgroup barrier) and signals
+// ------------------------------------------------------------------------------------------------
+__device__ __noinline__ void report_error(uint32_t* ctrl, uint32_t code, int cu, int task, int ctr, uint32_t expected,
+                                          uint32_t seen) {
+  if (atomicCAS(&ctrl[CTRL_ERR], 0u, code) == 0u) {
+    stc(&ctrl[CTRL_ERR + 1], (uint32_t)cu);
+    stc(&ctrl[CTRL_ERR + 2], (uint32_t)task);
+    stc(&ctrl[CTRL_ERR + 3], (uint32_t)ctr);
+    stc(&ctrl[CTRL_ERR + 4], expected);
+    stc(&ctrl[CTRL_ERR + 5], seen);
+  }
+  stc(&ctrl[CTRL_ABORT], 1u);
+}
+
+// Executed by the 64 lanes of wave 0.  Returns when the dependency is met, the launch was
+// aborted, or the spin limit ran out (which aborts the launch).
+__device__ __noinline__ void wave_wait(uint32_t* ctrl, const uint32_t* word, int prod, int count, int lag, int e,
+                                       int counters_mode, int64_t spin_limit, int cu, int task, int ctr) {
+  const int lane = threadIdx.x & 63;
+  int64_t spins = 0;
+  if (counters_mode) {
+    const int64_t need = (int64_t)(e - lag) * prod + count;
+    if (need <= 0) return;
+    while (true) {
+      const uint32_t v = ldc(word);
+      if ((int64_t)v >= need) return;
+      if (ldc(&ctrl[CTRL_ABORT])) return;
+      if (++spins > spin_limit) {
+        if (lane == 0) report_error(ctrl, PMK_ERR_TIMEOUT, cu, task, ctr, (uint32_t)need, v);
+        return;
+      }
+    }
+  } else {
+    const int target = e - lag + 1;
+    if (target <= 0) return;
+    while (true) {
+      int have = 0;
+      for (int base = 0; base < prod; base += 64) {
+        const int i = base + lane;
+        const bool ok = i < prod && (int)ldc(&word[i]) >= target;
+        have += __popcll(__ballot(ok));
+      }
+      if (have >= count) return;
+      if (ldc(&ctrl[CTRL_ABORT])) return;
+      if (++spins > spin_limit) {
+        if (lane == 0) report_error(ctrl, PMK_ERR_TIMEOUT, cu, task, ctr, (uint32_t)target, (uint32_t)have);
+        return;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void block_wait(const KParams& P, int ctr, int count, int lag, int e, int cu, int task) {
+  if (ctr >= 0 && threadIdx.x < 64) {
+    const bool cm = P.sync_mode == PMK_SYNC_COUNTERS;
+    const uint32_t* word = cm ? P.counters + ctr : P.flags + P.ctr_flag[ctr];
+    wave_wait(P.ctrl, word, P.ctr_prod[ctr], count, lag, e, cm ? 1 : 0, P.spin_limit, cu, task, ctr);
+  }
+  __syncthreads();
+}
+
+// All waves drain their stores, then thread 0 publishes.
+__device__ __forceinline__ void block_signal(const KParams& P, int ctr, int slot, int e) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0 && ctr >= 0) {
+    if (P.sync_mode == PMK_SYNC_COUNTERS)
+      __hip_atomic_fetch_add(&P.counters[ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      stc(&P.flags[P.ctr_flag[ctr] + slot], (uint32_t)(e + 1));
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// GEMV: rows [r0, r1) of W (row-major [rows][K]) against the activation vector staged in LDS.
+// Each wave owns a contiguous block of row groups (PAIR rows each).  A lane reads 16-byte
+// chunks c = j*64 + lane of a row (j = slice), so one wave instruction streams 1 KiB.  Weight
+// loads run through a ring of D registers per lane; the first D are issued BEFORE the task's
+// dependency wait (weights do not depend on it), then each consumed slot is refilled with the
+// chunk D units ahead.  Past the end the refill re-reads the tile's first chunk (a cache hit).
+// ------------------------------------------------------------------------------------------------
+template <int WDT>
+struct WFmt {
+  static constexpr int EPL = WDT == WFP8 ? 16 : 8;  // elements per 16-byte chunk
+  static constexpr int ES = WDT == WFP8 ? 1 : 2;     // bytes per element
+};
+
+template <int WDT>
+__device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x) {
+  if constexpr (WDT == WFP8) {
+    const float4 x0 = *reinterpret_cast<const float4*>(x);
+    const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
+    const float4 x2 = *reinterpret_cast<const float4*>(x + 8);
+    const float4 x3 = *reinterpret_cast<const float4*>(x + 12);
+    float a = 0.f, b = 0.f;
+    f32x2 p;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false); a = fmaf(p.x, x0.x, a); b = fmaf(p.y, x0.y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);  a = fmaf(p.x, x0.z, a); b = fmaf(p.y, x0.w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false); a = fmaf(p.x, x1.x, a); b = fmaf(p.y, x1.y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);  a = fmaf(p.x, x1.z, a); b = fmaf(p.y, x1.w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, false); a = fmaf(p.x, x2.x, a); b = fmaf(p.y, x2.y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, true);  a = fmaf(p.x, x2.z, a); b = fmaf(p.y, x2.w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, false); a = fmaf(p.x, x3.x, a); b = fmaf(p.y, x3.y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, true);  a = fmaf(p.x, x3.z, a); b = fmaf(p.y, x3.w, b);
+    return a + b;
+  } else {
+    const float4 x0 = *reinterpret_cast<const float4*>(x);
+    const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
+    float a = 0.f, b = 0.f;
+    a = fmaf(dec16<WDT>((uint16_t)(w.x & 0xffffu)), x0.x, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.x >> 16)), x0.y, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.y & 0xffffu)), x0.z, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.y >> 16)), x0.w, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.z & 0xffffu)), x1.x, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.z >> 16)), x1.y, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.w & 0xffffu)), x1.z, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.w >> 16)), x1.w, b);
+    return a + b;
+  }
+}
+
+constexpr int kRing = 8;
+
+// Sync: block-wide callable (wait + stage the input vector into LDS), run by every thread once.
+// ScaleRow: row -> pointer to the row's 128-column block scales (fp8 only).
+// Epi: PAIR == 1: epi(row, value); PAIR == 2: epi(even_row, value_even, value_odd).  Called by
+// every lane of the owning wave with wave-uniform arguments.
+template <int WDT, int PAIR, class Sync, class ScaleRow, class Epi>
+__device__ __forceinline__ void gemv_task(const uint8_t* __restrict__ W, int K, int r0, int r1, const float* xs,
+                                          Sync sync, ScaleRow srow, Epi epi) {
+  constexpr int EPL = WFmt<WDT>::EPL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
+  const int nch = K / EPL, nsl = (nch + 63) >> 6;
+  const int ngr = (r1 - r0) / PAIR;
+  const int wr0 = r0 + PAIR * (int)((int64_t)ngr * wave / kWaves);
+  const int wr1 = r0 + PAIR * (int)((int64_t)ngr * (wave + 1) / kWaves);
+  const int nunits = (wr1 - wr0) * nsl;
+
+  u32x4 ring[kRing];
+  float rsc[kRing];
+  int lrow = wr0, lj = 0;
+  const uint8_t* safe = W + (int64_t)r0 * rb;
+  auto issue = [&](int d) {
+    const int c = lj * 64 + lane;
+    const bool ok = lrow < wr1 && c < nch;
+    const uint8_t* p = ok ? W + (int64_t)lrow * rb + (int64_t)c * 16 : safe;
+    u32x4 v = ld_nt(p);
+    ring[d] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (WDT == WFP8) rsc[d] = ok ? srow(lrow)[c >> 3] : 0.f;
+    if (++lj == nsl) { lj = 0; ++lrow; }
+  };
+  if (nunits > 0) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) issue(d);
+  }
+  sync();
+  if (nunits <= 0) return;
+  float acc = 0.f, v_even = 0.f;
+  int crow = wr0, cj = 0;
+  for (int base = 0; base < nunits; base += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      const u32x4 w = ring[d];
+      float s = 1.f;
+      if constexpr (WDT == WFP8) s = rsc[d];
+      issue(d);
+      if (base + d < nunits) {
+        const float part = chunk_dot<WDT>(w, xs + (cj * 64 + lane) * EPL);
+        if constexpr (WDT == WFP8) acc = fmaf(part, s, acc);
+        else acc += part;
+        if (++cj == nsl) {
+          cj = 0;
+          const float v = wave_sum(acc);
+          acc = 0.f;
+          if constexpr (PAIR == 2) {
+            if (((crow - wr0) & 1) == 0) v_even = v;
+            else epi(crow - 1, v_even, v);
+          } else {
+            epi(crow, v);
+          }
+          ++crow;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// input staging (RMSNorm prologue fused into the consuming GEMV)
+// ------------------------------------------------------------------------------------------------
+// xs[0..H) = rmsnorm(src) * gain, xs[H..pad) = 0.  src is either a coherent fp32 vector or (emb != null)
+// a 16-bit embedding row.
+template <int EDT>
+__device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* emb, const float* gain, int H, int pad,
+                                              float eps, float* xs, float* red) {
+  float ss = 0.f;
+  for (int i = 2 * threadIdx.x; i < H; i += 2 * kThreads) {
+    float2 v;
+    if (emb) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(emb + i);
+      v = make_float2(dec16<EDT>((uint16_t)(u & 0xffff)), dec16<EDT>((uint16_t)(u >> 16)));
+    } else {
+      v = ldc2(src + i);
+    }
+    xs[i] = v.x;
+    xs[i + 1] = v.y;
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+  }
+  for (int i = H + threadIdx.x; i < pad; i += kThreads) xs[i] = 0.f;
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += kThreads) xs[i] = (xs[i] * r) * gain[i];
+  __syncthreads();
+}
+
+// xs[0..n) = src (coherent), zero padding
+__device__ __forceinline__ void stage_copy(const float* src, int n, int pad, float* xs) {
+  for (int i = 2 * threadIdx.x; i < n; i += 2 * kThreads) {
+    const float2 v = ldc2(src + i);
+    xs[i] = v.x;
+    xs[i + 1] = v.y;
+  }
+  for (int i = n + threadIdx.x; i < pad; i += kThreads) xs[i] = 0.f;
+  __syncthreads();
+}
+
+__device__ __forceinline__ int pad_len(int n, int epl) {
+  const int slice = 64 * epl;
+  return (n + slice - 1) / slice * slice;
+}
+
+// ------------------------------------------------------------------------------------------------
+// step context and token handling
+// ------------------------------------------------------------------------------------------------
+struct StepCtx {
+  int e;        // global step (since the last reset)
+  int s;        // step within this call
+  int pos;      // position written by this step
+  int tok;      // input token if already known, else -1
+  bool per_op;  // per-op kernels: no waits (kernel boundaries order the tasks)
+};
+
+__device__ __forceinline__ int key_token(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ __forceinline__ int input_token(const KParams& P, const StepCtx& sc) {
+  int tok = sc.tok;
+  if (tok < 0) tok = key_token(ldc(&P.keys[sc.s - 1]));
+  return tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
+}
+
+__device__ __forceinline__ void trace_mark(const KParams& P, int s, int ti, int slot, uint64_t value) {
+  if (threadIdx.x == 0 && P.trace_steps > 0 && P.call->trace && s < P.trace_steps)
+    P.trace[((int64_t)s * P.n_tasks + ti) * 4 + slot] = value;
+}
+
+__device__ __forceinline__ void maybe_wait(const KParams& P, const pmk_task& t, const StepCtx& sc, int cu, int ti) {
+  if (sc.per_op) return;
+  block_wait(P, t.wait_ctr, t.wait_count, t.wait_lag, sc.e, cu, ti);
+  trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
+}
+
+// ------------------------------------------------------------------------------------------------
+// tasks
+// ------------------------------------------------------------------------------------------------
+template <int WDT>
+__device__ __forceinline__ const float* fp8_rows(const KParams& P, int l, int which) {
+  return P.scales + (int64_t)l * P.sc_layer + P.sc_off[which];
+}
+
+// QKV: RMSNorm(x) -> packed QKV rows [a0, a1) -> RoPE on q/k pairs -> q to the workspace,
+// k and v appended to the cache at `pos`.
+template <int WDT, int KVDT>
+__device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
+  const int l = t.layer, H = P.H, hd = P.hd, half = hd / 2;
+  const int pad = pad_len(H, WFmt<WDT>::EPL);
+  float* xs = lds;
+  float* red = lds + P.xs_floats;
+  const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_qkv;
+  auto sync = [&]() {
+    maybe_wait(P, t, sc, cu, ti);
+    if (l == 0) {
+      const int tok = input_token(P, sc);
+      stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, P.eps, xs, red);
+    } else {
+      stage_rmsnorm<EDT>(P.x + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H, H, pad, P.eps, xs, red);
+    }
+  };
+  const int qrows = P.qdim, krows = P.nkv * hd;
+  const int nbc = (H + 127) / 128;
+  auto srow = [&](int r) -> const float* {
+    int which, orow;
+    if (r < qrows) { which = 0; orow = r; }
+    else if (r < qrows + krows) { which = 1; orow = r - qrows; }
+    else { which = 2; orow = r - qrows - krows; }
+    const int head = orow / hd, pr = orow % hd;
+    const int dim = (pr >> 1) + (pr & 1) * half;
+    return fp8_rows<WDT>(P, l, which) + (int64_t)((head * hd + dim) / 128) * nbc;
+  };
+  const float2* rope = P.rope + (int64_t)sc.pos * half;
+  auto epi = [&](int r, float a, float b) {
+    if ((threadIdx.x & 63) != 0) return;
+    int sec, base;
+    if (r < qrows) { sec = 0; base = 0; }
+    else if (r < qrows + krows) { sec = 1; base = qrows; }
+    else { sec = 2; base = qrows + krows; }
+    const int head = (r - base) / hd, i = ((r - base) % hd) >> 1;
+    if (sec < 2) {
+      const float2 cs = rope[i];
+      const float a2 = a * cs.x - b * cs.y;
+      const float b2 = b * cs.x + a * cs.y;
+      a = a2;
+      b = b2;
+    }
+    if (sec == 0) {
+      float* q = P.q + (int64_t)l * P.qdim + head * hd;
+      stc(q + i, a);
+      stc(q + i + half, b);
+      return;
+    }
+    const int64_t row = (((int64_t)l * P.nkv + head) * P.max_seq + sc.pos) * hd;
+    uint8_t* cache = sec == 1 ? P.kc : P.vc;
+    if constexpr (KVDT == WFP8) {
+      const float s = P.kv_scale[((int64_t)l * P.nkv + head) * 2 + (sec - 1)];
+      stc(cache + row + i, enc_e4m3(a / s));
+      stc(cache + row + i + half, enc_e4m3(b / s));
+    } else {
+      uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
+      stc(c16 + row + i, enc16<KVDT>(a));
+      stc(c16 + row + i + half, enc16<KVDT>(b));
+    }
+  };
+  gemv_task<WDT, 2>(W, H, t.a0, t.a1, xs, sync, srow, epi);
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
+// query heads of the group; the partial (m, l, acc[hd]) per head goes to the workspace.  The last
+// split to finish (atomic ticket) combines all splits of the head group into o.
+// Thread layout: scores take one position per thread (K row in registers, q broadcast from LDS);
+// P.V takes positions across waves and head dimensions across lanes.  K and V rows of past
+// positions are loaded before the dependency wait; the current position's row after it.
+template <int KVDT>
+__device__ __forceinline__ uint32_t load_v_word(const uint8_t* vrow, int lane, int dpl, bool coherent) {
+  constexpr int KES = KVDT == WFP8 ? 1 : 2;
+  const int bytes = dpl * KES;  // 1, 2 or 4
+  const uint8_t* p = vrow + lane * bytes;
+  if (bytes == 4) return coherent ? ldc(reinterpret_cast<const uint32_t*>(p)) : *reinterpret_cast<const uint32_t*>(p);
+  if (bytes == 2)
+    return coherent ? (uint32_t)__hip_atomic_load(reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(p)), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                    : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+  return coherent ? (uint32_t)__hip_atomic_load(const_cast<uint8_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : (uint32_t)*p;
+}
+
+template <int KVDT>
+__device__ __forceinline__ float2 decode_v_word(uint32_t w, int dpl, float vscale) {
+  if constexpr (KVDT == WFP8) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    return make_float2(f.x * vscale, dpl == 2 ? f.y * vscale : 0.f);
+  } else {
+    return make_float2(dec16<KVDT>((uint16_t)(w & 0xffff)), dpl == 2 ? dec16<KVDT>((uint16_t)(w >> 16)) : 0.f);
+  }
+}
+
+__device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  return u32x4{ldc(q), ldc(q + 1), ldc(q + 2), ldc(q + 3)};
+}
+
+template <int KVDT>
+__device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  constexpr int KES = KVDT == WFP8 ? 1 : 2;
+  constexpr int KEPL = KVDT == WFP8 ? 16 : 8;  // K elements per 16-byte chunk
+  constexpr int VB = 16;                       // V words prefetched per lane
+  const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp, hd = P.hd;
+  const int T = sc.pos + 1;
+  const int chunk = (T + S - 1) / S;
+  const int t0 = min(T, split * chunk), t1 = min(T, t0 + chunk);
+  const int n = t1 - t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t headbase = ((int64_t)l * P.nkv + g) * P.max_seq;
+  const int rowbytes = hd * KES;  // 128 or 256
+  const int nvec = rowbytes / 16;  // 8 or 16
+  const int dpl = hd / 64;         // head dims per lane in P.V: 1 or 2
+  const uint8_t* Kc = P.kc + headbase * rowbytes;
+  const uint8_t* Vc = P.vc + headbase * rowbytes;
+  const int sstride = (n + 3) & ~3;
+  float* qs = lds;                        // [grp][hd]
+  float* sc_lds = qs + grp * hd;          // [grp][sstride]
+  float* red = sc_lds + grp * sstride;    // [kWaves][grp][hd]
+  float* small = lds + P.xs_floats;       // scalars
+  float kscale = 1.f, vscale = 1.f;
+  if constexpr (KVDT == WFP8) {
+    kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
+    vscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2 + 1];
+  }
+  // ---- loads that do not depend on this step: K row of this thread's position, first V words ----
+  u32x4 krow[16];
+  const bool one_pass = n <= kThreads;
+  const int my_t = t0 + tid;
+  if (one_pass && tid < n && my_t < sc.pos) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (v < nvec) krow[v] = ld_nt(Kc + (int64_t)my_t * rowbytes + v * 16);
+  }
+  uint32_t vreg[VB];
+#pragma unroll
+  for (int k = 0; k < VB; ++k) {
+    const int tt = wave + kWaves * k, pt = t0 + tt;
+    vreg[k] = (tt < n && pt < sc.pos) ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, false) : 0u;
+  }
+  maybe_wait(P, t, sc, cu, ti);
+  const float* qsrc = P.q + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
+  for (int i = 2 * tid; i < grp * hd; i += 2 * kThreads) {
+    const float2 v = ldc2(qsrc + i);
+    qs[i] = v.x;
+    qs[i + 1] = v.y;
+  }
+  if (one_pass && tid < n && my_t == sc.pos) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (v < nvec) krow[v] = ldc16B(Kc + (int64_t)my_t * rowbytes + v * 16);
+  }
+  __syncthreads();
+  // ---- scores ----
+  if (one_pass) {
+    if (tid < n) {
+      for (int j = 0; j < grp; ++j) {
+        const float* qj = qs + j * hd;
+        float a = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (v < nvec) a += chunk_dot<KVDT>(krow[v], qj + v * KEPL);
+        sc_lds[j * sstride + tid] = a * kscale * P.attn_scale;
+      }
+    }
+  } else {
+    for (int base = 0; base < n; base += kThreads) {
+      const int tt = base + tid;
+      if (tt < n) {
+        const int pt = t0 + tt;
+        const uint8_t* kp = Kc + (int64_t)pt * rowbytes;
+        for (int j = 0; j < grp; ++j) {
+          const float* qj = qs + j * hd;
+          float a = 0.f;
+          for (int v = 0; v < nvec; ++v) {
+            const u32x4 kv = pt < sc.pos ? ld_nt(kp + v * 16) : ldc16B(kp + v * 16);
+            a += chunk_dot<KVDT>(kv, qj + v * KEPL);
+          }
+          sc_lds[j * sstride + tt] = a * kscale * P.attn_scale;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- softmax statistics per head ----
+  float* mvals = small;       // [grp]
+  float* lvals = small + 8;   // [grp]
+  float* red8 = small + 16;   // [kWaves]
+  for (int j = 0; j < grp; ++j) {
+    float m = -INFINITY;
+    for (int tt = tid; tt < n; tt += kThreads) m = fmaxf(m, sc_lds[j * sstride + tt]);
+    m = block_max(m, red8);
+    float sum = 0.f;
+    for (int tt = tid; tt < n; tt += kThreads) {
+      const float p = expf(sc_lds[j * sstride + tt] - m);
+      sc_lds[j * sstride + tt] = p;
+      sum += p;
+    }
+    sum = block_sum(sum, red8);
+    if (tid == 0) { mvals[j] = m; lvals[j] = sum; }
+  }
+  __syncthreads();
+  // ---- P.V ----
+  float acc[8][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { acc[j][0] = 0.f; acc[j][1] = 0.f; }
+  const int nk = (n - wave + kWaves - 1) / kWaves;  // positions of this wave
+  for (int kb = 0; kb < nk; kb += VB) {
+    if (kb > 0) {
+#pragma unroll
+      for (int k = 0; k < VB; ++k) {
+        const int tt = wave + kWaves * (kb + k), pt = t0 + tt;
+        vreg[k] = (tt < n && pt < sc.pos) ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, false) : 0u;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < VB; ++k) {
+      const int tt = wave + kWaves * (kb + k), pt = t0 + tt;
+      if (tt < n) {
+        const uint32_t w = pt == sc.pos ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, true) : vreg[k];
+        const float2 v = decode_v_word<KVDT>(w, dpl, vscale);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < grp) {
+            const float p = sc_lds[j * sstride + tt];
+            acc[j][0] = fmaf(p, v.x, acc[j][0]);
+            acc[j][1] = fmaf(p, v.y, acc[j][1]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < grp) {
+      red[(wave * grp + j) * hd + lane * dpl] = acc[j][0];
+      if (dpl == 2) red[(wave * grp + j) * hd + lane * dpl + 1] = acc[j][1];
+    }
+  }
+  __syncthreads();
+  float* part = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * (hd + 2);
+  for (int i = tid; i < grp * hd; i += kThreads) {
+    const int j = i / hd, d = i % hd;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[(w * grp + j) * hd + d];
+    stc(part + (int64_t)j * (hd + 2) + 2 + d, s);
+  }
+  if (tid < grp) {
+    stc(part + (int64_t)tid * (hd + 2), mvals[tid]);
+    stc(part + (int64_t)tid * (hd + 2) + 1, lvals[tid]);
+  }
+  drain();
+  __syncthreads();
+  // ---- ticket: the last split of this head group combines ----
+  int* last = reinterpret_cast<int*>(small + 32);
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&P.tickets[l * P.nkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = (int)(old % (uint32_t)S) == S - 1;
+  }
+  __syncthreads();
+  if (!*last) return;
+  const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * (hd + 2);
+  float* ml = lds;                 // [S*grp][2]
+  float* wts = lds + 2 * S * grp;  // [grp][S]
+  for (int i = tid; i < S * grp; i += kThreads) {
+    const float2 v = ldc2(pg + (int64_t)i * (hd + 2));
+    ml[2 * i] = v.x;
+    ml[2 * i + 1] = v.y;
+  }
+  __syncthreads();
+  for (int j = tid; j < grp; j += kThreads) {
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, ml[2 * (s2 * grp + j)]);
+    float den = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float m = ml[2 * (s2 * grp + j)];
+      const float w = m == -INFINITY ? 0.f : expf(m - M);
+      wts[j * S + s2] = w;
+      den += w * ml[2 * (s2 * grp + j) + 1];
+    }
+    const float inv = 1.0f / den;
+    for (int s2 = 0; s2 < S; ++s2) wts[j * S + s2] *= inv;
+  }
+  __syncthreads();
+  float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
+  for (int i = tid; i < grp * hd; i += kThreads) {
+    const int j = i / hd, d = i % hd;
+    const float* src = pg + (int64_t)j * (hd + 2) + 2 + d;
+    const int64_t sstep = (int64_t)grp * (hd + 2);
+    float s = 0.f;
+    int s2 = 0;
+    for (; s2 + 8 <= S; s2 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ldc(src + (s2 + u) * sstep);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s = fmaf(wts[j * S + s2 + u], v[u], s);
+    }
+    for (; s2 < S; ++s2) s = fmaf(wts[j * S + s2], ldc(src + s2 * sstep), s);
+    stc(o + i, s);
+  }
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// O projection + residual: xm[r] = x[r] + Wo[r].o
+template <int WDT>
+__device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
+  const int l = t.layer, K = P.qdim;
+  float* xs = lds;
+  const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
+  auto sync = [&]() {
+    maybe_wait(P, t, sc, cu, ti);
+    stage_copy(P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+  };
+  const int nbc = (K + 127) / 128;
+  auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
+  auto epi = [&](int r, float v) {
+    if ((threadIdx.x & 63) != 0) return;
+    float res;
+    if (l == 0) {
+      const int tok = input_token(P, sc);
+      res = dec16<EDT>(P.embed[(int64_t)tok * P.H + r]);
+    } else {
+      res = ldc(P.x + (int64_t)l * P.H + r);
+    }
+    stc(P.xm + (int64_t)l * P.H + r, res + v);
+  };
+  gemv_task<WDT, 1>(W, K, t.a0, t.a1, xs, sync, srow, epi);
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// RMSNorm(xm) -> interleaved gate/up rows [a0, a1) -> h[n] = silu(gate_n) * up_n
+template <int WDT>
+__device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  const int l = t.layer, H = P.H;
+  float* xs = lds;
+  float* red = lds + P.xs_floats;
+  const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_gu;
+  auto sync = [&]() {
+    maybe_wait(P, t, sc, cu, ti);
+    stage_rmsnorm<WBF16>(P.xm + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H + H, H,
+                         pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+  };
+  const int nbc = (H + 127) / 128;
+  auto srow = [&](int r) -> const float* {
+    return fp8_rows<WDT>(P, l, (r & 1) ? 5 : 4) + (int64_t)((r >> 1) / 128) * nbc;
+  };
+  auto epi = [&](int r, float gte, float up) {
+    if ((threadIdx.x & 63) != 0) return;
+    const float hval = gte / (1.0f + expf(-gte)) * up;
+    stc(P.h + (int64_t)l * P.F + (r >> 1), hval);
+  };
+  gemv_task<WDT, 2>(W, H, t.a0, t.a1, xs, sync, srow, epi);
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// down projection + residual: x[l+1][r] = xm[r] + Wd[r].h
+template <int WDT>
+__device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  const int l = t.layer, K = P.F;
+  float* xs = lds;
+  const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_d;
+  auto sync = [&]() {
+    maybe_wait(P, t, sc, cu, ti);
+    stage_copy(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+  };
+  const int nbc = (K + 127) / 128;
+  auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 6) + (int64_t)(r / 128) * nbc; };
+  auto epi = [&](int r, float v) {
+    if ((threadIdx.x & 63) != 0) return;
+    const float res = ldc(P.xm + (int64_t)l * P.H + r);
+    stc(P.x + (int64_t)(l + 1) * P.H + r, res + v);
+  };
+  gemv_task<WDT, 1>(W, K, t.a0, t.a1, xs, sync, srow, epi);
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// final RMSNorm + LM-head rows [a0, a1); tile argmax folded into the step's 64-bit key
+__device__ __forceinline__ uint32_t orderable(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int WDT>
+__device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  const int H = P.H;
+  float* xs = lds;
+  float* red = lds + P.xs_floats;
+  CallParams* cp = P.call;
+  float* out_logits = cp->out_logits;
+  auto sync = [&]() {
+    maybe_wait(P, t, sc, cu, ti);
+    stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+  };
+  const int nbc = (H + 127) / 128;
+  auto srow = [&](int r) -> const float* { return P.sc_lm + (int64_t)(r / 128) * nbc; };
+  float best = -INFINITY;
+  int best_i = 0x7fffffff;
+  bool nan_seen = false;
+  auto epi = [&](int r, float v) {
+    if (v != v) nan_seen = true;
+    if (v > best || (v == best && r < best_i)) { best = v; best_i = r; }
+    if (out_logits && (threadIdx.x & 63) == 0) out_logits[(int64_t)sc.s * P.V + r] = v;
+  };
+  gemv_task<WDT, 1>(P.lm, H, t.a0, t.a1, xs, sync, srow, epi);
+  // workgroup argmax -> one atomic max per task
+  unsigned long long* kred = reinterpret_cast<unsigned long long*>(red + 16);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    kred[wave] = best_i == 0x7fffffff ? 0ull
+                                      : (((unsigned long long)orderable(best)) << 32) | (0xFFFFFFFFu - (uint32_t)best_i);
+    if (nan_seen) report_error(P.ctrl, PMK_ERR_NAN, cu, ti, -1, 0, 0);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long k = 0;
+    for (int w = 0; w < kWaves; ++w) k = kred[w] > k ? kred[w] : k;
+    __hip_atomic_fetch_max(&P.keys[sc.s], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// greedy token of the step: output, next-input slot; per-op kernels also advance the step state
+__device__ __forceinline__ void task_token(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+  maybe_wait(P, t, sc, cu, ti);
+  if (threadIdx.x == 0) {
+    CallParams* cp = P.call;
+    const unsigned long long key = ldc(&P.keys[sc.s]);
+    int tok = key_token(key);
+    const uint32_t ov = (uint32_t)(key >> 32);
+    const float best = __uint_as_float((ov & 0x80000000u) ? (ov & 0x7fffffffu) : ~ov);
+    if (key == 0ull || best != best) {
+      report_error(P.ctrl, PMK_ERR_NAN, cu, ti, -1, 0, 0);
+      tok = 0;
+    }
+    if (cp->out_tokens) cp->out_tokens[sc.s] = tok;
+    stc(&P.ctrl[CTRL_TOKEN], (uint32_t)tok);
+    if (sc.per_op) {
+      const bool stop = cp->eos >= 0 && tok == cp->eos && cp->forced == nullptr;
+      stc(&P.ctrl[CTRL_POS], (uint32_t)(sc.pos + 1));
+      stc(&P.ctrl[CTRL_EPOCH], (uint32_t)(sc.e + 1));
+      stc(&P.ctrl[CTRL_STEP], (uint32_t)(sc.s + 1));
+      if (stop) stc(&P.ctrl[CTRL_STOPPED], 1u);
+      if (cp->n_done) cp->n_done[0] = sc.s + 1;
+    }
+  }
+  (void)lds;
+  (void)t;
+}
+
+template <int WDT, int KVDT>
+__device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                         int cu) {
+  switch (t.op) {
+    case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_ATTN: task_attn<KVDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_OPROJ: task_oproj<WDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_DOWN: task_down<WDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_LMHEAD: task_lmhead<WDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_TOKEN: task_token(P, t, ti, sc, lds, cu); break;
+    default: break;
+  }
+  __syncthreads();  // LDS is reused by the next task
+}
+
+// ------------------------------------------------------------------------------------------------
+// the persistent kernel: one workgroup per CU, n steps of this CU's queue
+// ------------------------------------------------------------------------------------------------
+template <int WDT, int KVDT>
+__global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
+  extern __shared__ float lds[];
+  const int cu = blockIdx.x;
+  const CallParams cp = *P.call;
+  const int epoch0 = (int)P.ctrl[CTRL_EPOCH];
+  const int pos0 = (int)P.ctrl[CTRL_POS];
+  const int tok0 = (int)P.ctrl[CTRL_TOKEN];
+  const int q0 = P.qoff[cu], q1 = P.qoff[cu + 1];
+  const int lm_ctr = P.tasks[P.qtasks[P.qoff[1] - 1]].wait_ctr;  // queue 0 ends with the TOKEN task
+  int steps = 0;
+  for (int s = 0; s < cp.n_steps; ++s) {
+    const int e = epoch0 + s;
+    if (s > 0 && cp.eos >= 0 && cp.forced == nullptr) {
+      block_wait(P, lm_ctr, P.ctr_prod[lm_ctr], 1, e, cu, -1);
+      if (key_token(ldc(&P.keys[s - 1])) == cp.eos) break;
+    }
+    StepCtx sc;
+    sc.e = e;
+    sc.s = s;
+    sc.pos = pos0 + s;
+    sc.tok = cp.forced ? cp.forced[s] : (s == 0 ? tok0 : -1);
+    if (sc.tok >= P.V) sc.tok = P.V - 1;
+    sc.per_op = false;
+    for (int qi = q0; qi < q1; ++qi) {
+      const int ti = P.qtasks[qi];
+      const pmk_task t = P.tasks[ti];
+      trace_mark(P, s, ti, 0, __builtin_amdgcn_s_memrealtime());
+      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu);
+      trace_mark(P, s, ti, 2, __builtin_amdgcn_s_memrealtime());
+      trace_mark(P, s, ti, 3, (uint64_t)cu);
+    }
+    steps = s + 1;
+  }
+  if (cu == 0 && threadIdx.x == 0) {
+    stc(&P.ctrl[CTRL_EPOCH], (uint32_t)(epoch0 + steps));
+    stc(&P.ctrl[CTRL_POS], (uint32_t)(pos0 + steps));
+    if (cp.n_done) cp.n_done[0] = steps;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// per-op kernels (hipGraph baseline): one workgroup per task of one phase, no waits
+// ------------------------------------------------------------------------------------------------
+template <int WDT, int KVDT>
+__global__ __launch_bounds__(kThreads, 1) void pmk_phase(KParams P, int first_task) {
+  extern __shared__ float lds[];
+  const CallParams* cp = P.call;
+  const int s = (int)P.ctrl[CTRL_STEP];
+  if (P.ctrl[CTRL_STOPPED] || s >= cp->n_steps) return;
+  StepCtx sc;
+  sc.e = (int)P.ctrl[CTRL_EPOCH];
+  sc.s = s;
+  sc.pos = (int)P.ctrl[CTRL_POS];
+  sc.tok = cp->forced ? cp->forced[s] : (int)P.ctrl[CTRL_TOKEN];
+  if (sc.tok >= P.V) sc.tok = P.V - 1;
+  if (sc.tok < 0) sc.tok = 0;
+  sc.per_op = true;
+  const int ti = first_task + blockIdx.x;
+  const pmk_task t = P.tasks[ti];
+  run_task<WDT, KVDT>(P, t, ti, sc, lds, blockIdx.x);
+}
+
+// ------------------------------------------------------------------------------------------------
+// small service kernels
+// ------------------------------------------------------------------------------------------------
+__global__ void pmk_begin_call(KParams P, CallParams cp) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) {
+    *P.call = cp;
+    P.ctrl[CTRL_STEP] = 0;
+    P.ctrl[CTRL_STOPPED] = 0;
+    if (cp.n_done) cp.n_done[0] = 0;
+  }
+  for (int k = i; k <= cp.n_steps; k += gridDim.x * blockDim.x) P.keys[k] = 0ull;
+}
+
+// zero flags, counters, tickets and control words; set position and next token
+__global__ void pmk_reset(KParams P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x, n = gridDim.x * blockDim.x;
+  for (int k = i; k < n_flags; k += n) P.flags[k] = 0u;
+  for (int k = i; k < n_counters; k += n) P.counters[k] = 0u;
+  for (int k = i; k < P.L * P.nkv; k += n) P.tickets[k] = 0u;
+  for (int k = i; k < CTRL_WORDS; k += n) P.ctrl[k] = 0u;
+  __syncthreads();
+  if (i == 0) {
+    P.ctrl[CTRL_POS] = (uint32_t)pos;
+    P.ctrl[CTRL_TOKEN] = (uint32_t)(d_token ? *d_token : token);
+  }
+}
+
+// rewind: position and next token only (counters keep counting from the current epoch)
+__global__ void pmk_set_pos(KParams P, int pos, const int32_t* d_token) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    P.ctrl[CTRL_POS] = (uint32_t)pos;
+    P.ctrl[CTRL_TOKEN] = (uint32_t)*d_token;
+  }
+}
+
+__global__ void pmk_copy_token(const KParams P, int32_t* dst) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *dst = (int32_t)P.ctrl[CTRL_TOKEN];
+}
+
+// KV rows [L][nkv][P][hd] (element bytes es) -> cache [L][nkv][max_seq][hd]
+__global__ void pmk_load_kv_rows(KParams P, const uint8_t* src_k, const uint8_t* src_v, int npos, int es) {
+  const int64_t rowb = (int64_t)P.hd * es;
+  const int64_t total = (int64_t)P.L * P.nkv * npos * rowb / 16;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t byte = i * 16;
+    const int64_t row = byte / rowb, off = byte % rowb;
+    const int64_t lg = row / npos, p = row % npos;
+    const int64_t dst = (lg * P.max_seq + p) * rowb + off;
+    *reinterpret_cast<u32x4*>(P.kc + dst) = *reinterpret_cast<const u32x4*>(src_k + byte);
+    *reinterpret_cast<u32x4*>(P.vc + dst) = *reinterpret_cast<const u32x4*>(src_v + byte);
+  }
+}
+
+// Repack: packed QKV row r of layer l <- wq/wk/wv row (head*hd + pair + half*hd/2)
+__global__ void pmk_repack_qkv(uint8_t* dst, const uint8_t* wq, const uint8_t* wk, const uint8_t* wv, int nq, int nkv,
+                               int hd, int64_t rowb) {
+  const int r = blockIdx.x;
+  const int qrows = nq * hd, krows = nkv * hd;
+  const uint8_t* src;
+  int base;
+  if (r < qrows) { src = wq; base = 0; }
+  else if (r < qrows + krows) { src = wk; base = qrows; }
+  else { src = wv; base = qrows + krows; }
+  const int head = (r - base) / hd, pr = (r - base) % hd;
+  const int orow = head * hd + (pr >> 1) + (pr & 1) * (hd / 2);
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + (int64_t)orow * rowb);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)r * rowb);
+  for (int i = threadIdx.x; i < rowb / 16; i += blockDim.x) d[i] = s[i];
+}
+
+// Repack: packed gate/up row r <- gate row r/2 (r even) or up row r/2 (r odd)
+__global__ void pmk_repack_gu(uint8_t* dst, const uint8_t* wg, const uint8_t* wu, int64_t rowb) {
+  const int r = blockIdx.x;
+  const uint8_t* src = (r & 1) ? wu : wg;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + (int64_t)(r >> 1) * rowb);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + (int64_t)r * rowb);
+  for (int i = threadIdx.x; i < rowb / 16; i += blockDim.x) d[i] = s[i];
+}
+
+// 16-bit gain -> fp32
+__global__ void pmk_widen(float* dst, const uint16_t* src, int n, int bf16) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf16 ? dec16<WBF16>(src[i]) : dec16<WF16>(src[i]);
+}
+
+// ------------------------------------------------------------------------------------------------
+// host-visible launch helpers
+// ------------------------------------------------------------------------------------------------
+typedef void (*KernelFn)(KParams);
+typedef void (*PhaseFn)(KParams, int);
+
+const void* persistent_kernel(int wdt, int kvdt) {
+  if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_persistent<WF16, WF16>;
+  if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_persistent<WBF16, WBF16>;
+  if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_persistent<WFP8, WFP8>;
+  return nullptr;
+}
+
+const void* phase_kernel(int wdt, int kvdt) {
+  if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_phase<WF16, WF16>;
+  if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_phase<WBF16, WBF16>;
+  if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_phase<WFP8, WFP8>;
+  return nullptr;
+}
+
+hipError_t launch_begin_call(const KParams& P, const CallParams& cp, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_begin_call, dim3(16), dim3(256), 0, st, P, cp);
+  return hipGetLastError();
+}
+hipError_t launch_reset(const KParams& P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(pmk_reset, dim3(1), dim3(1024), 0, st, P, n_flags, n_counters, pos, token, d_token);
+  return hipGetLastError();
+}
+hipError_t launch_set_pos(const KParams& P, int pos, const int32_t* d_token, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_set_pos, dim3(1), dim3(64), 0, st, P, pos, d_token);
+  return hipGetLastError();
+}
+hipError_t launch_copy_token(const KParams& P, int32_t* dst, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_copy_token, dim3(1), dim3(64), 0, st, P, dst);
+  return hipGetLastError();
+}
+hipError_t launch_load_kv_rows(const KParams& P, const void* k, const void* v, int npos, int es, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_load_kv_rows, dim3(2048), dim3(256), 0, st, P, (const uint8_t*)k, (const uint8_t*)v, npos, es);
+  return hipGetLastError();
+}
+hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const void* wv, int nq, int nkv, int hd,
+                             int64_t rowb, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_repack_qkv, dim3((nq + 2 * nkv) * hd), dim3(256), 0, st, dst, (const uint8_t*)wq,
+                     (const uint8_t*)wk, (const uint8_t*)wv, nq, nkv, hd, rowb);
+  return hipGetLastError();
+}
+hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_repack_gu, dim3(2 * F), dim3(256), 0, st, dst, (const uint8_t*)wg, (const uint8_t*)wu, rowb);
+  return hipGetLastError();
+}
+hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_widen, dim3((n + 255) / 256), dim3(256), 0, st, dst, (const uint16_t*)src, n, bf16);
+  return hipGetLastError();
+}
+
+}  // namespace pmk

@@ -1,0 +1,805 @@
+// Host runtime behind the C ABI declared in include/pmk.h.
+//
+// Pages: "Netra Kernel" summary, details (a runtime with a C ABI binds persistent and boundary
+// buffers and launches fixed kernels, or replays a prepared HIP graph, on a caller-owned stream;
+// requests outside the exact operation contract are rejected rather than approximated) and
+// "AutoMegaKernel" explainer, Safety Gate (an invalid schedule is rejected before any launch).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/pmk.h"
+#include "pmk_device.h"
+#include "schedule.h"
+
+namespace pmk {
+const void* persistent_kernel(int wdt, int kvdt);
+const void* phase_kernel(int wdt, int kvdt);
+hipError_t launch_begin_call(const KParams& P, const CallParams& cp, hipStream_t st);
+hipError_t launch_reset(const KParams& P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token,
+                        hipStream_t st);
+hipError_t launch_set_pos(const KParams& P, int pos, const int32_t* d_token, hipStream_t st);
+hipError_t launch_copy_token(const KParams& P, int32_t* dst, hipStream_t st);
+hipError_t launch_load_kv_rows(const KParams& P, const void* k, const void* v, int npos, int es, hipStream_t st);
+hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const void* wv, int nq, int nkv, int hd,
+                             int64_t rowb, hipStream_t st);
+hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st);
+hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st);
+}  // namespace pmk
+
+using namespace pmk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+int64_t nblk(int64_t n) { return (n + 127) / 128; }
+
+struct Phase {
+  int first, count;
+};
+
+}  // namespace
+
+struct pmk_ctx {
+  pmk_model_config cfg;
+  pmk_schedule_config sc;
+  ModelDims m;
+  Schedule sched;
+  DeviceTables tabs;
+  int device = -1;
+  int n_cus = 0;
+  int wes = 2, kves = 2;
+  pmk_sizes sizes{};
+  // arena layout (bytes)
+  int64_t a_embed = 0, a_lm = 0, a_layers = 0, layer_bytes = 0, off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0;
+  int64_t a_gains = 0, a_final = 0, a_scales = 0, sc_layer = 0, sc_off[7] = {}, a_sclm = 0, a_rope = 0;
+  // workspace layout (bytes)
+  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_tickets = 0, w_keys = 0, w_kvscale = 0, w_x = 0,
+          w_xm = 0, w_q = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
+          w_cprod = 0, w_cflag = 0;
+  uint8_t* arena = nullptr;
+  uint8_t* kv = nullptr;
+  uint8_t* ws = nullptr;
+  bool bound = false, weights = false, kv_ready = false;
+  int32_t pos_host = 0;
+  int mode = PMK_MODE_MEGAKERNEL;
+  int trace_on = 0;
+  int xs_floats = 0;
+  size_t lds_bytes = 0;
+  KParams kp{};
+  std::vector<Phase> phases;
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
+  std::string err;
+  std::vector<float> rope_host;
+  uint64_t hash = 0;
+};
+
+namespace {
+
+pmk_status fail(pmk_ctx* c, pmk_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  g_err = msg;
+  return s;
+}
+
+#define HIPCHK(ctx, call)                                                                        \
+  do {                                                                                           \
+    hipError_t e_ = (call);                                                                      \
+    if (e_ != hipSuccess)                                                                        \
+      return fail(ctx, PMK_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));          \
+  } while (0)
+
+std::string contract_check(const pmk_model_config& c) {
+  if (c.has_bias) return "biased projections are outside the contract";
+  if (c.tie_embeddings) return "tied embeddings are outside the contract";
+  if (c.n_layers < 1 || c.hidden < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.ffn < 1 || c.vocab < 1 || c.max_seq < 1)
+    return "every dimension must be positive";
+  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+  if (c.n_q_heads / c.n_kv_heads > 8) return "at most 8 query heads per kv head";
+  const bool ok_pair = (c.weight_dtype == PMK_DT_F16 && c.kv_dtype == PMK_DT_F16) ||
+                       (c.weight_dtype == PMK_DT_BF16 && c.kv_dtype == PMK_DT_BF16) ||
+                       (c.weight_dtype == PMK_DT_FP8_E4M3 && c.kv_dtype == PMK_DT_FP8_E4M3);
+  if (!ok_pair) return "supported (weight, kv) formats: (f16, f16), (bf16, bf16), (fp8, fp8)";
+  const int epl = c.weight_dtype == PMK_DT_FP8_E4M3 ? 16 : 8;
+  if (c.hidden % epl || c.ffn % epl || (c.n_q_heads * c.head_dim) % epl)
+    return "hidden, ffn and n_q_heads*head_dim must be multiples of 8 (16 for fp8 weights)";
+  const int kves = c.kv_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
+  if (c.head_dim * kves < 128) return "a KV row (head_dim * element size) must cover at least 128 bytes";
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return "rms_eps and rope_theta must be positive";
+  if (c.ffn > 36864 || c.hidden > 36864) return "hidden and ffn above 36864 exceed the staged-activation LDS budget";
+  return "";
+}
+
+ModelDims dims_of(const pmk_model_config& c) {
+  ModelDims m;
+  m.L = c.n_layers;
+  m.H = c.hidden;
+  m.nq = c.n_q_heads;
+  m.nkv = c.n_kv_heads;
+  m.hd = c.head_dim;
+  m.F = c.ffn;
+  m.V = c.vocab;
+  m.max_seq = c.max_seq;
+  m.wdt = c.weight_dtype;
+  m.kvdt = c.kv_dtype;
+  m.eps = c.rms_eps;
+  m.theta = c.rope_theta;
+  return m;
+}
+
+pmk_schedule_config defaults(const pmk_schedule_config* s) {
+  pmk_schedule_config d{};
+  if (s) d = *s;
+  if (d.spin_limit <= 0) d.spin_limit = 1ll << 22;
+  if (d.prefetch == 0) d.prefetch = 1;
+  return d;
+}
+
+void compute_layout(pmk_ctx* c) {
+  const ModelDims& m = c->m;
+  const int64_t wes = c->wes, H = m.H, F = m.F, V = m.V, qd = m.qdim(), L = m.L;
+  int64_t a = 0;
+  c->a_embed = a; a = align256(a + V * H * 2);
+  c->a_lm = a; a = align256(a + V * H * wes);
+  int64_t lb = 0;
+  c->off_qkv = lb; lb = align256(lb + (int64_t)m.qkv_rows() * H * wes);
+  c->off_o = lb; lb = align256(lb + H * qd * wes);
+  c->off_gu = lb; lb = align256(lb + 2 * F * H * wes);
+  c->off_d = lb; lb = align256(lb + H * F * wes);
+  c->layer_bytes = lb;
+  c->a_layers = a; a = align256(a + L * lb);
+  c->a_gains = a; a = align256(a + L * 2 * H * 4);
+  c->a_final = a; a = align256(a + H * 4);
+  c->a_scales = a;
+  if (m.wdt == PMK_DT_FP8_E4M3) {
+    const int64_t kvd = (int64_t)m.nkv * m.hd;
+    const int64_t sz[7] = {nblk(qd) * nblk(H), nblk(kvd) * nblk(H), nblk(kvd) * nblk(H), nblk(H) * nblk(qd),
+                           nblk(F) * nblk(H),  nblk(F) * nblk(H),   nblk(H) * nblk(F)};
+    int64_t off = 0;
+    for (int i = 0; i < 7; ++i) { c->sc_off[i] = off; off += sz[i]; }
+    c->sc_layer = off;
+    a = align256(a + L * off * 4);
+    c->a_sclm = a;
+    a = align256(a + nblk(V) * nblk(H) * 4);
+  } else {
+    c->sc_layer = 0;
+    c->a_sclm = a;
+  }
+  c->a_rope = a; a = align256(a + (int64_t)m.max_seq * (m.hd / 2) * 8);
+  c->sizes.arena_bytes = a;
+  c->sizes.kv_bytes = 2 * align256((int64_t)L * m.nkv * m.max_seq * m.hd * c->kves);
+
+  const Schedule& s = c->sched;
+  const int64_t NT = (int64_t)s.tasks.size();
+  int64_t w = 0;
+  c->w_ctrl = w; w = align256(w + CTRL_WORDS * 4);
+  c->w_call = w; w = align256(w + sizeof(CallParams));
+  c->w_flags = w; w = align256(w + (int64_t)s.n_flags * 4);
+  c->w_counters = w; w = align256(w + (int64_t)s.counters.size() * 4);
+  c->w_tickets = w; w = align256(w + L * m.nkv * 4);
+  c->w_keys = w; w = align256(w + ((int64_t)m.max_seq + 1) * 8);
+  c->w_kvscale = w; w = align256(w + L * m.nkv * 2 * 4);
+  c->w_x = w; w = align256(w + (L + 1) * H * 4);
+  c->w_xm = w; w = align256(w + L * H * 4);
+  c->w_q = w; w = align256(w + L * qd * 4);
+  c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 2) * 4);
+  c->w_o = w; w = align256(w + L * qd * 4);
+  c->w_h = w; w = align256(w + L * F * 4);
+  c->w_trace = w; w = align256(w + (int64_t)std::max(0, c->sc.trace_steps) * NT * 32);
+  c->w_tasks = w; w = align256(w + NT * (int64_t)sizeof(pmk_task));
+  c->w_qoff = w; w = align256(w + ((int64_t)s.n_queues + 1) * 4);
+  c->w_qtasks = w; w = align256(w + NT * 4);
+  c->w_cprod = w; w = align256(w + (int64_t)s.counters.size() * 4);
+  c->w_cflag = w; w = align256(w + (int64_t)s.counters.size() * 4);
+  c->sizes.workspace_bytes = w;
+
+  // LDS: staged activation vectors, or the attention scratch
+  const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
+  auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
+  const int64_t S = s.attn_splits, grp = m.grp();
+  const int64_t chunk = (m.max_seq + S - 1) / S;
+  const int64_t attn = grp * m.hd + grp * ((chunk + 3) & ~3ll) + kWaves * grp * m.hd;
+  const int64_t comb = 3 * S * grp;
+  const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn, comb});
+  c->xs_floats = (int)((xs + 63) / 64 * 64);
+  c->lds_bytes = (size_t)(c->xs_floats + 64) * 4;
+}
+
+void fill_params(pmk_ctx* c) {
+  KParams& P = c->kp;
+  const ModelDims& m = c->m;
+  P = KParams{};
+  P.L = m.L; P.H = m.H; P.nq = m.nq; P.nkv = m.nkv; P.hd = m.hd; P.F = m.F; P.V = m.V;
+  P.grp = m.grp(); P.qkv_rows = m.qkv_rows(); P.qdim = m.qdim(); P.max_seq = m.max_seq; P.S = c->sched.attn_splits;
+  P.wdt = m.wdt; P.kvdt = m.kvdt; P.eps = m.eps;
+  P.attn_scale = (float)(1.0 / std::sqrt((double)m.hd));
+  uint8_t* A = c->arena;
+  P.embed = reinterpret_cast<const uint16_t*>(A + c->a_embed);
+  P.gains = reinterpret_cast<const float*>(A + c->a_gains);
+  P.final_gain = reinterpret_cast<const float*>(A + c->a_final);
+  P.wbase = A + c->a_layers;
+  P.layer_bytes = c->layer_bytes;
+  P.off_qkv = c->off_qkv; P.off_o = c->off_o; P.off_gu = c->off_gu; P.off_d = c->off_d;
+  P.lm = A + c->a_lm;
+  P.scales = reinterpret_cast<const float*>(A + c->a_scales);
+  P.sc_layer = c->sc_layer;
+  for (int i = 0; i < 7; ++i) P.sc_off[i] = c->sc_off[i];
+  P.sc_lm = reinterpret_cast<const float*>(A + c->a_sclm);
+  P.rope = reinterpret_cast<const float2*>(A + c->a_rope);
+  P.kc = c->kv;
+  P.vc = c->kv + c->sizes.kv_bytes / 2;
+  uint8_t* W = c->ws;
+  P.ctrl = reinterpret_cast<uint32_t*>(W + c->w_ctrl);
+  P.call = reinterpret_cast<CallParams*>(W + c->w_call);
+  P.flags = reinterpret_cast<uint32_t*>(W + c->w_flags);
+  P.counters = reinterpret_cast<uint32_t*>(W + c->w_counters);
+  P.tickets = reinterpret_cast<uint32_t*>(W + c->w_tickets);
+  P.keys = reinterpret_cast<unsigned long long*>(W + c->w_keys);
+  P.kv_scale = reinterpret_cast<float*>(W + c->w_kvscale);
+  P.x = reinterpret_cast<float*>(W + c->w_x);
+  P.xm = reinterpret_cast<float*>(W + c->w_xm);
+  P.q = reinterpret_cast<float*>(W + c->w_q);
+  P.part = reinterpret_cast<float*>(W + c->w_part);
+  P.o = reinterpret_cast<float*>(W + c->w_o);
+  P.h = reinterpret_cast<float*>(W + c->w_h);
+  P.trace = reinterpret_cast<unsigned long long*>(W + c->w_trace);
+  P.tasks = reinterpret_cast<const pmk_task*>(W + c->w_tasks);
+  P.qoff = reinterpret_cast<const int32_t*>(W + c->w_qoff);
+  P.qtasks = reinterpret_cast<const int32_t*>(W + c->w_qtasks);
+  P.ctr_prod = reinterpret_cast<const int32_t*>(W + c->w_cprod);
+  P.ctr_flag = reinterpret_cast<const int32_t*>(W + c->w_cflag);
+  P.n_queues = c->sched.n_queues;
+  P.n_tasks = (int)c->sched.tasks.size();
+  P.sync_mode = c->sched.sync_mode;
+  P.prefetch = c->sc.prefetch;
+  P.trace_steps = std::max(0, c->sc.trace_steps);
+  P.spin_limit = c->sc.spin_limit;
+  P.xs_floats = c->xs_floats;
+}
+
+void compute_phases(pmk_ctx* c) {
+  c->phases.clear();
+  const auto& T = c->sched.tasks;
+  for (int i = 0; i < (int)T.size();) {
+    int j = i;
+    while (j < (int)T.size() && T[j].op == T[i].op && T[j].layer == T[i].layer) ++j;
+    c->phases.push_back({i, j - i});
+    i = j;
+  }
+}
+
+pmk_status need_device(pmk_ctx* c) {
+  if (!c) return PMK_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
+  if (!c->bound) return fail(c, PMK_ERR_NOT_BOUND, "buffers are not bound (pmk_bind)");
+  HIPCHK(c, hipSetDevice(c->device));
+  return PMK_OK;
+}
+
+pmk_status launch_persistent(pmk_ctx* c, hipStream_t st) {
+  const void* fn = persistent_kernel(c->m.wdt, c->m.kvdt);
+  void* args[] = {&c->kp};
+  HIPCHK(c, hipLaunchCooperativeKernel(fn, dim3(c->n_cus), dim3(kThreads), args, (unsigned)c->lds_bytes, st));
+  return PMK_OK;
+}
+
+pmk_status launch_step_per_op(pmk_ctx* c, hipStream_t st) {
+  const void* fn = phase_kernel(c->m.wdt, c->m.kvdt);
+  for (const Phase& ph : c->phases) {
+    int first = ph.first;
+    void* args[] = {&c->kp, &first};
+    HIPCHK(c, hipLaunchKernel(fn, dim3(ph.count), dim3(kThreads), args, c->lds_bytes, st));
+  }
+  return PMK_OK;
+}
+
+pmk_status ensure_graph(pmk_ctx* c) {
+  if (c->graph_exec) return PMK_OK;
+  if (!c->cap_stream) HIPCHK(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+  HIPCHK(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+  pmk_status s = launch_step_per_op(c, c->cap_stream);
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
+  if (s != PMK_OK) return s;
+  if (e != hipSuccess) return fail(c, PMK_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  c->graph = g;
+  HIPCHK(c, hipGraphInstantiate(&c->graph_exec, g, nullptr, nullptr, 0));
+  return PMK_OK;
+}
+
+// Run `n` steps of the current call (begin_call already issued) in the context's mode.
+pmk_status run_steps(pmk_ctx* c, int n, hipStream_t st) {
+  if (c->mode == PMK_MODE_MEGAKERNEL) return launch_persistent(c, st);
+  if (c->mode == PMK_MODE_GRAPH) {
+    pmk_status s = ensure_graph(c);
+    if (s != PMK_OK) return s;
+    for (int i = 0; i < n; ++i) HIPCHK(c, hipGraphLaunch(c->graph_exec, st));
+    return PMK_OK;
+  }
+  for (int i = 0; i < n; ++i) {
+    pmk_status s = launch_step_per_op(c, st);
+    if (s != PMK_OK) return s;
+  }
+  return PMK_OK;
+}
+
+pmk_status begin_call(pmk_ctx* c, const CallParams& cp, hipStream_t st) {
+  HIPCHK(c, launch_begin_call(c->kp, cp, st));
+  return PMK_OK;
+}
+
+pmk_status set_kv_scales(pmk_ctx* c, const float* d_kv_scales, hipStream_t st) {
+  const size_t bytes = (size_t)c->m.L * c->m.nkv * 2 * 4;
+  if (c->m.kvdt == PMK_DT_FP8_E4M3) {
+    if (!d_kv_scales) return fail(c, PMK_ERR_INVALID_ARG, "an fp8 KV cache needs d_kv_scales [n_layers][n_kv][2]");
+    HIPCHK(c, hipMemcpyAsync(c->ws + c->w_kvscale, d_kv_scales, bytes, hipMemcpyDeviceToDevice, st));
+  }
+  return PMK_OK;
+}
+
+}  // namespace
+
+// =================================================================================================
+// C ABI
+// =================================================================================================
+extern "C" {
+
+int pmk_abi_version(void) { return PMK_ABI_VERSION; }
+
+const char* pmk_status_str(pmk_status s) {
+  switch (s) {
+    case PMK_OK: return "ok";
+    case PMK_ERR_INVALID_ARG: return "invalid argument";
+    case PMK_ERR_UNSUPPORTED: return "outside the operation contract";
+    case PMK_ERR_SCHEDULE_INVALID: return "schedule rejected by the static validator";
+    case PMK_ERR_CAPACITY: return "KV capacity exceeded";
+    case PMK_ERR_NOT_BOUND: return "not bound or not loaded";
+    case PMK_ERR_HIP: return "HIP runtime error";
+    case PMK_ERR_TIMEOUT: return "device wait timed out";
+    case PMK_ERR_NAN: return "NaN logits";
+    case PMK_ERR_DEVICE: return "unsupported device";
+  }
+  return "unknown status";
+}
+
+const char* pmk_last_error(const pmk_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+const char* pmk_last_global_error(void) { return g_err.c_str(); }
+
+pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sched, int hip_device, pmk_ctx** out) {
+  g_err.clear();
+  if (!cfg || !out) return fail(nullptr, PMK_ERR_INVALID_ARG, "cfg and out must not be NULL");
+  *out = nullptr;
+  const std::string why = contract_check(*cfg);
+  if (!why.empty()) return fail(nullptr, PMK_ERR_UNSUPPORTED, why);
+  pmk_ctx* c = new pmk_ctx();
+  c->cfg = *cfg;
+  c->sc = defaults(sched);
+  c->m = dims_of(*cfg);
+  c->wes = cfg->weight_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
+  c->kves = cfg->kv_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
+  c->device = hip_device;
+  int n_cus = c->sc.n_cus;
+  if (hip_device >= 0) {
+    hipDeviceProp_t p;
+    hipError_t e = hipGetDeviceProperties(&p, hip_device);
+    if (e != hipSuccess) { delete c; return fail(nullptr, PMK_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e)); }
+    if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) {
+      delete c;
+      return fail(nullptr, PMK_ERR_DEVICE, std::string("device is ") + p.gcnArchName + ", the kernels are built for gfx950");
+    }
+    if (!p.cooperativeLaunch) { delete c; return fail(nullptr, PMK_ERR_DEVICE, "device lacks cooperative launch"); }
+    if (n_cus <= 0 || n_cus > p.multiProcessorCount) n_cus = p.multiProcessorCount;
+  } else if (n_cus <= 0) {
+    n_cus = 256;
+  }
+  c->n_cus = n_cus;
+  std::string e = build_schedule(c->m, c->sc, n_cus, &c->sched);
+  if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
+  e = validate_schedule(c->sched);
+  if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
+  c->tabs = flatten(c->sched);
+  c->hash = schedule_hash(c->sched);
+  compute_layout(c);
+  if (c->lds_bytes > 160 * 1024) {
+    delete c;
+    return fail(nullptr, PMK_ERR_UNSUPPORTED, "the staged activations and attention scratch exceed 160 KiB of LDS");
+  }
+  compute_phases(c);
+  if (hip_device >= 0) {
+    hipError_t he = hipSetDevice(hip_device);
+    const void* fns[2] = {persistent_kernel(c->m.wdt, c->m.kvdt), phase_kernel(c->m.wdt, c->m.kvdt)};
+    for (const void* fn : fns) {
+      if (he == hipSuccess) he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->lds_bytes);
+    }
+    int per_cu = 0;
+    if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[0], kThreads, c->lds_bytes);
+    if (he != hipSuccess) { delete c; return fail(nullptr, PMK_ERR_HIP, std::string("kernel setup: ") + hipGetErrorString(he)); }
+    if (per_cu < 1) { delete c; return fail(nullptr, PMK_ERR_DEVICE, "the persistent kernel cannot be resident on a CU"); }
+  }
+  *out = c;
+  return PMK_OK;
+}
+
+void pmk_destroy(pmk_ctx* c) {
+  if (!c) return;
+  if (c->device >= 0) (void)hipSetDevice(c->device);
+  if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  delete c;
+}
+
+pmk_status pmk_buffer_sizes(const pmk_ctx* c, pmk_sizes* out) {
+  if (!c || !out) return PMK_ERR_INVALID_ARG;
+  *out = c->sizes;
+  return PMK_OK;
+}
+
+pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
+  if (!c) return PMK_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
+  if (!d_arena || !d_kv || !d_ws) return fail(c, PMK_ERR_INVALID_ARG, "buffers must not be NULL");
+  if (((uintptr_t)d_arena | (uintptr_t)d_kv | (uintptr_t)d_ws) & 255)
+    return fail(c, PMK_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
+  HIPCHK(c, hipSetDevice(c->device));
+  c->arena = (uint8_t*)d_arena;
+  c->kv = (uint8_t*)d_kv;
+  c->ws = (uint8_t*)d_ws;
+  fill_params(c);
+  // schedule tables and a clean synchronisation state
+  HIPCHK(c, hipMemcpy(c->ws + c->w_tasks, c->tabs.tasks.data(), c->tabs.tasks.size() * sizeof(pmk_task), hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_qoff, c->tabs.qoff.data(), c->tabs.qoff.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_qtasks, c->tabs.qtasks.data(), c->tabs.qtasks.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_cprod, c->tabs.ctr_producers.data(), c->tabs.ctr_producers.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_cflag, c->tabs.ctr_flag_base.data(), c->tabs.ctr_flag_base.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemset(c->ws + c->w_kvscale, 0, (size_t)c->m.L * c->m.nkv * 2 * 4));
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), 0, 0, nullptr, nullptr));
+  HIPCHK(c, hipDeviceSynchronize());
+  if (c->graph_exec) { (void)hipGraphExecDestroy(c->graph_exec); c->graph_exec = nullptr; }
+  if (c->graph) { (void)hipGraphDestroy(c->graph); c->graph = nullptr; }
+  c->bound = true;
+  c->weights = false;
+  c->kv_ready = false;
+  c->pos_host = 0;
+  return PMK_OK;
+}
+
+pmk_status pmk_load_weights(pmk_ctx* c, const pmk_weight_ptrs* w, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const ModelDims& m = c->m;
+  const bool fp8 = m.wdt == PMK_DT_FP8_E4M3;
+  if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->layers) return fail(c, PMK_ERR_INVALID_ARG, "missing weight pointers");
+  if (fp8 && (!w->lm_head_scale || !w->layer_scales)) return fail(c, PMK_ERR_INVALID_ARG, "fp8 weights need block scales");
+  const int64_t H = m.H, F = m.F, V = m.V, qd = m.qdim(), kvd = (int64_t)m.nkv * m.hd, wes = c->wes;
+  const int gbf16 = (fp8 || m.wdt == PMK_DT_BF16) ? 1 : 0;
+  for (int l = 0; l < m.L; ++l)
+    for (int k = 0; k < 9; ++k)
+      if (!w->layers[l * 9 + k]) return fail(c, PMK_ERR_INVALID_ARG, "missing layer weight pointer");
+  HIPCHK(c, hipMemcpyAsync(c->arena + c->a_embed, w->embed, V * H * 2, hipMemcpyDeviceToDevice, st));
+  HIPCHK(c, hipMemcpyAsync(c->arena + c->a_lm, w->lm_head, V * H * wes, hipMemcpyDeviceToDevice, st));
+  for (int l = 0; l < m.L; ++l) {
+    const void* const* L9 = w->layers + l * 9;
+    uint8_t* base = c->arena + c->a_layers + l * c->layer_bytes;
+    HIPCHK(c, launch_repack_qkv(base + c->off_qkv, L9[0], L9[1], L9[2], m.nq, m.nkv, m.hd, H * wes, st));
+    HIPCHK(c, hipMemcpyAsync(base + c->off_o, L9[3], H * qd * wes, hipMemcpyDeviceToDevice, st));
+    HIPCHK(c, launch_repack_gu(base + c->off_gu, L9[4], L9[5], m.F, H * wes, st));
+    HIPCHK(c, hipMemcpyAsync(base + c->off_d, L9[6], H * F * wes, hipMemcpyDeviceToDevice, st));
+    float* g = reinterpret_cast<float*>(c->arena + c->a_gains) + (int64_t)l * 2 * H;
+    HIPCHK(c, launch_widen(g, L9[7], (int)H, gbf16, st));
+    HIPCHK(c, launch_widen(g + H, L9[8], (int)H, gbf16, st));
+    if (fp8) {
+      const float* const* S7 = w->layer_scales + l * 7;
+      const int64_t sz[7] = {nblk(qd) * nblk(H), nblk(kvd) * nblk(H), nblk(kvd) * nblk(H), nblk(H) * nblk(qd),
+                             nblk(F) * nblk(H),  nblk(F) * nblk(H),   nblk(H) * nblk(F)};
+      float* sb = reinterpret_cast<float*>(c->arena + c->a_scales) + l * c->sc_layer;
+      for (int k = 0; k < 7; ++k) {
+        if (!S7[k]) return fail(c, PMK_ERR_INVALID_ARG, "missing block-scale pointer");
+        HIPCHK(c, hipMemcpyAsync(sb + c->sc_off[k], S7[k], sz[k] * 4, hipMemcpyDeviceToDevice, st));
+      }
+    }
+  }
+  HIPCHK(c, launch_widen(reinterpret_cast<float*>(c->arena + c->a_final), w->final_norm, (int)H, gbf16, st));
+  if (fp8)
+    HIPCHK(c, hipMemcpyAsync(c->arena + c->a_sclm, w->lm_head_scale, nblk(V) * nblk(H) * 4, hipMemcpyDeviceToDevice, st));
+  // RoPE table: angle p * theta^(-2i/hd) in double, cos and sin rounded to fp32
+  const int half = m.hd / 2;
+  c->rope_host.resize((size_t)m.max_seq * half * 2);
+  for (int p = 0; p < m.max_seq; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)m.theta, -2.0 * i / (double)m.hd);
+      c->rope_host[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+      c->rope_host[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  HIPCHK(c, hipMemcpyAsync(c->arena + c->a_rope, c->rope_host.data(), c->rope_host.size() * 4, hipMemcpyHostToDevice, st));
+  c->weights = true;
+  return PMK_OK;
+}
+
+pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const float* d_kv_scales, int32_t* d_first_token,
+                          void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!c->weights) return fail(c, PMK_ERR_NOT_BOUND, "weights are not loaded");
+  if (!d_tokens || P <= 0) return fail(c, PMK_ERR_INVALID_ARG, "prefill needs P > 0 device tokens");
+  if (P > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "prompt longer than max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  s = set_kv_scales(c, d_kv_scales, st);
+  if (s != PMK_OK) return s;
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), 0, 0, nullptr, st));
+  const int chunk = 256;
+  for (int off = 0; off < P; off += chunk) {
+    const int n = std::min(chunk, P - off);
+    CallParams cp{};
+    cp.forced = d_tokens + off;
+    cp.n_steps = n;
+    cp.eos = -1;
+    s = begin_call(c, cp, st);
+    if (s != PMK_OK) return s;
+    s = run_steps(c, n, st);
+    if (s != PMK_OK) return s;
+  }
+  if (d_first_token) HIPCHK(c, launch_copy_token(c->kp, d_first_token, st));
+  c->pos_host = P;
+  c->kv_ready = true;
+  return PMK_OK;
+}
+
+pmk_status pmk_load_kv(pmk_ctx* c, const void* d_k, const void* d_v, int32_t P, int32_t next_token, const float* d_kv_scales,
+                       void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (P < 0 || P > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "P exceeds max_seq");
+  if (P > 0 && (!d_k || !d_v)) return fail(c, PMK_ERR_INVALID_ARG, "missing KV pointers");
+  if (next_token < 0 || next_token >= c->m.V) return fail(c, PMK_ERR_INVALID_ARG, "next_token out of range");
+  hipStream_t st = (hipStream_t)stream;
+  s = set_kv_scales(c, d_kv_scales, st);
+  if (s != PMK_OK) return s;
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P, next_token, nullptr, st));
+  if (P > 0) HIPCHK(c, launch_load_kv_rows(c->kp, d_k, d_v, P, c->kves, st));
+  c->pos_host = P;
+  c->kv_ready = true;
+  return PMK_OK;
+}
+
+pmk_status pmk_rewind(pmk_ctx* c, int32_t pos, const int32_t* d_token, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "no KV state to rewind");
+  if (pos <= 0 || pos > c->pos_host || !d_token) return fail(c, PMK_ERR_INVALID_ARG, "rewind needs 0 < pos <= position and a token");
+  HIPCHK(c, launch_set_pos(c->kp, pos, d_token, (hipStream_t)stream));
+  c->pos_host = pos;
+  return PMK_OK;
+}
+
+pmk_status pmk_decode_n_tokens(pmk_ctx* c, int32_t n, int32_t* d_out_tokens, float* d_out_logits, int32_t eos_id,
+                               int32_t* d_n_done, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
+  if (n <= 0 || !d_out_tokens) return fail(c, PMK_ERR_INVALID_ARG, "n > 0 and d_out_tokens are required");
+  if ((int64_t)c->pos_host + n > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + n exceeds max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  CallParams cp{};
+  cp.out_tokens = d_out_tokens;
+  cp.out_logits = d_out_logits;
+  cp.n_done = d_n_done;
+  cp.forced = nullptr;
+  cp.n_steps = n;
+  cp.eos = eos_id;
+  cp.trace = c->trace_on;
+  s = begin_call(c, cp, st);
+  if (s != PMK_OK) return s;
+  s = run_steps(c, n, st);
+  if (s != PMK_OK) return s;
+  c->pos_host += n;
+  return PMK_OK;
+}
+
+pmk_status pmk_set_mode(pmk_ctx* c, int32_t mode) {
+  if (!c || mode < PMK_MODE_MEGAKERNEL || mode > PMK_MODE_PER_OP) return PMK_ERR_INVALID_ARG;
+  c->mode = mode;
+  return PMK_OK;
+}
+
+pmk_status pmk_get_position(const pmk_ctx* c, int32_t* pos) {
+  if (!c || !pos) return PMK_ERR_INVALID_ARG;
+  *pos = c->pos_host;
+  return PMK_OK;
+}
+
+pmk_status pmk_poll_error(pmk_ctx* c, pmk_device_error* err) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  uint32_t w[6];
+  HIPCHK(c, hipMemcpy(w, c->ws + c->w_ctrl + CTRL_ERR * 4, sizeof w, hipMemcpyDeviceToHost));
+  if (err) {
+    err->code = (int32_t)w[0];
+    err->cu = (int32_t)w[1];
+    err->task = (int32_t)w[2];
+    err->counter = (int32_t)w[3];
+    err->expected = w[4];
+    err->seen = w[5];
+  }
+  return (pmk_status)w[0];
+}
+
+pmk_status pmk_set_trace(pmk_ctx* c, int32_t on) {
+  if (!c) return PMK_ERR_INVALID_ARG;
+  if (on && c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "the schedule has no trace buffer (trace_steps = 0)");
+  c->trace_on = on ? 1 : 0;
+  return PMK_OK;
+}
+
+static pmk_status read_trace(pmk_ctx* c, std::vector<unsigned long long>& t) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "no trace buffer");
+  HIPCHK(c, hipDeviceSynchronize());
+  t.resize((size_t)c->sc.trace_steps * c->sched.tasks.size() * 4);
+  HIPCHK(c, hipMemcpy(t.data(), c->ws + c->w_trace, t.size() * 8, hipMemcpyDeviceToHost));
+  return PMK_OK;
+}
+
+pmk_status pmk_trace_stats(pmk_ctx* c, double* wait_share, double* step_us) {
+  std::vector<unsigned long long> t;
+  pmk_status s = read_trace(c, t);
+  if (s != PMK_OK) return s;
+  const size_t NT = c->sched.tasks.size();
+  double wait = 0, wall = 0, steps_us = 0;
+  int nsteps = 0;
+  for (int st = 0; st < c->sc.trace_steps; ++st) {
+    unsigned long long lo = ~0ull, hi = 0;
+    bool any = false;
+    for (size_t i = 0; i < NT; ++i) {
+      const unsigned long long* r = &t[((size_t)st * NT + i) * 4];
+      if (!r[0] || !r[2] || r[2] < r[0]) continue;
+      any = true;
+      const unsigned long long t1 = (r[1] >= r[0] && r[1] <= r[2]) ? r[1] : r[0];
+      wait += (double)(t1 - r[0]);
+      wall += (double)(r[2] - r[0]);
+      lo = std::min(lo, r[0]);
+      hi = std::max(hi, r[2]);
+    }
+    if (any) { steps_us += (hi - lo) * 0.01; ++nsteps; }
+  }
+  if (wait_share) *wait_share = wall > 0 ? wait / wall : 0.0;
+  if (step_us) *step_us = nsteps ? steps_us / nsteps : 0.0;
+  return PMK_OK;
+}
+
+pmk_status pmk_trace_export(pmk_ctx* c, const char* path) {
+  if (!path) return PMK_ERR_INVALID_ARG;
+  std::vector<unsigned long long> t;
+  pmk_status s = read_trace(c, t);
+  if (s != PMK_OK) return s;
+  FILE* f = std::fopen(path, "w");
+  if (!f) return fail(c, PMK_ERR_INVALID_ARG, std::string("cannot open ") + path);
+  static const char* names[] = {"?", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "token"};
+  const size_t NT = c->sched.tasks.size();
+  unsigned long long t0 = ~0ull;
+  for (size_t i = 0; i < t.size(); i += 4)
+    if (t[i]) t0 = std::min(t0, t[i]);
+  std::fprintf(f, "{\"traceEvents\":[\n");
+  bool first = true;
+  for (int st = 0; st < c->sc.trace_steps; ++st)
+    for (size_t i = 0; i < NT; ++i) {
+      const unsigned long long* r = &t[((size_t)st * NT + i) * 4];
+      if (!r[0] || !r[2]) continue;
+      const pmk_task& k = c->sched.tasks[i];
+      const unsigned long long t1 = (r[1] >= r[0] && r[1] <= r[2]) ? r[1] : r[0];
+      std::fprintf(f, "%s{\"name\":\"wait\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}", first ? "" : ",\n",
+                   st, r[3], (r[0] - t0) * 0.01, (t1 - r[0]) * 0.01);
+      std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}",
+                   names[k.op >= 1 && k.op <= 7 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01);
+      first = false;
+    }
+  std::fprintf(f, "\n]}\n");
+  std::fclose(f);
+  return PMK_OK;
+}
+
+pmk_status pmk_schedule_get_info(const pmk_ctx* c, pmk_schedule_info* info) {
+  if (!c || !info) return PMK_ERR_INVALID_ARG;
+  info->n_tasks = (int32_t)c->sched.tasks.size();
+  info->n_counters = (int32_t)c->sched.counters.size();
+  info->n_cus = c->sched.n_queues;
+  info->attn_splits = c->sched.attn_splits;
+  int mx = 0;
+  for (auto& q : c->sched.queues) mx = std::max(mx, (int)q.size());
+  info->max_tasks_per_cu = mx;
+  info->sync_mode = c->sched.sync_mode;
+  info->hash = c->hash;
+  return PMK_OK;
+}
+
+// ---- schedule IR API ----
+pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus, pmk_schedule** out) {
+  g_err.clear();
+  if (!cfg || !out || n_cus <= 0) return fail(nullptr, PMK_ERR_INVALID_ARG, "bad arguments");
+  *out = nullptr;
+  const std::string why = contract_check(*cfg);
+  if (!why.empty()) return fail(nullptr, PMK_ERR_UNSUPPORTED, why);
+  pmk_schedule* s = new pmk_schedule();
+  const pmk_schedule_config sc = defaults(sched);
+  const std::string e = build_schedule(dims_of(*cfg), sc, n_cus, &s->s);
+  if (!e.empty()) { delete s; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
+  *out = s;
+  return PMK_OK;
+}
+
+void pmk_schedule_free(pmk_schedule* s) { delete s; }
+int32_t pmk_schedule_num_tasks(const pmk_schedule* s) { return s ? (int32_t)s->s.tasks.size() : 0; }
+int32_t pmk_schedule_num_counters(const pmk_schedule* s) { return s ? (int32_t)s->s.counters.size() : 0; }
+int32_t pmk_schedule_num_queues(const pmk_schedule* s) { return s ? s->s.n_queues : 0; }
+
+pmk_status pmk_schedule_get_task(const pmk_schedule* s, int32_t i, pmk_task* t) {
+  if (!s || !t || i < 0 || i >= (int32_t)s->s.tasks.size()) return PMK_ERR_INVALID_ARG;
+  *t = s->s.tasks[i];
+  return PMK_OK;
+}
+
+pmk_status pmk_schedule_set_task(pmk_schedule* s, int32_t i, const pmk_task* t) {
+  if (!s || !t || i < 0 || i >= (int32_t)s->s.tasks.size()) return PMK_ERR_INVALID_ARG;
+  s->s.tasks[i] = *t;
+  return PMK_OK;
+}
+
+const int32_t* pmk_schedule_queue(const pmk_schedule* s, int32_t q, int32_t* len) {
+  if (!s || q < 0 || q >= s->s.n_queues) { if (len) *len = 0; return nullptr; }
+  if (len) *len = (int32_t)s->s.queues[q].size();
+  return s->s.queues[q].data();
+}
+
+pmk_status pmk_schedule_set_queue(pmk_schedule* s, int32_t q, const int32_t* tasks, int32_t len) {
+  if (!s || q < 0 || q >= s->s.n_queues || len < 0 || (len && !tasks)) return PMK_ERR_INVALID_ARG;
+  s->s.queues[q].assign(tasks, tasks + len);
+  return PMK_OK;
+}
+
+int32_t pmk_schedule_counter_producers(const pmk_schedule* s, int32_t c) {
+  if (!s || c < 0 || c >= (int32_t)s->s.counters.size()) return -1;
+  return s->s.counters[c].producers;
+}
+
+pmk_status pmk_schedule_set_counter_producers(pmk_schedule* s, int32_t c, int32_t producers) {
+  if (!s || c < 0 || c >= (int32_t)s->s.counters.size()) return PMK_ERR_INVALID_ARG;
+  s->s.counters[c].producers = producers;
+  return PMK_OK;
+}
+
+pmk_status pmk_schedule_validate(const pmk_schedule* s, char* report, size_t cap) {
+  if (!s) return PMK_ERR_INVALID_ARG;
+  const std::string e = validate_schedule(s->s);
+  if (report && cap) {
+    std::strncpy(report, e.c_str(), cap - 1);
+    report[cap - 1] = 0;
+  }
+  return e.empty() ? PMK_OK : PMK_ERR_SCHEDULE_INVALID;
+}
+
+pmk_status pmk_schedule_simulate(const pmk_schedule* s, int32_t steps, uint64_t seed, char* report, size_t cap) {
+  if (!s || steps <= 0) return PMK_ERR_INVALID_ARG;
+  std::string r;
+  const pmk_status st = simulate_schedule(s->s, steps, seed, &r);
+  if (report && cap) {
+    std::strncpy(report, r.c_str(), cap - 1);
+    report[cap - 1] = 0;
+  }
+  return st;
+}
+
+uint64_t pmk_schedule_hash(const pmk_schedule* s) { return s ? schedule_hash(s->s) : 0; }
+
+}  // extern "C"

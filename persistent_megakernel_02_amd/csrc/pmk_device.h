@@ -1,0 +1,85 @@
+// Parameters shared by the host runtime and the gfx950 kernels.
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/pmk.h"
+
+namespace pmk {
+
+constexpr int kThreads = 512;   // one workgroup per CU: 8 wave64s (2 per SIMD)
+constexpr int kWaves = kThreads / 64;
+
+// control words (workspace, uint32) -------------------------------------------------------------
+enum Ctrl : int {
+  CTRL_EPOCH = 0,    // global decode steps since the last reset (counters / flags are relative to it)
+  CTRL_POS = 1,      // next position to write
+  CTRL_TOKEN = 2,    // next input token
+  CTRL_STEP = 3,     // per-op modes: step index within the current call
+  CTRL_STOPPED = 4,  // per-op modes: eos seen in this call
+  CTRL_ABORT = 5,    // watchdog: a wait gave up; every wait exits
+  CTRL_ERR = 8,      // pmk_device_error: code, cu, task, counter, expected, seen (6 words)
+  CTRL_WORDS = 64
+};
+
+// per-call parameters kept in device memory so a captured graph can read them
+struct CallParams {
+  int32_t* out_tokens;
+  float* out_logits;
+  int32_t* n_done;
+  const int32_t* forced;  // teacher-forced input tokens (prefill), or null
+  int32_t n_steps;
+  int32_t eos;
+  int32_t trace;
+  int32_t pad;
+};
+
+struct KParams {
+  // model
+  int L, H, nq, nkv, hd, F, V, grp, qkv_rows, qdim, max_seq, S;
+  int wdt, kvdt;
+  float eps;
+  float attn_scale;  // 1/sqrt(hd)
+  // arena
+  const uint16_t* embed;  // [V][H] 16-bit
+  const float* gains;     // [L][2][H]
+  const float* final_gain;
+  const uint8_t* wbase;   // layer l block at wbase + l*layer_bytes
+  int64_t layer_bytes;
+  int64_t off_qkv, off_o, off_gu, off_d;
+  const uint8_t* lm;      // [V][H]
+  const float* scales;    // fp8: per layer [q k v o g u d] block-scale arrays, then the LM head's
+  int64_t sc_layer;       // floats per layer
+  int64_t sc_off[7];      // offsets (floats) of the 7 arrays inside a layer
+  const float* sc_lm;
+  const float2* rope;     // [max_seq][hd/2] (cos, sin)
+  // kv cache [L][nkv][max_seq][hd]
+  uint8_t* kc;
+  uint8_t* vc;
+  // workspace
+  uint32_t* ctrl;
+  CallParams* call;
+  uint32_t* flags;
+  uint32_t* counters;
+  uint32_t* tickets;      // [L][nkv]
+  unsigned long long* keys;  // [max_seq + 1]
+  float* kv_scale;        // [L][nkv][2]
+  float* x;               // [L+1][H]
+  float* xm;              // [L][H]
+  float* q;               // [L][qdim]
+  float* part;            // [L][nkv][S][grp][hd+2]
+  float* o;               // [L][qdim]
+  float* h;               // [L][F]
+  unsigned long long* trace;  // [trace_steps][n_tasks][4]
+  // schedule tables
+  const pmk_task* tasks;
+  const int32_t* qoff;
+  const int32_t* qtasks;
+  const int32_t* ctr_prod;
+  const int32_t* ctr_flag;
+  int n_queues, n_tasks, sync_mode, prefetch, trace_steps;
+  int64_t spin_limit;
+  int xs_floats;          // LDS floats reserved for staged activation vectors
+};
+
+}  // namespace pmk

@@ -1,0 +1,723 @@
+// Schedule builder, static validator and CPU simulator for the persistent decode kernel.
+//
+// Pages: "AutoMegaKernel" explainer — Method, Layer 2 (the model is lowered into a typed task
+// DAG synchronised by monotonic counters, shaped by a ScheduleConfig: tiling, CU allocation,
+// pipelining) and the Safety Gate (a schedule is rejected before launch unless the
+// producer/consumer DAG is acyclic, every wait threshold t satisfies 1 <= t <= #producers,
+// per-queue order is valid, multi-producer counters are joined, memory accesses respect
+// happens-before, outputs are reachable and references are intact).  "Kog AI MI300X
+// monokernel tutorial": work is split over a fixed grid of CUs ahead of time.
+#include "schedule.h"
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <random>
+#include <set>
+#include <sstream>
+#include <thread>
+
+namespace pmk {
+
+namespace {
+
+std::string fmt(const char* f, long a = 0, long b = 0, long c = 0, long d = 0, long e = 0) {
+  char buf[512];
+  snprintf(buf, sizeof buf, f, a, b, c, d, e);
+  return buf;
+}
+
+const char* op_name(int op) {
+  switch (op) {
+    case PMK_OP_QKV: return "QKV";
+    case PMK_OP_ATTN: return "ATTN";
+    case PMK_OP_OPROJ: return "OPROJ";
+    case PMK_OP_GATEUP: return "GATEUP";
+    case PMK_OP_DOWN: return "DOWN";
+    case PMK_OP_LMHEAD: return "LMHEAD";
+    case PMK_OP_TOKEN: return "TOKEN";
+  }
+  return "?";
+}
+
+// Split `n` units into `parts` contiguous ranges; range i = [lo, hi).
+void split_range(int n, int parts, int i, int* lo, int* hi) {
+  *lo = (int)((int64_t)n * i / parts);
+  *hi = (int)((int64_t)n * (i + 1) / parts);
+}
+
+}  // namespace
+
+// ================================================================================================
+// Builder
+// ================================================================================================
+std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out) {
+  if (n_queues <= 0) return "builder: no queues";
+  Schedule s;
+  s.m = m;
+  s.n_queues = n_queues;
+  s.sync_mode = sc.sync_mode == PMK_SYNC_COUNTERS ? PMK_SYNC_COUNTERS : PMK_SYNC_FLAGS;
+  int S = sc.attn_splits;
+  if (S <= 0) {
+    S = std::max(1, n_queues / m.nkv);
+    S = std::min(S, std::max(1, m.max_seq / 16));
+  }
+  s.attn_splits = S;
+  s.queues.assign(n_queues, {});
+
+  auto add_counter = [&](int producers, int phase, int layer) {
+    Counter c{producers, s.n_flags, phase, layer};
+    s.n_flags += producers;
+    s.counters.push_back(c);
+    return (int)s.counters.size() - 1;
+  };
+  const int L = m.L;
+  const int n_qkv = std::min(n_queues, m.qkv_rows() / 2);
+  const int n_attn = m.nkv * S;
+  const int n_o = std::min(n_queues, m.H);
+  const int n_gu = std::min(n_queues, m.F);
+  const int n_down = std::min(n_queues, m.H);
+  const int n_lm = std::min(n_queues, m.V);
+  for (int l = 0; l < L; ++l) {
+    s.c_qkv.push_back(add_counter(n_qkv, PMK_OP_QKV, l));
+    s.c_cmb.push_back(add_counter(m.nkv, PMK_OP_ATTN, l));
+    s.c_oproj.push_back(add_counter(n_o, PMK_OP_OPROJ, l));
+    s.c_gu.push_back(add_counter(n_gu, PMK_OP_GATEUP, l));
+    s.c_down.push_back(add_counter(n_down, PMK_OP_DOWN, l));
+  }
+  s.c_lm = add_counter(n_lm, PMK_OP_LMHEAD, -1);
+
+  auto push = [&](int q, pmk_task t) {
+    s.tasks.push_back(t);
+    s.queues[q].push_back((int32_t)s.tasks.size() - 1);
+  };
+  for (int l = 0; l < L; ++l) {
+    // QKV: packed rows in pairs (each RoPE pair adjacent)
+    for (int i = 0; i < n_qkv; ++i) {
+      int lo, hi;
+      split_range(m.qkv_rows() / 2, n_qkv, i, &lo, &hi);
+      pmk_task t{PMK_OP_QKV, l, 2 * lo, 2 * hi, -1, 0, 0, s.c_qkv[l], i};
+      if (l == 0) { t.wait_ctr = s.c_lm; t.wait_count = n_lm; t.wait_lag = 1; }
+      else { t.wait_ctr = s.c_down[l - 1]; t.wait_count = n_down; t.wait_lag = 0; }
+      push(i % n_queues, t);
+    }
+    // ATTN: kv head g, split j; the last arriver of each head combines and signals c_cmb[l]
+    for (int i = 0; i < n_attn; ++i) {
+      const int g = i / S, j = i % S;
+      pmk_task t{PMK_OP_ATTN, l, g, j, s.c_qkv[l], n_qkv, 0, s.c_cmb[l], g};
+      push(i % n_queues, t);
+    }
+    for (int i = 0; i < n_o; ++i) {
+      int lo, hi;
+      split_range(m.H, n_o, i, &lo, &hi);
+      push(i % n_queues, pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv, 0, s.c_oproj[l], i});
+    }
+    for (int i = 0; i < n_gu; ++i) {
+      int lo, hi;
+      split_range(m.F, n_gu, i, &lo, &hi);
+      push(i % n_queues, pmk_task{PMK_OP_GATEUP, l, 2 * lo, 2 * hi, s.c_oproj[l], n_o, 0, s.c_gu[l], i});
+    }
+    for (int i = 0; i < n_down; ++i) {
+      int lo, hi;
+      split_range(m.H, n_down, i, &lo, &hi);
+      push(i % n_queues, pmk_task{PMK_OP_DOWN, l, lo, hi, s.c_gu[l], n_gu, 0, s.c_down[l], i});
+    }
+  }
+  for (int i = 0; i < n_lm; ++i) {
+    int lo, hi;
+    split_range(m.V, n_lm, i, &lo, &hi);
+    push(i % n_queues, pmk_task{PMK_OP_LMHEAD, -1, lo, hi, s.c_down[L - 1], n_down, 0, s.c_lm, i});
+  }
+  push(0, pmk_task{PMK_OP_TOKEN, -1, 0, 0, s.c_lm, n_lm, 0, -1, 0});
+  *out = std::move(s);
+  return "";
+}
+
+// ================================================================================================
+// Access model: what each task reads and writes (shared by the validator and the simulator)
+// ================================================================================================
+namespace {
+
+enum Buf { B_X = 0, B_XM, B_Q, B_KVCUR, B_PART, B_O, B_H, B_KEY, B_TOKSLOT, B_LOGITS, B_OUT, B_COUNT };
+enum Kind { A_READ = 0, A_WRITE = 1, A_ATOMIC = 2 };
+
+struct Access {
+  int buf;
+  int64_t lo, hi;  // element range in the buffer (regions are laid out in one index space per buffer)
+  int kind;
+  int expect;      // stamp a correct read observes (global step of the write + 1; 0 = initial contents)
+};
+
+struct BufDims {
+  int64_t size[B_COUNT];
+};
+
+BufDims buf_dims(const Schedule& s, int steps) {
+  const ModelDims& m = s.m;
+  BufDims d;
+  d.size[B_X] = (int64_t)(m.L + 1) * m.H;
+  d.size[B_XM] = (int64_t)m.L * m.H;
+  d.size[B_Q] = (int64_t)m.L * m.qdim();
+  d.size[B_KVCUR] = (int64_t)m.L * m.nkv * 2 * m.hd;
+  d.size[B_PART] = (int64_t)m.L * m.nkv * s.attn_splits;
+  d.size[B_O] = (int64_t)m.L * m.qdim();
+  d.size[B_H] = (int64_t)m.L * m.F;
+  d.size[B_KEY] = steps + 1;
+  d.size[B_TOKSLOT] = 1;
+  d.size[B_LOGITS] = (int64_t)(steps + 1) * m.V;
+  d.size[B_OUT] = steps + 1;
+  return d;
+}
+
+// Rows [a0, a1) of the packed QKV matrix -> element ranges written in Q (q heads) and KVCUR (k, v).
+// Packed row r in a section is head = r / hd, pair i = (r % hd) / 2, half = r % 2; it holds original
+// dimension i + half * hd/2.  A range of whole pairs [p0, p1) of one head covers dims [p0, p1) and
+// [p0 + hd/2, p1 + hd/2).
+void qkv_writes(const ModelDims& m, int l, int a0, int a1, int e, std::vector<Access>& acc) {
+  const int hd = m.hd, half = hd / 2, qrows = m.qdim(), krows = m.nkv * hd;
+  for (int r = a0; r < a1;) {
+    int sec, base;
+    if (r < qrows) { sec = 0; base = 0; }
+    else if (r < qrows + krows) { sec = 1; base = qrows; }
+    else { sec = 2; base = qrows + krows; }
+    const int head = (r - base) / hd;
+    const int head_end = base + (head + 1) * hd;
+    const int stop = std::min(a1, head_end);
+    const int p0 = ((r - base) % hd) / 2, p1 = ((stop - base - 1) % hd) / 2 + 1;
+    if (sec == 0) {
+      const int64_t off = (int64_t)l * m.qdim() + head * hd;
+      acc.push_back({B_Q, off + p0, off + p1, A_WRITE, 0});
+      acc.push_back({B_Q, off + half + p0, off + half + p1, A_WRITE, 0});
+    } else {
+      const int64_t off = ((int64_t)l * m.nkv + head) * 2 * hd + (sec == 2 ? hd : 0);
+      acc.push_back({B_KVCUR, off + p0, off + p1, A_WRITE, 0});
+      acc.push_back({B_KVCUR, off + half + p0, off + half + p1, A_WRITE, 0});
+    }
+    r = stop;
+  }
+  (void)e;
+}
+
+// Accesses of task t at global step e (e >= 0).  `combine` selects the last-arriver combine
+// of an ATTN task instead of the task's own partial.
+void task_accesses(const Schedule& s, const pmk_task& t, int e, bool combine, std::vector<Access>& acc) {
+  const ModelDims& m = s.m;
+  const int H = m.H, l = t.layer;
+  const int W1 = e + 1;  // stamp written at step e
+  auto token_read = [&]() {
+    if (e == 0) acc.push_back({B_TOKSLOT, 0, 1, A_READ, 0});
+    else acc.push_back({B_KEY, e - 1, e, A_READ, e});
+  };
+  switch (t.op) {
+    case PMK_OP_QKV: {
+      if (l == 0) token_read();
+      else acc.push_back({B_X, (int64_t)l * H, (int64_t)(l + 1) * H, A_READ, W1});
+      size_t first = acc.size();
+      qkv_writes(m, l, t.a0, t.a1, e, acc);
+      for (size_t i = first; i < acc.size(); ++i) acc[i].expect = W1;
+      break;
+    }
+    case PMK_OP_ATTN: {
+      const int g = t.a0, grp = m.grp();
+      const int64_t part = ((int64_t)l * m.nkv + g) * s.attn_splits;
+      if (!combine) {
+        acc.push_back({B_Q, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
+                       (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_READ, W1});
+        const int64_t kv = ((int64_t)l * m.nkv + g) * 2 * m.hd;
+        acc.push_back({B_KVCUR, kv, kv + 2 * m.hd, A_READ, W1});
+        acc.push_back({B_PART, part + t.a1, part + t.a1 + 1, A_WRITE, W1});
+      } else {
+        acc.push_back({B_PART, part, part + s.attn_splits, A_READ, W1});
+        acc.push_back({B_O, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
+                       (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_WRITE, W1});
+      }
+      break;
+    }
+    case PMK_OP_OPROJ:
+      acc.push_back({B_O, (int64_t)l * m.qdim(), (int64_t)(l + 1) * m.qdim(), A_READ, W1});
+      if (l == 0) token_read();
+      else acc.push_back({B_X, (int64_t)l * H + t.a0, (int64_t)l * H + t.a1, A_READ, W1});
+      acc.push_back({B_XM, (int64_t)l * H + t.a0, (int64_t)l * H + t.a1, A_WRITE, W1});
+      break;
+    case PMK_OP_GATEUP:
+      acc.push_back({B_XM, (int64_t)l * H, (int64_t)(l + 1) * H, A_READ, W1});
+      acc.push_back({B_H, (int64_t)l * m.F + t.a0 / 2, (int64_t)l * m.F + (t.a1 + 1) / 2, A_WRITE, W1});
+      break;
+    case PMK_OP_DOWN:
+      acc.push_back({B_H, (int64_t)l * m.F, (int64_t)(l + 1) * m.F, A_READ, W1});
+      acc.push_back({B_XM, (int64_t)l * H + t.a0, (int64_t)l * H + t.a1, A_READ, W1});
+      acc.push_back({B_X, (int64_t)(l + 1) * H + t.a0, (int64_t)(l + 1) * H + t.a1, A_WRITE, W1});
+      break;
+    case PMK_OP_LMHEAD:
+      acc.push_back({B_X, (int64_t)m.L * H, (int64_t)(m.L + 1) * H, A_READ, W1});
+      acc.push_back({B_LOGITS, (int64_t)e * m.V + t.a0, (int64_t)e * m.V + t.a1, A_WRITE, W1});
+      acc.push_back({B_KEY, e, e + 1, A_ATOMIC, W1});
+      break;
+    case PMK_OP_TOKEN:
+      acc.push_back({B_KEY, e, e + 1, A_READ, W1});
+      acc.push_back({B_OUT, e, e + 1, A_WRITE, W1});
+      acc.push_back({B_TOKSLOT, 0, 1, A_WRITE, W1});
+      break;
+  }
+}
+
+bool valid_op(int op) { return op >= PMK_OP_QKV && op <= PMK_OP_TOKEN; }
+
+// Full-count waits are the only ones that order a specific producer before the waiter.
+bool full_wait(const Schedule& s, const pmk_task& t) {
+  return t.wait_ctr >= 0 && t.wait_count == s.counters[t.wait_ctr].producers;
+}
+
+}  // namespace
+
+// ================================================================================================
+// Static validator
+// ================================================================================================
+std::string validate_schedule(const Schedule& s) {
+  const ModelDims& m = s.m;
+  const int NT = (int)s.tasks.size(), NQ = s.n_queues, NC = (int)s.counters.size();
+  const int S = s.attn_splits;
+  // ---- 1. referential integrity ----
+  if (NQ <= 0 || (int)s.queues.size() != NQ) return "integrity: queue table size mismatch";
+  std::vector<int> seen(NT, 0);
+  std::vector<int> queue_of(NT, -1), pos_of(NT, -1);
+  for (int q = 0; q < NQ; ++q)
+    for (int i = 0; i < (int)s.queues[q].size(); ++i) {
+      const int t = s.queues[q][i];
+      if (t < 0 || t >= NT) return fmt("integrity: queue %ld entry %ld names task %ld which does not exist", q, i, t);
+      if (seen[t]++) return fmt("integrity: task %ld appears in more than one queue slot", t);
+      queue_of[t] = q;
+      pos_of[t] = i;
+    }
+  for (int t = 0; t < NT; ++t)
+    if (!seen[t]) return fmt("integrity: task %ld is in no queue", t);
+  for (int t = 0; t < NT; ++t) {
+    const pmk_task& k = s.tasks[t];
+    if (!valid_op(k.op)) return fmt("integrity: task %ld has unknown op %ld", t, k.op);
+    if (k.wait_ctr < -1 || k.wait_ctr >= NC) return fmt("integrity: task %ld waits on missing counter %ld", t, k.wait_ctr);
+    if (k.signal_ctr < -1 || k.signal_ctr >= NC)
+      return fmt("integrity: task %ld signals missing counter %ld", t, k.signal_ctr);
+    if (k.wait_lag < 0 || k.wait_lag > 1) return fmt("integrity: task %ld has wait lag %ld", t, k.wait_lag);
+    const bool layered = k.op != PMK_OP_LMHEAD && k.op != PMK_OP_TOKEN;
+    if (layered && (k.layer < 0 || k.layer >= m.L)) return fmt("integrity: task %ld layer %ld out of range", t, k.layer);
+    int lim = 0;
+    switch (k.op) {
+      case PMK_OP_QKV: lim = m.qkv_rows(); break;
+      case PMK_OP_OPROJ: case PMK_OP_DOWN: lim = m.H; break;
+      case PMK_OP_GATEUP: lim = 2 * m.F; break;
+      case PMK_OP_LMHEAD: lim = m.V; break;
+      default: break;
+    }
+    if (k.op == PMK_OP_ATTN) {
+      if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 < 0 || k.a1 >= S)
+        return fmt("integrity: ATTN task %ld has kv head %ld / split %ld out of range", t, k.a0, k.a1);
+    } else if (lim) {
+      if (k.a0 < 0 || k.a1 > lim || k.a0 >= k.a1) return fmt("integrity: task %ld row range [%ld,%ld) invalid", t, k.a0, k.a1);
+      if ((k.op == PMK_OP_QKV || k.op == PMK_OP_GATEUP) && ((k.a0 | k.a1) & 1))
+        return fmt("integrity: task %ld row range [%ld,%ld) splits a row pair", t, k.a0, k.a1);
+    }
+  }
+  // ---- 2. thresholds and producer counts ----
+  std::vector<std::vector<int>> producers(NC);  // tasks that signal c (ATTN: grouped by slot below)
+  std::map<std::pair<int, int>, std::vector<int>> attn_groups;  // (ctr, slot) -> ATTN tasks
+  for (int t = 0; t < NT; ++t) {
+    const pmk_task& k = s.tasks[t];
+    if (k.signal_ctr < 0) continue;
+    if (k.op == PMK_OP_ATTN) attn_groups[{k.signal_ctr, k.signal_slot}].push_back(t);
+    else producers[k.signal_ctr].push_back(t);
+  }
+  for (auto& kv : attn_groups) {
+    if (!producers[kv.first.first].empty())
+      return fmt("thresholds: counter %ld mixes combine and task signals", kv.first.first);
+    if ((int)kv.second.size() != S)
+      return fmt("thresholds: combine slot %ld of counter %ld has %ld splits, the kernel joins %ld", kv.first.second,
+                 kv.first.first, (long)kv.second.size(), S);
+    std::set<int> splits;
+    for (int t : kv.second) splits.insert(s.tasks[t].a1);
+    if ((int)splits.size() != S) return fmt("thresholds: combine slot %ld of counter %ld repeats a split", kv.first.second, kv.first.first);
+  }
+  std::vector<int> nprod(NC, 0);
+  for (int c = 0; c < NC; ++c) nprod[c] = (int)producers[c].size();
+  for (auto& kv : attn_groups) nprod[kv.first.first] += 1;
+  for (int c = 0; c < NC; ++c) {
+    if (nprod[c] != s.counters[c].producers)
+      return fmt("thresholds: counter %ld declares %ld producers but %ld tasks signal it", c, s.counters[c].producers, nprod[c]);
+    std::set<int> slots;
+    for (int t : producers[c]) slots.insert(s.tasks[t].signal_slot);
+    for (auto& kv : attn_groups)
+      if (kv.first.first == c) slots.insert(kv.first.second);
+    if ((int)slots.size() != nprod[c] || (nprod[c] && (*slots.begin() != 0 || *slots.rbegin() != nprod[c] - 1)))
+      return fmt("thresholds: counter %ld producer slots are not 0..%ld", c, nprod[c] - 1);
+  }
+  for (int t = 0; t < NT; ++t) {
+    const pmk_task& k = s.tasks[t];
+    if (k.wait_ctr < 0) continue;
+    const int P = s.counters[k.wait_ctr].producers;
+    if (k.wait_count < 1 || k.wait_count > P)
+      return fmt("thresholds: task %ld waits for %ld signals of counter %ld which has %ld producers", t, k.wait_count, k.wait_ctr, P);
+  }
+  // ---- 3. deadlock freedom: monotone execution of two steps ----
+  {
+    const int STEPS = 2;
+    std::vector<int64_t> ctr(NC, 0);
+    std::map<std::pair<int, int>, int64_t> ticket;
+    std::vector<int> head(NQ, 0);  // position in the unrolled queue (step * len + i)
+    bool progress = true;
+    while (progress) {
+      progress = false;
+      for (int q = 0; q < NQ; ++q) {
+        const int len = (int)s.queues[q].size();
+        while (head[q] < STEPS * len) {
+          const int e = head[q] / len;
+          const pmk_task& k = s.tasks[s.queues[q][head[q] % len]];
+          if (k.wait_ctr >= 0) {
+            const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
+            if (ctr[k.wait_ctr] < need) break;
+          }
+          if (k.signal_ctr >= 0) {
+            if (k.op == PMK_OP_ATTN) {
+              int64_t& tk = ticket[{k.signal_ctr, k.signal_slot}];
+              if (++tk % S == 0) ctr[k.signal_ctr] += 1;
+            } else {
+              ctr[k.signal_ctr] += 1;
+            }
+          }
+          ++head[q];
+          progress = true;
+        }
+      }
+    }
+    for (int q = 0; q < NQ; ++q) {
+      const int len = (int)s.queues[q].size();
+      if (head[q] < STEPS * len) {
+        const int t = s.queues[q][head[q] % len];
+        const pmk_task& k = s.tasks[t];
+        std::ostringstream os;
+        os << "deadlock: queue " << q << " stalls at step " << head[q] / len << " on task " << t << " (" << op_name(k.op)
+           << " waits on counter " << k.wait_ctr << " for " << k.wait_count << " signals, lag " << k.wait_lag << ")";
+        return os.str();
+      }
+    }
+  }
+  // ---- 4/5. happens-before over two unrolled steps (vector clocks) ----
+  // Nodes: real tasks (t, e) on queue q at unrolled index e*len(q)+i; virtual combine nodes
+  // (counter, slot, e) on their own virtual queue at index e.
+  std::vector<std::pair<int, int>> vkeys;
+  std::map<std::pair<int, int>, int> vidx;
+  for (auto& kv : attn_groups) {
+    vidx[kv.first] = (int)vkeys.size();
+    vkeys.push_back(kv.first);
+  }
+  const int NV = (int)vkeys.size();
+  const int W = NQ + NV;  // vector clock width
+  const int STEPS = 2;
+  // topological processing: simulate again, computing clocks as tasks complete
+  std::vector<int16_t> vc_task((size_t)STEPS * NT * W, -1);
+  std::vector<int16_t> vc_virt((size_t)STEPS * NV * W, -1);
+  std::vector<int16_t> join_ctr((size_t)STEPS * NC * W, -1);
+  std::vector<int> join_count((size_t)STEPS * NC, 0);
+  auto vt = [&](int t, int e) { return &vc_task[((size_t)e * NT + t) * W]; };
+  auto vv = [&](int v, int e) { return &vc_virt[((size_t)e * NV + v) * W]; };
+  auto jc = [&](int c, int e) { return &join_ctr[((size_t)e * NC + c) * W]; };
+  auto vmax = [&](int16_t* a, const int16_t* b) { for (int i = 0; i < W; ++i) a[i] = std::max(a[i], b[i]); };
+  {
+    std::vector<int64_t> ctr(NC, 0);
+    std::map<std::pair<int, int>, int64_t> ticket;
+    std::vector<int> head(NQ, 0);
+    bool progress = true;
+    while (progress) {
+      progress = false;
+      for (int q = 0; q < NQ; ++q) {
+        const int len = (int)s.queues[q].size();
+        while (head[q] < STEPS * len) {
+          const int e = head[q] / len, i = head[q] % len, t = s.queues[q][i];
+          const pmk_task& k = s.tasks[t];
+          if (k.wait_ctr >= 0) {
+            const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
+            if (ctr[k.wait_ctr] < need) break;
+          }
+          int16_t* v = vt(t, e);
+          if (head[q] > 0) {
+            const int pt = s.queues[q][(head[q] - 1) % len], pe = (head[q] - 1) / len;
+            std::memcpy(v, vt(pt, pe), W * sizeof(int16_t));
+          }
+          v[q] = (int16_t)head[q];
+          if (full_wait(s, k) && e - k.wait_lag >= 0) vmax(v, jc(k.wait_ctr, e - k.wait_lag));
+          if (k.signal_ctr >= 0) {
+            if (k.op == PMK_OP_ATTN) {
+              const int vi = vidx[{k.signal_ctr, k.signal_slot}];
+              int16_t* cv = vv(vi, e);
+              vmax(cv, v);
+              int64_t& tk = ticket[{k.signal_ctr, k.signal_slot}];
+              if (++tk % S == 0) {
+                cv[NQ + vi] = (int16_t)e;
+                vmax(jc(k.signal_ctr, e), cv);
+                join_count[(size_t)e * NC + k.signal_ctr]++;
+                ctr[k.signal_ctr] += 1;
+              }
+            } else {
+              vmax(jc(k.signal_ctr, e), v);
+              join_count[(size_t)e * NC + k.signal_ctr]++;
+              ctr[k.signal_ctr] += 1;
+            }
+          }
+          ++head[q];
+          progress = true;
+        }
+      }
+    }
+  }
+  // node identity for hb queries
+  struct Node { int queue, index; const int16_t* vc; };
+  auto task_node = [&](int t, int e) { return Node{queue_of[t], e * (int)s.queues[queue_of[t]].size() + pos_of[t], vt(t, e)}; };
+  auto virt_node = [&](int v, int e) { return Node{NQ + v, e, vv(v, e)}; };
+  auto hb = [&](const Node& a, const Node& b) { return b.vc[a.queue] >= a.index; };
+
+  // ---- 4. join completeness: a reader of a region written by a multi-producer phase waits on all of it ----
+  struct Acc { Access a; Node n; int task; int e; bool virt; };
+  std::vector<std::vector<Acc>> by_buf(B_COUNT);
+  std::vector<Access> tmp;
+  for (int e = 0; e < STEPS; ++e) {
+    for (int t = 0; t < NT; ++t) {
+      tmp.clear();
+      task_accesses(s, s.tasks[t], e, false, tmp);
+      for (auto& a : tmp) by_buf[a.buf].push_back({a, task_node(t, e), t, e, false});
+    }
+    for (int v = 0; v < NV; ++v) {
+      tmp.clear();
+      const int t0 = attn_groups[vkeys[v]][0];
+      task_accesses(s, s.tasks[t0], e, true, tmp);
+      for (auto& a : tmp) by_buf[a.buf].push_back({a, virt_node(v, e), t0, e, true});
+    }
+  }
+  for (int t = 0; t < NT; ++t) {
+    const pmk_task& k = s.tasks[t];
+    if (k.wait_ctr < 0 || full_wait(s, k)) continue;
+    // partial wait: does this task read anything that producers of the waited counter write?
+    tmp.clear();
+    task_accesses(s, k, 1, false, tmp);
+    std::vector<Access> prod;
+    for (int p = 0; p < NT; ++p) {
+      const pmk_task& pk = s.tasks[p];
+      if (pk.signal_ctr != k.wait_ctr) continue;
+      task_accesses(s, pk, 1 - k.wait_lag, pk.op == PMK_OP_ATTN, prod);
+    }
+    for (auto& r : tmp)
+      if (r.kind == A_READ)
+        for (auto& w : prod)
+          if (w.kind != A_READ && w.buf == r.buf && w.lo < r.hi && r.lo < w.hi)
+            return fmt("join: task %ld reads a region that %ld producers of counter %ld write but waits for only %ld of them",
+                       t, s.counters[k.wait_ctr].producers, k.wait_ctr, k.wait_count);
+  }
+  // ---- 5. happens-before on every conflicting pair (within a step and across consecutive steps) ----
+  for (int b = 0; b < B_COUNT; ++b) {
+    auto& v = by_buf[b];
+    std::sort(v.begin(), v.end(), [](const Acc& x, const Acc& y) { return x.a.lo < y.a.lo; });
+    for (size_t i = 0; i < v.size(); ++i)
+      for (size_t j = i + 1; j < v.size() && v[j].a.lo < v[i].a.hi; ++j) {
+        const Acc& x = v[i];
+        const Acc& y = v[j];
+        if (x.a.kind == A_READ && y.a.kind == A_READ) continue;
+        if (x.a.kind == A_ATOMIC && y.a.kind == A_ATOMIC) continue;
+        if (x.n.queue == y.n.queue && x.n.index == y.n.index) continue;  // same node
+        const Acc* first = &x;
+        const Acc* second = &y;
+        if (x.e != y.e) {
+          if (x.e > y.e) std::swap(first, second);  // across steps: the earlier step's access first
+        } else if (x.a.kind == A_READ || y.a.kind == A_READ) {
+          // one step, a read and a write: a read of this step's value follows the write; a read of
+          // the value from before the step (a lagged read) precedes it
+          const Acc* r = x.a.kind == A_READ ? &x : &y;
+          const Acc* w = x.a.kind == A_READ ? &y : &x;
+          const bool same_step_value = r->a.expect == r->e + 1;
+          first = same_step_value ? w : r;
+          second = same_step_value ? r : w;
+        } else {
+          // two writers (or a writer and an atomic) of one step: either order, but ordered
+          if (hb(x.n, y.n) || hb(y.n, x.n)) continue;
+          return fmt("race: tasks %ld and %ld both write buffer %ld [%ld, ...) in one step without ordering", x.task, y.task, b,
+                     (long)std::max(x.a.lo, y.a.lo));
+        }
+        if (!hb(first->n, second->n)) {
+          std::ostringstream os;
+          os << "race: " << (first->virt ? "combine after " : "") << op_name(s.tasks[first->task].op) << " task " << first->task
+             << " (step " << first->e << ", " << (first->a.kind == A_READ ? "read" : "write") << ") is not ordered before "
+             << (second->virt ? "combine after " : "") << op_name(s.tasks[second->task].op) << " task " << second->task
+             << " (step " << second->e << ", " << (second->a.kind == A_READ ? "read" : "write") << ") on buffer " << b
+             << " elements [" << std::max(x.a.lo, y.a.lo) << ", " << std::min(x.a.hi, y.a.hi) << ")";
+          return os.str();
+        }
+      }
+  }
+  // monotonic counters: every signal of step e+1 follows every signal of step e on the same counter
+  for (int c = 0; c < NC; ++c) {
+    for (int t1 : producers[c]) {
+      const Node n1 = task_node(t1, 1);
+      for (int t0 : producers[c])
+        if (!hb(task_node(t0, 0), n1))
+          return fmt("counter: task %ld signals counter %ld for step 1 before task %ld has signalled it for step 0", t1, c, t0);
+    }
+  }
+  // ---- 6. output reachability ----
+  int tok = -1;
+  for (int t = 0; t < NT; ++t)
+    if (s.tasks[t].op == PMK_OP_TOKEN) { if (tok >= 0) return "reachability: more than one TOKEN task"; tok = t; }
+  if (tok < 0) return "reachability: no TOKEN task (the greedy choice is never read)";
+  const Node tn = task_node(tok, 0);
+  for (int t = 0; t < NT; ++t)
+    if (t != tok && !hb(task_node(t, 0), tn))
+      return fmt("reachability: task %ld does not reach the greedy choice of its step (", t) + op_name(s.tasks[t].op) + ")";
+  for (int v = 0; v < NV; ++v)
+    if (!hb(virt_node(v, 0), tn)) return fmt("reachability: combine %ld does not reach the greedy choice", v);
+  return "";
+}
+
+// ================================================================================================
+// CPU simulator: one host thread per queue, poisoned stamp buffers, random yields
+// ================================================================================================
+pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::string* report) {
+  const int NQ = s.n_queues, NC = (int)s.counters.size(), S = s.attn_splits;
+  BufDims bd = buf_dims(s, steps);
+  int64_t total = 0;
+  for (int b = 0; b < B_COUNT; ++b) total += bd.size[b];
+  if (total > 50'000'000) { *report = "simulate: model too large for the simulator"; return PMK_ERR_INVALID_ARG; }
+  std::vector<std::unique_ptr<std::atomic<int32_t>[]>> stamps(B_COUNT);
+  for (int b = 0; b < B_COUNT; ++b) {
+    stamps[b].reset(new std::atomic<int32_t>[bd.size[b]]);
+    for (int64_t i = 0; i < bd.size[b]; ++i) stamps[b][i].store(b == B_TOKSLOT ? 0 : -1);  // -1 = poison
+  }
+  std::unique_ptr<std::atomic<int64_t>[]> ctr(new std::atomic<int64_t>[NC]);
+  for (int c = 0; c < NC; ++c) ctr[c].store(0);
+  std::map<std::pair<int, int>, int> tslot;
+  for (auto& t : s.tasks)
+    if (t.op == PMK_OP_ATTN && t.signal_ctr >= 0) tslot.emplace(std::make_pair(t.signal_ctr, t.signal_slot), (int)tslot.size());
+  std::unique_ptr<std::atomic<int64_t>[]> ticket(new std::atomic<int64_t>[tslot.size() + 1]);
+  for (size_t i = 0; i <= tslot.size(); ++i) ticket[i].store(0);
+  std::atomic<bool> abort_flag{false};
+  std::mutex mu;
+  std::string first_error;
+  pmk_status status = PMK_OK;
+  auto fail = [&](pmk_status st, const std::string& msg) {
+    std::lock_guard<std::mutex> g(mu);
+    if (status == PMK_OK) { status = st; first_error = msg; }
+    abort_flag.store(true);
+  };
+  auto run_accesses = [&](std::mt19937_64& rng, const std::vector<Access>& acc, int e, bool writes, const char* what,
+                          int task) {
+    for (const Access& a : acc) {
+      if (a.kind == A_READ && !writes) {
+        for (int64_t i = a.lo; i < a.hi; ++i) {
+          const int32_t st = stamps[a.buf][i].load();
+          if (st != a.expect) {
+            std::ostringstream os;
+            os << "race: " << what << " task " << task << " at step " << e << " read buffer " << a.buf << "[" << i
+               << "] with stamp " << st << ", expected " << a.expect << (st < 0 ? " (poisoned)" : "");
+            fail(PMK_ERR_SCHEDULE_INVALID, os.str());
+            return;
+          }
+          if ((rng() & 63) == 0) std::this_thread::yield();
+        }
+      } else if (a.kind != A_READ && writes) {
+        for (int64_t i = a.lo; i < a.hi; ++i) {
+          stamps[a.buf][i].store(a.expect);
+          if ((rng() & 63) == 0) std::this_thread::yield();
+        }
+      }
+    }
+  };
+  auto worker = [&](int q) {
+    std::mt19937_64 rng(seed * 1000003ull + q);
+    std::vector<Access> acc, cacc;
+    const auto& queue = s.queues[q];
+    for (int e = 0; e < steps && !abort_flag.load(); ++e) {
+      for (int t : queue) {
+        const pmk_task& k = s.tasks[t];
+        if (k.wait_ctr >= 0) {
+          const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
+          auto t0 = std::chrono::steady_clock::now();
+          while (ctr[k.wait_ctr].load() < need) {
+            if (abort_flag.load()) return;
+            std::this_thread::yield();
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(5)) {
+              std::ostringstream os;
+              os << "deadlock: queue " << q << " waited 5 s at step " << e << " on counter " << k.wait_ctr << " (" << op_name(k.op)
+                 << " task " << t << ", has " << ctr[k.wait_ctr].load() << ", needs " << need << ")";
+              fail(PMK_ERR_TIMEOUT, os.str());
+              return;
+            }
+          }
+        }
+        acc.clear();
+        task_accesses(s, k, e, false, acc);
+        run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads at start
+        if ((rng() & 3) == 0) std::this_thread::yield();
+        run_accesses(rng, acc, e, true, op_name(k.op), t);   // writes
+        if (k.op != PMK_OP_ATTN) run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads again: catches WAR
+        if (abort_flag.load()) return;
+        if (k.signal_ctr < 0) continue;
+        if (k.op == PMK_OP_ATTN) {
+          auto& tk = ticket[tslot[{k.signal_ctr, k.signal_slot}]];
+          const int64_t old = tk.fetch_add(1);
+          if (old % S == S - 1) {
+            cacc.clear();
+            task_accesses(s, k, e, true, cacc);
+            run_accesses(rng, cacc, e, false, "combine", t);
+            run_accesses(rng, cacc, e, true, "combine", t);
+            ctr[k.signal_ctr].fetch_add(1);
+          }
+        } else {
+          ctr[k.signal_ctr].fetch_add(1);
+        }
+      }
+    }
+  };
+  std::vector<std::thread> th;
+  for (int q = 0; q < NQ; ++q) th.emplace_back(worker, q);
+  for (auto& t : th) t.join();
+  *report = first_error;
+  return status;
+}
+
+// ================================================================================================
+// hashing and flattening
+// ================================================================================================
+uint64_t schedule_hash(const Schedule& s) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](const void* p, size_t n) {
+    const uint8_t* b = (const uint8_t*)p;
+    for (size_t i = 0; i < n; ++i) { h ^= b[i]; h *= 1099511628211ull; }
+  };
+  mix(&s.m, sizeof(s.m));
+  mix(&s.n_queues, sizeof(int));
+  mix(&s.attn_splits, sizeof(int));
+  mix(&s.sync_mode, sizeof(int));
+  for (auto& t : s.tasks) mix(&t, sizeof(t));
+  for (auto& q : s.queues) {
+    int n = (int)q.size();
+    mix(&n, sizeof n);
+    mix(q.data(), q.size() * sizeof(int32_t));
+  }
+  for (auto& c : s.counters) mix(&c, sizeof c);
+  return h;
+}
+
+DeviceTables flatten(const Schedule& s) {
+  DeviceTables d;
+  d.tasks = s.tasks;
+  d.qoff.push_back(0);
+  for (auto& q : s.queues) {
+    d.qtasks.insert(d.qtasks.end(), q.begin(), q.end());
+    d.qoff.push_back((int32_t)d.qtasks.size());
+  }
+  for (auto& c : s.counters) {
+    d.ctr_producers.push_back(c.producers);
+    d.ctr_flag_base.push_back(c.flag_base);
+  }
+  return d;
+}
+
+}  // namespace pmk

@@ -1,0 +1,124 @@
+"""GPU-vs-oracle parity harness (test helper).
+
+The GPU path runs through the C ABI (persistent_megakernel_02_amd.Decoder); the oracle runs
+teacher-forced on the GPU's own input tokens, so both compare the same context at every step.
+Pass rule: max |logit difference| <= tol, and the GPU's greedy token equals the oracle's argmax
+wherever the oracle's top-2 gap exceeds 1e-2 (both top tokens are correct below that gap).
+"""
+from __future__ import annotations
+
+import sys
+import time
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+import oracle
+import synthgen
+
+GAP = 1e-2
+
+
+def tol_for(w) -> float:
+    return 1e-1 if w.wdtype == "fp8" else 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class GpuRun:
+    first: int
+    tokens: np.ndarray      # [n] greedy outputs
+    logits: np.ndarray      # [n][V]
+    n_done: int
+    seconds: float
+
+
+def gpu_run(w, weights, steps: int, mode: int = 0, prompt: Optional[np.ndarray] = None, kv=None,
+            next_token: int = 0, sched=None, kv_scales: Optional[np.ndarray] = None, chunks=None,
+            logits: bool = True, dec=None):
+    import torch
+    import persistent_megakernel_02_amd as pmk
+    own = dec is None
+    if own:
+        dec = pmk.Decoder(pmk.model_config(w), 0, sched)
+        dec.load_weights(pmk.DeviceWeights(weights))
+    dec.set_mode(mode)
+    dev = torch.device("cuda", 0)
+    ks = torch.from_numpy(kv_scales).to(dev) if kv_scales is not None else None
+    if kv is not None:
+        k, v, P = kv
+        dec.load_kv(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), P, next_token, ks)
+        first = next_token
+    else:
+        first_t = dec.prefill(torch.from_numpy(np.ascontiguousarray(prompt, np.int32)).to(dev), ks)
+        torch.cuda.synchronize()
+        first = int(first_t.item())
+    t0 = time.time()
+    outs, lgs, done = [], [], 0
+    for n in (chunks or [steps]):
+        toks, lg, nd = dec.decode(n, logits=logits)
+        torch.cuda.synchronize()
+        outs.append(toks.cpu().numpy())
+        if logits:
+            lgs.append(lg.cpu().numpy())
+        done += int(nd.item())
+    secs = time.time() - t0
+    err = dec.poll_error()
+    assert err.code == 0, f"device error {err.code} cu {err.cu} task {err.task} ctr {err.counter} " \
+                          f"expected {err.expected} seen {err.seen}"
+    run = GpuRun(first, np.concatenate(outs), np.concatenate(lgs) if logits else None, done, secs)
+    if own:
+        dec.close()
+    return run
+
+
+def oracle_teacher_forced(w, weights, run: GpuRun, prompt=None, kv=None, kv_scales=None, steps=None,
+                          max_seq=None):
+    """Oracle logits for each GPU step, fed the GPU's input tokens; also checks the first token."""
+    om = oracle.OracleModel(weights, max_seq=max_seq)
+    if kv_scales is not None:
+        om.set_kv_scales(kv_scales)
+    first_ok = True
+    if kv is not None:
+        k, v, P = kv
+        om.load_kv(k, v, P)
+    else:
+        tok0, lg0 = om.prefill(prompt)
+        first_ok = _token_ok(lg0, run.first)
+    n = len(run.tokens) if steps is None else steps
+    out = []
+    inp = run.first
+    for i in range(n):
+        _, lg = om.step(inp)
+        out.append(lg)
+        inp = int(run.tokens[i])
+    return np.stack(out), first_ok
+
+
+def _token_ok(lg: np.ndarray, tok: int) -> bool:
+    order = np.argsort(-lg.astype(np.float64), kind="stable")
+    top, second = order[0], order[1]
+    if lg[top] - lg[second] > GAP:
+        return int(tok) == int(top)
+    # near tie: the GPU token must be one whose logit is within the gap of the top
+    return lg[top] - lg[int(tok)] <= GAP
+
+
+def check(w, run: GpuRun, ref: np.ndarray, first_ok: bool = True, label: str = ""):
+    n = ref.shape[0]
+    diff = np.abs(run.logits[:n].astype(np.float64) - ref.astype(np.float64))
+    md = float(diff.max())
+    tol = tol_for(w)
+    bad = [i for i in range(n) if not _token_ok(ref[i], run.tokens[i])]
+    log(f"[parity {label}] steps={n} max|dlogit|={md:.3e} (tol {tol}) token mismatches={bad} first_ok={first_ok} "
+        f"logit scale={float(np.abs(ref).max()):.3f}")
+    assert md <= tol, f"{label}: max |dlogit| {md} > {tol}"
+    assert not bad, f"{label}: greedy tokens differ at steps {bad}"
+    assert first_ok, f"{label}: prefill token differs"
+    assert np.isfinite(run.logits).all()
+    return md

@@ -1,0 +1,119 @@
+"""GPU parity: the decode path through the C ABI against the CPU oracle (teacher-forced).
+
+Tolerance (stated by the workload): logits within max-abs 2e-2 for fp16/bf16, 1e-1 for fp8, and
+identical greedy tokens wherever the oracle's top-2 gap exceeds 1e-2.  Small workloads run the
+full prefill + decode; the full-size workloads start from synthetic KV contents of their full
+prompt length (a generator input given to both sides) and compare sampled decode steps.
+"""
+import numpy as np
+import pytest
+
+import synthgen
+from synthgen import WORKLOADS
+from tests.parity import check, gpu_run, log, oracle_teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+TINY = WORKLOADS["tiny"]
+TINY_FP8 = TINY.with_(name="tiny_fp8", wdtype="fp8", kvdtype="fp8", n_q=4, n_kv=2, head_dim=128, hidden=512,
+                      ffn=1024)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synthgen.make_weights(TINY, gain_std=0.1)
+
+
+def _modes():
+    import persistent_megakernel_02_amd as pmk
+    return [("megakernel", pmk.PMK_MODE_MEGAKERNEL), ("graph", pmk.PMK_MODE_GRAPH), ("per_op", pmk.PMK_MODE_PER_OP)]
+
+
+@pytest.mark.parametrize("mode_name", ["megakernel", "graph", "per_op"])
+def test_tiny_full_prefill_and_decode(tiny, mode_name):
+    mode = dict(_modes())[mode_name]
+    prompt = synthgen.make_prompt(TINY)
+    log(f"tiny {mode_name}: prefill {len(prompt)} + decode {TINY.steps}")
+    run = gpu_run(TINY, tiny, TINY.steps, mode=mode, prompt=prompt)
+    ref, first_ok = oracle_teacher_forced(TINY, tiny, run, prompt=prompt)
+    check(TINY, run, ref, first_ok, f"tiny/{mode_name}")
+
+
+def test_tiny_counter_sync_mode(tiny):
+    import persistent_megakernel_02_amd as pmk
+    prompt = synthgen.make_prompt(TINY)
+    run = gpu_run(TINY, tiny, TINY.steps, prompt=prompt, sched=pmk.schedule_config(sync_mode=pmk.PMK_SYNC_COUNTERS))
+    ref, first_ok = oracle_teacher_forced(TINY, tiny, run, prompt=prompt)
+    check(TINY, run, ref, first_ok, "tiny/counters")
+
+
+def test_modes_agree_bitwise_and_chunking(tiny):
+    """The three modes run the same task functions in the same order: identical logits.  Decoding in
+    chunks (the KV cache, position and next-token slot persist between calls) equals one call."""
+    prompt = synthgen.make_prompt(TINY)
+    runs = {name: gpu_run(TINY, tiny, TINY.steps, mode=m, prompt=prompt) for name, m in _modes()}
+    base = runs["megakernel"]
+    for name, r in runs.items():
+        assert np.array_equal(r.tokens, base.tokens), name
+        assert np.array_equal(r.logits, base.logits), name
+    chunked = gpu_run(TINY, tiny, TINY.steps, prompt=prompt, chunks=[5, 11, 16])
+    assert np.array_equal(chunked.tokens, base.tokens)
+    assert np.array_equal(chunked.logits, base.logits)
+    again = gpu_run(TINY, tiny, TINY.steps, prompt=prompt)
+    assert np.array_equal(again.logits, base.logits)  # deterministic
+
+
+def test_tiny_eos_stops_early(tiny):
+    import torch
+    import persistent_megakernel_02_amd as pmk
+    prompt = synthgen.make_prompt(TINY)
+    ref = gpu_run(TINY, tiny, TINY.steps, prompt=prompt)
+    eos = int(ref.tokens[3])
+    stop = int(np.argmax(ref.tokens == eos)) + 1
+    for _, mode in _modes():
+        dec = pmk.Decoder(pmk.model_config(TINY), 0)
+        dec.load_weights(pmk.DeviceWeights(tiny))
+        dec.set_mode(mode)
+        dec.prefill(torch.from_numpy(prompt).cuda())
+        toks, _, nd = dec.decode(TINY.steps, eos=eos)
+        torch.cuda.synchronize()
+        assert int(nd.item()) == stop
+        assert np.array_equal(toks.cpu().numpy()[:stop], ref.tokens[:stop])
+        dec.close()
+
+
+def test_tiny_fp8_prefill_and_decode():
+    w = TINY_FP8
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32)
+    run = gpu_run(w, wts, w.steps, prompt=prompt, kv_scales=scales)
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt, kv_scales=scales)
+    check(w, run, ref, first_ok, "tiny_fp8")
+
+
+# ------------------------------------------------------------------------------------------------
+# workloads at their full model size: synthetic KV of the full prompt length, sampled decode steps
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,steps", [("1b", 6), ("2b", 4), ("8b", 3), ("8b_fp8", 3)])
+def test_full_size_decode_from_synthetic_kv(name, steps):
+    w = WORKLOADS[name]
+    log(f"{name}: generating weights")
+    wts = synthgen.make_weights(w)
+    k, v, scales = synthgen.make_kv(w, w.prompt)
+    kv = (k, v, w.prompt)
+    nxt = int(synthgen.make_prompt(w, 1)[0])
+    log(f"{name}: GPU decode from KV {w.prompt}")
+    run = gpu_run(w, wts, steps, kv=kv, next_token=nxt, kv_scales=scales)
+    log(f"{name}: oracle {steps} steps")
+    ref, _ = oracle_teacher_forced(w, wts, run, kv=kv, kv_scales=scales)
+    check(w, run, ref, True, name)
+
+
+def test_1b_prefill_short_prompt():
+    w = WORKLOADS["1b"].with_(prompt=24, steps=8)
+    wts = synthgen.make_weights(w)
+    prompt = synthgen.make_prompt(w)
+    run = gpu_run(w, wts, w.steps, prompt=prompt)
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt)
+    check(w, run, ref, first_ok, "1b/prefill24")
