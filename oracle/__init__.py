@@ -75,6 +75,7 @@ def lib():
         L.orc_read_kv.argtypes = [vp, vp, vp, i32]
         L.orc_prefill.argtypes = [vp, vp, i32, i32, vp]
         L.orc_step.argtypes = [vp, i32, vp]
+        L.orc_num_threads.argtypes = []
         _lib = L
     return _lib
 
@@ -139,6 +140,11 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, fmt: int, ks: float = 1.
 
 def silu(z: float) -> float:
     return lib().orc_silu(z)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().orc_num_threads()
 
 
 def argmax(v: np.ndarray) -> int:

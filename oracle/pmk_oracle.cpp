@@ -439,3 +439,6 @@ int orc_step(orc_model* m, int32_t tok, float* logits) {
 }
 
 }  // extern "C"
+
+#include <omp.h>
+extern "C" int orc_num_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,236 @@
+"""The static validator (Safety Gate) and the CPU schedule simulator.
+
+Real lowerings over a spread of shapes, queue counts, split counts and sync modes must all be
+accepted; a generated corpus of unsafe mutants of real lowerings (dropped waits, lowered or
+raised thresholds, wrong step lag, swapped queue entries, back edges, aliased output ranges,
+dropped signals, removed producers, shared flag slots) must all be rejected: zero false
+accepts.  Each mutation kind is unsafe by construction (the comment at each generator says
+why); the simulator confirms deadlocks and races on tiny schedules.
+"""
+import ctypes
+import random
+
+import pytest
+
+import persistent_megakernel_02_amd as pmk
+from persistent_megakernel_02_amd import _lib
+from synthgen import WORKLOADS
+
+OPS = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "TOKEN"}
+
+
+class Sched:
+    def __init__(self, w, n_cus, **kw):
+        self.lib = pmk.load()
+        self.h = ctypes.c_void_p()
+        cfg = pmk.model_config(w)
+        st = self.lib.pmk_schedule_build(ctypes.byref(cfg), ctypes.byref(pmk.schedule_config(**kw)), n_cus,
+                                         ctypes.byref(self.h))
+        assert st == 0, self.lib.pmk_last_global_error()
+
+    def __del__(self):
+        if self.h:
+            self.lib.pmk_schedule_free(self.h)
+
+    @property
+    def n_tasks(self):
+        return self.lib.pmk_schedule_num_tasks(self.h)
+
+    @property
+    def n_queues(self):
+        return self.lib.pmk_schedule_num_queues(self.h)
+
+    def task(self, i):
+        t = pmk.pmk_task()
+        assert self.lib.pmk_schedule_get_task(self.h, i, ctypes.byref(t)) == 0
+        return t
+
+    def set_task(self, i, t):
+        assert self.lib.pmk_schedule_set_task(self.h, i, ctypes.byref(t)) == 0
+
+    def queue(self, q):
+        n = ctypes.c_int32()
+        p = self.lib.pmk_schedule_queue(self.h, q, ctypes.byref(n))
+        return [p[i] for i in range(n.value)]
+
+    def set_queue(self, q, lst):
+        arr = (ctypes.c_int32 * len(lst))(*lst)
+        assert self.lib.pmk_schedule_set_queue(self.h, q, arr, len(lst)) == 0
+
+    def producers(self, c):
+        return self.lib.pmk_schedule_counter_producers(self.h, c)
+
+    def set_producers(self, c, p):
+        assert self.lib.pmk_schedule_set_counter_producers(self.h, c, p) == 0
+
+    def validate(self):
+        buf = ctypes.create_string_buffer(512)
+        st = self.lib.pmk_schedule_validate(self.h, buf, 512)
+        return st, buf.value.decode()
+
+    def simulate(self, steps=3, seed=1):
+        buf = ctypes.create_string_buffer(512)
+        st = self.lib.pmk_schedule_simulate(self.h, steps, seed, buf, 512)
+        return st, buf.value.decode()
+
+
+REAL = [("tiny", n, {}) for n in (1, 2, 3, 4, 7, 8, 16, 64, 256)] + \
+       [("tiny", 8, dict(attn_splits=s)) for s in (1, 2, 5)] + \
+       [("tiny", 8, dict(sync_mode=pmk.PMK_SYNC_COUNTERS))] + \
+       [("1b", n, {}) for n in (16, 100, 256)] + [("2b", 256, {}), ("8b", 256, {}), ("8b_fp8", 256, {}),
+                                                  ("8b", 304, dict(attn_splits=16))]
+
+
+@pytest.mark.parametrize("name,n_cus,kw", REAL)
+def test_real_lowerings_are_accepted(name, n_cus, kw):
+    s = Sched(WORKLOADS[name], n_cus, **kw)
+    st, msg = s.validate()
+    assert st == 0, msg
+
+
+@pytest.mark.parametrize("n_cus", [2, 5, 8])
+def test_simulator_runs_real_lowerings_clean(n_cus):
+    s = Sched(WORKLOADS["tiny"], n_cus)
+    for seed in (1, 2):
+        st, msg = s.simulate(steps=3, seed=seed)
+        assert st == 0, msg
+
+
+# ------------------------------------------------------------------------------------------------
+# mutation corpus
+# ------------------------------------------------------------------------------------------------
+def mutants(w, n_cus, rng, per_kind):
+    """Yield (kind, mutate(sched)) pairs; every mutant is unsafe by construction."""
+    base = Sched(w, n_cus)
+    NT, NQ = base.n_tasks, base.n_queues
+    tasks = [base.task(i) for i in range(NT)]
+    q0 = set(base.queue(0))
+    # the first QKV tasks on the queue that ends with the TOKEN task are already ordered after the
+    # previous step's LM head by program order, so their wait is redundant (dropping it is safe)
+    waiting = [i for i, t in enumerate(tasks) if t.wait_ctr >= 0 and not (t.op == 1 and t.layer == 0 and i in q0)]
+    signalling = [i for i, t in enumerate(tasks) if t.signal_ctr >= 0 and t.op != 2]
+    full = [i for i in waiting if tasks[i].wait_count == base.producers(tasks[i].wait_ctr)
+            and base.producers(tasks[i].wait_ctr) > 1]
+
+    def drop_wait(s, i):      # the task reads data other queues produce in the same (or previous) step
+        t = s.task(i); t.wait_ctr = -1; s.set_task(i, t)
+
+    def lower_threshold(s, i):  # join incomplete: a reader of a multi-producer region waits for fewer
+        t = s.task(i); t.wait_count = max(1, t.wait_count - 1 - rng.randrange(t.wait_count - 1 or 1)); s.set_task(i, t)
+
+    def raise_threshold(s, i):  # never satisfiable
+        t = s.task(i); t.wait_count = s.producers(t.wait_ctr) + 1 + rng.randrange(3); s.set_task(i, t)
+
+    def zero_threshold(s, i):
+        t = s.task(i); t.wait_count = 0; s.set_task(i, t)
+
+    def wrong_lag(s, i):        # waits for the previous step's producers: reads stale data
+        t = s.task(i); t.wait_lag = 1 - t.wait_lag; s.set_task(i, t)
+
+    def back_edge(s, i):        # waits on a counter produced later in the same step (by its dependants)
+        t = s.task(i)
+        own = max(t.signal_ctr, t.wait_ctr if t.wait_lag == 0 else -1)
+        later = sorted({tasks[j].signal_ctr for j in signalling if tasks[j].signal_ctr > own})
+        t.wait_ctr = rng.choice(later)
+        t.wait_lag = 0
+        t.wait_count = s.producers(t.wait_ctr)
+        s.set_task(i, t)
+
+    def drop_signal(s, i):      # the counter never reaches its producer count
+        t = s.task(i); t.signal_ctr = -1; s.set_task(i, t)
+
+    def remove_producer(s, i):  # declared producer count no longer matches the signalling tasks
+        c = s.task(i).signal_ctr; s.set_producers(c, s.producers(c) - 1)
+
+    def shared_slot(s, i):      # two producers publish through one flag word
+        t = s.task(i)
+        peers = [j for j in signalling if tasks[j].signal_ctr == t.signal_ctr and j != i]
+        if peers:
+            t.signal_slot = tasks[rng.choice(peers)].signal_slot
+        else:
+            t.signal_slot = t.signal_slot + 1
+        s.set_task(i, t)
+
+    def alias_rows(s, i):       # two tasks of one phase write overlapping output rows
+        t = s.task(i)
+        peers = [j for j in signalling if tasks[j].op == t.op and tasks[j].layer == t.layer and j != i
+                 and t.op in (3, 5, 6)]
+        if not peers:
+            t.a1 = t.a0  # empty range: referential integrity
+        else:
+            p = tasks[rng.choice(peers)]
+            t.a0, t.a1 = p.a0, p.a1
+        s.set_task(i, t)
+
+    def swap_queue(s, q):       # a task moved before the task whose signal it (transitively) needs
+        lst = s.queue(q)
+        if len(lst) < 2:
+            lst = lst + lst[:1]  # duplicate entry: integrity
+        else:
+            k = rng.randrange(len(lst) - 1)
+            lst[k], lst[k + 1] = lst[k + 1], lst[k]
+        s.set_queue(q, lst)
+
+    def drop_from_queue(s, q):  # a task in no queue
+        lst = s.queue(q)
+        if lst:
+            lst.pop(rng.randrange(len(lst)))
+        s.set_queue(q, lst)
+
+    kinds = [("drop_wait", drop_wait, waiting), ("lower_threshold", lower_threshold, full),
+             ("raise_threshold", raise_threshold, waiting), ("zero_threshold", zero_threshold, waiting),
+             ("wrong_lag", wrong_lag, waiting), ("back_edge", back_edge, [i for i in waiting if tasks[i].op not in (6, 7)]),
+             ("drop_signal", drop_signal, signalling), ("remove_producer", remove_producer, signalling),
+             ("shared_slot", shared_slot, signalling), ("alias_rows", alias_rows, signalling)]
+    for kind, fn, sites in kinds:
+        for i in rng.sample(sites, min(per_kind, len(sites))):
+            yield kind, (lambda s, fn=fn, i=i: fn(s, i))
+    for kind, fn in (("swap_queue", swap_queue), ("drop_from_queue", drop_from_queue)):
+        for _ in range(per_kind):
+            q = rng.randrange(NQ)
+            yield kind, (lambda s, fn=fn, q=q: fn(s, q))
+
+
+def test_mutation_corpus_has_no_false_accepts():
+    rng = random.Random(20260609)
+    total, by_kind, accepted = 0, {}, []
+    for name, n_cus, per_kind in (("tiny", 4, 40), ("tiny", 8, 40), ("tiny", 32, 20), ("1b", 16, 10)):
+        w = WORKLOADS[name]
+        for kind, mutate in mutants(w, n_cus, rng, per_kind):
+            s = Sched(w, n_cus)
+            mutate(s)
+            st, msg = s.validate()
+            total += 1
+            by_kind[kind] = by_kind.get(kind, 0) + 1
+            if st == 0:
+                accepted.append((name, n_cus, kind))
+    print(f"mutants: {total} {by_kind}")
+    assert total >= 800
+    assert not accepted, f"false accepts: {accepted[:10]}"
+
+
+def test_swapping_across_a_dependency_is_a_deadlock():
+    s = Sched(WORKLOADS["tiny"], 4)
+    q = s.queue(0)
+    # the queue's ATTN(0) waits for all QKV(0) tasks, including this queue's own, which now follows it
+    i_qkv = next(k for k, t in enumerate(q) if s.task(t).op == 1)
+    i_attn = next(k for k, t in enumerate(q) if s.task(t).op == 2)
+    q[i_qkv], q[i_attn] = q[i_attn], q[i_qkv]
+    s.set_queue(0, q)
+    st, msg = s.validate()
+    assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith("deadlock"), msg
+    st, msg = s.simulate(steps=2)
+    assert st == _lib.PMK_ERR_TIMEOUT and "deadlock" in msg, msg
+
+
+def test_simulator_catches_a_race_the_validator_rejects():
+    s = Sched(WORKLOADS["tiny"], 16)
+    gu = [i for i in range(s.n_tasks) if s.task(i).op == 4 and s.task(i).layer == 0]
+    for i in gu:
+        t = s.task(i)
+        t.wait_ctr = -1
+        s.set_task(i, t)
+    st, msg = s.validate()
+    assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith("race"), msg
+    caught = [s.simulate(steps=2, seed=k) for k in range(5)]
+    assert any(st == _lib.PMK_ERR_SCHEDULE_INVALID and "race" in m for st, m in caught), caught
