@@ -65,7 +65,10 @@ def main():
     ap.add_argument("--no-graph-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--repeat", type=int, default=1, help="extra timed launches reported as a spread")
-    ap.add_argument("--kernel-only", action="store_true", help="skip every leg but the timed launches (profiling)")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="profiling: start from synthetic KV instead of a prefill and skip every leg but the timed launches")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (counter scale calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures the single-GPU decode path only; --gpus {args.gpus} is not supported "
@@ -104,13 +107,28 @@ def main():
     if w.kvdtype == "fp8":
         # static per (layer, kv head, K|V) scale: 8 maps to 448 (k, v of these models have unit-order spread)
         kv_scales = torch.full((w.layers, w.n_kv, 2), 8.0 / 448.0, dtype=torch.float32, device=dev)
-    log(f"[bench] prefill {P} tokens")
     torch.cuda.synchronize()
     t0 = time.time()
-    first = dec.prefill(prompt, kv_scales)
+    if args.kernel_only:
+        log(f"[bench] synthetic KV of {P} positions")
+        k, v, sc = synthgen.make_kv(w, P)
+        nxt = int(synthgen.make_prompt(w, 1)[0])
+        dec.load_kv(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), P, nxt,
+                    torch.from_numpy(sc).to(dev) if sc is not None else None)
+        del k, v
+        first = torch.tensor([nxt], dtype=torch.int32, device=dev)
+    else:
+        log(f"[bench] prefill {P} tokens")
+        first = dec.prefill(prompt, kv_scales)
     torch.cuda.synchronize()
     prefill_s = time.time() - t0
     first_tok = first.clone()
+    if args.copy_calib:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     out_tokens = torch.empty(max(K, W), dtype=torch.int32, device=dev)
     n_done = torch.zeros(1, dtype=torch.int32, device=dev)
     # ---- warm-up, rewind, timed launch ----
@@ -140,7 +158,9 @@ def main():
     achieved = bytes_launch / elapsed / 1e9
     log(f"[bench] {K} steps in {elapsed * 1e3:.2f} ms: {tokens_per_s:.1f} tok/s, {achieved:.0f} GB/s "
         f"({100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s)")
-    extra = {"prefill_tokens_per_s": round(P / prefill_s, 1), "timed_launches_s": [round(t, 6) for t in times]}
+    extra = {"timed_launches_s": [round(t, 6) for t in times]}
+    if not args.kernel_only:
+        extra["prefill_tokens_per_s"] = round(P / prefill_s, 1)
 
     # ---- sync share from the per-task trace (separate, untimed call) ----
     if trace_steps:
