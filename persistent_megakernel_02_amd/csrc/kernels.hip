@@ -289,25 +289,43 @@ __device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x)
 
 constexpr int kRing = 8;
 
-// Sync: block-wide callable (wait + stage the input vector into LDS), run by every thread once.
-// ScaleRow: row -> pointer to the row's 128-column block scales (fp8 only).
-// Epi: PAIR == 1: epi(row, value); PAIR == 2: epi(even_row, value_even, value_odd).  Called by
-// every lane of the owning wave with wave-uniform arguments.
-template <int WDT, int PAIR, class Sync, class ScaleRow, class Epi>
-__device__ __forceinline__ void gemv_task(const uint8_t* __restrict__ W, int K, int r0, int r1, const float* xs,
-                                          Sync sync, ScaleRow srow, Epi epi) {
+// Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
+// KS minimises the largest per-wave unit count (short tiles then still keep all waves streaming).
+__device__ __forceinline__ int choose_ks(int rows, int nsl) {
+  int best = 0x7fffffff, ks_best = 1;
+  for (int ks = 1; ks <= kWaves; ks <<= 1) {
+    const int g = kWaves / ks;
+    const int cost = ((rows + g - 1) / g) * ((nsl + ks - 1) / ks);
+    if (cost < best) { best = cost; ks_best = ks; }
+  }
+  return ks_best;
+}
+
+// GEMV over rows [r0, r1) of W (row-major [rows][K]) against the vector staged in LDS by `sync`.
+// On return (after a workgroup barrier) y[r - r0] holds row r's fp32 dot product.  yp is LDS
+// scratch of 8 * (r1 - r0) floats for the per-slice partial sums (summed in slice order).
+// A lane reads 16-byte chunks c = j*64 + lane of a row (slice j), so one wave instruction streams
+// 1 KiB.  Weight loads run through a ring of kRing registers per lane; the first kRing are issued
+// BEFORE the dependency wait (weights do not depend on it); each consumed slot is refilled with
+// the chunk kRing units ahead.  Past the end the refill re-reads the tile's first chunk (a cache
+// hit) so that the load sequence stays branch free.  The loop issues no other global load.
+template <int WDT, class Sync, class ScaleRow>
+__device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, int r0, int r1, const float* xs,
+                                          float* yp, float* y, Sync sync, ScaleRow srow) {
   constexpr int EPL = WFmt<WDT>::EPL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
-  const int ngr = (r1 - r0) / PAIR;
-  const int wr0 = r0 + PAIR * (int)((int64_t)ngr * wave / kWaves);
-  const int wr1 = r0 + PAIR * (int)((int64_t)ngr * (wave + 1) / kWaves);
-  const int nunits = (wr1 - wr0) * nsl;
+  const int R = r1 - r0;
+  const int KS = choose_ks(R, nsl);
+  const int G = kWaves / KS, gi = wave / KS, si = wave % KS;
+  const int wr0 = r0 + (int)((int64_t)R * gi / G), wr1 = r0 + (int)((int64_t)R * (gi + 1) / G);
+  const int s0 = (int)((int64_t)nsl * si / KS), s1 = (int)((int64_t)nsl * (si + 1) / KS);
+  const int nunits = (wr1 - wr0) * (s1 - s0);
 
   u32x4 ring[kRing];
   float rsc[kRing];
-  int lrow = wr0, lj = 0;
+  int lrow = wr0, lj = s0;
   const uint8_t* safe = W + (int64_t)r0 * rb;
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
@@ -316,42 +334,45 @@ __device__ __forceinline__ void gemv_task(const uint8_t* __restrict__ W, int K, 
     u32x4 v = ld_nt(p);
     ring[d] = ok ? v : u32x4{0u, 0u, 0u, 0u};
     if constexpr (WDT == WFP8) rsc[d] = ok ? srow(lrow)[c >> 3] : 0.f;
-    if (++lj == nsl) { lj = 0; ++lrow; }
+    if (++lj == s1) { lj = s0; ++lrow; }
   };
   if (nunits > 0) {
 #pragma unroll
     for (int d = 0; d < kRing; ++d) issue(d);
   }
   sync();
-  if (nunits <= 0) return;
-  float acc = 0.f, v_even = 0.f;
-  int crow = wr0, cj = 0;
-  for (int base = 0; base < nunits; base += kRing) {
+  if (nunits > 0) {
+    float acc = 0.f;
+    int crow = wr0, cj = s0;
+    for (int base = 0; base < nunits; base += kRing) {
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      const u32x4 w = ring[d];
-      float s = 1.f;
-      if constexpr (WDT == WFP8) s = rsc[d];
-      issue(d);
-      if (base + d < nunits) {
-        const float part = chunk_dot<WDT>(w, xs + (cj * 64 + lane) * EPL);
-        if constexpr (WDT == WFP8) acc = fmaf(part, s, acc);
-        else acc += part;
-        if (++cj == nsl) {
-          cj = 0;
-          const float v = wave_sum(acc);
-          acc = 0.f;
-          if constexpr (PAIR == 2) {
-            if (((crow - wr0) & 1) == 0) v_even = v;
-            else epi(crow - 1, v_even, v);
-          } else {
-            epi(crow, v);
+      for (int d = 0; d < kRing; ++d) {
+        const u32x4 w = ring[d];
+        float sc = 1.f;
+        if constexpr (WDT == WFP8) sc = rsc[d];
+        issue(d);
+        if (base + d < nunits) {
+          const float part = chunk_dot<WDT>(w, xs + (cj * 64 + lane) * EPL);
+          if constexpr (WDT == WFP8) acc = fmaf(part, sc, acc);
+          else acc += part;
+          if (++cj == s1) {
+            cj = s0;
+            const float v = wave_sum(acc);
+            acc = 0.f;
+            if (lane == 0) yp[(crow - r0) * KS + si] = v;
+            ++crow;
           }
-          ++crow;
         }
       }
     }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R; i += kThreads) {
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k) v += yp[i * KS + k];
+    y[i] = v;
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -438,17 +459,26 @@ __device__ __forceinline__ const float* fp8_rows(const KParams& P, int l, int wh
 }
 
 // QKV: RMSNorm(x) -> packed QKV rows [a0, a1) -> RoPE on q/k pairs -> q to the workspace,
-// k and v appended to the cache at `pos`.
+// k and v appended to the cache at `pos`.  The RoPE row of this position (and the fp8 K/V scales)
+// are staged in LDS with the input, so the epilogue reads no global memory.
 template <int WDT, int KVDT>
-__device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+__device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                         int cu) {
   constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
   const int l = t.layer, H = P.H, hd = P.hd, half = hd / 2;
   const int pad = pad_len(H, WFmt<WDT>::EPL);
   float* xs = lds;
   float* red = lds + P.xs_floats;
+  float2* rope = reinterpret_cast<float2*>(lds + P.epi_off);  // [hd/2] (cos, sin), then [2*nkv] (scale, -)
+  float* yp = lds + P.yp_off;
+  float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_qkv;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
+    for (int i = threadIdx.x; i < half; i += kThreads) rope[i] = P.rope[(int64_t)sc.pos * half + i];
+    if constexpr (KVDT == WFP8)
+      for (int i = threadIdx.x; i < 2 * P.nkv; i += kThreads)
+        rope[half + i] = make_float2(P.kv_scale[(int64_t)l * P.nkv * 2 + i], 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
       stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, P.eps, xs, red);
@@ -467,9 +497,11 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     const int dim = (pr >> 1) + (pr & 1) * half;
     return fp8_rows<WDT>(P, l, which) + (int64_t)((head * hd + dim) / 128) * nbc;
   };
-  const float2* rope = P.rope + (int64_t)sc.pos * half;
-  auto epi = [&](int r, float a, float b) {
-    if ((threadIdx.x & 63) != 0) return;
+  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  const int npairs = (t.a1 - t.a0) >> 1;
+  for (int p = threadIdx.x; p < npairs; p += kThreads) {
+    const int r = t.a0 + 2 * p;
+    float a = y[2 * p], b = y[2 * p + 1];
     int sec, base;
     if (r < qrows) { sec = 0; base = 0; }
     else if (r < qrows + krows) { sec = 1; base = qrows; }
@@ -486,52 +518,21 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
       float* q = P.q + (int64_t)l * P.qdim + head * hd;
       stc(q + i, a);
       stc(q + i + half, b);
-      return;
+      continue;
     }
     const int64_t row = (((int64_t)l * P.nkv + head) * P.max_seq + sc.pos) * hd;
     uint8_t* cache = sec == 1 ? P.kc : P.vc;
     if constexpr (KVDT == WFP8) {
-      const float s = P.kv_scale[((int64_t)l * P.nkv + head) * 2 + (sec - 1)];
-      stc(cache + row + i, enc_e4m3(a / s));
-      stc(cache + row + i + half, enc_e4m3(b / s));
+      const float s8 = rope[half + 2 * head + (sec - 1)].x;
+      stc(cache + row + i, enc_e4m3(a / s8));
+      stc(cache + row + i + half, enc_e4m3(b / s8));
     } else {
       uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
       stc(c16 + row + i, enc16<KVDT>(a));
       stc(c16 + row + i + half, enc16<KVDT>(b));
     }
-  };
-  gemv_task<WDT, 2>(W, H, t.a0, t.a1, xs, sync, srow, epi);
-  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
-}
-
-// Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
-// query heads of the group; the partial (m, l, acc[hd]) per head goes to the workspace.  The last
-// split to finish (atomic ticket) combines all splits of the head group into o.
-// Thread layout: scores take one position per thread (K row in registers, q broadcast from LDS);
-// P.V takes positions across waves and head dimensions across lanes.  K and V rows of past
-// positions are loaded before the dependency wait; the current position's row after it.
-template <int KVDT>
-__device__ __forceinline__ uint32_t load_v_word(const uint8_t* vrow, int lane, int dpl, bool coherent) {
-  constexpr int KES = KVDT == WFP8 ? 1 : 2;
-  const int bytes = dpl * KES;  // 1, 2 or 4
-  const uint8_t* p = vrow + lane * bytes;
-  if (bytes == 4) return coherent ? ldc(reinterpret_cast<const uint32_t*>(p)) : *reinterpret_cast<const uint32_t*>(p);
-  if (bytes == 2)
-    return coherent ? (uint32_t)__hip_atomic_load(reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(p)), __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                    : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
-  return coherent ? (uint32_t)__hip_atomic_load(const_cast<uint8_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                  : (uint32_t)*p;
-}
-
-template <int KVDT>
-__device__ __forceinline__ float2 decode_v_word(uint32_t w, int dpl, float vscale) {
-  if constexpr (KVDT == WFP8) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    return make_float2(f.x * vscale, dpl == 2 ? f.y * vscale : 0.f);
-  } else {
-    return make_float2(dec16<KVDT>((uint16_t)(w & 0xffff)), dpl == 2 ? dec16<KVDT>((uint16_t)(w >> 16)) : 0.f);
   }
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 __device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
@@ -539,48 +540,102 @@ __device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
   return u32x4{ldc(q), ldc(q + 1), ldc(q + 2), ldc(q + 3)};
 }
 
+// Sum over groups of `n` adjacent lanes (n = 8 or 16, inside one DPP row); every lane of the
+// group receives the group's sum.
+__device__ __forceinline__ float group_sum(float v, int n) {
+  int x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  x = __float_as_int(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  if (n == 16) {
+    x = __float_as_int(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  }
+  return v;
+}
+
 template <int KVDT>
-__device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+__device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
+  if constexpr (KVDT == WFP8) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], true);
+      out[4 * k] = lo.x;
+      out[4 * k + 1] = lo.y;
+      out[4 * k + 2] = hi.x;
+      out[4 * k + 3] = hi.y;
+    }
+  } else {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = dec16<KVDT>((uint16_t)(wd[k] & 0xffffu));
+      out[2 * k + 1] = dec16<KVDT>((uint16_t)(wd[k] >> 16));
+    }
+  }
+}
+
+// Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
+// query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
+// the last split to finish (atomic ticket) combines all splits of the group into o.
+// The K and V chunks are contiguous ([pos][hd]) and are streamed with coalesced 16-byte loads:
+// LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
+// row block b of the chunk goes to wave b % 8.  Rows of past positions are loaded before the
+// dependency wait; the current position's row (written this step) after it, coherently.
+template <int KVDT>
+__device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                          int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
-  constexpr int KEPL = KVDT == WFP8 ? 16 : 8;  // K elements per 16-byte chunk
-  constexpr int VB = 16;                       // V words prefetched per lane
+  constexpr int EPL = 16 / KES;  // elements per 16-byte chunk
+  constexpr int NB = 8;          // row blocks per wave held in registers per batch
   const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp, hd = P.hd;
   const int T = sc.pos + 1;
   const int chunk = (T + S - 1) / S;
   const int t0 = min(T, split * chunk), t1 = min(T, t0 + chunk);
   const int n = t1 - t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rowbytes = hd * KES;   // 128 or 256
+  const int LPR = rowbytes / 16;   // 8 or 16 lanes per row
+  const int RPI = 64 / LPR;        // 8 or 4 rows per wave instruction
+  const int sub = lane / LPR, part = lane % LPR;
+  const int nblk = (n + RPI - 1) / RPI;
   const int64_t headbase = ((int64_t)l * P.nkv + g) * P.max_seq;
-  const int rowbytes = hd * KES;  // 128 or 256
-  const int nvec = rowbytes / 16;  // 8 or 16
-  const int dpl = hd / 64;         // head dims per lane in P.V: 1 or 2
   const uint8_t* Kc = P.kc + headbase * rowbytes;
   const uint8_t* Vc = P.vc + headbase * rowbytes;
   const int sstride = (n + 3) & ~3;
-  float* qs = lds;                        // [grp][hd]
-  float* sc_lds = qs + grp * hd;          // [grp][sstride]
-  float* red = sc_lds + grp * sstride;    // [kWaves][grp][hd]
-  float* small = lds + P.xs_floats;       // scalars
+  float* qs = lds;                      // [grp][hd]
+  float* scr = qs + grp * hd;           // [grp][sstride] scores, then probabilities
+  float* red = scr + grp * sstride;     // [kWaves][grp][hd]
+  float* small = lds + P.xs_floats;     // [0, 8): m, [8, 16): l
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
     kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
     vscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2 + 1];
   }
-  // ---- loads that do not depend on this step: K row of this thread's position, first V words ----
-  u32x4 krow[16];
-  const bool one_pass = n <= kThreads;
-  const int my_t = t0 + tid;
-  if (one_pass && tid < n && my_t < sc.pos) {
+  auto row_of = [&](int i) { return t0 + (wave + kWaves * i) * RPI + sub; };  // position of register slot i
+  u32x4 kb[NB], vb[NB];
+  auto load_batch = [&](int i0, bool after_wait) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (v < nvec) krow[v] = ld_nt(Kc + (int64_t)my_t * rowbytes + v * 16);
-  }
-  uint32_t vreg[VB];
-#pragma unroll
-  for (int k = 0; k < VB; ++k) {
-    const int tt = wave + kWaves * k, pt = t0 + tt;
-    vreg[k] = (tt < n && pt < sc.pos) ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, false) : 0u;
-  }
+    for (int i = 0; i < NB; ++i) {
+      const int pt = row_of(i0 + i);
+      const bool ok = pt < t1;
+      const bool cur = pt == sc.pos;
+      const int64_t off = (int64_t)(ok ? pt : t0) * rowbytes + part * 16;
+      if (!after_wait) {
+        kb[i] = ok && !cur ? ld_nt(Kc + off) : u32x4{0u, 0u, 0u, 0u};
+        vb[i] = ok && !cur ? ld_nt(Vc + off) : u32x4{0u, 0u, 0u, 0u};
+      } else if (ok) {
+        kb[i] = cur ? ldc16B(Kc + off) : ld_nt(Kc + off);
+        vb[i] = cur ? ldc16B(Vc + off) : ld_nt(Vc + off);
+      }
+    }
+  };
+  const int nbw = (nblk - wave + kWaves - 1) / kWaves;  // row blocks of this wave
+  if (n > 0) load_batch(0, false);
   maybe_wait(P, t, sc, cu, ti);
   const float* qsrc = P.q + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
   for (int i = 2 * tid; i < grp * hd; i += 2 * kThreads) {
@@ -588,110 +643,111 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     qs[i] = v.x;
     qs[i + 1] = v.y;
   }
-  if (one_pass && tid < n && my_t == sc.pos) {
+  // the current position's rows, written in this step
+  if (n > 0) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (v < nvec) krow[v] = ldc16B(Kc + (int64_t)my_t * rowbytes + v * 16);
+    for (int i = 0; i < NB; ++i)
+      if (row_of(i) == sc.pos) {
+        const int64_t off = (int64_t)sc.pos * rowbytes + part * 16;
+        kb[i] = ldc16B(Kc + off);
+        vb[i] = ldc16B(Vc + off);
+      }
   }
   __syncthreads();
-  // ---- scores ----
-  if (one_pass) {
-    if (tid < n) {
-      for (int j = 0; j < grp; ++j) {
-        const float* qj = qs + j * hd;
-        float a = 0.f;
+  const float qk_scale = kscale * P.attn_scale;
+  // ---- scores and P.V accumulation, batch by batch of register-held rows ----
+  // pass 1: scores
+  for (int ib = 0; ib < nbw; ib += NB) {
+    if (ib > 0) load_batch(ib, true);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (v < nvec) a += chunk_dot<KVDT>(krow[v], qj + v * KEPL);
-        sc_lds[j * sstride + tid] = a * kscale * P.attn_scale;
-      }
-    }
-  } else {
-    for (int base = 0; base < n; base += kThreads) {
-      const int tt = base + tid;
-      if (tt < n) {
-        const int pt = t0 + tt;
-        const uint8_t* kp = Kc + (int64_t)pt * rowbytes;
+    for (int i = 0; i < NB; ++i) {
+      const int pt = row_of(ib + i);
+      if (ib + i < nbw) {
+        float kv[EPL];
+        decode_chunk<KVDT>(kb[i], kv);
         for (int j = 0; j < grp; ++j) {
-          const float* qj = qs + j * hd;
+          const float* qj = qs + j * hd + part * EPL;
           float a = 0.f;
-          for (int v = 0; v < nvec; ++v) {
-            const u32x4 kv = pt < sc.pos ? ld_nt(kp + v * 16) : ldc16B(kp + v * 16);
-            a += chunk_dot<KVDT>(kv, qj + v * KEPL);
-          }
-          sc_lds[j * sstride + tt] = a * kscale * P.attn_scale;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) a = fmaf(kv[e], qj[e], a);
+          a = group_sum(a, LPR);
+          if (part == 0 && pt < t1) scr[j * sstride + (pt - t0)] = a * qk_scale;
         }
       }
     }
   }
   __syncthreads();
-  // ---- softmax statistics per head ----
-  float* mvals = small;       // [grp]
-  float* lvals = small + 8;   // [grp]
-  float* red8 = small + 16;   // [kWaves]
-  for (int j = 0; j < grp; ++j) {
+  // ---- softmax statistics: one wave per head ----
+  for (int j = wave; j < grp; j += kWaves) {
     float m = -INFINITY;
-    for (int tt = tid; tt < n; tt += kThreads) m = fmaxf(m, sc_lds[j * sstride + tt]);
-    m = block_max(m, red8);
+    for (int tt = lane; tt < n; tt += 64) m = fmaxf(m, scr[j * sstride + tt]);
+    m = wave_max(m);
     float sum = 0.f;
-    for (int tt = tid; tt < n; tt += kThreads) {
-      const float p = expf(sc_lds[j * sstride + tt] - m);
-      sc_lds[j * sstride + tt] = p;
-      sum += p;
+    for (int tt = lane; tt < n; tt += 64) {
+      const float pr = expf(scr[j * sstride + tt] - m);
+      scr[j * sstride + tt] = pr;
+      sum += pr;
     }
-    sum = block_sum(sum, red8);
-    if (tid == 0) { mvals[j] = m; lvals[j] = sum; }
+    sum = wave_sum_shfl(sum);
+    if (lane == 0) { small[j] = m; small[8 + j] = sum; }
   }
   __syncthreads();
-  // ---- P.V ----
-  float acc[8][2];
+  // ---- P.V: each lane accumulates its EPL dimensions of up to 4 heads at a time ----
+  const bool reload = nbw > NB;  // rows beyond the first batch were overwritten: reload batch 0
+  for (int jb = 0; jb < grp; jb += 4) {
+    float acc[4][EPL];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { acc[j][0] = 0.f; acc[j][1] = 0.f; }
-  const int nk = (n - wave + kWaves - 1) / kWaves;  // positions of this wave
-  for (int kb = 0; kb < nk; kb += VB) {
-    if (kb > 0) {
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int k = 0; k < VB; ++k) {
-        const int tt = wave + kWaves * (kb + k), pt = t0 + tt;
-        vreg[k] = (tt < n && pt < sc.pos) ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, false) : 0u;
-      }
-    }
+      for (int e = 0; e < EPL; ++e) acc[jj][e] = 0.f;
+    for (int ib = 0; ib < nbw; ib += NB) {
+      if (reload || jb > 0) load_batch(ib, true);
 #pragma unroll
-    for (int k = 0; k < VB; ++k) {
-      const int tt = wave + kWaves * (kb + k), pt = t0 + tt;
-      if (tt < n) {
-        const uint32_t w = pt == sc.pos ? load_v_word<KVDT>(Vc + (int64_t)pt * rowbytes, lane, dpl, true) : vreg[k];
-        const float2 v = decode_v_word<KVDT>(w, dpl, vscale);
+      for (int i = 0; i < NB; ++i) {
+        const int pt = row_of(ib + i);
+        if (ib + i < nbw && pt < t1) {
+          float vv[EPL];
+          decode_chunk<KVDT>(vb[i], vv);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j < grp) {
-            const float p = sc_lds[j * sstride + tt];
-            acc[j][0] = fmaf(p, v.x, acc[j][0]);
-            acc[j][1] = fmaf(p, v.y, acc[j][1]);
+          for (int jj = 0; jj < 4; ++jj) {
+            if (jb + jj < grp) {
+              const float pr = scr[(jb + jj) * sstride + (pt - t0)] * vscale;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr, vv[e], acc[jj][e]);
+            }
           }
         }
       }
     }
-  }
+    // reduce over the RPI rows of a wave instruction (lanes with the same `part`)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < grp) {
-      red[(wave * grp + j) * hd + lane * dpl] = acc[j][0];
-      if (dpl == 2) red[(wave * grp + j) * hd + lane * dpl + 1] = acc[j][1];
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float v = acc[jj][e];
+        for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
+        acc[jj][e] = v;
+      }
+    if (sub == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (jb + jj < grp)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) red[(wave * grp + jb + jj) * hd + part * EPL + e] = acc[jj][e];
     }
   }
   __syncthreads();
-  float* part = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * (hd + 2);
+  float* partp = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * (hd + 2);
   for (int i = tid; i < grp * hd; i += kThreads) {
     const int j = i / hd, d = i % hd;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) s += red[(w * grp + j) * hd + d];
-    stc(part + (int64_t)j * (hd + 2) + 2 + d, s);
+    stc(partp + (int64_t)j * (hd + 2) + 2 + d, s);
   }
   if (tid < grp) {
-    stc(part + (int64_t)tid * (hd + 2), mvals[tid]);
-    stc(part + (int64_t)tid * (hd + 2) + 1, lvals[tid]);
+    stc(partp + (int64_t)tid * (hd + 2), n > 0 ? small[tid] : -INFINITY);
+    stc(partp + (int64_t)tid * (hd + 2) + 1, n > 0 ? small[8 + tid] : 0.f);
   }
   drain();
   __syncthreads();
@@ -703,24 +759,34 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   }
   __syncthreads();
   if (!*last) return;
+  // all partials of the head group (S x grp x (hd+2) floats) in one batch of coherent loads
   const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * (hd + 2);
-  float* ml = lds;                 // [S*grp][2]
-  float* wts = lds + 2 * S * grp;  // [grp][S]
-  for (int i = tid; i < S * grp; i += kThreads) {
-    const float2 v = ldc2(pg + (int64_t)i * (hd + 2));
-    ml[2 * i] = v.x;
-    ml[2 * i + 1] = v.y;
+  const int ntot = S * grp * (hd + 2);  // even: hd + 2 is even
+  float* pl = lds;                      // [S][grp][hd+2]
+  float* wts = lds + ntot;              // [grp][S]
+  for (int i0 = 2 * tid; i0 < ntot; i0 += 8 * kThreads) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 2 * kThreads;
+      v[u] = i < ntot ? ldc2(pg + i) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 2 * kThreads;
+      if (i < ntot) { pl[i] = v[u].x; pl[i + 1] = v[u].y; }
+    }
   }
   __syncthreads();
   for (int j = tid; j < grp; j += kThreads) {
     float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, ml[2 * (s2 * grp + j)]);
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, pl[(s2 * grp + j) * (hd + 2)]);
     float den = 0.f;
     for (int s2 = 0; s2 < S; ++s2) {
-      const float m = ml[2 * (s2 * grp + j)];
+      const float m = pl[(s2 * grp + j) * (hd + 2)];
       const float w = m == -INFINITY ? 0.f : expf(m - M);
       wts[j * S + s2] = w;
-      den += w * ml[2 * (s2 * grp + j) + 1];
+      den += w * pl[(s2 * grp + j) * (hd + 2) + 1];
     }
     const float inv = 1.0f / den;
     for (int s2 = 0; s2 < S; ++s2) wts[j * S + s2] *= inv;
@@ -729,57 +795,50 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
   for (int i = tid; i < grp * hd; i += kThreads) {
     const int j = i / hd, d = i % hd;
-    const float* src = pg + (int64_t)j * (hd + 2) + 2 + d;
-    const int64_t sstep = (int64_t)grp * (hd + 2);
     float s = 0.f;
-    int s2 = 0;
-    for (; s2 + 8 <= S; s2 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ldc(src + (s2 + u) * sstep);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) s = fmaf(wts[j * S + s2 + u], v[u], s);
-    }
-    for (; s2 < S; ++s2) s = fmaf(wts[j * S + s2], ldc(src + s2 * sstep), s);
+    for (int s2 = 0; s2 < S; ++s2) s = fmaf(wts[j * S + s2], pl[(s2 * grp + j) * (hd + 2) + 2 + d], s);
     stc(o + i, s);
   }
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
-// O projection + residual: xm[r] = x[r] + Wo[r].o
+// O projection + residual: xm[r] = x[r] + Wo[r].o  (residual rows staged in LDS with the input)
 template <int WDT>
-__device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+__device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                           int cu) {
   constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
-  const int l = t.layer, K = P.qdim;
+  const int l = t.layer, K = P.qdim, R = t.a1 - t.a0;
   float* xs = lds;
+  float* res = lds + P.epi_off;
+  float* yp = lds + P.yp_off;
+  float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
+    if (l == 0) {
+      const int tok = input_token(P, sc);
+      for (int i = threadIdx.x; i < R; i += kThreads) res[i] = dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i]);
+    } else {
+      for (int i = threadIdx.x; i < R; i += kThreads) res[i] = ldc(P.x + (int64_t)l * P.H + t.a0 + i);
+    }
     stage_copy(P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
-  auto epi = [&](int r, float v) {
-    if ((threadIdx.x & 63) != 0) return;
-    float res;
-    if (l == 0) {
-      const int tok = input_token(P, sc);
-      res = dec16<EDT>(P.embed[(int64_t)tok * P.H + r]);
-    } else {
-      res = ldc(P.x + (int64_t)l * P.H + r);
-    }
-    stc(P.xm + (int64_t)l * P.H + r, res + v);
-  };
-  gemv_task<WDT, 1>(W, K, t.a0, t.a1, xs, sync, srow, epi);
+  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 // RMSNorm(xm) -> interleaved gate/up rows [a0, a1) -> h[n] = silu(gate_n) * up_n
 template <int WDT>
-__device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
+__device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                            int cu) {
   const int l = t.layer, H = P.H;
   float* xs = lds;
   float* red = lds + P.xs_floats;
+  float* yp = lds + P.yp_off;
+  float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_gu;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
@@ -790,73 +849,83 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
   auto srow = [&](int r) -> const float* {
     return fp8_rows<WDT>(P, l, (r & 1) ? 5 : 4) + (int64_t)((r >> 1) / 128) * nbc;
   };
-  auto epi = [&](int r, float gte, float up) {
-    if ((threadIdx.x & 63) != 0) return;
-    const float hval = gte / (1.0f + expf(-gte)) * up;
-    stc(P.h + (int64_t)l * P.F + (r >> 1), hval);
-  };
-  gemv_task<WDT, 2>(W, H, t.a0, t.a1, xs, sync, srow, epi);
+  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  const int npairs = (t.a1 - t.a0) >> 1;
+  for (int p = threadIdx.x; p < npairs; p += kThreads) {
+    const float gte = y[2 * p], up = y[2 * p + 1];
+    stc(P.h + (int64_t)l * P.F + (t.a0 >> 1) + p, gte / (1.0f + expf(-gte)) * up);
+  }
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
-// down projection + residual: x[l+1][r] = xm[r] + Wd[r].h
+// down projection + residual: x[l+1][r] = xm[r] + Wd[r].h  (residual rows staged in LDS)
 template <int WDT>
-__device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
-  const int l = t.layer, K = P.F;
+__device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                          int cu) {
+  const int l = t.layer, K = P.F, R = t.a1 - t.a0;
   float* xs = lds;
+  float* res = lds + P.epi_off;
+  float* yp = lds + P.yp_off;
+  float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_d;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
+    for (int i = threadIdx.x; i < R; i += kThreads) res[i] = ldc(P.xm + (int64_t)l * P.H + t.a0 + i);
     stage_copy(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 6) + (int64_t)(r / 128) * nbc; };
-  auto epi = [&](int r, float v) {
-    if ((threadIdx.x & 63) != 0) return;
-    const float res = ldc(P.xm + (int64_t)l * P.H + r);
-    stc(P.x + (int64_t)(l + 1) * P.H + r, res + v);
-  };
-  gemv_task<WDT, 1>(W, K, t.a0, t.a1, xs, sync, srow, epi);
+  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  for (int i = threadIdx.x; i < R; i += kThreads) stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 // final RMSNorm + LM-head rows [a0, a1); tile argmax folded into the step's 64-bit key
+// (orderable value in the high word, inverted index in the low word: max value, lowest index)
 __device__ __forceinline__ uint32_t orderable(float v) {
   const uint32_t u = __float_as_uint(v);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = ((unsigned long long)(uint32_t)__shfl_xor((int)(k >> 32), o) << 32) |
+                                     (uint32_t)__shfl_xor((int)(uint32_t)k, o);
+    k = other > k ? other : k;
+  }
+  return k;
+}
+
 template <int WDT>
-__device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds, int cu) {
-  const int H = P.H;
+__device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                            int cu) {
+  const int H = P.H, R = t.a1 - t.a0;
   float* xs = lds;
   float* red = lds + P.xs_floats;
-  CallParams* cp = P.call;
-  float* out_logits = cp->out_logits;
+  float* yp = lds + P.yp_off;
+  float* y = lds + P.y_off;
+  float* out_logits = P.call->out_logits;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
   };
   const int nbc = (H + 127) / 128;
   auto srow = [&](int r) -> const float* { return P.sc_lm + (int64_t)(r / 128) * nbc; };
-  float best = -INFINITY;
-  int best_i = 0x7fffffff;
+  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  unsigned long long key = 0ull;
   bool nan_seen = false;
-  auto epi = [&](int r, float v) {
+  for (int i = threadIdx.x; i < R; i += kThreads) {
+    const float v = y[i];
     if (v != v) nan_seen = true;
-    if (v > best || (v == best && r < best_i)) { best = v; best_i = r; }
-    if (out_logits && (threadIdx.x & 63) == 0) out_logits[(int64_t)sc.s * P.V + r] = v;
-  };
-  gemv_task<WDT, 1>(P.lm, H, t.a0, t.a1, xs, sync, srow, epi);
-  // workgroup argmax -> one atomic max per task
+    const unsigned long long k = ((unsigned long long)orderable(v) << 32) | (0xFFFFFFFFu - (uint32_t)(t.a0 + i));
+    key = k > key ? k : key;
+    if (out_logits) out_logits[(int64_t)sc.s * P.V + t.a0 + i] = v;
+  }
+  key = wave_max_u64(key);
   unsigned long long* kred = reinterpret_cast<unsigned long long*>(red + 16);
   const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    kred[wave] = best_i == 0x7fffffff ? 0ull
-                                      : (((unsigned long long)orderable(best)) << 32) | (0xFFFFFFFFu - (uint32_t)best_i);
-    if (nan_seen) report_error(P.ctrl, PMK_ERR_NAN, cu, ti, -1, 0, 0);
-  }
+  if ((threadIdx.x & 63) == 0) kred[wave] = key;
+  if (nan_seen) report_error(P.ctrl, PMK_ERR_NAN, cu, ti, -1, 0, 0);
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long k = 0;

@@ -72,6 +72,7 @@ struct pmk_ctx {
   int mode = PMK_MODE_MEGAKERNEL;
   int trace_on = 0;
   int xs_floats = 0;
+  int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0;
   size_t lds_bytes = 0;
   KParams kp{};
   std::vector<Phase> phases;
@@ -209,10 +210,21 @@ void compute_layout(pmk_ctx* c) {
   const int64_t S = s.attn_splits, grp = m.grp();
   const int64_t chunk = (m.max_seq + S - 1) / S;
   const int64_t attn = grp * m.hd + grp * ((chunk + 3) & ~3ll) + kWaves * grp * m.hd;
-  const int64_t comb = 3 * S * grp;
+  const int64_t comb = S * grp * (m.hd + 2) + grp * S;
   const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn, comb});
   c->xs_floats = (int)((xs + 63) / 64 * 64);
-  c->lds_bytes = (size_t)(c->xs_floats + 64) * 4;
+  // epilogue inputs staged behind the scratch words: the RoPE row (+ fp8 K/V scales) of QKV tasks,
+  // the residual rows of OPROJ and DOWN tasks
+  int64_t epi = m.hd + 4 * (int64_t)m.nkv, rmax = 1;
+  for (const pmk_task& t : s.tasks) {
+    if (t.op == PMK_OP_OPROJ || t.op == PMK_OP_DOWN) epi = std::max<int64_t>(epi, t.a1 - t.a0);
+    if (t.op != PMK_OP_ATTN && t.op != PMK_OP_TOKEN) rmax = std::max<int64_t>(rmax, t.a1 - t.a0);
+  }
+  c->epi_floats = (int)((epi + 63) / 64 * 64);
+  c->epi_off = c->xs_floats + 64;
+  c->yp_off = c->epi_off + c->epi_floats;
+  c->y_off = c->yp_off + (int)((kWaves * rmax + 63) / 64 * 64);
+  c->lds_bytes = (size_t)(c->y_off + (rmax + 63) / 64 * 64) * 4;
 }
 
 void fill_params(pmk_ctx* c) {
@@ -265,6 +277,9 @@ void fill_params(pmk_ctx* c) {
   P.trace_steps = std::max(0, c->sc.trace_steps);
   P.spin_limit = c->sc.spin_limit;
   P.xs_floats = c->xs_floats;
+  P.epi_off = c->epi_off;
+  P.yp_off = c->yp_off;
+  P.y_off = c->y_off;
 }
 
 void compute_phases(pmk_ctx* c) {

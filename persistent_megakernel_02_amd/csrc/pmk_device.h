@@ -79,7 +79,10 @@ struct KParams {
   const int32_t* ctr_flag;
   int n_queues, n_tasks, sync_mode, prefetch, trace_steps;
   int64_t spin_limit;
-  int xs_floats;          // LDS floats reserved for staged activation vectors
+  int xs_floats;          // LDS floats reserved for staged activation vectors (or attention scratch)
+  int epi_off;            // LDS float offset of staged epilogue inputs (RoPE row, residual rows)
+  int yp_off;             // LDS float offset of per-slice GEMV partial sums [8 * rows]
+  int y_off;              // LDS float offset of GEMV row results [rows]
 };
 
 }  // namespace pmk

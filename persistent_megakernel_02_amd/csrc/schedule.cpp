@@ -65,6 +65,8 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   if (S <= 0) {
     S = std::max(1, n_queues / m.nkv);
     S = std::min(S, std::max(1, m.max_seq / 16));
+    // the last split's combine stages every partial (S x grp x (hd + 2) floats) in LDS
+    S = std::min(S, std::max(1, 32000 / (m.grp() * (m.hd + 3))));
   }
   s.attn_splits = S;
   s.queues.assign(n_queues, {});
