@@ -211,9 +211,10 @@ pmk_status pmk_get_position(const pmk_ctx* ctx, int32_t* pos);
 /* After the caller synchronised the stream: reads the device error word. */
 pmk_status pmk_poll_error(pmk_ctx* ctx, pmk_device_error* err);
 
-/* Trace: with trace_steps > 0 and pmk_set_trace(ctx, 1), each task of the first trace_steps
- * steps of the next decode call records (wait begin, start, end) from the constant 100 MHz
- * clock.  pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats
+/* Trace: with trace_steps > 0 and pmk_set_trace(ctx, 1) (which clears the ring), each task of
+ * the first trace_steps steps of the next decode call records its wait begin, start and end, and
+ * up to four task-specific sub-phase stamps (GEMV: input staged, rows done; attention: scores,
+ * partial stored, ticket, combine done), from the constant 100 MHz clock.  pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats
  * gives the mean share of queue time spent waiting. */
 pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
 pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);

@@ -68,6 +68,18 @@ __device__ __forceinline__ void drain() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Agent-coherent 16-byte load through a buffer resource (cache policy sc1).  Reads at or past
+// `bytes` return zero (hardware range check), which also zero-fills padding.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ldc16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
+}
+__device__ __forceinline__ float4 as_f4(u32x4 v) {
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 __device__ __forceinline__ u32x4 ld_nt(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -288,6 +300,7 @@ __device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x)
 }
 
 constexpr int kRing = 8;
+constexpr int kAttnBlocks = 8;  // attention row blocks per wave (see the builder's split bound)
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
 // KS minimises the largest per-wave unit count (short tiles then still keep all waves streaming).
@@ -378,26 +391,64 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
 // ------------------------------------------------------------------------------------------------
 // input staging (RMSNorm prologue fused into the consuming GEMV)
 // ------------------------------------------------------------------------------------------------
+// Load n fp32 values from a coherent buffer into xs[0..pad) (zeros past n), every load of a
+// batch issued before any is consumed.  Returns the sum of squares of the loaded values when
+// `want_ss` (thread partial).
+template <bool want_ss>
+__device__ __forceinline__ float load_vector(const float* src, int n, int pad, float* xs) {
+  const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 4);
+  constexpr int B = 8;
+  float ss = 0.f;
+  for (int base = 0; base < pad; base += B * 4 * kThreads) {
+    u32x4 v[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
+      v[k] = i < pad ? ldc16(r, (uint32_t)i * 4) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
+      if (i < pad) {
+        const float4 f = as_f4(v[k]);
+        *reinterpret_cast<float4*>(xs + i) = f;
+        if (want_ss) ss = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, ss))));
+      }
+    }
+  }
+  return ss;
+}
+
 // xs[0..H) = rmsnorm(src) * gain, xs[H..pad) = 0.  src is either a coherent fp32 vector or (emb != null)
 // a 16-bit embedding row.
 template <int EDT>
 __device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* emb, const float* gain, int H, int pad,
                                               float eps, float* xs, float* red) {
   float ss = 0.f;
-  for (int i = 2 * threadIdx.x; i < H; i += 2 * kThreads) {
-    float2 v;
-    if (emb) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(emb + i);
-      v = make_float2(dec16<EDT>((uint16_t)(u & 0xffff)), dec16<EDT>((uint16_t)(u >> 16)));
-    } else {
-      v = ldc2(src + i);
+  if (emb) {
+    for (int i = 8 * threadIdx.x; i < pad; i += 8 * kThreads) {
+      float f[8];
+      if (i < H) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(emb + i);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[2 * k] = dec16<EDT>((uint16_t)(wd[k] & 0xffff));
+          f[2 * k + 1] = dec16<EDT>((uint16_t)(wd[k] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        xs[i + k] = f[k];
+        ss = fmaf(f[k], f[k], ss);
+      }
     }
-    xs[i] = v.x;
-    xs[i + 1] = v.y;
-    ss = fmaf(v.x, v.x, ss);
-    ss = fmaf(v.y, v.y, ss);
+  } else {
+    ss = load_vector<true>(src, H, pad, xs);
   }
-  for (int i = H + threadIdx.x; i < pad; i += kThreads) xs[i] = 0.f;
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
   for (int i = threadIdx.x; i < H; i += kThreads) xs[i] = (xs[i] * r) * gain[i];
@@ -406,12 +457,7 @@ __device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* 
 
 // xs[0..n) = src (coherent), zero padding
 __device__ __forceinline__ void stage_copy(const float* src, int n, int pad, float* xs) {
-  for (int i = 2 * threadIdx.x; i < n; i += 2 * kThreads) {
-    const float2 v = ldc2(src + i);
-    xs[i] = v.x;
-    xs[i + 1] = v.y;
-  }
-  for (int i = n + threadIdx.x; i < pad; i += kThreads) xs[i] = 0.f;
+  load_vector<false>(src, n, pad, xs);
   __syncthreads();
 }
 
@@ -441,7 +487,12 @@ __device__ __forceinline__ int input_token(const KParams& P, const StepCtx& sc) 
 
 __device__ __forceinline__ void trace_mark(const KParams& P, int s, int ti, int slot, uint64_t value) {
   if (threadIdx.x == 0 && P.trace_steps > 0 && P.call->trace && s < P.trace_steps)
-    P.trace[((int64_t)s * P.n_tasks + ti) * 4 + slot] = value;
+    P.trace[((int64_t)s * P.n_tasks + ti) * 8 + slot] = value;
+}
+
+// sub-phase timestamp of the running task (trace slots 4..7)
+__device__ __forceinline__ void mark(const KParams& P, const StepCtx& sc, int ti, int slot) {
+  if (!sc.per_op) trace_mark(P, sc.s, ti, slot, __builtin_amdgcn_s_memrealtime());
 }
 
 __device__ __forceinline__ void maybe_wait(const KParams& P, const pmk_task& t, const StepCtx& sc, int cu, int ti) {
@@ -475,16 +526,21 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_qkv;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
-    for (int i = threadIdx.x; i < half; i += kThreads) rope[i] = P.rope[(int64_t)sc.pos * half + i];
+    // half <= 64 < kThreads and 2 * nkv <= kThreads: one value per thread, loaded with the input
+    const float2 cs = threadIdx.x < half ? P.rope[(int64_t)sc.pos * half + threadIdx.x] : make_float2(0.f, 0.f);
+    float ks8 = 0.f;
     if constexpr (KVDT == WFP8)
-      for (int i = threadIdx.x; i < 2 * P.nkv; i += kThreads)
-        rope[half + i] = make_float2(P.kv_scale[(int64_t)l * P.nkv * 2 + i], 0.f);
+      if (threadIdx.x < 2 * P.nkv) ks8 = P.kv_scale[(int64_t)l * P.nkv * 2 + threadIdx.x];
+    if (threadIdx.x < half) rope[threadIdx.x] = cs;
+    if constexpr (KVDT == WFP8)
+      if (threadIdx.x < 2 * P.nkv) rope[half + threadIdx.x] = make_float2(ks8, 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
       stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, P.eps, xs, red);
     } else {
       stage_rmsnorm<EDT>(P.x + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H, H, pad, P.eps, xs, red);
     }
+    mark(P, sc, ti, 4);
   };
   const int qrows = P.qdim, krows = P.nkv * hd;
   const int nbc = (H + 127) / 128;
@@ -498,6 +554,7 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     return fp8_rows<WDT>(P, l, which) + (int64_t)((head * hd + dim) / 128) * nbc;
   };
   gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  mark(P, sc, ti, 5);
   const int npairs = (t.a1 - t.a0) >> 1;
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
     const int r = t.a0 + 2 * p;
@@ -556,6 +613,18 @@ __device__ __forceinline__ float group_sum(float v, int n) {
   return v;
 }
 
+// Sum over the lanes that share `lane % n` (n = 8 or 16): the other half of the DPP row for n = 8,
+// then across the four rows with the gfx950 row-swap moves.  Every lane receives its column's sum.
+__device__ __forceinline__ float column_sum(float v, int n) {
+  if (n == 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 template <int KVDT>
 __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
   if constexpr (KVDT == WFP8) {
@@ -582,6 +651,7 @@ __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
 // Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
 // query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
 // the last split to finish (atomic ticket) combines all splits of the group into o.
+// Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
 // The K and V chunks are contiguous ([pos][hd]) and are streamed with coalesced 16-byte loads:
 // LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
 // row block b of the chunk goes to wave b % 8.  Rows of past positions are loaded before the
@@ -591,25 +661,25 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
   constexpr int EPL = 16 / KES;  // elements per 16-byte chunk
-  constexpr int NB = 8;          // row blocks per wave held in registers per batch
+  constexpr int NB = kAttnBlocks;  // row blocks per wave, all held in registers (the builder bounds the split)
   const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp, hd = P.hd;
   const int T = sc.pos + 1;
   const int chunk = (T + S - 1) / S;
   const int t0 = min(T, split * chunk), t1 = min(T, t0 + chunk);
   const int n = t1 - t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int PSTR = hd + 4;  // partial record: m, l, 2 pad, acc[hd] (16-byte aligned)
   const int rowbytes = hd * KES;   // 128 or 256
   const int LPR = rowbytes / 16;   // 8 or 16 lanes per row
   const int RPI = 64 / LPR;        // 8 or 4 rows per wave instruction
   const int sub = lane / LPR, part = lane % LPR;
-  const int nblk = (n + RPI - 1) / RPI;
   const int64_t headbase = ((int64_t)l * P.nkv + g) * P.max_seq;
   const uint8_t* Kc = P.kc + headbase * rowbytes;
   const uint8_t* Vc = P.vc + headbase * rowbytes;
   const int sstride = (n + 3) & ~3;
   float* qs = lds;                      // [grp][hd]
   float* scr = qs + grp * hd;           // [grp][sstride] scores, then probabilities
-  float* red = scr + grp * sstride;     // [kWaves][grp][hd]
+  float* red = scr + grp * sstride;     // [kWaves][grp][hd] P.V partials of each wave
   float* small = lds + P.xs_floats;     // [0, 8): m, [8, 16): l
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
@@ -617,66 +687,60 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     vscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2 + 1];
   }
   auto row_of = [&](int i) { return t0 + (wave + kWaves * i) * RPI + sub; };  // position of register slot i
+  // rows of past positions: loaded before the dependency wait
   u32x4 kb[NB], vb[NB];
-  auto load_batch = [&](int i0, bool after_wait) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int pt = row_of(i0 + i);
-      const bool ok = pt < t1;
-      const bool cur = pt == sc.pos;
-      const int64_t off = (int64_t)(ok ? pt : t0) * rowbytes + part * 16;
-      if (!after_wait) {
-        kb[i] = ok && !cur ? ld_nt(Kc + off) : u32x4{0u, 0u, 0u, 0u};
-        vb[i] = ok && !cur ? ld_nt(Vc + off) : u32x4{0u, 0u, 0u, 0u};
-      } else if (ok) {
-        kb[i] = cur ? ldc16B(Kc + off) : ld_nt(Kc + off);
-        vb[i] = cur ? ldc16B(Vc + off) : ld_nt(Vc + off);
-      }
-    }
-  };
-  const int nbw = (nblk - wave + kWaves - 1) / kWaves;  // row blocks of this wave
-  if (n > 0) load_batch(0, false);
-  maybe_wait(P, t, sc, cu, ti);
-  const float* qsrc = P.q + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
-  for (int i = 2 * tid; i < grp * hd; i += 2 * kThreads) {
-    const float2 v = ldc2(qsrc + i);
-    qs[i] = v.x;
-    qs[i + 1] = v.y;
+  for (int i = 0; i < NB; ++i) {
+    const int pt = row_of(i);
+    const bool ok = pt < t1 && pt != sc.pos;
+    const int64_t off = (int64_t)(ok ? pt : t0) * rowbytes + part * 16;
+    kb[i] = ok ? ld_nt(Kc + off) : u32x4{0u, 0u, 0u, 0u};
+    vb[i] = ok ? ld_nt(Vc + off) : u32x4{0u, 0u, 0u, 0u};
   }
+  maybe_wait(P, t, sc, cu, ti);
+  load_vector<false>(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * hd, grp * hd, grp * hd, qs);
   // the current position's rows, written in this step
   if (n > 0) {
+    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(Kc + (int64_t)sc.pos * rowbytes, rowbytes);
+    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(Vc + (int64_t)sc.pos * rowbytes, rowbytes);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       if (row_of(i) == sc.pos) {
-        const int64_t off = (int64_t)sc.pos * rowbytes + part * 16;
-        kb[i] = ldc16B(Kc + off);
-        vb[i] = ldc16B(Vc + off);
+        kb[i] = ldc16(rk, part * 16);
+        vb[i] = ldc16(rv, part * 16);
       }
   }
   __syncthreads();
   const float qk_scale = kscale * P.attn_scale;
-  // ---- scores and P.V accumulation, batch by batch of register-held rows ----
-  // pass 1: scores
-  for (int ib = 0; ib < nbw; ib += NB) {
-    if (ib > 0) load_batch(ib, true);
+  // ---- scores: q of this lane's dimensions in registers, four heads at a time, branch free ----
+  for (int jb = 0; jb < grp; jb += 4) {
+    float qr[4][EPL];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qr[jj][e] = jb + jj < grp ? qs[(jb + jj) * hd + part * EPL + e] : 0.f;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int pt = row_of(ib + i);
-      if (ib + i < nbw) {
-        float kv[EPL];
-        decode_chunk<KVDT>(kb[i], kv);
-        for (int j = 0; j < grp; ++j) {
-          const float* qj = qs + j * hd + part * EPL;
-          float a = 0.f;
+      const int pt = row_of(i);
+      float kv[EPL];
+      decode_chunk<KVDT>(kb[i], kv);
+      float a[4];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) a = fmaf(kv[e], qj[e], a);
-          a = group_sum(a, LPR);
-          if (part == 0 && pt < t1) scr[j * sstride + (pt - t0)] = a * qk_scale;
-        }
+      for (int jj = 0; jj < 4; ++jj) {
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x = fmaf(kv[e], qr[jj][e], x);
+        a[jj] = group_sum(x, LPR);
+      }
+      if (part == 0 && pt < t1) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (jb + jj < grp) scr[(jb + jj) * sstride + (pt - t0)] = a[jj] * qk_scale;
       }
     }
   }
   __syncthreads();
+  mark(P, sc, ti, 4);
   // ---- softmax statistics: one wave per head ----
   for (int j = wave; j < grp; j += kWaves) {
     float m = -INFINITY;
@@ -692,65 +756,63 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     if (lane == 0) { small[j] = m; small[8 + j] = sum; }
   }
   __syncthreads();
-  // ---- P.V: each lane accumulates its EPL dimensions of up to 4 heads at a time ----
-  const bool reload = nbw > NB;  // rows beyond the first batch were overwritten: reload batch 0
+  // ---- P.V: each lane accumulates its EPL dimensions for four heads at a time; the rows of one
+  // wave instruction are summed in registers, the eight waves' partials in LDS ----
   for (int jb = 0; jb < grp; jb += 4) {
     float acc[4][EPL];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[jj][e] = 0.f;
-    for (int ib = 0; ib < nbw; ib += NB) {
-      if (reload || jb > 0) load_batch(ib, true);
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int pt = row_of(ib + i);
-        if (ib + i < nbw && pt < t1) {
-          float vv[EPL];
-          decode_chunk<KVDT>(vb[i], vv);
+    for (int i = 0; i < NB; ++i) {
+      const int pt = row_of(i);
+      const bool valid = pt < t1;
+      const int idx = valid ? pt - t0 : 0;
+      float pr[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            if (jb + jj < grp) {
-              const float pr = scr[(jb + jj) * sstride + (pt - t0)] * vscale;
-#pragma unroll
-              for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr, vv[e], acc[jj][e]);
-            }
-          }
-        }
+      for (int jj = 0; jj < 4; ++jj) {
+        const float v = scr[(jb + jj < grp ? jb + jj : 0) * sstride + idx];
+        pr[jj] = valid && jb + jj < grp ? v * vscale : 0.f;
       }
+      float vv[EPL];
+      decode_chunk<KVDT>(vb[i], vv);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr[jj], vv[e], acc[jj][e]);
     }
-    // reduce over the RPI rows of a wave instruction (lanes with the same `part`)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float v = acc[jj][e];
-        for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
-        acc[jj][e] = v;
-      }
+      for (int e = 0; e < EPL; ++e) acc[jj][e] = column_sum(acc[jj][e], LPR);
     if (sub == 0) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        if (jb + jj < grp)
+        if (jb + jj < grp) {
+          float* dst = red + ((int64_t)wave * grp + jb + jj) * hd + part * EPL;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) red[(wave * grp + jb + jj) * hd + part * EPL + e] = acc[jj][e];
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(dst + e) = make_float4(acc[jj][e], acc[jj][e + 1], acc[jj][e + 2], acc[jj][e + 3]);
+        }
     }
   }
   __syncthreads();
-  float* partp = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * (hd + 2);
+  float* partp = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * PSTR;
   for (int i = tid; i < grp * hd; i += kThreads) {
-    const int j = i / hd, d = i % hd;
-    float s = 0.f;
+    float s8[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += red[(w * grp + j) * hd + d];
-    stc(partp + (int64_t)j * (hd + 2) + 2 + d, s);
+    for (int w = 0; w < kWaves; ++w) s8[w] = red[(int64_t)w * grp * hd + i];
+    const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    stc(partp + i / hd * PSTR + 4 + i % hd, s);
   }
   if (tid < grp) {
-    stc(partp + (int64_t)tid * (hd + 2), n > 0 ? small[tid] : -INFINITY);
-    stc(partp + (int64_t)tid * (hd + 2) + 1, n > 0 ? small[8 + tid] : 0.f);
+    stc(partp + (int64_t)tid * PSTR, n > 0 ? small[tid] : -INFINITY);
+    stc(partp + (int64_t)tid * PSTR + 1, n > 0 ? small[8 + tid] : 0.f);
   }
   drain();
   __syncthreads();
+  mark(P, sc, ti, 5);
   // ---- ticket: the last split of this head group combines ----
   int* last = reinterpret_cast<int*>(small + 32);
   if (tid == 0) {
@@ -758,47 +820,45 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     *last = (int)(old % (uint32_t)S) == S - 1;
   }
   __syncthreads();
+  mark(P, sc, ti, 6);
   if (!*last) return;
-  // all partials of the head group (S x grp x (hd+2) floats) in one batch of coherent loads
-  const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * (hd + 2);
-  const int ntot = S * grp * (hd + 2);  // even: hd + 2 is even
-  float* pl = lds;                      // [S][grp][hd+2]
-  float* wts = lds + ntot;              // [grp][S]
-  for (int i0 = 2 * tid; i0 < ntot; i0 += 8 * kThreads) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 2 * kThreads;
-      v[u] = i < ntot ? ldc2(pg + i) : make_float2(0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 2 * kThreads;
-      if (i < ntot) { pl[i] = v[u].x; pl[i + 1] = v[u].y; }
-    }
-  }
+  // all partials of the head group (S x grp x (hd+4) floats) in one batch of coherent loads
+  const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * PSTR;
+  const int ntot = S * grp * PSTR;
+  const int npad = (ntot + 3) & ~3;
+  float* pl = lds;              // [S][grp][hd+4]
+  float* wts = lds + npad;      // [grp][S]
+  load_vector<false>(pg, ntot, npad, pl);
   __syncthreads();
-  for (int j = tid; j < grp; j += kThreads) {
+  for (int j = wave; j < grp; j += kWaves) {
     float M = -INFINITY;
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, pl[(s2 * grp + j) * (hd + 2)]);
+    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, pl[(s2 * grp + j) * PSTR]);
+    M = wave_max(M);
     float den = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float m = pl[(s2 * grp + j) * (hd + 2)];
+    for (int s2 = lane; s2 < S; s2 += 64) {
+      const float m = pl[(s2 * grp + j) * PSTR];
       const float w = m == -INFINITY ? 0.f : expf(m - M);
       wts[j * S + s2] = w;
-      den += w * pl[(s2 * grp + j) * (hd + 2) + 1];
+      den += w * pl[(s2 * grp + j) * PSTR + 1];
     }
+    den = wave_sum_shfl(den);
     const float inv = 1.0f / den;
-    for (int s2 = 0; s2 < S; ++s2) wts[j * S + s2] *= inv;
+    for (int s2 = lane; s2 < S; s2 += 64) wts[j * S + s2] *= inv;
   }
   __syncthreads();
   float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
   for (int i = tid; i < grp * hd; i += kThreads) {
     const int j = i / hd, d = i % hd;
-    float s = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) s = fmaf(wts[j * S + s2], pl[(s2 * grp + j) * (hd + 2) + 2 + d], s);
-    stc(o + i, s);
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    int s2 = 0;
+    for (; s2 + 4 <= S; s2 += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s4[k] = fmaf(wts[j * S + s2 + k], pl[((s2 + k) * grp + j) * PSTR + 4 + d], s4[k]);
+    }
+    for (; s2 < S; ++s2) s4[0] = fmaf(wts[j * S + s2], pl[(s2 * grp + j) * PSTR + 4 + d], s4[0]);
+    stc(o + i, (s4[0] + s4[1]) + (s4[2] + s4[3]));
   }
+  mark(P, sc, ti, 7);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
@@ -815,17 +875,21 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
-    if (l == 0) {
-      const int tok = input_token(P, sc);
-      for (int i = threadIdx.x; i < R; i += kThreads) res[i] = dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i]);
-    } else {
-      for (int i = threadIdx.x; i < R; i += kThreads) res[i] = ldc(P.x + (int64_t)l * P.H + t.a0 + i);
-    }
-    stage_copy(P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    const int tok = l == 0 ? input_token(P, sc) : 0;
+    float rv = 0.f;  // first kThreads residual rows ride with the input loads
+    if ((int)threadIdx.x < R)
+      rv = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + threadIdx.x]) : ldc(P.x + (int64_t)l * P.H + t.a0 + threadIdx.x);
+    for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
+      res[i] = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i]) : ldc(P.x + (int64_t)l * P.H + t.a0 + i);
+    load_vector<false>(P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
+    __syncthreads();
+    mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
@@ -844,12 +908,14 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
     maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm<WBF16>(P.xm + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H + H, H,
                          pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+    mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
   auto srow = [&](int r) -> const float* {
     return fp8_rows<WDT>(P, l, (r & 1) ? 5 : 4) + (int64_t)((r >> 1) / 128) * nbc;
   };
   gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  mark(P, sc, ti, 5);
   const int npairs = (t.a1 - t.a0) >> 1;
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
     const float gte = y[2 * p], up = y[2 * p + 1];
@@ -870,12 +936,18 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_d;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
-    for (int i = threadIdx.x; i < R; i += kThreads) res[i] = ldc(P.xm + (int64_t)l * P.H + t.a0 + i);
-    stage_copy(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    float rv = 0.f;
+    if ((int)threadIdx.x < R) rv = ldc(P.xm + (int64_t)l * P.H + t.a0 + threadIdx.x);
+    for (int i = threadIdx.x + kThreads; i < R; i += kThreads) res[i] = ldc(P.xm + (int64_t)l * P.H + t.a0 + i);
+    load_vector<false>(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
+    __syncthreads();
+    mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 6) + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
@@ -908,10 +980,12 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+    mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
   auto srow = [&](int r) -> const float* { return P.sc_lm + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  mark(P, sc, ti, 5);
   unsigned long long key = 0ull;
   bool nan_seen = false;
   for (int i = threadIdx.x; i < R; i += kThreads) {

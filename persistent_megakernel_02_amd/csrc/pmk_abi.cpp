@@ -193,10 +193,10 @@ void compute_layout(pmk_ctx* c) {
   c->w_x = w; w = align256(w + (L + 1) * H * 4);
   c->w_xm = w; w = align256(w + L * H * 4);
   c->w_q = w; w = align256(w + L * qd * 4);
-  c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 2) * 4);
+  c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 4) * 4);
   c->w_o = w; w = align256(w + L * qd * 4);
   c->w_h = w; w = align256(w + L * F * 4);
-  c->w_trace = w; w = align256(w + (int64_t)std::max(0, c->sc.trace_steps) * NT * 32);
+  c->w_trace = w; w = align256(w + (int64_t)std::max(0, c->sc.trace_steps) * NT * 64);
   c->w_tasks = w; w = align256(w + NT * (int64_t)sizeof(pmk_task));
   c->w_qoff = w; w = align256(w + ((int64_t)s.n_queues + 1) * 4);
   c->w_qtasks = w; w = align256(w + NT * 4);
@@ -210,7 +210,7 @@ void compute_layout(pmk_ctx* c) {
   const int64_t S = s.attn_splits, grp = m.grp();
   const int64_t chunk = (m.max_seq + S - 1) / S;
   const int64_t attn = grp * m.hd + grp * ((chunk + 3) & ~3ll) + kWaves * grp * m.hd;
-  const int64_t comb = S * grp * (m.hd + 2) + grp * S;
+  const int64_t comb = S * grp * (m.hd + 4) + grp * S + 4;
   const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn, comb});
   c->xs_floats = (int)((xs + 63) / 64 * 64);
   // epilogue inputs staged behind the scratch words: the RoPE row (+ fp8 K/V scales) of QKV tasks,
@@ -653,6 +653,10 @@ pmk_status pmk_poll_error(pmk_ctx* c, pmk_device_error* err) {
 pmk_status pmk_set_trace(pmk_ctx* c, int32_t on) {
   if (!c) return PMK_ERR_INVALID_ARG;
   if (on && c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "the schedule has no trace buffer (trace_steps = 0)");
+  if (on && c->bound) {
+    HIPCHK(c, hipSetDevice(c->device));
+    HIPCHK(c, hipMemset(c->ws + c->w_trace, 0, (size_t)c->sc.trace_steps * c->sched.tasks.size() * 64));
+  }
   c->trace_on = on ? 1 : 0;
   return PMK_OK;
 }
@@ -662,7 +666,7 @@ static pmk_status read_trace(pmk_ctx* c, std::vector<unsigned long long>& t) {
   if (s != PMK_OK) return s;
   if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "no trace buffer");
   HIPCHK(c, hipDeviceSynchronize());
-  t.resize((size_t)c->sc.trace_steps * c->sched.tasks.size() * 4);
+  t.resize((size_t)c->sc.trace_steps * c->sched.tasks.size() * 8);
   HIPCHK(c, hipMemcpy(t.data(), c->ws + c->w_trace, t.size() * 8, hipMemcpyDeviceToHost));
   return PMK_OK;
 }
@@ -678,7 +682,7 @@ pmk_status pmk_trace_stats(pmk_ctx* c, double* wait_share, double* step_us) {
     unsigned long long lo = ~0ull, hi = 0;
     bool any = false;
     for (size_t i = 0; i < NT; ++i) {
-      const unsigned long long* r = &t[((size_t)st * NT + i) * 4];
+      const unsigned long long* r = &t[((size_t)st * NT + i) * 8];
       if (!r[0] || !r[2] || r[2] < r[0]) continue;
       any = true;
       const unsigned long long t1 = (r[1] >= r[0] && r[1] <= r[2]) ? r[1] : r[0];
@@ -704,20 +708,22 @@ pmk_status pmk_trace_export(pmk_ctx* c, const char* path) {
   static const char* names[] = {"?", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "token"};
   const size_t NT = c->sched.tasks.size();
   unsigned long long t0 = ~0ull;
-  for (size_t i = 0; i < t.size(); i += 4)
+  for (size_t i = 0; i < t.size(); i += 8)
     if (t[i]) t0 = std::min(t0, t[i]);
   std::fprintf(f, "{\"traceEvents\":[\n");
   bool first = true;
   for (int st = 0; st < c->sc.trace_steps; ++st)
     for (size_t i = 0; i < NT; ++i) {
-      const unsigned long long* r = &t[((size_t)st * NT + i) * 4];
+      const unsigned long long* r = &t[((size_t)st * NT + i) * 8];
       if (!r[0] || !r[2]) continue;
       const pmk_task& k = c->sched.tasks[i];
       const unsigned long long t1 = (r[1] >= r[0] && r[1] <= r[2]) ? r[1] : r[0];
       std::fprintf(f, "%s{\"name\":\"wait\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}", first ? "" : ",\n",
                    st, r[3], (r[0] - t0) * 0.01, (t1 - r[0]) * 0.01);
-      std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}",
-                   names[k.op >= 1 && k.op <= 7 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01);
+      std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f,\"args\":{\"m4\":%.2f,\"m5\":%.2f,\"m6\":%.2f,\"m7\":%.2f}}",
+                   names[k.op >= 1 && k.op <= 7 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01,
+                   r[4] >= t1 ? (r[4] - t1) * 0.01 : -1.0, r[5] >= t1 ? (r[5] - t1) * 0.01 : -1.0,
+                   r[6] >= t1 ? (r[6] - t1) * 0.01 : -1.0, r[7] >= t1 ? (r[7] - t1) * 0.01 : -1.0);
       first = false;
     }
   std::fprintf(f, "\n]}\n");

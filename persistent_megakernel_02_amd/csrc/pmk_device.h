@@ -67,7 +67,7 @@ struct KParams {
   float* x;               // [L+1][H]
   float* xm;              // [L][H]
   float* q;               // [L][qdim]
-  float* part;            // [L][nkv][S][grp][hd+2]
+  float* part;            // [L][nkv][S][grp][hd+4]: m, l, 2 pad, acc[hd]
   float* o;               // [L][qdim]
   float* h;               // [L][F]
   unsigned long long* trace;  // [trace_steps][n_tasks][4]

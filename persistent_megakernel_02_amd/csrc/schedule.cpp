@@ -52,6 +52,12 @@ void split_range(int n, int parts, int i, int* lo, int* hi) {
 
 }  // namespace
 
+int attn_max_chunk(const ModelDims& m) {
+  const int rowbytes = m.hd * (m.kvdt == PMK_DT_FP8_E4M3 ? 1 : 2);
+  const int rpi = 64 / (rowbytes / 16);
+  return 64 * rpi;
+}
+
 // ================================================================================================
 // Builder
 // ================================================================================================
@@ -65,9 +71,15 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   if (S <= 0) {
     S = std::max(1, n_queues / m.nkv);
     S = std::min(S, std::max(1, m.max_seq / 16));
-    // the last split's combine stages every partial (S x grp x (hd + 2) floats) in LDS
-    S = std::min(S, std::max(1, 32000 / (m.grp() * (m.hd + 3))));
+    // the last split's combine stages every partial (S x grp x (hd + 4) floats) in LDS
+    S = std::min(S, std::max(1, 32000 / (m.grp() * (m.hd + 5))));
   }
+  // each split's rows must fit the attention task's register batch: 8 waves x 8 row blocks of
+  // RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) <= 64 * RPI
+  const int max_chunk = attn_max_chunk(m);
+  S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
+  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > 36000)
+    return "builder: the context is too long for the attention combine's LDS budget";
   s.attn_splits = S;
   s.queues.assign(n_queues, {});
 
@@ -332,6 +344,8 @@ std::string validate_schedule(const Schedule& s) {
     if (k.op == PMK_OP_ATTN) attn_groups[{k.signal_ctr, k.signal_slot}].push_back(t);
     else producers[k.signal_ctr].push_back(t);
   }
+  if ((m.max_seq + S - 1) / S > attn_max_chunk(m))
+    return fmt("thresholds: %ld attention splits leave chunks longer than the %ld rows a task holds", S, attn_max_chunk(m));
   for (auto& kv : attn_groups) {
     if (!producers[kv.first.first].empty())
       return fmt("thresholds: counter %ld mixes combine and task signals", kv.first.first);

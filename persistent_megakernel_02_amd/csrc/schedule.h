@@ -45,6 +45,9 @@ struct Schedule {
   std::vector<int> c_qkv, c_cmb, c_oproj, c_gu, c_down;
 };
 
+// Longest attention split (positions) one task holds in registers.
+int attn_max_chunk(const ModelDims& m);
+
 // Builder: lowers the model into per-queue task lists (one decode step; the kernel repeats it).
 std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out);
 
