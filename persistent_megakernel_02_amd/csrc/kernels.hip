@@ -113,30 +113,6 @@ __device__ __forceinline__ float wave_sum_shfl(float v) {
   return v;
 }
 
-// block sum (all threads get the result); `red` holds >= kWaves floats of LDS
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum_shfl(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) t += red[i];
-  return t;
-}
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) t = fmaxf(t, red[i]);
-  return t;
-}
-
 // ------------------------------------------------------------------------------------------------
 // storage formats
 // ------------------------------------------------------------------------------------------------
@@ -198,13 +174,16 @@ __device__ __noinline__ void wave_wait(uint32_t* ctrl, const uint32_t* word, int
                                        int counters_mode, int64_t spin_limit, int cu, int task, int ctr) {
   const int lane = threadIdx.x & 63;
   int64_t spins = 0;
+  // Every poll issues all of its loads (the watched words and the abort word) before it waits for
+  // any of them, so one poll costs one memory round trip.
   if (counters_mode) {
     const int64_t need = (int64_t)(e - lag) * prod + count;
     if (need <= 0) return;
     while (true) {
+      const uint32_t ab = ldc(&ctrl[CTRL_ABORT]);
       const uint32_t v = ldc(word);
       if ((int64_t)v >= need) return;
-      if (ldc(&ctrl[CTRL_ABORT])) return;
+      if (ab) return;
       if (++spins > spin_limit) {
         if (lane == 0) report_error(ctrl, PMK_ERR_TIMEOUT, cu, task, ctr, (uint32_t)need, v);
         return;
@@ -213,15 +192,26 @@ __device__ __noinline__ void wave_wait(uint32_t* ctrl, const uint32_t* word, int
   } else {
     const int target = e - lag + 1;
     if (target <= 0) return;
+    constexpr int MW = 8;  // flag words per lane in one batch (512 producers per round trip)
+    // the address is wave uniform: move it to scalar registers so the resource is too
+    const uint64_t wa = (uint64_t)word;
+    const uint64_t wu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wa) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(wa >> 32)) << 32);
+    const int produ = __builtin_amdgcn_readfirstlane(prod);
+    const __amdgpu_buffer_rsrc_t r = coherent_rsrc((const void*)wu, (uint32_t)produ * 4);  // words past prod read 0
     while (true) {
+      const uint32_t ab = ldc(&ctrl[CTRL_ABORT]);
       int have = 0;
-      for (int base = 0; base < prod; base += 64) {
-        const int i = base + lane;
-        const bool ok = i < prod && (int)ldc(&word[i]) >= target;
-        have += __popcll(__ballot(ok));
+      for (int base = 0; base < prod; base += 64 * MW) {
+        uint32_t v[MW];
+#pragma unroll
+        for (int k = 0; k < MW; ++k)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(base + k * 64 + lane) * 4, 0, 16);
+#pragma unroll
+        for (int k = 0; k < MW; ++k) have += __popcll(__ballot((int)v[k] >= target));
       }
       if (have >= count) return;
-      if (ldc(&ctrl[CTRL_ABORT])) return;
+      if (ab) return;
       if (++spins > spin_limit) {
         if (lane == 0) report_error(ctrl, PMK_ERR_TIMEOUT, cu, task, ctr, (uint32_t)target, (uint32_t)have);
         return;
@@ -299,7 +289,18 @@ __device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x)
   }
 }
 
-constexpr int kRing = 8;
+// register ring depth (16-byte weight loads in flight per lane); fp8 slots also carry a block scale
+#ifndef PMK_RING_UNITS
+#define PMK_RING_UNITS 10
+#endif
+template <int WDT>
+constexpr int ring_depth() { return WDT == WFP8 && PMK_RING_UNITS > 16 ? 16 : PMK_RING_UNITS; }
+// of which issued before a task's dependency wait
+#ifndef PMK_PREFETCH_UNITS
+#define PMK_PREFETCH_UNITS 10
+#endif
+template <int WDT>
+constexpr int prefetch_depth() { return PMK_PREFETCH_UNITS < ring_depth<WDT>() ? PMK_PREFETCH_UNITS : ring_depth<WDT>(); }
 constexpr int kAttnBlocks = 8;  // attention row blocks per wave (see the builder's split bound)
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
@@ -318,13 +319,14 @@ __device__ __forceinline__ int choose_ks(int rows, int nsl) {
 // On return (after a workgroup barrier) y[r - r0] holds row r's fp32 dot product.  yp is LDS
 // scratch of 8 * (r1 - r0) floats for the per-slice partial sums (summed in slice order).
 // A lane reads 16-byte chunks c = j*64 + lane of a row (slice j), so one wave instruction streams
-// 1 KiB.  Weight loads run through a ring of kRing registers per lane; the first kRing are issued
-// BEFORE the dependency wait (weights do not depend on it); each consumed slot is refilled with
-// the chunk kRing units ahead.  Past the end the refill re-reads the tile's first chunk (a cache
-// hit) so that the load sequence stays branch free.  The loop issues no other global load.
+// 1 KiB.  Weight loads run through a ring of kRing registers per lane (10 x 16 B: 80 KiB in flight
+// per workgroup; measured on the 8B-class decode, deeper rings stream more slowly and shallower
+// ones cannot cover the latency); the first kPre (the whole ring by default) are issued BEFORE the
+// dependency wait (weights do not depend on it); each consumed slot is refilled with the chunk
+// kRing units ahead, until the wave's units are all issued.  The loop issues no other global load.
 template <int WDT, class Sync, class ScaleRow>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, int r0, int r1, const float* xs,
-                                          float* yp, float* y, Sync sync, ScaleRow srow) {
+                                          float* yp, float* y, bool prefetch, Sync sync, ScaleRow srow) {
   constexpr int EPL = WFmt<WDT>::EPL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
@@ -336,37 +338,51 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   const int s0 = (int)((int64_t)nsl * si / KS), s1 = (int)((int64_t)nsl * (si + 1) / KS);
   const int nunits = (wr1 - wr0) * (s1 - s0);
 
+  constexpr int kRing = ring_depth<WDT>();
   u32x4 ring[kRing];
   float rsc[kRing];
+  // The tile's rows go through a buffer resource: an offset past the tile (units after the wave's
+  // last one, the unused lanes of a partial last slice) reads zeros without touching memory, so
+  // no loaded value is ever selected on and every load stays in flight until it is consumed.
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(W + (int64_t)r0 * rb), (short)0, (int)((int64_t)R * rb), 0x00020000);
+  constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;  // past any tile the validator accepts
   int lrow = wr0, lj = s0;
-  const uint8_t* safe = W + (int64_t)r0 * rb;
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
     const bool ok = lrow < wr1 && c < nch;
-    const uint8_t* p = ok ? W + (int64_t)lrow * rb + (int64_t)c * 16 : safe;
-    u32x4 v = ld_nt(p);
-    ring[d] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (WDT == WFP8) rsc[d] = ok ? srow(lrow)[c >> 3] : 0.f;
+    const uint32_t off = ok ? (uint32_t)((int64_t)(lrow - r0) * rb + (int64_t)c * 16) : kOut;
+    ring[d] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nontemporal
+    if constexpr (WDT == WFP8) rsc[d] = srow(lrow < wr1 ? lrow : wr0)[(c < nch ? c : 0) >> 3];
     if (++lj == s1) { lj = s0; ++lrow; }
   };
-  if (nunits > 0) {
+  // kPre units per lane are issued before the dependency wait (when prefetching), the rest of the
+  // ring after it: loads leave a workgroup in issue order, so a deep pre-wait backlog would delay
+  // the wait's polls and the input staging behind it.  Both branches issue the same number of
+  // loads, which keeps the compiler's load counting exact for the first pass of the ring.
+  constexpr int kPre = prefetch_depth<WDT>();
+  if (prefetch) {
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) issue(d);
+    for (int d = 0; d < kPre; ++d) issue(d);
+    sync();
+  } else {
+    sync();
+#pragma unroll
+    for (int d = 0; d < kPre; ++d) issue(d);
   }
-  sync();
+#pragma unroll
+  for (int d = kPre; d < kRing; ++d) issue(d);
   if (nunits > 0) {
     float acc = 0.f;
     int crow = wr0, cj = s0;
     for (int base = 0; base < nunits; base += kRing) {
 #pragma unroll
       for (int d = 0; d < kRing; ++d) {
-        const u32x4 w = ring[d];
-        float sc = 1.f;
-        if constexpr (WDT == WFP8) sc = rsc[d];
-        issue(d);
+        // consume slot d, then refill it: the refill lands in the slot's own registers, so the
+        // ring never needs copying (a copy would have to wait for every load in flight)
         if (base + d < nunits) {
-          const float part = chunk_dot<WDT>(w, xs + (cj * 64 + lane) * EPL);
-          if constexpr (WDT == WFP8) acc = fmaf(part, sc, acc);
+          const float part = chunk_dot<WDT>(ring[d], xs + (cj * 64 + lane) * EPL);
+          if constexpr (WDT == WFP8) acc = fmaf(part, rsc[d], acc);
           else acc += part;
           if (++cj == s1) {
             cj = s0;
@@ -376,6 +392,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
             ++crow;
           }
         }
+        issue(d);
       }
     }
   }
@@ -392,44 +409,54 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
 // input staging (RMSNorm prologue fused into the consuming GEMV)
 // ------------------------------------------------------------------------------------------------
 // Load n fp32 values from a coherent buffer into xs[0..pad) (zeros past n), every load of a
-// batch issued before any is consumed.  Returns the sum of squares of the loaded values when
-// `want_ss` (thread partial).
-template <bool want_ss>
-__device__ __forceinline__ float load_vector(const float* src, int n, int pad, float* xs) {
+// batch issued before any is consumed.  With `gain` (a plain fp32 array of n values, loaded in the
+// same batch) the stored values are src * gain.  Returns the thread's partial sum of squares of
+// the unscaled src values when `want_ss`.
+template <bool want_ss, int B = 8>
+__device__ __forceinline__ float load_vector(const float* src, int n, int pad, float* xs, const float* gain = nullptr) {
   const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 4);
-  constexpr int B = 8;
   float ss = 0.f;
   for (int base = 0; base < pad; base += B * 4 * kThreads) {
     u32x4 v[B];
+    float4 g[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
       v[k] = i < pad ? ldc16(r, (uint32_t)i * 4) : u32x4{0u, 0u, 0u, 0u};
+      if (gain) g[k] = i < n ? *reinterpret_cast<const float4*>(gain + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
       if (i < pad) {
-        const float4 f = as_f4(v[k]);
-        *reinterpret_cast<float4*>(xs + i) = f;
+        float4 f = as_f4(v[k]);
         if (want_ss) ss = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, ss))));
+        if (gain) f = make_float4(f.x * g[k].x, f.y * g[k].y, f.z * g[k].z, f.w * g[k].w);
+        *reinterpret_cast<float4*>(xs + i) = f;
       }
     }
   }
   return ss;
 }
 
-// xs[0..H) = rmsnorm(src) * gain, xs[H..pad) = 0.  src is either a coherent fp32 vector or (emb != null)
-// a 16-bit embedding row.
+// RMSNorm prologue, split in two.  stage_rmsnorm writes xs[0..H) = src * gain (xs[H..pad) = 0)
+// and red[w] = wave w's share of sum(src^2), with one batch of loads and one barrier; the factor
+// 1/sqrt(mean(src^2) + eps) (rms_factor) then scales the GEMV results, since every row's dot
+// product with (src * gain) times that factor is its dot product with the normalised input.
+// src is either a coherent fp32 vector or (emb != null) a 16-bit embedding row.
 template <int EDT>
 __device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* emb, const float* gain, int H, int pad,
-                                              float eps, float* xs, float* red) {
+                                              float* xs, float* red) {
   float ss = 0.f;
   if (emb) {
     for (int i = 8 * threadIdx.x; i < pad; i += 8 * kThreads) {
-      float f[8];
+      float f[8], g[8];
       if (i < H) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(emb + i);
+        const float4 g0 = *reinterpret_cast<const float4*>(gain + i);
+        const float4 g1 = *reinterpret_cast<const float4*>(gain + i + 4);
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
         const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -438,21 +465,27 @@ __device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* 
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) f[k] = 0.f;
+        for (int k = 0; k < 8; ++k) f[k] = g[k] = 0.f;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        xs[i + k] = f[k];
+        xs[i + k] = f[k] * g[k];
         ss = fmaf(f[k], f[k], ss);
       }
     }
   } else {
-    ss = load_vector<true>(src, H, pad, xs);
+    ss = load_vector<true>(src, H, pad, xs, gain);
   }
-  ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int i = threadIdx.x; i < H; i += kThreads) xs[i] = (xs[i] * r) * gain[i];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
+}
+
+__device__ __forceinline__ float rms_factor(const float* red, int H, float eps) {
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  return 1.0f / sqrtf(t / (float)H + eps);
 }
 
 // xs[0..n) = src (coherent), zero padding
@@ -525,20 +558,21 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
   float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_qkv;
   auto sync = [&]() {
-    maybe_wait(P, t, sc, cu, ti);
-    // half <= 64 < kThreads and 2 * nkv <= kThreads: one value per thread, loaded with the input
+    // the RoPE row of this position and the K/V scales do not depend on the wait: loaded before it
+    // (half <= 64 < kThreads and 2 * nkv <= kThreads: one value per thread)
     const float2 cs = threadIdx.x < half ? P.rope[(int64_t)sc.pos * half + threadIdx.x] : make_float2(0.f, 0.f);
     float ks8 = 0.f;
     if constexpr (KVDT == WFP8)
       if (threadIdx.x < 2 * P.nkv) ks8 = P.kv_scale[(int64_t)l * P.nkv * 2 + threadIdx.x];
+    maybe_wait(P, t, sc, cu, ti);
     if (threadIdx.x < half) rope[threadIdx.x] = cs;
     if constexpr (KVDT == WFP8)
       if (threadIdx.x < 2 * P.nkv) rope[half + threadIdx.x] = make_float2(ks8, 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
-      stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, P.eps, xs, red);
+      stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
     } else {
-      stage_rmsnorm<EDT>(P.x + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H, H, pad, P.eps, xs, red);
+      stage_rmsnorm<EDT>(P.x + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H, H, pad, xs, red);
     }
     mark(P, sc, ti, 4);
   };
@@ -553,12 +587,13 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     const int dim = (pr >> 1) + (pr & 1) * half;
     return fp8_rows<WDT>(P, l, which) + (int64_t)((head * hd + dim) / 128) * nbc;
   };
-  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
+  const float rn = rms_factor(red, H, P.eps);
   const int npairs = (t.a1 - t.a0) >> 1;
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
     const int r = t.a0 + 2 * p;
-    float a = y[2 * p], b = y[2 * p + 1];
+    float a = y[2 * p] * rn, b = y[2 * p + 1] * rn;
     int sec, base;
     if (r < qrows) { sec = 0; base = 0; }
     else if (r < qrows + krows) { sec = 1; base = qrows; }
@@ -656,6 +691,9 @@ __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
 // LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
 // row block b of the chunk goes to wave b % 8.  Rows of past positions are loaded before the
 // dependency wait; the current position's row (written this step) after it, coherently.
+// 16-byte loads per thread that bring every partial of a head group into LDS in one batch
+constexpr int kCombineBatch = (kCombineMaxFloats + 4 * kThreads - 1) / (4 * kThreads);
+
 template <int KVDT>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
@@ -687,6 +725,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     vscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2 + 1];
   }
   auto row_of = [&](int i) { return t0 + (wave + kWaves * i) * RPI + sub; };  // position of register slot i
+  const int nbu = (n + kWaves * RPI - 1) / (kWaves * RPI);  // register slots that hold rows (block uniform)
   // rows of past positions: loaded before the dependency wait
   u32x4 kb[NB], vb[NB];
 #pragma unroll
@@ -721,6 +760,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       for (int e = 0; e < EPL; ++e) qr[jj][e] = jb + jj < grp ? qs[(jb + jj) * hd + part * EPL + e] : 0.f;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
+      if (i >= nbu) break;
       const int pt = row_of(i);
       float kv[EPL];
       decode_chunk<KVDT>(kb[i], kv);
@@ -766,6 +806,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       for (int e = 0; e < EPL; ++e) acc[jj][e] = 0.f;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
+      if (i >= nbu) break;
       const int pt = row_of(i);
       const bool valid = pt < t1;
       const int idx = valid ? pt - t0 : 0;
@@ -828,7 +869,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   const int npad = (ntot + 3) & ~3;
   float* pl = lds;              // [S][grp][hd+4]
   float* wts = lds + npad;      // [grp][S]
-  load_vector<false>(pg, ntot, npad, pl);
+  load_vector<false, kCombineBatch>(pg, ntot, npad, pl);
   __syncthreads();
   for (int j = wave; j < grp; j += kWaves) {
     float M = -INFINITY;
@@ -888,7 +929,7 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -907,18 +948,19 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm<WBF16>(P.xm + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H + H, H,
-                         pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+                         pad_len(H, WFmt<WDT>::EPL), xs, red);
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
   auto srow = [&](int r) -> const float* {
     return fp8_rows<WDT>(P, l, (r & 1) ? 5 : 4) + (int64_t)((r >> 1) / 128) * nbc;
   };
-  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   const int npairs = (t.a1 - t.a0) >> 1;
+  const float rn = rms_factor(red, H, P.eps);
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
-    const float gte = y[2 * p], up = y[2 * p + 1];
+    const float gte = y[2 * p] * rn, up = y[2 * p + 1] * rn;
     stc(P.h + (int64_t)l * P.F + (t.a0 >> 1) + p, gte / (1.0f + expf(-gte)) * up);
   }
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -946,7 +988,7 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 6) + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, sync, srow);
+  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -979,17 +1021,18 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
   float* out_logits = P.call->out_logits;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
-    stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), P.eps, xs, red);
+    stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), xs, red);
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
   auto srow = [&](int r) -> const float* { return P.sc_lm + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, sync, srow);
+  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
+  const float rn = rms_factor(red, H, P.eps);
   unsigned long long key = 0ull;
   bool nan_seen = false;
   for (int i = threadIdx.x; i < R; i += kThreads) {
-    const float v = y[i];
+    const float v = y[i] * rn;
     if (v != v) nan_seen = true;
     const unsigned long long k = ((unsigned long long)orderable(v) << 32) | (0xFFFFFFFFu - (uint32_t)(t.a0 + i));
     key = k > key ? k : key;

@@ -142,7 +142,7 @@ pmk_schedule_config defaults(const pmk_schedule_config* s) {
   pmk_schedule_config d{};
   if (s) d = *s;
   if (d.spin_limit <= 0) d.spin_limit = 1ll << 22;
-  if (d.prefetch == 0) d.prefetch = 1;
+  d.prefetch = d.prefetch < 0 ? 0 : 1;
   return d;
 }
 

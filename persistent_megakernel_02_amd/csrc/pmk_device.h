@@ -4,6 +4,7 @@
 #include <cstdint>
 
 #include "../../include/pmk.h"
+#include "pmk_limits.h"
 
 namespace pmk {
 

@@ -9,6 +9,8 @@
 // monokernel tutorial": work is split over a fixed grid of CUs ahead of time.
 #include "schedule.h"
 
+#include "pmk_limits.h"
+
 #include <algorithm>
 #include <atomic>
 #include <chrono>
@@ -78,7 +80,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   // RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) <= 64 * RPI
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
-  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > 36000)
+  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > kCombineMaxFloats)
     return "builder: the context is too long for the attention combine's LDS budget";
   s.attn_splits = S;
   s.queues.assign(n_queues, {});
@@ -333,6 +335,11 @@ std::string validate_schedule(const Schedule& s) {
       if (k.a0 < 0 || k.a1 > lim || k.a0 >= k.a1) return fmt("integrity: task %ld row range [%ld,%ld) invalid", t, k.a0, k.a1);
       if ((k.op == PMK_OP_QKV || k.op == PMK_OP_GATEUP) && ((k.a0 | k.a1) & 1))
         return fmt("integrity: task %ld row range [%ld,%ld) splits a row pair", t, k.a0, k.a1);
+      // the GEMV addresses a tile with 32-bit offsets below kMaxTileBytes
+      const int64_t K = k.op == PMK_OP_DOWN ? m.F : (k.op == PMK_OP_OPROJ ? m.qdim() : m.H);
+      const int64_t es = m.wdt == PMK_DT_FP8_E4M3 ? 1 : 2;
+      if ((int64_t)(k.a1 - k.a0) * K * es > kMaxTileBytes)
+        return fmt("integrity: task %ld weight tile of %ld rows exceeds the GEMV's 32-bit offsets", t, k.a1 - k.a0);
     }
   }
   // ---- 2. thresholds and producer counts ----
@@ -346,6 +353,8 @@ std::string validate_schedule(const Schedule& s) {
   }
   if ((m.max_seq + S - 1) / S > attn_max_chunk(m))
     return fmt("thresholds: %ld attention splits leave chunks longer than the %ld rows a task holds", S, attn_max_chunk(m));
+  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > kCombineMaxFloats)
+    return fmt("thresholds: %ld attention splits exceed the combine's LDS budget", S);
   for (auto& kv : attn_groups) {
     if (!producers[kv.first.first].empty())
       return fmt("thresholds: counter %ld mixes combine and task signals", kv.first.first);
