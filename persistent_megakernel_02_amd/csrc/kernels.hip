@@ -104,13 +104,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Max over the 64 lanes with the same DPP row pattern as wave_sum; every lane receives it.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max(float a) {
+  const int x = __float_as_int(a);
+  return fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xF, false)));
 }
-__device__ __forceinline__ float wave_sum_shfl(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast15 -> rows 1,3
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast31 -> rows 2,3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -301,7 +308,6 @@ constexpr int ring_depth() { return WDT == WFP8 && PMK_RING_UNITS > 16 ? 16 : PM
 #endif
 template <int WDT>
 constexpr int prefetch_depth() { return PMK_PREFETCH_UNITS < ring_depth<WDT>() ? PMK_PREFETCH_UNITS : ring_depth<WDT>(); }
-constexpr int kAttnBlocks = 8;  // attention row blocks per wave (see the builder's split bound)
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
 // KS minimises the largest per-wave unit count (short tiles then still keep all waves streaming).
@@ -648,18 +654,6 @@ __device__ __forceinline__ float group_sum(float v, int n) {
   return v;
 }
 
-// Sum over the lanes that share `lane % n` (n = 8 or 16): the other half of the DPP row for n = 8,
-// then across the four rows with the gfx950 row-swap moves.  Every lane receives its column's sum.
-__device__ __forceinline__ float column_sum(float v, int n) {
-  if (n == 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
-  const uint32_t u = __float_as_uint(v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const uint32_t w = __float_as_uint(v);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
-
 template <int KVDT>
 __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
   if constexpr (KVDT == WFP8) {
@@ -683,42 +677,71 @@ __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
   }
 }
 
+// Sum / max over the lanes that share `lane % N` (N = 8 or 16 lanes per row): the other half of
+// the DPP row for N = 8, then across the four rows with the gfx950 row-swap moves.  Every lane
+// receives its column's result.
+template <int N>
+__device__ __forceinline__ float column_sum(float v) {
+  if constexpr (N == 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+template <int N>
+__device__ __forceinline__ float column_max(float v) {
+  if constexpr (N == 8)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// 16-byte loads per thread that bring every partial of a head group into LDS in one batch
+constexpr int kCombineBatch = (kCombineMaxFloats + 4 * kThreads - 1) / (4 * kThreads);
+
 // Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
 // query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
 // the last split to finish (atomic ticket) combines all splits of the group into o.
 // Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
 // The K and V chunks are contiguous ([pos][hd]) and are streamed with coalesced 16-byte loads:
 // LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
-// row block b of the chunk goes to wave b % 8.  Rows of past positions are loaded before the
-// dependency wait; the current position's row (written this step) after it, coherently.
-// 16-byte loads per thread that bring every partial of a head group into LDS in one batch
-constexpr int kCombineBatch = (kCombineMaxFloats + 4 * kThreads - 1) / (4 * kThreads);
-
-template <int KVDT>
+// row block b of the chunk goes to wave b % 8, register slot b / 8.  Rows of past positions are
+// loaded before the dependency wait; the current position's row (written this step) after it,
+// coherently, in the same round trip as q.
+// Inside the workgroup each wave runs its own softmax over its rows, in registers: scores, the
+// wave's max and sum per head (reduced across the rows of an instruction with column_max /
+// column_sum), probabilities and P.V; the eight waves' (max, sum, acc) are then merged in LDS with
+// the usual rescaling, exactly as the splits are merged by the combine.
+template <int KVDT, int HD>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
-  constexpr int EPL = 16 / KES;  // elements per 16-byte chunk
-  constexpr int NB = kAttnBlocks;  // row blocks per wave, all held in registers (the builder bounds the split)
-  const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp, hd = P.hd;
+  constexpr int EPL = 16 / KES;       // elements per 16-byte chunk
+  constexpr int NB = kAttnBlocks;     // row blocks per wave, all held in registers (the builder bounds the split)
+  constexpr int ROWB = HD * KES;      // row bytes: 128 or 256
+  constexpr int LPR = ROWB / 16;      // 8 or 16 lanes per row
+  constexpr int RPI = 64 / LPR;       // 8 or 4 rows per wave instruction
+  constexpr int PSTR = HD + 4;        // partial record: m, l, 2 pad, acc[hd] (16-byte aligned)
+  const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp;
   const int T = sc.pos + 1;
   const int chunk = (T + S - 1) / S;
   const int t0 = min(T, split * chunk), t1 = min(T, t0 + chunk);
   const int n = t1 - t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int PSTR = hd + 4;  // partial record: m, l, 2 pad, acc[hd] (16-byte aligned)
-  const int rowbytes = hd * KES;   // 128 or 256
-  const int LPR = rowbytes / 16;   // 8 or 16 lanes per row
-  const int RPI = 64 / LPR;        // 8 or 4 rows per wave instruction
   const int sub = lane / LPR, part = lane % LPR;
   const int64_t headbase = ((int64_t)l * P.nkv + g) * P.max_seq;
-  const uint8_t* Kc = P.kc + headbase * rowbytes;
-  const uint8_t* Vc = P.vc + headbase * rowbytes;
-  const int sstride = (n + 3) & ~3;
-  float* qs = lds;                      // [grp][hd]
-  float* scr = qs + grp * hd;           // [grp][sstride] scores, then probabilities
-  float* red = scr + grp * sstride;     // [kWaves][grp][hd] P.V partials of each wave
-  float* small = lds + P.xs_floats;     // [0, 8): m, [8, 16): l
+  const uint8_t* Kc = P.kc + headbase * ROWB;
+  const uint8_t* Vc = P.vc + headbase * ROWB;
+  float* qs = lds;                      // [grp][HD]
+  float* red = qs + grp * HD;           // [kWaves][grp][HD] per-wave P.V partials
+  float* wml = red + kWaves * grp * HD; // [kWaves][grp][2] per-wave (max, sum)
+  float* small = lds + P.xs_floats;     // ticket result
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
     kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
@@ -732,124 +755,141 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   for (int i = 0; i < NB; ++i) {
     const int pt = row_of(i);
     const bool ok = pt < t1 && pt != sc.pos;
-    const int64_t off = (int64_t)(ok ? pt : t0) * rowbytes + part * 16;
+    const int64_t off = (int64_t)(ok ? pt : t0) * ROWB + part * 16;
     kb[i] = ok ? ld_nt(Kc + off) : u32x4{0u, 0u, 0u, 0u};
     vb[i] = ok ? ld_nt(Vc + off) : u32x4{0u, 0u, 0u, 0u};
   }
   maybe_wait(P, t, sc, cu, ti);
-  load_vector<false>(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * hd, grp * hd, grp * hd, qs);
-  // the current position's rows, written in this step
-  if (n > 0) {
-    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(Kc + (int64_t)sc.pos * rowbytes, rowbytes);
-    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(Vc + (int64_t)sc.pos * rowbytes, rowbytes);
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      if (row_of(i) == sc.pos) {
-        kb[i] = ldc16(rk, part * 16);
-        vb[i] = ldc16(rv, part * 16);
-      }
+  // the current position's row (this split holds it when t0 <= pos < t1): issued with q's loads
+  const int rel = sc.pos - t0;
+  const bool cur_here = rel >= 0 && rel < n;
+  const int cur_slot = cur_here ? rel / RPI / kWaves : -1;
+  const bool cur_lane = cur_here && (rel / RPI) % kWaves == wave && rel % RPI == sub;
+  u32x4 kcur = u32x4{0u, 0u, 0u, 0u}, vcur = u32x4{0u, 0u, 0u, 0u};
+  if (cur_lane) {
+    kcur = ldc16(coherent_rsrc(Kc + (int64_t)sc.pos * ROWB, ROWB), part * 16);
+    vcur = ldc16(coherent_rsrc(Vc + (int64_t)sc.pos * ROWB, ROWB), part * 16);
   }
+  load_vector<false>(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD, grp * HD, qs);
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (cur_lane && i == cur_slot) {
+      kb[i] = kcur;
+      vb[i] = vcur;
+    }
   __syncthreads();
   const float qk_scale = kscale * P.attn_scale;
-  // ---- scores: q of this lane's dimensions in registers, four heads at a time, branch free ----
   for (int jb = 0; jb < grp; jb += 4) {
-    float qr[4][EPL];
+    // ---- scores of this lane's row in each slot, four heads at a time ----
+    float sco[NB][4];
+    {
+      float qr[4][EPL];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qr[jj][e] = jb + jj < grp ? qs[(jb + jj) * hd + part * EPL + e] : 0.f;
+        for (int e = 0; e < EPL; ++e) qr[jj][e] = jb + jj < grp ? qs[(jb + jj) * HD + part * EPL + e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i >= nbu) break;
-      const int pt = row_of(i);
-      float kv[EPL];
-      decode_chunk<KVDT>(kb[i], kv);
-      float a[4];
+      for (int i = 0; i < NB; ++i) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float x = 0.f;
+        for (int jj = 0; jj < 4; ++jj) sco[i][jj] = -INFINITY;
+        if (i < nbu) {
+          float kv[EPL];
+          decode_chunk<KVDT>(kb[i], kv);
+          const bool valid = row_of(i) < t1;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) x = fmaf(kv[e], qr[jj][e], x);
-        a[jj] = group_sum(x, LPR);
-      }
-      if (part == 0 && pt < t1) {
+          for (int jj = 0; jj < 4; ++jj) {
+            float x = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (jb + jj < grp) scr[(jb + jj) * sstride + (pt - t0)] = a[jj] * qk_scale;
+            for (int e = 0; e < EPL; ++e) x = fmaf(kv[e], qr[jj][e], x);
+            x = group_sum(x, LPR);
+            sco[i][jj] = valid ? x * qk_scale : -INFINITY;
+          }
+        }
       }
     }
-  }
-  __syncthreads();
-  mark(P, sc, ti, 4);
-  // ---- softmax statistics: one wave per head ----
-  for (int j = wave; j < grp; j += kWaves) {
-    float m = -INFINITY;
-    for (int tt = lane; tt < n; tt += 64) m = fmaxf(m, scr[j * sstride + tt]);
-    m = wave_max(m);
-    float sum = 0.f;
-    for (int tt = lane; tt < n; tt += 64) {
-      const float pr = expf(scr[j * sstride + tt] - m);
-      scr[j * sstride + tt] = pr;
-      sum += pr;
+    // ---- the wave's softmax statistics per head, probabilities in place of the scores ----
+    float mw[4], lw[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (i < nbu) m = fmaxf(m, sco[i][jj]);
+      m = column_max<LPR>(m);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (i < nbu) {
+          const float pr = m == -INFINITY ? 0.f : expf(sco[i][jj] - m);
+          sco[i][jj] = pr;
+          sum += pr;
+        }
+      mw[jj] = m;
+      lw[jj] = column_sum<LPR>(sum);  // one lane per row in each column
     }
-    sum = wave_sum_shfl(sum);
-    if (lane == 0) { small[j] = m; small[8 + j] = sum; }
-  }
-  __syncthreads();
-  // ---- P.V: each lane accumulates its EPL dimensions for four heads at a time; the rows of one
-  // wave instruction are summed in registers, the eight waves' partials in LDS ----
-  for (int jb = 0; jb < grp; jb += 4) {
+    // ---- P.V over the wave's rows ----
     float acc[4][EPL];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[jj][e] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i >= nbu) break;
-      const int pt = row_of(i);
-      const bool valid = pt < t1;
-      const int idx = valid ? pt - t0 : 0;
-      float pr[4];
+    for (int i = 0; i < NB; ++i)
+      if (i < nbu) {
+        float vv[EPL];
+        decode_chunk<KVDT>(vb[i], vv);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float v = scr[(jb + jj < grp ? jb + jj : 0) * sstride + idx];
-        pr[jj] = valid && jb + jj < grp ? v * vscale : 0.f;
+        for (int jj = 0; jj < 4; ++jj) {
+          const float pr = sco[i][jj] * vscale;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr, vv[e], acc[jj][e]);
+        }
       }
-      float vv[EPL];
-      decode_chunk<KVDT>(vb[i], vv);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr[jj], vv[e], acc[jj][e]);
-    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[jj][e] = column_sum(acc[jj][e], LPR);
+      for (int e = 0; e < EPL; ++e) acc[jj][e] = column_sum<LPR>(acc[jj][e]);
     if (sub == 0) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         if (jb + jj < grp) {
-          float* dst = red + ((int64_t)wave * grp + jb + jj) * hd + part * EPL;
+          float* dst = red + ((int64_t)wave * grp + jb + jj) * HD + part * EPL;
 #pragma unroll
           for (int e = 0; e < EPL; e += 4)
             *reinterpret_cast<float4*>(dst + e) = make_float4(acc[jj][e], acc[jj][e + 1], acc[jj][e + 2], acc[jj][e + 3]);
         }
     }
+    if (lane == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (jb + jj < grp) {
+          wml[(wave * grp + jb + jj) * 2] = mw[jj];
+          wml[(wave * grp + jb + jj) * 2 + 1] = lw[jj];
+        }
+    }
   }
   __syncthreads();
+  mark(P, sc, ti, 4);
+  // ---- merge the eight waves into this split's partial ----
   float* partp = P.part + ((((int64_t)l * P.nkv + g) * S + split) * grp) * PSTR;
-  for (int i = tid; i < grp * hd; i += kThreads) {
-    float s8[kWaves];
+  for (int i = tid; i < grp * HD; i += kThreads) {
+    const int j = i / HD, d = i % HD;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s8[w] = red[(int64_t)w * grp * hd + i];
-    const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-    stc(partp + i / hd * PSTR + 4 + i % hd, s);
-  }
-  if (tid < grp) {
-    stc(partp + (int64_t)tid * PSTR, n > 0 ? small[tid] : -INFINITY);
-    stc(partp + (int64_t)tid * PSTR + 1, n > 0 ? small[8 + tid] : 0.f);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wml[(w * grp + j) * 2]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mwv = wml[(w * grp + j) * 2];
+      const float sc_w = mwv == -INFINITY ? 0.f : expf(mwv - M);
+      o = fmaf(sc_w, red[((int64_t)w * grp + j) * HD + d], o);
+      lsum = fmaf(sc_w, wml[(w * grp + j) * 2 + 1], lsum);
+    }
+    stc(partp + (int64_t)j * PSTR + 4 + d, o);
+    if (d == 0) {
+      stc(partp + (int64_t)j * PSTR, M);
+      stc(partp + (int64_t)j * PSTR + 1, lsum);
+    }
   }
   drain();
   __syncthreads();
@@ -882,14 +922,14 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       wts[j * S + s2] = w;
       den += w * pl[(s2 * grp + j) * PSTR + 1];
     }
-    den = wave_sum_shfl(den);
+    den = wave_sum(den);
     const float inv = 1.0f / den;
     for (int s2 = lane; s2 < S; s2 += 64) wts[j * S + s2] *= inv;
   }
   __syncthreads();
-  float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * hd;
-  for (int i = tid; i < grp * hd; i += kThreads) {
-    const int j = i / hd, d = i % hd;
+  float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
+  for (int i = tid; i < grp * HD; i += kThreads) {
+    const int j = i / HD, d = i % HD;
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
     int s2 = 0;
     for (; s2 + 4 <= S; s2 += 4) {
@@ -1085,7 +1125,10 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
                                          int cu) {
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
-    case PMK_OP_ATTN: task_attn<KVDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_ATTN:
+      if (P.hd == 128) task_attn<KVDT, 128>(P, t, ti, sc, lds, cu);
+      else task_attn<KVDT, 64>(P, t, ti, sc, lds, cu);
+      break;
     case PMK_OP_OPROJ: task_oproj<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_DOWN: task_down<WDT>(P, t, ti, sc, lds, cu); break;

@@ -208,8 +208,8 @@ void compute_layout(pmk_ctx* c) {
   const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
   auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
   const int64_t S = s.attn_splits, grp = m.grp();
-  const int64_t chunk = (m.max_seq + S - 1) / S;
-  const int64_t attn = grp * m.hd + grp * ((chunk + 3) & ~3ll) + kWaves * grp * m.hd;
+  // attention: q [grp][hd], per-wave P.V partials [8][grp][hd], per-wave (max, sum) [8][grp][2]
+  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2;
   const int64_t comb = S * grp * (m.hd + 4) + grp * S + 4;
   const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn, comb});
   c->xs_floats = (int)((xs + 63) / 64 * 64);

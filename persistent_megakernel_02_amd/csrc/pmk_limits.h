@@ -11,4 +11,8 @@ constexpr int kCombineMaxFloats = 36000;
 // resource with 32-bit offsets, and offsets at or past this bound read as zeros.
 constexpr long long kMaxTileBytes = 0x7FFFFFF0ll;
 
+// Register slots of K/V rows per wave in the attention task: one split holds at most
+// 8 waves x kAttnBlocks x (rows per wave instruction) positions.
+constexpr int kAttnBlocks = 5;
+
 }  // namespace pmk

@@ -57,7 +57,7 @@ void split_range(int n, int parts, int i, int* lo, int* hi) {
 int attn_max_chunk(const ModelDims& m) {
   const int rowbytes = m.hd * (m.kvdt == PMK_DT_FP8_E4M3 ? 1 : 2);
   const int rpi = 64 / (rowbytes / 16);
-  return 64 * rpi;
+  return 8 * kAttnBlocks * rpi;
 }
 
 // ================================================================================================
@@ -76,8 +76,8 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     // the last split's combine stages every partial (S x grp x (hd + 4) floats) in LDS
     S = std::min(S, std::max(1, 32000 / (m.grp() * (m.hd + 5))));
   }
-  // each split's rows must fit the attention task's register batch: 8 waves x 8 row blocks of
-  // RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) <= 64 * RPI
+  // each split's rows must fit the attention task's register batch: 8 waves x kAttnBlocks row
+  // blocks of RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) is bounded
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
   if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > kCombineMaxFloats)
