@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="speed-weighted GEMV row split before the timed launch (pmk_tune; neutral on the boxes measured)")
     ap.add_argument("--repeat", type=int, default=1, help="extra timed launches reported as a spread")
     ap.add_argument("--kernel-only", action="store_true",
                     help="profiling: start from synthetic KV instead of a prefill and skip every leg but the timed launches")
@@ -92,7 +94,7 @@ def main():
     wts = synthgen.make_weights(w)
     log(f"[bench] weights generated in {time.time() - t_setup:.1f}s; uploading")
     sync_mode = pmk.PMK_SYNC_COUNTERS if args.sync == "counters" else pmk.PMK_SYNC_FLAGS
-    trace_steps = 0 if args.no_trace or args.kernel_only else 8
+    trace_steps = 0 if args.no_trace and not args.tune else 8
     dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(sync_mode=sync_mode, trace_steps=trace_steps))
     dw = pmk.DeviceWeights(wts)
     dec.load_weights(dw)
@@ -131,11 +133,18 @@ def main():
         del src, dst
     out_tokens = torch.empty(max(K, W), dtype=torch.int32, device=dev)
     n_done = torch.zeros(1, dtype=torch.int32, device=dev)
-    # ---- warm-up, rewind, timed launch ----
+    # ---- warm-up, speed-weighted row split (untimed), rewind, timed launch ----
     if W > 0:
         dec.decode(W, out_tokens=out_tokens, n_done=n_done)
         torch.cuda.synchronize()
         dec.rewind(P, first_tok)
+    if args.tune:
+        t_tune = time.time()
+        for _ in range(2):
+            dec.tune(trace_steps)
+        torch.cuda.synchronize()
+        log(f"[bench] tuned the GEMV row split in {time.time() - t_tune:.2f}s "
+            f"(schedule {dec.schedule_info().hash:#018x})")
     stream = torch.cuda.current_stream()
     times = []
     for r in range(max(1, args.repeat)):
@@ -163,7 +172,7 @@ def main():
         extra["prefill_tokens_per_s"] = round(P / prefill_s, 1)
 
     # ---- sync share from the per-task trace (separate, untimed call) ----
-    if trace_steps:
+    if trace_steps and not args.no_trace and not args.kernel_only:
         dec.set_trace(True)
         dec.decode(trace_steps, out_tokens=out_tokens, n_done=n_done)
         torch.cuda.synchronize()

@@ -221,6 +221,17 @@ pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
 pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);
 pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
 
+/* Speed-weighted row split (tuning).  Runs `steps` decode steps (<= the trace ring; <= 0: all of
+ * it) from the current position with the megakernel and tracing on, measures every queue's
+ * weight-streaming rate per GEMV phase (QKV, O, gate/up, down, LM head) from the trace, rebuilds
+ * the schedule with each GEMV task's rows proportional to its queue's rate (compute units of a
+ * device do not stream at one rate: the split evens out when they finish a phase), validates and
+ * installs it, then restores the position and next input token it started from (the KV rows it
+ * wrote past that position are rewritten by the next decode).  Synchronous on `stream`.  Requires
+ * bound weights and KV state and a context created with trace_steps >= 1.  Row assignment never
+ * changes a row's arithmetic beyond the grouping of its partial sums. */
+pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, void* stream);
+
 /* Schedule inspection (host only, also for device-less contexts). */
 pmk_status pmk_schedule_get_info(const pmk_ctx* ctx, pmk_schedule_info* info);
 
@@ -253,6 +264,11 @@ typedef struct pmk_schedule pmk_schedule;
 /* Build the schedule for `n_cus` queues without a device. */
 pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
                               pmk_schedule** out);
+/* The same with per-queue row weights for the GEMV phases: weights[op * n_cus + q] for pmk_op op
+ * (QKV, OPROJ, GATEUP, DOWN, LMHEAD; other rows of the 8 x n_cus array are ignored), positive; each
+ * GEMV task's rows are proportional to its queue's weight (at least one row or row pair each). */
+pmk_status pmk_schedule_build_weighted(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
+                                       const float* weights, pmk_schedule** out);
 void pmk_schedule_free(pmk_schedule* s);
 int32_t pmk_schedule_num_tasks(const pmk_schedule* s);
 int32_t pmk_schedule_num_counters(const pmk_schedule* s);

@@ -165,6 +165,11 @@ class Decoder:
         check(self.lib.pmk_trace_stats(self.ctx, ctypes.byref(a), ctypes.byref(b)), self.ctx)
         return a.value, b.value
 
+    def tune(self, steps: int = 0, stream=None):
+        """Measure each compute unit's streaming rate over `steps` traced decode steps and rebuild
+        the schedule with speed-proportional GEMV row shares (position and next token restored)."""
+        check(self.lib.pmk_tune(self.ctx, steps, _stream(stream)), self.ctx)
+
     def trace_export(self, path: str):
         check(self.lib.pmk_trace_export(self.ctx, path.encode()), self.ctx)
 

@@ -82,6 +82,7 @@ struct pmk_ctx {
   std::string err;
   std::vector<float> rope_host;
   uint64_t hash = 0;
+  RowWeights rw;  // per-queue GEMV row shares set by pmk_tune (empty: even split)
 };
 
 namespace {
@@ -671,6 +672,118 @@ static pmk_status read_trace(pmk_ctx* c, std::vector<unsigned long long>& t) {
   return PMK_OK;
 }
 
+// Replace the context's schedule by `s` (same task and counter counts): validate, re-derive the
+// tables and the LDS layout, upload the tables.  The device must be idle.
+static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
+  const std::string e = validate_schedule(s);
+  if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
+  if (s.tasks.size() != c->sched.tasks.size() || s.counters.size() != c->sched.counters.size() ||
+      s.n_flags != c->sched.n_flags)
+    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the rebuilt schedule changed its task or counter count");
+  const pmk_sizes old_sizes = c->sizes;
+  Schedule prev = std::move(c->sched);
+  c->sched = std::move(s);
+  compute_layout(c);
+  if (c->sizes.workspace_bytes != old_sizes.workspace_bytes || c->lds_bytes > 160 * 1024) {
+    c->sched = std::move(prev);
+    compute_layout(c);
+    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the rebuilt schedule does not fit the bound buffers or LDS");
+  }
+  c->tabs = flatten(c->sched);
+  c->hash = schedule_hash(c->sched);
+  compute_phases(c);
+  const void* fns[2] = {persistent_kernel(c->m.wdt, c->m.kvdt), phase_kernel(c->m.wdt, c->m.kvdt)};
+  for (const void* fn : fns) HIPCHK(c, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->lds_bytes));
+  fill_params(c);
+  HIPCHK(c, hipMemcpy(c->ws + c->w_tasks, c->tabs.tasks.data(), c->tabs.tasks.size() * sizeof(pmk_task), hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_qoff, c->tabs.qoff.data(), c->tabs.qoff.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_qtasks, c->tabs.qtasks.data(), c->tabs.qtasks.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_cprod, c->tabs.ctr_producers.data(), c->tabs.ctr_producers.size() * 4, hipMemcpyHostToDevice));
+  HIPCHK(c, hipMemcpy(c->ws + c->w_cflag, c->tabs.ctr_flag_base.data(), c->tabs.ctr_flag_base.size() * 4, hipMemcpyHostToDevice));
+  if (c->graph_exec) { (void)hipGraphExecDestroy(c->graph_exec); c->graph_exec = nullptr; }
+  if (c->graph) { (void)hipGraphDestroy(c->graph); c->graph = nullptr; }
+  return PMK_OK;
+}
+
+pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
+  if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "tuning reads the trace: create the context with trace_steps >= 1");
+  if (steps <= 0 || steps > c->sc.trace_steps) steps = c->sc.trace_steps;
+  if ((int64_t)c->pos_host + steps > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + steps exceeds max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, hipSetDevice(c->device));
+  // save the next input token and the position; run `steps` traced steps with the megakernel
+  int32_t* saved = reinterpret_cast<int32_t*>(c->ws + c->w_ctrl + CTRL_SAVED * 4);
+  HIPCHK(c, launch_copy_token(c->kp, saved, st));
+  const int32_t pos0 = c->pos_host;
+  const int trace_prev = c->trace_on;
+  HIPCHK(c, hipStreamSynchronize(st));
+  s = pmk_set_trace(c, 1);
+  if (s != PMK_OK) return s;
+  CallParams cp{};
+  cp.n_steps = steps;
+  cp.eos = -1;
+  cp.trace = 1;
+  s = begin_call(c, cp, st);
+  if (s == PMK_OK) s = launch_persistent(c, st);
+  if (s != PMK_OK) return s;
+  c->pos_host += steps;
+  std::vector<unsigned long long> t;
+  s = read_trace(c, t);
+  if (s != PMK_OK) return s;
+  // streamed bytes and streaming time (staged -> GEMV done) per GEMV op and queue
+  const size_t NT = c->sched.tasks.size();
+  const int NQ = c->sched.n_queues;
+  std::vector<int> queue_of(NT, 0);
+  for (int q = 0; q < NQ; ++q)
+    for (int32_t ti : c->sched.queues[q]) queue_of[ti] = q;
+  std::vector<double> bytes(8 * (size_t)NQ, 0.0), ticks(8 * (size_t)NQ, 0.0);
+  const ModelDims& m = c->m;
+  const double es = m.wdt == PMK_DT_FP8_E4M3 ? 1.0 : 2.0;
+  for (int sp = 0; sp < steps; ++sp)
+    for (size_t i = 0; i < NT; ++i) {
+      const pmk_task& k = c->sched.tasks[i];
+      if (k.op == PMK_OP_ATTN || k.op == PMK_OP_TOKEN) continue;
+      const unsigned long long* r = &t[((size_t)sp * NT + i) * 8];
+      if (!r[4] || !r[5] || r[5] <= r[4]) continue;
+      const double K = k.op == PMK_OP_DOWN ? m.F : k.op == PMK_OP_OPROJ ? m.qdim() : m.H;
+      const size_t at = (size_t)k.op * NQ + queue_of[i];
+      // bytes streamed after staging: the tile less what the pre-wait prefetch already holds
+      const double tile = (k.a1 - k.a0) * K * es;
+      bytes[at] += std::max(0.0, tile - (double)kPrefetchBytes);
+      ticks[at] += (double)(r[5] - r[4]);
+    }
+  RowWeights rw;
+  // only phases whose tiles are several times the prefetch give a usable rate
+  for (int op : {PMK_OP_GATEUP, PMK_OP_DOWN, PMK_OP_LMHEAD}) {
+    std::vector<double> w(NQ, 0.0);
+    double mean = 0;
+    int n = 0;
+    for (int q = 0; q < NQ; ++q) {
+      const size_t at = (size_t)op * NQ + q;
+      if (ticks[at] > 0) { w[q] = bytes[at] / ticks[at]; mean += w[q]; ++n; }
+    }
+    if (n < NQ || mean <= 0) continue;  // not every queue measured: keep the even split
+    mean /= n;
+    for (double& x : w) x = std::min(std::max(x / mean, 0.5), 2.0);
+    rw.w[op] = w;
+  }
+  // restore the position and the next input token
+  HIPCHK(c, launch_set_pos(c->kp, pos0, saved, st));
+  HIPCHK(c, hipStreamSynchronize(st));
+  c->pos_host = pos0;
+  c->trace_on = trace_prev;
+  Schedule ns;
+  const std::string e = build_schedule(c->m, c->sc, NQ, &ns, &rw);
+  if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
+  s = install_schedule(c, std::move(ns));
+  if (s != PMK_OK) return s;
+  c->rw = rw;
+  return PMK_OK;
+}
+
 pmk_status pmk_trace_stats(pmk_ctx* c, double* wait_share, double* step_us) {
   std::vector<unsigned long long> t;
   pmk_status s = read_trace(c, t);
@@ -746,18 +859,31 @@ pmk_status pmk_schedule_get_info(const pmk_ctx* c, pmk_schedule_info* info) {
 }
 
 // ---- schedule IR API ----
-pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus, pmk_schedule** out) {
+pmk_status pmk_schedule_build_weighted(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
+                                       const float* weights, pmk_schedule** out) {
   g_err.clear();
   if (!cfg || !out || n_cus <= 0) return fail(nullptr, PMK_ERR_INVALID_ARG, "bad arguments");
   *out = nullptr;
   const std::string why = contract_check(*cfg);
   if (!why.empty()) return fail(nullptr, PMK_ERR_UNSUPPORTED, why);
+  RowWeights rw;
+  if (weights) {
+    for (int op : {PMK_OP_QKV, PMK_OP_OPROJ, PMK_OP_GATEUP, PMK_OP_DOWN, PMK_OP_LMHEAD}) {
+      rw.w[op].assign(weights + (size_t)op * n_cus, weights + (size_t)(op + 1) * n_cus);
+      for (double x : rw.w[op])
+        if (!(x > 0)) return fail(nullptr, PMK_ERR_INVALID_ARG, "row weights must be positive");
+    }
+  }
   pmk_schedule* s = new pmk_schedule();
   const pmk_schedule_config sc = defaults(sched);
-  const std::string e = build_schedule(dims_of(*cfg), sc, n_cus, &s->s);
+  const std::string e = build_schedule(dims_of(*cfg), sc, n_cus, &s->s, weights ? &rw : nullptr);
   if (!e.empty()) { delete s; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
   *out = s;
   return PMK_OK;
+}
+
+pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus, pmk_schedule** out) {
+  return pmk_schedule_build_weighted(cfg, sched, n_cus, nullptr, out);
 }
 
 void pmk_schedule_free(pmk_schedule* s) { delete s; }

@@ -20,6 +20,7 @@ enum Ctrl : int {
   CTRL_STOPPED = 4,  // per-op modes: eos seen in this call
   CTRL_ABORT = 5,    // watchdog: a wait gave up; every wait exits
   CTRL_ERR = 8,      // pmk_device_error: code, cu, task, counter, expected, seen (6 words)
+  CTRL_SAVED = 16,   // next input token saved while the schedule is tuned
   CTRL_WORDS = 64
 };
 

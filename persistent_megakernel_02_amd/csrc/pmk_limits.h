@@ -15,4 +15,7 @@ constexpr long long kMaxTileBytes = 0x7FFFFFF0ll;
 // 8 waves x kAttnBlocks x (rows per wave instruction) positions.
 constexpr int kAttnBlocks = 5;
 
+// Weight bytes a GEMV workgroup loads before its dependency wait (8 waves x 10 x 1 KiB).
+constexpr long long kPrefetchBytes = 8 * 10 * 1024;
+
 }  // namespace pmk

@@ -63,7 +63,24 @@ int attn_max_chunk(const ModelDims& m) {
 // ================================================================================================
 // Builder
 // ================================================================================================
-std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out) {
+// Split `units` into `parts` contiguous non-empty ranges with sizes proportional to w[0..parts)
+// (cumulative rounding); requires units >= parts.
+void split_weighted(int units, int parts, const std::vector<double>& w, std::vector<int>* bounds) {
+  double tot = 0;
+  for (int i = 0; i < parts; ++i) tot += std::max(w[i], 1e-9);
+  bounds->assign(parts + 1, 0);
+  double acc = 0;
+  for (int i = 0; i < parts; ++i) {
+    acc += std::max(w[i], 1e-9);
+    (*bounds)[i + 1] = (int)std::llround((double)units * acc / tot);
+  }
+  for (int i = 1; i < parts; ++i) (*bounds)[i] = std::max((*bounds)[i], (*bounds)[i - 1] + 1);  // non-empty
+  (*bounds)[parts] = units;
+  for (int i = parts - 1; i > 0; --i) (*bounds)[i] = std::min((*bounds)[i], (*bounds)[i + 1] - 1);
+}
+
+std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out,
+                           const RowWeights* rw) {
   if (n_queues <= 0) return "builder: no queues";
   Schedule s;
   s.m = m;
@@ -111,11 +128,23 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     s.tasks.push_back(t);
     s.queues[q].push_back((int32_t)s.tasks.size() - 1);
   };
+  // row range of task i of a GEMV op over `units` (rows, or row pairs) split `parts` ways; task i
+  // runs on queue i
+  std::vector<int> wb;
+  auto split_op = [&](int op, int units, int parts, int i, int* lo, int* hi) {
+    if (rw && (int)rw->w[op].size() >= parts) {
+      if (i == 0) split_weighted(units, parts, rw->w[op], &wb);
+      *lo = wb[i];
+      *hi = wb[i + 1];
+    } else {
+      split_range(units, parts, i, lo, hi);
+    }
+  };
   for (int l = 0; l < L; ++l) {
     // QKV: packed rows in pairs (each RoPE pair adjacent)
     for (int i = 0; i < n_qkv; ++i) {
       int lo, hi;
-      split_range(m.qkv_rows() / 2, n_qkv, i, &lo, &hi);
+      split_op(PMK_OP_QKV, m.qkv_rows() / 2, n_qkv, i, &lo, &hi);
       pmk_task t{PMK_OP_QKV, l, 2 * lo, 2 * hi, -1, 0, 0, s.c_qkv[l], i};
       if (l == 0) { t.wait_ctr = s.c_lm; t.wait_count = n_lm; t.wait_lag = 1; }
       else { t.wait_ctr = s.c_down[l - 1]; t.wait_count = n_down; t.wait_lag = 0; }
@@ -129,23 +158,23 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     }
     for (int i = 0; i < n_o; ++i) {
       int lo, hi;
-      split_range(m.H, n_o, i, &lo, &hi);
+      split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi);
       push(i % n_queues, pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv, 0, s.c_oproj[l], i});
     }
     for (int i = 0; i < n_gu; ++i) {
       int lo, hi;
-      split_range(m.F, n_gu, i, &lo, &hi);
+      split_op(PMK_OP_GATEUP, m.F, n_gu, i, &lo, &hi);
       push(i % n_queues, pmk_task{PMK_OP_GATEUP, l, 2 * lo, 2 * hi, s.c_oproj[l], n_o, 0, s.c_gu[l], i});
     }
     for (int i = 0; i < n_down; ++i) {
       int lo, hi;
-      split_range(m.H, n_down, i, &lo, &hi);
+      split_op(PMK_OP_DOWN, m.H, n_down, i, &lo, &hi);
       push(i % n_queues, pmk_task{PMK_OP_DOWN, l, lo, hi, s.c_gu[l], n_gu, 0, s.c_down[l], i});
     }
   }
   for (int i = 0; i < n_lm; ++i) {
     int lo, hi;
-    split_range(m.V, n_lm, i, &lo, &hi);
+    split_op(PMK_OP_LMHEAD, m.V, n_lm, i, &lo, &hi);
     push(i % n_queues, pmk_task{PMK_OP_LMHEAD, -1, lo, hi, s.c_down[L - 1], n_down, 0, s.c_lm, i});
   }
   push(0, pmk_task{PMK_OP_TOKEN, -1, 0, 0, s.c_lm, n_lm, 0, -1, 0});

@@ -48,8 +48,15 @@ struct Schedule {
 // Longest attention split (positions) one task holds in registers.
 int attn_max_chunk(const ModelDims& m);
 
+// Relative streaming speed of each queue per GEMV op (indexed by pmk_op; an empty vector means
+// equal speeds): the builder gives each GEMV task a row share proportional to its queue's weight.
+struct RowWeights {
+  std::vector<double> w[8];
+};
+
 // Builder: lowers the model into per-queue task lists (one decode step; the kernel repeats it).
-std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out);
+std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, int n_queues, Schedule* out,
+                           const RowWeights* rw = nullptr);
 
 // Static validator; returns "" when the schedule passes, else "<check>: <detail>".
 std::string validate_schedule(const Schedule& s);

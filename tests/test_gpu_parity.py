@@ -63,6 +63,37 @@ def test_modes_agree_bitwise_and_chunking(tiny):
     assert np.array_equal(again.logits, base.logits)  # deterministic
 
 
+@pytest.mark.parametrize("name", ["tiny", "1b"])
+def test_tuned_schedule_keeps_parity(name, tiny):
+    """pmk_tune re-splits the GEMV rows by measured speed and restores the position and next token:
+    decoding afterwards still matches the oracle, and the modes still agree bitwise."""
+    import torch
+    import persistent_megakernel_02_amd as pmk
+    w = synthgen.WORKLOADS[name]
+    wts = tiny if name == "tiny" else synthgen.make_weights(w)
+    dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(trace_steps=4))
+    dec.load_weights(pmk.DeviceWeights(wts))
+    prompt = synthgen.make_prompt(w)
+    first = dec.prefill(torch.from_numpy(np.ascontiguousarray(prompt, np.int32)).cuda())
+    torch.cuda.synchronize()
+    pos = dec.position()
+    log(f"{name}: tune at position {pos}")
+    h0 = dec.schedule_info().hash
+    dec.tune(4)
+    dec.tune(4)
+    assert dec.position() == pos
+    assert dec.poll_error().code == 0
+    log(f"{name}: schedule hash {h0:#x} -> {dec.schedule_info().hash:#x}")
+    steps = 8
+    runs = {}
+    for mname, m in _modes():
+        runs[mname] = gpu_run(w, wts, steps, mode=m, prompt=prompt, dec=dec)
+    ref, first_ok = oracle_teacher_forced(w, wts, runs["megakernel"], prompt=prompt)
+    check(w, runs["megakernel"], ref, first_ok, f"{name}/tuned")
+    for mname, r in runs.items():
+        assert np.array_equal(r.logits, runs["megakernel"].logits), mname
+
+
 def test_tiny_eos_stops_early(tiny):
     import torch
     import persistent_megakernel_02_amd as pmk

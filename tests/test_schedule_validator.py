@@ -234,3 +234,31 @@ def test_simulator_catches_a_race_the_validator_rejects():
     assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith("race"), msg
     caught = [s.simulate(steps=2, seed=k) for k in range(5)]
     assert any(st == _lib.PMK_ERR_SCHEDULE_INVALID and "race" in m for st, m in caught), caught
+
+
+def test_weighted_row_splits_are_accepted_and_proportional():
+    """Speed-weighted GEMV splits (what tuning installs) pass the validator and follow the weights."""
+    lib = pmk.load()
+    for name, n_cus in (("tiny", 8), ("1b", 64), ("8b", 256)):
+        w = WORKLOADS[name]
+        rng = random.Random(7)
+        weights = (ctypes.c_float * (8 * n_cus))(*[0.7 + 0.6 * rng.random() for _ in range(8 * n_cus)])
+        h = ctypes.c_void_p()
+        cfg = pmk.model_config(w)
+        st = lib.pmk_schedule_build_weighted(ctypes.byref(cfg), ctypes.byref(pmk.schedule_config()), n_cus, weights,
+                                             ctypes.byref(h))
+        assert st == 0, lib.pmk_last_global_error()
+        buf = ctypes.create_string_buffer(512)
+        assert lib.pmk_schedule_validate(h, buf, 512) == 0, buf.value.decode()
+        # the LM head rows of each queue follow its weight (within rounding)
+        t = pmk.pmk_task()
+        rows, wts = [], []
+        for i in range(lib.pmk_schedule_num_tasks(h)):
+            assert lib.pmk_schedule_get_task(h, i, ctypes.byref(t)) == 0
+            if t.op == 6:
+                rows.append(t.a1 - t.a0)
+                wts.append(weights[6 * n_cus + t.signal_slot])
+        total = sum(rows)
+        for r, x in zip(rows, wts):
+            assert abs(r - total * x / sum(wts)) <= 1.5
+        lib.pmk_schedule_free(h)
