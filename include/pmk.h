@@ -101,8 +101,10 @@ typedef struct {
   int32_t n_cus;        /* grid size = number of queues (default: all CUs of the device) */
   int32_t sync_mode;    /* pmk_sync_mode (default FLAGS) */
   int32_t attn_splits;  /* split-KV chunks per KV head (default: n_cus / n_kv_heads, capped by max_seq/16) */
-  int32_t prefetch;     /* >= 0 (default): a GEMV task issues the first 10 of its 16-byte weight
-                           loads per lane before its dependency wait; -1: all after it */
+  int32_t prefetch;     /* 0 (default): a GEMV task issues the first 10 of its 16-byte weight loads
+                           per lane before its dependency wait, and an O-projection task whose tile
+                           fits in LDS copies all of it there (LDS-DMA) before its wait instead;
+                           1: the register loads only; -1: every weight load after the wait */
   int32_t trace_steps;  /* steps kept in the per-task trace ring (default 0 = no trace buffer) */
   int64_t spin_limit;   /* polls before a wait gives up and aborts the launch (default 1<<22) */
 } pmk_schedule_config;

@@ -26,7 +26,7 @@ def model_config(w, max_seq: Optional[int] = None) -> pmk_model_config:
                             _DT[w.kvdtype], 0, 0)
 
 
-def schedule_config(n_cus: int = 0, sync_mode: int = PMK_SYNC_FLAGS, attn_splits: int = 0, prefetch: int = 1,
+def schedule_config(n_cus: int = 0, sync_mode: int = PMK_SYNC_FLAGS, attn_splits: int = 0, prefetch: int = 0,
                     trace_steps: int = 0, spin_limit: int = 0) -> pmk_schedule_config:
     return pmk_schedule_config(n_cus, sync_mode, attn_splits, prefetch, trace_steps, spin_limit)
 

@@ -311,15 +311,30 @@ constexpr int prefetch_depth() { return PMK_PREFETCH_UNITS < ring_depth<WDT>() ?
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
 // KS minimises the largest per-wave unit count (short tiles then still keep all waves streaming).
-__device__ __forceinline__ int choose_ks(int rows, int nsl) {
-  int best = 0x7fffffff, ks_best = 1;
-  for (int ks = 1; ks <= kWaves; ks <<= 1) {
-    const int g = kWaves / ks;
-    const int cost = ((rows + g - 1) / g) * ((nsl + ks - 1) / ks);
-    if (cost < best) { best = cost; ks_best = ks; }
+// Wave w takes row group w / KS and slice range w % KS; its units (one 16-byte chunk per lane of
+// one row and one 64-chunk slice) run row by row, slices in order within a row.
+struct TileSplit {
+  int R, KS, gi, si, wr0, wr1, s0, s1, nunits, max_units;
+  __device__ __forceinline__ TileSplit(int r0, int r1, int nsl, int wave) {
+    R = r1 - r0;
+    int best = 0x7fffffff;
+    KS = 1;
+    for (int ks = 1; ks <= kWaves; ks <<= 1) {
+      const int g = kWaves / ks;
+      const int cost = ((R + g - 1) / g) * ((nsl + ks - 1) / ks);
+      if (cost < best) { best = cost; KS = ks; }
+    }
+    max_units = best;  // units of the busiest wave
+    const int G = kWaves / KS;
+    gi = wave / KS;
+    si = wave % KS;
+    wr0 = r0 + (int)((int64_t)R * gi / G);
+    wr1 = r0 + (int)((int64_t)R * (gi + 1) / G);
+    s0 = (int)((int64_t)nsl * si / KS);
+    s1 = (int)((int64_t)nsl * (si + 1) / KS);
+    nunits = (wr1 - wr0) * (s1 - s0);
   }
-  return ks_best;
-}
+};
 
 // GEMV over rows [r0, r1) of W (row-major [rows][K]) against the vector staged in LDS by `sync`.
 // On return (after a workgroup barrier) y[r - r0] holds row r's fp32 dot product.  yp is LDS
@@ -337,12 +352,9 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
-  const int R = r1 - r0;
-  const int KS = choose_ks(R, nsl);
-  const int G = kWaves / KS, gi = wave / KS, si = wave % KS;
-  const int wr0 = r0 + (int)((int64_t)R * gi / G), wr1 = r0 + (int)((int64_t)R * (gi + 1) / G);
-  const int s0 = (int)((int64_t)nsl * si / KS), s1 = (int)((int64_t)nsl * (si + 1) / KS);
-  const int nunits = (wr1 - wr0) * (s1 - s0);
+  const TileSplit sp(r0, r1, nsl, wave);
+  const int R = sp.R, KS = sp.KS, si = sp.si, wr0 = sp.wr0, wr1 = sp.wr1, s0 = sp.s0, s1 = sp.s1;
+  const int nunits = sp.nunits;
 
   constexpr int kRing = ring_depth<WDT>();
   u32x4 ring[kRing];
@@ -399,6 +411,73 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
           }
         }
         issue(d);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R; i += kThreads) {
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k) v += yp[i * KS + k];
+    y[i] = v;
+  }
+  __syncthreads();
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy a GEMV tile (rows [r0, r1) of W) into LDS with LDS-DMA buffer loads: no registers, and an
+// out-of-range lane (past the last chunk of a row) writes zeros.  Wave w's units land at
+// pf + w * ustride KiB in the order gemv_rows_lds consumes them; each wave later reads only the
+// units it copied itself, so its own load counter orders the copy before the reads (the compiler
+// waits on outstanding LDS-DMA before an LDS access that may alias it).
+template <int WDT>
+__device__ __forceinline__ void tile_to_lds(const uint8_t* __restrict__ W, int K, int r0, int r1, float* pf,
+                                            int ustride) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
+  const int nch = K / WFmt<WDT>::EPL, nsl = (nch + 63) >> 6;
+  const TileSplit sp(r0, r1, nsl, wave);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(W + (int64_t)r0 * rb), (short)0, (int)((int64_t)sp.R * rb), 0x00020000);
+  constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;
+  float* dst = pf + wave * ustride * 256;
+  int lrow = sp.wr0, lj = sp.s0;
+  for (int u = 0; u < sp.nunits; ++u) {
+    const int c = lj * 64 + lane;
+    const uint32_t off = c < nch ? (uint32_t)((int64_t)(lrow - r0) * rb + (int64_t)c * 16) : kOut;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(dst + u * 256), 16, off, 0, 0, 2);  // nontemporal
+    if (++lj == sp.s1) { lj = sp.s0; ++lrow; }
+  }
+}
+
+// gemv_rows over a tile that tile_to_lds copies into LDS (issued before this call, so the copy
+// overlaps `sync`, the dependency wait and input staging): the same split, the same per-lane
+// chunk order and the same summation order, so the results are bitwise those of gemv_rows.
+template <int WDT, class Sync, class ScaleRow>
+__device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float* xs, const float* pf, int ustride,
+                                              float* yp, float* y, Sync sync, ScaleRow srow) {
+  constexpr int EPL = WFmt<WDT>::EPL;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nch = K / EPL, nsl = (nch + 63) >> 6;
+  const TileSplit sp(r0, r1, nsl, wave);
+  const int R = sp.R, KS = sp.KS, si = sp.si, s0 = sp.s0, s1 = sp.s1;
+  sync();
+  if (sp.nunits > 0) {
+    const float* src = pf + wave * ustride * 256 + lane * 4;
+    float acc = 0.f;
+    int crow = sp.wr0, cj = s0;
+    for (int u = 0; u < sp.nunits; ++u) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + u * 256);
+      const int c = cj * 64 + lane;
+      const float part = chunk_dot<WDT>(w, xs + c * EPL);
+      if constexpr (WDT == WFP8) acc = fmaf(part, srow(crow)[(c < nch ? c : 0) >> 3], acc);
+      else acc += part;
+      if (++cj == s1) {
+        cj = s0;
+        const float v = wave_sum(acc);
+        acc = 0.f;
+        if (lane == 0) yp[(crow - r0) * KS + si] = v;
+        ++crow;
       }
     }
   }
@@ -515,6 +594,13 @@ struct StepCtx {
   int tok;      // input token if already known, else -1
   bool per_op;  // per-op kernels: no waits (kernel boundaries order the tasks)
 };
+
+// An O projection tile that fits the LDS tile area is copied there whole (LDS-DMA) before the
+// task's dependency wait, instead of the register ring's first units: the wait for the attention
+// combine is long enough for all of it to land, and the GEMV then runs from LDS.
+__device__ __forceinline__ bool oproj_tile_in_lds(const KParams& P, const pmk_task& t, const StepCtx& sc, int nsl) {
+  return P.prefetch == 2 && P.pf_wave > 0 && !sc.per_op && TileSplit(t.a0, t.a1, nsl, 0).max_units <= P.pf_wave;
+}
 
 __device__ __forceinline__ int key_token(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
@@ -654,6 +740,16 @@ __device__ __forceinline__ float group_sum(float v, int n) {
   return v;
 }
 
+// Max / sum over the four lanes of a quad (quad_perm DPP); every lane of the quad receives it.
+__device__ __forceinline__ float quad_max(float v) {
+  v = dpp_max<0xB1, 0xF>(v);  // quad_perm [1,0,3,2]
+  return dpp_max<0x4E, 0xF>(v);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
 template <int KVDT>
 __device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
   if constexpr (KVDT == WFP8) {
@@ -702,9 +798,6 @@ __device__ __forceinline__ float column_max(float v) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-// 16-byte loads per thread that bring every partial of a head group into LDS in one batch
-constexpr int kCombineBatch = (kCombineMaxFloats + 4 * kThreads - 1) / (4 * kThreads);
-
 // Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
 // query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
 // the last split to finish (atomic ticket) combines all splits of the group into o.
@@ -718,7 +811,7 @@ constexpr int kCombineBatch = (kCombineMaxFloats + 4 * kThreads - 1) / (4 * kThr
 // wave's max and sum per head (reduced across the rows of an instruction with column_max /
 // column_sum), probabilities and P.V; the eight waves' (max, sum, acc) are then merged in LDS with
 // the usual rescaling, exactly as the splits are merged by the combine.
-template <int KVDT, int HD>
+template <int WDT, int KVDT, int HD>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
@@ -741,7 +834,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   float* qs = lds;                      // [grp][HD]
   float* red = qs + grp * HD;           // [kWaves][grp][HD] per-wave P.V partials
   float* wml = red + kWaves * grp * HD; // [kWaves][grp][2] per-wave (max, sum)
-  float* small = lds + P.xs_floats;     // ticket result
+  int* last = reinterpret_cast<int*>(wml + kWaves * grp * 2);  // ticket result
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
     kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
@@ -895,7 +988,6 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   __syncthreads();
   mark(P, sc, ti, 5);
   // ---- ticket: the last split of this head group combines ----
-  int* last = reinterpret_cast<int*>(small + 32);
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&P.tickets[l * P.nkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last = (int)(old % (uint32_t)S) == S - 1;
@@ -903,41 +995,63 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   __syncthreads();
   mark(P, sc, ti, 6);
   if (!*last) return;
-  // all partials of the head group (S x grp x (hd+4) floats) in one batch of coherent loads
-  const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * PSTR;
-  const int ntot = S * grp * PSTR;
-  const int npad = (ntot + 3) & ~3;
-  float* pl = lds;              // [S][grp][hd+4]
-  float* wts = lds + npad;      // [grp][S]
-  load_vector<false, kCombineBatch>(pg, ntot, npad, pl);
-  __syncthreads();
-  for (int j = wave; j < grp; j += kWaves) {
-    float M = -INFINITY;
-    for (int s2 = lane; s2 < S; s2 += 64) M = fmaxf(M, pl[(s2 * grp + j) * PSTR]);
-    M = wave_max(M);
-    float den = 0.f;
-    for (int s2 = lane; s2 < S; s2 += 64) {
-      const float m = pl[(s2 * grp + j) * PSTR];
-      const float w = m == -INFINITY ? 0.f : expf(m - M);
-      wts[j * S + s2] = w;
-      den += w * pl[(s2 * grp + j) * PSTR + 1];
-    }
-    den = wave_sum(den);
-    const float inv = 1.0f / den;
-    for (int s2 = lane; s2 < S; s2 += 64) wts[j * S + s2] *= inv;
-  }
-  __syncthreads();
-  float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
-  for (int i = tid; i < grp * HD; i += kThreads) {
-    const int j = i / HD, d = i % HD;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-    int s2 = 0;
-    for (; s2 + 4 <= S; s2 += 4) {
+  // Combine, in registers (LDS stays free for the next task's tile): a quad of threads owns four
+  // consecutive dims of one head; its threads take every fourth split and merge them online in
+  // batches of coherent loads (header m, l and the four acc values), then the quad merges its
+  // four (max, sum, acc) with DPP and each thread stores one dim.
+  {
+    constexpr int QPH = HD / 4;  // dim quads per head
+    constexpr int CB = 8;        // splits per thread per batch
+    constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;
+    const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * PSTR;
+    const __amdgpu_buffer_rsrc_t pr = coherent_rsrc(pg, (uint32_t)((int64_t)S * grp * PSTR * 4));
+    float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
+    const int r = tid & 3;
+    for (int qd = tid >> 2; qd < grp * QPH; qd += kThreads / 4) {
+      const int j = qd / QPH, d0 = (qd % QPH) * 4;
+      float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int sb = 0; sb < S; sb += 4 * CB) {
+        u32x4 hv[CB], av[CB];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s4[k] = fmaf(wts[j * S + s2 + k], pl[((s2 + k) * grp + j) * PSTR + 4 + d], s4[k]);
+        for (int k = 0; k < CB; ++k) {
+          const int s2 = sb + 4 * k + r;
+          const uint32_t off = s2 < S ? (uint32_t)((s2 * grp + j) * PSTR) * 4u : kOut;
+          hv[k] = ldc16(pr, off);
+          av[k] = ldc16(pr, off + (uint32_t)(4 + d0) * 4u);
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < CB; ++k)
+          if (sb + 4 * k + r < S) mb = fmaxf(mb, __uint_as_float(hv[k].x));
+        const float Mn = fmaxf(M, mb);
+        if (Mn != -INFINITY) {
+          const float f = M == -INFINITY ? 0.f : expf(M - Mn);
+          den *= f; a0 *= f; a1 *= f; a2 *= f; a3 *= f;
+#pragma unroll
+          for (int k = 0; k < CB; ++k) {
+            const float m = __uint_as_float(hv[k].x);
+            if (sb + 4 * k + r < S && m != -INFINITY) {
+              const float w = expf(m - Mn);
+              den = fmaf(w, __uint_as_float(hv[k].y), den);
+              a0 = fmaf(w, __uint_as_float(av[k].x), a0);
+              a1 = fmaf(w, __uint_as_float(av[k].y), a1);
+              a2 = fmaf(w, __uint_as_float(av[k].z), a2);
+              a3 = fmaf(w, __uint_as_float(av[k].w), a3);
+            }
+          }
+          M = Mn;
+        }
+      }
+      const float Mq = quad_max(M);  // finite: every head has at least the current position
+      const float f = M == -INFINITY ? 0.f : expf(M - Mq);
+      den = quad_sum(den * f);
+      a0 = quad_sum(a0 * f);
+      a1 = quad_sum(a1 * f);
+      a2 = quad_sum(a2 * f);
+      a3 = quad_sum(a3 * f);
+      const float v = r == 0 ? a0 : r == 1 ? a1 : r == 2 ? a2 : a3;
+      stc(o + j * HD + d0 + r, v / den);
     }
-    for (; s2 < S; ++s2) s4[0] = fmaf(wts[j * S + s2], pl[(s2 * grp + j) * PSTR + 4 + d], s4[0]);
-    stc(o + i, (s4[0] + s4[1]) + (s4[2] + s4[3]));
   }
   mark(P, sc, ti, 7);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -949,10 +1063,11 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
                                            int cu) {
   constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
   const int l = t.layer, K = P.qdim, R = t.a1 - t.a0;
+  // compact LDS layout (o, residual rows, partial sums, results) below the LDS tile area
   float* xs = lds;
-  float* res = lds + P.epi_off;
-  float* yp = lds + P.yp_off;
-  float* y = lds + P.y_off;
+  float* res = lds + P.o_epi_off;
+  float* yp = lds + P.o_yp_off;
+  float* y = lds + P.o_y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
@@ -969,7 +1084,11 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   };
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
+  if (oproj_tile_in_lds(P, t, sc, (K / WFmt<WDT>::EPL + 63) >> 6)) {
+    tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, P.pf_wave);
+    gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, P.pf_wave, yp, y, sync, srow);
+  } else
+    gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -1126,8 +1245,8 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_ATTN:
-      if (P.hd == 128) task_attn<KVDT, 128>(P, t, ti, sc, lds, cu);
-      else task_attn<KVDT, 64>(P, t, ti, sc, lds, cu);
+      if (P.hd == 128) task_attn<WDT, KVDT, 128>(P, t, ti, sc, lds, cu);
+      else task_attn<WDT, KVDT, 64>(P, t, ti, sc, lds, cu);
       break;
     case PMK_OP_OPROJ: task_oproj<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;

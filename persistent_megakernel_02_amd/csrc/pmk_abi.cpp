@@ -73,7 +73,9 @@ struct pmk_ctx {
   int trace_on = 0;
   int xs_floats = 0;
   int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0;
-  size_t lds_bytes = 0;
+  int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_wave = 0;
+  size_t lds_bytes = 0;     // per-op kernels
+  size_t lds_bytes_pk = 0;  // persistent kernel (adds the O-projection tile area)
   KParams kp{};
   std::vector<Phase> phases;
   hipStream_t cap_stream = nullptr;
@@ -143,7 +145,7 @@ pmk_schedule_config defaults(const pmk_schedule_config* s) {
   pmk_schedule_config d{};
   if (s) d = *s;
   if (d.spin_limit <= 0) d.spin_limit = 1ll << 22;
-  d.prefetch = d.prefetch < 0 ? 0 : 1;
+  d.prefetch = d.prefetch < 0 ? 0 : d.prefetch == 1 ? 1 : 2;
   return d;
 }
 
@@ -210,9 +212,10 @@ void compute_layout(pmk_ctx* c) {
   auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
   const int64_t S = s.attn_splits, grp = m.grp();
   // attention: q [grp][hd], per-wave P.V partials [8][grp][hd], per-wave (max, sum) [8][grp][2]
-  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2;
-  const int64_t comb = S * grp * (m.hd + 4) + grp * S + 4;
-  const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn, comb});
+  // and the ticket word
+  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2 + 4;
+  (void)S;
+  const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn});
   c->xs_floats = (int)((xs + 63) / 64 * 64);
   // epilogue inputs staged behind the scratch words: the RoPE row (+ fp8 K/V scales) of QKV tasks,
   // the residual rows of OPROJ and DOWN tasks
@@ -226,6 +229,21 @@ void compute_layout(pmk_ctx* c) {
   c->yp_off = c->epi_off + c->epi_floats;
   c->y_off = c->yp_off + (int)((kWaves * rmax + 63) / 64 * 64);
   c->lds_bytes = (size_t)(c->y_off + (rmax + 63) / 64 * 64) * 4;
+  // OPROJ tasks keep o, their residual rows, partial sums and results in a compact block; the rest
+  // of LDS (persistent kernel only) holds the O-projection tile, copied before the task's wait.
+  int64_t ormax = 1;
+  for (const pmk_task& t : s.tasks)
+    if (t.op == PMK_OP_OPROJ) ormax = std::max<int64_t>(ormax, t.a1 - t.a0);
+  auto r64 = [](int64_t n) { return (n + 63) / 64 * 64; };
+  c->o_epi_off = (int)r64(padn(qd));
+  c->o_yp_off = c->o_epi_off + (int)r64(ormax);
+  c->o_y_off = c->o_yp_off + (int)r64(kWaves * ormax);
+  const int64_t o_end = c->o_y_off + r64(ormax);
+  c->pf_off = (int)((std::max(o_end, r64(attn)) + 255) / 256 * 256);
+  const int64_t lds_floats = kLdsBytes / 4;
+  c->pf_wave = c->sc.prefetch == 2 ? (int)std::max<int64_t>(0, (lds_floats - c->pf_off) / 256 / kWaves) : 0;
+  c->lds_bytes_pk = c->pf_wave > 0 ? std::max(c->lds_bytes, (size_t)(c->pf_off + (int64_t)kWaves * c->pf_wave * 256) * 4)
+                                   : c->lds_bytes;
 }
 
 void fill_params(pmk_ctx* c) {
@@ -281,6 +299,11 @@ void fill_params(pmk_ctx* c) {
   P.epi_off = c->epi_off;
   P.yp_off = c->yp_off;
   P.y_off = c->y_off;
+  P.o_epi_off = c->o_epi_off;
+  P.o_yp_off = c->o_yp_off;
+  P.o_y_off = c->o_y_off;
+  P.pf_off = c->pf_off;
+  P.pf_wave = c->pf_wave;
 }
 
 void compute_phases(pmk_ctx* c) {
@@ -305,7 +328,7 @@ pmk_status need_device(pmk_ctx* c) {
 pmk_status launch_persistent(pmk_ctx* c, hipStream_t st) {
   const void* fn = persistent_kernel(c->m.wdt, c->m.kvdt);
   void* args[] = {&c->kp};
-  HIPCHK(c, hipLaunchCooperativeKernel(fn, dim3(c->n_cus), dim3(kThreads), args, (unsigned)c->lds_bytes, st));
+  HIPCHK(c, hipLaunchCooperativeKernel(fn, dim3(c->n_cus), dim3(kThreads), args, (unsigned)c->lds_bytes_pk, st));
   return PMK_OK;
 }
 
@@ -426,7 +449,7 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   c->tabs = flatten(c->sched);
   c->hash = schedule_hash(c->sched);
   compute_layout(c);
-  if (c->lds_bytes > 160 * 1024) {
+  if (c->lds_bytes > (size_t)kLdsBytes || c->lds_bytes_pk > (size_t)kLdsBytes) {
     delete c;
     return fail(nullptr, PMK_ERR_UNSUPPORTED, "the staged activations and attention scratch exceed 160 KiB of LDS");
   }
@@ -434,11 +457,12 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   if (hip_device >= 0) {
     hipError_t he = hipSetDevice(hip_device);
     const void* fns[2] = {persistent_kernel(c->m.wdt, c->m.kvdt), phase_kernel(c->m.wdt, c->m.kvdt)};
+    // the attribute is an upper bound shared by every context: allow all of a CU's LDS
     for (const void* fn : fns) {
-      if (he == hipSuccess) he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->lds_bytes);
+      if (he == hipSuccess) he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     }
     int per_cu = 0;
-    if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[0], kThreads, c->lds_bytes);
+    if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[0], kThreads, c->lds_bytes_pk);
     if (he != hipSuccess) { delete c; return fail(nullptr, PMK_ERR_HIP, std::string("kernel setup: ") + hipGetErrorString(he)); }
     if (per_cu < 1) { delete c; return fail(nullptr, PMK_ERR_DEVICE, "the persistent kernel cannot be resident on a CU"); }
   }
@@ -684,7 +708,7 @@ static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
   Schedule prev = std::move(c->sched);
   c->sched = std::move(s);
   compute_layout(c);
-  if (c->sizes.workspace_bytes != old_sizes.workspace_bytes || c->lds_bytes > 160 * 1024) {
+  if (c->sizes.workspace_bytes != old_sizes.workspace_bytes || c->lds_bytes > (size_t)kLdsBytes || c->lds_bytes_pk > (size_t)kLdsBytes) {
     c->sched = std::move(prev);
     compute_layout(c);
     return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the rebuilt schedule does not fit the bound buffers or LDS");
@@ -692,8 +716,6 @@ static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
   c->tabs = flatten(c->sched);
   c->hash = schedule_hash(c->sched);
   compute_phases(c);
-  const void* fns[2] = {persistent_kernel(c->m.wdt, c->m.kvdt), phase_kernel(c->m.wdt, c->m.kvdt)};
-  for (const void* fn : fns) HIPCHK(c, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->lds_bytes));
   fill_params(c);
   HIPCHK(c, hipMemcpy(c->ws + c->w_tasks, c->tabs.tasks.data(), c->tabs.tasks.size() * sizeof(pmk_task), hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(c->ws + c->w_qoff, c->tabs.qoff.data(), c->tabs.qoff.size() * 4, hipMemcpyHostToDevice));

@@ -10,6 +10,7 @@ namespace pmk {
 
 constexpr int kThreads = 512;   // one workgroup per CU: 8 wave64s (2 per SIMD)
 constexpr int kWaves = kThreads / 64;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 
 // control words (workspace, uint32) -------------------------------------------------------------
 enum Ctrl : int {
@@ -85,6 +86,9 @@ struct KParams {
   int epi_off;            // LDS float offset of staged epilogue inputs (RoPE row, residual rows)
   int yp_off;             // LDS float offset of per-slice GEMV partial sums [8 * rows]
   int y_off;              // LDS float offset of GEMV row results [rows]
+  int o_epi_off, o_yp_off, o_y_off;  // the same three areas for OPROJ tasks, packed below pf_off
+  int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)
+  int pf_wave;            // 1 KiB units per wave in that area (0: the copy is off)
 };
 
 }  // namespace pmk
