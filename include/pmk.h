@@ -216,9 +216,10 @@ pmk_status pmk_poll_error(pmk_ctx* ctx, pmk_device_error* err);
 
 /* Trace: with trace_steps > 0 and pmk_set_trace(ctx, 1) (which clears the ring), each task of
  * the first trace_steps steps of the next decode call records its wait begin, start and end, and
- * up to four task-specific sub-phase stamps (GEMV: input staged, rows done; attention: scores,
- * partial stored, ticket, combine done), from the constant 100 MHz clock.  pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats
- * gives the mean share of queue time spent waiting. */
+ * up to four task-specific sub-phase stamps (GEMV: input staged, rows done; attention: scores
+ * done, partial stored; combine: partials loaded), from the constant 100 MHz clock.
+ * pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats gives the
+ * mean share of queue time spent waiting. */
 pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
 pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);
 pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
@@ -240,12 +241,13 @@ pmk_status pmk_schedule_get_info(const pmk_ctx* ctx, pmk_schedule_info* info);
 /* ---- Schedule IR, exposed for the validator's tests and the validator CLI ---- */
 typedef enum {
   PMK_OP_QKV = 1,     /* RMSNorm prologue + packed QKV GEMV rows [a0,a1) + RoPE + KV append */
-  PMK_OP_ATTN = 2,    /* split-KV attention partial for kv head a0, split a1 (+ last-arriver combine) */
+  PMK_OP_ATTN = 2,    /* split-KV attention partial (max, sum, P.V) for kv head a0, split a1 */
   PMK_OP_OPROJ = 3,   /* O GEMV rows [a0,a1) + residual */
   PMK_OP_GATEUP = 4,  /* RMSNorm prologue + interleaved gate/up GEMV rows [a0,a1) + SwiGLU */
   PMK_OP_DOWN = 5,    /* down GEMV rows [a0,a1) + residual */
   PMK_OP_LMHEAD = 6,  /* final RMSNorm + LM-head rows [a0,a1) + tile argmax into the step key */
-  PMK_OP_TOKEN = 7    /* reads the step key, writes the output token and the next-input slot */
+  PMK_OP_TOKEN = 7,   /* reads the step key, writes the output token and the next-input slot */
+  PMK_OP_COMBINE = 8  /* merges the attention partials of every split of kv head a0 into o */
 } pmk_op;
 
 typedef struct {
@@ -257,7 +259,7 @@ typedef struct {
   int32_t wait_lag;    /* 0: producers of the same step; 1: of the previous step.  At global step e
                           the wait needs counter >= (e - lag) * producers + wait_count (flags mode:
                           at least wait_count producer flags >= e - lag + 1). */
-  int32_t signal_ctr;  /* counter index, or -1 (ATTN: signalled by the last arriver's combine) */
+  int32_t signal_ctr;  /* counter index, or -1 */
   int32_t signal_slot; /* this producer's flag slot in signal_ctr */
 } pmk_task;
 

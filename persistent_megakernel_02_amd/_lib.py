@@ -26,6 +26,7 @@ PMK_DT_F16, PMK_DT_BF16, PMK_DT_FP8_E4M3 = 0, 1, 2
 PMK_MODE_MEGAKERNEL, PMK_MODE_GRAPH, PMK_MODE_PER_OP = 0, 1, 2
 PMK_SYNC_FLAGS, PMK_SYNC_COUNTERS = 0, 1
 PMK_OP_QKV, PMK_OP_ATTN, PMK_OP_OPROJ, PMK_OP_GATEUP, PMK_OP_DOWN, PMK_OP_LMHEAD, PMK_OP_TOKEN = range(1, 8)
+PMK_OP_COMBINE = 8
 
 i32, i64, u64, f32, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p,
                               ctypes.c_size_t)

@@ -800,7 +800,7 @@ __device__ __forceinline__ float column_max(float v) {
 
 // Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
 // query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
-// the last split to finish (atomic ticket) combines all splits of the group into o.
+// the group's COMBINE task merges the splits into o.
 // Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
 // The K and V chunks are contiguous ([pos][hd]) and are streamed with coalesced 16-byte loads:
 // LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
@@ -834,7 +834,6 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   float* qs = lds;                      // [grp][HD]
   float* red = qs + grp * HD;           // [kWaves][grp][HD] per-wave P.V partials
   float* wml = red + kWaves * grp * HD; // [kWaves][grp][2] per-wave (max, sum)
-  int* last = reinterpret_cast<int*>(wml + kWaves * grp * 2);  // ticket result
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
     kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
@@ -984,21 +983,20 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       stc(partp + (int64_t)j * PSTR + 1, lsum);
     }
   }
-  drain();
-  __syncthreads();
   mark(P, sc, ti, 5);
-  // ---- ticket: the last split of this head group combines ----
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&P.tickets[l * P.nkv + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *last = (int)(old % (uint32_t)S) == S - 1;
-  }
-  __syncthreads();
-  mark(P, sc, ti, 6);
-  if (!*last) return;
-  // Combine, in registers (LDS stays free for the next task's tile): a quad of threads owns four
-  // consecutive dims of one head; its threads take every fourth split and merge them online in
-  // batches of coherent loads (header m, l and the four acc values), then the quad merges its
-  // four (max, sum, acc) with DPP and each thread stores one dim.
+  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// Combine of the attention splits of kv head g: waits for all S partials of the head group, then
+// o = sum_s exp(m_s - M) acc_s / sum_s exp(m_s - M) l_s per head, M = max_s m_s.
+template <int HD>
+__device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, int cu) {
+  constexpr int PSTR = HD + 4;  // partial record: m, l, 2 pad, acc[hd]
+  const int l = t.layer, g = t.a0, S = P.S, grp = P.grp, tid = threadIdx.x;
+  maybe_wait(P, t, sc, cu, ti);
+  // In registers: a quad of threads owns four consecutive dims of one head; its threads take every
+  // fourth split and merge them online in batches of coherent loads (header m, l and the four acc
+  // values), then the quad merges its four (max, sum, acc) with DPP and each thread stores one dim.
   {
     constexpr int QPH = HD / 4;  // dim quads per head
     constexpr int CB = 8;        // splits per thread per batch
@@ -1053,7 +1051,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       stc(o + j * HD + d0 + r, v / den);
     }
   }
-  mark(P, sc, ti, 7);
+  mark(P, sc, ti, 4);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
@@ -1248,6 +1246,10 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
       if (P.hd == 128) task_attn<WDT, KVDT, 128>(P, t, ti, sc, lds, cu);
       else task_attn<WDT, KVDT, 64>(P, t, ti, sc, lds, cu);
       break;
+    case PMK_OP_COMBINE:
+      if (P.hd == 128) task_combine<128>(P, t, ti, sc, cu);
+      else task_combine<64>(P, t, ti, sc, cu);
+      break;
     case PMK_OP_OPROJ: task_oproj<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_DOWN: task_down<WDT>(P, t, ti, sc, lds, cu); break;
@@ -1338,12 +1340,11 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
   for (int k = i; k <= cp.n_steps; k += gridDim.x * blockDim.x) P.keys[k] = 0ull;
 }
 
-// zero flags, counters, tickets and control words; set position and next token
+// zero flags, counters and control words; set position and next token
 __global__ void pmk_reset(KParams P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x, n = gridDim.x * blockDim.x;
   for (int k = i; k < n_flags; k += n) P.flags[k] = 0u;
   for (int k = i; k < n_counters; k += n) P.counters[k] = 0u;
-  for (int k = i; k < P.L * P.nkv; k += n) P.tickets[k] = 0u;
   for (int k = i; k < CTRL_WORDS; k += n) P.ctrl[k] = 0u;
   __syncthreads();
   if (i == 0) {

@@ -61,7 +61,7 @@ struct pmk_ctx {
   int64_t a_embed = 0, a_lm = 0, a_layers = 0, layer_bytes = 0, off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0;
   int64_t a_gains = 0, a_final = 0, a_scales = 0, sc_layer = 0, sc_off[7] = {}, a_sclm = 0, a_rope = 0;
   // workspace layout (bytes)
-  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_tickets = 0, w_keys = 0, w_kvscale = 0, w_x = 0,
+  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_kvscale = 0, w_x = 0,
           w_xm = 0, w_q = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
           w_cprod = 0, w_cflag = 0;
   uint8_t* arena = nullptr;
@@ -190,7 +190,6 @@ void compute_layout(pmk_ctx* c) {
   c->w_call = w; w = align256(w + sizeof(CallParams));
   c->w_flags = w; w = align256(w + (int64_t)s.n_flags * 4);
   c->w_counters = w; w = align256(w + (int64_t)s.counters.size() * 4);
-  c->w_tickets = w; w = align256(w + L * m.nkv * 4);
   c->w_keys = w; w = align256(w + ((int64_t)m.max_seq + 1) * 8);
   c->w_kvscale = w; w = align256(w + L * m.nkv * 2 * 4);
   c->w_x = w; w = align256(w + (L + 1) * H * 4);
@@ -210,11 +209,9 @@ void compute_layout(pmk_ctx* c) {
   // LDS: staged activation vectors, or the attention scratch
   const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
   auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
-  const int64_t S = s.attn_splits, grp = m.grp();
+  const int64_t grp = m.grp();
   // attention: q [grp][hd], per-wave P.V partials [8][grp][hd], per-wave (max, sum) [8][grp][2]
-  // and the ticket word
-  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2 + 4;
-  (void)S;
+  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2;
   const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn});
   c->xs_floats = (int)((xs + 63) / 64 * 64);
   // epilogue inputs staged behind the scratch words: the RoPE row (+ fp8 K/V scales) of QKV tasks,
@@ -222,7 +219,7 @@ void compute_layout(pmk_ctx* c) {
   int64_t epi = m.hd + 4 * (int64_t)m.nkv, rmax = 1;
   for (const pmk_task& t : s.tasks) {
     if (t.op == PMK_OP_OPROJ || t.op == PMK_OP_DOWN) epi = std::max<int64_t>(epi, t.a1 - t.a0);
-    if (t.op != PMK_OP_ATTN && t.op != PMK_OP_TOKEN) rmax = std::max<int64_t>(rmax, t.a1 - t.a0);
+    if (t.op != PMK_OP_ATTN && t.op != PMK_OP_TOKEN && t.op != PMK_OP_COMBINE) rmax = std::max<int64_t>(rmax, t.a1 - t.a0);
   }
   c->epi_floats = (int)((epi + 63) / 64 * 64);
   c->epi_off = c->xs_floats + 64;
@@ -274,7 +271,6 @@ void fill_params(pmk_ctx* c) {
   P.call = reinterpret_cast<CallParams*>(W + c->w_call);
   P.flags = reinterpret_cast<uint32_t*>(W + c->w_flags);
   P.counters = reinterpret_cast<uint32_t*>(W + c->w_counters);
-  P.tickets = reinterpret_cast<uint32_t*>(W + c->w_tickets);
   P.keys = reinterpret_cast<unsigned long long*>(W + c->w_keys);
   P.kv_scale = reinterpret_cast<float*>(W + c->w_kvscale);
   P.x = reinterpret_cast<float*>(W + c->w_x);
@@ -767,7 +763,7 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
   for (int sp = 0; sp < steps; ++sp)
     for (size_t i = 0; i < NT; ++i) {
       const pmk_task& k = c->sched.tasks[i];
-      if (k.op == PMK_OP_ATTN || k.op == PMK_OP_TOKEN) continue;
+      if (k.op == PMK_OP_ATTN || k.op == PMK_OP_TOKEN || k.op == PMK_OP_COMBINE) continue;
       const unsigned long long* r = &t[((size_t)sp * NT + i) * 8];
       if (!r[4] || !r[5] || r[5] <= r[4]) continue;
       const double K = k.op == PMK_OP_DOWN ? m.F : k.op == PMK_OP_OPROJ ? m.qdim() : m.H;
@@ -840,7 +836,7 @@ pmk_status pmk_trace_export(pmk_ctx* c, const char* path) {
   if (s != PMK_OK) return s;
   FILE* f = std::fopen(path, "w");
   if (!f) return fail(c, PMK_ERR_INVALID_ARG, std::string("cannot open ") + path);
-  static const char* names[] = {"?", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "token"};
+  static const char* names[] = {"?", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "token", "combine"};
   const size_t NT = c->sched.tasks.size();
   unsigned long long t0 = ~0ull;
   for (size_t i = 0; i < t.size(); i += 8)
@@ -856,7 +852,7 @@ pmk_status pmk_trace_export(pmk_ctx* c, const char* path) {
       std::fprintf(f, "%s{\"name\":\"wait\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}", first ? "" : ",\n",
                    st, r[3], (r[0] - t0) * 0.01, (t1 - r[0]) * 0.01);
       std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f,\"args\":{\"m4\":%.2f,\"m5\":%.2f,\"m6\":%.2f,\"m7\":%.2f}}",
-                   names[k.op >= 1 && k.op <= 7 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01,
+                   names[k.op >= 1 && k.op <= 8 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01,
                    r[4] >= t1 ? (r[4] - t1) * 0.01 : -1.0, r[5] >= t1 ? (r[5] - t1) * 0.01 : -1.0,
                    r[6] >= t1 ? (r[6] - t1) * 0.01 : -1.0, r[7] >= t1 ? (r[7] - t1) * 0.01 : -1.0);
       first = false;

@@ -64,7 +64,6 @@ struct KParams {
   CallParams* call;
   uint32_t* flags;
   uint32_t* counters;
-  uint32_t* tickets;      // [L][nkv]
   unsigned long long* keys;  // [max_seq + 1]
   float* kv_scale;        // [L][nkv][2]
   float* x;               // [L+1][H]

@@ -3,10 +3,6 @@
 
 namespace pmk {
 
-// LDS floats the attention combine may stage: every partial of a head group (S x grp x (hd + 4))
-// plus the per-split weights (S x grp)
-constexpr int kCombineMaxFloats = 36000;
-
 // Largest weight tile (bytes) one GEMV task may cover: tiles are addressed through a buffer
 // resource with 32-bit offsets, and offsets at or past this bound read as zeros.
 constexpr long long kMaxTileBytes = 0x7FFFFFF0ll;

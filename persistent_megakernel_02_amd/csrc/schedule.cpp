@@ -42,6 +42,7 @@ const char* op_name(int op) {
     case PMK_OP_DOWN: return "DOWN";
     case PMK_OP_LMHEAD: return "LMHEAD";
     case PMK_OP_TOKEN: return "TOKEN";
+    case PMK_OP_COMBINE: return "COMBINE";
   }
   return "?";
 }
@@ -90,15 +91,11 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   if (S <= 0) {
     S = std::max(1, n_queues / m.nkv);
     S = std::min(S, std::max(1, m.max_seq / 16));
-    // the last split's combine stages every partial (S x grp x (hd + 4) floats) in LDS
-    S = std::min(S, std::max(1, 32000 / (m.grp() * (m.hd + 5))));
   }
   // each split's rows must fit the attention task's register batch: 8 waves x kAttnBlocks row
   // blocks of RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) is bounded
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
-  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > kCombineMaxFloats)
-    return "builder: the context is too long for the attention combine's LDS budget";
   s.attn_splits = S;
   s.queues.assign(n_queues, {});
 
@@ -111,13 +108,26 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   const int L = m.L;
   const int n_qkv = std::min(n_queues, m.qkv_rows() / 2);
   const int n_attn = m.nkv * S;
-  const int n_o = std::min(n_queues, m.H);
+  // COMBINE of kv head g runs on the queue of its last split (the shortest one), right after it;
+  // the O projection then skips those queues when enough others remain, so a combine's latency
+  // never delays an O-projection tile
+  std::vector<char> comb_q(n_queues, 0);
+  for (int g = 0; g < m.nkv; ++g) comb_q[(g * S + S - 1) % n_queues] = 1;
+  std::vector<int> o_queues;
+  for (int q = 0; q < n_queues; ++q)
+    if (!comb_q[q]) o_queues.push_back(q);
+  if ((int)o_queues.size() * 2 < n_queues) {
+    o_queues.clear();
+    for (int q = 0; q < n_queues; ++q) o_queues.push_back(q);
+  }
+  const int n_o = std::min((int)o_queues.size(), m.H);
   const int n_gu = std::min(n_queues, m.F);
   const int n_down = std::min(n_queues, m.H);
   const int n_lm = std::min(n_queues, m.V);
   for (int l = 0; l < L; ++l) {
     s.c_qkv.push_back(add_counter(n_qkv, PMK_OP_QKV, l));
-    s.c_cmb.push_back(add_counter(m.nkv, PMK_OP_ATTN, l));
+    for (int g = 0; g < m.nkv; ++g) s.c_attn.push_back(add_counter(S, PMK_OP_ATTN, l));
+    s.c_cmb.push_back(add_counter(m.nkv, PMK_OP_COMBINE, l));
     s.c_oproj.push_back(add_counter(n_o, PMK_OP_OPROJ, l));
     s.c_gu.push_back(add_counter(n_gu, PMK_OP_GATEUP, l));
     s.c_down.push_back(add_counter(n_down, PMK_OP_DOWN, l));
@@ -129,11 +139,15 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     s.queues[q].push_back((int32_t)s.tasks.size() - 1);
   };
   // row range of task i of a GEMV op over `units` (rows, or row pairs) split `parts` ways; task i
-  // runs on queue i
+  // runs on queue qmap[i] (queue i without a map), whose weight sizes its share
   std::vector<int> wb;
-  auto split_op = [&](int op, int units, int parts, int i, int* lo, int* hi) {
+  auto split_op = [&](int op, int units, int parts, int i, int* lo, int* hi, const std::vector<int>* qmap = nullptr) {
     if (rw && (int)rw->w[op].size() >= parts) {
-      if (i == 0) split_weighted(units, parts, rw->w[op], &wb);
+      if (i == 0) {
+        std::vector<double> w(parts);
+        for (int k = 0; k < parts; ++k) w[k] = rw->w[op][qmap ? (*qmap)[k] : k];
+        split_weighted(units, parts, w, &wb);
+      }
       *lo = wb[i];
       *hi = wb[i + 1];
     } else {
@@ -150,16 +164,18 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
       else { t.wait_ctr = s.c_down[l - 1]; t.wait_count = n_down; t.wait_lag = 0; }
       push(i % n_queues, t);
     }
-    // ATTN: kv head g, split j; the last arriver of each head combines and signals c_cmb[l]
+    // ATTN: kv head g, split j, signals the head's counter; COMBINE(g) joins all S splits
     for (int i = 0; i < n_attn; ++i) {
       const int g = i / S, j = i % S;
-      pmk_task t{PMK_OP_ATTN, l, g, j, s.c_qkv[l], n_qkv, 0, s.c_cmb[l], g};
-      push(i % n_queues, t);
+      push(i % n_queues, pmk_task{PMK_OP_ATTN, l, g, j, s.c_qkv[l], n_qkv, 0, s.c_attn[l * m.nkv + g], j});
     }
+    for (int g = 0; g < m.nkv; ++g)
+      push((g * S + S - 1) % n_queues,
+           pmk_task{PMK_OP_COMBINE, l, g, 0, s.c_attn[l * m.nkv + g], S, 0, s.c_cmb[l], g});
     for (int i = 0; i < n_o; ++i) {
       int lo, hi;
-      split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi);
-      push(i % n_queues, pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv, 0, s.c_oproj[l], i});
+      split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi, &o_queues);
+      push(o_queues[i], pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv, 0, s.c_oproj[l], i});
     }
     for (int i = 0; i < n_gu; ++i) {
       int lo, hi;
@@ -247,9 +263,8 @@ void qkv_writes(const ModelDims& m, int l, int a0, int a1, int e, std::vector<Ac
   (void)e;
 }
 
-// Accesses of task t at global step e (e >= 0).  `combine` selects the last-arriver combine
-// of an ATTN task instead of the task's own partial.
-void task_accesses(const Schedule& s, const pmk_task& t, int e, bool combine, std::vector<Access>& acc) {
+// Accesses of task t at global step e (e >= 0).
+void task_accesses(const Schedule& s, const pmk_task& t, int e, std::vector<Access>& acc) {
   const ModelDims& m = s.m;
   const int H = m.H, l = t.layer;
   const int W1 = e + 1;  // stamp written at step e
@@ -269,17 +284,19 @@ void task_accesses(const Schedule& s, const pmk_task& t, int e, bool combine, st
     case PMK_OP_ATTN: {
       const int g = t.a0, grp = m.grp();
       const int64_t part = ((int64_t)l * m.nkv + g) * s.attn_splits;
-      if (!combine) {
-        acc.push_back({B_Q, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
-                       (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_READ, W1});
-        const int64_t kv = ((int64_t)l * m.nkv + g) * 2 * m.hd;
-        acc.push_back({B_KVCUR, kv, kv + 2 * m.hd, A_READ, W1});
-        acc.push_back({B_PART, part + t.a1, part + t.a1 + 1, A_WRITE, W1});
-      } else {
-        acc.push_back({B_PART, part, part + s.attn_splits, A_READ, W1});
-        acc.push_back({B_O, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
-                       (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_WRITE, W1});
-      }
+      acc.push_back({B_Q, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
+                     (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_READ, W1});
+      const int64_t kv = ((int64_t)l * m.nkv + g) * 2 * m.hd;
+      acc.push_back({B_KVCUR, kv, kv + 2 * m.hd, A_READ, W1});
+      acc.push_back({B_PART, part + t.a1, part + t.a1 + 1, A_WRITE, W1});
+      break;
+    }
+    case PMK_OP_COMBINE: {
+      const int g = t.a0, grp = m.grp();
+      const int64_t part = ((int64_t)l * m.nkv + g) * s.attn_splits;
+      acc.push_back({B_PART, part, part + s.attn_splits, A_READ, W1});
+      acc.push_back({B_O, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
+                     (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_WRITE, W1});
       break;
     }
     case PMK_OP_OPROJ:
@@ -310,7 +327,7 @@ void task_accesses(const Schedule& s, const pmk_task& t, int e, bool combine, st
   }
 }
 
-bool valid_op(int op) { return op >= PMK_OP_QKV && op <= PMK_OP_TOKEN; }
+bool valid_op(int op) { return op >= PMK_OP_QKV && op <= PMK_OP_COMBINE; }
 
 // Full-count waits are the only ones that order a specific producer before the waiter.
 bool full_wait(const Schedule& s, const pmk_task& t) {
@@ -360,6 +377,9 @@ std::string validate_schedule(const Schedule& s) {
     if (k.op == PMK_OP_ATTN) {
       if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 < 0 || k.a1 >= S)
         return fmt("integrity: ATTN task %ld has kv head %ld / split %ld out of range", t, k.a0, k.a1);
+    } else if (k.op == PMK_OP_COMBINE) {
+      if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 != 0)
+        return fmt("integrity: COMBINE task %ld has kv head %ld out of range", t, k.a0);
     } else if (lim) {
       if (k.a0 < 0 || k.a1 > lim || k.a0 >= k.a1) return fmt("integrity: task %ld row range [%ld,%ld) invalid", t, k.a0, k.a1);
       if ((k.op == PMK_OP_QKV || k.op == PMK_OP_GATEUP) && ((k.a0 | k.a1) & 1))
@@ -372,38 +392,20 @@ std::string validate_schedule(const Schedule& s) {
     }
   }
   // ---- 2. thresholds and producer counts ----
-  std::vector<std::vector<int>> producers(NC);  // tasks that signal c (ATTN: grouped by slot below)
-  std::map<std::pair<int, int>, std::vector<int>> attn_groups;  // (ctr, slot) -> ATTN tasks
+  std::vector<std::vector<int>> producers(NC);  // tasks that signal c
   for (int t = 0; t < NT; ++t) {
     const pmk_task& k = s.tasks[t];
-    if (k.signal_ctr < 0) continue;
-    if (k.op == PMK_OP_ATTN) attn_groups[{k.signal_ctr, k.signal_slot}].push_back(t);
-    else producers[k.signal_ctr].push_back(t);
+    if (k.signal_ctr >= 0) producers[k.signal_ctr].push_back(t);
   }
   if ((m.max_seq + S - 1) / S > attn_max_chunk(m))
     return fmt("thresholds: %ld attention splits leave chunks longer than the %ld rows a task holds", S, attn_max_chunk(m));
-  if ((int64_t)S * m.grp() * (m.hd + 4) + (int64_t)m.grp() * S > kCombineMaxFloats)
-    return fmt("thresholds: %ld attention splits exceed the combine's LDS budget", S);
-  for (auto& kv : attn_groups) {
-    if (!producers[kv.first.first].empty())
-      return fmt("thresholds: counter %ld mixes combine and task signals", kv.first.first);
-    if ((int)kv.second.size() != S)
-      return fmt("thresholds: combine slot %ld of counter %ld has %ld splits, the kernel joins %ld", kv.first.second,
-                 kv.first.first, (long)kv.second.size(), S);
-    std::set<int> splits;
-    for (int t : kv.second) splits.insert(s.tasks[t].a1);
-    if ((int)splits.size() != S) return fmt("thresholds: combine slot %ld of counter %ld repeats a split", kv.first.second, kv.first.first);
-  }
   std::vector<int> nprod(NC, 0);
   for (int c = 0; c < NC; ++c) nprod[c] = (int)producers[c].size();
-  for (auto& kv : attn_groups) nprod[kv.first.first] += 1;
   for (int c = 0; c < NC; ++c) {
     if (nprod[c] != s.counters[c].producers)
       return fmt("thresholds: counter %ld declares %ld producers but %ld tasks signal it", c, s.counters[c].producers, nprod[c]);
     std::set<int> slots;
     for (int t : producers[c]) slots.insert(s.tasks[t].signal_slot);
-    for (auto& kv : attn_groups)
-      if (kv.first.first == c) slots.insert(kv.first.second);
     if ((int)slots.size() != nprod[c] || (nprod[c] && (*slots.begin() != 0 || *slots.rbegin() != nprod[c] - 1)))
       return fmt("thresholds: counter %ld producer slots are not 0..%ld", c, nprod[c] - 1);
   }
@@ -418,7 +420,6 @@ std::string validate_schedule(const Schedule& s) {
   {
     const int STEPS = 2;
     std::vector<int64_t> ctr(NC, 0);
-    std::map<std::pair<int, int>, int64_t> ticket;
     std::vector<int> head(NQ, 0);  // position in the unrolled queue (step * len + i)
     bool progress = true;
     while (progress) {
@@ -432,14 +433,7 @@ std::string validate_schedule(const Schedule& s) {
             const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
             if (ctr[k.wait_ctr] < need) break;
           }
-          if (k.signal_ctr >= 0) {
-            if (k.op == PMK_OP_ATTN) {
-              int64_t& tk = ticket[{k.signal_ctr, k.signal_slot}];
-              if (++tk % S == 0) ctr[k.signal_ctr] += 1;
-            } else {
-              ctr[k.signal_ctr] += 1;
-            }
-          }
+          if (k.signal_ctr >= 0) ctr[k.signal_ctr] += 1;
           ++head[q];
           progress = true;
         }
@@ -458,29 +452,17 @@ std::string validate_schedule(const Schedule& s) {
     }
   }
   // ---- 4/5. happens-before over two unrolled steps (vector clocks) ----
-  // Nodes: real tasks (t, e) on queue q at unrolled index e*len(q)+i; virtual combine nodes
-  // (counter, slot, e) on their own virtual queue at index e.
-  std::vector<std::pair<int, int>> vkeys;
-  std::map<std::pair<int, int>, int> vidx;
-  for (auto& kv : attn_groups) {
-    vidx[kv.first] = (int)vkeys.size();
-    vkeys.push_back(kv.first);
-  }
-  const int NV = (int)vkeys.size();
-  const int W = NQ + NV;  // vector clock width
+  // Nodes: tasks (t, e) on queue q at unrolled index e*len(q)+i.
+  const int W = NQ;  // vector clock width
   const int STEPS = 2;
   // topological processing: simulate again, computing clocks as tasks complete
   std::vector<int16_t> vc_task((size_t)STEPS * NT * W, -1);
-  std::vector<int16_t> vc_virt((size_t)STEPS * NV * W, -1);
   std::vector<int16_t> join_ctr((size_t)STEPS * NC * W, -1);
-  std::vector<int> join_count((size_t)STEPS * NC, 0);
   auto vt = [&](int t, int e) { return &vc_task[((size_t)e * NT + t) * W]; };
-  auto vv = [&](int v, int e) { return &vc_virt[((size_t)e * NV + v) * W]; };
   auto jc = [&](int c, int e) { return &join_ctr[((size_t)e * NC + c) * W]; };
   auto vmax = [&](int16_t* a, const int16_t* b) { for (int i = 0; i < W; ++i) a[i] = std::max(a[i], b[i]); };
   {
     std::vector<int64_t> ctr(NC, 0);
-    std::map<std::pair<int, int>, int64_t> ticket;
     std::vector<int> head(NQ, 0);
     bool progress = true;
     while (progress) {
@@ -502,22 +484,8 @@ std::string validate_schedule(const Schedule& s) {
           v[q] = (int16_t)head[q];
           if (full_wait(s, k) && e - k.wait_lag >= 0) vmax(v, jc(k.wait_ctr, e - k.wait_lag));
           if (k.signal_ctr >= 0) {
-            if (k.op == PMK_OP_ATTN) {
-              const int vi = vidx[{k.signal_ctr, k.signal_slot}];
-              int16_t* cv = vv(vi, e);
-              vmax(cv, v);
-              int64_t& tk = ticket[{k.signal_ctr, k.signal_slot}];
-              if (++tk % S == 0) {
-                cv[NQ + vi] = (int16_t)e;
-                vmax(jc(k.signal_ctr, e), cv);
-                join_count[(size_t)e * NC + k.signal_ctr]++;
-                ctr[k.signal_ctr] += 1;
-              }
-            } else {
-              vmax(jc(k.signal_ctr, e), v);
-              join_count[(size_t)e * NC + k.signal_ctr]++;
-              ctr[k.signal_ctr] += 1;
-            }
+            vmax(jc(k.signal_ctr, e), v);
+            ctr[k.signal_ctr] += 1;
           }
           ++head[q];
           progress = true;
@@ -528,37 +496,29 @@ std::string validate_schedule(const Schedule& s) {
   // node identity for hb queries
   struct Node { int queue, index; const int16_t* vc; };
   auto task_node = [&](int t, int e) { return Node{queue_of[t], e * (int)s.queues[queue_of[t]].size() + pos_of[t], vt(t, e)}; };
-  auto virt_node = [&](int v, int e) { return Node{NQ + v, e, vv(v, e)}; };
   auto hb = [&](const Node& a, const Node& b) { return b.vc[a.queue] >= a.index; };
 
   // ---- 4. join completeness: a reader of a region written by a multi-producer phase waits on all of it ----
-  struct Acc { Access a; Node n; int task; int e; bool virt; };
+  struct Acc { Access a; Node n; int task; int e; };
   std::vector<std::vector<Acc>> by_buf(B_COUNT);
   std::vector<Access> tmp;
-  for (int e = 0; e < STEPS; ++e) {
+  for (int e = 0; e < STEPS; ++e)
     for (int t = 0; t < NT; ++t) {
       tmp.clear();
-      task_accesses(s, s.tasks[t], e, false, tmp);
-      for (auto& a : tmp) by_buf[a.buf].push_back({a, task_node(t, e), t, e, false});
+      task_accesses(s, s.tasks[t], e, tmp);
+      for (auto& a : tmp) by_buf[a.buf].push_back({a, task_node(t, e), t, e});
     }
-    for (int v = 0; v < NV; ++v) {
-      tmp.clear();
-      const int t0 = attn_groups[vkeys[v]][0];
-      task_accesses(s, s.tasks[t0], e, true, tmp);
-      for (auto& a : tmp) by_buf[a.buf].push_back({a, virt_node(v, e), t0, e, true});
-    }
-  }
   for (int t = 0; t < NT; ++t) {
     const pmk_task& k = s.tasks[t];
     if (k.wait_ctr < 0 || full_wait(s, k)) continue;
     // partial wait: does this task read anything that producers of the waited counter write?
     tmp.clear();
-    task_accesses(s, k, 1, false, tmp);
+    task_accesses(s, k, 1, tmp);
     std::vector<Access> prod;
     for (int p = 0; p < NT; ++p) {
       const pmk_task& pk = s.tasks[p];
       if (pk.signal_ctr != k.wait_ctr) continue;
-      task_accesses(s, pk, 1 - k.wait_lag, pk.op == PMK_OP_ATTN, prod);
+      task_accesses(s, pk, 1 - k.wait_lag, prod);
     }
     for (auto& r : tmp)
       if (r.kind == A_READ)
@@ -566,6 +526,42 @@ std::string validate_schedule(const Schedule& s) {
           if (w.kind != A_READ && w.buf == r.buf && w.lo < r.hi && r.lo < w.hi)
             return fmt("join: task %ld reads a region that %ld producers of counter %ld write but waits for only %ld of them",
                        t, s.counters[k.wait_ctr].producers, k.wait_ctr, k.wait_count);
+  }
+  // ---- 4b. coverage: every element a task reads as a value of some step is written in that step ----
+  for (int b = 0; b < B_COUNT; ++b) {
+    // merged write intervals per stamp (stamp = step of the write + 1)
+    std::map<int, std::vector<std::pair<int64_t, int64_t>>> wr;
+    for (const Acc& x : by_buf[b])
+      if (x.a.kind != A_READ) wr[x.a.expect].push_back({x.a.lo, x.a.hi});
+    for (auto& kv : wr) {
+      auto& v = kv.second;
+      std::sort(v.begin(), v.end());
+      std::vector<std::pair<int64_t, int64_t>> merged;
+      for (auto& iv : v) {
+        if (!merged.empty() && iv.first <= merged.back().second) merged.back().second = std::max(merged.back().second, iv.second);
+        else merged.push_back(iv);
+      }
+      v.swap(merged);
+    }
+    for (const Acc& x : by_buf[b]) {
+      if (x.a.kind != A_READ || x.a.expect < 1) continue;  // stamp 0: contents from before the first step
+      const auto it = wr.find(x.a.expect);
+      bool ok = false;
+      if (it != wr.end()) {
+        const auto& v = it->second;
+        auto p = std::upper_bound(v.begin(), v.end(), std::make_pair(x.a.lo, INT64_MAX));
+        if (p != v.begin()) {
+          --p;
+          ok = p->first <= x.a.lo && x.a.hi <= p->second;
+        }
+      }
+      if (!ok) {
+        std::ostringstream os;
+        os << "coverage: " << op_name(s.tasks[x.task].op) << " task " << x.task << " (step " << x.e << ") reads buffer " << b
+           << " elements [" << x.a.lo << ", " << x.a.hi << ") that no task of step " << x.a.expect - 1 << " writes whole";
+        return os.str();
+      }
+    }
   }
   // ---- 5. happens-before on every conflicting pair (within a step and across consecutive steps) ----
   for (int b = 0; b < B_COUNT; ++b) {
@@ -598,9 +594,9 @@ std::string validate_schedule(const Schedule& s) {
         }
         if (!hb(first->n, second->n)) {
           std::ostringstream os;
-          os << "race: " << (first->virt ? "combine after " : "") << op_name(s.tasks[first->task].op) << " task " << first->task
+          os << "race: " << op_name(s.tasks[first->task].op) << " task " << first->task
              << " (step " << first->e << ", " << (first->a.kind == A_READ ? "read" : "write") << ") is not ordered before "
-             << (second->virt ? "combine after " : "") << op_name(s.tasks[second->task].op) << " task " << second->task
+             << op_name(s.tasks[second->task].op) << " task " << second->task
              << " (step " << second->e << ", " << (second->a.kind == A_READ ? "read" : "write") << ") on buffer " << b
              << " elements [" << std::max(x.a.lo, y.a.lo) << ", " << std::min(x.a.hi, y.a.hi) << ")";
           return os.str();
@@ -625,8 +621,6 @@ std::string validate_schedule(const Schedule& s) {
   for (int t = 0; t < NT; ++t)
     if (t != tok && !hb(task_node(t, 0), tn))
       return fmt("reachability: task %ld does not reach the greedy choice of its step (", t) + op_name(s.tasks[t].op) + ")";
-  for (int v = 0; v < NV; ++v)
-    if (!hb(virt_node(v, 0), tn)) return fmt("reachability: combine %ld does not reach the greedy choice", v);
   return "";
 }
 
@@ -634,7 +628,7 @@ std::string validate_schedule(const Schedule& s) {
 // CPU simulator: one host thread per queue, poisoned stamp buffers, random yields
 // ================================================================================================
 pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::string* report) {
-  const int NQ = s.n_queues, NC = (int)s.counters.size(), S = s.attn_splits;
+  const int NQ = s.n_queues, NC = (int)s.counters.size();
   BufDims bd = buf_dims(s, steps);
   int64_t total = 0;
   for (int b = 0; b < B_COUNT; ++b) total += bd.size[b];
@@ -646,11 +640,6 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
   }
   std::unique_ptr<std::atomic<int64_t>[]> ctr(new std::atomic<int64_t>[NC]);
   for (int c = 0; c < NC; ++c) ctr[c].store(0);
-  std::map<std::pair<int, int>, int> tslot;
-  for (auto& t : s.tasks)
-    if (t.op == PMK_OP_ATTN && t.signal_ctr >= 0) tslot.emplace(std::make_pair(t.signal_ctr, t.signal_slot), (int)tslot.size());
-  std::unique_ptr<std::atomic<int64_t>[]> ticket(new std::atomic<int64_t>[tslot.size() + 1]);
-  for (size_t i = 0; i <= tslot.size(); ++i) ticket[i].store(0);
   std::atomic<bool> abort_flag{false};
   std::mutex mu;
   std::string first_error;
@@ -685,7 +674,7 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
   };
   auto worker = [&](int q) {
     std::mt19937_64 rng(seed * 1000003ull + q);
-    std::vector<Access> acc, cacc;
+    std::vector<Access> acc;
     const auto& queue = s.queues[q];
     for (int e = 0; e < steps && !abort_flag.load(); ++e) {
       for (int t : queue) {
@@ -706,26 +695,13 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
           }
         }
         acc.clear();
-        task_accesses(s, k, e, false, acc);
+        task_accesses(s, k, e, acc);
         run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads at start
         if ((rng() & 3) == 0) std::this_thread::yield();
         run_accesses(rng, acc, e, true, op_name(k.op), t);   // writes
-        if (k.op != PMK_OP_ATTN) run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads again: catches WAR
+        run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads again: catches WAR
         if (abort_flag.load()) return;
-        if (k.signal_ctr < 0) continue;
-        if (k.op == PMK_OP_ATTN) {
-          auto& tk = ticket[tslot[{k.signal_ctr, k.signal_slot}]];
-          const int64_t old = tk.fetch_add(1);
-          if (old % S == S - 1) {
-            cacc.clear();
-            task_accesses(s, k, e, true, cacc);
-            run_accesses(rng, cacc, e, false, "combine", t);
-            run_accesses(rng, cacc, e, true, "combine", t);
-            ctr[k.signal_ctr].fetch_add(1);
-          }
-        } else {
-          ctr[k.signal_ctr].fetch_add(1);
-        }
+        if (k.signal_ctr >= 0) ctr[k.signal_ctr].fetch_add(1);
       }
     }
   };

@@ -25,7 +25,7 @@ struct ModelDims {
 };
 
 struct Counter {
-  int producers;  // signals per step (ATTN combine counters: one per kv head)
+  int producers;  // signals per step
   int flag_base;  // first flag word of this counter in flags mode
   int phase;      // op of its producers (for diagnostics)
   int layer;
@@ -42,7 +42,7 @@ struct Schedule {
   int n_flags = 0;
   // counter ids
   int c_lm = -1;
-  std::vector<int> c_qkv, c_cmb, c_oproj, c_gu, c_down;
+  std::vector<int> c_qkv, c_attn, c_cmb, c_oproj, c_gu, c_down;  // c_attn: [L][nkv]
 };
 
 // Longest attention split (positions) one task holds in registers.

@@ -16,7 +16,7 @@ import persistent_megakernel_02_amd as pmk
 from persistent_megakernel_02_amd import _lib
 from synthgen import WORKLOADS
 
-OPS = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "TOKEN"}
+OPS = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "TOKEN", 8: "COMBINE"}
 
 
 class Sched:
@@ -108,7 +108,7 @@ def mutants(w, n_cus, rng, per_kind):
     # the first QKV tasks on the queue that ends with the TOKEN task are already ordered after the
     # previous step's LM head by program order, so their wait is redundant (dropping it is safe)
     waiting = [i for i, t in enumerate(tasks) if t.wait_ctr >= 0 and not (t.op == 1 and t.layer == 0 and i in q0)]
-    signalling = [i for i, t in enumerate(tasks) if t.signal_ctr >= 0 and t.op != 2]
+    signalling = [i for i, t in enumerate(tasks) if t.signal_ctr >= 0]
     full = [i for i in waiting if tasks[i].wait_count == base.producers(tasks[i].wait_ctr)
             and base.producers(tasks[i].wait_ctr) > 1]
 
@@ -127,10 +127,11 @@ def mutants(w, n_cus, rng, per_kind):
     def wrong_lag(s, i):        # waits for the previous step's producers: reads stale data
         t = s.task(i); t.wait_lag = 1 - t.wait_lag; s.set_task(i, t)
 
-    def back_edge(s, i):        # waits on a counter produced later in the same step (by its dependants)
-        t = s.task(i)
+    def back_edge(s, i):        # waits on a counter produced later in the same step (by its dependants;
+        t = s.task(i)           # another kv head's attention splits do not depend on an ATTN task)
         own = max(t.signal_ctr, t.wait_ctr if t.wait_lag == 0 else -1)
-        later = sorted({tasks[j].signal_ctr for j in signalling if tasks[j].signal_ctr > own})
+        later = sorted({tasks[j].signal_ctr for j in signalling
+                        if tasks[j].signal_ctr > own and not (t.op == 2 and tasks[j].op == 2)})
         t.wait_ctr = rng.choice(later)
         t.wait_lag = 0
         t.wait_count = s.producers(t.wait_ctr)
@@ -151,15 +152,22 @@ def mutants(w, n_cus, rng, per_kind):
             t.signal_slot = t.signal_slot + 1
         s.set_task(i, t)
 
-    def alias_rows(s, i):       # two tasks of one phase write overlapping output rows
-        t = s.task(i)
-        peers = [j for j in signalling if tasks[j].op == t.op and tasks[j].layer == t.layer and j != i
-                 and t.op in (3, 5, 6)]
-        if not peers:
-            t.a1 = t.a0  # empty range: referential integrity
-        else:
+    def alias_rows(s, i):       # two tasks of one phase produce the same output, so some output of
+        t = s.task(i)           # the phase is produced by none (or an empty range: integrity)
+        peers = [j for j in signalling if tasks[j].op == t.op and tasks[j].layer == t.layer and j != i]
+        if t.op in (3, 5, 6) and peers:
             p = tasks[rng.choice(peers)]
             t.a0, t.a1 = p.a0, p.a1
+        elif t.op == 2 and peers:   # ATTN: another task's (kv head, split)
+            p = tasks[rng.choice(peers)]
+            t.a0, t.a1 = p.a0, p.a1
+        elif t.op == 8:             # COMBINE: another head's combine, or an invalid field
+            if peers:
+                t.a0 = tasks[rng.choice(peers)].a0
+            else:
+                t.a1 = 1
+        else:
+            t.a1 = t.a0
         s.set_task(i, t)
 
     def swap_queue(s, q):       # a task moved before the task whose signal it (transitively) needs
