@@ -111,7 +111,8 @@ typedef struct {
 
 typedef struct {
   uint64_t arena_bytes;     /* packed weights, gains, scales, RoPE table */
-  uint64_t kv_bytes;        /* K and V caches: 2 * L * n_kv * max_seq * head_dim * elem */
+  uint64_t kv_bytes;        /* K and V caches: 2 * L * n_kv * seqcap * head_dim * elem, where
+                               seqcap = max_seq rounded up to 32 (each half 256-byte aligned) */
   uint64_t workspace_bytes; /* activations, partials, flags, counters, trace */
 } pmk_sizes;
 

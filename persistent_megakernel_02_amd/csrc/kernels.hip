@@ -704,16 +704,21 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
       stc(q + i + half, b);
       continue;
     }
-    const int64_t row = (((int64_t)l * P.nkv + head) * P.max_seq + sc.pos) * hd;
+    // element index of dims i and i + hd/2 at this position: K [pos][hd] rows; V in blocks of 32
+    // positions, [pos / 32][hd][pos % 32]
+    const int64_t hb = (int64_t)l * P.nkv + head;
+    const int64_t ia = sec == 1 ? (hb * P.seqcap + sc.pos) * hd + i
+                                : ((hb * (P.seqcap / 32) + sc.pos / 32) * hd + i) * 32 + sc.pos % 32;
+    const int64_t ib = sec == 1 ? ia + half : ia + (int64_t)half * 32;
     uint8_t* cache = sec == 1 ? P.kc : P.vc;
     if constexpr (KVDT == WFP8) {
       const float s8 = rope[half + 2 * head + (sec - 1)].x;
-      stc(cache + row + i, enc_e4m3(a / s8));
-      stc(cache + row + i + half, enc_e4m3(b / s8));
+      stc(cache + ia, enc_e4m3(a / s8));
+      stc(cache + ib, enc_e4m3(b / s8));
     } else {
       uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
-      stc(c16 + row + i, enc16<KVDT>(a));
-      stc(c16 + row + i + half, enc16<KVDT>(b));
+      stc(c16 + ia, enc16<KVDT>(a));
+      stc(c16 + ib, enc16<KVDT>(b));
     }
   }
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
@@ -724,53 +729,14 @@ __device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
   return u32x4{ldc(q), ldc(q + 1), ldc(q + 2), ldc(q + 3)};
 }
 
-// Sum over groups of `n` adjacent lanes (n = 8 or 16, inside one DPP row); every lane of the
-// group receives the group's sum.
-__device__ __forceinline__ float group_sum(float v, int n) {
-  int x = __float_as_int(v);
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
-  x = __float_as_int(v);
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
-  x = __float_as_int(v);
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  if (n == 16) {
-    x = __float_as_int(v);
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));  // row_mirror
-  }
-  return v;
-}
-
 // Max / sum over the four lanes of a quad (quad_perm DPP); every lane of the quad receives it.
 __device__ __forceinline__ float quad_max(float v) {
-  v = dpp_max<0xB1, 0xF>(v);  // quad_perm [1,0,3,2]
+  v = dpp_max<0xB1, 0xF>(v);     // quad_perm [1,0,3,2]
   return dpp_max<0x4E, 0xF>(v);  // quad_perm [2,3,0,1]
 }
 __device__ __forceinline__ float quad_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-
-template <int KVDT>
-__device__ __forceinline__ void decode_chunk(u32x4 w, float* out) {
-  if constexpr (KVDT == WFP8) {
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], true);
-      out[4 * k] = lo.x;
-      out[4 * k + 1] = lo.y;
-      out[4 * k + 2] = hi.x;
-      out[4 * k + 3] = hi.y;
-    }
-  } else {
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      out[2 * k] = dec16<KVDT>((uint16_t)(wd[k] & 0xffffu));
-      out[2 * k + 1] = dec16<KVDT>((uint16_t)(wd[k] >> 16));
-    }
-  }
 }
 
 // Sum / max over the lanes that share `lane % N` (N = 8 or 16 lanes per row): the other half of
@@ -798,166 +764,217 @@ __device__ __forceinline__ float column_max(float v) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// ---- 16-bit matrix-core operands (v_mfma_f32_16x16x32_{f16,bf16}) ----
+// A (16 x 32): lane l holds row l % 16, k = 8 (l / 16) .. + 8; B (32 x 16): lane l holds column
+// l % 16, k = 8 (l / 16) .. + 8; C (16 x 16): lane l holds rows 4 (l / 16) + i, column l % 16.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// the MFMA input type for a KV cache format: f16 for an f16 cache, bf16 otherwise (FP8 E4M3
+// values are exact in bf16)
+template <int KVDT>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (KVDT == WF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+// fp32 x[8] as two 16-bit vectors with x = hi + lo to ~2^-17 relative: an fp32 operand of a
+// 16-bit matrix product costs two products (hi, then lo) accumulated in fp32.
+template <int KVDT>
+__device__ __forceinline__ void split16(const float* x, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = x[2 * k], b = x[2 * k + 1];
+    if constexpr (KVDT == WF16) {
+      const auto hp = __builtin_amdgcn_cvt_pkrtz(a, b);
+      const auto lp = __builtin_amdgcn_cvt_pkrtz(a - (float)hp[0], b - (float)hp[1]);
+      h[k] = __builtin_bit_cast(uint32_t, hp);
+      o[k] = __builtin_bit_cast(uint32_t, lp);
+    } else {
+      const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+      const float ha = __uint_as_float(hb << 16), hbv = __uint_as_float(hb & 0xFFFF0000u);
+      h[k] = hb;
+      o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a - ha, b - hbv}, bf16x2));
+    }
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// 8 FP8 E4M3 values -> 8 bf16 (exact)
+__device__ __forceinline__ u32x4 fp8x8_bf16(u32x2 w) {
+  const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+  const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+  auto hi16 = [](f32x2 f) { return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u); };
+  return u32x4{hi16(f0), hi16(f1), hi16(f2), hi16(f3)};
+}
+
+// KV cache element loads through a buffer resource (out of range: zeros): 8 elements per lane;
+// past rows are streamed (nontemporal), the current position coherently.
+template <int KVDT, bool COHERENT>
+__device__ __forceinline__ u32x4 kv_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (KVDT == WFP8) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, COHERENT ? 16 : 2);
+    return fp8x8_bf16(w);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, COHERENT ? 16 : 2);
+  }
+}
+
+// Zero the 16-bit elements j >= nv of an 8-element operand (0 <= nv < 8).
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] &= (2 * k < nv ? 0x0000FFFFu : 0u) | (2 * k + 1 < nv ? 0xFFFF0000u : 0u);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Split-KV attention for kv head g, split j over positions [t0, t1) of T = pos + 1, for the grp
-// query heads of the group; the partial (m, l, acc[hd]) of each head goes to the workspace, and
-// the group's COMBINE task merges the splits into o.
+// query heads of the group (grp <= 16); the partial (m, l, acc[hd]) of each head goes to the
+// workspace, and the group's COMBINE task merges the splits into o.
 // Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
-// The K and V chunks are contiguous ([pos][hd]) and are streamed with coalesced 16-byte loads:
-// LPR lanes cover one row (LPR = row bytes / 16), so a wave instruction covers RPI = 64 / LPR rows;
-// row block b of the chunk goes to wave b % 8, register slot b / 8.  Rows of past positions are
-// loaded before the dependency wait; the current position's row (written this step) after it,
-// coherently, in the same round trip as q.
-// Inside the workgroup each wave runs its own softmax over its rows, in registers: scores, the
-// wave's max and sum per head (reduced across the rows of an instruction with column_max /
-// column_sum), probabilities and P.V; the eight waves' (max, sum, acc) are then merged in LDS with
-// the usual rescaling, exactly as the splits are merged by the combine.
+// On the matrix cores: wave w takes the 32 positions p0 = t0 + 32 w .. + 32 (chunks are whole
+// 32-position blocks).  Scores are two 16 x 16 products per 32-dim slice, K rows (A, from
+// the [pos][hd] cache) times q (B, heads as columns); the A rows are the positions in the order
+// p0 + 8 (r / 4) + r % 4 (block 0) and + 4 (block 1), so that lane l ends up holding the scores of
+// positions p0 + 8 (l / 16) .. + 8 of head l % 16, which is exactly its B operand of P.V.  P.V is
+// V^T (A: 8 positions of one dim per lane) times P, one 16 x 16 product
+// per 16 dims (V is stored in blocks of 32 positions, [pos / 32][hd][pos % 32], so one wave
+// instruction reads 1 KiB of contiguous cache).  q and P enter as 16-bit hi + lo pairs (two products each), so the result keeps
+// about fp32 precision.  Rows of past positions are loaded before the dependency wait; the
+// current position (written this step) after it, coherently.  The wave's softmax (max and sum
+// across the four lanes of a head column with column_max / column_sum) runs on the 8 scores a
+// lane holds; the eight waves' (max, sum, acc) are then merged in LDS with the usual rescaling,
+// exactly as the splits are merged by the combine.
 template <int WDT, int KVDT, int HD>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
-  constexpr int EPL = 16 / KES;       // elements per 16-byte chunk
-  constexpr int NB = kAttnBlocks;     // row blocks per wave, all held in registers (the builder bounds the split)
-  constexpr int ROWB = HD * KES;      // row bytes: 128 or 256
-  constexpr int LPR = ROWB / 16;      // 8 or 16 lanes per row
-  constexpr int RPI = 64 / LPR;       // 8 or 4 rows per wave instruction
+  constexpr int ROWB = HD * KES;      // K row bytes
+  constexpr int NC = HD / 32;         // 32-dim slices of the score product
+  constexpr int NT = HD / 16;         // 16-dim tiles of P.V
   constexpr int PSTR = HD + 4;        // partial record: m, l, 2 pad, acc[hd] (16-byte aligned)
+  constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;
   const int l = t.layer, g = t.a0, split = t.a1, S = P.S, grp = P.grp;
   const int T = sc.pos + 1;
-  const int chunk = (T + S - 1) / S;
+  const int chunk = ((T + S - 1) / S + 31) & ~31;
   const int t0 = min(T, split * chunk), t1 = min(T, t0 + chunk);
-  const int n = t1 - t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPR, part = lane % LPR;
-  const int64_t headbase = ((int64_t)l * P.nkv + g) * P.max_seq;
-  const uint8_t* Kc = P.kc + headbase * ROWB;
-  const uint8_t* Vc = P.vc + headbase * ROWB;
+  const int col = lane & 15, grp4 = lane >> 4;  // MFMA column / row-group of this lane
+  const int64_t head = (int64_t)l * P.nkv + g;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      P.kc + head * P.seqcap * ROWB, (short)0, (int)((int64_t)P.seqcap * ROWB), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      P.vc + head * HD * P.seqcap * KES, (short)0, (int)((int64_t)HD * P.seqcap * KES), 0x00020000);
   float* qs = lds;                      // [grp][HD]
   float* red = qs + grp * HD;           // [kWaves][grp][HD] per-wave P.V partials
   float* wml = red + kWaves * grp * HD; // [kWaves][grp][2] per-wave (max, sum)
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
-    kscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2];
-    vscale = P.kv_scale[((int64_t)l * P.nkv + g) * 2 + 1];
+    kscale = P.kv_scale[head * 2];
+    vscale = P.kv_scale[head * 2 + 1];
   }
-  auto row_of = [&](int i) { return t0 + (wave + kWaves * i) * RPI + sub; };  // position of register slot i
-  const int nbu = (n + kWaves * RPI - 1) / (kWaves * RPI);  // register slots that hold rows (block uniform)
-  // rows of past positions: loaded before the dependency wait
-  u32x4 kb[NB], vb[NB];
+  const int p0 = t0 + 32 * wave;
+  // K rows of this lane in the two score blocks, V^T positions of this lane
+  const int pk0 = p0 + 8 * (col >> 2) + (col & 3), pk1 = pk0 + 4;
+  const int pv = p0 + 8 * grp4;
+  const bool cur0 = pk0 == sc.pos, cur1 = pk1 == sc.pos;
+  const bool vcur = pv <= sc.pos && sc.pos < pv + 8;
+  auto koff = [&](int p, int c) {
+    return p < t1 ? (uint32_t)(p * ROWB + (32 * c + 8 * grp4) * KES) : kOut;
+  };
+  auto voff = [&](int tt) {
+    return pv < t1 ? (uint32_t)((((pv >> 5) * HD + 16 * tt + col) * 32 + (pv & 31)) * KES) : kOut;
+  };
+  // past positions: before the dependency wait
+  u32x4 ka[NC], kb[NC], vt[NT];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int pt = row_of(i);
-    const bool ok = pt < t1 && pt != sc.pos;
-    const int64_t off = (int64_t)(ok ? pt : t0) * ROWB + part * 16;
-    kb[i] = ok ? ld_nt(Kc + off) : u32x4{0u, 0u, 0u, 0u};
-    vb[i] = ok ? ld_nt(Vc + off) : u32x4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < NC; ++c) {
+    ka[c] = kv_load8<KVDT, false>(kr, cur0 ? kOut : koff(pk0, c));
+    kb[c] = kv_load8<KVDT, false>(kr, cur1 ? kOut : koff(pk1, c));
   }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, false>(vr, vcur ? kOut : voff(tt));
   maybe_wait(P, t, sc, cu, ti);
-  // the current position's row (this split holds it when t0 <= pos < t1): issued with q's loads
-  const int rel = sc.pos - t0;
-  const bool cur_here = rel >= 0 && rel < n;
-  const int cur_slot = cur_here ? rel / RPI / kWaves : -1;
-  const bool cur_lane = cur_here && (rel / RPI) % kWaves == wave && rel % RPI == sub;
-  u32x4 kcur = u32x4{0u, 0u, 0u, 0u}, vcur = u32x4{0u, 0u, 0u, 0u};
-  if (cur_lane) {
-    kcur = ldc16(coherent_rsrc(Kc + (int64_t)sc.pos * ROWB, ROWB), part * 16);
-    vcur = ldc16(coherent_rsrc(Vc + (int64_t)sc.pos * ROWB, ROWB), part * 16);
+  // the current position (written this step): coherent loads, with q's
+  if (cur0 || cur1) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 v = kv_load8<KVDT, true>(kr, koff(sc.pos, c));
+      if (cur0) ka[c] = v;
+      else kb[c] = v;
+    }
+  }
+  if (vcur) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, true>(vr, voff(tt));
   }
   load_vector<false>(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD, grp * HD, qs);
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (cur_lane && i == cur_slot) {
-      kb[i] = kcur;
-      vb[i] = vcur;
-    }
   __syncthreads();
+  // positions past the split's end (the last V^T group may straddle it) contribute nothing
+  if (pv < t1 && pv + 8 > t1) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = keep_first(vt[tt], t1 - pv);
+  }
   const float qk_scale = kscale * P.attn_scale;
-  for (int jb = 0; jb < grp; jb += 4) {
-    // ---- scores of this lane's row in each slot, four heads at a time ----
-    float sco[NB][4];
-    {
-      float qr[4][EPL];
+  // ---- scores: blocks 0 and 1 of 16 positions x 16 head columns ----
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+  for (int c = 0; c < NC; ++c) {
+    float qv[8];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qr[jj][e] = jb + jj < grp ? qs[(jb + jj) * HD + part * EPL + e] : 0.f;
+    for (int e = 0; e < 8; ++e) qv[e] = col < grp ? qs[col * HD + 32 * c + 8 * grp4 + e] : 0.f;
+    u32x4 qh, ql;
+    split16<KVDT>(qv, qh, ql);
+    s0 = mfma16<KVDT>(ka[c], qh, s0);
+    s0 = mfma16<KVDT>(ka[c], ql, s0);
+    s1 = mfma16<KVDT>(kb[c], qh, s1);
+    s1 = mfma16<KVDT>(kb[c], ql, s1);
+  }
+  // ---- softmax over this wave's positions: lane holds positions pv + 0..7 of head col ----
+  float sc8[8];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    sc8[i] = pv + i < t1 ? s0[i] * qk_scale : -INFINITY;
+    sc8[4 + i] = pv + 4 + i < t1 ? s1[i] * qk_scale : -INFINITY;
+  }
+  float m = sc8[0];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sco[i][jj] = -INFINITY;
-        if (i < nbu) {
-          float kv[EPL];
-          decode_chunk<KVDT>(kb[i], kv);
-          const bool valid = row_of(i) < t1;
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, sc8[i]);
+  m = column_max<16>(m);
+  float sum = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float x = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    sc8[i] = m == -INFINITY ? 0.f : expf(sc8[i] - m);
+    sum += sc8[i];
+  }
+  sum = column_sum<16>(sum);
+  // ---- P.V: 16 dims x 16 head columns per tile ----
+  u32x4 ph, pl;
+  split16<KVDT>(sc8, ph, pl);
+  f32x4 acc[NT];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) x = fmaf(kv[e], qr[jj][e], x);
-            x = group_sum(x, LPR);
-            sco[i][jj] = valid ? x * qk_scale : -INFINITY;
-          }
-        }
-      }
-    }
-    // ---- the wave's softmax statistics per head, probabilities in place of the scores ----
-    float mw[4], lw[4];
+  for (int tt = 0; tt < NT; ++tt) {
+    acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
+    acc[tt] = mfma16<KVDT>(vt[tt], pl, acc[tt]);
+  }
+  if (col < grp) {
+    float* dst = red + ((int64_t)wave * grp + col) * HD + 4 * grp4;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < nbu) m = fmaxf(m, sco[i][jj]);
-      m = column_max<LPR>(m);
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (i < nbu) {
-          const float pr = m == -INFINITY ? 0.f : expf(sco[i][jj] - m);
-          sco[i][jj] = pr;
-          sum += pr;
-        }
-      mw[jj] = m;
-      lw[jj] = column_sum<LPR>(sum);  // one lane per row in each column
-    }
-    // ---- P.V over the wave's rows ----
-    float acc[4][EPL];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[jj][e] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      if (i < nbu) {
-        float vv[EPL];
-        decode_chunk<KVDT>(vb[i], vv);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float pr = sco[i][jj] * vscale;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[jj][e] = fmaf(pr, vv[e], acc[jj][e]);
-        }
-      }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[jj][e] = column_sum<LPR>(acc[jj][e]);
-    if (sub == 0) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (jb + jj < grp) {
-          float* dst = red + ((int64_t)wave * grp + jb + jj) * HD + part * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; e += 4)
-            *reinterpret_cast<float4*>(dst + e) = make_float4(acc[jj][e], acc[jj][e + 1], acc[jj][e + 2], acc[jj][e + 3]);
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (jb + jj < grp) {
-          wml[(wave * grp + jb + jj) * 2] = mw[jj];
-          wml[(wave * grp + jb + jj) * 2 + 1] = lw[jj];
-        }
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<float4*>(dst + 16 * tt) =
+          make_float4(acc[tt][0] * vscale, acc[tt][1] * vscale, acc[tt][2] * vscale, acc[tt][3] * vscale);
+    if (grp4 == 0) {
+      wml[(wave * grp + col) * 2] = m;
+      wml[(wave * grp + col) * 2 + 1] = sum;
     }
   }
   __syncthreads();
@@ -1365,7 +1382,8 @@ __global__ void pmk_copy_token(const KParams P, int32_t* dst) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *dst = (int32_t)P.ctrl[CTRL_TOKEN];
 }
 
-// KV rows [L][nkv][P][hd] (element bytes es) -> cache [L][nkv][max_seq][hd]
+// KV rows [L][nkv][P][hd] (element bytes es) -> K cache [L][nkv][seqcap][hd] and the V cache in
+// blocks of 32 positions, [L][nkv][seqcap / 32][hd][32]
 __global__ void pmk_load_kv_rows(KParams P, const uint8_t* src_k, const uint8_t* src_v, int npos, int es) {
   const int64_t rowb = (int64_t)P.hd * es;
   const int64_t total = (int64_t)P.L * P.nkv * npos * rowb / 16;
@@ -1373,9 +1391,15 @@ __global__ void pmk_load_kv_rows(KParams P, const uint8_t* src_k, const uint8_t*
     const int64_t byte = i * 16;
     const int64_t row = byte / rowb, off = byte % rowb;
     const int64_t lg = row / npos, p = row % npos;
-    const int64_t dst = (lg * P.max_seq + p) * rowb + off;
+    const int64_t dst = (lg * P.seqcap + p) * rowb + off;
     *reinterpret_cast<u32x4*>(P.kc + dst) = *reinterpret_cast<const u32x4*>(src_k + byte);
-    *reinterpret_cast<u32x4*>(P.vc + dst) = *reinterpret_cast<const u32x4*>(src_v + byte);
+  }
+  const int64_t nel = (int64_t)P.L * P.nkv * npos * P.hd;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nel; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t d = i % P.hd, p = (i / P.hd) % npos, lg = i / ((int64_t)P.hd * npos);
+    const int64_t dst = ((lg * (P.seqcap / 32) + p / 32) * P.hd + d) * 32 + p % 32;
+    if (es == 1) P.vc[dst] = src_v[i];
+    else reinterpret_cast<uint16_t*>(P.vc)[dst] = reinterpret_cast<const uint16_t*>(src_v)[i];
   }
 }
 

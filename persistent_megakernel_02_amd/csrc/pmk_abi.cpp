@@ -149,6 +149,9 @@ pmk_schedule_config defaults(const pmk_schedule_config* s) {
   return d;
 }
 
+// KV cache positions per head: the V cache is stored in blocks of 32 positions
+int64_t seqcap_of(const ModelDims& m) { return ((int64_t)m.max_seq + 31) / 32 * 32; }
+
 void compute_layout(pmk_ctx* c) {
   const ModelDims& m = c->m;
   const int64_t wes = c->wes, H = m.H, F = m.F, V = m.V, qd = m.qdim(), L = m.L;
@@ -181,7 +184,7 @@ void compute_layout(pmk_ctx* c) {
   }
   c->a_rope = a; a = align256(a + (int64_t)m.max_seq * (m.hd / 2) * 8);
   c->sizes.arena_bytes = a;
-  c->sizes.kv_bytes = 2 * align256((int64_t)L * m.nkv * m.max_seq * m.hd * c->kves);
+  c->sizes.kv_bytes = 2 * align256((int64_t)L * m.nkv * seqcap_of(m) * m.hd * c->kves);
 
   const Schedule& s = c->sched;
   const int64_t NT = (int64_t)s.tasks.size();
@@ -249,6 +252,7 @@ void fill_params(pmk_ctx* c) {
   P = KParams{};
   P.L = m.L; P.H = m.H; P.nq = m.nq; P.nkv = m.nkv; P.hd = m.hd; P.F = m.F; P.V = m.V;
   P.grp = m.grp(); P.qkv_rows = m.qkv_rows(); P.qdim = m.qdim(); P.max_seq = m.max_seq; P.S = c->sched.attn_splits;
+  P.seqcap = (int)seqcap_of(m);
   P.wdt = m.wdt; P.kvdt = m.kvdt; P.eps = m.eps;
   P.attn_scale = (float)(1.0 / std::sqrt((double)m.hd));
   uint8_t* A = c->arena;

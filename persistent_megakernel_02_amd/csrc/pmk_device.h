@@ -40,6 +40,7 @@ struct CallParams {
 struct KParams {
   // model
   int L, H, nq, nkv, hd, F, V, grp, qkv_rows, qdim, max_seq, S;
+  int seqcap;             // KV cache positions per head: max_seq rounded up to 32
   int wdt, kvdt;
   float eps;
   float attn_scale;  // 1/sqrt(hd)
@@ -56,7 +57,7 @@ struct KParams {
   int64_t sc_off[7];      // offsets (floats) of the 7 arrays inside a layer
   const float* sc_lm;
   const float2* rope;     // [max_seq][hd/2] (cos, sin)
-  // kv cache [L][nkv][max_seq][hd]
+  // kv cache: K [L][nkv][seqcap][hd], V [L][nkv][seqcap / 32][hd][32]
   uint8_t* kc;
   uint8_t* vc;
   // workspace

@@ -56,9 +56,8 @@ void split_range(int n, int parts, int i, int* lo, int* hi) {
 }  // namespace
 
 int attn_max_chunk(const ModelDims& m) {
-  const int rowbytes = m.hd * (m.kvdt == PMK_DT_FP8_E4M3 ? 1 : 2);
-  const int rpi = 64 / (rowbytes / 16);
-  return 8 * kAttnBlocks * rpi;
+  (void)m;
+  return kAttnMaxChunk;
 }
 
 // ================================================================================================
@@ -92,8 +91,8 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     S = std::max(1, n_queues / m.nkv);
     S = std::min(S, std::max(1, m.max_seq / 16));
   }
-  // each split's rows must fit the attention task's register batch: 8 waves x kAttnBlocks row
-  // blocks of RPI rows (RPI = 64 lanes / (row bytes / 16)), so chunk = ceil(max_seq / S) is bounded
+  // each split's positions must fit the attention task (8 waves x 32): chunk = ceil(max_seq / S)
+  // rounded up to whole 32-position blocks is bounded
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
   s.attn_splits = S;
@@ -397,7 +396,7 @@ std::string validate_schedule(const Schedule& s) {
     const pmk_task& k = s.tasks[t];
     if (k.signal_ctr >= 0) producers[k.signal_ctr].push_back(t);
   }
-  if ((m.max_seq + S - 1) / S > attn_max_chunk(m))
+  if (((m.max_seq + S - 1) / S + 31) / 32 * 32 > attn_max_chunk(m))
     return fmt("thresholds: %ld attention splits leave chunks longer than the %ld rows a task holds", S, attn_max_chunk(m));
   std::vector<int> nprod(NC, 0);
   for (int c = 0; c < NC; ++c) nprod[c] = (int)producers[c].size();

@@ -69,7 +69,8 @@ def test_sizes_and_device_less_context():
         assert st == 0, msg
         s = pmk.pmk_sizes()
         assert lib.pmk_buffer_sizes(ctx, ctypes.byref(s)) == 0
-        kv_half = w.layers * w.n_kv * w.max_seq * w.head_dim * (1 if w.kvdtype == "fp8" else 2)
+        seqcap = (w.max_seq + 31) // 32 * 32  # the V cache is stored in blocks of 32 positions
+        kv_half = w.layers * w.n_kv * seqcap * w.head_dim * (1 if w.kvdtype == "fp8" else 2)
         assert s.kv_bytes == 2 * ((kv_half + 255) // 256 * 256)
         # the arena holds at least every streamed weight byte
         assert s.arena_bytes >= w.weight_bytes()

@@ -108,6 +108,18 @@ def mutants(w, n_cus, rng, per_kind):
     # the first QKV tasks on the queue that ends with the TOKEN task are already ordered after the
     # previous step's LM head by program order, so their wait is redundant (dropping it is safe)
     waiting = [i for i, t in enumerate(tasks) if t.wait_ctr >= 0 and not (t.op == 1 and t.layer == 0 and i in q0)]
+    # tasks whose queue already joined the same counter earlier in the step (lag 0, full count):
+    # their own wait is redundant, so weakening it is safe
+    joined_before = set()
+    for q in range(NQ):
+        seen = set()
+        for i in base.queue(q):
+            t = tasks[i]
+            if t.wait_ctr >= 0 and t.wait_ctr in seen:
+                joined_before.add(i)
+            if t.wait_ctr >= 0 and t.wait_lag == 0 and t.wait_count == base.producers(t.wait_ctr):
+                seen.add(t.wait_ctr)
+    weakenable = [i for i in waiting if i not in joined_before]
     signalling = [i for i, t in enumerate(tasks) if t.signal_ctr >= 0]
     full = [i for i in waiting if tasks[i].wait_count == base.producers(tasks[i].wait_ctr)
             and base.producers(tasks[i].wait_ctr) > 1]
@@ -170,12 +182,16 @@ def mutants(w, n_cus, rng, per_kind):
             t.a1 = t.a0
         s.set_task(i, t)
 
-    def swap_queue(s, q):       # a task moved before the task whose signal it (transitively) needs
-        lst = s.queue(q)
-        if len(lst) < 2:
+    def swap_queue(s, q):       # a task moved before the task whose signal it needs (its full-count
+        lst = s.queue(q)        # wait then includes a producer queued behind it: deadlock)
+        pairs = [k for k in range(len(lst) - 1)
+                 if tasks[lst[k + 1]].wait_ctr >= 0 and tasks[lst[k + 1]].wait_ctr == tasks[lst[k]].signal_ctr
+                 and tasks[lst[k + 1]].wait_lag == 0
+                 and tasks[lst[k + 1]].wait_count == base.producers(tasks[lst[k + 1]].wait_ctr)]
+        if not pairs:
             lst = lst + lst[:1]  # duplicate entry: integrity
         else:
-            k = rng.randrange(len(lst) - 1)
+            k = rng.choice(pairs)
             lst[k], lst[k + 1] = lst[k + 1], lst[k]
         s.set_queue(q, lst)
 
@@ -185,9 +201,10 @@ def mutants(w, n_cus, rng, per_kind):
             lst.pop(rng.randrange(len(lst)))
         s.set_queue(q, lst)
 
-    kinds = [("drop_wait", drop_wait, waiting), ("lower_threshold", lower_threshold, full),
+    kinds = [("drop_wait", drop_wait, weakenable),
+             ("lower_threshold", lower_threshold, [i for i in full if i not in joined_before]),
              ("raise_threshold", raise_threshold, waiting), ("zero_threshold", zero_threshold, waiting),
-             ("wrong_lag", wrong_lag, waiting), ("back_edge", back_edge, [i for i in waiting if tasks[i].op not in (6, 7)]),
+             ("wrong_lag", wrong_lag, weakenable), ("back_edge", back_edge, [i for i in waiting if tasks[i].op not in (6, 7)]),
              ("drop_signal", drop_signal, signalling), ("remove_producer", remove_producer, signalling),
              ("shared_slot", shared_slot, signalling), ("alias_rows", alias_rows, signalling)]
     for kind, fn, sites in kinds:
