@@ -310,21 +310,21 @@ template <int WDT>
 constexpr int prefetch_depth() { return PMK_PREFETCH_UNITS < ring_depth<WDT>() ? PMK_PREFETCH_UNITS : ring_depth<WDT>(); }
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
-// KS minimises the largest per-wave unit count (short tiles then still keep all waves streaming).
-// Wave w takes row group w / KS and slice range w % KS; its units (one 16-byte chunk per lane of
-// one row and one 64-chunk slice) run row by row, slices in order within a row.
+// KS minimises the busiest wave's cost, units plus row_cost per row (a row ends in a wave-wide
+// reduction; short tiles then still keep all waves streaming).  Wave w takes row group w / KS
+// and slice range w % KS; its units (one 16-byte chunk per lane of one row and one 64-chunk
+// slice) run row by row, slices in order within a row.
 struct TileSplit {
-  int R, KS, gi, si, wr0, wr1, s0, s1, nunits, max_units;
-  __device__ __forceinline__ TileSplit(int r0, int r1, int nsl, int wave) {
+  int R, KS, gi, si, wr0, wr1, s0, s1, nunits;
+  __device__ __forceinline__ TileSplit(int r0, int r1, int nsl, int wave, int row_cost = 0) {
     R = r1 - r0;
     int best = 0x7fffffff;
     KS = 1;
     for (int ks = 1; ks <= kWaves; ks <<= 1) {
       const int g = kWaves / ks;
-      const int cost = ((R + g - 1) / g) * ((nsl + ks - 1) / ks);
+      const int cost = ((R + g - 1) / g) * ((nsl + ks - 1) / ks + row_cost);
       if (cost < best) { best = cost; KS = ks; }
     }
-    max_units = best;  // units of the busiest wave
     const int G = kWaves / KS;
     gi = wave / KS;
     si = wave % KS;
@@ -347,12 +347,13 @@ struct TileSplit {
 // kRing units ahead, until the wave's units are all issued.  The loop issues no other global load.
 template <int WDT, class Sync, class ScaleRow>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, int r0, int r1, const float* xs,
-                                          float* yp, float* y, bool prefetch, Sync sync, ScaleRow srow) {
+                                          float* yp, float* y, bool prefetch, Sync sync, ScaleRow srow,
+                                          int row_cost = 0) {
   constexpr int EPL = WFmt<WDT>::EPL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
-  const TileSplit sp(r0, r1, nsl, wave);
+  const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const int R = sp.R, KS = sp.KS, si = sp.si, wr0 = sp.wr0, wr1 = sp.wr1, s0 = sp.s0, s1 = sp.s1;
   const int nunits = sp.nunits;
 
@@ -426,26 +427,26 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy a GEMV tile (rows [r0, r1) of W) into LDS with LDS-DMA buffer loads: no registers, and an
-// out-of-range lane (past the last chunk of a row) writes zeros.  Wave w's units land at
-// pf + w * ustride KiB in the order gemv_rows_lds consumes them; each wave later reads only the
-// units it copied itself, so its own load counter orders the copy before the reads (the compiler
-// waits on outstanding LDS-DMA before an LDS access that may alias it).
+// out-of-range lane (past the last chunk of a row) writes zeros.  Unit (row, slice) lands at
+// pf + ((row - r0) * nsl + slice) KiB; each wave copies the units gemv_rows_lds has it consume
+// (same split), so its own load counter orders the copy before its reads (the compiler waits on
+// outstanding LDS-DMA before an LDS access that may alias it).
 template <int WDT>
 __device__ __forceinline__ void tile_to_lds(const uint8_t* __restrict__ W, int K, int r0, int r1, float* pf,
-                                            int ustride) {
+                                            int row_cost) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
   const int nch = K / WFmt<WDT>::EPL, nsl = (nch + 63) >> 6;
-  const TileSplit sp(r0, r1, nsl, wave);
+  const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + (int64_t)r0 * rb), (short)0, (int)((int64_t)sp.R * rb), 0x00020000);
   constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;
-  float* dst = pf + wave * ustride * 256;
   int lrow = sp.wr0, lj = sp.s0;
   for (int u = 0; u < sp.nunits; ++u) {
     const int c = lj * 64 + lane;
     const uint32_t off = c < nch ? (uint32_t)((int64_t)(lrow - r0) * rb + (int64_t)c * 16) : kOut;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(dst + u * 256), 16, off, 0, 0, 2);  // nontemporal
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(pf + ((lrow - r0) * nsl + lj) * 256), 16, off, 0, 0,
+                                             2);  // nontemporal
     if (++lj == sp.s1) { lj = sp.s0; ++lrow; }
   }
 }
@@ -454,31 +455,36 @@ __device__ __forceinline__ void tile_to_lds(const uint8_t* __restrict__ W, int K
 // overlaps `sync`, the dependency wait and input staging): the same split, the same per-lane
 // chunk order and the same summation order, so the results are bitwise those of gemv_rows.
 template <int WDT, class Sync, class ScaleRow>
-__device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float* xs, const float* pf, int ustride,
-                                              float* yp, float* y, Sync sync, ScaleRow srow) {
+__device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float* xs, const float* pf, float* yp,
+                                              float* y, Sync sync, ScaleRow srow, int row_cost) {
   constexpr int EPL = WFmt<WDT>::EPL;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
-  const TileSplit sp(r0, r1, nsl, wave);
+  const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const int R = sp.R, KS = sp.KS, si = sp.si, s0 = sp.s0, s1 = sp.s1;
   sync();
   if (sp.nunits > 0) {
-    const float* src = pf + wave * ustride * 256 + lane * 4;
-    float acc = 0.f;
-    int crow = sp.wr0, cj = s0;
-    for (int u = 0; u < sp.nunits; ++u) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(src + u * 256);
-      const int c = cj * 64 + lane;
-      const float part = chunk_dot<WDT>(w, xs + c * EPL);
-      if constexpr (WDT == WFP8) acc = fmaf(part, srow(crow)[(c < nch ? c : 0) >> 3], acc);
-      else acc += part;
-      if (++cj == s1) {
-        cj = s0;
-        const float v = wave_sum(acc);
-        acc = 0.f;
-        if (lane == 0) yp[(crow - r0) * KS + si] = v;
-        ++crow;
+    for (int row = sp.wr0; row < sp.wr1; ++row) {
+      const float* src = pf + (row - r0) * nsl * 256 + lane * 4;
+      int u = s0;
+      float acc = 0.f;
+      auto step = [&](const u32x4& w, int j) {
+        const int c = j * 64 + lane;
+        const float part = chunk_dot<WDT>(w, xs + c * EPL);
+        if constexpr (WDT == WFP8) acc = fmaf(part, srow(row)[(c < nch ? c : 0) >> 3], acc);
+        else acc += part;
+      };
+      int j = s0;
+      for (; j + 4 <= s1; j += 4, u += 4) {  // four units' LDS reads in flight
+        u32x4 w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = *reinterpret_cast<const u32x4*>(src + (u + k) * 256);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) step(w[k], j + k);
       }
+      for (; j < s1; ++j, ++u) step(*reinterpret_cast<const u32x4*>(src + u * 256), j);
+      const float v = wave_sum(acc);
+      if (lane == 0) yp[(row - r0) * KS + si] = v;
     }
   }
   __syncthreads();
@@ -599,8 +605,12 @@ struct StepCtx {
 // task's dependency wait, instead of the register ring's first units: the wait for the attention
 // combine is long enough for all of it to land, and the GEMV then runs from LDS.
 __device__ __forceinline__ bool oproj_tile_in_lds(const KParams& P, const pmk_task& t, const StepCtx& sc, int nsl) {
-  return P.prefetch == 2 && P.pf_wave > 0 && !sc.per_op && TileSplit(t.a0, t.a1, nsl, 0).max_units <= P.pf_wave;
+  return P.prefetch == 2 && !sc.per_op && (t.a1 - t.a0) * nsl <= P.pf_units;
 }
+
+// O-projection tiles are short (a few rows per CU): the split weighs each row's reduction like
+// four units, the same in every mode, so the LDS path and the streaming path agree bitwise
+constexpr int kOprojRowCost = 4;
 
 __device__ __forceinline__ int key_token(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
@@ -881,7 +891,9 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     kscale = P.kv_scale[head * 2];
     vscale = P.kv_scale[head * 2 + 1];
   }
-  const int p0 = t0 + 32 * wave;
+  // wave 0 polls the dependency: it takes the last group (only splits of 8 groups use it), so its
+  // poll is not queued behind K/V loads, and it alone stages q
+  const int p0 = t0 + 32 * ((wave + kWaves - 1) % kWaves);
   // K rows of this lane in the two score blocks, V^T positions of this lane
   const int pk0 = p0 + 8 * (col >> 2) + (col & 3), pk1 = pk0 + 4;
   const int pv = p0 + 8 * grp4;
@@ -916,7 +928,15 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, true>(vr, voff(tt));
   }
-  load_vector<false>(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD, grp * HD, qs);
+  if (wave == 0) {
+    const __amdgpu_buffer_rsrc_t qr = coherent_rsrc(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD * 4);
+    u32x4 qv[(16 * HD) / 256];  // grp <= 16 heads: grp * HD floats, 4 per lane per load
+#pragma unroll
+    for (int k = 0; k < (16 * HD) / 256; ++k) qv[k] = ldc16(qr, (uint32_t)(k * 256 + lane * 4) * 4u);
+#pragma unroll
+    for (int k = 0; k < (16 * HD) / 256; ++k)
+      if (k * 256 + lane * 4 < grp * HD) *reinterpret_cast<float4*>(qs + k * 256 + lane * 4) = as_f4(qv[k]);
+  }
   __syncthreads();
   // positions past the split's end (the last V^T group may straddle it) contribute nothing
   if (pv < t1 && pv + 8 > t1) {
@@ -1100,10 +1120,10 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   const int nbc = (K + 127) / 128;
   auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
   if (oproj_tile_in_lds(P, t, sc, (K / WFmt<WDT>::EPL + 63) >> 6)) {
-    tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, P.pf_wave);
-    gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, P.pf_wave, yp, y, sync, srow);
+    tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, kOprojRowCost);
+    gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, yp, y, sync, srow, kOprojRowCost);
   } else
-    gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
+    gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow, kOprojRowCost);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);

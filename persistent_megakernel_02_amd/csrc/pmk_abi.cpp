@@ -73,7 +73,7 @@ struct pmk_ctx {
   int trace_on = 0;
   int xs_floats = 0;
   int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0;
-  int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_wave = 0;
+  int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_units = 0;
   size_t lds_bytes = 0;     // per-op kernels
   size_t lds_bytes_pk = 0;  // persistent kernel (adds the O-projection tile area)
   KParams kp{};
@@ -241,9 +241,9 @@ void compute_layout(pmk_ctx* c) {
   const int64_t o_end = c->o_y_off + r64(ormax);
   c->pf_off = (int)((std::max(o_end, r64(attn)) + 255) / 256 * 256);
   const int64_t lds_floats = kLdsBytes / 4;
-  c->pf_wave = c->sc.prefetch == 2 ? (int)std::max<int64_t>(0, (lds_floats - c->pf_off) / 256 / kWaves) : 0;
-  c->lds_bytes_pk = c->pf_wave > 0 ? std::max(c->lds_bytes, (size_t)(c->pf_off + (int64_t)kWaves * c->pf_wave * 256) * 4)
-                                   : c->lds_bytes;
+  c->pf_units = c->sc.prefetch == 2 ? (int)std::max<int64_t>(0, (lds_floats - c->pf_off) / 256) : 0;
+  c->lds_bytes_pk = c->pf_units > 0 ? std::max(c->lds_bytes, (size_t)(c->pf_off + (int64_t)c->pf_units * 256) * 4)
+                                    : c->lds_bytes;
 }
 
 void fill_params(pmk_ctx* c) {
@@ -303,7 +303,7 @@ void fill_params(pmk_ctx* c) {
   P.o_yp_off = c->o_yp_off;
   P.o_y_off = c->o_y_off;
   P.pf_off = c->pf_off;
-  P.pf_wave = c->pf_wave;
+  P.pf_units = c->pf_units;
 }
 
 void compute_phases(pmk_ctx* c) {

@@ -88,7 +88,7 @@ struct KParams {
   int y_off;              // LDS float offset of GEMV row results [rows]
   int o_epi_off, o_yp_off, o_y_off;  // the same three areas for OPROJ tasks, packed below pf_off
   int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)
-  int pf_wave;            // 1 KiB units per wave in that area (0: the copy is off)
+  int pf_units;           // 1 KiB units in that area (0: the copy is off)
 };
 
 }  // namespace pmk
