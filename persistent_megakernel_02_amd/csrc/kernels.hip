@@ -61,6 +61,15 @@ __device__ __forceinline__ void stc(uint16_t* p, uint16_t v) {
 __device__ __forceinline__ void stc(uint8_t* p, uint8_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void stc(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A value that carries its own readiness: the step tag (global step + 1) in the high word and the
+// fp32 bits in the low word, written with one 8-byte atomic store (single-copy atomic), so a
+// reader that sees the tag of its step sees that step's value.
+__device__ __forceinline__ unsigned long long tagged(float v, int e) {
+  return ((unsigned long long)(uint32_t)(e + 1) << 32) | __float_as_uint(v);
+}
 // wait until every memory access this wave issued has completed
 __device__ __forceinline__ void drain() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1040,7 +1049,7 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
     constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;
     const float* pg = P.part + (((int64_t)l * P.nkv + g) * S) * grp * PSTR;
     const __amdgpu_buffer_rsrc_t pr = coherent_rsrc(pg, (uint32_t)((int64_t)S * grp * PSTR * 4));
-    float* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
+    unsigned long long* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
     const int r = tid & 3;
     for (int qd = tid >> 2; qd < grp * QPH; qd += kThreads / 4) {
       const int j = qd / QPH, d0 = (qd % QPH) * 4;
@@ -1085,11 +1094,55 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
       a2 = quad_sum(a2 * f);
       a3 = quad_sum(a3 * f);
       const float v = r == 0 ? a0 : r == 1 ? a1 : r == 2 ? a2 : a3;
-      stc(o + j * HD + d0 + r, v / den);
+      stc(o + j * HD + d0 + r, tagged(v / den, sc.e));
     }
   }
   mark(P, sc, ti, 4);
-  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+  // With flags, the O projection polls the tags of o itself (no drain, no flag); counters keep
+  // the drained signal.
+  if (P.sync_mode == PMK_SYNC_COUNTERS) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+}
+
+// Stage the tagged attention output o[0..n) of step e into xs (zero padding to pad): every thread
+// re-reads its 16-byte pairs until both tags show step e (bounded by the watchdog; the abort word
+// is checked on every retry), then the workgroup barrier.  The reads are the wait.
+__device__ __forceinline__ void stage_tagged(const KParams& P, const unsigned long long* src, int n, int pad,
+                                             float* xs, int e, bool poll, int cu, int task) {
+  constexpr int B = 4;  // 16-byte loads (two values) per thread per batch
+  const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 8);
+  const uint32_t want = (uint32_t)(e + 1);
+  for (int base = 0; base < pad; base += B * 2 * kThreads) {
+    u32x4 v[B];
+    bool ok[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) ok[k] = false;
+    int64_t spins = 0;
+    while (true) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // each retry reads memory again
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
+        if (!ok[k]) v[k] = i < n ? ldc16(r, (uint32_t)i * 8) : u32x4{0u, want, 0u, want};
+      }
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        ok[k] = ok[k] || !poll || (v[k].y == want && v[k].w == want);
+        all = all && ok[k];
+      }
+      if (all) break;
+      if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
+      if (++spins > P.spin_limit) {
+        report_error(P.ctrl, PMK_ERR_TIMEOUT, cu, task, -1, want, v[0].y);
+        break;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
+      if (i < pad) *reinterpret_cast<float2*>(xs + i) = make_float2(__uint_as_float(v[k].x), __uint_as_float(v[k].z));
+    }
+  }
 }
 
 // O projection + residual: xm[r] = x[r] + Wo[r].o  (residual rows staged in LDS with the input)
@@ -1104,17 +1157,20 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   float* yp = lds + P.o_yp_off;
   float* y = lds + P.o_y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
+  // flags mode: the wait on the combines is the tag poll of o below
+  const bool poll_o = !sc.per_op && P.sync_mode != PMK_SYNC_COUNTERS;
   auto sync = [&]() {
-    maybe_wait(P, t, sc, cu, ti);
+    if (!poll_o) maybe_wait(P, t, sc, cu, ti);
     const int tok = l == 0 ? input_token(P, sc) : 0;
     float rv = 0.f;  // first kThreads residual rows ride with the input loads
     if ((int)threadIdx.x < R)
       rv = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + threadIdx.x]) : ldc(P.x + (int64_t)l * P.H + t.a0 + threadIdx.x);
     for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
       res[i] = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i]) : ldc(P.x + (int64_t)l * P.H + t.a0 + i);
-    load_vector<false>(P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    stage_tagged(P, P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs, sc.e, !sc.per_op, cu, ti);
     if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
     __syncthreads();
+    if (poll_o) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
@@ -1377,11 +1433,13 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
   for (int k = i; k <= cp.n_steps; k += gridDim.x * blockDim.x) P.keys[k] = 0ull;
 }
 
-// zero flags, counters and control words; set position and next token
+// zero flags, counters, control words and the step tags of the attention output; set position
+// and next token
 __global__ void pmk_reset(KParams P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x, n = gridDim.x * blockDim.x;
   for (int k = i; k < n_flags; k += n) P.flags[k] = 0u;
   for (int k = i; k < n_counters; k += n) P.counters[k] = 0u;
+  for (int64_t k = i; k < (int64_t)P.L * P.qdim; k += n) P.o[k] = 0ull;
   for (int k = i; k < CTRL_WORDS; k += n) P.ctrl[k] = 0u;
   __syncthreads();
   if (i == 0) {

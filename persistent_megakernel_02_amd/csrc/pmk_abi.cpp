@@ -199,7 +199,7 @@ void compute_layout(pmk_ctx* c) {
   c->w_xm = w; w = align256(w + L * H * 4);
   c->w_q = w; w = align256(w + L * qd * 4);
   c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 4) * 4);
-  c->w_o = w; w = align256(w + L * qd * 4);
+  c->w_o = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
   c->w_h = w; w = align256(w + L * F * 4);
   c->w_trace = w; w = align256(w + (int64_t)std::max(0, c->sc.trace_steps) * NT * 64);
   c->w_tasks = w; w = align256(w + NT * (int64_t)sizeof(pmk_task));
@@ -281,7 +281,7 @@ void fill_params(pmk_ctx* c) {
   P.xm = reinterpret_cast<float*>(W + c->w_xm);
   P.q = reinterpret_cast<float*>(W + c->w_q);
   P.part = reinterpret_cast<float*>(W + c->w_part);
-  P.o = reinterpret_cast<float*>(W + c->w_o);
+  P.o = reinterpret_cast<unsigned long long*>(W + c->w_o);
   P.h = reinterpret_cast<float*>(W + c->w_h);
   P.trace = reinterpret_cast<unsigned long long*>(W + c->w_trace);
   P.tasks = reinterpret_cast<const pmk_task*>(W + c->w_tasks);

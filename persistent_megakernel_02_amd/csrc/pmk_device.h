@@ -71,7 +71,7 @@ struct KParams {
   float* xm;              // [L][H]
   float* q;               // [L][qdim]
   float* part;            // [L][nkv][S][grp][hd+4]: m, l, 2 pad, acc[hd]
-  float* o;               // [L][qdim]
+  unsigned long long* o;  // [L][qdim] attention output, each value tagged: (step + 1) << 32 | fp32 bits
   float* h;               // [L][F]
   unsigned long long* trace;  // [trace_steps][n_tasks][4]
   // schedule tables
