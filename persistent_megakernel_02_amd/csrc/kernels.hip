@@ -689,14 +689,20 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
   };
   const int qrows = P.qdim, krows = P.nkv * hd;
   const int nbc = (H + 127) / 128;
-  auto srow = [&](int r) -> const float* {
-    int which, orow;
-    if (r < qrows) { which = 0; orow = r; }
-    else if (r < qrows + krows) { which = 1; orow = r - qrows; }
-    else { which = 2; orow = r - qrows - krows; }
+  // scale-array bases taken before the loop (a dynamically indexed kernel argument would be
+  // re-read from memory for every weight unit, behind a full wait)
+  const float* const sq = fp8_rows<WDT>(P, l, 0);
+  const float* const sk = fp8_rows<WDT>(P, l, 1);
+  const float* const sv = fp8_rows<WDT>(P, l, 2);
+  auto srow = [=](int r) -> const float* {
+    const float* base;
+    int orow;
+    if (r < qrows) { base = sq; orow = r; }
+    else if (r < qrows + krows) { base = sk; orow = r - qrows; }
+    else { base = sv; orow = r - qrows - krows; }
     const int head = orow / hd, pr = orow % hd;
     const int dim = (pr >> 1) + (pr & 1) * half;
-    return fp8_rows<WDT>(P, l, which) + (int64_t)((head * hd + dim) / 128) * nbc;
+    return base + (int64_t)((head * hd + dim) / 128) * nbc;
   };
   gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
@@ -1174,7 +1180,8 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
     mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
-  auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 3) + (int64_t)(r / 128) * nbc; };
+  const float* const so = fp8_rows<WDT>(P, l, 3);
+  auto srow = [=](int r) -> const float* { return so + (int64_t)(r / 128) * nbc; };
   if (oproj_tile_in_lds(P, t, sc, (K / WFmt<WDT>::EPL + 63) >> 6)) {
     tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, kOprojRowCost);
     gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, yp, y, sync, srow, kOprojRowCost);
@@ -1202,9 +1209,9 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
-  auto srow = [&](int r) -> const float* {
-    return fp8_rows<WDT>(P, l, (r & 1) ? 5 : 4) + (int64_t)((r >> 1) / 128) * nbc;
-  };
+  const float* const sg = fp8_rows<WDT>(P, l, 4);
+  const float* const su = fp8_rows<WDT>(P, l, 5);
+  auto srow = [=](int r) -> const float* { return ((r & 1) ? su : sg) + (int64_t)((r >> 1) / 128) * nbc; };
   gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   const int npairs = (t.a1 - t.a0) >> 1;
@@ -1237,7 +1244,8 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
     mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
-  auto srow = [&](int r) -> const float* { return fp8_rows<WDT>(P, l, 6) + (int64_t)(r / 128) * nbc; };
+  const float* const sd = fp8_rows<WDT>(P, l, 6);
+  auto srow = [=](int r) -> const float* { return sd + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads) stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, res[i] + y[i]);
@@ -1275,7 +1283,8 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
-  auto srow = [&](int r) -> const float* { return P.sc_lm + (int64_t)(r / 128) * nbc; };
+  const float* const sl = P.sc_lm;
+  auto srow = [=](int r) -> const float* { return sl + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   const float rn = rms_factor(red, H, P.eps);
