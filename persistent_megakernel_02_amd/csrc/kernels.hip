@@ -865,8 +865,8 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // query heads of the group (grp <= 16); the partial (m, l, acc[hd]) of each head goes to the
 // workspace, and the group's COMBINE task merges the splits into o.
 // Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
-// On the matrix cores: wave w takes the 32 positions p0 = t0 + 32 w .. + 32 (chunks are whole
-// 32-position blocks).  Scores are two 16 x 16 products per 32-dim slice, K rows (A, from
+// On the matrix cores: the split is cut into 32-position groups (chunks are whole groups, at most
+// 16) and each wave takes one or two of them.  Scores are two 16 x 16 products per 32-dim slice, K rows (A, from
 // the [pos][hd] cache) times q (B, heads as columns); the A rows are the positions in the order
 // p0 + 8 (r / 4) + r % 4 (block 0) and + 4 (block 1), so that lane l ends up holding the scores of
 // positions p0 + 8 (l / 16) .. + 8 of head l % 16, which is exactly its B operand of P.V.  P.V is
@@ -878,7 +878,7 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // across the four lanes of a head column with column_max / column_sum) runs on the 8 scores a
 // lane holds; the eight waves' (max, sum, acc) are then merged in LDS with the usual rescaling,
 // exactly as the splits are merged by the combine.
-template <int WDT, int KVDT, int HD>
+template <int WDT, int KVDT, int HD, int NGW>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
@@ -906,42 +906,66 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     kscale = P.kv_scale[head * 2];
     vscale = P.kv_scale[head * 2 + 1];
   }
-  // wave 0 polls the dependency: it takes the last group (only splits of 8 groups use it), so its
-  // poll is not queued behind K/V loads, and it alone stages q
-  const int p0 = t0 + 32 * ((wave + kWaves - 1) % kWaves);
-  // K rows of this lane in the two score blocks, V^T positions of this lane
-  const int pk0 = p0 + 8 * (col >> 2) + (col & 3), pk1 = pk0 + 4;
-  const int pv = p0 + 8 * grp4;
-  const bool cur0 = pk0 == sc.pos, cur1 = pk1 == sc.pos;
-  const bool vcur = pv <= sc.pos && sc.pos < pv + 8;
+  // Wave w takes the 32-position groups v, v + 8, ... (NGW of them) with v = (w + 7) mod 8: wave 0
+  // takes the last group of each round (used only when the split needs it), so its dependency
+  // poll is normally not queued behind K/V loads, and it alone stages q.  The first group's rows
+  // of past positions are loaded before the dependency wait; a second group reuses the same
+  // registers, its K rows loaded once the first group's scores are done and its V^T rows once the
+  // first group's P.V is, with an online rescale of the wave's (max, sum, acc).
+  const int wv = __builtin_amdgcn_readfirstlane((wave + kWaves - 1) % kWaves);
   auto koff = [&](int p, int c) {
     return p < t1 ? (uint32_t)(p * ROWB + (32 * c + 8 * grp4) * KES) : kOut;
   };
-  auto voff = [&](int tt) {
+  auto voff = [&](int pv, int tt) {
     return pv < t1 ? (uint32_t)((((pv >> 5) * HD + 16 * tt + col) * 32 + (pv & 31)) * KES) : kOut;
   };
-  // past positions: before the dependency wait
+  // K rows of this lane (score blocks 0 and 1) and V^T positions of this lane, for group k
+  auto pk_of = [&](int k) { return t0 + 32 * (wv + kWaves * k) + 8 * (col >> 2) + (col & 3); };
+  auto pv_of = [&](int k) { return t0 + 32 * (wv + kWaves * k) + 8 * grp4; };
   u32x4 ka[NC], kb[NC], vt[NT];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    ka[c] = kv_load8<KVDT, false>(kr, cur0 ? kOut : koff(pk0, c));
-    kb[c] = kv_load8<KVDT, false>(kr, cur1 ? kOut : koff(pk1, c));
-  }
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, false>(vr, vcur ? kOut : voff(tt));
-  maybe_wait(P, t, sc, cu, ti);
-  // the current position (written this step): coherent loads, with q's
-  if (cur0 || cur1) {
+  // K rows of group k; the current position (written this step) coherently, after the wait
+  auto load_k = [&](int k, bool after_wait) {
+    const int pk0 = pk_of(k);
+    const bool c0 = pk0 == sc.pos, c1 = pk0 + 4 == sc.pos;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const u32x4 v = kv_load8<KVDT, true>(kr, koff(sc.pos, c));
-      if (cur0) ka[c] = v;
-      else kb[c] = v;
+      if (after_wait && (c0 || c1)) {
+        ka[c] = c0 ? kv_load8<KVDT, true>(kr, koff(pk0, c)) : kv_load8<KVDT, false>(kr, koff(pk0, c));
+        kb[c] = c1 ? kv_load8<KVDT, true>(kr, koff(pk0 + 4, c)) : kv_load8<KVDT, false>(kr, koff(pk0 + 4, c));
+      } else {
+        ka[c] = kv_load8<KVDT, false>(kr, c0 ? kOut : koff(pk0, c));
+        kb[c] = kv_load8<KVDT, false>(kr, c1 ? kOut : koff(pk0 + 4, c));
+      }
     }
-  }
-  if (vcur) {
+  };
+  auto load_v = [&](int k, bool after_wait) {
+    const int pv = pv_of(k);
+    const bool cur = pv <= sc.pos && sc.pos < pv + 8;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, true>(vr, voff(tt));
+    for (int tt = 0; tt < NT; ++tt)
+      vt[tt] = after_wait && cur ? kv_load8<KVDT, true>(vr, voff(pv, tt))
+                                 : kv_load8<KVDT, false>(vr, cur ? kOut : voff(pv, tt));
+  };
+  // group 0, past positions: before the dependency wait
+  load_k(0, false);
+  load_v(0, false);
+  maybe_wait(P, t, sc, cu, ti);
+  {
+    // group 0, the current position: coherent loads, with q's
+    const int pk0 = pk_of(0), pv = pv_of(0);
+    const bool cur0 = pk0 == sc.pos, cur1 = pk0 + 4 == sc.pos;
+    if (cur0 || cur1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 v = kv_load8<KVDT, true>(kr, koff(sc.pos, c));
+        if (cur0) ka[c] = v;
+        else kb[c] = v;
+      }
+    }
+    if (pv <= sc.pos && sc.pos < pv + 8) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, true>(vr, voff(pv, tt));
+    }
   }
   if (wave == 0) {
     const __amdgpu_buffer_rsrc_t qr = coherent_rsrc(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD * 4);
@@ -953,53 +977,72 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       if (k * 256 + lane * 4 < grp * HD) *reinterpret_cast<float4*>(qs + k * 256 + lane * 4) = as_f4(qv[k]);
   }
   __syncthreads();
-  // positions past the split's end (the last V^T group may straddle it) contribute nothing
-  if (pv < t1 && pv + 8 > t1) {
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) vt[tt] = keep_first(vt[tt], t1 - pv);
-  }
   const float qk_scale = kscale * P.attn_scale;
-  // ---- scores: blocks 0 and 1 of 16 positions x 16 head columns ----
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = col < grp ? qs[col * HD + 32 * c + 8 * grp4 + e] : 0.f;
-    u32x4 qh, ql;
-    split16<KVDT>(qv, qh, ql);
-    s0 = mfma16<KVDT>(ka[c], qh, s0);
-    s0 = mfma16<KVDT>(ka[c], ql, s0);
-    s1 = mfma16<KVDT>(kb[c], qh, s1);
-    s1 = mfma16<KVDT>(kb[c], ql, s1);
-  }
-  // ---- softmax over this wave's positions: lane holds positions pv + 0..7 of head col ----
-  float sc8[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc8[i] = pv + i < t1 ? s0[i] * qk_scale : -INFINITY;
-    sc8[4 + i] = pv + 4 + i < t1 ? s1[i] * qk_scale : -INFINITY;
-  }
-  float m = sc8[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) m = fmaxf(m, sc8[i]);
-  m = column_max<16>(m);
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    sc8[i] = m == -INFINITY ? 0.f : expf(sc8[i] - m);
-    sum += sc8[i];
-  }
-  sum = column_sum<16>(sum);
-  // ---- P.V: 16 dims x 16 head columns per tile ----
-  u32x4 ph, pl;
-  split16<KVDT>(sc8, ph, pl);
+  float m = -INFINITY, sum = 0.f;
   f32x4 acc[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
-    acc[tt] = mfma16<KVDT>(vt[tt], pl, acc[tt]);
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NGW; ++k) {
+    if (t0 + 32 * (wv + kWaves * k) >= t1) break;  // wave-uniform: no positions left
+    const int pv = pv_of(k);
+    // positions past the split's end (the last V^T group may straddle it) contribute nothing
+    if (pv < t1 && pv + 8 > t1) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) vt[tt] = keep_first(vt[tt], t1 - pv);
+    }
+    // ---- scores: blocks 0 and 1 of 16 positions x 16 head columns ----
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float qv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = col < grp ? qs[col * HD + 32 * c + 8 * grp4 + e] : 0.f;
+      u32x4 qh, ql;
+      split16<KVDT>(qv, qh, ql);
+      s0 = mfma16<KVDT>(ka[c], qh, s0);
+      s0 = mfma16<KVDT>(ka[c], ql, s0);
+      s1 = mfma16<KVDT>(kb[c], qh, s1);
+      s1 = mfma16<KVDT>(kb[c], ql, s1);
+    }
+    const bool next = k + 1 < NGW && t0 + 32 * (wv + kWaves * (k + 1)) < t1;
+    if (next) load_k(k + 1, true);
+    // ---- softmax: the lane holds positions pv + 0..7 of head column col ----
+    float sc8[8];
+    float mk = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc8[i] = pv + i < t1 ? s0[i] * qk_scale : -INFINITY;
+      sc8[4 + i] = pv + 4 + i < t1 ? s1[i] * qk_scale : -INFINITY;
+      mk = fmaxf(mk, fmaxf(sc8[i], sc8[4 + i]));
+    }
+    const float mn = fmaxf(m, column_max<16>(mk));
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sc8[i] = mn == -INFINITY ? 0.f : expf(sc8[i] - mn);
+      ps += sc8[i];
+    }
+    ps = column_sum<16>(ps);
+    if (k > 0) {
+      const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+      sum *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
+    }
+    sum += ps;
+    m = mn;
+    // ---- P.V: 16 dims x 16 head columns per tile ----
+    u32x4 ph, pl;
+    split16<KVDT>(sc8, ph, pl);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
+      acc[tt] = mfma16<KVDT>(vt[tt], pl, acc[tt]);
+    }
+    if (next) load_v(k + 1, true);
   }
   if (col < grp) {
     float* dst = red + ((int64_t)wave * grp + col) * HD + 4 * grp4;
@@ -1345,8 +1388,14 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_ATTN:
-      if (P.hd == 128) task_attn<WDT, KVDT, 128>(P, t, ti, sc, lds, cu);
-      else task_attn<WDT, KVDT, 64>(P, t, ti, sc, lds, cu);
+      // splits longer than 8 groups of 32 positions give each wave a second group
+      if (((sc.pos + P.S) / P.S + 31) / 32 > kWaves) {
+        if (P.hd == 128) task_attn<WDT, KVDT, 128, 2>(P, t, ti, sc, lds, cu);
+        else task_attn<WDT, KVDT, 64, 2>(P, t, ti, sc, lds, cu);
+      } else {
+        if (P.hd == 128) task_attn<WDT, KVDT, 128, 1>(P, t, ti, sc, lds, cu);
+        else task_attn<WDT, KVDT, 64, 1>(P, t, ti, sc, lds, cu);
+      }
       break;
     case PMK_OP_COMBINE:
       if (P.hd == 128) task_combine<128>(P, t, ti, sc, cu);

@@ -7,9 +7,9 @@ namespace pmk {
 // resource with 32-bit offsets, and offsets at or past this bound read as zeros.
 constexpr long long kMaxTileBytes = 0x7FFFFFF0ll;
 
-// Positions one attention task holds: 8 waves x 32 (one matrix-core block of 32 positions per
-// wave); splits are whole 32-position blocks.
-constexpr int kAttnMaxChunk = 256;
+// Positions one attention task holds: 8 waves x 2 matrix-core blocks of 32 positions; splits are
+// whole 32-position blocks.
+constexpr int kAttnMaxChunk = 512;
 
 // Weight bytes a GEMV workgroup loads before its dependency wait (8 waves x 10 x 1 KiB).
 constexpr long long kPrefetchBytes = 8 * 10 * 1024;

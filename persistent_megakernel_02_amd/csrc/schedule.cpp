@@ -91,7 +91,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     S = std::max(1, n_queues / m.nkv);
     S = std::min(S, std::max(1, m.max_seq / 16));
   }
-  // each split's positions must fit the attention task (8 waves x 32): chunk = ceil(max_seq / S)
+  // each split's positions must fit the attention task (8 waves x 2 x 32): chunk = ceil(max_seq / S)
   // rounded up to whole 32-position blocks is bounded
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);

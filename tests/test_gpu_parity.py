@@ -123,6 +123,27 @@ def test_tiny_fp8_prefill_and_decode():
     check(w, run, ref, first_ok, "tiny_fp8")
 
 
+@pytest.mark.parametrize("wname", ["tiny", "tiny_fp8"])
+def test_long_split_two_groups_per_wave(wname):
+    """One attention split over up to 332 positions (11 groups of 32 for eight waves): once the
+    split passes 256 positions some waves take a second group, whose K/V rows load after the wait,
+    with an online rescale of the wave's softmax.  Prefill crosses that point, decode stays past it;
+    the modes still agree bitwise."""
+    import persistent_megakernel_02_amd as pmk
+    base = TINY if wname == "tiny" else TINY_FP8
+    w = base.with_(name=f"{wname}_long", prompt=300, steps=32)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32) if w.kvdtype == "fp8" else None
+    sched = pmk.schedule_config(attn_splits=1)
+    runs = {name: gpu_run(w, wts, w.steps, mode=m, prompt=prompt, sched=sched, kv_scales=scales)
+            for name, m in _modes()}
+    ref, first_ok = oracle_teacher_forced(w, wts, runs["megakernel"], prompt=prompt, kv_scales=scales)
+    check(w, runs["megakernel"], ref, first_ok, f"{wname}/one split")
+    for name, r in runs.items():
+        assert np.array_equal(r.logits, runs["megakernel"].logits), name
+
+
 # ------------------------------------------------------------------------------------------------
 # workloads at their full model size: synthetic KV of the full prompt length, sampled decode steps
 # ------------------------------------------------------------------------------------------------
