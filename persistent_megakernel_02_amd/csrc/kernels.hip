@@ -509,72 +509,58 @@ __device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float
 // input staging (RMSNorm prologue fused into the consuming GEMV)
 // ------------------------------------------------------------------------------------------------
 // Load n fp32 values from a coherent buffer into xs[0..pad) (zeros past n), every load of a
-// batch issued before any is consumed.  With `gain` (a plain fp32 array of n values, loaded in the
-// same batch) the stored values are src * gain.  Returns the thread's partial sum of squares of
-// the unscaled src values when `want_ss`.
-template <bool want_ss, int B = 8>
-__device__ __forceinline__ float load_vector(const float* src, int n, int pad, float* xs, const float* gain = nullptr) {
+// batch issued before any is consumed.
+template <int B = 8>
+__device__ __forceinline__ void load_vector(const float* src, int n, int pad, float* xs) {
   const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 4);
-  float ss = 0.f;
   for (int base = 0; base < pad; base += B * 4 * kThreads) {
     u32x4 v[B];
-    float4 g[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
       v[k] = i < pad ? ldc16(r, (uint32_t)i * 4) : u32x4{0u, 0u, 0u, 0u};
-      if (gain) g[k] = i < n ? *reinterpret_cast<const float4*>(gain + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
-      if (i < pad) {
-        float4 f = as_f4(v[k]);
-        if (want_ss) ss = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, ss))));
-        if (gain) f = make_float4(f.x * g[k].x, f.y * g[k].y, f.z * g[k].z, f.w * g[k].w);
-        *reinterpret_cast<float4*>(xs + i) = f;
-      }
+      if (i < pad) *reinterpret_cast<float4*>(xs + i) = as_f4(v[k]);
     }
   }
-  return ss;
 }
 
-// RMSNorm prologue, split in two.  stage_rmsnorm writes xs[0..H) = src * gain (xs[H..pad) = 0)
+// RMSNorm prologue, split in two.  The staging writes xs[0..H) = src * gain (xs[H..pad) = 0)
 // and red[w] = wave w's share of sum(src^2), with one batch of loads and one barrier; the factor
 // 1/sqrt(mean(src^2) + eps) (rms_factor) then scales the GEMV results, since every row's dot
 // product with (src * gain) times that factor is its dot product with the normalised input.
-// src is either a coherent fp32 vector or (emb != null) a 16-bit embedding row.
+// This one stages a 16-bit embedding row (the first layer's input); stage_rmsnorm_tagged stages
+// the tagged residual stream.
 template <int EDT>
-__device__ __forceinline__ void stage_rmsnorm(const float* src, const uint16_t* emb, const float* gain, int H, int pad,
-                                              float* xs, float* red) {
+__device__ __forceinline__ void stage_rmsnorm_embed(const uint16_t* emb, const float* gain, int H, int pad, float* xs,
+                                                    float* red) {
   float ss = 0.f;
-  if (emb) {
-    for (int i = 8 * threadIdx.x; i < pad; i += 8 * kThreads) {
-      float f[8], g[8];
-      if (i < H) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(emb + i);
-        const float4 g0 = *reinterpret_cast<const float4*>(gain + i);
-        const float4 g1 = *reinterpret_cast<const float4*>(gain + i + 4);
-        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  for (int i = 8 * threadIdx.x; i < pad; i += 8 * kThreads) {
+    float f[8], g[8];
+    if (i < H) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(emb + i);
+      const float4 g0 = *reinterpret_cast<const float4*>(gain + i);
+      const float4 g1 = *reinterpret_cast<const float4*>(gain + i + 4);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f[2 * k] = dec16<EDT>((uint16_t)(wd[k] & 0xffff));
-          f[2 * k + 1] = dec16<EDT>((uint16_t)(wd[k] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) f[k] = g[k] = 0.f;
+      for (int k = 0; k < 4; ++k) {
+        f[2 * k] = dec16<EDT>((uint16_t)(wd[k] & 0xffff));
+        f[2 * k + 1] = dec16<EDT>((uint16_t)(wd[k] >> 16));
       }
+    } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        xs[i + k] = f[k] * g[k];
-        ss = fmaf(f[k], f[k], ss);
-      }
+      for (int k = 0; k < 8; ++k) f[k] = g[k] = 0.f;
     }
-  } else {
-    ss = load_vector<true>(src, H, pad, xs, gain);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xs[i + k] = f[k] * g[k];
+      ss = fmaf(f[k], f[k], ss);
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -586,12 +572,6 @@ __device__ __forceinline__ float rms_factor(const float* red, int H, float eps) 
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t += red[w];
   return 1.0f / sqrtf(t / (float)H + eps);
-}
-
-// xs[0..n) = src (coherent), zero padding
-__device__ __forceinline__ void stage_copy(const float* src, int n, int pad, float* xs) {
-  load_vector<false>(src, n, pad, xs);
-  __syncthreads();
 }
 
 __device__ __forceinline__ int pad_len(int n, int epl) {
@@ -609,6 +589,99 @@ struct StepCtx {
   int tok;      // input token if already known, else -1
   bool per_op;  // per-op kernels: no waits (kernel boundaries order the tasks)
 };
+
+// Stage a tagged vector src[0..n) of step e into xs (zero padding to pad): every thread re-reads
+// its 16-byte pairs until both tags show step e (bounded by the watchdog; the abort word is
+// checked on every retry).  The reads are the wait; the caller's barrier ends it.  With NORM, xs
+// holds src * gain and the return value is this thread's share of sum(src^2) (the gains are
+// loaded before the first read, since they do not depend on the wait).
+template <bool NORM = false>
+__device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned long long* src, int n, int pad,
+                                              float* xs, int e, bool poll, int cu, int task,
+                                              const float* gain = nullptr) {
+  constexpr int B = 4;  // 16-byte loads (two values) per thread per batch
+  const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 8);
+  const uint32_t want = (uint32_t)(e + 1);
+  float ss = 0.f;
+  for (int base = 0; base < pad; base += B * 2 * kThreads) {
+    u32x4 v[B];
+    bool ok[B];
+    float2 g[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      ok[k] = false;
+      const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
+      if constexpr (NORM) g[k] = i < n ? *reinterpret_cast<const float2*>(gain + i) : make_float2(0.f, 0.f);
+    }
+    int64_t spins = 0;
+    while (true) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // each retry reads memory again
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
+        if (!ok[k]) v[k] = i < n ? ldc16(r, (uint32_t)i * 8) : u32x4{0u, want, 0u, want};
+      }
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        ok[k] = ok[k] || !poll || (v[k].y == want && v[k].w == want);
+        all = all && ok[k];
+      }
+      if (all) break;
+      if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
+      if (++spins > P.spin_limit) {
+        report_error(P.ctrl, PMK_ERR_TIMEOUT, cu, task, -1, want, v[0].y);
+        break;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
+      float a = __uint_as_float(v[k].x), b = __uint_as_float(v[k].z);
+      if constexpr (NORM) {
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+        a *= g[k].x;
+        b *= g[k].y;
+      }
+      if (i < pad) *reinterpret_cast<float2*>(xs + i) = make_float2(a, b);
+    }
+  }
+  return ss;
+}
+
+// RMSNorm prologue from a tagged vector (as stage_rmsnorm): xs = src * gain, red[w] = wave w's
+// share of sum(src^2), one barrier.
+__device__ __forceinline__ void stage_rmsnorm_tagged(const KParams& P, const unsigned long long* src, const float* gain,
+                                                     int H, int pad, float* xs, float* red, int e, bool poll, int cu,
+                                                     int task) {
+  float ss = stage_tagged<true>(P, src, H, pad, xs, e, poll, cu, task, gain);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+}
+
+// One tagged value of step e (re-read until its tag shows e, like stage_tagged).
+__device__ __forceinline__ float ld_tagged(const KParams& P, const unsigned long long* p, int e, bool poll, int cu,
+                                           int task) {
+  const uint32_t want = (uint32_t)(e + 1);
+  int64_t spins = 0;
+  while (true) {
+    const unsigned long long v = ldc(p);
+    if (!poll || (uint32_t)(v >> 32) == want) return __uint_as_float((uint32_t)v);
+    if (ldc(&P.ctrl[CTRL_ABORT]) != 0u || ++spins > P.spin_limit) {
+      if (spins > P.spin_limit) report_error(P.ctrl, PMK_ERR_TIMEOUT, cu, task, -1, want, (uint32_t)(v >> 32));
+      return __uint_as_float((uint32_t)v);
+    }
+  }
+}
+
+// In flags mode a consumer of a tagged vector (x, xm, o) polls the tags instead of its producers'
+// flags, and those producers publish no flag; counters mode keeps counter waits and signals.
+__device__ __forceinline__ bool polls_tags(const KParams& P, const StepCtx& sc) {
+  return !sc.per_op && P.sync_mode != PMK_SYNC_COUNTERS;
+}
+
 
 // An O projection tile that fits the LDS tile area is copied there whole (LDS-DMA) before the
 // task's dependency wait, instead of the register ring's first units: the wait for the attention
@@ -675,16 +748,19 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     float ks8 = 0.f;
     if constexpr (KVDT == WFP8)
       if (threadIdx.x < 2 * P.nkv) ks8 = P.kv_scale[(int64_t)l * P.nkv * 2 + threadIdx.x];
-    maybe_wait(P, t, sc, cu, ti);
+    const bool poll_x = l > 0 && polls_tags(P, sc);
+    if (!poll_x) maybe_wait(P, t, sc, cu, ti);
     if (threadIdx.x < half) rope[threadIdx.x] = cs;
     if constexpr (KVDT == WFP8)
       if (threadIdx.x < 2 * P.nkv) rope[half + threadIdx.x] = make_float2(ks8, 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
-      stage_rmsnorm<EDT>(nullptr, P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
+      stage_rmsnorm_embed<EDT>(P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
     } else {
-      stage_rmsnorm<EDT>(P.x + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H, H, pad, xs, red);
+      stage_rmsnorm_tagged(P, P.x + (int64_t)l * H, P.gains + (int64_t)l * 2 * H, H, pad, xs, red, sc.e,
+                           !sc.per_op, cu, ti);
     }
+    if (poll_x) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int qrows = P.qdim, krows = P.nkv * hd;
@@ -724,9 +800,9 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
       b = b2;
     }
     if (sec == 0) {
-      float* q = P.q + (int64_t)l * P.qdim + head * hd;
-      stc(q + i, a);
-      stc(q + i + half, b);
+      unsigned long long* q = P.q + (int64_t)l * P.qdim + head * hd;
+      stc(q + i, tagged(a, sc.e));
+      stc(q + i + half, tagged(b, sc.e));
       continue;
     }
     // element index of dims i and i + hd/2 at this position: K [pos][hd] rows; V in blocks of 32
@@ -736,17 +812,28 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
                                 : ((hb * (P.seqcap / 32) + sc.pos / 32) * hd + i) * 32 + sc.pos % 32;
     const int64_t ib = sec == 1 ? ia + half : ia + (int64_t)half * 32;
     uint8_t* cache = sec == 1 ? P.kc : P.vc;
+    uint32_t ba, bb;  // the stored elements as 16-bit matrix-core operands (fp8: its bf16 value)
     if constexpr (KVDT == WFP8) {
       const float s8 = rope[half + 2 * head + (sec - 1)].x;
-      stc(cache + ia, enc_e4m3(a / s8));
-      stc(cache + ib, enc_e4m3(b / s8));
+      const uint8_t ca = enc_e4m3(a / s8), cb = enc_e4m3(b / s8);
+      stc(cache + ia, ca);
+      stc(cache + ib, cb);
+      ba = __float_as_uint(dec_e4m3(ca, 0)) >> 16;  // exact: E4M3 values are bf16 values
+      bb = __float_as_uint(dec_e4m3(cb, 0)) >> 16;
     } else {
       uint16_t* c16 = reinterpret_cast<uint16_t*>(cache);
-      stc(c16 + ia, enc16<KVDT>(a));
-      stc(c16 + ib, enc16<KVDT>(b));
+      const uint16_t ca = enc16<KVDT>(a), cb = enc16<KVDT>(b);
+      stc(c16 + ia, ca);
+      stc(c16 + ib, cb);
+      ba = ca;
+      bb = cb;
     }
+    // this step's attention takes the current position from here (tagged), not from the cache
+    unsigned long long* cur = P.kvcur + ((int64_t)hb * 2 + (sec - 1)) * hd;
+    stc(cur + i, tagged(__uint_as_float(ba), sc.e));
+    stc(cur + i + half, tagged(__uint_as_float(bb), sc.e));
   }
-  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+  if (!polls_tags(P, sc)) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 __device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
@@ -873,8 +960,8 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // V^T (A: 8 positions of one dim per lane) times P, one 16 x 16 product
 // per 16 dims (V is stored in blocks of 32 positions, [pos / 32][hd][pos % 32], so one wave
 // instruction reads 1 KiB of contiguous cache).  q and P enter as 16-bit hi + lo pairs (two products each), so the result keeps
-// about fp32 precision.  Rows of past positions are loaded before the dependency wait; the
-// current position (written this step) after it, coherently.  The wave's softmax (max and sum
+// about fp32 precision.  K/V rows are loaded from the cache before the dependency wait; the
+// current position (written this step) comes from its tagged copy, which wave 0 stages with q.  The wave's softmax (max and sum
 // across the four lanes of a head column with column_max / column_sum) runs on the 8 scores a
 // lane holds; the eight waves' (max, sum, acc) are then merged in LDS with the usual rescaling,
 // exactly as the splits are merged by the combine.
@@ -901,6 +988,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   float* qs = lds;                      // [grp][HD]
   float* red = qs + grp * HD;           // [kWaves][grp][HD] per-wave P.V partials
   float* wml = red + kWaves * grp * HD; // [kWaves][grp][2] per-wave (max, sum)
+  uint32_t* kvs = reinterpret_cast<uint32_t*>(wml + kWaves * grp * 2);  // [2][HD] current K row, V column
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KVDT == WFP8) {
     kscale = P.kv_scale[head * 2];
@@ -923,58 +1011,117 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   auto pk_of = [&](int k) { return t0 + 32 * (wv + kWaves * k) + 8 * (col >> 2) + (col & 3); };
   auto pv_of = [&](int k) { return t0 + 32 * (wv + kWaves * k) + 8 * grp4; };
   u32x4 ka[NC], kb[NC], vt[NT];
-  // K rows of group k; the current position (written this step) coherently, after the wait
-  auto load_k = [&](int k, bool after_wait) {
+  // K rows and V^T positions of group k from the cache; the current position's slot (written
+  // this step) is replaced from the tagged copy staged in LDS before it is used
+  auto load_k = [&](int k) {
     const int pk0 = pk_of(k);
-    const bool c0 = pk0 == sc.pos, c1 = pk0 + 4 == sc.pos;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (after_wait && (c0 || c1)) {
-        ka[c] = c0 ? kv_load8<KVDT, true>(kr, koff(pk0, c)) : kv_load8<KVDT, false>(kr, koff(pk0, c));
-        kb[c] = c1 ? kv_load8<KVDT, true>(kr, koff(pk0 + 4, c)) : kv_load8<KVDT, false>(kr, koff(pk0 + 4, c));
-      } else {
-        ka[c] = kv_load8<KVDT, false>(kr, c0 ? kOut : koff(pk0, c));
-        kb[c] = kv_load8<KVDT, false>(kr, c1 ? kOut : koff(pk0 + 4, c));
-      }
+      ka[c] = kv_load8<KVDT, false>(kr, koff(pk0, c));
+      kb[c] = kv_load8<KVDT, false>(kr, koff(pk0 + 4, c));
     }
   };
-  auto load_v = [&](int k, bool after_wait) {
+  auto load_v = [&](int k) {
     const int pv = pv_of(k);
-    const bool cur = pv <= sc.pos && sc.pos < pv + 8;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-      vt[tt] = after_wait && cur ? kv_load8<KVDT, true>(vr, voff(pv, tt))
-                                 : kv_load8<KVDT, false>(vr, cur ? kOut : voff(pv, tt));
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, false>(vr, voff(pv, tt));
   };
-  // group 0, past positions: before the dependency wait
-  load_k(0, false);
-  load_v(0, false);
-  maybe_wait(P, t, sc, cu, ti);
-  {
-    // group 0, the current position: coherent loads, with q's
-    const int pk0 = pk_of(0), pv = pv_of(0);
-    const bool cur0 = pk0 == sc.pos, cur1 = pk0 + 4 == sc.pos;
-    if (cur0 || cur1) {
+  auto patch_k = [&](int k) {
+    const int pk0 = pk_of(k);
+    const bool c0 = pk0 == sc.pos, c1 = pk0 + 4 == sc.pos;
+    if (c0 || c1) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 v = kv_load8<KVDT, true>(kr, koff(sc.pos, c));
-        if (cur0) ka[c] = v;
+        const uint32_t* e = kvs + 32 * c + 8 * grp4;
+        const u32x4 v = {e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        if (c0) ka[c] = v;
         else kb[c] = v;
       }
     }
+  };
+  auto patch_v = [&](int k) {
+    const int pv = pv_of(k);
     if (pv <= sc.pos && sc.pos < pv + 8) {
+      const int e = sc.pos - pv, wi = e >> 1;
+      const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      const int sh = (e & 1) ? 16 : 0;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, true>(vr, voff(pv, tt));
+      for (int tt = 0; tt < NT; ++tt) {
+        const uint32_t b = kvs[HD + 16 * tt + col] << sh;
+        vt[tt].x = wi == 0 ? (vt[tt].x & keep) | b : vt[tt].x;
+        vt[tt].y = wi == 1 ? (vt[tt].y & keep) | b : vt[tt].y;
+        vt[tt].z = wi == 2 ? (vt[tt].z & keep) | b : vt[tt].z;
+        vt[tt].w = wi == 3 ? (vt[tt].w & keep) | b : vt[tt].w;
+      }
     }
-  }
+  };
+  // group 0: before the dependency wait
+  load_k(0);
+  load_v(0);
+  // Wave 0 stages q of the group's heads and, in the split that holds the current position, that
+  // position's K row and V column (16-bit operand bits), all tagged with the step.  In flags mode
+  // the tagged reads are the wait; otherwise the counter wait comes first.
+  const bool poll = polls_tags(P, sc);
+  if (!poll) maybe_wait(P, t, sc, cu, ti);
   if (wave == 0) {
-    const __amdgpu_buffer_rsrc_t qr = coherent_rsrc(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, grp * HD * 4);
-    u32x4 qv[(16 * HD) / 256];  // grp <= 16 heads: grp * HD floats, 4 per lane per load
+    constexpr int QB = 4, CB = HD / 64;  // 16-byte pairs per lane per round: q; current K and V
+    const uint32_t want = (uint32_t)(sc.e + 1);
+    const int nq = grp * HD;
+    const bool has_cur = t0 <= sc.pos && sc.pos < t1;
+    const __amdgpu_buffer_rsrc_t qr = coherent_rsrc(P.q + (int64_t)l * P.qdim + (int64_t)g * grp * HD, nq * 8);
+    const __amdgpu_buffer_rsrc_t cr = coherent_rsrc(P.kvcur + head * 2 * HD, 2 * HD * 8);
+    for (int base = 0; base < nq; base += QB * 128) {
+      const bool first = base == 0;
+      u32x4 v[QB], c[CB];
+      bool okv[QB], okc[CB];
 #pragma unroll
-    for (int k = 0; k < (16 * HD) / 256; ++k) qv[k] = ldc16(qr, (uint32_t)(k * 256 + lane * 4) * 4u);
+      for (int k = 0; k < QB; ++k) okv[k] = false;
 #pragma unroll
-    for (int k = 0; k < (16 * HD) / 256; ++k)
-      if (k * 256 + lane * 4 < grp * HD) *reinterpret_cast<float4*>(qs + k * 256 + lane * 4) = as_f4(qv[k]);
+      for (int k = 0; k < CB; ++k) okc[k] = false;
+      int64_t spins = 0;
+      while (true) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // each retry reads memory again
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+          const int i = base + (k * 64 + lane) * 2;
+          if (!okv[k]) v[k] = i < nq ? ldc16(qr, (uint32_t)i * 8) : u32x4{0u, want, 0u, want};
+        }
+#pragma unroll
+        for (int k = 0; k < CB; ++k)
+          if (!okc[k]) c[k] = first && has_cur ? ldc16(cr, (uint32_t)(k * 64 + lane) * 16) : u32x4{0u, want, 0u, want};
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < QB; ++k) {
+          okv[k] = okv[k] || sc.per_op || (v[k].y == want && v[k].w == want);
+          all = all && okv[k];
+        }
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+          okc[k] = okc[k] || sc.per_op || (c[k].y == want && c[k].w == want);
+          all = all && okc[k];
+        }
+        if (__ballot(!all) == 0ull) break;
+        if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
+        if (++spins > P.spin_limit) {
+          report_error(P.ctrl, PMK_ERR_TIMEOUT, cu, ti, -1, want, v[0].y);
+          break;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < QB; ++k) {
+        const int i = base + (k * 64 + lane) * 2;
+        if (i < nq) *reinterpret_cast<float2*>(qs + i) = make_float2(__uint_as_float(v[k].x), __uint_as_float(v[k].z));
+      }
+      if (first && has_cur) {
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+          const int i = (k * 64 + lane) * 2;
+          kvs[i] = c[k].x;
+          kvs[i + 1] = c[k].z;
+        }
+      }
+    }
+    if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
   }
   __syncthreads();
   const float qk_scale = kscale * P.attn_scale;
@@ -986,6 +1133,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   for (int k = 0; k < NGW; ++k) {
     if (t0 + 32 * (wv + kWaves * k) >= t1) break;  // wave-uniform: no positions left
     const int pv = pv_of(k);
+    patch_k(k);
     // positions past the split's end (the last V^T group may straddle it) contribute nothing
     if (pv < t1 && pv + 8 > t1) {
 #pragma unroll
@@ -1006,7 +1154,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       s1 = mfma16<KVDT>(kb[c], ql, s1);
     }
     const bool next = k + 1 < NGW && t0 + 32 * (wv + kWaves * (k + 1)) < t1;
-    if (next) load_k(k + 1, true);
+    if (next) load_k(k + 1);
     // ---- softmax: the lane holds positions pv + 0..7 of head column col ----
     float sc8[8];
     float mk = -INFINITY;
@@ -1035,6 +1183,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     sum += ps;
     m = mn;
     // ---- P.V: 16 dims x 16 head columns per tile ----
+    patch_v(k);
     u32x4 ph, pl;
     split16<KVDT>(sc8, ph, pl);
 #pragma unroll
@@ -1042,7 +1191,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
       acc[tt] = mfma16<KVDT>(vt[tt], pl, acc[tt]);
     }
-    if (next) load_v(k + 1, true);
+    if (next) load_v(k + 1);
   }
   if (col < grp) {
     float* dst = red + ((int64_t)wave * grp + col) * HD + 4 * grp4;
@@ -1149,49 +1298,7 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
   mark(P, sc, ti, 4);
   // With flags, the O projection polls the tags of o itself (no drain, no flag); counters keep
   // the drained signal.
-  if (P.sync_mode == PMK_SYNC_COUNTERS) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
-}
-
-// Stage the tagged attention output o[0..n) of step e into xs (zero padding to pad): every thread
-// re-reads its 16-byte pairs until both tags show step e (bounded by the watchdog; the abort word
-// is checked on every retry), then the workgroup barrier.  The reads are the wait.
-__device__ __forceinline__ void stage_tagged(const KParams& P, const unsigned long long* src, int n, int pad,
-                                             float* xs, int e, bool poll, int cu, int task) {
-  constexpr int B = 4;  // 16-byte loads (two values) per thread per batch
-  const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 8);
-  const uint32_t want = (uint32_t)(e + 1);
-  for (int base = 0; base < pad; base += B * 2 * kThreads) {
-    u32x4 v[B];
-    bool ok[B];
-#pragma unroll
-    for (int k = 0; k < B; ++k) ok[k] = false;
-    int64_t spins = 0;
-    while (true) {
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // each retry reads memory again
-#pragma unroll
-      for (int k = 0; k < B; ++k) {
-        const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
-        if (!ok[k]) v[k] = i < n ? ldc16(r, (uint32_t)i * 8) : u32x4{0u, want, 0u, want};
-      }
-      bool all = true;
-#pragma unroll
-      for (int k = 0; k < B; ++k) {
-        ok[k] = ok[k] || !poll || (v[k].y == want && v[k].w == want);
-        all = all && ok[k];
-      }
-      if (all) break;
-      if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
-      if (++spins > P.spin_limit) {
-        report_error(P.ctrl, PMK_ERR_TIMEOUT, cu, task, -1, want, v[0].y);
-        break;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int i = base + (k * kThreads + (int)threadIdx.x) * 2;
-      if (i < pad) *reinterpret_cast<float2*>(xs + i) = make_float2(__uint_as_float(v[k].x), __uint_as_float(v[k].z));
-    }
-  }
+  if (!polls_tags(P, sc)) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 // O projection + residual: xm[r] = x[r] + Wo[r].o  (residual rows staged in LDS with the input)
@@ -1207,15 +1314,17 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   float* y = lds + P.o_y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_o;
   // flags mode: the wait on the combines is the tag poll of o below
-  const bool poll_o = !sc.per_op && P.sync_mode != PMK_SYNC_COUNTERS;
+  const bool poll_o = polls_tags(P, sc);
   auto sync = [&]() {
     if (!poll_o) maybe_wait(P, t, sc, cu, ti);
     const int tok = l == 0 ? input_token(P, sc) : 0;
     float rv = 0.f;  // first kThreads residual rows ride with the input loads
     if ((int)threadIdx.x < R)
-      rv = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + threadIdx.x]) : ldc(P.x + (int64_t)l * P.H + t.a0 + threadIdx.x);
+      rv = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + threadIdx.x])
+                  : ld_tagged(P, P.x + (int64_t)l * P.H + t.a0 + threadIdx.x, sc.e, !sc.per_op, cu, ti);
     for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
-      res[i] = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i]) : ldc(P.x + (int64_t)l * P.H + t.a0 + i);
+      res[i] = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i])
+                      : ld_tagged(P, P.x + (int64_t)l * P.H + t.a0 + i, sc.e, !sc.per_op, cu, ti);
     stage_tagged(P, P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs, sc.e, !sc.per_op, cu, ti);
     if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
     __syncthreads();
@@ -1231,8 +1340,8 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   } else
     gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow, kOprojRowCost);
   mark(P, sc, ti, 5);
-  for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, res[i] + y[i]);
-  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+  for (int i = threadIdx.x; i < R; i += kThreads) stc(P.xm + (int64_t)l * P.H + t.a0 + i, tagged(res[i] + y[i], sc.e));
+  if (!polls_tags(P, sc)) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 // RMSNorm(xm) -> interleaved gate/up rows [a0, a1) -> h[n] = silu(gate_n) * up_n
@@ -1246,9 +1355,11 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
   float* y = lds + P.y_off;
   const uint8_t* W = P.wbase + (int64_t)l * P.layer_bytes + P.off_gu;
   auto sync = [&]() {
-    maybe_wait(P, t, sc, cu, ti);
-    stage_rmsnorm<WBF16>(P.xm + (int64_t)l * H, nullptr, P.gains + (int64_t)l * 2 * H + H, H,
-                         pad_len(H, WFmt<WDT>::EPL), xs, red);
+    const bool poll = polls_tags(P, sc);
+    if (!poll) maybe_wait(P, t, sc, cu, ti);
+    stage_rmsnorm_tagged(P, P.xm + (int64_t)l * H, P.gains + (int64_t)l * 2 * H + H, H, pad_len(H, WFmt<WDT>::EPL),
+                         xs, red, sc.e, !sc.per_op, cu, ti);
+    if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
@@ -1279,9 +1390,10 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
   auto sync = [&]() {
     maybe_wait(P, t, sc, cu, ti);
     float rv = 0.f;
-    if ((int)threadIdx.x < R) rv = ldc(P.xm + (int64_t)l * P.H + t.a0 + threadIdx.x);
-    for (int i = threadIdx.x + kThreads; i < R; i += kThreads) res[i] = ldc(P.xm + (int64_t)l * P.H + t.a0 + i);
-    load_vector<false>(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    if ((int)threadIdx.x < R) rv = ld_tagged(P, P.xm + (int64_t)l * P.H + t.a0 + threadIdx.x, sc.e, !sc.per_op, cu, ti);
+    for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
+      res[i] = ld_tagged(P, P.xm + (int64_t)l * P.H + t.a0 + i, sc.e, !sc.per_op, cu, ti);
+    load_vector(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
     if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
     __syncthreads();
     mark(P, sc, ti, 4);
@@ -1291,8 +1403,9 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
   auto srow = [=](int r) -> const float* { return sd + (int64_t)(r / 128) * nbc; };
   gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
-  for (int i = threadIdx.x; i < R; i += kThreads) stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, res[i] + y[i]);
-  block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
+  for (int i = threadIdx.x; i < R; i += kThreads)
+    stc(P.x + (int64_t)(l + 1) * P.H + t.a0 + i, tagged(res[i] + y[i], sc.e));
+  if (!polls_tags(P, sc)) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
 // final RMSNorm + LM-head rows [a0, a1); tile argmax folded into the step's 64-bit key
@@ -1321,8 +1434,11 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
   float* y = lds + P.y_off;
   float* out_logits = P.call->out_logits;
   auto sync = [&]() {
-    maybe_wait(P, t, sc, cu, ti);
-    stage_rmsnorm<WBF16>(P.x + (int64_t)P.L * H, nullptr, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), xs, red);
+    const bool poll = polls_tags(P, sc);
+    if (!poll) maybe_wait(P, t, sc, cu, ti);
+    stage_rmsnorm_tagged(P, P.x + (int64_t)P.L * H, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), xs, red, sc.e,
+                         !sc.per_op, cu, ti);
+    if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
@@ -1498,6 +1614,10 @@ __global__ void pmk_reset(KParams P, int n_flags, int n_counters, int pos, int t
   for (int k = i; k < n_flags; k += n) P.flags[k] = 0u;
   for (int k = i; k < n_counters; k += n) P.counters[k] = 0u;
   for (int64_t k = i; k < (int64_t)P.L * P.qdim; k += n) P.o[k] = 0ull;
+  for (int64_t k = i; k < (int64_t)(P.L + 1) * P.H; k += n) P.x[k] = 0ull;
+  for (int64_t k = i; k < (int64_t)P.L * P.H; k += n) P.xm[k] = 0ull;
+  for (int64_t k = i; k < (int64_t)P.L * P.qdim; k += n) P.q[k] = 0ull;
+  for (int64_t k = i; k < (int64_t)P.L * P.nkv * 2 * P.hd; k += n) P.kvcur[k] = 0ull;
   for (int k = i; k < CTRL_WORDS; k += n) P.ctrl[k] = 0u;
   __syncthreads();
   if (i == 0) {

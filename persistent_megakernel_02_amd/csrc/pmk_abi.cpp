@@ -62,7 +62,7 @@ struct pmk_ctx {
   int64_t a_gains = 0, a_final = 0, a_scales = 0, sc_layer = 0, sc_off[7] = {}, a_sclm = 0, a_rope = 0;
   // workspace layout (bytes)
   int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_kvscale = 0, w_x = 0,
-          w_xm = 0, w_q = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
+          w_xm = 0, w_q = 0, w_kvcur = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
           w_cprod = 0, w_cflag = 0;
   uint8_t* arena = nullptr;
   uint8_t* kv = nullptr;
@@ -195,9 +195,10 @@ void compute_layout(pmk_ctx* c) {
   c->w_counters = w; w = align256(w + (int64_t)s.counters.size() * 4);
   c->w_keys = w; w = align256(w + ((int64_t)m.max_seq + 1) * 8);
   c->w_kvscale = w; w = align256(w + L * m.nkv * 2 * 4);
-  c->w_x = w; w = align256(w + (L + 1) * H * 4);
-  c->w_xm = w; w = align256(w + L * H * 4);
-  c->w_q = w; w = align256(w + L * qd * 4);
+  c->w_x = w; w = align256(w + (L + 1) * H * 8);  // (tag, value) pairs
+  c->w_xm = w; w = align256(w + L * H * 8);
+  c->w_q = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
+  c->w_kvcur = w; w = align256(w + L * m.nkv * 2 * m.hd * 8);
   c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 4) * 4);
   c->w_o = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
   c->w_h = w; w = align256(w + L * F * 4);
@@ -214,7 +215,7 @@ void compute_layout(pmk_ctx* c) {
   auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
   const int64_t grp = m.grp();
   // attention: q [grp][hd], per-wave P.V partials [8][grp][hd], per-wave (max, sum) [8][grp][2]
-  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2;
+  const int64_t attn = grp * m.hd + kWaves * grp * m.hd + kWaves * grp * 2 + 2 * m.hd;
   const int64_t xs = std::max({padn(H), padn(qd), padn(F), attn});
   c->xs_floats = (int)((xs + 63) / 64 * 64);
   // epilogue inputs staged behind the scratch words: the RoPE row (+ fp8 K/V scales) of QKV tasks,
@@ -277,9 +278,10 @@ void fill_params(pmk_ctx* c) {
   P.counters = reinterpret_cast<uint32_t*>(W + c->w_counters);
   P.keys = reinterpret_cast<unsigned long long*>(W + c->w_keys);
   P.kv_scale = reinterpret_cast<float*>(W + c->w_kvscale);
-  P.x = reinterpret_cast<float*>(W + c->w_x);
-  P.xm = reinterpret_cast<float*>(W + c->w_xm);
-  P.q = reinterpret_cast<float*>(W + c->w_q);
+  P.x = reinterpret_cast<unsigned long long*>(W + c->w_x);
+  P.xm = reinterpret_cast<unsigned long long*>(W + c->w_xm);
+  P.q = reinterpret_cast<unsigned long long*>(W + c->w_q);
+  P.kvcur = reinterpret_cast<unsigned long long*>(W + c->w_kvcur);
   P.part = reinterpret_cast<float*>(W + c->w_part);
   P.o = reinterpret_cast<unsigned long long*>(W + c->w_o);
   P.h = reinterpret_cast<float*>(W + c->w_h);

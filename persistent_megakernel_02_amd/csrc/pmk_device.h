@@ -67,9 +67,10 @@ struct KParams {
   uint32_t* counters;
   unsigned long long* keys;  // [max_seq + 1]
   float* kv_scale;        // [L][nkv][2]
-  float* x;               // [L+1][H]
-  float* xm;              // [L][H]
-  float* q;               // [L][qdim]
+  unsigned long long* x;   // [L+1][H] residual stream entering each layer (and the final norm), tagged
+  unsigned long long* xm;  // [L][H] residual after the attention block, tagged
+  unsigned long long* q;      // [L][qdim] roped queries, tagged
+  unsigned long long* kvcur;  // [L][nkv][2][hd] the step's K row and V column as 16-bit operand bits, tagged
   float* part;            // [L][nkv][S][grp][hd+4]: m, l, 2 pad, acc[hd]
   unsigned long long* o;  // [L][qdim] attention output, each value tagged: (step + 1) << 32 | fp32 bits
   float* h;               // [L][F]
