@@ -64,8 +64,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
-    ap.add_argument("--tune", action="store_true",
-                    help="speed-weighted GEMV row split before the timed launch (pmk_tune; neutral on the boxes measured)")
+    ap.add_argument("--no-tune", dest="tune", action="store_false",
+                    help="keep the even GEMV row split (default: pmk_tune re-splits the gate/up rows by the streaming "
+                         "rate each CU measured in a traced warm-up, before the timed launch)")
     ap.add_argument("--repeat", type=int, default=1, help="extra timed launches reported as a spread")
     ap.add_argument("--kernel-only", action="store_true",
                     help="profiling: start from synthetic KV instead of a prefill and skip every leg but the timed launches")
@@ -236,7 +237,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, random prompt)",
         "config": {"workload": w.name, "layers": w.layers, "hidden": w.hidden, "heads": [w.n_q, w.n_kv],
                    "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "prompt": P, "decode_steps": K,
-                   "batch": 1, "mode": args.mode, "sync": args.sync, "parallelism": "single GPU"},
+                   "batch": 1, "mode": args.mode, "sync": args.sync, "parallelism": "single GPU",
+                   "row_split": "tuned (gate/up)" if args.tune else "even"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
