@@ -227,10 +227,10 @@ pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
 
 /* Speed-weighted row split (tuning).  Runs `steps` decode steps (<= the trace ring; <= 0: all of
  * it) from the current position with the megakernel and tracing on, measures every queue's
- * weight-streaming rate per GEMV phase (QKV, O, gate/up, down, LM head) from the trace, rebuilds
- * the schedule with each GEMV task's rows proportional to its queue's rate (compute units of a
- * device do not stream at one rate: the split evens out when they finish a phase), validates and
- * installs it, then restores the position and next input token it started from (the KV rows it
+ * gate/up weight-streaming rate from the trace, rebuilds the schedule with each gate/up task's
+ * row share moved half-way from even toward proportional to its queue's rate (compute units of a
+ * device do not stream at one rate: the split evens out when they finish the phase; the other
+ * GEMV phases keep the even split), validates and installs it, then restores the position and next input token it started from (the KV rows it
  * wrote past that position are rewritten by the next decode).  Synchronous on `stream`.  Requires
  * bound weights and KV state and a context created with trace_steps >= 1.  Row assignment never
  * changes a row's arithmetic beyond the grouping of its partial sums. */
