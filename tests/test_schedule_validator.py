@@ -88,6 +88,18 @@ def test_real_lowerings_are_accepted(name, n_cus, kw):
     assert st == 0, msg
 
 
+@pytest.mark.parametrize("max_seq,want_s", [(512, 1), (513, 2), (1024, 2), (1100, 3)])
+def test_split_count_keeps_chunks_within_two_groups_per_wave(max_seq, want_s):
+    """An attention task holds at most 512 positions (8 waves x two 32-position groups): asking for
+    one split raises the count to ceil(max_seq / 512), and the lowering validates."""
+    w = WORKLOADS["tiny"].with_(prompt=max_seq - 32, steps=32)
+    s = Sched(w, 8, attn_splits=1)
+    tasks = [s.task(i) for i in range(s.n_tasks)]
+    assert sum(1 for t in tasks if t.op == 2 and t.layer == 0 and t.a0 == 0) == want_s
+    st, msg = s.validate()
+    assert st == 0, msg
+
+
 @pytest.mark.parametrize("n_cus", [2, 5, 8])
 def test_simulator_runs_real_lowerings_clean(n_cus):
     s = Sched(WORKLOADS["tiny"], n_cus)
