@@ -965,7 +965,7 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // across the four lanes of a head column with column_max / column_sum) runs on the 8 scores a
 // lane holds; the eight waves' (max, sum, acc) are then merged in LDS with the usual rescaling,
 // exactly as the splits are merged by the combine.
-template <int WDT, int KVDT, int HD, int NGW>
+template <int WDT, int KVDT, int HD, int NGW, bool G2LDS = false>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
@@ -1058,6 +1058,41 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   // group 0: before the dependency wait
   load_k(0);
   load_v(0);
+  // A second group (splits of more than 8 groups), in the persistent kernel when LDS has room: its
+  // K rows and V block (contiguous in the cache) are copied to this wave's LDS buffer before the
+  // wait too, so its loads are not issued only after the first group's products (two exposed
+  // memory round trips); per-op kernels load them into registers as below.  Rows past the
+  // split's end are zeroed as the buffer-resource path does.
+  constexpr int G2K = 32 * ROWB, G2B = G2K + HD * 32 * KES;  // bytes: K rows, + V block
+  constexpr bool g2_lds = NGW == 2 && G2LDS;  // the caller checked: persistent kernel, buffers present
+  const int p1 = t0 + 32 * (wv + kWaves);  // the second group's first position
+  const uint8_t* g2 = reinterpret_cast<const uint8_t*>(lds + (P.attn_g2_off < 0 ? 0 : P.attn_g2_off)) + wave * G2B;
+  if (g2_lds && p1 < t1) {
+#pragma unroll
+    for (int u = 0; u < G2K / 1024; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g2 + u * 1024), 16,
+                                               (uint32_t)(p1 * ROWB + u * 1024 + lane * 16), 0, 0, 2);
+#pragma unroll
+    for (int u = 0; u < (G2B - G2K) / 1024; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g2 + G2K + u * 1024), 16,
+                                               (uint32_t)((p1 >> 5) * HD * 32 * KES + u * 1024 + lane * 16), 0,
+                                               0, 2);
+  }
+  auto lds8 = [&](int off) -> u32x4 {  // 8 elements of the second group's buffer as 16-bit operands
+    if constexpr (KVDT == WFP8) return fp8x8_bf16(*reinterpret_cast<const u32x2*>(g2 + off));
+    else return *reinterpret_cast<const u32x4*>(g2 + off);
+  };
+  auto lds_group2 = [&]() {
+    const int pk0 = pk_of(1), pv = pv_of(1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      ka[c] = pk0 < t1 ? lds8((pk0 - p1) * ROWB + (32 * c + 8 * grp4) * KES) : u32x4{0u, 0u, 0u, 0u};
+      kb[c] = pk0 + 4 < t1 ? lds8((pk0 + 4 - p1) * ROWB + (32 * c + 8 * grp4) * KES) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      vt[tt] = pv < t1 ? lds8(G2K + ((16 * tt + col) * 32 + (pv & 31)) * KES) : u32x4{0u, 0u, 0u, 0u};
+  };
   // Wave 0 stages q of the group's heads and, in the split that holds the current position, that
   // position's K row and V column (16-bit operand bits), all tagged with the step.  In flags mode
   // the tagged reads are the wait; otherwise the counter wait comes first.
@@ -1133,6 +1168,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   for (int k = 0; k < NGW; ++k) {
     if (t0 + 32 * (wv + kWaves * k) >= t1) break;  // wave-uniform: no positions left
     const int pv = pv_of(k);
+    if (k > 0 && g2_lds) lds_group2();
     patch_k(k);
     // positions past the split's end (the last V^T group may straddle it) contribute nothing
     if (pv < t1 && pv + 8 > t1) {
@@ -1154,7 +1190,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       s1 = mfma16<KVDT>(kb[c], ql, s1);
     }
     const bool next = k + 1 < NGW && t0 + 32 * (wv + kWaves * (k + 1)) < t1;
-    if (next) load_k(k + 1);
+    if (next && !g2_lds) load_k(k + 1);
     // ---- softmax: the lane holds positions pv + 0..7 of head column col ----
     float sc8[8];
     float mk = -INFINITY;
@@ -1191,7 +1227,7 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
       acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
       acc[tt] = mfma16<KVDT>(vt[tt], pl, acc[tt]);
     }
-    if (next) load_v(k + 1);
+    if (next && !g2_lds) load_v(k + 1);
   }
   if (col < grp) {
     float* dst = red + ((int64_t)wave * grp + col) * HD + 4 * grp4;
@@ -1506,8 +1542,13 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
     case PMK_OP_ATTN:
       // splits longer than 8 groups of 32 positions give each wave a second group
       if (((sc.pos + P.S) / P.S + 31) / 32 > kWaves) {
-        if (P.hd == 128) task_attn<WDT, KVDT, 128, 2>(P, t, ti, sc, lds, cu);
-        else task_attn<WDT, KVDT, 64, 2>(P, t, ti, sc, lds, cu);
+        if (!sc.per_op && P.attn_g2_off >= 0) {
+          if (P.hd == 128) task_attn<WDT, KVDT, 128, 2, true>(P, t, ti, sc, lds, cu);
+          else task_attn<WDT, KVDT, 64, 2, true>(P, t, ti, sc, lds, cu);
+        } else {
+          if (P.hd == 128) task_attn<WDT, KVDT, 128, 2>(P, t, ti, sc, lds, cu);
+          else task_attn<WDT, KVDT, 64, 2>(P, t, ti, sc, lds, cu);
+        }
       } else {
         if (P.hd == 128) task_attn<WDT, KVDT, 128, 1>(P, t, ti, sc, lds, cu);
         else task_attn<WDT, KVDT, 64, 1>(P, t, ti, sc, lds, cu);

@@ -73,7 +73,7 @@ struct pmk_ctx {
   int trace_on = 0;
   int xs_floats = 0;
   int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0;
-  int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_units = 0;
+  int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_units = 0, attn_g2_off = -1;
   size_t lds_bytes = 0;     // per-op kernels
   size_t lds_bytes_pk = 0;  // persistent kernel (adds the O-projection tile area)
   KParams kp{};
@@ -245,6 +245,18 @@ void compute_layout(pmk_ctx* c) {
   c->pf_units = c->sc.prefetch == 2 ? (int)std::max<int64_t>(0, (lds_floats - c->pf_off) / 256) : 0;
   c->lds_bytes_pk = c->pf_units > 0 ? std::max(c->lds_bytes, (size_t)(c->pf_off + (int64_t)c->pf_units * 256) * 4)
                                     : c->lds_bytes;
+  // attention splits longer than 8 groups of 32 positions: per-wave buffers for the second group
+  // (its K rows and V block), behind the attention scratch, when they fit
+  c->attn_g2_off = -1;
+  if (((int64_t)m.max_seq + s.attn_splits - 1) / s.attn_splits > 32 * kWaves) {
+    const int64_t kes = m.kvdt == PMK_DT_FP8_E4M3 ? 1 : 2;
+    const int64_t g2_floats = kWaves * (32 * m.hd * kes + m.hd * 32 * kes) / 4;
+    const int64_t off = r64(attn);
+    if (off + g2_floats <= lds_floats) {
+      c->attn_g2_off = (int)off;
+      c->lds_bytes_pk = std::max(c->lds_bytes_pk, (size_t)(off + g2_floats) * 4);
+    }
+  }
 }
 
 void fill_params(pmk_ctx* c) {
@@ -305,6 +317,7 @@ void fill_params(pmk_ctx* c) {
   P.o_yp_off = c->o_yp_off;
   P.o_y_off = c->o_y_off;
   P.pf_off = c->pf_off;
+  P.attn_g2_off = c->attn_g2_off;
   P.pf_units = c->pf_units;
 }
 

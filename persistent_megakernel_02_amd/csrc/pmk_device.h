@@ -88,6 +88,7 @@ struct KParams {
   int yp_off;             // LDS float offset of per-slice GEMV partial sums [8 * rows]
   int y_off;              // LDS float offset of GEMV row results [rows]
   int o_epi_off, o_yp_off, o_y_off;  // the same three areas for OPROJ tasks, packed below pf_off
+  int attn_g2_off;        // LDS float offset of the attention's per-wave second-group buffers (-1: none)
   int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)
   int pf_units;           // 1 KiB units in that area (0: the copy is off)
 };
