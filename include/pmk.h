@@ -248,7 +248,8 @@ typedef enum {
   PMK_OP_DOWN = 5,    /* down GEMV rows [a0,a1) + residual */
   PMK_OP_LMHEAD = 6,  /* final RMSNorm + LM-head rows [a0,a1) + tile argmax into the step key */
   PMK_OP_TOKEN = 7,   /* reads the step key, writes the output token and the next-input slot */
-  PMK_OP_COMBINE = 8  /* merges the attention partials of every split of kv head a0 into o */
+  PMK_OP_COMBINE = 8  /* merges the attention partials of every split of kv head a0 into o, for the
+                         group's q heads [a1 & 255, a1 >> 8) */
 } pmk_op;
 
 typedef struct {

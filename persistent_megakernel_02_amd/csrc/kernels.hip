@@ -1267,8 +1267,10 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
 }
 
-// Combine of the attention splits of kv head g: waits for all S partials of the head group, then
-// o = sum_s exp(m_s - M) acc_s / sum_s exp(m_s - M) l_s per head, M = max_s m_s.
+// Combine of the attention splits of kv head g for the group's q heads [j0, j1) (a1 = j0 | j1 << 8;
+// a group is split over several combines when one would read too many partials): waits for all
+// S partials of the head group, then o = sum_s exp(m_s - M) acc_s / sum_s exp(m_s - M) l_s per
+// head, M = max_s m_s.
 template <int HD>
 __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, int cu) {
   constexpr int PSTR = HD + 4;  // partial record: m, l, 2 pad, acc[hd]
@@ -1285,8 +1287,9 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
     const __amdgpu_buffer_rsrc_t pr = coherent_rsrc(pg, (uint32_t)((int64_t)S * grp * PSTR * 4));
     unsigned long long* o = P.o + (int64_t)l * P.qdim + (int64_t)g * grp * HD;
     const int r = tid & 3;
-    for (int qd = tid >> 2; qd < grp * QPH; qd += kThreads / 4) {
-      const int j = qd / QPH, d0 = (qd % QPH) * 4;
+    const int j0 = t.a1 & 255, j1 = t.a1 >> 8;  // this task's q heads of the group
+    for (int qd = tid >> 2; qd < (j1 - j0) * QPH; qd += kThreads / 4) {
+      const int j = j0 + qd / QPH, d0 = (qd % QPH) * 4;
       float M = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
       for (int sb = 0; sb < S; sb += 4 * CB) {
         u32x4 hv[CB], av[CB];

@@ -109,9 +109,32 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   const int n_attn = m.nkv * S;
   // COMBINE of kv head g runs on the queue of its last split (the shortest one), right after it;
   // the O projection then skips those queues when enough others remain, so a combine's latency
-  // never delays an O-projection tile
+  // never delays an O-projection tile.  A combine reads every split's partial of its heads, one
+  // batch of loads per thread per 32 splits: when that is much more than ~48 KiB for one CU, the
+  // head group is split over CP combines (a divisor of the group, each on the queue of one of the
+  // last CP splits), as long as the O-projection tiles of the remaining queues still fit the LDS
+  // tile area (~128 KiB).
+  const int grp = m.grp();
+  const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
+  const int64_t o_slices = ((int64_t)m.qdim() / epl + 63) / 64;
+  const int64_t cbytes = (int64_t)S * grp * (m.hd + 4) * 4;
+  auto o_fits = [&](int cp) {
+    const int64_t nq = n_queues - (int64_t)m.nkv * cp;
+    if (nq * 2 < n_queues) return cp == 1;
+    return ((m.H + nq - 1) / nq) * o_slices <= 128;
+  };
+  int CP = 1;
+  for (int d = 1; d <= grp; ++d)
+    if (grp % d == 0 && (int64_t)m.nkv * d * 2 <= n_queues && o_fits(d)) {
+      CP = d;
+      if (cbytes / d <= 48 * 1024) break;
+    }
+  if (cbytes <= 48 * 1024 * 3 / 2) CP = 1;  // one batch round either way
+  s.combine_parts = CP;
+  auto comb_queue = [&](int g, int p) { return (g * S + S - 1 - p % S + n_queues) % n_queues; };
   std::vector<char> comb_q(n_queues, 0);
-  for (int g = 0; g < m.nkv; ++g) comb_q[(g * S + S - 1) % n_queues] = 1;
+  for (int g = 0; g < m.nkv; ++g)
+    for (int p = 0; p < CP; ++p) comb_q[comb_queue(g, p)] = 1;
   std::vector<int> o_queues;
   for (int q = 0; q < n_queues; ++q)
     if (!comb_q[q]) o_queues.push_back(q);
@@ -126,7 +149,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   for (int l = 0; l < L; ++l) {
     s.c_qkv.push_back(add_counter(n_qkv, PMK_OP_QKV, l));
     for (int g = 0; g < m.nkv; ++g) s.c_attn.push_back(add_counter(S, PMK_OP_ATTN, l));
-    s.c_cmb.push_back(add_counter(m.nkv, PMK_OP_COMBINE, l));
+    s.c_cmb.push_back(add_counter(m.nkv * CP, PMK_OP_COMBINE, l));
     s.c_oproj.push_back(add_counter(n_o, PMK_OP_OPROJ, l));
     s.c_gu.push_back(add_counter(n_gu, PMK_OP_GATEUP, l));
     s.c_down.push_back(add_counter(n_down, PMK_OP_DOWN, l));
@@ -168,13 +191,18 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
       const int g = i / S, j = i % S;
       push(i % n_queues, pmk_task{PMK_OP_ATTN, l, g, j, s.c_qkv[l], n_qkv, 0, s.c_attn[l * m.nkv + g], j});
     }
+    // COMBINE(g, p) merges q heads [j0, j1) of the group, encoded a1 = j0 | j1 << 8
     for (int g = 0; g < m.nkv; ++g)
-      push((g * S + S - 1) % n_queues,
-           pmk_task{PMK_OP_COMBINE, l, g, 0, s.c_attn[l * m.nkv + g], S, 0, s.c_cmb[l], g});
+      for (int p = 0; p < CP; ++p) {
+        int j0, j1;
+        split_range(grp, CP, p, &j0, &j1);
+        push(comb_queue(g, p), pmk_task{PMK_OP_COMBINE, l, g, j0 | (j1 << 8), s.c_attn[l * m.nkv + g], S, 0,
+                                        s.c_cmb[l], g * CP + p});
+      }
     for (int i = 0; i < n_o; ++i) {
       int lo, hi;
       split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi, &o_queues);
-      push(o_queues[i], pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv, 0, s.c_oproj[l], i});
+      push(o_queues[i], pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv * CP, 0, s.c_oproj[l], i});
     }
     for (int i = 0; i < n_gu; ++i) {
       int lo, hi;
@@ -291,11 +319,11 @@ void task_accesses(const Schedule& s, const pmk_task& t, int e, std::vector<Acce
       break;
     }
     case PMK_OP_COMBINE: {
-      const int g = t.a0, grp = m.grp();
+      const int g = t.a0, grp = m.grp(), j0 = t.a1 & 255, j1 = t.a1 >> 8;
       const int64_t part = ((int64_t)l * m.nkv + g) * s.attn_splits;
       acc.push_back({B_PART, part, part + s.attn_splits, A_READ, W1});
-      acc.push_back({B_O, (int64_t)l * m.qdim() + (int64_t)g * grp * m.hd,
-                     (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_WRITE, W1});
+      acc.push_back({B_O, (int64_t)l * m.qdim() + ((int64_t)g * grp + j0) * m.hd,
+                     (int64_t)l * m.qdim() + ((int64_t)g * grp + j1) * m.hd, A_WRITE, W1});
       break;
     }
     case PMK_OP_OPROJ:
@@ -377,8 +405,9 @@ std::string validate_schedule(const Schedule& s) {
       if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 < 0 || k.a1 >= S)
         return fmt("integrity: ATTN task %ld has kv head %ld / split %ld out of range", t, k.a0, k.a1);
     } else if (k.op == PMK_OP_COMBINE) {
-      if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 != 0)
-        return fmt("integrity: COMBINE task %ld has kv head %ld out of range", t, k.a0);
+      const int j0 = k.a1 & 255, j1 = k.a1 >> 8;
+      if (k.a0 < 0 || k.a0 >= m.nkv || k.a1 < 0 || j1 > m.grp() || j0 >= j1)
+        return fmt("integrity: COMBINE task %ld has kv head %ld / head range [%ld,%ld) out of range", t, k.a0, j0, j1);
     } else if (lim) {
       if (k.a0 < 0 || k.a1 > lim || k.a0 >= k.a1) return fmt("integrity: task %ld row range [%ld,%ld) invalid", t, k.a0, k.a1);
       if ((k.op == PMK_OP_QKV || k.op == PMK_OP_GATEUP) && ((k.a0 | k.a1) & 1))

@@ -88,6 +88,29 @@ def test_real_lowerings_are_accepted(name, n_cus, kw):
     assert st == 0, msg
 
 
+# 128 splits x 4 heads x (64 + 4) fp32 partials per kv head: 136 KiB for one combine, so the
+# builder splits each head group over 4 combines (one q head each)
+SPLIT_COMBINE = WORKLOADS["tiny"].with_(name="tiny_split_combine", n_q=8, n_kv=2, prompt=2016, steps=32)
+
+
+@pytest.mark.parametrize("name,n_cus,want", [("tiny_split_combine", 256, 4), ("2b", 256, 5), ("8b", 256, 1),
+                                             ("8b_fp8", 256, 1), ("1b", 256, 1)])
+def test_combines_per_kv_head(name, n_cus, want):
+    """Several COMBINE tasks per kv head, each over a range of its q heads, when one would read too
+    many partials (and the O-projection tiles still fit); together they cover every head once."""
+    w = SPLIT_COMBINE if name == "tiny_split_combine" else WORKLOADS[name]
+    s = Sched(w, n_cus)
+    comb = [s.task(i) for i in range(s.n_tasks) if s.task(i).op == 8 and s.task(i).layer == 0]
+    grp = w.n_q // w.n_kv
+    for g in range(w.n_kv):
+        ranges = sorted((t.a1 & 255, t.a1 >> 8) for t in comb if t.a0 == g)
+        assert len(ranges) == want
+        assert ranges[0][0] == 0 and ranges[-1][1] == grp
+        assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
+    st, msg = s.validate()
+    assert st == 0, msg
+
+
 @pytest.mark.parametrize("max_seq,want_s", [(512, 1), (513, 2), (1024, 2), (1100, 3)])
 def test_split_count_keeps_chunks_within_two_groups_per_wave(max_seq, want_s):
     """An attention task holds at most 512 positions (8 waves x two 32-position groups): asking for
@@ -185,11 +208,12 @@ def mutants(w, n_cus, rng, per_kind):
         elif t.op == 2 and peers:   # ATTN: another task's (kv head, split)
             p = tasks[rng.choice(peers)]
             t.a0, t.a1 = p.a0, p.a1
-        elif t.op == 8:             # COMBINE: another head's combine, or an invalid field
+        elif t.op == 8:             # COMBINE: another combine's (kv head, head range), or an invalid one
             if peers:
-                t.a0 = tasks[rng.choice(peers)].a0
+                p = tasks[rng.choice(peers)]
+                t.a0, t.a1 = p.a0, p.a1
             else:
-                t.a1 = 1
+                t.a1 = 1            # head range [1, 0): empty
         else:
             t.a1 = t.a0
         s.set_task(i, t)
@@ -231,8 +255,9 @@ def mutants(w, n_cus, rng, per_kind):
 def test_mutation_corpus_has_no_false_accepts():
     rng = random.Random(20260609)
     total, by_kind, accepted = 0, {}, []
-    for name, n_cus, per_kind in (("tiny", 4, 40), ("tiny", 8, 40), ("tiny", 32, 20), ("1b", 16, 10)):
-        w = WORKLOADS[name]
+    for name, n_cus, per_kind in (("tiny", 4, 40), ("tiny", 8, 40), ("tiny", 32, 20), ("1b", 16, 10),
+                                  ("tiny_split_combine", 256, 10)):
+        w = SPLIT_COMBINE if name == "tiny_split_combine" else WORKLOADS[name]
         for kind, mutate in mutants(w, n_cus, rng, per_kind):
             s = Sched(w, n_cus)
             mutate(s)
