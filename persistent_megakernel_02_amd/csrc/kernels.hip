@@ -928,15 +928,16 @@ __device__ __forceinline__ u32x4 fp8x8_bf16(u32x2 w) {
   return u32x4{hi16(f0), hi16(f1), hi16(f2), hi16(f3)};
 }
 
-// KV cache element loads through a buffer resource (out of range: zeros): 8 elements per lane;
-// past rows are streamed (nontemporal), the current position coherently.
-template <int KVDT, bool COHERENT>
+// KV cache element loads through a buffer resource (out of range: zeros): 8 elements per lane as
+// 16-bit matrix-core operands, streamed (nontemporal).  Every position read this way was written
+// in an earlier step; the current one comes from its tagged copy.
+template <int KVDT>
 __device__ __forceinline__ u32x4 kv_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (KVDT == WFP8) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, COHERENT ? 16 : 2);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
     return fp8x8_bf16(w);
   } else {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, COHERENT ? 16 : 2);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
   }
 }
 
@@ -953,18 +954,19 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // workspace, and the group's COMBINE task merges the splits into o.
 // Partial record per (split, head): m, l, two pad words, acc[hd] (hd + 4 floats).
 // On the matrix cores: the split is cut into 32-position groups (chunks are whole groups, at most
-// 16) and each wave takes one or two of them.  Scores are two 16 x 16 products per 32-dim slice, K rows (A, from
-// the [pos][hd] cache) times q (B, heads as columns); the A rows are the positions in the order
-// p0 + 8 (r / 4) + r % 4 (block 0) and + 4 (block 1), so that lane l ends up holding the scores of
-// positions p0 + 8 (l / 16) .. + 8 of head l % 16, which is exactly its B operand of P.V.  P.V is
-// V^T (A: 8 positions of one dim per lane) times P, one 16 x 16 product
-// per 16 dims (V is stored in blocks of 32 positions, [pos / 32][hd][pos % 32], so one wave
-// instruction reads 1 KiB of contiguous cache).  q and P enter as 16-bit hi + lo pairs (two products each), so the result keeps
-// about fp32 precision.  K/V rows are loaded from the cache before the dependency wait; the
-// current position (written this step) comes from its tagged copy, which wave 0 stages with q.  The wave's softmax (max and sum
-// across the four lanes of a head column with column_max / column_sum) runs on the 8 scores a
-// lane holds; the eight waves' (max, sum, acc) are then merged in LDS with the usual rescaling,
-// exactly as the splits are merged by the combine.
+// 16) and each wave takes one or two of them.  Scores are two 16 x 16 products per 32-dim slice,
+// K rows (A, from the [pos][hd] cache) times q (B, heads as columns); the A rows are the positions
+// in the order p0 + 8 (r / 4) + r % 4 (block 0) and + 4 (block 1), so that lane l ends up holding
+// the scores of positions p0 + 8 (l / 16) .. + 8 of head l % 16, which is exactly its B operand of
+// P.V.  P.V is V^T (A: 8 positions of one dim per lane) times P, one 16 x 16 product per 16 dims
+// (V is stored in blocks of 32 positions, [pos / 32][hd][pos % 32], so one wave instruction reads
+// 1 KiB of contiguous cache).  q and P enter as 16-bit hi + lo pairs (two products each), so the
+// result keeps about fp32 precision.  K/V rows are loaded from the cache before the dependency
+// wait; the current position (written this step) comes from its tagged copy, which wave 0 stages
+// with q.  The wave's softmax (max and sum across the four lanes of a head column with
+// column_max / column_sum) runs on the 8 scores a lane holds; the eight waves' (max, sum, acc)
+// are then merged in LDS with the usual rescaling, exactly as the splits are merged by the
+// combine.
 template <int WDT, int KVDT, int HD, int NGW, bool G2LDS = false>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
@@ -1017,14 +1019,14 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     const int pk0 = pk_of(k);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      ka[c] = kv_load8<KVDT, false>(kr, koff(pk0, c));
-      kb[c] = kv_load8<KVDT, false>(kr, koff(pk0 + 4, c));
+      ka[c] = kv_load8<KVDT>(kr, koff(pk0, c));
+      kb[c] = kv_load8<KVDT>(kr, koff(pk0 + 4, c));
     }
   };
   auto load_v = [&](int k) {
     const int pv = pv_of(k);
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, false>(vr, voff(pv, tt));
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT>(vr, voff(pv, tt));
   };
   auto patch_k = [&](int k) {
     const int pk0 = pk_of(k);
