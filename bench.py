@@ -5,7 +5,8 @@ One bench step = one decode token: the whole hot path (RMSNorm, QKV/O/gate-up/do
 KV append, split-KV GQA attention, LM head, greedy argmax) for every layer.  After a real GPU
 prefill of the workload's random prompt (untimed), W warm-up steps run, the position is rewound,
 and exactly K steps are timed as ONE persistent-kernel launch, bracketed by device syncs and HIP
-events on the launch stream.
+events on the launch stream; this is repeated (default 3 launches, rewinding to the same
+position) and the median launch gives the value.
 
 Prints one JSON line: tokens/s, ms per token, the HBM roofline block of the persistent kernel
 (algorithmic weight + KV bytes per launch over its duration), the oracle's CPU baseline on a
@@ -67,7 +68,8 @@ def main():
     ap.add_argument("--no-tune", dest="tune", action="store_false",
                     help="keep the even GEMV row split (default: pmk_tune re-splits the gate/up rows by the streaming "
                          "rate each CU measured in a traced warm-up, before the timed launch)")
-    ap.add_argument("--repeat", type=int, default=1, help="extra timed launches reported as a spread")
+    ap.add_argument("--repeat", type=int, default=3,
+                    help="timed launches of K steps each (from the same position); value is the median one")
     ap.add_argument("--kernel-only", action="store_true",
                     help="profiling: start from synthetic KV instead of a prefill and skip every leg but the timed launches")
     ap.add_argument("--copy-calib", action="store_true",
@@ -161,7 +163,7 @@ def main():
         if err.code:
             raise RuntimeError(f"device error {err.code} (cu {err.cu} task {err.task})")
         dec.rewind(P, first_tok)
-    elapsed = times[0]
+    elapsed = sorted(times)[len(times) // 2]  # the median launch
     ms_per_step = elapsed * 1e3 / K
     tokens_per_s = K / elapsed
     bytes_launch = sum(w.weight_bytes() + w.kv_bytes_read(i) for i in range(K))
