@@ -4,8 +4,8 @@
  * The library runs single-stream (batch 1) greedy decode of a dense Llama-style decoder as
  * ONE persistent, CU-resident kernel per decode call: every CU executes a static queue of
  * tasks (GEMV tiles, attention splits, LM-head tiles) that the host lowers from the model
- * into a task DAG synchronised by monotonic counters or epoch flags, after a static
- * validator has proved the schedule deadlock- and race-free.
+ * into a task DAG synchronised by step-tagged data and epoch flags (or monotonic counters),
+ * after a static validator has proved the schedule deadlock- and race-free.
  *
  * Sources of the design (pages, by title and section):
  *  - "AutoMegaKernel: A Statically-Checked Agent Harness for Self-Retargeting Megakernel
@@ -71,8 +71,12 @@ typedef enum {
 } pmk_mode;
 
 typedef enum {
-  PMK_SYNC_FLAGS = 0,   /* each producer stores its epoch into its own flag word; waiters poll them */
-  PMK_SYNC_COUNTERS = 1 /* producers add 1 to a shared monotonic counter; waiters poll it */
+  PMK_SYNC_FLAGS = 0,   /* whole-vector joins (the residual stream, q and the step's K/V row, the
+                           attention output) carry a step tag in every value and the consumers
+                           poll the data; the other joins (attention splits, gate/up, LM head)
+                           give each producer an epoch flag word that waiters poll */
+  PMK_SYNC_COUNTERS = 1 /* every join: producers add 1 to a shared monotonic counter; waiters poll
+                           it (the tagged data is then read once) */
 } pmk_sync_mode;
 
 /* The operation contract.  Supported: no biases, untied embeddings, head_dim in {64, 128},

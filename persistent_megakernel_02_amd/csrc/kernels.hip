@@ -45,10 +45,6 @@ __device__ __forceinline__ uint32_t ldc(const uint32_t* p) {
 __device__ __forceinline__ unsigned long long ldc(const unsigned long long* p) {
   return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float2 ldc2(const float* p) {  // 8-byte aligned pair
-  unsigned long long u = ldc(reinterpret_cast<const unsigned long long*>(p));
-  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-}
 __device__ __forceinline__ void stc(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -89,10 +85,6 @@ __device__ __forceinline__ float4 as_f4(u32x4 v) {
   return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 
-__device__ __forceinline__ u32x4 ld_nt(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
 // ------------------------------------------------------------------------------------------------
 // reductions
 // ------------------------------------------------------------------------------------------------
@@ -113,20 +105,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Max over the 64 lanes with the same DPP row pattern as wave_sum; every lane receives it.
+// One DPP max step: a lane's value against the lane the DPP control CTRL selects (rows ROWS).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_max(float a) {
   const int x = __float_as_int(a);
   return fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xF, false)));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_max<0x140, 0xF>(v);  // row_mirror
-  v = dpp_max<0x142, 0xA>(v);  // row_bcast15 -> rows 1,3
-  v = dpp_max<0x143, 0xC>(v);  // row_bcast31 -> rows 2,3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -682,7 +665,6 @@ __device__ __forceinline__ bool polls_tags(const KParams& P, const StepCtx& sc) 
   return !sc.per_op && P.sync_mode != PMK_SYNC_COUNTERS;
 }
 
-
 // An O projection tile that fits the LDS tile area is copied there whole (LDS-DMA) before the
 // task's dependency wait, instead of the register ring's first units: the wait for the attention
 // combine is long enough for all of it to land, and the GEMV then runs from LDS.
@@ -834,11 +816,6 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     stc(cur + i + half, tagged(__uint_as_float(bb), sc.e));
   }
   if (!polls_tags(P, sc)) block_signal(P, t.signal_ctr, t.signal_slot, sc.e);
-}
-
-__device__ __forceinline__ u32x4 ldc16B(const uint8_t* p) {
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-  return u32x4{ldc(q), ldc(q + 1), ldc(q + 2), ldc(q + 3)};
 }
 
 // Max / sum over the four lanes of a quad (quad_perm DPP); every lane of the quad receives it.
