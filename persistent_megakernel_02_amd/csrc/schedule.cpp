@@ -12,6 +12,7 @@
 #include "pmk_limits.h"
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <chrono>
 #include <cstring>
@@ -118,30 +119,46 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
   const int64_t o_slices = ((int64_t)m.qdim() / epl + 63) / 64;
   const int64_t cbytes = (int64_t)S * grp * (m.hd + 4) * 4;
+  // O-projection tile rows (in 1 KiB units) that fit the LDS tile area
+  constexpr int64_t kOTileUnits = 136;
+  // the largest O tile when the combine queues take no O rows (excl) or half a share each
+  auto o_units = [&](int cp, bool half_on_comb) {
+    const int64_t nc = (int64_t)m.nkv * cp, no = n_queues - nc;
+    const double shares = half_on_comb ? no + 0.5 * nc : (double)no;
+    return (int64_t)std::ceil(m.H / shares + 1e-9) * o_slices;
+  };
   auto o_fits = [&](int cp) {
-    const int64_t nq = n_queues - (int64_t)m.nkv * cp;
-    if (nq * 2 < n_queues) return cp == 1;
-    return ((m.H + nq - 1) / nq) * o_slices <= 128;
+    if ((int64_t)m.nkv * cp * 2 > n_queues) return cp == 1;
+    return cp == 1 || o_units(cp, false) <= kOTileUnits || o_units(cp, true) <= kOTileUnits;
   };
   int CP = 1;
   for (int d = 1; d <= grp; ++d)
-    if (grp % d == 0 && (int64_t)m.nkv * d * 2 <= n_queues && o_fits(d)) {
+    if (grp % d == 0 && o_fits(d)) {
       CP = d;
       if (cbytes / d <= 48 * 1024) break;
     }
   s.combine_parts = CP;
+  // with several combines per head group and O tiles that would not fit the queues left, the
+  // combine queues keep half an O-projection share each (a short tile, copied after the combine)
+  const bool o_on_comb = CP > 1 && o_units(CP, false) > kOTileUnits;
   auto comb_queue = [&](int g, int p) { return (g * S + S - 1 - p % S + n_queues) % n_queues; };
   std::vector<char> comb_q(n_queues, 0);
   for (int g = 0; g < m.nkv; ++g)
     for (int p = 0; p < CP; ++p) comb_q[comb_queue(g, p)] = 1;
   std::vector<int> o_queues;
   for (int q = 0; q < n_queues; ++q)
-    if (!comb_q[q]) o_queues.push_back(q);
+    if (!comb_q[q] || o_on_comb) o_queues.push_back(q);
   if ((int)o_queues.size() * 2 < n_queues) {
     o_queues.clear();
     for (int q = 0; q < n_queues; ++q) o_queues.push_back(q);
   }
   const int n_o = std::min((int)o_queues.size(), m.H);
+  std::vector<int> o_bounds;  // row bounds of the O tiles when the combine queues take half shares
+  if (o_on_comb && n_o == (int)o_queues.size()) {
+    std::vector<double> w(n_o);
+    for (int i = 0; i < n_o; ++i) w[i] = comb_q[o_queues[i]] ? 0.5 : 1.0;
+    split_weighted(m.H, n_o, w, &o_bounds);
+  }
   const int n_gu = std::min(n_queues, m.F);
   const int n_down = std::min(n_queues, m.H);
   const int n_lm = std::min(n_queues, m.V);
@@ -200,7 +217,12 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
       }
     for (int i = 0; i < n_o; ++i) {
       int lo, hi;
-      split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi, &o_queues);
+      if (!o_bounds.empty()) {
+        lo = o_bounds[i];
+        hi = o_bounds[i + 1];
+      } else {
+        split_op(PMK_OP_OPROJ, m.H, n_o, i, &lo, &hi, &o_queues);
+      }
       push(o_queues[i], pmk_task{PMK_OP_OPROJ, l, lo, hi, s.c_cmb[l], m.nkv * CP, 0, s.c_oproj[l], i});
     }
     for (int i = 0; i < n_gu; ++i) {

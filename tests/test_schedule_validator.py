@@ -93,7 +93,7 @@ def test_real_lowerings_are_accepted(name, n_cus, kw):
 SPLIT_COMBINE = WORKLOADS["tiny"].with_(name="tiny_split_combine", n_q=8, n_kv=2, prompt=2016, steps=32)
 
 
-@pytest.mark.parametrize("name,n_cus,want", [("tiny_split_combine", 256, 4), ("2b", 256, 5), ("8b", 256, 1),
+@pytest.mark.parametrize("name,n_cus,want", [("tiny_split_combine", 256, 4), ("2b", 256, 5), ("8b", 256, 2),
                                              ("8b_fp8", 256, 2), ("1b", 256, 1)])
 def test_combines_per_kv_head(name, n_cus, want):
     """Several COMBINE tasks per kv head, each over a range of its q heads, when one would read too
