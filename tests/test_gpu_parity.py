@@ -123,6 +123,18 @@ def test_tiny_fp8_prefill_and_decode():
     check(w, run, ref, first_ok, "tiny_fp8")
 
 
+@pytest.mark.parametrize("mode_name", ["megakernel", "per_op"])
+def test_tiny_one_token_prompt_and_one_step(tiny, mode_name):
+    """The smallest call: a one-token prompt (one position in the cache, every split but the first
+    empty) and a single decode step."""
+    mode = dict(_modes())[mode_name]
+    w = TINY.with_(prompt=1, steps=1)
+    prompt = synthgen.make_prompt(w)
+    run = gpu_run(w, tiny, 1, mode=mode, prompt=prompt)
+    ref, first_ok = oracle_teacher_forced(w, tiny, run, prompt=prompt)
+    check(w, run, ref, first_ok, f"tiny/one token/{mode_name}")
+
+
 @pytest.mark.parametrize("wname", ["tiny", "tiny_fp8"])
 def test_long_split_two_groups_per_wave(wname):
     """One attention split over up to 332 positions (11 groups of 32 for eight waves): once the
