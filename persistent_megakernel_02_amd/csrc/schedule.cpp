@@ -111,7 +111,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   // COMBINE of kv head g runs on the queue of its last split (the shortest one), right after it;
   // the O projection then skips those queues when enough others remain, so a combine's latency
   // never delays an O-projection tile.  A combine reads every split's partial of its heads, one
-  // batch of loads per thread per 32 splits: when that is more than ~48 KiB for one CU, the
+  // batch of loads per thread per 32 splits: when that is more than ~33 KiB for one CU, the
   // head group is split over CP combines (a divisor of the group, each on the queue of one of the
   // last CP splits), as long as the O-projection tiles of the remaining queues still fit the LDS
   // tile area (~128 KiB).
@@ -135,7 +135,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   for (int d = 1; d <= grp; ++d)
     if (grp % d == 0 && o_fits(d)) {
       CP = d;
-      if (cbytes / d <= 48 * 1024) break;
+      if (cbytes / d <= 33 * 1024) break;
     }
   s.combine_parts = CP;
   // with several combines per head group and O tiles that would not fit the queues left, the

@@ -94,7 +94,7 @@ SPLIT_COMBINE = WORKLOADS["tiny"].with_(name="tiny_split_combine", n_q=8, n_kv=2
 
 
 @pytest.mark.parametrize("name,n_cus,want", [("tiny_split_combine", 256, 4), ("2b", 256, 5), ("8b", 256, 2),
-                                             ("8b_fp8", 256, 2), ("1b", 256, 1)])
+                                             ("8b_fp8", 256, 2), ("1b", 256, 2)])
 def test_combines_per_kv_head(name, n_cus, want):
     """Several COMBINE tasks per kv head, each over a range of its q heads, when one would read too
     many partials (and the O-projection tiles still fit); together they cover every head once."""
