@@ -89,8 +89,11 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   s.sync_mode = sc.sync_mode == PMK_SYNC_COUNTERS ? PMK_SYNC_COUNTERS : PMK_SYNC_FLAGS;
   int S = sc.attn_splits;
   if (S <= 0) {
+    // one split per queue and kv head, but at least two 32-position groups per split: shorter
+    // splits leave most of a task's waves idle and multiply the partials the combine reads
+    // (2B, 1280 positions: 64 splits of 20 positions 789 tok/s, 20 splits of 64 807)
     S = std::max(1, n_queues / m.nkv);
-    S = std::min(S, std::max(1, m.max_seq / 16));
+    S = std::min(S, std::max(1, m.max_seq / 64));
   }
   // each split's positions must fit the attention task (8 waves x 2 x 32): chunk = ceil(max_seq / S)
   // rounded up to whole 32-position blocks is bounded

@@ -157,14 +157,17 @@ def test_long_split_two_groups_per_wave(wname):
 
 
 def test_split_combines_match_oracle_and_modes():
-    """128 splits x 4 heads: each kv head's combine is split over 4 tasks (one q head each); from
+    """128 splits x 4 heads (requested): each kv head's combine is split over 4 tasks (one q head each); from
     synthetic KV of 2016 positions, megakernel, graph and per-op decode agree bitwise and match the
     oracle."""
+    import persistent_megakernel_02_amd as pmk
     w = TINY.with_(name="tiny_split_combine", n_q=8, n_kv=2, prompt=2016, steps=16)
     wts = synthgen.make_weights(w, gain_std=0.1)
     k, v, scales = synthgen.make_kv(w, w.prompt)
     nxt = int(synthgen.make_prompt(w, 1)[0])
-    runs = {name: gpu_run(w, wts, w.steps, mode=m, kv=(k, v, w.prompt), next_token=nxt) for name, m in _modes()}
+    sched = pmk.schedule_config(attn_splits=128)
+    runs = {name: gpu_run(w, wts, w.steps, mode=m, kv=(k, v, w.prompt), next_token=nxt, sched=sched)
+            for name, m in _modes()}
     ref, _ = oracle_teacher_forced(w, wts, runs["megakernel"], kv=(k, v, w.prompt))
     check(w, runs["megakernel"], ref, True, "tiny/split combines")
     for name, r in runs.items():
