@@ -358,14 +358,25 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + (int64_t)r0 * rb), (short)0, (int)((int64_t)R * rb), 0x00020000);
   constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;  // past any tile the validator accepts
+  // The issue cursor (row, slice) moves row by row; the row's byte offset in the tile and (fp8)
+  // its block-scale row are updated when the row changes, not recomputed per unit: the fp8 loops
+  // run close to the vector-ALU issue limit, and the per-unit index arithmetic was most of it.
   int lrow = wr0, lj = s0;
+  uint32_t roff = (uint32_t)((int64_t)(wr0 - r0) * rb);
+  const float* srp = nullptr;
+  if constexpr (WDT == WFP8) srp = srow(wr0);
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
     const bool ok = lrow < wr1 && c < nch;
-    const uint32_t off = ok ? (uint32_t)((int64_t)(lrow - r0) * rb + (int64_t)c * 16) : kOut;
+    const uint32_t off = ok ? roff + (uint32_t)c * 16u : kOut;
     ring[d] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nontemporal
-    if constexpr (WDT == WFP8) rsc[d] = srow(lrow < wr1 ? lrow : wr0)[(c < nch ? c : 0) >> 3];
-    if (++lj == s1) { lj = s0; ++lrow; }
+    if constexpr (WDT == WFP8) rsc[d] = srp[(c < nch ? c : 0) >> 3];
+    if (++lj == s1) {
+      lj = s0;
+      ++lrow;
+      roff += (uint32_t)rb;
+      if constexpr (WDT == WFP8) srp = srow(lrow < wr1 ? lrow : wr0);
+    }
   };
   // kPre units per lane are issued before the dependency wait (when prefetching), the rest of the
   // ring after it: loads leave a workgroup in issue order, so a deep pre-wait backlog would delay
