@@ -66,8 +66,9 @@ def main():
     ap.add_argument("--no-graph-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-tune", dest="tune", action="store_false",
-                    help="keep the even GEMV row split (default: pmk_tune re-splits the gate/up rows by the streaming "
-                         "rate each CU measured in a traced warm-up, before the timed launch)")
+                    help="keep the even GEMV row split (default: before the timed launch, pmk_tune twice re-splits the "
+                         "gate/up rows by the streaming rate each CU measured in traced warm-up steps and keeps a "
+                         "re-split only if those steps then run faster)")
     ap.add_argument("--repeat", type=int, default=3,
                     help="timed launches of K steps each (from the same position); value is the median one")
     ap.add_argument("--kernel-only", action="store_true",
@@ -141,12 +142,13 @@ def main():
         dec.decode(W, out_tokens=out_tokens, n_done=n_done)
         torch.cuda.synchronize()
         dec.rewind(P, first_tok)
+    tune_kept = 0
     if args.tune:
         t_tune = time.time()
         for _ in range(2):
-            dec.tune(trace_steps)
+            tune_kept += int(dec.tune(trace_steps))
         torch.cuda.synchronize()
-        log(f"[bench] tuned the GEMV row split in {time.time() - t_tune:.2f}s "
+        log(f"[bench] tuned the GEMV row split in {time.time() - t_tune:.2f}s: {tune_kept} of 2 re-splits kept "
             f"(schedule {dec.schedule_info().hash:#018x})")
     stream = torch.cuda.current_stream()
     times = []
@@ -240,7 +242,8 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "hidden": w.hidden, "heads": [w.n_q, w.n_kv],
                    "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "prompt": P, "decode_steps": K,
                    "batch": 1, "mode": args.mode, "sync": args.sync, "parallelism": "single GPU",
-                   "row_split": "tuned (gate/up)" if args.tune else "even"},
+                   "row_split": ("tuned (gate/up)" if tune_kept else "even (tuned split measured slower)")
+                   if args.tune else "even"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},

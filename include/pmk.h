@@ -233,12 +233,16 @@ pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
  * it) from the current position with the megakernel and tracing on, measures every queue's
  * gate/up weight-streaming rate from the trace, rebuilds the schedule with each gate/up task's
  * row share moved half-way from even toward proportional to its queue's rate (compute units of a
- * device do not stream at one rate: the split evens out when they finish the phase; the other
- * GEMV phases keep the even split), validates and installs it, then restores the position and next input token it started from (the KV rows it
- * wrote past that position are rewritten by the next decode).  Synchronous on `stream`.  Requires
- * bound weights and KV state and a context created with trace_steps >= 1.  Row assignment never
- * changes a row's arithmetic beyond the grouping of its partial sums. */
-pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, void* stream);
+ * device do not always stream at one rate: the split evens out when they finish the phase; the
+ * other GEMV phases keep the even split), validates and installs it, and runs the same steps from
+ * the same state again.  The new split is kept only if their mean traced step time is lower;
+ * otherwise the split in force before the call is reinstalled.  *kept (may be NULL) receives 1 if
+ * the new split was kept, else 0.  The position and next input token the call started from are
+ * restored (the KV rows it wrote past that position are rewritten by the next decode).
+ * Synchronous on `stream`.  Requires bound weights and KV state and a context created with
+ * trace_steps >= 1.  Row assignment never changes a row's arithmetic beyond the grouping of its
+ * partial sums. */
+pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, int32_t* kept, void* stream);
 
 /* Schedule inspection (host only, also for device-less contexts). */
 pmk_status pmk_schedule_get_info(const pmk_ctx* ctx, pmk_schedule_info* info);

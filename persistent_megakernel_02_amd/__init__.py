@@ -165,10 +165,13 @@ class Decoder:
         check(self.lib.pmk_trace_stats(self.ctx, ctypes.byref(a), ctypes.byref(b)), self.ctx)
         return a.value, b.value
 
-    def tune(self, steps: int = 0, stream=None):
-        """Measure each compute unit's streaming rate over `steps` traced decode steps and rebuild
-        the schedule with speed-proportional GEMV row shares (position and next token restored)."""
-        check(self.lib.pmk_tune(self.ctx, steps, _stream(stream)), self.ctx)
+    def tune(self, steps: int = 0, stream=None) -> bool:
+        """Measure each compute unit's gate/up streaming rate over `steps` traced decode steps,
+        rebuild the schedule with speed-weighted row shares and keep it only if the same steps then
+        run faster (position and next token restored).  Returns whether the new split was kept."""
+        kept = ctypes.c_int32(0)
+        check(self.lib.pmk_tune(self.ctx, steps, ctypes.byref(kept), _stream(stream)), self.ctx)
+        return bool(kept.value)
 
     def trace_export(self, path: str):
         check(self.lib.pmk_trace_export(self.ctx, path.encode()), self.ctx)

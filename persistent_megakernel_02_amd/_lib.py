@@ -87,7 +87,7 @@ SIGNATURES = {
     "pmk_get_position": (i32, [vp, ctypes.POINTER(i32)]),
     "pmk_poll_error": (i32, [vp, ctypes.POINTER(pmk_device_error)]),
     "pmk_set_trace": (i32, [vp, i32]),
-    "pmk_tune": (i32, [vp, i32, vp]),
+    "pmk_tune": (i32, [vp, i32, vp, vp]),
     "pmk_trace_export": (i32, [vp, ctypes.c_char_p]),
     "pmk_trace_stats": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "pmk_schedule_get_info": (i32, [vp, ctypes.POINTER(pmk_schedule_info)]),

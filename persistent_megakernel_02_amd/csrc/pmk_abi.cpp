@@ -742,16 +742,36 @@ static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
   return PMK_OK;
 }
 
-pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
+// Mean wall time of the traced steps [0, steps) in µs: per step, the first task start to the last
+// task end over all queues (timestamps in 10 ns ticks).
+static double traced_step_us(const pmk_ctx* c, const std::vector<unsigned long long>& t, int steps) {
+  const size_t NT = c->sched.tasks.size();
+  double sum = 0;
+  int n = 0;
+  for (int st = 0; st < steps; ++st) {
+    unsigned long long lo = ~0ull, hi = 0;
+    for (size_t i = 0; i < NT; ++i) {
+      const unsigned long long* r = &t[((size_t)st * NT + i) * 8];
+      if (!r[0] || !r[2] || r[2] < r[0]) continue;
+      lo = std::min(lo, r[0]);
+      hi = std::max(hi, r[2]);
+    }
+    if (hi > lo) { sum += (double)(hi - lo) * 0.01; ++n; }
+  }
+  return n ? sum / n : 0.0;
+}
+
+pmk_status pmk_tune(pmk_ctx* c, int32_t steps, int32_t* kept, void* stream) {
   pmk_status s = need_device(c);
   if (s != PMK_OK) return s;
+  if (kept) *kept = 0;
   if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
   if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "tuning reads the trace: create the context with trace_steps >= 1");
   if (steps <= 0 || steps > c->sc.trace_steps) steps = c->sc.trace_steps;
   if ((int64_t)c->pos_host + steps > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + steps exceeds max_seq");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(c, hipSetDevice(c->device));
-  // save the next input token and the position; run `steps` traced steps with the megakernel
+  // save the next input token and the position: every traced run below starts from them
   int32_t* saved = reinterpret_cast<int32_t*>(c->ws + c->w_ctrl + CTRL_SAVED * 4);
   HIPCHK(c, launch_copy_token(c->kp, saved, st));
   const int32_t pos0 = c->pos_host;
@@ -759,17 +779,27 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
   HIPCHK(c, hipStreamSynchronize(st));
   s = pmk_set_trace(c, 1);
   if (s != PMK_OK) return s;
-  CallParams cp{};
-  cp.n_steps = steps;
-  cp.eos = -1;
-  cp.trace = 1;
-  s = begin_call(c, cp, st);
-  if (s == PMK_OK) s = launch_persistent(c, st);
-  if (s != PMK_OK) return s;
-  c->pos_host += steps;
+  // `steps` traced megakernel steps from (pos0, saved token), then back to them
+  auto traced_run = [&](std::vector<unsigned long long>& tr) -> pmk_status {
+    CallParams cp{};
+    cp.n_steps = steps;
+    cp.eos = -1;
+    cp.trace = 1;
+    pmk_status s2 = begin_call(c, cp, st);
+    if (s2 == PMK_OK) s2 = launch_persistent(c, st);
+    if (s2 != PMK_OK) return s2;
+    c->pos_host += steps;
+    s2 = read_trace(c, tr);
+    if (s2 != PMK_OK) return s2;
+    HIPCHK(c, launch_set_pos(c->kp, pos0, saved, st));
+    HIPCHK(c, hipStreamSynchronize(st));
+    c->pos_host = pos0;
+    return PMK_OK;
+  };
   std::vector<unsigned long long> t;
-  s = read_trace(c, t);
+  s = traced_run(t);
   if (s != PMK_OK) return s;
+  const double before_us = traced_step_us(c, t, steps);
   // streamed bytes and streaming time (staged -> GEMV done) per GEMV op and queue
   const size_t NT = c->sched.tasks.size();
   const int NQ = c->sched.n_queues;
@@ -794,8 +824,8 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
     }
   RowWeights rw;
   // only phases whose tiles are several times the prefetch give a usable rate
-  // gate/up only: its per-queue rates differ reproducibly (by XCD on the boxes measured); the
-  // other phases measured flat, and re-splitting them only adds noise
+  // gate/up only: its per-queue rates can differ reproducibly (by XCD on some boxes); the other
+  // phases measured flat, and re-splitting them only adds noise
   for (int op : {PMK_OP_GATEUP}) {
     std::vector<double> w(NQ, 0.0);
     double mean = 0;
@@ -810,17 +840,28 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, void* stream) {
     for (double& x : w) x = std::min(std::max(1.0 + 0.5 * (x / mean - 1.0), 0.5), 2.0);
     rw.w[op] = w;
   }
-  // restore the position and the next input token
-  HIPCHK(c, launch_set_pos(c->kp, pos0, saved, st));
-  HIPCHK(c, hipStreamSynchronize(st));
-  c->pos_host = pos0;
-  c->trace_on = trace_prev;
   Schedule ns;
-  const std::string e = build_schedule(c->m, c->sc, NQ, &ns, &rw);
+  std::string e = build_schedule(c->m, c->sc, NQ, &ns, &rw);
   if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
   s = install_schedule(c, std::move(ns));
   if (s != PMK_OK) return s;
-  c->rw = rw;
+  // keep the new split only if the same steps from the same state now run faster: when the
+  // rates are flat, the measured differences are noise and a re-split only adds imbalance
+  std::vector<unsigned long long> t2;
+  s = traced_run(t2);
+  if (s != PMK_OK) return s;
+  const double after_us = traced_step_us(c, t2, steps);
+  if (after_us > 0 && after_us < before_us) {
+    c->rw = rw;
+    if (kept) *kept = 1;
+  } else {
+    Schedule ps;
+    e = build_schedule(c->m, c->sc, NQ, &ps, &c->rw);  // the split in force before this call
+    if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
+    s = install_schedule(c, std::move(ps));
+    if (s != PMK_OK) return s;
+  }
+  c->trace_on = trace_prev;
   return PMK_OK;
 }
 

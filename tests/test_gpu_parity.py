@@ -65,8 +65,9 @@ def test_modes_agree_bitwise_and_chunking(tiny):
 
 @pytest.mark.parametrize("name", ["tiny", "1b"])
 def test_tuned_schedule_keeps_parity(name, tiny):
-    """pmk_tune re-splits the GEMV rows by measured speed and restores the position and next token:
-    decoding afterwards still matches the oracle, and the modes still agree bitwise."""
+    """pmk_tune re-splits the GEMV rows by measured speed, keeps the split only if it runs faster and
+    restores the position and next token: decoding afterwards still matches the oracle, and the
+    modes still agree bitwise."""
     import torch
     import persistent_megakernel_02_amd as pmk
     w = synthgen.WORKLOADS[name]
@@ -79,8 +80,16 @@ def test_tuned_schedule_keeps_parity(name, tiny):
     pos = dec.position()
     log(f"{name}: tune at position {pos}")
     h0 = dec.schedule_info().hash
-    dec.tune(4)
-    dec.tune(4)
+    k1 = dec.tune(4)
+    h1 = dec.schedule_info().hash
+    k2 = dec.tune(4)
+    h2 = dec.schedule_info().hash
+    # a re-split that did not run faster is undone: the schedule in force before comes back
+    if not k1:
+        assert h1 == h0
+    if not k2:
+        assert h2 == h1
+    log(f"{name}: re-splits kept {k1}, {k2}")
     assert dec.position() == pos
     assert dec.poll_error().code == 0
     log(f"{name}: schedule hash {h0:#x} -> {dec.schedule_info().hash:#x}")
