@@ -686,6 +686,11 @@ __device__ __forceinline__ bool oproj_tile_in_lds(const KParams& P, const pmk_ta
 // O-projection tiles are short (a few rows per CU): the split weighs each row's reduction like
 // four units, the same in every mode, so the LDS path and the streaming path agree bitwise
 constexpr int kOprojRowCost = 4;
+// LM-head tiles are long (~500 rows per CU on a 128K vocabulary) and short-rowed (4 or 8 slices):
+// with no row cost the split gave every wave one slice of every row, so each unit ended in a
+// wave-wide reduction, which made the fp8 head vector-ALU bound (~20 GB/s per CU against ~28 for
+// the other phases).  Weighing a row end like one unit keeps whole rows in one wave.
+constexpr int kLmheadRowCost = 1;
 
 __device__ __forceinline__ int key_token(unsigned long long key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
@@ -1473,7 +1478,7 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
   const int nbc = (H + 127) / 128;
   const float* const sl = P.sc_lm;
   auto srow = [=](int r) -> const float* { return sl + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
+  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow, kLmheadRowCost);
   mark(P, sc, ti, 5);
   const float rn = rms_factor(red, H, P.eps);
   unsigned long long key = 0ull;
