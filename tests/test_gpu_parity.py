@@ -39,6 +39,24 @@ def test_tiny_full_prefill_and_decode(tiny, mode_name):
     check(TINY, run, ref, first_ok, f"tiny/{mode_name}")
 
 
+def test_tiny_varied_token_stream():
+    """At N(0, 0.02) weights the tiny model's greedy stream repeats one token; at N(0, 0.1) (gains
+    1 + N(0, 0.1)) it changes at nearly every step, with wide top-2 gaps, so the emitted tokens
+    themselves are compared with the oracle's, in every mode, along with the logits."""
+    w = TINY.with_(steps=32)
+    wts = synthgen.make_weights(w, std=0.1, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    runs = {name: gpu_run(w, wts, w.steps, mode=m, prompt=prompt) for name, m in _modes()}
+    base = runs["megakernel"]
+    ref, first_ok = oracle_teacher_forced(w, wts, base, prompt=prompt)
+    check(w, base, ref, first_ok, "tiny/varied stream")
+    toks = [base.first] + [int(t) for t in base.tokens]
+    assert len(set(toks)) > len(toks) // 2, toks
+    for name, r in runs.items():
+        assert np.array_equal(r.tokens, base.tokens), name
+        assert np.array_equal(r.logits, base.logits), name
+
+
 def test_tiny_counter_sync_mode(tiny):
     import persistent_megakernel_02_amd as pmk
     prompt = synthgen.make_prompt(TINY)
