@@ -150,6 +150,25 @@ def test_tiny_fp8_prefill_and_decode():
     check(w, run, ref, first_ok, "tiny_fp8")
 
 
+def test_tiny_fp8_varied_token_stream():
+    """The FP8 path (block-scaled weights, FP8 KV at a fixed scale given to both sides) with
+    weights ~N(0, 0.05): 32 distinct tokens in 33, tokens and logits against the oracle, and the
+    modes bitwise equal."""
+    w = TINY_FP8.with_(steps=32)
+    wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32)
+    runs = {name: gpu_run(w, wts, w.steps, mode=m, prompt=prompt, kv_scales=scales) for name, m in _modes()}
+    base = runs["megakernel"]
+    ref, first_ok = oracle_teacher_forced(w, wts, base, prompt=prompt, kv_scales=scales)
+    check(w, base, ref, first_ok, "tiny_fp8/varied stream")
+    toks = [base.first] + [int(t) for t in base.tokens]
+    assert len(set(toks)) > len(toks) // 2, toks
+    for name, r in runs.items():
+        assert np.array_equal(r.tokens, base.tokens), name
+        assert np.array_equal(r.logits, base.logits), name
+
+
 @pytest.mark.parametrize("mode_name", ["megakernel", "per_op"])
 def test_tiny_one_token_prompt_and_one_step(tiny, mode_name):
     """The smallest call: a one-token prompt (one position in the cache, every split but the first
