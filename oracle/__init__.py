@@ -75,7 +75,12 @@ def lib():
         L.orc_read_kv.argtypes = [vp, vp, vp, i32]
         L.orc_prefill.argtypes = [vp, vp, i32, i32, vp]
         L.orc_step.argtypes = [vp, i32, vp]
+        L.orc_step_forced.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.orc_num_threads.argtypes = []
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_kv_amax.argtypes = [vp, vp]
+        L.orc_reset_kv_amax.argtypes = [vp]
+        L.orc_kv_scales_from_amax.argtypes = [vp, vp]
         _lib = L
     return _lib
 
@@ -147,6 +152,11 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on."""
+    lib().orc_set_threads(int(n))
+
+
 def argmax(v: np.ndarray) -> int:
     v = np.ascontiguousarray(v, np.float32)
     return lib().orc_argmax(_p(v), v.size)
@@ -207,6 +217,22 @@ class OracleModel:
         assert s.shape == (self.w.layers, self.w.n_kv, 2)
         lib().orc_set_kv_scales(self.h, _p(s))
 
+    def kv_amax(self) -> np.ndarray:
+        """Largest |k| (after RoPE) and |v| per (layer, kv head) appended since the last reset,
+        before rounding to the cache format: [layers][n_kv][2]."""
+        out = np.empty((self.w.layers, self.w.n_kv, 2), np.float32)
+        lib().orc_kv_amax(self.h, _p(out))
+        return out
+
+    def reset_kv_amax(self):
+        lib().orc_reset_kv_amax(self.h)
+
+    def kv_scales_from_amax(self) -> np.ndarray:
+        """Static FP8 KV scales from kv_amax(): amax / 448 in fp32, 1 where amax is 0."""
+        out = np.empty((self.w.layers, self.w.n_kv, 2), np.float32)
+        lib().orc_kv_scales_from_amax(self.h, _p(out))
+        return out
+
     def load_kv(self, k: np.ndarray, v: np.ndarray, P: int):
         k = np.ascontiguousarray(k)
         v = np.ascontiguousarray(v)
@@ -228,6 +254,23 @@ class OracleModel:
         if tok < 0:
             raise RuntimeError(f"oracle prefill failed ({tok})")
         return tok, lg
+
+    def step_forced(self, tok: int, k_row: np.ndarray, v_row: np.ndarray):
+        """One step that appends the given KV row (cache-format codes [layers][n_kv][head_dim]) instead
+        of its own rounding of k and v, as a teacher-forced step takes a given token.  Returns
+        (next token, logits, own k row, own v row): the codes this step itself would have appended."""
+        w = self.w
+        k_row = np.ascontiguousarray(k_row)
+        v_row = np.ascontiguousarray(v_row)
+        assert k_row.shape == (w.layers, w.n_kv, w.head_dim) and v_row.shape == k_row.shape
+        own_k, own_v = np.empty_like(k_row), np.empty_like(v_row)
+        lg = np.empty(w.vocab, np.float32)
+        nxt = lib().orc_step_forced(self.h, int(tok), _p(k_row), _p(v_row), _p(own_k), _p(own_v), _p(lg))
+        if nxt == -2:
+            raise RuntimeError("oracle KV capacity exceeded")
+        if nxt < 0:
+            raise RuntimeError("oracle logits contain NaN")
+        return nxt, lg, own_k, own_v
 
     def step(self, tok: int, want_logits: bool = True):
         lg = np.empty(self.w.vocab, np.float32) if want_logits else None

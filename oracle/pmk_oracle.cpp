@@ -17,6 +17,7 @@
 //   x += Wd (silu(Wg xn) * (Wu xn)); finally logits = Wlm rmsnorm(x, gf), token = argmax
 //   with the lowest index winning ties.
 // Every function is pinned by the oracle tests (closed forms, invariants, brute force).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -98,10 +99,24 @@ uint8_t enc_e4m3(float f) {
   return sign | (uint8_t)(code > 0x7e ? 0x7e : code);
 }
 
+// Every binary16 and E4M3 code decoded once by the definitions above: whole-model runs decode
+// billions of weights, and a table look-up returns the same value as the definition.
+struct DecodeTables {
+  std::vector<float> f16, e4m3;
+  DecodeTables() : f16(65536), e4m3(256) {
+    for (uint32_t c = 0; c < 65536; ++c) f16[c] = dec_f16((uint16_t)c);
+    for (uint32_t c = 0; c < 256; ++c) e4m3[c] = dec_e4m3((uint8_t)c);
+  }
+};
+const DecodeTables& tables() {
+  static const DecodeTables t;
+  return t;
+}
+
 inline float dec(int fmt, const void* p, size_t i) {
-  if (fmt == F16) return dec_f16(((const uint16_t*)p)[i]);
+  if (fmt == F16) return tables().f16[((const uint16_t*)p)[i]];
   if (fmt == BF16) return dec_bf16(((const uint16_t*)p)[i]);
-  return dec_e4m3(((const uint8_t*)p)[i]);
+  return tables().e4m3[((const uint8_t*)p)[i]];
 }
 
 inline size_t fmt_size(int fmt) { return fmt == E4M3 ? 1 : 2; }
@@ -136,6 +151,12 @@ void matmul_tokens(int fmt, const void* W, const float* S, int rows, int cols, c
 #pragma omp for schedule(static)
     for (int n = 0; n < rows; ++n) {
       for (int k = 0; k < cols; ++k) wrow[k] = weight(fmt, W, S, cols, n, k);
+      if (B == 1) {  // one token (decode): the same sum, in a register
+        float a = 0.f;
+        for (int k = 0; k < cols; ++k) a = a + wrow[k] * X[k];
+        Y[n] = a;
+        continue;
+      }
       for (int t = 0; t < B; ++t) acc[t] = 0.f;
       for (int k = 0; k < cols; ++k) {
         const float w = wrow[k];
@@ -240,6 +261,7 @@ struct orc_model {
   std::vector<std::vector<float>> gains;  // per layer: attn_norm, ffn_norm as fp32
   std::vector<uint8_t> kcache, vcache;    // [L][nkv][max_seq][hd] in the cache format
   std::vector<float> kv_scale;            // [L][nkv][2]
+  std::vector<float> kv_amax;             // [L][nkv][2]: largest |k|, |v| appended since the last reset
   int pos;
 };
 
@@ -300,6 +322,7 @@ orc_model* orc_create(const orc_config* c, const orc_weights* w) {
   m->kcache.assign(kvn, 0);
   m->vcache.assign(kvn, 0);
   m->kv_scale.assign((size_t)c->L * c->nkv * 2, 1.0f);
+  m->kv_amax.assign((size_t)c->L * c->nkv * 2, 0.0f);
   m->pos = 0;
   return m;
 }
@@ -310,6 +333,20 @@ int orc_get_pos(const orc_model* m) { return m->pos; }
 
 void orc_set_kv_scales(orc_model* m, const float* s) {
   std::memcpy(m->kv_scale.data(), s, m->kv_scale.size() * sizeof(float));
+}
+
+// Largest |k| (after RoPE) and |v| per (layer, kv head) over the rows appended since the last reset,
+// before rounding to the cache format: out [L][nkv][2].
+void orc_kv_amax(const orc_model* m, float* out) {
+  std::memcpy(out, m->kv_amax.data(), m->kv_amax.size() * sizeof(float));
+}
+
+void orc_reset_kv_amax(orc_model* m) { std::fill(m->kv_amax.begin(), m->kv_amax.end(), 0.0f); }
+
+// Static FP8 KV scales from those maxima: the largest value maps to the largest E4M3 magnitude,
+// S = amax / 448 in fp32 (1 where nothing but zeros was appended).
+void orc_kv_scales_from_amax(const orc_model* m, float* out) {
+  for (size_t i = 0; i < m->kv_amax.size(); ++i) out[i] = m->kv_amax[i] > 0.0f ? m->kv_amax[i] / 448.0f : 1.0f;
 }
 
 static inline size_t kv_index(const orc_config& c, int l, int g, int p) {
@@ -347,7 +384,12 @@ int orc_read_kv(const orc_model* m, void* k, void* v, int P) {
 // Run B consecutive tokens at positions pos..pos+B-1 through the decoder (causal attention
 // over the cache).  logits (if not NULL) receives the logits of the LAST token.  Returns the
 // argmax of those logits when they are computed, else 0.
-static int forward_tokens(orc_model* m, const int32_t* toks, int B, float* logits) {
+// Teacher-forced rounding (B == 1 only): with force_k / force_v (cache-format codes [L][nkv][hd])
+// the row appended at this position is the given one, not this step's own rounding of k and v,
+// which goes to own_k / own_v (if not NULL) instead; the rest of the step then reads the forced
+// row, as a teacher-forced step reads a given token.
+static int forward_tokens(orc_model* m, const int32_t* toks, int B, float* logits, const uint8_t* force_k = nullptr,
+                          const uint8_t* force_v = nullptr, uint8_t* own_k = nullptr, uint8_t* own_v = nullptr) {
   const orc_config& c = m->c;
   const int H = c.H, hd = c.hd, qd = c.nq * hd, kvd = c.nkv * hd, grp = c.nq / c.nkv;
   const int p0 = m->pos;
@@ -373,6 +415,11 @@ static int forward_tokens(orc_model* m, const int32_t* toks, int B, float* logit
         rope(kg, hd, p, c.theta);
         uint8_t* kdst = &m->kcache[kv_index(c, l, g, p) * es];
         uint8_t* vdst = &m->vcache[kv_index(c, l, g, p) * es];
+        float* amax = &m->kv_amax[((size_t)l * c.nkv + g) * 2];
+        for (int i = 0; i < hd; ++i) {
+          amax[0] = std::fabs(kg[i]) > amax[0] ? std::fabs(kg[i]) : amax[0];
+          amax[1] = std::fabs(vg[i]) > amax[1] ? std::fabs(vg[i]) : amax[1];
+        }
         if (c.kvfmt == E4M3) {
           const float ks = m->kv_scale[((size_t)l * c.nkv + g) * 2], vs = m->kv_scale[((size_t)l * c.nkv + g) * 2 + 1];
           for (int i = 0; i < hd; ++i) {
@@ -383,6 +430,11 @@ static int forward_tokens(orc_model* m, const int32_t* toks, int B, float* logit
           orc_encode(c.kvfmt, kg, hd, kdst);
           orc_encode(c.kvfmt, vg, hd, vdst);
         }
+        const size_t row = ((size_t)l * c.nkv + g) * hd * es;  // this (layer, kv head) row in [L][nkv][hd]
+        if (own_k) std::memcpy(own_k + row, kdst, hd * es);
+        if (own_v) std::memcpy(own_v + row, vdst, hd * es);
+        if (force_k) std::memcpy(kdst, force_k + row, hd * es);
+        if (force_v) std::memcpy(vdst, force_v + row, hd * es);
       }
     }
 #pragma omp parallel for schedule(dynamic) collapse(2)
@@ -428,6 +480,19 @@ int orc_prefill(orc_model* m, const int32_t* toks, int P, int block, float* logi
   return tok;
 }
 
+// One decode step with teacher-forced rounding of the appended KV row (see forward_tokens):
+// force_k / force_v [L][nkv][hd] codes are appended; own_k / own_v receive this step's own codes.
+int orc_step_forced(orc_model* m, int32_t tok, const void* force_k, const void* force_v, void* own_k, void* own_v,
+                    float* logits) {
+  const orc_config& c = m->c;
+  if (m->pos >= c.max_seq) return -2;
+  std::vector<float> lg(c.V);
+  const int next = forward_tokens(m, &tok, 1, lg.data(), (const uint8_t*)force_k, (const uint8_t*)force_v,
+                                  (uint8_t*)own_k, (uint8_t*)own_v);
+  if (logits) std::memcpy(logits, lg.data(), sizeof(float) * c.V);
+  return next;
+}
+
 // One decode step: token `tok` at position pos; pos += 1.  Returns the greedy next token.
 int orc_step(orc_model* m, int32_t tok, float* logits) {
   const orc_config& c = m->c;
@@ -442,3 +507,4 @@ int orc_step(orc_model* m, int32_t tok, float* logits) {
 
 #include <omp.h>
 extern "C" int orc_num_threads(void) { return omp_get_max_threads(); }
+extern "C" void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

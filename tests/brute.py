@@ -69,11 +69,16 @@ def _rope_rows(M, positions, hd, theta):
     return Mh.reshape(T, -1)
 
 
-def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=None):
+def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=None, collect_kv=None,
+               forced_last=None):
     """Logits at the LAST position of `tokens`, recomputing everything.
 
     cached_kv: optional (k, v) fp64 arrays [L][nkv][P0][hd] of already-dequantised cache
     contents for positions 0..P0-1 that precede `tokens` (then `tokens` sit at P0..).
+    collect_kv: optional list; receives per layer the (k, v) fp64 values [T][nkv][hd] of `tokens`
+    (k after RoPE) before they are rounded into the cache format.
+    forced_last: optional (k, v) fp64 arrays [L][nkv][hd]: the already-dequantised cache row of the
+    LAST token, used in place of its own rounded k and v.
     """
     w = weights.workload
     efmt = "bf16" if w.wdtype == "fp8" else w.wdtype
@@ -93,6 +98,8 @@ def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=No
         Vv = Xn @ linear(weights, l, "wv").T
         K = K.reshape(T, nkv, hd)
         Vv = Vv.reshape(T, nkv, hd)
+        if collect_kv is not None:
+            collect_kv.append((K.copy(), Vv.copy()))
         Kr = np.empty_like(K)
         Vr = np.empty_like(Vv)
         for g in range(nkv):
@@ -100,6 +107,9 @@ def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=No
             vs = 1.0 if kv_scales is None else float(kv_scales[l, g, 1])
             Kr[:, g] = round_to(K[:, g], w.kvdtype, ks)
             Vr[:, g] = round_to(Vv[:, g], w.kvdtype, vs)
+            if forced_last is not None:
+                Kr[-1, g] = forced_last[0][l, g]
+                Vr[-1, g] = forced_last[1][l, g]
         if cached_kv is not None:
             Kr = np.concatenate([np.transpose(cached_kv[0][l], (1, 0, 2)), Kr], axis=0)
             Vr = np.concatenate([np.transpose(cached_kv[1][l], (1, 0, 2)), Vr], axis=0)

@@ -427,3 +427,133 @@ def test_oracle_matches_its_recorded_tiny_run():
     assert now["tokens"] == gold["tokens"] and now["prompt"] == gold["prompt"]
     for k, v in gold["logits_head"].items():
         assert np.array_equal(np.float32(now["logits_head"][k]), np.float32(v)), k
+
+
+# ---------------------------------------------------------------------------------------------
+# static FP8 KV scales derived from a prompt: the largest |k| (after RoPE) and |v| per (layer, kv
+# head) over the appended rows, S = amax / 448 (a reading of the pages' static per-head FP8-KV
+# scale: "Netra Kernel" summary, details, FP8-KV attention with explicit scale semantics)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kvfmt", ["f16", "fp8"])
+def test_kv_amax_matches_brute_force_values(kvfmt):
+    """The recorded maxima equal the largest |k|, |v| of an independent fp64 recomputation of the
+    prompt (same rounding of earlier layers' KV into the cache format, scale 1)."""
+    w = TINY.with_(kvdtype=kvfmt, wdtype=kvfmt, hidden=256, ffn=384, head_dim=128 if kvfmt == "fp8" else 64)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    m = oracle.OracleModel(wts)
+    ones = np.ones((w.layers, w.n_kv, 2), np.float32)
+    if kvfmt == "fp8":
+        m.set_kv_scales(ones)
+    prompt = synthgen.make_prompt(w, 12)
+    m.prefill(prompt)
+    got = m.kv_amax()
+    kv = []
+    brute.logits_all(wts, prompt, kv_scales=ones if kvfmt == "fp8" else None, collect_kv=kv)
+    ref = np.array([[[np.abs(K[:, g]).max(), np.abs(V[:, g]).max()] for g in range(w.n_kv)] for K, V in kv])
+    assert ref.min() > 0.05
+    np.testing.assert_allclose(got, ref, rtol=2e-3)
+    # the maxima restart from zero after a reset
+    m.reset_kv_amax()
+    assert (m.kv_amax() == 0).all()
+
+
+@pytest.mark.parametrize("kvfmt", ["bf16", "fp8"])
+def test_kv_amax_rounds_to_the_largest_cache_element(kvfmt):
+    """Round-to-nearest-even (saturating for E4M3) is monotone in |x|, so the largest |cache
+    element| of each (layer, head, K|V) is the maximum rounded into the cache format: exact."""
+    w = TINY.with_(kvdtype=kvfmt, wdtype="fp8" if kvfmt == "fp8" else kvfmt, hidden=256, ffn=384, head_dim=128)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    m = oracle.OracleModel(wts)
+    if kvfmt == "fp8":
+        m.set_kv_scales(np.ones((w.layers, w.n_kv, 2), np.float32))
+    P = 10
+    m.prefill(synthgen.make_prompt(w, P))
+    amax = m.kv_amax()
+    k, v = m.read_kv(P)
+    fmt = oracle.FMT[kvfmt]
+    for l in range(w.layers):
+        for g in range(w.n_kv):
+            for j, c in enumerate((k, v)):
+                largest = np.abs(oracle.decode(fmt, c[l, g])).max()
+                rounded = abs(float(oracle.decode(fmt, oracle.encode(fmt, amax[l, g, j:j + 1]))[0]))
+                assert largest == rounded, (l, g, j, largest, rounded)
+
+
+def test_derived_fp8_scales_map_layer0_maximum_to_448_and_zero_to_one():
+    """With S = amax / 448 the largest calibrated value of layer 0 (whose k and v do not depend on
+    the cache contents) becomes the largest E4M3 magnitude; a head whose values are all zero keeps
+    scale 1 (here every v, by zeroing Wv)."""
+    w = TINY.with_(wdtype="fp8", kvdtype="fp8", hidden=256, ffn=384, head_dim=128)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    for d in wts.layers:
+        d["wv"][...] = 0
+    prompt = synthgen.make_prompt(w, 12)
+    cal = oracle.OracleModel(wts)
+    cal.set_kv_scales(np.ones((w.layers, w.n_kv, 2), np.float32))
+    cal.prefill(prompt)
+    amax = cal.kv_amax()
+    S = cal.kv_scales_from_amax()
+    assert (amax[..., 1] == 0).all() and (S[..., 1] == 1.0).all()
+    assert (S[..., 0] > 0).all() and (S[..., 0] != 1.0).all()
+    m = oracle.OracleModel(wts)
+    m.set_kv_scales(S)
+    m.prefill(prompt)
+    k, _ = m.read_kv(len(prompt))
+    for g in range(w.n_kv):
+        assert np.abs(oracle.decode(oracle.E4M3, k[0, g])).max() == 448.0
+
+
+# ---------------------------------------------------------------------------------------------
+# teacher-forced rounding of the appended KV row (the parity protocol's teacher forcing extended
+# from the input token to the step's rounding decisions)
+# ---------------------------------------------------------------------------------------------
+def test_forced_kv_row_equal_to_own_row_changes_nothing(tiny_weights):
+    m1, m2 = oracle.OracleModel(tiny_weights), oracle.OracleModel(tiny_weights)
+    prompt = synthgen.make_prompt(TINY, 6)
+    for m in (m1, m2):
+        m.prefill(prompt[:5])
+    tok, lg = m1.step(int(prompt[5]))
+    k, v = m1.read_kv(6)
+    tok2, lg2, own_k, own_v = m2.step_forced(int(prompt[5]), k[:, :, 5], v[:, :, 5])
+    assert tok2 == tok and np.array_equal(lg2, lg)
+    assert np.array_equal(own_k, k[:, :, 5]) and np.array_equal(own_v, v[:, :, 5])
+
+
+@pytest.mark.parametrize("kvfmt", ["f16", "fp8"])
+def test_forced_kv_row_matches_brute_force(kvfmt):
+    """A step that appends a perturbed row (every code of layer 0 moved by one, every V code of the
+    last layer by one) against an fp64 recomputation that uses the same row: the forced row is what
+    the step's attention reads, and the step's own codes are still reported."""
+    w = TINY.with_(kvdtype=kvfmt, wdtype=kvfmt, hidden=256, ffn=384, head_dim=128 if kvfmt == "fp8" else 64)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32) if kvfmt == "fp8" else None
+    prompt = synthgen.make_prompt(w, 7)
+    ref_m = oracle.OracleModel(wts)
+    m = oracle.OracleModel(wts)
+    for x in (ref_m, m):
+        if scales is not None:
+            x.set_kv_scales(scales)
+        x.prefill(prompt[:6])
+    ref_m.step(int(prompt[6]))
+    own_k, own_v = ref_m.read_kv(7)
+    fk, fv = own_k[:, :, 6].copy(), own_v[:, :, 6].copy()
+    fk[0] = fk[0] + 1
+    fv[0] = fv[0] + 1
+    fv[-1] = fv[-1] + 1
+    _, lg, ok, ov = m.step_forced(int(prompt[6]), fk, fv)
+    # layer 0's own k, v do not depend on the forced row (later layers' do: they read it)
+    assert np.array_equal(ok[0], own_k[0, :, 6]) and np.array_equal(ov[0], own_v[0, :, 6])
+    assert not np.array_equal(ok[-1], own_k[-1, :, 6])
+    k_after, v_after = m.read_kv(7)
+    assert np.array_equal(k_after[:, :, 6], fk) and np.array_equal(v_after[:, :, 6], fv)
+    fmt = oracle.FMT[kvfmt]
+    deq = []
+    for j, row in enumerate((fk, fv)):
+        d = oracle.decode(fmt, row).astype(np.float64)
+        if kvfmt == "fp8":
+            d = d * scales[:, :, j][:, :, None]
+        deq.append(d)
+    ref = brute.logits_all(wts, prompt, kv_scales=scales, forced_last=tuple(deq))
+    assert np.abs(lg - ref).max() < 2e-3 and np.abs(ref).max() > 0.05
+    plain = brute.logits_all(wts, prompt, kv_scales=scales)
+    assert np.abs(plain - ref).max() > 10 * np.abs(lg - ref).max()  # the forcing is visible
