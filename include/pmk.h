@@ -160,63 +160,136 @@ typedef struct {
 
 typedef struct pmk_ctx pmk_ctx;
 
+/* Citations below name a page by its title and the section of it that defines the operation:
+ *   [AMK] "AutoMegaKernel: A Statically-Checked Agent Harness for Self-Retargeting Megakernel
+ *         Synthesis" (explainer page); [Kog] "Kog AI MI300X monokernel tutorial" (news page);
+ *   [Netra] "Netra Kernel" summary page. */
+
+/* Version of this ABI (PMK_ABI_VERSION), for a caller's compatibility check.
+ * Passage: [Netra] details, "C ABI" runtime with fixed symbols.  No error case. */
 int pmk_abi_version(void);
+/* Static text for a status code (never NULL; unknown codes give "unknown status"). */
 const char* pmk_status_str(pmk_status s);
 /* Text of the last failure on ctx (never NULL; empty when none).  Valid until the next call. */
 const char* pmk_last_error(const pmk_ctx* ctx);
 /* Text of the last failure of a call that could not return a context (pmk_create). */
 const char* pmk_last_global_error(void);
 
-/* Host only.  Checks the contract, builds the schedule for the device's CU count and runs
- * the static validator; returns PMK_ERR_UNSUPPORTED / PMK_ERR_SCHEDULE_INVALID with the
- * reason in pmk_last_global_error().  hip_device < 0 builds a device-less context (for
- * schedule inspection; every device call then returns PMK_ERR_NOT_BOUND). */
+/* Create a context.  Host only.
+ * Passages: [Netra] details (kernels are selected by the operation's exact contract: shapes, data
+ * formats, accumulation order, layout; a request outside it is rejected, never approximated);
+ * [AMK] Method, Layer 2 (the model is lowered into a typed task DAG shaped by a ScheduleConfig) and
+ * Safety Gate (the schedule is checked statically before any launch and rejected if it fails).
+ * cfg: the model (read during the call only); sched: NULL for the defaults; hip_device: the HIP
+ * device index, or < 0 for a device-less context (schedule inspection only; every device call on it
+ * returns PMK_ERR_NOT_BOUND).  On success *out owns a new context (release with pmk_destroy).
+ * Errors: PMK_ERR_INVALID_ARG (NULL cfg/out), PMK_ERR_UNSUPPORTED (outside the contract),
+ * PMK_ERR_SCHEDULE_INVALID (the validator rejected the lowering), PMK_ERR_DEVICE (not gfx950, no
+ * cooperative launch, or the kernel cannot be resident), PMK_ERR_HIP; the reason is in
+ * pmk_last_global_error().  Nothing is allocated on the device. */
 pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sched, int hip_device,
                       pmk_ctx** out);
+/* Release a context (NULL is ignored).  The caller's buffers are not freed.  Passage: [Netra]
+ * details (the runtime binds caller buffers; ownership stays with the caller). */
 void pmk_destroy(pmk_ctx* ctx);
 
+/* Bytes of the three caller-allocated device buffers (arena, KV cache, workspace).
+ * Passage: [Netra] details (the engine carries a static memory and layout plan; the runtime only
+ * binds buffers).  Errors: PMK_ERR_INVALID_ARG for NULL arguments. */
 pmk_status pmk_buffer_sizes(const pmk_ctx* ctx, pmk_sizes* out);
-/* Non-owning.  arena, kv and workspace must be 256-byte aligned device pointers of at
- * least the reported sizes. */
+/* Bind caller-owned device buffers.  Non-owning: they must stay allocated until pmk_destroy or the
+ * next bind.  arena, kv and workspace must be 256-byte aligned device pointers of at least the
+ * reported sizes.  Uploads the schedule tables and clears the synchronisation state (synchronous).
+ * Passage: [Netra] details (the runtime links persistent and boundary buffers, then launches on a
+ * caller-owned stream).  Errors: PMK_ERR_INVALID_ARG (NULL or misaligned), PMK_ERR_NOT_BOUND
+ * (device-less context), PMK_ERR_HIP.  Weights and KV state must be loaded again after a bind. */
 pmk_status pmk_bind(pmk_ctx* ctx, void* d_arena, void* d_kv, void* d_workspace);
 
-/* Repack the canonical tensors into the arena (QKV rows concatenated with each RoPE pair
- * made adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table).
- * Asynchronous on `stream`; the sources may be freed once the stream has synchronised. */
+/* Repack the canonical tensors into the arena (QKV rows concatenated with each RoPE pair made
+ * adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table).
+ * Passages: [Netra] details (weight layout and FP8 E4M3 block-scale semantics are fixed ahead of
+ * time); [AMK] Method (HF Llama-family models are imported into the schedule).
+ * src: device pointers to the canonical tensors (pmk_weight_ptrs; the host arrays are read during
+ * the call only).  Asynchronous on `stream` (a hipStream_t, NULL = default stream); the sources may
+ * be freed once the stream has synchronised.  Errors: PMK_ERR_NOT_BOUND, PMK_ERR_INVALID_ARG
+ * (missing pointers or FP8 scales), PMK_ERR_HIP. */
 pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stream);
 
-/* Teacher-forced prefill: runs positions 0..P-1 from d_tokens[P] (device), writing the KV
- * cache; the greedy choice after the last position becomes the next input token (and is
- * also stored to d_first_token if not NULL).  For an FP8 KV cache, d_kv_scales
- * [n_layers][n_kv][2] (K, V) fp32 gives the static scales; it is required.
- * Resets the position and the synchronisation state.  PMK_ERR_CAPACITY if P > max_seq. */
+/* Teacher-forced prefill: runs positions 0..P-1 from d_tokens[P] (device int32), writing the KV
+ * cache; the greedy choice after the last position becomes the next input token (and is also
+ * stored to d_first_token, a device int32, if not NULL).
+ * Passages: [Kog] how the monokernel removes kernel-launch overhead (prefill, decode, LM-head
+ * sampling and the EOS check run in the resident program); [Netra] details (GQA attention over an
+ * FP8 KV cache, with its scale semantics fixed by the contract).
+ * FP8 KV cache: d_kv_scales [n_layers][n_kv][2] (K, V) fp32 device array gives static scales; with
+ * NULL the library derives them from this prompt: a calibration pass with every scale 1 records the
+ * largest |k| and |v| per (layer, kv head), each scale becomes that maximum / 448 in fp32 (1 if the
+ * maximum is 0), and the prefill then runs with those scales (read them back with pmk_get_kv_scales).
+ * Other KV formats ignore d_kv_scales.  Resets the position and the synchronisation state.
+ * Asynchronous on `stream`.  Errors: PMK_ERR_NOT_BOUND (no weights), PMK_ERR_INVALID_ARG (NULL
+ * tokens, P <= 0), PMK_ERR_CAPACITY (P > max_seq), PMK_ERR_HIP. */
 pmk_status pmk_prefill_kv(pmk_ctx* ctx, const int32_t* d_tokens, int32_t P, const float* d_kv_scales,
                           int32_t* d_first_token, void* stream);
 
+/* Copy the FP8 KV scales in force, [n_layers][n_kv][2] (K, V) fp32, to the device array d_out.
+ * Passage: [Netra] details (FP8 KV attention with explicit scale semantics).  Asynchronous on
+ * `stream`.  Errors: PMK_ERR_INVALID_ARG (NULL d_out, or a KV cache that is not FP8),
+ * PMK_ERR_NOT_BOUND, PMK_ERR_HIP. */
+pmk_status pmk_get_kv_scales(pmk_ctx* ctx, float* d_out, void* stream);
+
 /* Resume from saved state: copies KV contents d_k, d_v [n_layers][n_kv][P][head_dim] (cache
- * element format) into positions 0..P-1, sets the position to P and the next input token to
- * `next_token`.  d_kv_scales as for pmk_prefill_kv. */
+ * element format, device) into positions 0..P-1, sets the position to P and the next input token to
+ * `next_token`.  d_kv_scales as for pmk_prefill_kv, but required for an FP8 cache (the contents are
+ * already quantised).  Passage: [Netra] details (persistent buffers bound by the runtime; FP8-KV
+ * scale semantics).  Asynchronous.  Errors: PMK_ERR_CAPACITY (P > max_seq), PMK_ERR_INVALID_ARG
+ * (missing pointers or scales, next_token outside the vocabulary), PMK_ERR_NOT_BOUND, PMK_ERR_HIP. */
 pmk_status pmk_load_kv(pmk_ctx* ctx, const void* d_k, const void* d_v, int32_t P, int32_t next_token,
                        const float* d_kv_scales, void* stream);
 
-/* Rewind to position `pos` (0 < pos <= current position) with next input token read from
- * d_token (device int32).  KV entries at positions >= pos are overwritten by later steps. */
+/* Save state: copies positions 0..P-1 of the KV cache (P <= the current position) to d_k, d_v
+ * [n_layers][n_kv][P][head_dim] in the cache element format (device), the layout pmk_load_kv takes.
+ * Passage: [Netra] details (persistent buffers the runtime binds; here the cache contents leave the
+ * library in the canonical layout).  Asynchronous on `stream`.  Errors: PMK_ERR_NOT_BOUND (no KV
+ * state), PMK_ERR_INVALID_ARG (P outside [0, position], missing pointers), PMK_ERR_HIP. */
+pmk_status pmk_read_kv(pmk_ctx* ctx, void* d_k, void* d_v, int32_t P, void* stream);
+
+/* Rewind to position `pos` (0 < pos <= current position) with the next input token read from
+ * d_token (device int32).  KV entries at positions >= pos are overwritten by later steps.  After a
+ * decode call with an eos id this first reads the exact position from the device (synchronising).
+ * Passage: [AMK] Results (teacher-forced and greedy runs from the same state are compared).
+ * Errors: PMK_ERR_INVALID_ARG (pos outside (0, position], NULL token), PMK_ERR_NOT_BOUND. */
 pmk_status pmk_rewind(pmk_ctx* ctx, int32_t pos, const int32_t* d_token, void* stream);
 
-/* n greedy decode steps from the next-token slot at the current position.  Step i consumes
- * the current input token at position pos+i, appends its K and V, and writes the greedy
- * next token to d_out_tokens[i]; with d_out_logits != NULL the fp32 logits go to
- * d_out_logits[i*vocab ...].  eos_id >= 0 stops after the step that emits it; the number of
- * steps run goes to *d_n_done (device, may be NULL).  MEGAKERNEL mode is ONE kernel launch.
- * The host advances its position by n (an upper bound when eos stops early; the device
- * keeps the exact position).  PMK_ERR_CAPACITY if position + n > max_seq. */
+/* n greedy decode steps from the next-token slot at the current position.  Step i consumes the
+ * current input token at position pos+i, appends its K and V, and writes the greedy next token to
+ * d_out_tokens[i] (device int32 [n]); with d_out_logits != NULL the fp32 logits go to
+ * d_out_logits[i*vocab ...] (device).  eos_id >= 0 stops after the step that emits it; the number of
+ * steps run goes to *d_n_done (device int32, may be NULL).  MEGAKERNEL mode is ONE kernel launch;
+ * GRAPH mode replays one captured graph of per-op kernels per step; PER_OP launches them directly.
+ * Passages: [Kog] how the monokernel removes kernel-launch overhead (the whole decode loop, LM-head
+ * sampling and the EOS check stay in one resident kernel with no host re-entry); [AMK] Problem
+ * (batch-1 decode is bandwidth bound: the floor is weight bytes over HBM bandwidth) and Method,
+ * Layer 0 (one cooperative block per compute unit runs its queue: wait, dispatch, signal).
+ * Asynchronous on `stream`; the host does not re-enter during the call.  The position advances by
+ * the steps run (after an eos stop the device keeps the exact position; pmk_get_position reads it).
+ * Errors: PMK_ERR_NOT_BOUND (weights or KV state missing), PMK_ERR_INVALID_ARG (n <= 0, NULL
+ * d_out_tokens), PMK_ERR_CAPACITY (position + n > max_seq), PMK_ERR_HIP.  Device-side failures
+ * (watchdog time-out, NaN logits) are reported by pmk_poll_error. */
 pmk_status pmk_decode_n_tokens(pmk_ctx* ctx, int32_t n, int32_t* d_out_tokens, float* d_out_logits,
                                int32_t eos_id, int32_t* d_n_done, void* stream);
 
+/* Execution mode (pmk_mode) of later calls.  Passages: [AMK] Problem (per-op launches and graph
+ * replay keep the operator boundaries the megakernel removes); [Netra] details (a HIP graph
+ * prepared at initialisation is replayed).  Errors: PMK_ERR_INVALID_ARG for an unknown mode. */
 pmk_status pmk_set_mode(pmk_ctx* ctx, int32_t mode);
+/* Current position (next position to be written).  After a decode call with an eos id this
+ * synchronises the device and reads the exact position.  Errors: PMK_ERR_INVALID_ARG (NULL). */
 pmk_status pmk_get_position(const pmk_ctx* ctx, int32_t* pos);
 
-/* After the caller synchronised the stream: reads the device error word. */
+/* After the caller synchronised the stream: reads the device error word into *err (may be NULL) and
+ * returns its code (PMK_ERR_TIMEOUT: a wait exceeded its spin limit; PMK_ERR_NAN: NaN logits).
+ * Passage: [AMK] Safety Gate (an unsafe schedule must not stall the GPU: every wait here is
+ * bounded by a watchdog that aborts the launch instead). */
 pmk_status pmk_poll_error(pmk_ctx* ctx, pmk_device_error* err);
 
 /* Trace: with trace_steps > 0 and pmk_set_trace(ctx, 1) (which clears the ring), each task of
@@ -224,7 +297,9 @@ pmk_status pmk_poll_error(pmk_ctx* ctx, pmk_device_error* err);
  * up to four task-specific sub-phase stamps (GEMV: input staged, rows done; attention: scores
  * done, partial stored; combine: partials loaded), from the constant 100 MHz clock.
  * pmk_trace_export writes Chrome-trace JSON (synchronises the device); pmk_trace_stats gives the
- * mean share of queue time spent waiting. */
+ * mean share of queue time spent waiting and the mean step time.
+ * Passage: [Kog] how the monokernel removes kernel-launch overhead (synchronisation is measured as
+ * a share of token time).  Errors: PMK_ERR_INVALID_ARG (no trace buffer, unwritable path). */
 pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
 pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);
 pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
@@ -241,13 +316,20 @@ pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
  * restored (the KV rows it wrote past that position are rewritten by the next decode).
  * Synchronous on `stream`.  Requires bound weights and KV state and a context created with
  * trace_steps >= 1.  Row assignment never changes a row's arithmetic beyond the grouping of its
- * partial sums. */
+ * partial sums.  Passage: [AMK] Autoresearch loop (propose a ScheduleConfig change, validate it,
+ * time it, keep it or revert).  Errors: PMK_ERR_NOT_BOUND, PMK_ERR_INVALID_ARG (no trace ring),
+ * PMK_ERR_CAPACITY, PMK_ERR_SCHEDULE_INVALID, PMK_ERR_HIP. */
 pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, int32_t* kept, void* stream);
 
-/* Schedule inspection (host only, also for device-less contexts). */
+/* Schedule inspection (host only, also for device-less contexts).  Passage: [Netra] details
+ * (deterministic engine artifacts: the schedule hash is reproducible across runs).
+ * Errors: PMK_ERR_INVALID_ARG for NULL arguments. */
 pmk_status pmk_schedule_get_info(const pmk_ctx* ctx, pmk_schedule_info* info);
 
-/* ---- Schedule IR, exposed for the validator's tests and the validator CLI ---- */
+/* ---- Schedule IR, exposed for the validator's tests and the validator CLI ----
+ * Passage for this whole block: [AMK] Method, Layer 2 (the model lowered into a typed Schedule IR:
+ * a task DAG over per-compute-unit queues synchronised by monotonic counters) and Safety Gate (the
+ * static checks run on that IR before any launch).  Host only; no device is needed. */
 typedef enum {
   PMK_OP_QKV = 1,     /* RMSNorm prologue + packed QKV GEMV rows [a0,a1) + RoPE + KV append */
   PMK_OP_ATTN = 2,    /* split-KV attention partial (max, sum, P.V) for kv head a0, split a1 */
@@ -275,14 +357,21 @@ typedef struct {
 
 typedef struct pmk_schedule pmk_schedule;
 
-/* Build the schedule for `n_cus` queues without a device. */
+/* Build the schedule for `n_cus` queues without a device ([AMK] Method, Layer 2: lowering with a
+ * ScheduleConfig).  *out owns a new schedule (pmk_schedule_free).  Errors: PMK_ERR_INVALID_ARG,
+ * PMK_ERR_UNSUPPORTED (outside the contract), PMK_ERR_SCHEDULE_INVALID (the lowering failed). */
 pmk_status pmk_schedule_build(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
                               pmk_schedule** out);
 /* The same with per-queue row weights for the GEMV phases: weights[op * n_cus + q] for pmk_op op
  * (QKV, OPROJ, GATEUP, DOWN, LMHEAD; other rows of the 8 x n_cus array are ignored), positive; each
- * GEMV task's rows are proportional to its queue's weight (at least one row or row pair each). */
+ * GEMV task's rows are proportional to its queue's weight (at least one row or row pair each).
+ * ([AMK] Method, Layer 2: CU allocation is a ScheduleConfig knob.)  Errors as pmk_schedule_build,
+ * and PMK_ERR_INVALID_ARG for a weight that is not positive. */
 pmk_status pmk_schedule_build_weighted(const pmk_model_config* cfg, const pmk_schedule_config* sched, int32_t n_cus,
                                        const float* weights, pmk_schedule** out);
+/* Accessors and editors of the IR ([AMK] Method, Layer 2: the schedule is the edit surface that
+ * proposals change; Safety Gate: every edited schedule is re-validated before use).  NULL or an
+ * index out of range gives PMK_ERR_INVALID_ARG (or 0 / -1 / NULL for the value-returning ones). */
 void pmk_schedule_free(pmk_schedule* s);
 int32_t pmk_schedule_num_tasks(const pmk_schedule* s);
 int32_t pmk_schedule_num_counters(const pmk_schedule* s);
@@ -294,14 +383,17 @@ const int32_t* pmk_schedule_queue(const pmk_schedule* s, int32_t q, int32_t* len
 pmk_status pmk_schedule_set_queue(pmk_schedule* s, int32_t q, const int32_t* tasks, int32_t len);
 int32_t pmk_schedule_counter_producers(const pmk_schedule* s, int32_t c);
 pmk_status pmk_schedule_set_counter_producers(pmk_schedule* s, int32_t c, int32_t producers);
-/* Static validator: returns PMK_OK or PMK_ERR_SCHEDULE_INVALID with the first failed check
- * (one line, "<check>: <detail>") copied into report[0..cap). */
+/* Static validator ([AMK] Safety Gate: deadlock-freedom, race-freedom, correctness): returns PMK_OK
+ * or PMK_ERR_SCHEDULE_INVALID with the first failed check (one line, "<check>: <detail>") copied
+ * into report[0..cap). */
 pmk_status pmk_schedule_validate(const pmk_schedule* s, char* report, size_t cap);
-/* CPU simulator: executes the queues for `steps` steps with one host thread per queue
- * and randomised yields, treating each task as reading/writing its declared regions in
- * NaN-poisoned buffers.  Returns PMK_OK, PMK_ERR_TIMEOUT (a queue stuck: deadlock) or
- * PMK_ERR_SCHEDULE_INVALID (a read observed a poisoned or stale value: race). */
+/* CPU simulator ([AMK] Safety Gate, checked dynamically): executes the queues for `steps` steps
+ * with one host thread per queue and randomised yields, treating each task as reading/writing its
+ * declared regions in poisoned stamp buffers.  Returns PMK_OK, PMK_ERR_TIMEOUT (a queue stuck:
+ * deadlock), PMK_ERR_SCHEDULE_INVALID (a read observed a poisoned or stale value: race) or
+ * PMK_ERR_INVALID_ARG (NULL, steps <= 0, or a model too large to simulate). */
 pmk_status pmk_schedule_simulate(const pmk_schedule* s, int32_t steps, uint64_t seed, char* report, size_t cap);
+/* FNV-1a hash of the serialised schedule ([Netra] details: deterministic artifacts); 0 for NULL. */
 uint64_t pmk_schedule_hash(const pmk_schedule* s);
 
 #ifdef __cplusplus

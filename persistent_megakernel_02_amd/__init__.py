@@ -121,6 +121,24 @@ class Decoder:
                                       _stream(stream)), self.ctx)
         return first
 
+    def kv_scales(self, stream=None):
+        """The FP8 KV scales in force, [layers][n_kv][2] (K, V) fp32 on the device."""
+        import torch
+        out = torch.empty((self.cfg.n_layers, self.cfg.n_kv_heads, 2), dtype=torch.float32,
+                          device=torch.device("cuda", self.device))
+        check(self.lib.pmk_get_kv_scales(self.ctx, out.data_ptr(), _stream(stream)), self.ctx)
+        return out
+
+    def read_kv(self, P: int, stream=None):
+        """KV cache positions 0..P-1 as device tensors [layers][n_kv][P][head_dim] (cache format)."""
+        import torch
+        dt = torch.uint8 if self.cfg.kv_dtype == PMK_DT_FP8_E4M3 else torch.int16
+        shape = (self.cfg.n_layers, self.cfg.n_kv_heads, P, self.cfg.head_dim)
+        dev = torch.device("cuda", self.device)
+        k, v = torch.empty(shape, dtype=dt, device=dev), torch.empty(shape, dtype=dt, device=dev)
+        check(self.lib.pmk_read_kv(self.ctx, k.data_ptr(), v.data_ptr(), P, _stream(stream)), self.ctx)
+        return k, v
+
     def load_kv(self, k, v, P: int, next_token: int, kv_scales=None, stream=None):
         check(self.lib.pmk_load_kv(self.ctx, k.data_ptr() if k is not None else None,
                                    v.data_ptr() if v is not None else None, P, next_token,

@@ -80,6 +80,8 @@ SIGNATURES = {
     "pmk_bind": (i32, [vp, vp, vp, vp]),
     "pmk_load_weights": (i32, [vp, ctypes.POINTER(pmk_weight_ptrs), vp]),
     "pmk_prefill_kv": (i32, [vp, vp, i32, vp, vp, vp]),
+    "pmk_get_kv_scales": (i32, [vp, vp, vp]),
+    "pmk_read_kv": (i32, [vp, vp, vp, i32, vp]),
     "pmk_load_kv": (i32, [vp, vp, vp, i32, i32, vp, vp]),
     "pmk_rewind": (i32, [vp, i32, vp, vp]),
     "pmk_decode_n_tokens": (i32, [vp, i32, vp, vp, i32, vp, vp]),

@@ -17,9 +17,11 @@
 // coherent loads, so no L2 write-back or invalidate is needed.  A producer drains its stores
 // (s_waitcnt vmcnt(0) in every wave, then a workgroup barrier) before one thread publishes the
 // flag or counter; a consumer polls that word and only then issues its coherent data loads.
-// Weights and KV rows of past steps are read with plain non-temporal loads: they were written
-// before this launch or, for KV rows, before their first read in this launch, and every KV row
-// covers whole 128-byte lines (head_dim * element size >= 128 is part of the contract).
+// Weights and the KV rows of positions written before this launch are read with plain
+// non-temporal loads (kernel boundaries order them).  KV rows of positions written during this
+// launch are read with coherent loads by the splits that hold them (a V-cache line holds 32
+// positions, so it is read before all of its slots are written), and the position written in the
+// current step is never read from the cache but from its step-tagged copy.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -580,8 +582,10 @@ struct StepCtx {
   int e;        // global step (since the last reset)
   int s;        // step within this call
   int pos;      // position written by this step
+  int pos0;     // first position written by this kernel launch (KV rows from pos0 on are read coherently)
   int tok;      // input token if already known, else -1
   bool per_op;  // per-op kernels: no waits (kernel boundaries order the tasks)
+  bool calib;   // FP8 KV scale calibration: QKV records max |k|, |v| of every appended row
 };
 
 // Stage a tagged vector src[0..n) of step e into xs (zero padding to pad): every thread re-reads
@@ -812,6 +816,9 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
     uint8_t* cache = sec == 1 ? P.kc : P.vc;
     uint32_t ba, bb;  // the stored elements as 16-bit matrix-core operands (fp8: its bf16 value)
     if constexpr (KVDT == WFP8) {
+      if (sc.calib)
+        __hip_atomic_fetch_max(&P.kv_amax[hb * 2 + (sec - 1)], __float_as_uint(fmaxf(fabsf(a), fabsf(b))),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const float s8 = rope[half + 2 * head + (sec - 1)].x;
       const uint8_t ca = enc_e4m3(a / s8), cb = enc_e4m3(b / s8);
       stc(cache + ia, ca);
@@ -922,15 +929,19 @@ __device__ __forceinline__ u32x4 fp8x8_bf16(u32x2 w) {
 }
 
 // KV cache element loads through a buffer resource (out of range: zeros): 8 elements per lane as
-// 16-bit matrix-core operands, streamed (nontemporal).  Every position read this way was written
-// in an earlier step; the current one comes from its tagged copy.
-template <int KVDT>
+// 16-bit matrix-core operands.  Rows of positions written before this launch are streamed
+// (nontemporal); a split that holds positions written during this launch (COH) reads every row with
+// agent-coherent loads (sc1), as it reads any other value another CU stored in this launch: a
+// V-cache line holds 32 positions, so it is read at the steps before all of its slots are written.
+// The current position is never read from the cache: it comes from its tagged copy.
+template <int KVDT, bool COH>
 __device__ __forceinline__ u32x4 kv_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  constexpr int kPol = COH ? 16 : 2;  // sc1 : nt
   if constexpr (KVDT == WFP8) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPol);
     return fp8x8_bf16(w);
   } else {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPol);
   }
 }
 
@@ -960,7 +971,7 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nv) {
 // column_max / column_sum) runs on the 8 scores a lane holds; the eight waves' (max, sum, acc)
 // are then merged in LDS with the usual rescaling, exactly as the splits are merged by the
 // combine.
-template <int WDT, int KVDT, int HD, int NGW, bool G2LDS = false>
+template <int WDT, int KVDT, int HD, int NGW, bool G2LDS, bool COH>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
@@ -996,8 +1007,10 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   // registers, its K rows loaded once the first group's scores are done and its V^T rows once the
   // first group's P.V is, with an online rescale of the wave's (max, sum, acc).
   const int wv = __builtin_amdgcn_readfirstlane((wave + kWaves - 1) % kWaves);
+  // the current position's row is not read from the cache (it is written in this step): zeros,
+  // replaced from the tagged copy before use
   auto koff = [&](int p, int c) {
-    return p < t1 ? (uint32_t)(p * ROWB + (32 * c + 8 * grp4) * KES) : kOut;
+    return p < t1 && p != sc.pos ? (uint32_t)(p * ROWB + (32 * c + 8 * grp4) * KES) : kOut;
   };
   auto voff = [&](int pv, int tt) {
     return pv < t1 ? (uint32_t)((((pv >> 5) * HD + 16 * tt + col) * 32 + (pv & 31)) * KES) : kOut;
@@ -1012,14 +1025,14 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     const int pk0 = pk_of(k);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      ka[c] = kv_load8<KVDT>(kr, koff(pk0, c));
-      kb[c] = kv_load8<KVDT>(kr, koff(pk0 + 4, c));
+      ka[c] = kv_load8<KVDT, COH>(kr, koff(pk0, c));
+      kb[c] = kv_load8<KVDT, COH>(kr, koff(pk0 + 4, c));
     }
   };
   auto load_v = [&](int k) {
     const int pv = pv_of(k);
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT>(vr, voff(pv, tt));
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = kv_load8<KVDT, COH>(vr, voff(pv, tt));
   };
   auto patch_k = [&](int k) {
     const int pk0 = pk_of(k);
@@ -1063,15 +1076,16 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
   const int p1 = t0 + 32 * (wv + kWaves);  // the second group's first position
   const uint8_t* g2 = reinterpret_cast<const uint8_t*>(lds + (P.attn_g2_off < 0 ? 0 : P.attn_g2_off)) + wave * G2B;
   if (g2_lds && p1 < t1) {
+    constexpr int kPol = COH ? 16 : 2;  // sc1 : nt (as kv_load8)
 #pragma unroll
     for (int u = 0; u < G2K / 1024; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(g2 + u * 1024), 16,
-                                               (uint32_t)(p1 * ROWB + u * 1024 + lane * 16), 0, 0, 2);
+                                               (uint32_t)(p1 * ROWB + u * 1024 + lane * 16), 0, 0, kPol);
 #pragma unroll
     for (int u = 0; u < (G2B - G2K) / 1024; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(g2 + G2K + u * 1024), 16,
                                                (uint32_t)((p1 >> 5) * HD * 32 * KES + u * 1024 + lane * 16), 0,
-                                               0, 2);
+                                               0, kPol);
   }
   auto lds8 = [&](int off) -> u32x4 {  // 8 elements of the second group's buffer as 16-bit operands
     if constexpr (KVDT == WFP8) return fp8x8_bf16(*reinterpret_cast<const u32x2*>(g2 + off));
@@ -1532,26 +1546,38 @@ __device__ __forceinline__ void task_token(const KParams& P, const pmk_task& t, 
   (void)t;
 }
 
+template <int WDT, int KVDT, int NGW, bool G2LDS, bool COH>
+__device__ __forceinline__ void attn_hd(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
+                                        int cu) {
+  if (P.hd == 128) task_attn<WDT, KVDT, 128, NGW, G2LDS, COH>(P, t, ti, sc, lds, cu);
+  else task_attn<WDT, KVDT, 64, NGW, G2LDS, COH>(P, t, ti, sc, lds, cu);
+}
+
 template <int WDT, int KVDT>
 __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                          int cu) {
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
-    case PMK_OP_ATTN:
-      // splits longer than 8 groups of 32 positions give each wave a second group
-      if (((sc.pos + P.S) / P.S + 31) / 32 > kWaves) {
+    case PMK_OP_ATTN: {
+      // splits longer than 8 groups of 32 positions give each wave a second group; a split that
+      // reaches the 32-position block of this launch's first position reads coherently
+      const int T = sc.pos + 1;
+      const int chunk = ((T + P.S - 1) / P.S + 31) & ~31;
+      const bool coh = min(T, (t.a1 + 1) * chunk) > (sc.pos0 & ~31);
+      if (chunk / 32 > kWaves) {
         if (!sc.per_op && P.attn_g2_off >= 0) {
-          if (P.hd == 128) task_attn<WDT, KVDT, 128, 2, true>(P, t, ti, sc, lds, cu);
-          else task_attn<WDT, KVDT, 64, 2, true>(P, t, ti, sc, lds, cu);
+          if (coh) attn_hd<WDT, KVDT, 2, true, true>(P, t, ti, sc, lds, cu);
+          else attn_hd<WDT, KVDT, 2, true, false>(P, t, ti, sc, lds, cu);
         } else {
-          if (P.hd == 128) task_attn<WDT, KVDT, 128, 2>(P, t, ti, sc, lds, cu);
-          else task_attn<WDT, KVDT, 64, 2>(P, t, ti, sc, lds, cu);
+          if (coh) attn_hd<WDT, KVDT, 2, false, true>(P, t, ti, sc, lds, cu);
+          else attn_hd<WDT, KVDT, 2, false, false>(P, t, ti, sc, lds, cu);
         }
       } else {
-        if (P.hd == 128) task_attn<WDT, KVDT, 128, 1>(P, t, ti, sc, lds, cu);
-        else task_attn<WDT, KVDT, 64, 1>(P, t, ti, sc, lds, cu);
+        if (coh) attn_hd<WDT, KVDT, 1, false, true>(P, t, ti, sc, lds, cu);
+        else attn_hd<WDT, KVDT, 1, false, false>(P, t, ti, sc, lds, cu);
       }
       break;
+    }
     case PMK_OP_COMBINE:
       if (P.hd == 128) task_combine<128>(P, t, ti, sc, cu);
       else task_combine<64>(P, t, ti, sc, cu);
@@ -1590,9 +1616,11 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
     sc.e = e;
     sc.s = s;
     sc.pos = pos0 + s;
+    sc.pos0 = pos0;
     sc.tok = cp.forced ? cp.forced[s] : (s == 0 ? tok0 : -1);
     if (sc.tok >= P.V) sc.tok = P.V - 1;
     sc.per_op = false;
+    sc.calib = cp.calib != 0;
     for (int qi = q0; qi < q1; ++qi) {
       const int ti = P.qtasks[qi];
       const pmk_task t = P.tasks[ti];
@@ -1623,10 +1651,12 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_phase(KParams P, int first_ta
   sc.e = (int)P.ctrl[CTRL_EPOCH];
   sc.s = s;
   sc.pos = (int)P.ctrl[CTRL_POS];
+  sc.pos0 = sc.pos;  // every step is its own set of launches
   sc.tok = cp->forced ? cp->forced[s] : (int)P.ctrl[CTRL_TOKEN];
   if (sc.tok >= P.V) sc.tok = P.V - 1;
   if (sc.tok < 0) sc.tok = 0;
   sc.per_op = true;
+  sc.calib = cp->calib != 0;
   const int ti = first_task + blockIdx.x;
   const pmk_task t = P.tasks[ti];
   run_task<WDT, KVDT>(P, t, ti, sc, lds, blockIdx.x);
@@ -1673,6 +1703,22 @@ __global__ void pmk_set_pos(KParams P, int pos, const int32_t* d_token) {
   }
 }
 
+// FP8 KV scale calibration: before, every scale is 1 and every recorded maximum 0; after, each
+// (layer, kv head, K|V) scale is its recorded max |value| / 448 (1 where that maximum is 0), which
+// maps the largest calibrated value to the largest E4M3 magnitude
+__global__ void pmk_kv_calib(KParams P, int finish) {
+  const int n = P.L * P.nkv * 2;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    if (!finish) {
+      P.kv_scale[i] = 1.0f;
+      P.kv_amax[i] = 0u;
+    } else {
+      const float a = __uint_as_float(P.kv_amax[i]);
+      P.kv_scale[i] = a > 0.f ? a / 448.0f : 1.0f;
+    }
+  }
+}
+
 __global__ void pmk_copy_token(const KParams P, int32_t* dst) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *dst = (int32_t)P.ctrl[CTRL_TOKEN];
 }
@@ -1695,6 +1741,25 @@ __global__ void pmk_load_kv_rows(KParams P, const uint8_t* src_k, const uint8_t*
     const int64_t dst = ((lg * (P.seqcap / 32) + p / 32) * P.hd + d) * 32 + p % 32;
     if (es == 1) P.vc[dst] = src_v[i];
     else reinterpret_cast<uint16_t*>(P.vc)[dst] = reinterpret_cast<const uint16_t*>(src_v)[i];
+  }
+}
+
+// The inverse: positions 0..npos-1 of both caches -> canonical rows [L][nkv][npos][hd]
+__global__ void pmk_read_kv_rows(KParams P, uint8_t* dst_k, uint8_t* dst_v, int npos, int es) {
+  const int64_t rowb = (int64_t)P.hd * es;
+  const int64_t total = (int64_t)P.L * P.nkv * npos * rowb / 16;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t byte = i * 16;
+    const int64_t row = byte / rowb, off = byte % rowb;
+    const int64_t lg = row / npos, p = row % npos;
+    *reinterpret_cast<u32x4*>(dst_k + byte) = *reinterpret_cast<const u32x4*>(P.kc + (lg * P.seqcap + p) * rowb + off);
+  }
+  const int64_t nel = (int64_t)P.L * P.nkv * npos * P.hd;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nel; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t d = i % P.hd, p = (i / P.hd) % npos, lg = i / ((int64_t)P.hd * npos);
+    const int64_t src = ((lg * (P.seqcap / 32) + p / 32) * P.hd + d) * 32 + p % 32;
+    if (es == 1) dst_v[i] = P.vc[src];
+    else reinterpret_cast<uint16_t*>(dst_v)[i] = reinterpret_cast<const uint16_t*>(P.vc)[src];
   }
 }
 
@@ -1763,12 +1828,20 @@ hipError_t launch_set_pos(const KParams& P, int pos, const int32_t* d_token, hip
   hipLaunchKernelGGL(pmk_set_pos, dim3(1), dim3(64), 0, st, P, pos, d_token);
   return hipGetLastError();
 }
+hipError_t launch_kv_calib(const KParams& P, int finish, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_kv_calib, dim3(1), dim3(256), 0, st, P, finish);
+  return hipGetLastError();
+}
 hipError_t launch_copy_token(const KParams& P, int32_t* dst, hipStream_t st) {
   hipLaunchKernelGGL(pmk_copy_token, dim3(1), dim3(64), 0, st, P, dst);
   return hipGetLastError();
 }
 hipError_t launch_load_kv_rows(const KParams& P, const void* k, const void* v, int npos, int es, hipStream_t st) {
   hipLaunchKernelGGL(pmk_load_kv_rows, dim3(2048), dim3(256), 0, st, P, (const uint8_t*)k, (const uint8_t*)v, npos, es);
+  return hipGetLastError();
+}
+hipError_t launch_read_kv_rows(const KParams& P, void* k, void* v, int npos, int es, hipStream_t st) {
+  hipLaunchKernelGGL(pmk_read_kv_rows, dim3(2048), dim3(256), 0, st, P, (uint8_t*)k, (uint8_t*)v, npos, es);
   return hipGetLastError();
 }
 hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const void* wv, int nq, int nkv, int hd,

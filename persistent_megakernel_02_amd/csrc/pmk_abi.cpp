@@ -26,10 +26,12 @@ hipError_t launch_reset(const KParams& P, int n_flags, int n_counters, int pos, 
 hipError_t launch_set_pos(const KParams& P, int pos, const int32_t* d_token, hipStream_t st);
 hipError_t launch_copy_token(const KParams& P, int32_t* dst, hipStream_t st);
 hipError_t launch_load_kv_rows(const KParams& P, const void* k, const void* v, int npos, int es, hipStream_t st);
+hipError_t launch_read_kv_rows(const KParams& P, void* k, void* v, int npos, int es, hipStream_t st);
 hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const void* wv, int nq, int nkv, int hd,
                              int64_t rowb, hipStream_t st);
 hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st);
 hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st);
+hipError_t launch_kv_calib(const KParams& P, int finish, hipStream_t st);
 }  // namespace pmk
 
 using namespace pmk;
@@ -61,7 +63,7 @@ struct pmk_ctx {
   int64_t a_embed = 0, a_lm = 0, a_layers = 0, layer_bytes = 0, off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0;
   int64_t a_gains = 0, a_final = 0, a_scales = 0, sc_layer = 0, sc_off[7] = {}, a_sclm = 0, a_rope = 0;
   // workspace layout (bytes)
-  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_kvscale = 0, w_x = 0,
+  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_kvscale = 0, w_kvamax = 0, w_x = 0,
           w_xm = 0, w_q = 0, w_kvcur = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
           w_cprod = 0, w_cflag = 0;
   uint8_t* arena = nullptr;
@@ -69,6 +71,7 @@ struct pmk_ctx {
   uint8_t* ws = nullptr;
   bool bound = false, weights = false, kv_ready = false;
   int32_t pos_host = 0;
+  bool pos_exact = true;   // false after a decode call with an eos id: pos_host is then an upper bound
   int mode = PMK_MODE_MEGAKERNEL;
   int trace_on = 0;
   int xs_floats = 0;
@@ -195,6 +198,7 @@ void compute_layout(pmk_ctx* c) {
   c->w_counters = w; w = align256(w + (int64_t)s.counters.size() * 4);
   c->w_keys = w; w = align256(w + ((int64_t)m.max_seq + 1) * 8);
   c->w_kvscale = w; w = align256(w + L * m.nkv * 2 * 4);
+  c->w_kvamax = w; w = align256(w + L * m.nkv * 2 * 4);
   c->w_x = w; w = align256(w + (L + 1) * H * 8);  // (tag, value) pairs
   c->w_xm = w; w = align256(w + L * H * 8);
   c->w_q = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
@@ -290,6 +294,7 @@ void fill_params(pmk_ctx* c) {
   P.counters = reinterpret_cast<uint32_t*>(W + c->w_counters);
   P.keys = reinterpret_cast<unsigned long long*>(W + c->w_keys);
   P.kv_scale = reinterpret_cast<float*>(W + c->w_kvscale);
+  P.kv_amax = reinterpret_cast<uint32_t*>(W + c->w_kvamax);
   P.x = reinterpret_cast<unsigned long long*>(W + c->w_x);
   P.xm = reinterpret_cast<unsigned long long*>(W + c->w_xm);
   P.q = reinterpret_cast<unsigned long long*>(W + c->w_q);
@@ -337,6 +342,18 @@ pmk_status need_device(pmk_ctx* c) {
   if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
   if (!c->bound) return fail(c, PMK_ERR_NOT_BOUND, "buffers are not bound (pmk_bind)");
   HIPCHK(c, hipSetDevice(c->device));
+  return PMK_OK;
+}
+
+// After a decode call with an eos id the device's position word is the exact position: read it.
+pmk_status sync_position(pmk_ctx* c) {
+  if (c->pos_exact) return PMK_OK;
+  HIPCHK(c, hipSetDevice(c->device));
+  HIPCHK(c, hipDeviceSynchronize());
+  uint32_t pos = 0;
+  HIPCHK(c, hipMemcpy(&pos, c->ws + c->w_ctrl + CTRL_POS * 4, 4, hipMemcpyDeviceToHost));
+  c->pos_host = (int32_t)pos;
+  c->pos_exact = true;
   return PMK_OK;
 }
 
@@ -392,6 +409,24 @@ pmk_status begin_call(pmk_ctx* c, const CallParams& cp, hipStream_t st) {
   return PMK_OK;
 }
 
+pmk_status run_prefill(pmk_ctx* c, const int32_t* d_tokens, int32_t P, int calib, hipStream_t st) {
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), 0, 0, nullptr, st));
+  const int chunk = 256;
+  for (int off = 0; off < P; off += chunk) {
+    const int n = std::min(chunk, P - off);
+    CallParams cp{};
+    cp.forced = d_tokens + off;
+    cp.n_steps = n;
+    cp.eos = -1;
+    cp.calib = calib;
+    pmk_status s = begin_call(c, cp, st);
+    if (s != PMK_OK) return s;
+    s = run_steps(c, n, st);
+    if (s != PMK_OK) return s;
+  }
+  return PMK_OK;
+}
+
 pmk_status set_kv_scales(pmk_ctx* c, const float* d_kv_scales, hipStream_t st) {
   const size_t bytes = (size_t)c->m.L * c->m.nkv * 2 * 4;
   if (c->m.kvdt == PMK_DT_FP8_E4M3) {
@@ -400,6 +435,10 @@ pmk_status set_kv_scales(pmk_ctx* c, const float* d_kv_scales, hipStream_t st) {
   }
   return PMK_OK;
 }
+
+// Teacher-forced run of positions 0..P-1 from d_tokens (launches of at most 256 steps), from a
+// reset synchronisation state.
+pmk_status run_prefill(pmk_ctx* c, const int32_t* d_tokens, int32_t P, int calib, hipStream_t st);
 
 }  // namespace
 
@@ -500,13 +539,7 @@ pmk_status pmk_buffer_sizes(const pmk_ctx* c, pmk_sizes* out) {
   return PMK_OK;
 }
 
-pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
-  if (!c) return PMK_ERR_INVALID_ARG;
-  if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
-  if (!d_arena || !d_kv || !d_ws) return fail(c, PMK_ERR_INVALID_ARG, "buffers must not be NULL");
-  if (((uintptr_t)d_arena | (uintptr_t)d_kv | (uintptr_t)d_ws) & 255)
-    return fail(c, PMK_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
-  HIPCHK(c, hipSetDevice(c->device));
+static pmk_status bind_impl(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
   c->arena = (uint8_t*)d_arena;
   c->kv = (uint8_t*)d_kv;
   c->ws = (uint8_t*)d_ws;
@@ -518,6 +551,7 @@ pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
   HIPCHK(c, hipMemcpy(c->ws + c->w_cprod, c->tabs.ctr_producers.data(), c->tabs.ctr_producers.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(c->ws + c->w_cflag, c->tabs.ctr_flag_base.data(), c->tabs.ctr_flag_base.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(c, hipMemset(c->ws + c->w_kvscale, 0, (size_t)c->m.L * c->m.nkv * 2 * 4));
+  HIPCHK(c, hipMemset(c->ws + c->w_kvamax, 0, (size_t)c->m.L * c->m.nkv * 2 * 4));
   HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), 0, 0, nullptr, nullptr));
   HIPCHK(c, hipDeviceSynchronize());
   if (c->graph_exec) { (void)hipGraphExecDestroy(c->graph_exec); c->graph_exec = nullptr; }
@@ -526,7 +560,19 @@ pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
   c->weights = false;
   c->kv_ready = false;
   c->pos_host = 0;
+  c->pos_exact = true;
   return PMK_OK;
+}
+
+pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
+  if (!c) return PMK_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
+  if (!d_arena || !d_kv || !d_ws) return fail(c, PMK_ERR_INVALID_ARG, "buffers must not be NULL");
+  if (((uintptr_t)d_arena | (uintptr_t)d_kv | (uintptr_t)d_ws) & 255)
+    return fail(c, PMK_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
+  HIPCHK(c, hipSetDevice(c->device));
+  c->bound = false;
+  return bind_impl(c, d_arena, d_kv, d_ws);
 }
 
 pmk_status pmk_load_weights(pmk_ctx* c, const pmk_weight_ptrs* w, void* stream) {
@@ -590,24 +636,33 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
   if (!d_tokens || P <= 0) return fail(c, PMK_ERR_INVALID_ARG, "prefill needs P > 0 device tokens");
   if (P > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "prompt longer than max_seq");
   hipStream_t st = (hipStream_t)stream;
-  s = set_kv_scales(c, d_kv_scales, st);
-  if (s != PMK_OK) return s;
-  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), 0, 0, nullptr, st));
-  const int chunk = 256;
-  for (int off = 0; off < P; off += chunk) {
-    const int n = std::min(chunk, P - off);
-    CallParams cp{};
-    cp.forced = d_tokens + off;
-    cp.n_steps = n;
-    cp.eos = -1;
-    s = begin_call(c, cp, st);
+  if (c->m.kvdt == PMK_DT_FP8_E4M3 && !d_kv_scales) {
+    // static scales from this prompt: a calibration pass with every scale 1 records max |k|, |v|
+    // per (layer, kv head); each scale becomes that maximum / 448; then the real prefill
+    HIPCHK(c, launch_kv_calib(c->kp, 0, st));
+    s = run_prefill(c, d_tokens, P, 1, st);
     if (s != PMK_OK) return s;
-    s = run_steps(c, n, st);
+    HIPCHK(c, launch_kv_calib(c->kp, 1, st));
+  } else {
+    s = set_kv_scales(c, d_kv_scales, st);
     if (s != PMK_OK) return s;
   }
+  s = run_prefill(c, d_tokens, P, 0, st);
+  if (s != PMK_OK) return s;
   if (d_first_token) HIPCHK(c, launch_copy_token(c->kp, d_first_token, st));
   c->pos_host = P;
+  c->pos_exact = true;
   c->kv_ready = true;
+  return PMK_OK;
+}
+
+pmk_status pmk_get_kv_scales(pmk_ctx* c, float* d_out, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!d_out) return fail(c, PMK_ERR_INVALID_ARG, "d_out must not be NULL");
+  if (c->m.kvdt != PMK_DT_FP8_E4M3) return fail(c, PMK_ERR_INVALID_ARG, "only an fp8 KV cache has scales");
+  HIPCHK(c, hipMemcpyAsync(d_out, c->ws + c->w_kvscale, (size_t)c->m.L * c->m.nkv * 2 * 4, hipMemcpyDeviceToDevice,
+                           (hipStream_t)stream));
   return PMK_OK;
 }
 
@@ -624,7 +679,20 @@ pmk_status pmk_load_kv(pmk_ctx* c, const void* d_k, const void* d_v, int32_t P, 
   HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P, next_token, nullptr, st));
   if (P > 0) HIPCHK(c, launch_load_kv_rows(c->kp, d_k, d_v, P, c->kves, st));
   c->pos_host = P;
+  c->pos_exact = true;
   c->kv_ready = true;
+  return PMK_OK;
+}
+
+pmk_status pmk_read_kv(pmk_ctx* c, void* d_k, void* d_v, int32_t P, void* stream) {
+  pmk_status s = need_device(c);
+  if (s != PMK_OK) return s;
+  if (!c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "no KV state to read");
+  s = sync_position(c);
+  if (s != PMK_OK) return s;
+  if (P < 0 || P > c->pos_host) return fail(c, PMK_ERR_INVALID_ARG, "P must be within the written positions");
+  if (P > 0 && (!d_k || !d_v)) return fail(c, PMK_ERR_INVALID_ARG, "missing KV pointers");
+  if (P > 0) HIPCHK(c, launch_read_kv_rows(c->kp, d_k, d_v, P, c->kves, (hipStream_t)stream));
   return PMK_OK;
 }
 
@@ -632,6 +700,8 @@ pmk_status pmk_rewind(pmk_ctx* c, int32_t pos, const int32_t* d_token, void* str
   pmk_status s = need_device(c);
   if (s != PMK_OK) return s;
   if (!c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "no KV state to rewind");
+  s = sync_position(c);  // only positions whose KV rows were written are valid targets
+  if (s != PMK_OK) return s;
   if (pos <= 0 || pos > c->pos_host || !d_token) return fail(c, PMK_ERR_INVALID_ARG, "rewind needs 0 < pos <= position and a token");
   HIPCHK(c, launch_set_pos(c->kp, pos, d_token, (hipStream_t)stream));
   c->pos_host = pos;
@@ -644,6 +714,8 @@ pmk_status pmk_decode_n_tokens(pmk_ctx* c, int32_t n, int32_t* d_out_tokens, flo
   if (s != PMK_OK) return s;
   if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
   if (n <= 0 || !d_out_tokens) return fail(c, PMK_ERR_INVALID_ARG, "n > 0 and d_out_tokens are required");
+  s = sync_position(c);
+  if (s != PMK_OK) return s;
   if ((int64_t)c->pos_host + n > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + n exceeds max_seq");
   hipStream_t st = (hipStream_t)stream;
   CallParams cp{};
@@ -659,6 +731,7 @@ pmk_status pmk_decode_n_tokens(pmk_ctx* c, int32_t n, int32_t* d_out_tokens, flo
   s = run_steps(c, n, st);
   if (s != PMK_OK) return s;
   c->pos_host += n;
+  if (eos_id >= 0) c->pos_exact = false;  // the device stops after the eos step: it keeps the exact position
   return PMK_OK;
 }
 
@@ -668,8 +741,15 @@ pmk_status pmk_set_mode(pmk_ctx* c, int32_t mode) {
   return PMK_OK;
 }
 
-pmk_status pmk_get_position(const pmk_ctx* c, int32_t* pos) {
-  if (!c || !pos) return PMK_ERR_INVALID_ARG;
+pmk_status pmk_get_position(const pmk_ctx* cc, int32_t* pos) {
+  if (!cc || !pos) return PMK_ERR_INVALID_ARG;
+  pmk_ctx* c = const_cast<pmk_ctx*>(cc);  // the exact position may have to be read from the device
+  if (!c->pos_exact) {
+    pmk_status s = need_device(c);
+    if (s != PMK_OK) return s;
+    s = sync_position(c);
+    if (s != PMK_OK) return s;
+  }
   *pos = c->pos_host;
   return PMK_OK;
 }
@@ -767,6 +847,8 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, int32_t* kept, void* stream) {
   if (kept) *kept = 0;
   if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
   if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "tuning reads the trace: create the context with trace_steps >= 1");
+  s = sync_position(c);
+  if (s != PMK_OK) return s;
   if (steps <= 0 || steps > c->sc.trace_steps) steps = c->sc.trace_steps;
   if ((int64_t)c->pos_host + steps > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + steps exceeds max_seq");
   hipStream_t st = (hipStream_t)stream;

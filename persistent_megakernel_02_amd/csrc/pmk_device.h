@@ -34,7 +34,7 @@ struct CallParams {
   int32_t n_steps;
   int32_t eos;
   int32_t trace;
-  int32_t pad;
+  int32_t calib;  // FP8 KV: record max |k|, |v| per (layer, kv head) while the steps run (scale calibration)
 };
 
 struct KParams {
@@ -67,6 +67,7 @@ struct KParams {
   uint32_t* counters;
   unsigned long long* keys;  // [max_seq + 1]
   float* kv_scale;        // [L][nkv][2]
+  uint32_t* kv_amax;      // [L][nkv][2] calibration: fp32 bits of max |k|, |v| (non-negative: ordered as integers)
   unsigned long long* x;   // [L+1][H] residual stream entering each layer (and the final norm), tagged
   unsigned long long* xm;  // [L][H] residual after the attention block, tagged
   unsigned long long* q;      // [L][qdim] roped queries, tagged
