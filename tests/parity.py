@@ -36,16 +36,17 @@ class GpuRun:
     logits: np.ndarray      # [n][V]
     n_done: int
     seconds: float
+    kv_scales: Optional[np.ndarray] = None  # FP8 KV: the scales in force (derived by the library if none were given)
 
 
 def gpu_run(w, weights, steps: int, mode: int = 0, prompt: Optional[np.ndarray] = None, kv=None,
             next_token: int = 0, sched=None, kv_scales: Optional[np.ndarray] = None, chunks=None,
-            logits: bool = True, dec=None):
+            logits: bool = True, dec=None, max_seq: Optional[int] = None):
     import torch
     import persistent_megakernel_02_amd as pmk
     own = dec is None
     if own:
-        dec = pmk.Decoder(pmk.model_config(w), 0, sched)
+        dec = pmk.Decoder(pmk.model_config(w, max_seq), 0, sched)
         dec.load_weights(pmk.DeviceWeights(weights))
     dec.set_mode(mode)
     dev = torch.device("cuda", 0)
@@ -71,7 +72,10 @@ def gpu_run(w, weights, steps: int, mode: int = 0, prompt: Optional[np.ndarray] 
     err = dec.poll_error()
     assert err.code == 0, f"device error {err.code} cu {err.cu} task {err.task} ctr {err.counter} " \
                           f"expected {err.expected} seen {err.seen}"
-    run = GpuRun(first, np.concatenate(outs), np.concatenate(lgs) if logits else None, done, secs)
+    scales = kv_scales
+    if w.kvdtype == "fp8":
+        scales = dec.kv_scales().cpu().numpy()
+    run = GpuRun(first, np.concatenate(outs), np.concatenate(lgs) if logits else None, done, secs, scales)
     if own:
         dec.close()
     return run

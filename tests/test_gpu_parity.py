@@ -137,6 +137,17 @@ def test_tiny_eos_stops_early(tiny):
         torch.cuda.synchronize()
         assert int(nd.item()) == stop
         assert np.array_equal(toks.cpu().numpy()[:stop], ref.tokens[:stop])
+        # the position is exact after the early stop: a rewind past it is refused, and decoding on
+        # continues from it
+        assert dec.position() == len(prompt) + stop
+        tok = torch.tensor([eos], dtype=torch.int32, device="cuda")
+        with pytest.raises(pmk.PmkError):
+            dec.rewind(len(prompt) + stop + 1, tok)
+        dec.rewind(len(prompt) + stop, tok)
+        more, _, _ = dec.decode(2)
+        torch.cuda.synchronize()
+        assert dec.position() == len(prompt) + stop + 2
+        assert np.array_equal(more.cpu().numpy(), ref.tokens[stop:stop + 2])
         dec.close()
 
 
@@ -220,28 +231,190 @@ def test_split_combines_match_oracle_and_modes():
         assert np.array_equal(r.logits, runs["megakernel"].logits), name
 
 
-# ------------------------------------------------------------------------------------------------
-# workloads at their full model size: synthetic KV of the full prompt length, sampled decode steps
-# ------------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("name,steps", [("1b", 6), ("2b", 4), ("8b", 3), ("8b_fp8", 3)])
-def test_full_size_decode_from_synthetic_kv(name, steps):
-    w = WORKLOADS[name]
-    log(f"{name}: generating weights")
-    wts = synthgen.make_weights(w)
-    k, v, scales = synthgen.make_kv(w, w.prompt)
-    kv = (k, v, w.prompt)
-    nxt = int(synthgen.make_prompt(w, 1)[0])
-    log(f"{name}: GPU decode from KV {w.prompt}")
-    run = gpu_run(w, wts, steps, kv=kv, next_token=nxt, kv_scales=scales)
-    log(f"{name}: oracle {steps} steps")
-    ref, _ = oracle_teacher_forced(w, wts, run, kv=kv, kv_scales=scales)
-    check(w, run, ref, True, name)
+def _check_derived_scales(got, want):
+    """Layer 0's k and v are a function of the embedding rows alone, so its calibrated maxima agree
+    to rounding order; later layers read a cache rounded to E4M3 at scale 1 during calibration, where
+    a rounding that two correct implementations take differently moves the maxima by up to a few
+    percent, so those are checked for plausibility (the parity below uses the library's scales)."""
+    np.testing.assert_allclose(got[0], want[0], rtol=1e-4)
+    np.testing.assert_allclose(got, want, rtol=5e-2)
 
 
-def test_1b_prefill_short_prompt():
-    w = WORKLOADS["1b"].with_(prompt=24, steps=8)
-    wts = synthgen.make_weights(w)
+def test_tiny_fp8_kv_scales_derived_by_the_library():
+    """pmk_prefill_kv with no FP8 KV scales: the library calibrates them on the prompt (every scale 1,
+    max |k|, |v| per (layer, kv head), scale = max / 448).  They agree with the oracle's own
+    calibration of the same prompt, and decoding with them matches the oracle given the same scales."""
+    import oracle
+    w = TINY_FP8.with_(steps=16)
+    wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
     prompt = synthgen.make_prompt(w)
+    run = gpu_run(w, wts, w.steps, prompt=prompt, kv_scales=None)
+    cal = oracle.OracleModel(wts)
+    cal.set_kv_scales(np.ones((w.layers, w.n_kv, 2), np.float32))
+    cal.prefill(prompt)
+    want = cal.kv_scales_from_amax()
+    log(f"derived scales: gpu {run.kv_scales.ravel()[:4]} oracle {want.ravel()[:4]}")
+    assert (run.kv_scales != 1.0).all()
+    _check_derived_scales(run.kv_scales, want)
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt, kv_scales=run.kv_scales)
+    check(w, run, ref, first_ok, "tiny_fp8/derived scales")
+
+
+# ------------------------------------------------------------------------------------------------
+# the workloads as stated: full model size, the stated prompt and step counts where the oracle
+# finishes them in about a minute (1B, 2B); for the 8B models a GPU prefill of a short prompt at
+# full size, and decode from synthetic KV of nearly the full prompt length across the point where
+# the attention split grows by a 32-position group
+# ------------------------------------------------------------------------------------------------
+def _decoder(w):
+    import torch
+    import persistent_megakernel_02_amd as pmk
+    dec = pmk.Decoder(pmk.model_config(w), 0)
+    dw = pmk.DeviceWeights(synthgen_cache[w.name])
+    dec.load_weights(dw)
+    torch.cuda.synchronize()
+    del dw
+    torch.cuda.empty_cache()
+    return dec
+
+
+synthgen_cache = {}
+
+
+def _weights(w):
+    if w.name not in synthgen_cache:
+        synthgen_cache.clear()
+        log(f"{w.name}: generating weights")
+        synthgen_cache[w.name] = synthgen.make_weights(w)
+    return synthgen_cache[w.name]
+
+
+def test_1b_as_stated_prompt_512_then_128_steps():
+    """1B: GPU prefill of the 512-token random prompt, 128 greedy steps; every step's logits against
+    the oracle (teacher-forced), and the hipGraph per-op path bitwise equal to the megakernel."""
+    import persistent_megakernel_02_amd as pmk
+    w = WORKLOADS["1b"]
+    wts = _weights(w)
+    prompt = synthgen.make_prompt(w)
+    log(f"1b: prefill {w.prompt} + decode {w.steps} (megakernel)")
     run = gpu_run(w, wts, w.steps, prompt=prompt)
+    log("1b: hipGraph per-op run")
+    graph = gpu_run(w, wts, w.steps, mode=pmk.PMK_MODE_GRAPH, prompt=prompt)
+    log("1b: oracle")
     ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt)
-    check(w, run, ref, first_ok, "1b/prefill24")
+    check(w, run, ref, first_ok, "1b/as stated")
+    assert graph.first == run.first
+    assert np.array_equal(graph.tokens, run.tokens)
+    assert np.array_equal(graph.logits, run.logits)
+
+
+def test_2b_as_stated_prompt_1024_then_256_steps():
+    w = WORKLOADS["2b"]
+    wts = _weights(w)
+    prompt = synthgen.make_prompt(w)
+    log(f"2b: prefill {w.prompt} + decode {w.steps}")
+    run = gpu_run(w, wts, w.steps, prompt=prompt)
+    log("2b: oracle")
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt)
+    check(w, run, ref, first_ok, "2b/as stated")
+
+
+def _kv_excess(gpu, own, fmt):
+    """How far apart two rows of cache codes [..., hd] are, in units of what one rounding allows:
+    the spacing of the format at the larger magnitude (2^-7 of it for bf16, 2^-10 for f16, 2^-3 for
+    E4M3), plus 1e-4 of the row's RMS for values so close to zero that two correct fp32 results of
+    different rounding order land on different sides of it.  Returns (excess <= 1 everywhere is
+    within one rounding, fraction of codes that differ)."""
+    import oracle
+    f = oracle.FMT[fmt]
+    a = oracle.decode(f, np.ascontiguousarray(gpu)).astype(np.float64)
+    b = oracle.decode(f, np.ascontiguousarray(own)).astype(np.float64)
+    rel = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10, "fp8": 2.0 ** -3}[fmt]
+    rms = np.sqrt((b * b).mean(axis=-1, keepdims=True))
+    allowed = rel * np.maximum(np.abs(a), np.abs(b)) + 1e-4 * rms
+    return np.abs(a - b) / allowed, float(np.mean(gpu != own))
+
+
+def _full_size(name, kv_positions, steps, derive_scales):
+    """(1) GPU prefill of a 12-token prompt at full model size (the bench's KV capacity) and 4 decode
+    steps, every step checked from the GPU's own state: the oracle starts from the GPU's KV cache of
+    the earlier positions and appends the GPU's K/V row of the position (teacher-forced rounding, as
+    the tokens are teacher-forced); the codes it would itself have appended must be within one
+    rounding of the GPU's, the first token must pass the gap rule on the last prompt position's
+    logits, and the decode steps' logits must match within the workload's tolerance.  (2) `steps`
+    steps from synthetic KV of `kv_positions` positions (the same cache on both sides).
+
+    Why the rounding is teacher-forced at short context: both sides round the k and v they compute
+    to the cache format, and where two correct fp32 results straddle a rounding boundary they store
+    adjacent codes.  With few cached positions the step's own row carries a large attention weight,
+    so one such flip in a layer changes the next layer's k and v enough to flip others, through all
+    32 layers: two correct implementations then differ by more than the logit tolerance (on this
+    prompt the oracle's own prefill differs from an fp64 recomputation by 2.1e-2, 8B bf16).  Over
+    thousands of cached positions (part 2) a step's own row weighs little and no forcing is needed."""
+    import torch
+    import oracle
+    from tests.parity import _token_ok
+    w = WORKLOADS[name]
+    wts = _weights(w)
+    dec = _decoder(w)
+    P, N = 12, 4
+    prompt = synthgen.make_prompt(w.with_(prompt=P))
+    log(f"{name}: GPU prefill of {P} tokens (KV scales {'derived' if derive_scales else 'n/a'}) + {N} steps")
+    first = int(dec.prefill(torch.from_numpy(prompt).cuda()).item())
+    scales = dec.kv_scales().cpu().numpy() if w.kvdtype == "fp8" else None
+    toks, lg, _ = dec.decode(N, logits=True)
+    torch.cuda.synchronize()
+    toks, lg = toks.cpu().numpy(), lg.cpu().numpy()
+    gk, gv = (t.cpu().numpy() for t in dec.read_kv(P + N))
+    om = oracle.OracleModel(wts, max_seq=w.max_seq)
+    if derive_scales:
+        om.set_kv_scales(np.ones((w.layers, w.n_kv, 2), np.float32))
+        om.prefill(prompt, want_logits=False)
+        want = om.kv_scales_from_amax()
+        log(f"{name}: derived scales max rel diff: layer 0 {np.abs(scales[0] / want[0] - 1).max():.2e}, "
+            f"all {np.abs(scales / want - 1).max():.2e}")
+        _check_derived_scales(scales, want)
+    if scales is not None:
+        om.set_kv_scales(scales)
+    fmt = w.kvdtype
+    inputs = [int(t) for t in prompt] + [first] + [int(t) for t in toks[:N - 1]]
+    worst, differ, ref = 0.0, [], []
+    for p in range(P + N):
+        om.load_kv(gk[:, :, :p], gv[:, :, :p], p)
+        _, olg, own_k, own_v = om.step_forced(inputs[p], gk[:, :, p], gv[:, :, p])
+        for g_row, o_row in ((gk[:, :, p], own_k), (gv[:, :, p], own_v)):
+            ex, fr = _kv_excess(g_row, o_row, fmt)
+            worst = max(worst, float(ex.max()))
+            differ.append(fr)
+        if p == P - 1:
+            assert _token_ok(olg, first), f"{name}: prefill token {first}"
+        if p >= P:
+            ref.append(olg)
+    del om
+    log(f"{name}: appended K/V rows of {P + N} positions: {100 * np.mean(differ):.3f}% of codes differ, the "
+        f"largest difference is {worst:.3f} of one rounding")
+    assert worst <= 1.0 and np.mean(differ) <= 0.02
+    check(w, GpuRunLike(first, toks, lg), np.stack(ref), True, f"{name}/prefill {P} + {N} steps")
+    k, v, kvs = synthgen.make_kv(w, kv_positions)
+    nxt = int(synthgen.make_prompt(w, 1)[0])
+    log(f"{name}: {steps} steps from {kv_positions} synthetic KV positions")
+    run = gpu_run(w, wts, steps, kv=(k, v, kv_positions), next_token=nxt, kv_scales=kvs, dec=dec)
+    dec.close()
+    log(f"{name}: oracle {steps} steps")
+    ref, _ = oracle_teacher_forced(w, wts, run, kv=(k, v, kv_positions), kv_scales=kvs)
+    check(w, run, ref, True, f"{name}/from KV {kv_positions}")
+
+
+def GpuRunLike(first, tokens, logits):
+    from tests.parity import GpuRun
+    return GpuRun(first, tokens, logits, len(tokens), 0.0)
+
+
+def test_8b_full_size_prefill_and_decode_across_a_split_change():
+    # 32 splits per kv head: at T = 4097 a split grows from 4 to 5 groups of 32 positions
+    _full_size("8b", 4080, 40, derive_scales=False)
+
+
+def test_8b_fp8_full_size_derived_scales_and_two_groups_per_wave():
+    # 32 splits per kv head: at T = 8193 a split grows from 8 to 9 groups, so waves take two
+    _full_size("8b_fp8", 8180, 36, derive_scales=True)
