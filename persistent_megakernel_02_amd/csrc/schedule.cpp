@@ -254,7 +254,12 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
 // ================================================================================================
 namespace {
 
-enum Buf { B_X = 0, B_XM, B_Q, B_KVCUR, B_PART, B_O, B_H, B_KEY, B_TOKSLOT, B_LOGITS, B_OUT, B_COUNT };
+enum Buf { B_X = 0, B_XM, B_Q, B_KVCUR, B_PART, B_O, B_H, B_KEY, B_TOKSLOT, B_LOGITS, B_OUT, B_KV, B_COUNT };
+
+// Buffers whose every value carries the step that wrote it: their readers poll the values until the
+// tags show the step (in both sync modes), so a tagged read waits for exactly the tasks that write
+// the elements it reads.
+bool tagged_buf(int b) { return b == B_X || b == B_XM || b == B_Q || b == B_KVCUR || b == B_O; }
 enum Kind { A_READ = 0, A_WRITE = 1, A_ATOMIC = 2 };
 
 struct Access {
@@ -282,7 +287,14 @@ BufDims buf_dims(const Schedule& s, int steps) {
   d.size[B_TOKSLOT] = 1;
   d.size[B_LOGITS] = (int64_t)(steps + 1) * m.V;
   d.size[B_OUT] = steps + 1;
+  d.size[B_KV] = (int64_t)steps * m.L * m.nkv * 2 * m.hd;
   return d;
+}
+
+// KV cache: the row each step appends, as (relative step, layer, kv head, K|V, dim); step e writes
+// the position pos0 + e, and the attention of a later step reads it from the cache.
+int64_t kv_slot(const ModelDims& m, int e, int l, int g, int kv) {
+  return ((((int64_t)e * m.L + l) * m.nkv + g) * 2 + kv) * m.hd;
 }
 
 // Rows [a0, a1) of the packed QKV matrix -> element ranges written in Q (q heads) and KVCUR (k, v).
@@ -308,10 +320,13 @@ void qkv_writes(const ModelDims& m, int l, int a0, int a1, int e, std::vector<Ac
       const int64_t off = ((int64_t)l * m.nkv + head) * 2 * hd + (sec == 2 ? hd : 0);
       acc.push_back({B_KVCUR, off + p0, off + p1, A_WRITE, 0});
       acc.push_back({B_KVCUR, off + half + p0, off + half + p1, A_WRITE, 0});
+      // the same dims appended to the cache at this step's position
+      const int64_t kv = kv_slot(m, e, l, head, sec - 1);
+      acc.push_back({B_KV, kv + p0, kv + p1, A_WRITE, 0});
+      acc.push_back({B_KV, kv + half + p0, kv + half + p1, A_WRITE, 0});
     }
     r = stop;
   }
-  (void)e;
 }
 
 // Accesses of task t at global step e (e >= 0).
@@ -339,6 +354,8 @@ void task_accesses(const Schedule& s, const pmk_task& t, int e, std::vector<Acce
                      (int64_t)l * m.qdim() + (int64_t)(g + 1) * grp * m.hd, A_READ, W1});
       const int64_t kv = ((int64_t)l * m.nkv + g) * 2 * m.hd;
       acc.push_back({B_KVCUR, kv, kv + 2 * m.hd, A_READ, W1});
+      // every row the earlier steps appended (any split may hold a given position)
+      for (int e2 = 0; e2 < e; ++e2) acc.push_back({B_KV, kv_slot(m, e2, l, g, 0), kv_slot(m, e2, l, g, 0) + 2 * m.hd, A_READ, e2 + 1});
       acc.push_back({B_PART, part + t.a1, part + t.a1 + 1, A_WRITE, W1});
       break;
     }
@@ -380,9 +397,106 @@ void task_accesses(const Schedule& s, const pmk_task& t, int e, std::vector<Acce
 
 bool valid_op(int op) { return op >= PMK_OP_QKV && op <= PMK_OP_COMBINE; }
 
-// Full-count waits are the only ones that order a specific producer before the waiter.
+// What the kernel executes of a task's declared wait and signal.  In flags mode the consumers of a
+// whole step-tagged vector (QKV of layers after the first, ATTN, OPROJ, GATEUP, LMHEAD) poll the
+// tags instead of waiting, and the producers of those vectors (QKV, COMBINE, OPROJ, DOWN) publish
+// no flag; counters mode executes every declared wait and signal.
+int exec_wait(const Schedule& s, const pmk_task& t) {
+  if (s.sync_mode == PMK_SYNC_COUNTERS) return t.wait_ctr;
+  switch (t.op) {
+    case PMK_OP_QKV: return t.layer > 0 ? -1 : t.wait_ctr;
+    case PMK_OP_ATTN: case PMK_OP_OPROJ: case PMK_OP_GATEUP: case PMK_OP_LMHEAD: return -1;
+    default: return t.wait_ctr;
+  }
+}
+int exec_signal(const Schedule& s, const pmk_task& t) {
+  if (s.sync_mode == PMK_SYNC_COUNTERS) return t.signal_ctr;
+  switch (t.op) {
+    case PMK_OP_QKV: case PMK_OP_COMBINE: case PMK_OP_OPROJ: case PMK_OP_DOWN: return -1;
+    default: return t.signal_ctr;
+  }
+}
+
+// Full-count executed waits are the only counter waits that order a specific producer first.
 bool full_wait(const Schedule& s, const pmk_task& t) {
-  return t.wait_ctr >= 0 && t.wait_count == s.counters[t.wait_ctr].producers;
+  const int c = exec_wait(s, t);
+  return c >= 0 && t.wait_count == s.counters[c].producers;
+}
+
+// Is the executed wait of task t at global step e satisfied, given per-(counter, step) counts of
+// executed signals?  Counters mode: the counter (the sum over steps) reaches (e - lag) * P + t.
+// Flags mode: at least t producers have published step e - lag (producers publish in step order).
+bool wait_met(const Schedule& s, const pmk_task& t, int e, const std::vector<int64_t>& sig, int steps) {
+  const int c = exec_wait(s, t);
+  if (c < 0) return true;
+  const int target = e - t.wait_lag;
+  if (target < 0) return true;
+  if (s.sync_mode == PMK_SYNC_COUNTERS) {
+    int64_t total = 0;
+    for (int k = 0; k < steps; ++k) total += sig[(size_t)c * steps + k];
+    return total >= (int64_t)target * s.counters[c].producers + t.wait_count;
+  }
+  return sig[(size_t)c * steps + target] >= t.wait_count;
+}
+
+// The tasks that write the tagged elements each task reads (the same in every step): tagged reads
+// are grouped into lists of writers, one list per distinct (buffer, range) read.
+struct TagWaits {
+  std::vector<std::vector<int>> lists;     // writers per list
+  std::vector<std::vector<int>> of_task;   // lists each task waits on
+  std::vector<std::vector<int>> of_writer; // lists each task belongs to
+};
+
+TagWaits tag_waits(const Schedule& s) {
+  const int NT = (int)s.tasks.size();
+  struct W { int64_t lo, hi; int task; };
+  std::vector<std::vector<W>> wr(B_COUNT);
+  std::vector<Access> acc;
+  for (int t = 0; t < NT; ++t) {
+    acc.clear();
+    task_accesses(s, s.tasks[t], 1, acc);
+    for (const Access& a : acc)
+      if (tagged_buf(a.buf) && a.kind != A_READ) wr[a.buf].push_back({a.lo, a.hi, t});
+  }
+  std::vector<std::vector<int64_t>> pmax(B_COUNT);  // prefix max of hi over writes sorted by lo
+  for (int b = 0; b < B_COUNT; ++b) {
+    std::sort(wr[b].begin(), wr[b].end(), [](const W& x, const W& y) { return x.lo < y.lo; });
+    int64_t mx = INT64_MIN;
+    for (const W& w : wr[b]) { mx = std::max(mx, w.hi); pmax[b].push_back(mx); }
+  }
+  TagWaits tw;
+  tw.of_task.assign(NT, {});
+  tw.of_writer.assign(NT, {});
+  std::map<std::tuple<int, int64_t, int64_t>, int> ids;
+  for (int t = 0; t < NT; ++t) {
+    acc.clear();
+    task_accesses(s, s.tasks[t], 1, acc);
+    for (const Access& a : acc) {
+      if (!tagged_buf(a.buf) || a.kind != A_READ) continue;
+      const auto key = std::make_tuple(a.buf, a.lo, a.hi);
+      auto it = ids.find(key);
+      int id;
+      if (it == ids.end()) {
+        std::vector<int> ws;
+        const auto& v = wr[a.buf];
+        // writes with lo < hi of the read, scanned back while some earlier write may still reach lo
+        int k = (int)(std::lower_bound(v.begin(), v.end(), a.hi, [](const W& x, int64_t h) { return x.lo < h; }) -
+                      v.begin()) - 1;
+        for (; k >= 0 && pmax[a.buf][k] > a.lo; --k)
+          if (v[k].hi > a.lo) ws.push_back(v[k].task);
+        std::sort(ws.begin(), ws.end());
+        ws.erase(std::unique(ws.begin(), ws.end()), ws.end());
+        id = (int)tw.lists.size();
+        tw.lists.push_back(ws);
+        for (int w : ws) tw.of_writer[w].push_back(id);
+        ids.emplace(key, id);
+      } else {
+        id = it->second;
+      }
+      if (std::find(tw.of_task[t].begin(), tw.of_task[t].end(), id) == tw.of_task[t].end()) tw.of_task[t].push_back(id);
+    }
+  }
+  return tw;
 }
 
 }  // namespace
@@ -469,9 +583,25 @@ std::string validate_schedule(const Schedule& s) {
       return fmt("thresholds: task %ld waits for %ld signals of counter %ld which has %ld producers", t, k.wait_count, k.wait_ctr, P);
   }
   // ---- 3. deadlock freedom: monotone execution of two steps ----
+  // A task runs once its executed counter (or flag) wait is met and every task that writes the
+  // step-tagged elements it reads has run in the same step; monotone waits make any fair
+  // interleaving reach the same end state, so one greedy pass decides.
+  const int STEPS = 2;
+  const TagWaits tw = tag_waits(s);
+  const int NL = (int)tw.lists.size();
+  const int W = NQ;  // vector clock width
+  std::vector<int16_t> vc_task((size_t)STEPS * NT * W, -1);
+  std::vector<int16_t> join_ctr((size_t)STEPS * NC * W, -1);
+  std::vector<int16_t> join_list((size_t)STEPS * NL * W, -1);
+  auto vt = [&](int t, int e) { return &vc_task[((size_t)e * NT + t) * W]; };
+  auto jc = [&](int c, int e) { return &join_ctr[((size_t)e * NC + c) * W]; };
+  auto jl = [&](int k, int e) { return &join_list[((size_t)e * NL + k) * W]; };
+  auto vmax = [&](int16_t* a, const int16_t* b) { for (int i = 0; i < W; ++i) a[i] = std::max(a[i], b[i]); };
   {
-    const int STEPS = 2;
-    std::vector<int64_t> ctr(NC, 0);
+    std::vector<int64_t> sig((size_t)NC * STEPS, 0);       // executed signals per (counter, step)
+    std::vector<int> left((size_t)NL * STEPS, 0);          // writers of each tag list not yet run, per step
+    for (int k = 0; k < NL; ++k)
+      for (int e = 0; e < STEPS; ++e) left[(size_t)k * STEPS + e] = (int)tw.lists[k].size();
     std::vector<int> head(NQ, 0);  // position in the unrolled queue (step * len + i)
     bool progress = true;
     while (progress) {
@@ -479,13 +609,30 @@ std::string validate_schedule(const Schedule& s) {
       for (int q = 0; q < NQ; ++q) {
         const int len = (int)s.queues[q].size();
         while (head[q] < STEPS * len) {
-          const int e = head[q] / len;
-          const pmk_task& k = s.tasks[s.queues[q][head[q] % len]];
-          if (k.wait_ctr >= 0) {
-            const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
-            if (ctr[k.wait_ctr] < need) break;
+          const int e = head[q] / len, t = s.queues[q][head[q] % len];
+          const pmk_task& k = s.tasks[t];
+          if (!wait_met(s, k, e, sig, STEPS)) break;
+          bool tags = true;
+          for (int id : tw.of_task[t]) tags = tags && left[(size_t)id * STEPS + e] == 0;
+          if (!tags) break;
+          // vector clock: program order, the executed full wait's producers, the tag writers
+          int16_t* v = vt(t, e);
+          if (head[q] > 0) {
+            const int pt = s.queues[q][(head[q] - 1) % len], pe = (head[q] - 1) / len;
+            std::memcpy(v, vt(pt, pe), W * sizeof(int16_t));
           }
-          if (k.signal_ctr >= 0) ctr[k.signal_ctr] += 1;
+          v[q] = (int16_t)head[q];
+          if (full_wait(s, k) && e - k.wait_lag >= 0) vmax(v, jc(exec_wait(s, k), e - k.wait_lag));
+          for (int id : tw.of_task[t]) vmax(v, jl(id, e));
+          const int c = exec_signal(s, k);
+          if (c >= 0) {
+            vmax(jc(c, e), v);
+            sig[(size_t)c * STEPS + e] += 1;
+          }
+          for (int id : tw.of_writer[t]) {
+            vmax(jl(id, e), v);
+            left[(size_t)id * STEPS + e] -= 1;
+          }
           ++head[q];
           progress = true;
         }
@@ -496,55 +643,19 @@ std::string validate_schedule(const Schedule& s) {
       if (head[q] < STEPS * len) {
         const int t = s.queues[q][head[q] % len];
         const pmk_task& k = s.tasks[t];
+        const int e = head[q] / len;
         std::ostringstream os;
-        os << "deadlock: queue " << q << " stalls at step " << head[q] / len << " on task " << t << " (" << op_name(k.op)
-           << " waits on counter " << k.wait_ctr << " for " << k.wait_count << " signals, lag " << k.wait_lag << ")";
+        os << "deadlock: queue " << q << " stalls at step " << e << " on task " << t << " (" << op_name(k.op);
+        if (!wait_met(s, k, e, sig, STEPS))
+          os << " waits on counter " << exec_wait(s, k) << " for " << k.wait_count << " signals, lag " << k.wait_lag
+             << (s.sync_mode == PMK_SYNC_COUNTERS ? "" : ", flags") << ")";
+        else
+          os << " polls step-tagged data that a task which has not run writes)";
         return os.str();
       }
     }
   }
-  // ---- 4/5. happens-before over two unrolled steps (vector clocks) ----
-  // Nodes: tasks (t, e) on queue q at unrolled index e*len(q)+i.
-  const int W = NQ;  // vector clock width
-  const int STEPS = 2;
-  // topological processing: simulate again, computing clocks as tasks complete
-  std::vector<int16_t> vc_task((size_t)STEPS * NT * W, -1);
-  std::vector<int16_t> join_ctr((size_t)STEPS * NC * W, -1);
-  auto vt = [&](int t, int e) { return &vc_task[((size_t)e * NT + t) * W]; };
-  auto jc = [&](int c, int e) { return &join_ctr[((size_t)e * NC + c) * W]; };
-  auto vmax = [&](int16_t* a, const int16_t* b) { for (int i = 0; i < W; ++i) a[i] = std::max(a[i], b[i]); };
-  {
-    std::vector<int64_t> ctr(NC, 0);
-    std::vector<int> head(NQ, 0);
-    bool progress = true;
-    while (progress) {
-      progress = false;
-      for (int q = 0; q < NQ; ++q) {
-        const int len = (int)s.queues[q].size();
-        while (head[q] < STEPS * len) {
-          const int e = head[q] / len, i = head[q] % len, t = s.queues[q][i];
-          const pmk_task& k = s.tasks[t];
-          if (k.wait_ctr >= 0) {
-            const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
-            if (ctr[k.wait_ctr] < need) break;
-          }
-          int16_t* v = vt(t, e);
-          if (head[q] > 0) {
-            const int pt = s.queues[q][(head[q] - 1) % len], pe = (head[q] - 1) / len;
-            std::memcpy(v, vt(pt, pe), W * sizeof(int16_t));
-          }
-          v[q] = (int16_t)head[q];
-          if (full_wait(s, k) && e - k.wait_lag >= 0) vmax(v, jc(k.wait_ctr, e - k.wait_lag));
-          if (k.signal_ctr >= 0) {
-            vmax(jc(k.signal_ctr, e), v);
-            ctr[k.signal_ctr] += 1;
-          }
-          ++head[q];
-          progress = true;
-        }
-      }
-    }
-  }
+  // ---- 4/5. happens-before over the two unrolled steps (the vector clocks above) ----
   // node identity for hb queries
   struct Node { int queue, index; const int16_t* vc; };
   auto task_node = [&](int t, int e) { return Node{queue_of[t], e * (int)s.queues[queue_of[t]].size() + pos_of[t], vt(t, e)}; };
@@ -562,8 +673,8 @@ std::string validate_schedule(const Schedule& s) {
     }
   for (int t = 0; t < NT; ++t) {
     const pmk_task& k = s.tasks[t];
-    if (k.wait_ctr < 0 || full_wait(s, k)) continue;
-    // partial wait: does this task read anything that producers of the waited counter write?
+    if (exec_wait(s, k) < 0 || full_wait(s, k)) continue;
+    // executed partial wait: does this task read anything that producers of the waited counter write?
     tmp.clear();
     task_accesses(s, k, 1, tmp);
     std::vector<Access> prod;
@@ -573,7 +684,7 @@ std::string validate_schedule(const Schedule& s) {
       task_accesses(s, pk, 1 - k.wait_lag, prod);
     }
     for (auto& r : tmp)
-      if (r.kind == A_READ)
+      if (r.kind == A_READ && !tagged_buf(r.buf))  // a tagged read waits for its own writers
         for (auto& w : prod)
           if (w.kind != A_READ && w.buf == r.buf && w.lo < r.hi && r.lo < w.hi)
             return fmt("join: task %ld reads a region that %ld producers of counter %ld write but waits for only %ld of them",
@@ -655,9 +766,10 @@ std::string validate_schedule(const Schedule& s) {
         }
       }
   }
-  // monotonic counters: every signal of step e+1 follows every signal of step e on the same counter
+  // monotonic counters: every executed signal of step e+1 follows every one of step e on a counter
   for (int c = 0; c < NC; ++c) {
     for (int t1 : producers[c]) {
+      if (exec_signal(s, s.tasks[t1]) < 0) continue;
       const Node n1 = task_node(t1, 1);
       for (int t0 : producers[c])
         if (!hb(task_node(t0, 0), n1))
@@ -690,8 +802,9 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
     stamps[b].reset(new std::atomic<int32_t>[bd.size[b]]);
     for (int64_t i = 0; i < bd.size[b]; ++i) stamps[b][i].store(b == B_TOKSLOT ? 0 : -1);  // -1 = poison
   }
-  std::unique_ptr<std::atomic<int64_t>[]> ctr(new std::atomic<int64_t>[NC]);
-  for (int c = 0; c < NC; ++c) ctr[c].store(0);
+  // executed signals per (counter, step): counters mode sums them, flags mode counts one step's
+  std::unique_ptr<std::atomic<int64_t>[]> sig(new std::atomic<int64_t>[(size_t)NC * steps]);
+  for (size_t c = 0; c < (size_t)NC * steps; ++c) sig[c].store(0);
   std::atomic<bool> abort_flag{false};
   std::mutex mu;
   std::string first_error;
@@ -701,12 +814,44 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
     if (status == PMK_OK) { status = st; first_error = msg; }
     abort_flag.store(true);
   };
-  auto run_accesses = [&](std::mt19937_64& rng, const std::vector<Access>& acc, int e, bool writes, const char* what,
+  auto met = [&](const pmk_task& k, int e) {
+    const int c = exec_wait(s, k);
+    if (c < 0) return true;
+    const int target = e - k.wait_lag;
+    if (target < 0) return true;
+    if (s.sync_mode == PMK_SYNC_COUNTERS) {
+      int64_t tot = 0;
+      for (int x = 0; x < steps; ++x) tot += sig[(size_t)c * steps + x].load();
+      return tot >= (int64_t)target * s.counters[c].producers + k.wait_count;
+    }
+    return sig[(size_t)c * steps + target].load() >= k.wait_count;
+  };
+  const auto t_start = std::chrono::steady_clock::now();
+  auto stuck = [&](const std::chrono::steady_clock::time_point& t0) {
+    return std::chrono::steady_clock::now() - t0 > std::chrono::seconds(5);
+  };
+  // reads of tagged buffers poll until the element shows this step's stamp (a later step's stamp
+  // means it was overwritten before this read: a race); other reads must see it at once
+  auto run_accesses = [&](std::mt19937_64& rng, const std::vector<Access>& acc, int e, int phase, const char* what,
                           int task) {
     for (const Access& a : acc) {
-      if (a.kind == A_READ && !writes) {
+      if (a.kind == A_READ && phase != 1) {
         for (int64_t i = a.lo; i < a.hi; ++i) {
-          const int32_t st = stamps[a.buf][i].load();
+          int32_t st = stamps[a.buf][i].load();
+          if (phase == 0 && tagged_buf(a.buf) && st < a.expect) {
+            const auto t0 = std::chrono::steady_clock::now();
+            while ((st = stamps[a.buf][i].load()) < a.expect) {
+              if (abort_flag.load()) return;
+              std::this_thread::yield();
+              if (stuck(t0)) {
+                std::ostringstream os;
+                os << "deadlock: " << what << " task " << task << " at step " << e << " polled buffer " << a.buf << "[" << i
+                   << "] for 5 s (stamp " << st << ", expected " << a.expect << ")";
+                fail(PMK_ERR_TIMEOUT, os.str());
+                return;
+              }
+            }
+          }
           if (st != a.expect) {
             std::ostringstream os;
             os << "race: " << what << " task " << task << " at step " << e << " read buffer " << a.buf << "[" << i
@@ -716,7 +861,7 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
           }
           if ((rng() & 63) == 0) std::this_thread::yield();
         }
-      } else if (a.kind != A_READ && writes) {
+      } else if (a.kind != A_READ && phase == 1) {
         for (int64_t i = a.lo; i < a.hi; ++i) {
           stamps[a.buf][i].store(a.expect);
           if ((rng() & 63) == 0) std::this_thread::yield();
@@ -731,35 +876,34 @@ pmk_status simulate_schedule(const Schedule& s, int steps, uint64_t seed, std::s
     for (int e = 0; e < steps && !abort_flag.load(); ++e) {
       for (int t : queue) {
         const pmk_task& k = s.tasks[t];
-        if (k.wait_ctr >= 0) {
-          const int64_t need = (int64_t)(e - k.wait_lag) * s.counters[k.wait_ctr].producers + k.wait_count;
-          auto t0 = std::chrono::steady_clock::now();
-          while (ctr[k.wait_ctr].load() < need) {
-            if (abort_flag.load()) return;
-            std::this_thread::yield();
-            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(5)) {
-              std::ostringstream os;
-              os << "deadlock: queue " << q << " waited 5 s at step " << e << " on counter " << k.wait_ctr << " (" << op_name(k.op)
-                 << " task " << t << ", has " << ctr[k.wait_ctr].load() << ", needs " << need << ")";
-              fail(PMK_ERR_TIMEOUT, os.str());
-              return;
-            }
+        const auto t0 = std::chrono::steady_clock::now();
+        while (!met(k, e)) {
+          if (abort_flag.load()) return;
+          std::this_thread::yield();
+          if (stuck(t0)) {
+            std::ostringstream os;
+            os << "deadlock: queue " << q << " waited 5 s at step " << e << " on counter " << exec_wait(s, k) << " ("
+               << op_name(k.op) << " task " << t << ")";
+            fail(PMK_ERR_TIMEOUT, os.str());
+            return;
           }
         }
         acc.clear();
         task_accesses(s, k, e, acc);
-        run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads at start
+        run_accesses(rng, acc, e, 0, op_name(k.op), t);  // reads at start (tagged ones poll)
         if ((rng() & 3) == 0) std::this_thread::yield();
-        run_accesses(rng, acc, e, true, op_name(k.op), t);   // writes
-        run_accesses(rng, acc, e, false, op_name(k.op), t);  // reads again: catches WAR
+        run_accesses(rng, acc, e, 1, op_name(k.op), t);  // writes
+        run_accesses(rng, acc, e, 2, op_name(k.op), t);  // reads again: catches WAR
         if (abort_flag.load()) return;
-        if (k.signal_ctr >= 0) ctr[k.signal_ctr].fetch_add(1);
+        const int c = exec_signal(s, k);
+        if (c >= 0) sig[(size_t)c * steps + e].fetch_add(1);
       }
     }
   };
   std::vector<std::thread> th;
   for (int q = 0; q < NQ; ++q) th.emplace_back(worker, q);
   for (auto& t : th) t.join();
+  (void)t_start;
   *report = first_error;
   return status;
 }

@@ -134,15 +134,49 @@ def test_simulator_runs_real_lowerings_clean(n_cus):
 # ------------------------------------------------------------------------------------------------
 # mutation corpus
 # ------------------------------------------------------------------------------------------------
-def mutants(w, n_cus, rng, per_kind):
-    """Yield (kind, mutate(sched)) pairs; every mutant is unsafe by construction."""
-    base = Sched(w, n_cus)
+# What the kernel executes (mirrored from the task functions): the readers of step-tagged vectors
+# (QKV of layers after the first, ATTN, OPROJ, GATEUP, LMHEAD) poll the tags in both sync modes, so
+# their counter wait only adds ordering; in flags mode they do not execute it at all, and the
+# producers of those vectors (QKV, COMBINE, OPROJ, DOWN) publish no flag.
+def tag_reader(t):
+    return (t.op == 1 and t.layer > 0) or t.op in (2, 3, 4, 6)
+
+
+def exec_wait(t, mode):
+    if mode == pmk.PMK_SYNC_FLAGS and tag_reader(t):
+        return -1
+    return t.wait_ctr
+
+
+def exec_signal(t, mode):
+    if mode == pmk.PMK_SYNC_FLAGS and t.op in (1, 8, 3, 5):
+        return -1
+    return t.signal_ctr
+
+
+def qkv_groups(w, t):
+    """kv groups whose q, k or v rows a QKV task writes."""
+    hd, qd, kvd, grp = w.head_dim, w.n_q * w.head_dim, w.n_kv * w.head_dim, w.n_q // w.n_kv
+    gs = set()
+    for r in range(t.a0, t.a1):
+        gs.add((r // hd) // grp if r < qd else ((r - qd) // hd if r < qd + kvd else (r - qd - kvd) // hd))
+    return gs
+
+
+def mutants(w, n_cus, rng, per_kind, mode=pmk.PMK_SYNC_FLAGS):
+    """Yield (kind, mutate(sched)) pairs; every mutant is unsafe by construction in `mode`."""
+    base = Sched(w, n_cus, sync_mode=mode)
     NT, NQ = base.n_tasks, base.n_queues
     tasks = [base.task(i) for i in range(NT)]
     q0 = set(base.queue(0))
-    # the first QKV tasks on the queue that ends with the TOKEN task are already ordered after the
-    # previous step's LM head by program order, so their wait is redundant (dropping it is safe)
-    waiting = [i for i, t in enumerate(tasks) if t.wait_ctr >= 0 and not (t.op == 1 and t.layer == 0 and i in q0)]
+    # waits that protect data read without a tag: the first layer's QKV (the token of the previous
+    # step), COMBINE (attention partials), DOWN (h), TOKEN (the step's key).  The first QKV tasks on
+    # the queue that ends with the TOKEN task are already ordered after the previous step's LM head
+    # by program order, so their wait is redundant (dropping it is safe)
+    waiting = [i for i, t in enumerate(tasks) if exec_wait(t, mode) >= 0 and not tag_reader(t)
+               and not (t.op == 1 and t.layer == 0 and i in q0)]
+    declared = [i for i, t in enumerate(tasks) if t.wait_ctr >= 0]
+    executed = [i for i, t in enumerate(tasks) if exec_wait(t, mode) >= 0]
     # tasks whose queue already joined the same counter earlier in the step (lag 0, full count):
     # their own wait is redundant, so weakening it is safe
     joined_before = set()
@@ -152,7 +186,7 @@ def mutants(w, n_cus, rng, per_kind):
             t = tasks[i]
             if t.wait_ctr >= 0 and t.wait_ctr in seen:
                 joined_before.add(i)
-            if t.wait_ctr >= 0 and t.wait_lag == 0 and t.wait_count == base.producers(t.wait_ctr):
+            if exec_wait(t, mode) >= 0 and t.wait_lag == 0 and t.wait_count == base.producers(t.wait_ctr):
                 seen.add(t.wait_ctr)
     # tasks whose counter's producers all run earlier on their own queue (one attention split per
     # kv head: the combine after it): program order already orders them, so the wait is redundant
@@ -173,6 +207,8 @@ def mutants(w, n_cus, rng, per_kind):
     signalling = [i for i, t in enumerate(tasks) if t.signal_ctr >= 0]
     full = [i for i in waiting if tasks[i].wait_count == base.producers(tasks[i].wait_ctr)
             and base.producers(tasks[i].wait_ctr) > 1]
+    # counters whose producers publish nothing in this mode (flags: QKV, COMBINE, OPROJ, DOWN)
+    flagless = sorted({t.signal_ctr for t in tasks if t.signal_ctr >= 0 and exec_signal(t, mode) < 0})
 
     def drop_wait(s, i):      # the task reads data other queues produce in the same (or previous) step
         t = s.task(i); t.wait_ctr = -1; s.set_task(i, t)
@@ -180,7 +216,7 @@ def mutants(w, n_cus, rng, per_kind):
     def lower_threshold(s, i):  # join incomplete: a reader of a multi-producer region waits for fewer
         t = s.task(i); t.wait_count = max(1, t.wait_count - 1 - rng.randrange(t.wait_count - 1 or 1)); s.set_task(i, t)
 
-    def raise_threshold(s, i):  # never satisfiable
+    def raise_threshold(s, i):  # never satisfiable (and outside 1 <= t <= producers)
         t = s.task(i); t.wait_count = s.producers(t.wait_ctr) + 1 + rng.randrange(3); s.set_task(i, t)
 
     def zero_threshold(s, i):
@@ -189,12 +225,27 @@ def mutants(w, n_cus, rng, per_kind):
     def wrong_lag(s, i):        # waits for the previous step's producers: reads stale data
         t = s.task(i); t.wait_lag = 1 - t.wait_lag; s.set_task(i, t)
 
-    def back_edge(s, i):        # waits on a counter produced later in the same step (by its dependants;
-        t = s.task(i)           # another kv head's attention splits do not depend on an ATTN task)
+    def back_edge(s, i):        # an executed wait on a counter produced later in the same step (by its
+        t = s.task(i)           # dependants; another kv head's attention splits do not depend on it)
         own = max(t.signal_ctr, t.wait_ctr if t.wait_lag == 0 else -1)
+
+        def dependant(j):       # in flags mode an attention split polls only its own group's q, k, v
+            a = tasks[j]
+            if t.op == 2 and a.op == 2:
+                return False
+            if mode == pmk.PMK_SYNC_FLAGS and t.op == 1 and a.op == 2 and a.layer == t.layer:
+                return a.a0 in qkv_groups(w, t)
+            return True
         later = sorted({tasks[j].signal_ctr for j in signalling
-                        if tasks[j].signal_ctr > own and not (t.op == 2 and tasks[j].op == 2)})
+                        if tasks[j].signal_ctr > own and exec_signal(tasks[j], mode) >= 0 and dependant(j)})
         t.wait_ctr = rng.choice(later)
+        t.wait_lag = 0
+        t.wait_count = s.producers(t.wait_ctr)
+        s.set_task(i, t)
+
+    def flagless_wait(s, i):    # flags mode: an executed wait on a counter whose producers publish no
+        t = s.task(i)           # flag never ends, wherever program order already puts its producers
+        t.wait_ctr = rng.choice(flagless)
         t.wait_lag = 0
         t.wait_count = s.producers(t.wait_ctr)
         s.set_task(i, t)
@@ -233,12 +284,28 @@ def mutants(w, n_cus, rng, per_kind):
             t.a1 = t.a0
         s.set_task(i, t)
 
-    def swap_queue(s, q):       # a task moved before the task whose signal it needs (its full-count
-        lst = s.queue(q)        # wait then includes a producer queued behind it: deadlock)
-        pairs = [k for k in range(len(lst) - 1)
-                 if tasks[lst[k + 1]].wait_ctr >= 0 and tasks[lst[k + 1]].wait_ctr == tasks[lst[k]].signal_ctr
-                 and tasks[lst[k + 1]].wait_lag == 0
-                 and tasks[lst[k + 1]].wait_count == base.producers(tasks[lst[k + 1]].wait_ctr)]
+    def depends(c, p):
+        """Does task c wait, in this mode, for task p of the same step (executed full wait on p's
+        executed signal, or a tagged read of what p writes)?"""
+        tc, tp = tasks[c], tasks[p]
+        if exec_wait(tc, mode) >= 0 and tc.wait_ctr == exec_signal(tp, mode) and tc.wait_lag == 0 \
+                and tc.wait_count == base.producers(tc.wait_ctr):
+            return True
+        if tc.op == 2 and tp.op == 1 and tp.layer == tc.layer:      # q, k, v of its group
+            return tc.a0 in qkv_groups(w, tp)
+        if tc.op == 4 and tp.op == 3 and tp.layer == tc.layer:      # all of xm
+            return True
+        if tc.op == 3 and tp.op == 8 and tp.layer == tc.layer:      # all of o
+            return True
+        if tc.op == 1 and tp.op == 5 and tp.layer == tc.layer - 1:  # all of x
+            return True
+        if tc.op == 6 and tp.op == 5 and tp.layer == w.layers - 1:
+            return True
+        return False
+
+    def swap_queue(s, q):       # a task moved before a task it waits for: deadlock
+        lst = s.queue(q)
+        pairs = [k for k in range(len(lst) - 1) if depends(lst[k + 1], lst[k])]
         if not pairs:
             lst = lst + lst[:1]  # duplicate entry: integrity
         else:
@@ -254,10 +321,13 @@ def mutants(w, n_cus, rng, per_kind):
 
     kinds = [("drop_wait", drop_wait, weakenable),
              ("lower_threshold", lower_threshold, [i for i in full if i not in joined_before]),
-             ("raise_threshold", raise_threshold, waiting), ("zero_threshold", zero_threshold, waiting),
-             ("wrong_lag", wrong_lag, weakenable), ("back_edge", back_edge, [i for i in waiting if tasks[i].op not in (6, 7)]),
+             ("raise_threshold", raise_threshold, declared), ("zero_threshold", zero_threshold, declared),
+             ("wrong_lag", wrong_lag, weakenable),
+             ("back_edge", back_edge, [i for i in executed if tasks[i].op not in (6, 7)]),
              ("drop_signal", drop_signal, signalling), ("remove_producer", remove_producer, signalling),
              ("shared_slot", shared_slot, signalling), ("alias_rows", alias_rows, signalling)]
+    if mode == pmk.PMK_SYNC_FLAGS and flagless:
+        kinds.append(("flagless_wait", flagless_wait, executed))
     for kind, fn, sites in kinds:
         for i in rng.sample(sites, min(per_kind, len(sites))):
             yield kind, (lambda s, fn=fn, i=i: fn(s, i))
@@ -267,14 +337,15 @@ def mutants(w, n_cus, rng, per_kind):
             yield kind, (lambda s, fn=fn, q=q: fn(s, q))
 
 
-def test_mutation_corpus_has_no_false_accepts():
-    rng = random.Random(20260609)
+@pytest.mark.parametrize("mode", [pmk.PMK_SYNC_FLAGS, pmk.PMK_SYNC_COUNTERS], ids=["flags", "counters"])
+def test_mutation_corpus_has_no_false_accepts(mode):
+    rng = random.Random(20260609 + mode)
     total, by_kind, accepted = 0, {}, []
     for name, n_cus, per_kind in (("tiny", 4, 40), ("tiny", 8, 40), ("tiny", 32, 20), ("1b", 16, 10),
                                   ("tiny_split_combine", 256, 10)):
         w = SPLIT_COMBINE if name == "tiny_split_combine" else WORKLOADS[name]
-        for kind, mutate in mutants(w, n_cus, rng, per_kind):
-            s = Sched(w, n_cus)
+        for kind, mutate in mutants(w, n_cus, rng, per_kind, mode):
+            s = Sched(w, n_cus, sync_mode=mode)
             mutate(s)
             st, msg = s.validate()
             total += 1
@@ -286,10 +357,71 @@ def test_mutation_corpus_has_no_false_accepts():
     assert not accepted, f"false accepts: {accepted[:10]}"
 
 
+def _counter_of(s, op, layer):
+    for i in range(s.n_tasks):
+        t = s.task(i)
+        if t.op == op and t.layer == layer and t.signal_ctr >= 0:
+            return t.signal_ctr
+    raise AssertionError((op, layer))
+
+
+def test_flags_mode_rejects_a_wait_the_counter_model_accepts():
+    """A combine retargeted to wait for all QKV tasks of its layer (which on two queues all run
+    before it, with its attention split ahead of it on its own queue): with counters every such wait
+    completes and the schedule is safe; in flags mode QKV tasks publish no flag, so the combine would
+    wait forever: the validator models what each mode runs and rejects only the flags schedule."""
+    results = {}
+    for mode in (pmk.PMK_SYNC_COUNTERS, pmk.PMK_SYNC_FLAGS):
+        s = Sched(WORKLOADS["tiny"], 2, sync_mode=mode)
+        for i in range(s.n_tasks):
+            t = s.task(i)
+            if t.op == 8:
+                t.wait_ctr = _counter_of(s, 1, t.layer)
+                t.wait_count = s.producers(t.wait_ctr)
+                s.set_task(i, t)
+        results[mode] = s.validate()
+        if mode == pmk.PMK_SYNC_FLAGS:
+            assert s.simulate(steps=2)[0] == _lib.PMK_ERR_TIMEOUT
+        else:
+            assert s.simulate(steps=2) == (0, "")
+    assert results[pmk.PMK_SYNC_COUNTERS] == (0, ""), results
+    st, msg = results[pmk.PMK_SYNC_FLAGS]
+    assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith("deadlock"), msg
+
+
+def test_attention_ahead_of_another_groups_qkv_is_safe_only_with_flags():
+    """An attention task of kv group g moved ahead of a QKV task (on its queue) that writes only
+    another group's rows: with counters the attention waits for every QKV task, including that one
+    (deadlock); with flags it polls only its own group's q, k and v, so the schedule is safe."""
+    w = WORKLOADS["tiny"].with_(name="tiny_4kv", n_q=8, n_kv=4)
+    for mode, want in ((pmk.PMK_SYNC_COUNTERS, "deadlock"), (pmk.PMK_SYNC_FLAGS, "")):
+        s = Sched(w, 4, sync_mode=mode)
+        done = False
+        for q in range(s.n_queues):
+            lst = s.queue(q)
+            for k in range(len(lst) - 1):
+                a, b = s.task(lst[k]), s.task(lst[k + 1])
+                if a.op == 1 and b.op == 2 and a.layer == b.layer and b.a0 not in qkv_groups(w, a):
+                    lst[k], lst[k + 1] = lst[k + 1], lst[k]
+                    s.set_queue(q, lst)
+                    done = True
+                    break
+            if done:
+                break
+        assert done
+        st, msg = s.validate()
+        if want:
+            assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith(want), msg
+        else:
+            assert st == 0, msg
+            assert s.simulate(steps=3) == (0, "")
+
+
 def test_swapping_across_a_dependency_is_a_deadlock():
     s = Sched(WORKLOADS["tiny"], 4)
     q = s.queue(0)
-    # the queue's ATTN(0) waits for all QKV(0) tasks, including this queue's own, which now follows it
+    # the queue's ATTN(0) polls q and the current K/V of its group, which this queue's own QKV task
+    # writes; that task now follows it
     i_qkv = next(k for k, t in enumerate(q) if s.task(t).op == 1)
     i_attn = next(k for k, t in enumerate(q) if s.task(t).op == 2)
     q[i_qkv], q[i_attn] = q[i_attn], q[i_qkv]
@@ -302,8 +434,9 @@ def test_swapping_across_a_dependency_is_a_deadlock():
 
 def test_simulator_catches_a_race_the_validator_rejects():
     s = Sched(WORKLOADS["tiny"], 16)
-    gu = [i for i in range(s.n_tasks) if s.task(i).op == 4 and s.task(i).layer == 0]
-    for i in gu:
+    # the down projections no longer wait for the gate/up tasks whose h they read
+    dn = [i for i in range(s.n_tasks) if s.task(i).op == 5 and s.task(i).layer == 0]
+    for i in dn:
         t = s.task(i)
         t.wait_ctr = -1
         s.set_task(i, t)
@@ -311,6 +444,24 @@ def test_simulator_catches_a_race_the_validator_rejects():
     assert st == _lib.PMK_ERR_SCHEDULE_INVALID and msg.startswith("race"), msg
     caught = [s.simulate(steps=2, seed=k) for k in range(5)]
     assert any(st == _lib.PMK_ERR_SCHEDULE_INVALID and "race" in m for st, m in caught), caught
+
+
+def test_kv_cache_rows_are_checked():
+    """The KV cache is part of the access model: dropping the QKV task that appends a kv head's V
+    rows leaves the next step's attention reading a row no task wrote (coverage)."""
+    s = Sched(WORKLOADS["tiny"], 8)
+    w = WORKLOADS["tiny"]
+    qd, kvd = w.n_q * w.head_dim, w.n_kv * w.head_dim
+    for i in range(s.n_tasks):
+        t = s.task(i)
+        if t.op == 1 and t.layer == 0 and t.a0 >= qd + kvd:  # a task of V rows only
+            t.a1 = t.a0  # empty
+            s.set_task(i, t)
+            break
+    else:
+        raise AssertionError("no V-only QKV task")
+    st, msg = s.validate()
+    assert st == _lib.PMK_ERR_SCHEDULE_INVALID, msg
 
 
 def test_weighted_row_splits_are_accepted_and_proportional():
@@ -339,3 +490,25 @@ def test_weighted_row_splits_are_accepted_and_proportional():
         for r, x in zip(rows, wts):
             assert abs(r - total * x / sum(wts)) <= 1.5
         lib.pmk_schedule_free(h)
+
+
+def test_simulator_under_thread_sanitizer(tmp_path):
+    """The host simulator, built with g++ under ThreadSanitizer, runs clean and failing schedules in
+    both sync modes without a data-race report (its shared stamps and counters are atomics)."""
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "sim_tsan")
+    build = subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-pthread",
+                            os.path.join(root, "persistent_megakernel_02_amd", "csrc", "schedule.cpp"),
+                            os.path.join(root, "tests", "tsan_simulate.cpp"), "-o", exe],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=300,
+                         env=dict(os.environ, TSAN_OPTIONS="halt_on_error=1"))
+    out = run.stdout + run.stderr
+    assert "ThreadSanitizer" not in out, out[-3000:]
+    assert run.returncode == 0, out[-3000:]
