@@ -205,6 +205,20 @@ pmk_status pmk_buffer_sizes(const pmk_ctx* ctx, pmk_sizes* out);
  * (device-less context), PMK_ERR_HIP.  Weights and KV state must be loaded again after a bind. */
 pmk_status pmk_bind(pmk_ctx* ctx, void* d_arena, void* d_kv, void* d_workspace);
 
+/* pmk_bind for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is the library's own static device
+ * array of at most 32 MiB per device (held by each device that loads the library until the process
+ * ends), so only the arena and the KV cache are the caller's.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); like pmk_bind it uploads the schedule tables
+ * and clears the synchronisation state, so nothing of an earlier user of the array carries over.
+ * One context per device at a time: a later pmk_bind_static_workspace on the same device takes the
+ * array over, and device calls on the context that held it before then fail with
+ * PMK_ERR_NOT_BOUND; calls of two contexts on one device's array that overlap in time race.
+ * Errors: PMK_ERR_CAPACITY (the schedule's workspace exceeds the array: larger models or a trace
+ * ring need pmk_bind), PMK_ERR_INVALID_ARG, PMK_ERR_NOT_BOUND (device-less context),
+ * PMK_ERR_DEVICE, PMK_ERR_HIP. */
+pmk_status pmk_bind_static_workspace(pmk_ctx* ctx, void* d_arena, void* d_kv);
+
 /* Repack the canonical tensors into the arena (QKV rows concatenated with each RoPE pair made
  * adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table).
  * Passages: [Netra] details (weight layout and FP8 E4M3 block-scale semantics are fixed ahead of

@@ -78,7 +78,7 @@ class Decoder:
     """One library context: caller-owned buffers (torch uint8 tensors), weights, KV state."""
 
     def __init__(self, cfg: pmk_model_config, device: int = 0, sched: Optional[pmk_schedule_config] = None,
-                 allocate: bool = True):
+                 allocate: bool = True, static_workspace: bool = False):
         import torch
         self.lib = load()
         self.cfg = cfg
@@ -94,8 +94,13 @@ class Decoder:
             dev = torch.device("cuda", device)
             self._arena_raw, self.arena = _aligned_empty(s.arena_bytes, dev)
             self._kv_raw, self.kv = _aligned_empty(s.kv_bytes, dev)
-            self._ws_raw, self.ws = _aligned_empty(s.workspace_bytes, dev)
-            check(self.lib.pmk_bind(ctx, self.arena.data_ptr(), self.kv.data_ptr(), self.ws.data_ptr()), ctx)
+            if static_workspace:
+                # the workspace is the library's static device array: no allocation for it here
+                self.ws = None
+                check(self.lib.pmk_bind_static_workspace(ctx, self.arena.data_ptr(), self.kv.data_ptr()), ctx)
+            else:
+                self._ws_raw, self.ws = _aligned_empty(s.workspace_bytes, dev)
+                check(self.lib.pmk_bind(ctx, self.arena.data_ptr(), self.kv.data_ptr(), self.ws.data_ptr()), ctx)
 
     def close(self):
         if getattr(self, "ctx", None):

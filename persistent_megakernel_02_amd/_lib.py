@@ -78,6 +78,7 @@ SIGNATURES = {
     "pmk_destroy": (None, [vp]),
     "pmk_buffer_sizes": (i32, [vp, ctypes.POINTER(pmk_sizes)]),
     "pmk_bind": (i32, [vp, vp, vp, vp]),
+    "pmk_bind_static_workspace": (i32, [vp, vp, vp]),
     "pmk_load_weights": (i32, [vp, ctypes.POINTER(pmk_weight_ptrs), vp]),
     "pmk_prefill_kv": (i32, [vp, vp, i32, vp, vp, vp]),
     "pmk_get_kv_scales": (i32, [vp, vp, vp]),

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "pmk_device.h"
 
@@ -1793,6 +1794,31 @@ __global__ void pmk_repack_gu(uint8_t* dst, const uint8_t* wg, const uint8_t* wu
 __global__ void pmk_widen(float* dst, const uint16_t* src, int n, int bf16) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = bf16 ? dec16<WBF16>(src[i]) : dec16<WF16>(src[i]);
+}
+
+// ------------------------------------------------------------------------------------------------
+// static workspace, for callers that cannot allocate device memory
+// ------------------------------------------------------------------------------------------------
+// One array per device (each device that loads this library holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel or a copy (on the host it names a
+// stand-in, not device memory): it takes the device address from hipGetSymbolAddress, once per
+// device, with that device current, and uses that address from then on.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace_address(int device, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -32,6 +33,7 @@ hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const
 hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st);
 hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st);
 hipError_t launch_kv_calib(const KParams& P, int finish, hipStream_t st);
+hipError_t static_workspace_address(int device, void** out);
 }  // namespace pmk
 
 using namespace pmk;
@@ -70,6 +72,7 @@ struct pmk_ctx {
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
   bool bound = false, weights = false, kv_ready = false;
+  bool ws_static = false;  // the workspace is the device's static array (pmk_bind_static_workspace)
   int32_t pos_host = 0;
   bool pos_exact = true;   // false after a decode call with an eos id: pos_host is then an upper bound
   int mode = PMK_MODE_MEGAKERNEL;
@@ -337,10 +340,27 @@ void compute_phases(pmk_ctx* c) {
   }
 }
 
+// The context bound to each device's static workspace (one at a time: a later bind takes it over).
+std::mutex g_static_mu;
+pmk_ctx* g_static_owner[kMaxDevices] = {};
+
+bool owns_static(const pmk_ctx* c) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  return c->device >= 0 && c->device < kMaxDevices && g_static_owner[c->device] == c;
+}
+
+void release_static(pmk_ctx* c) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (c->device >= 0 && c->device < kMaxDevices && g_static_owner[c->device] == c) g_static_owner[c->device] = nullptr;
+  c->ws_static = false;
+}
+
 pmk_status need_device(pmk_ctx* c) {
   if (!c) return PMK_ERR_INVALID_ARG;
   if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
   if (!c->bound) return fail(c, PMK_ERR_NOT_BOUND, "buffers are not bound (pmk_bind)");
+  if (c->ws_static && !owns_static(c))
+    return fail(c, PMK_ERR_NOT_BOUND, "another context has since bound this device's static workspace; bind again");
   HIPCHK(c, hipSetDevice(c->device));
   return PMK_OK;
 }
@@ -526,6 +546,7 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
 
 void pmk_destroy(pmk_ctx* c) {
   if (!c) return;
+  release_static(c);
   if (c->device >= 0) (void)hipSetDevice(c->device);
   if (c->graph_exec) (void)hipGraphExecDestroy(c->graph_exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
@@ -571,8 +592,32 @@ pmk_status pmk_bind(pmk_ctx* c, void* d_arena, void* d_kv, void* d_ws) {
   if (((uintptr_t)d_arena | (uintptr_t)d_kv | (uintptr_t)d_ws) & 255)
     return fail(c, PMK_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
   HIPCHK(c, hipSetDevice(c->device));
+  release_static(c);
   c->bound = false;
   return bind_impl(c, d_arena, d_kv, d_ws);
+}
+
+pmk_status pmk_bind_static_workspace(pmk_ctx* c, void* d_arena, void* d_kv) {
+  if (!c) return PMK_ERR_INVALID_ARG;
+  if (c->sizes.workspace_bytes > kStaticWorkspaceBytes)
+    return fail(c, PMK_ERR_CAPACITY,
+                "this schedule's workspace needs " + std::to_string(c->sizes.workspace_bytes) +
+                    " bytes; the static workspace holds at most " + std::to_string(kStaticWorkspaceBytes) +
+                    " (use pmk_bind with a caller-allocated workspace, or a schedule without a trace ring)");
+  if (c->device < 0) return fail(c, PMK_ERR_NOT_BOUND, "context was created without a device");
+  if (c->device >= kMaxDevices) return fail(c, PMK_ERR_DEVICE, "device index beyond the static workspace table");
+  if (!d_arena || !d_kv) return fail(c, PMK_ERR_INVALID_ARG, "buffers must not be NULL");
+  if (((uintptr_t)d_arena | (uintptr_t)d_kv) & 255) return fail(c, PMK_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
+  HIPCHK(c, hipSetDevice(c->device));
+  void* ws = nullptr;
+  HIPCHK(c, static_workspace_address(c->device, &ws));
+  {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    g_static_owner[c->device] = c;  // a context bound before loses it (its device calls then fail)
+  }
+  c->ws_static = true;
+  c->bound = false;
+  return bind_impl(c, d_arena, d_kv, ws);
 }
 
 pmk_status pmk_load_weights(pmk_ctx* c, const pmk_weight_ptrs* w, void* stream) {

@@ -12,6 +12,10 @@ constexpr int kThreads = 512;   // one workgroup per CU: 8 wave64s (2 per SIMD)
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 
+// The static workspace (pmk_bind_static_workspace): bytes per device, and devices supported.
+constexpr size_t kStaticWorkspaceBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+
 // control words (workspace, uint32) -------------------------------------------------------------
 enum Ctrl : int {
   CTRL_EPOCH = 0,    // global decode steps since the last reset (counters / flags are relative to it)

@@ -41,12 +41,12 @@ class GpuRun:
 
 def gpu_run(w, weights, steps: int, mode: int = 0, prompt: Optional[np.ndarray] = None, kv=None,
             next_token: int = 0, sched=None, kv_scales: Optional[np.ndarray] = None, chunks=None,
-            logits: bool = True, dec=None, max_seq: Optional[int] = None):
+            logits: bool = True, dec=None, max_seq: Optional[int] = None, static_workspace: bool = False):
     import torch
     import persistent_megakernel_02_amd as pmk
     own = dec is None
     if own:
-        dec = pmk.Decoder(pmk.model_config(w, max_seq), 0, sched)
+        dec = pmk.Decoder(pmk.model_config(w, max_seq), 0, sched, static_workspace=static_workspace)
         dec.load_weights(pmk.DeviceWeights(weights))
     dec.set_mode(mode)
     dev = torch.device("cuda", 0)
