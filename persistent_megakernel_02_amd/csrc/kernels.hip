@@ -1353,7 +1353,7 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
 // O projection + residual: xm[r] = x[r] + Wo[r].o  (residual rows staged in LDS with the input)
 template <int WDT>
 __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
-                                           int cu) {
+                                           int cu, bool tile_copied = false) {
   constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
   const int l = t.layer, K = P.qdim, R = t.a1 - t.a0;
   // compact LDS layout (o, residual rows, partial sums, results) below the LDS tile area
@@ -1384,7 +1384,7 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
   const float* const so = fp8_rows<WDT>(P, l, 3);
   auto srow = [=](int r) -> const float* { return so + (int64_t)(r / 128) * nbc; };
   if (oproj_tile_in_lds(P, t, sc, (K / WFmt<WDT>::EPL + 63) >> 6)) {
-    tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, kOprojRowCost);
+    if (!tile_copied) tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, kOprojRowCost);
     gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, yp, y, sync, srow, kOprojRowCost);
   } else
     gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow, kOprojRowCost);
@@ -1554,9 +1554,23 @@ __device__ __forceinline__ void attn_hd(const KParams& P, const pmk_task& t, int
   else task_attn<WDT, KVDT, 64, NGW, G2LDS, COH>(P, t, ti, sc, lds, cu);
 }
 
+// An O-projection task that follows a COMBINE on the same queue has its LDS tile copied by the
+// combine, before the combine's wait: the combine uses no LDS, and otherwise the copy would start
+// only once the combine ends, which put those queues' O projections last on the chip's critical path.
+template <int WDT>
+__device__ __forceinline__ bool copy_next_oproj_tile(const KParams& P, const StepCtx& sc, int next_ti, int layer,
+                                                     float* lds) {
+  if (next_ti < 0) return false;
+  const pmk_task tn = P.tasks[next_ti];
+  const int K = P.qdim, nsl = (K / WFmt<WDT>::EPL + 63) >> 6;
+  if (tn.op != PMK_OP_OPROJ || tn.layer != layer || !oproj_tile_in_lds(P, tn, sc, nsl)) return false;
+  tile_to_lds<WDT>(P.wbase + (int64_t)layer * P.layer_bytes + P.off_o, K, tn.a0, tn.a1, lds + P.pf_off, kOprojRowCost);
+  return true;
+}
+
 template <int WDT, int KVDT>
 __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
-                                         int cu) {
+                                         int cu, int next_ti = -1, int* otile = nullptr) {
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_ATTN: {
@@ -1580,10 +1594,14 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
       break;
     }
     case PMK_OP_COMBINE:
+      if (otile && copy_next_oproj_tile<WDT>(P, sc, next_ti, t.layer, lds)) *otile = next_ti;
       if (P.hd == 128) task_combine<128>(P, t, ti, sc, cu);
       else task_combine<64>(P, t, ti, sc, cu);
       break;
-    case PMK_OP_OPROJ: task_oproj<WDT>(P, t, ti, sc, lds, cu); break;
+    case PMK_OP_OPROJ:
+      task_oproj<WDT>(P, t, ti, sc, lds, cu, otile && *otile == ti);
+      if (otile) *otile = -1;
+      break;
     case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_DOWN: task_down<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_LMHEAD: task_lmhead<WDT>(P, t, ti, sc, lds, cu); break;
@@ -1606,6 +1624,10 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
   const int tok0 = (int)P.ctrl[CTRL_TOKEN];
   const int q0 = P.qoff[cu], q1 = P.qoff[cu + 1];
   const int lm_ctr = P.tasks[P.qtasks[P.qoff[1] - 1]].wait_ctr;  // queue 0 ends with the TOKEN task
+  // the trace records which XCD (hardware XCC id) ran each queue, for XCD-aware row shares
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  const uint64_t who = ((uint64_t)(xcc & 0xfu) << 32) | (uint32_t)cu;
   int steps = 0;
   for (int s = 0; s < cp.n_steps; ++s) {
     const int e = epoch0 + s;
@@ -1622,13 +1644,14 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
     if (sc.tok >= P.V) sc.tok = P.V - 1;
     sc.per_op = false;
     sc.calib = cp.calib != 0;
+    int otile = -1;  // task whose O-projection tile this CU has already copied to LDS
     for (int qi = q0; qi < q1; ++qi) {
       const int ti = P.qtasks[qi];
       const pmk_task t = P.tasks[ti];
       trace_mark(P, s, ti, 0, __builtin_amdgcn_s_memrealtime());
-      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu);
+      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu, qi + 1 < q1 ? P.qtasks[qi + 1] : -1, &otile);
       trace_mark(P, s, ti, 2, __builtin_amdgcn_s_memrealtime());
-      trace_mark(P, s, ti, 3, (uint64_t)cu);
+      trace_mark(P, s, ti, 3, who);
     }
     steps = s + 1;
   }
