@@ -41,17 +41,77 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, bytes_per_launch_steps: int):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source; else None."""
+def traffic_from_profile(workload: str, algorithmic_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (calibrated FETCH_SIZE +
+    WRITE_SIZE of a profiled launch, over that launch's algorithmic bytes), scaled to this launch's
+    algorithmic bytes; None if the summary is missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_persistent_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_hash") != kernel_source_hash() or d.get("steps") != bytes_per_launch_steps:
+    if d.get("kernel_hash") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return round(d["hbm_bytes_per_launch"] / d["algorithmic_bytes_per_launch"] * algorithmic_bytes)
+
+
+def cpu_baseline(w, wts, dec, P):
+    """The oracle as it stands on the host's cores, on a bounded sample of the same workload:
+    teacher-forced decode steps from the synthetic KV of the bench's prompt length (timed without
+    loading the KV), a prefill of a few prompt tokens, and 1-thread decode figures for the tiny and
+    ~1B workloads.  The decode steps also give the bench line a parity check against the GPU."""
+    import numpy as np
+    import oracle
+    import synthgen
+    from tests.parity import check, gpu_run
+    sample = 2 if w.hidden >= 4096 else 4
+    k, v, sc = synthgen.make_kv(w, P)
+    nxt = int(synthgen.make_prompt(w, 1)[0])
+    run = gpu_run(w, wts, sample, kv=(k, v, P), next_token=nxt, kv_scales=sc, dec=dec)
+    om = oracle.OracleModel(wts)
+    if sc is not None:
+        om.set_kv_scales(sc)
+    om.load_kv(k, v, P)
+    del k, v
+    ref, inp = [], run.first
+    t0 = time.time()
+    for i in range(sample):
+        _, lg = om.step(inp)
+        ref.append(lg)
+        inp = int(run.tokens[i])
+    dsecs = time.time() - t0
+    md = check(w, run, np.stack(ref), True, f"bench/{w.name}")
+    npre = 16 if w.hidden >= 4096 else 64
+    om2 = oracle.OracleModel(wts, max_seq=npre)
+    if sc is not None:
+        om2.set_kv_scales(sc)
+    t0 = time.time()
+    om2.prefill(synthgen.make_prompt(w, npre), want_logits=False)
+    psecs = time.time() - t0
+    del om, om2
+    threads = oracle.num_threads()
+    one = {}
+    oracle.set_num_threads(1)
+    try:
+        for name, n in (("tiny", 8), ("1b", 2)):
+            ws = synthgen.WORKLOADS[name]
+            wt = wts if name == w.name else synthgen.make_weights(ws)
+            m = oracle.OracleModel(wt)
+            m.prefill(synthgen.make_prompt(ws), want_logits=False)
+            t0 = time.time()
+            tok = 0
+            for _ in range(n):
+                tok, _ = m.step(tok, want_logits=False)
+            one[name] = round(n / (time.time() - t0), 3)
+            del m, wt
+    finally:
+        oracle.set_num_threads(threads)
+    cpu = {"value": round(sample / dsecs, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{sample} teacher-forced decode steps of the full {w.name} model from {P} synthetic KV "
+                     f"positions (KV load not timed); prefill of {npre} prompt tokens timed apart; 1-thread decode of "
+                     f"the tiny and ~1B workloads after their stated prompts; fp32 accumulation",
+           "prefill_tokens_per_s": round(npre / psecs, 3), "one_thread_tokens_per_s": one}
+    return cpu, md
 
 
 def main():
@@ -66,9 +126,9 @@ def main():
     ap.add_argument("--no-graph-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--no-tune", dest="tune", action="store_false",
-                    help="keep the even GEMV row split (default: before the timed launch, pmk_tune twice re-splits the "
-                         "gate/up rows by the streaming rate each CU measured in traced warm-up steps and keeps a "
-                         "re-split only if those steps then run faster)")
+                    help="keep the default schedule (default: before the timed launch, pmk_tune searches the schedule "
+                         "knobs and speed-weighted row shares, keeping a change only if it passes the correctness gate "
+                         "and runs faster)")
     ap.add_argument("--repeat", type=int, default=3,
                     help="timed launches of K steps each (from the same position); value is the median one")
     ap.add_argument("--kernel-only", action="store_true",
@@ -99,6 +159,8 @@ def main():
     log(f"[bench] weights generated in {time.time() - t_setup:.1f}s; uploading")
     sync_mode = pmk.PMK_SYNC_COUNTERS if args.sync == "counters" else pmk.PMK_SYNC_FLAGS
     trace_steps = 0 if args.no_trace and not args.tune else 8
+    if args.kernel_only:
+        trace_steps = 0  # profiled runs time only the launches
     dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(sync_mode=sync_mode, trace_steps=trace_steps))
     dw = pmk.DeviceWeights(wts)
     dec.load_weights(dw)
@@ -142,14 +204,18 @@ def main():
         dec.decode(W, out_tokens=out_tokens, n_done=n_done)
         torch.cuda.synchronize()
         dec.rewind(P, first_tok)
-    tune_kept = 0
+    tune = None
     if args.tune:
         t_tune = time.time()
-        for _ in range(2):
-            tune_kept += int(dec.tune(trace_steps))
+        r = dec.tune(32)
         torch.cuda.synchronize()
-        log(f"[bench] tuned the GEMV row split in {time.time() - t_tune:.2f}s: {tune_kept} of 2 re-splits kept "
-            f"(schedule {dec.schedule_info().hash:#018x})")
+        tune = {"kept": r.desc.decode(), "candidates": r.tried, "accepted": r.kept, "gate_rejected": r.gate_rejected,
+                "invalid": r.invalid, "us_per_step_default": round(r.us_before, 2),
+                "us_per_step_tuned": round(r.us_after, 2), "gain": round(r.us_before / r.us_after, 4),
+                "attn_splits": r.chosen.attn_splits, "combine_parts": r.chosen.combine_parts,
+                "combine_o_share": r.chosen.combine_o_share}
+        log(f"[bench] tuning search in {time.time() - t_tune:.1f}s: {r.tried} candidates, kept [{tune['kept']}], "
+            f"{r.us_before:.1f} -> {r.us_after:.1f} us/step (schedule {dec.schedule_info().hash:#018x})")
     stream = torch.cuda.current_stream()
     times = []
     for r in range(max(1, args.repeat)):
@@ -209,23 +275,11 @@ def main():
     # ---- oracle CPU baseline on a bounded sample (+ parity of those steps) ----
     cpu = None
     if not args.no_cpu_baseline and not args.kernel_only:
-        import oracle
-        from tests.parity import check, gpu_run, oracle_teacher_forced
-        sample = 2 if w.hidden >= 4096 else 4
-        k, v, sc = synthgen.make_kv(w, P)
-        nxt = int(synthgen.make_prompt(w, 1)[0])
-        run = gpu_run(w, wts, sample, kv=(k, v, P), next_token=nxt, kv_scales=sc, dec=dec)
-        t0 = time.time()
-        ref, _ = oracle_teacher_forced(w, wts, run, kv=(k, v, P), kv_scales=sc)
-        osecs = time.time() - t0
-        md = check(w, run, ref, True, f"bench/{w.name}")
-        cpu = {"value": round(sample / osecs, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{sample} teacher-forced decode steps of the full {w.name} model from {P} synthetic KV "
-                         f"positions (including the oracle's KV load), fp32 accumulation"}
+        cpu, md = cpu_baseline(w, wts, dec, P)
         extra["parity_max_abs_logit_diff"] = float(f"{md:.3e}")
         extra["parity"] = "pass"
 
-    traffic = traffic_from_profile(w.name, K)
+    traffic = traffic_from_profile(w.name, bytes_launch)
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -242,8 +296,7 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "hidden": w.hidden, "heads": [w.n_q, w.n_kv],
                    "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "prompt": P, "decode_steps": K,
                    "batch": 1, "mode": args.mode, "sync": args.sync, "parallelism": "single GPU",
-                   "row_split": ("tuned (gate/up)" if tune_kept else "even (tuned split measured slower)")
-                   if args.tune else "even"},
+                   "tuning": tune if tune else "off (default schedule)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
@@ -253,7 +306,11 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+    # release the device buffers and the context before the interpreter exits
     dec.close()
+    del dec, out_tokens, n_done, first, first_tok, prompt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

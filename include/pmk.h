@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PMK_ABI_VERSION 1
+#define PMK_ABI_VERSION 2
 
 typedef enum {
   PMK_OK = 0,
@@ -111,6 +111,12 @@ typedef struct {
                            1: the register loads only; -1: every weight load after the wait */
   int32_t trace_steps;  /* steps kept in the per-task trace ring (default 0 = no trace buffer) */
   int64_t spin_limit;   /* polls before a wait gives up and aborts the launch (default 1<<22) */
+  int32_t combine_parts;    /* COMBINE tasks per kv head, each over a range of its q heads (a divisor of
+                               n_q_heads / n_kv_heads; default: the fewest that keep one combine's partials
+                               under ~33 KiB while the O-projection tiles still fit in LDS) */
+  int32_t combine_o_share;  /* O-projection rows on the queues that run a COMBINE: 0 automatic, 1 none,
+                               2 half a share, 3 a full share */
+  int32_t reserved[6];      /* must be 0 */
 } pmk_schedule_config;
 
 typedef struct {
@@ -318,22 +324,37 @@ pmk_status pmk_set_trace(pmk_ctx* ctx, int32_t on);
 pmk_status pmk_trace_export(pmk_ctx* ctx, const char* json_path);
 pmk_status pmk_trace_stats(pmk_ctx* ctx, double* wait_share, double* step_us);
 
-/* Speed-weighted row split (tuning).  Runs `steps` decode steps (<= the trace ring; <= 0: all of
- * it) from the current position with the megakernel and tracing on, measures every queue's
- * gate/up weight-streaming rate from the trace, rebuilds the schedule with each gate/up task's
- * row share moved half-way from even toward proportional to its queue's rate (compute units of a
- * device do not always stream at one rate: the split evens out when they finish the phase; the
- * other GEMV phases keep the even split), validates and installs it, and runs the same steps from
- * the same state again.  The new split is kept only if their mean traced step time is lower;
- * otherwise the split in force before the call is reinstalled.  *kept (may be NULL) receives 1 if
- * the new split was kept, else 0.  The position and next input token the call started from are
- * restored (the KV rows it wrote past that position are rewritten by the next decode).
- * Synchronous on `stream`.  Requires bound weights and KV state and a context created with
- * trace_steps >= 1.  Row assignment never changes a row's arithmetic beyond the grouping of its
- * partial sums.  Passage: [AMK] Autoresearch loop (propose a ScheduleConfig change, validate it,
- * time it, keep it or revert).  Errors: PMK_ERR_NOT_BOUND, PMK_ERR_INVALID_ARG (no trace ring),
- * PMK_ERR_CAPACITY, PMK_ERR_SCHEDULE_INVALID, PMK_ERR_HIP. */
-pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, int32_t* kept, void* stream);
+/* Result of pmk_tune. */
+typedef struct {
+  int32_t tried;          /* candidate schedules built */
+  int32_t kept;           /* candidates kept (each faster than the best before it by more than 0.2%) */
+  int32_t gate_rejected;  /* candidates whose outputs failed the correctness gate */
+  int32_t invalid;        /* candidates the validator, the workspace capacity or LDS refused */
+  double us_before;       /* µs per step of the measured steps on the schedule in force before */
+  double us_after;        /* the same on the schedule chosen */
+  pmk_schedule_config chosen;  /* the knobs in force after tuning (combine_parts, attn_splits resolved) */
+  char desc[232];         /* the changes kept, e.g. "gate/up rows per XCD x1.0; combine_o_share 3" */
+} pmk_tune_result;
+
+/* Schedule tuning: a keep-or-revert search over the ScheduleConfig knobs and the GEMV row shares.
+ * Passage: [AMK] Autoresearch loop (propose a ScheduleConfig change, validate it, check correctness
+ * against a reference, time it, keep it or revert) and Results (tuned schedules over the default
+ * configuration).  From the current position and next input token, the schedule in force is timed
+ * on `steps` megakernel steps (default 32, at most 64; HIP events, after an untimed pass of the same
+ * steps from the same state); then, one at a time, candidates are built, validated (Safety Gate),
+ * installed and timed the same way: gate/up and down row shares weighted by the streaming rate each
+ * queue measured in a traced run (grouped per queue or per XCD, the XCD id each workgroup read from
+ * the hardware, moved fully or half-way from even), the O-projection rows on the combine queues
+ * (none, half, full), the combines per kv head and fewer attention splits.  A candidate is kept if
+ * it emits the same greedy token at every measured step as the starting schedule, with the same
+ * largest logit within 1e-3 (a schedule change only regroups partial sums), and is faster than the
+ * best so far by more than 0.2%; otherwise the best schedule is reinstalled.  Rate-based candidates
+ * need a context created with trace_steps >= 2.  Every schedule change clears the synchronisation
+ * state; the position and next token are restored (KV rows past the position are rewritten by the
+ * next decode).  Synchronous on `stream`.  *result may be NULL.  Errors: PMK_ERR_NOT_BOUND,
+ * PMK_ERR_CAPACITY (position + steps > max_seq), PMK_ERR_SCHEDULE_INVALID, PMK_ERR_HIP, or a
+ * device error of a measured run. */
+pmk_status pmk_tune(pmk_ctx* ctx, int32_t steps, pmk_tune_result* result, void* stream);
 
 /* Schedule inspection (host only, also for device-less contexts).  Passage: [Netra] details
  * (deterministic engine artifacts: the schedule hash is reproducible across runs).

@@ -13,7 +13,8 @@ from typing import Optional
 from . import _lib
 from ._lib import (PMK_DT_BF16, PMK_DT_F16, PMK_DT_FP8_E4M3, PMK_MODE_GRAPH, PMK_MODE_MEGAKERNEL,  # noqa: F401
                    PMK_MODE_PER_OP, PMK_SYNC_COUNTERS, PMK_SYNC_FLAGS, PmkError, check, load, pmk_device_error,
-                   pmk_model_config, pmk_schedule_config, pmk_schedule_info, pmk_sizes, pmk_task, pmk_weight_ptrs)
+                   pmk_model_config, pmk_schedule_config, pmk_schedule_info, pmk_sizes, pmk_task, pmk_tune_result,
+                   pmk_weight_ptrs)
 
 _DT = {"f16": PMK_DT_F16, "bf16": PMK_DT_BF16, "fp8": PMK_DT_FP8_E4M3}
 
@@ -27,8 +28,10 @@ def model_config(w, max_seq: Optional[int] = None) -> pmk_model_config:
 
 
 def schedule_config(n_cus: int = 0, sync_mode: int = PMK_SYNC_FLAGS, attn_splits: int = 0, prefetch: int = 0,
-                    trace_steps: int = 0, spin_limit: int = 0) -> pmk_schedule_config:
-    return pmk_schedule_config(n_cus, sync_mode, attn_splits, prefetch, trace_steps, spin_limit)
+                    trace_steps: int = 0, spin_limit: int = 0, combine_parts: int = 0,
+                    combine_o_share: int = 0) -> pmk_schedule_config:
+    return pmk_schedule_config(n_cus, sync_mode, attn_splits, prefetch, trace_steps, spin_limit, combine_parts,
+                               combine_o_share)
 
 
 def _stream(stream=None) -> int:
@@ -188,13 +191,13 @@ class Decoder:
         check(self.lib.pmk_trace_stats(self.ctx, ctypes.byref(a), ctypes.byref(b)), self.ctx)
         return a.value, b.value
 
-    def tune(self, steps: int = 0, stream=None) -> bool:
-        """Measure each compute unit's gate/up streaming rate over `steps` traced decode steps,
-        rebuild the schedule with speed-weighted row shares and keep it only if the same steps then
-        run faster (position and next token restored).  Returns whether the new split was kept."""
-        kept = ctypes.c_int32(0)
-        check(self.lib.pmk_tune(self.ctx, steps, ctypes.byref(kept), _stream(stream)), self.ctx)
-        return bool(kept.value)
+    def tune(self, steps: int = 0, stream=None) -> pmk_tune_result:
+        """Keep-or-revert search over the schedule's knobs and GEMV row shares (pmk_tune): each
+        candidate is validated, gated on the greedy tokens and largest logits of `steps` measured
+        steps, timed, and kept only if faster.  Position and next token are restored."""
+        r = pmk_tune_result()
+        check(self.lib.pmk_tune(self.ctx, steps, ctypes.byref(r), _stream(stream)), self.ctx)
+        return r
 
     def trace_export(self, path: str):
         check(self.lib.pmk_trace_export(self.ctx, path.encode()), self.ctx)

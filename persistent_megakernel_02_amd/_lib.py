@@ -40,7 +40,7 @@ class pmk_model_config(ctypes.Structure):
 
 class pmk_schedule_config(ctypes.Structure):
     _fields_ = [("n_cus", i32), ("sync_mode", i32), ("attn_splits", i32), ("prefetch", i32), ("trace_steps", i32),
-                ("spin_limit", i64)]
+                ("spin_limit", i64), ("combine_parts", i32), ("combine_o_share", i32), ("reserved", i32 * 6)]
 
 
 class pmk_sizes(ctypes.Structure):
@@ -60,6 +60,11 @@ class pmk_device_error(ctypes.Structure):
 class pmk_schedule_info(ctypes.Structure):
     _fields_ = [("n_tasks", i32), ("n_counters", i32), ("n_cus", i32), ("attn_splits", i32),
                 ("max_tasks_per_cu", i32), ("sync_mode", i32), ("hash", u64)]
+
+
+class pmk_tune_result(ctypes.Structure):
+    _fields_ = [("tried", i32), ("kept", i32), ("gate_rejected", i32), ("invalid", i32), ("us_before", ctypes.c_double),
+                ("us_after", ctypes.c_double), ("chosen", pmk_schedule_config), ("desc", ctypes.c_char * 232)]
 
 
 class pmk_task(ctypes.Structure):
@@ -90,7 +95,7 @@ SIGNATURES = {
     "pmk_get_position": (i32, [vp, ctypes.POINTER(i32)]),
     "pmk_poll_error": (i32, [vp, ctypes.POINTER(pmk_device_error)]),
     "pmk_set_trace": (i32, [vp, i32]),
-    "pmk_tune": (i32, [vp, i32, vp, vp]),
+    "pmk_tune": (i32, [vp, i32, ctypes.POINTER(pmk_tune_result), vp]),
     "pmk_trace_export": (i32, [vp, ctypes.c_char_p]),
     "pmk_trace_stats": (i32, [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "pmk_schedule_get_info": (i32, [vp, ctypes.POINTER(pmk_schedule_info)]),

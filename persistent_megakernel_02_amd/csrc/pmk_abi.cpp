@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <map>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -43,6 +44,8 @@ namespace {
 thread_local std::string g_err;
 
 int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+constexpr int kMaxTuneSteps = 64;  // steps of one measured run of the tuning search
 int64_t nblk(int64_t n) { return (n + 127) / 128; }
 
 struct Phase {
@@ -65,7 +68,7 @@ struct pmk_ctx {
   int64_t a_embed = 0, a_lm = 0, a_layers = 0, layer_bytes = 0, off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0;
   int64_t a_gains = 0, a_final = 0, a_scales = 0, sc_layer = 0, sc_off[7] = {}, a_sclm = 0, a_rope = 0;
   // workspace layout (bytes)
-  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_kvscale = 0, w_kvamax = 0, w_x = 0,
+  int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_tune = 0, w_kvscale = 0, w_kvamax = 0, w_x = 0,
           w_xm = 0, w_q = 0, w_kvcur = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
           w_cprod = 0, w_cflag = 0;
   uint8_t* arena = nullptr;
@@ -91,6 +94,10 @@ struct pmk_ctx {
   std::vector<float> rope_host;
   uint64_t hash = 0;
   RowWeights rw;  // per-queue GEMV row shares set by pmk_tune (empty: even split)
+  // workspace capacity, fixed at creation: schedules the tuner installs later (other combine parts,
+  // O shares, fewer attention splits) must fit it, so no buffer moves when a schedule changes
+  int64_t cap_flags = 0, cap_tasks = 0;
+  int cap_splits = 0;
 };
 
 namespace {
@@ -193,20 +200,21 @@ void compute_layout(pmk_ctx* c) {
   c->sizes.kv_bytes = 2 * align256((int64_t)L * m.nkv * seqcap_of(m) * m.hd * c->kves);
 
   const Schedule& s = c->sched;
-  const int64_t NT = (int64_t)s.tasks.size();
+  const int64_t NT = std::max<int64_t>(c->cap_tasks, (int64_t)s.tasks.size());
   int64_t w = 0;
   c->w_ctrl = w; w = align256(w + CTRL_WORDS * 4);
   c->w_call = w; w = align256(w + sizeof(CallParams));
-  c->w_flags = w; w = align256(w + (int64_t)s.n_flags * 4);
+  c->w_flags = w; w = align256(w + std::max<int64_t>(c->cap_flags, s.n_flags) * 4);
   c->w_counters = w; w = align256(w + (int64_t)s.counters.size() * 4);
-  c->w_keys = w; w = align256(w + ((int64_t)m.max_seq + 1) * 8);
+  c->w_keys = w; w = align256(w + ((int64_t)std::max(m.max_seq, kMaxTuneSteps) + 1) * 8);
+  c->w_tune = w; w = align256(w + (int64_t)kMaxTuneSteps * 4);
   c->w_kvscale = w; w = align256(w + L * m.nkv * 2 * 4);
   c->w_kvamax = w; w = align256(w + L * m.nkv * 2 * 4);
   c->w_x = w; w = align256(w + (L + 1) * H * 8);  // (tag, value) pairs
   c->w_xm = w; w = align256(w + L * H * 8);
   c->w_q = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
   c->w_kvcur = w; w = align256(w + L * m.nkv * 2 * m.hd * 8);
-  c->w_part = w; w = align256(w + L * m.nkv * s.attn_splits * m.grp() * (m.hd + 4) * 4);
+  c->w_part = w; w = align256(w + L * m.nkv * std::max(c->cap_splits, s.attn_splits) * m.grp() * (m.hd + 4) * 4);
   c->w_o = w; w = align256(w + L * qd * 8);  // (tag, value) pairs
   c->w_h = w; w = align256(w + L * F * 4);
   c->w_trace = w; w = align256(w + (int64_t)std::max(0, c->sc.trace_steps) * NT * 64);
@@ -522,6 +530,21 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
   c->tabs = flatten(c->sched);
   c->hash = schedule_hash(c->sched);
+  {
+    // capacity for the schedules tuning may install: as many combines per kv head as q heads, full
+    // O-projection shares on their queues, at most the default attention splits
+    c->cap_flags = c->sched.n_flags;
+    c->cap_tasks = (int64_t)c->sched.tasks.size();
+    c->cap_splits = c->sched.attn_splits;
+    pmk_schedule_config cap_sc = c->sc;
+    cap_sc.combine_parts = c->m.grp();
+    cap_sc.combine_o_share = 3;
+    Schedule cap;
+    if (build_schedule(c->m, cap_sc, n_cus, &cap).empty()) {
+      c->cap_flags = std::max<int64_t>(c->cap_flags, cap.n_flags);
+      c->cap_tasks = std::max<int64_t>(c->cap_tasks, (int64_t)cap.tasks.size());
+    }
+  }
   compute_layout(c);
   if (c->lds_bytes > (size_t)kLdsBytes || c->lds_bytes_pk > (size_t)kLdsBytes) {
     delete c;
@@ -836,14 +859,16 @@ static pmk_status read_trace(pmk_ctx* c, std::vector<unsigned long long>& t) {
   return PMK_OK;
 }
 
-// Replace the context's schedule by `s` (same task and counter counts): validate, re-derive the
-// tables and the LDS layout, upload the tables.  The device must be idle.
-static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
+// Replace the context's schedule by `s`: validate, check it fits the workspace capacity and LDS,
+// re-derive the tables and the LDS layout, upload the tables, and discard the synchronisation state
+// of the previous schedule (flags, counters and step tags cleared, epoch restarted) while keeping the
+// position `pos` and next input token `token`.  Synchronous on `st`.
+static pmk_status install_schedule(pmk_ctx* c, Schedule&& s, int32_t pos, int32_t token, hipStream_t st) {
   const std::string e = validate_schedule(s);
   if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
-  if (s.tasks.size() != c->sched.tasks.size() || s.counters.size() != c->sched.counters.size() ||
-      s.n_flags != c->sched.n_flags)
-    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the rebuilt schedule changed its task or counter count");
+  if (s.counters.size() != c->sched.counters.size() || s.n_flags > c->cap_flags ||
+      (int64_t)s.tasks.size() > c->cap_tasks || s.attn_splits > c->cap_splits)
+    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the schedule exceeds the workspace capacity fixed at creation");
   const pmk_sizes old_sizes = c->sizes;
   Schedule prev = std::move(c->sched);
   c->sched = std::move(s);
@@ -851,12 +876,13 @@ static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
   if (c->sizes.workspace_bytes != old_sizes.workspace_bytes || c->lds_bytes > (size_t)kLdsBytes || c->lds_bytes_pk > (size_t)kLdsBytes) {
     c->sched = std::move(prev);
     compute_layout(c);
-    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the rebuilt schedule does not fit the bound buffers or LDS");
+    return fail(c, PMK_ERR_SCHEDULE_INVALID, "tune: the schedule does not fit the bound buffers or LDS");
   }
   c->tabs = flatten(c->sched);
   c->hash = schedule_hash(c->sched);
   compute_phases(c);
   fill_params(c);
+  HIPCHK(c, hipStreamSynchronize(st));
   HIPCHK(c, hipMemcpy(c->ws + c->w_tasks, c->tabs.tasks.data(), c->tabs.tasks.size() * sizeof(pmk_task), hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(c->ws + c->w_qoff, c->tabs.qoff.data(), c->tabs.qoff.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(c, hipMemcpy(c->ws + c->w_qtasks, c->tabs.qtasks.data(), c->tabs.qtasks.size() * 4, hipMemcpyHostToDevice));
@@ -864,131 +890,262 @@ static pmk_status install_schedule(pmk_ctx* c, Schedule&& s) {
   HIPCHK(c, hipMemcpy(c->ws + c->w_cflag, c->tabs.ctr_flag_base.data(), c->tabs.ctr_flag_base.size() * 4, hipMemcpyHostToDevice));
   if (c->graph_exec) { (void)hipGraphExecDestroy(c->graph_exec); c->graph_exec = nullptr; }
   if (c->graph) { (void)hipGraphDestroy(c->graph); c->graph = nullptr; }
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), pos, token, nullptr, st));
+  HIPCHK(c, hipStreamSynchronize(st));
   return PMK_OK;
 }
 
-// Mean wall time of the traced steps [0, steps) in µs: per step, the first task start to the last
-// task end over all queues (timestamps in 10 ns ticks).
-static double traced_step_us(const pmk_ctx* c, const std::vector<unsigned long long>& t, int steps) {
-  const size_t NT = c->sched.tasks.size();
-  double sum = 0;
-  int n = 0;
-  for (int st = 0; st < steps; ++st) {
-    unsigned long long lo = ~0ull, hi = 0;
-    for (size_t i = 0; i < NT; ++i) {
-      const unsigned long long* r = &t[((size_t)st * NT + i) * 8];
-      if (!r[0] || !r[2] || r[2] < r[0]) continue;
-      lo = std::min(lo, r[0]);
-      hi = std::max(hi, r[2]);
-    }
-    if (hi > lo) { sum += (double)(hi - lo) * 0.01; ++n; }
-  }
-  return n ? sum / n : 0.0;
+namespace {
+
+// One measured configuration of the tuning search.
+struct TuneRun {
+  double us = 0;                         // µs per step of the timed steps
+  std::vector<unsigned long long> keys;  // per step: orderable max logit << 32 | ~argmax
+};
+
+float key_value(unsigned long long k) {
+  const uint32_t ov = (uint32_t)(k >> 32);
+  const uint32_t u = (ov & 0x80000000u) ? (ov & 0x7fffffffu) : ~ov;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
 }
 
-pmk_status pmk_tune(pmk_ctx* c, int32_t steps, int32_t* kept, void* stream) {
-  pmk_status s = need_device(c);
-  if (s != PMK_OK) return s;
-  if (kept) *kept = 0;
-  if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
-  if (c->sc.trace_steps <= 0) return fail(c, PMK_ERR_INVALID_ARG, "tuning reads the trace: create the context with trace_steps >= 1");
-  s = sync_position(c);
-  if (s != PMK_OK) return s;
-  if (steps <= 0 || steps > c->sc.trace_steps) steps = c->sc.trace_steps;
-  if ((int64_t)c->pos_host + steps > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + steps exceeds max_seq");
-  hipStream_t st = (hipStream_t)stream;
-  HIPCHK(c, hipSetDevice(c->device));
-  // save the next input token and the position: every traced run below starts from them
-  int32_t* saved = reinterpret_cast<int32_t*>(c->ws + c->w_ctrl + CTRL_SAVED * 4);
-  HIPCHK(c, launch_copy_token(c->kp, saved, st));
-  const int32_t pos0 = c->pos_host;
-  const int trace_prev = c->trace_on;
-  HIPCHK(c, hipStreamSynchronize(st));
-  s = pmk_set_trace(c, 1);
-  if (s != PMK_OK) return s;
-  // `steps` traced megakernel steps from (pos0, saved token), then back to them
-  auto traced_run = [&](std::vector<unsigned long long>& tr) -> pmk_status {
+}  // namespace
+
+// `steps` megakernel steps from (pos, token), after an untimed pass of the same steps from the same
+// state; timed with HIP events on `st`; the steps' argmax keys are read back for the correctness
+// gate.  The state is back at (pos, token) afterwards.
+static pmk_status tune_timed_run(pmk_ctx* c, int steps, int32_t pos, int32_t token, hipStream_t st, TuneRun* r) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIPCHK(c, hipEventCreate(&e0));
+  HIPCHK(c, hipEventCreate(&e1));
+  pmk_status s = PMK_OK;
+  for (int pass = 0; pass < 2 && s == PMK_OK; ++pass) {
     CallParams cp{};
+    cp.out_tokens = reinterpret_cast<int32_t*>(c->ws + c->w_tune);
     cp.n_steps = steps;
     cp.eos = -1;
-    cp.trace = 1;
-    pmk_status s2 = begin_call(c, cp, st);
-    if (s2 == PMK_OK) s2 = launch_persistent(c, st);
-    if (s2 != PMK_OK) return s2;
-    c->pos_host += steps;
-    s2 = read_trace(c, tr);
-    if (s2 != PMK_OK) return s2;
-    HIPCHK(c, launch_set_pos(c->kp, pos0, saved, st));
-    HIPCHK(c, hipStreamSynchronize(st));
-    c->pos_host = pos0;
-    return PMK_OK;
-  };
-  std::vector<unsigned long long> t;
-  s = traced_run(t);
+    if (pass == 1) HIPCHK(c, hipEventRecord(e0, st));
+    s = begin_call(c, cp, st);
+    if (s == PMK_OK) s = launch_persistent(c, st);
+    if (s == PMK_OK && pass == 1) HIPCHK(c, hipEventRecord(e1, st));
+    if (s == PMK_OK) HIPCHK(c, hipStreamSynchronize(st));
+    if (s == PMK_OK && pass == 1) {
+      float ms = 0;
+      HIPCHK(c, hipEventElapsedTime(&ms, e0, e1));
+      r->us = ms * 1e3 / steps;
+      r->keys.resize(steps);
+      HIPCHK(c, hipMemcpy(r->keys.data(), c->ws + c->w_keys, steps * 8, hipMemcpyDeviceToHost));
+    }
+    if (s == PMK_OK) HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), pos, token, nullptr, st));
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   if (s != PMK_OK) return s;
-  const double before_us = traced_step_us(c, t, steps);
-  // streamed bytes and streaming time (staged -> GEMV done) per GEMV op and queue
+  uint32_t err = 0;
+  HIPCHK(c, hipMemcpy(&err, c->ws + c->w_ctrl + CTRL_ERR * 4, 4, hipMemcpyDeviceToHost));
+  if (err) return fail(c, (pmk_status)err, "tune: a device error during a measured run");
+  return PMK_OK;
+}
+
+// Per-queue streaming rate (bytes per tick, after the pre-wait prefetch) of a GEMV op, and each
+// queue's XCD, from a traced run of the installed schedule.
+static pmk_status tune_rates(pmk_ctx* c, int steps, int32_t pos, int32_t token, hipStream_t st,
+                             std::vector<double> rate[8], std::vector<int>* xcd) {
+  pmk_status s = pmk_set_trace(c, 1);
+  if (s != PMK_OK) return s;
+  CallParams cp{};
+  cp.out_tokens = reinterpret_cast<int32_t*>(c->ws + c->w_tune);
+  cp.n_steps = steps;
+  cp.eos = -1;
+  cp.trace = 1;
+  s = begin_call(c, cp, st);
+  if (s == PMK_OK) s = launch_persistent(c, st);
+  if (s != PMK_OK) return s;
+  std::vector<unsigned long long> t;
+  s = read_trace(c, t);
+  c->trace_on = 0;
+  if (s != PMK_OK) return s;
+  HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), pos, token, nullptr, st));
+  HIPCHK(c, hipStreamSynchronize(st));
   const size_t NT = c->sched.tasks.size();
   const int NQ = c->sched.n_queues;
   std::vector<int> queue_of(NT, 0);
   for (int q = 0; q < NQ; ++q)
     for (int32_t ti : c->sched.queues[q]) queue_of[ti] = q;
+  xcd->assign(NQ, -1);
   std::vector<double> bytes(8 * (size_t)NQ, 0.0), ticks(8 * (size_t)NQ, 0.0);
   const ModelDims& m = c->m;
   const double es = m.wdt == PMK_DT_FP8_E4M3 ? 1.0 : 2.0;
-  for (int sp = 0; sp < steps; ++sp)
+  for (int sp = 1; sp < steps; ++sp)  // the first step also pays the launch
     for (size_t i = 0; i < NT; ++i) {
       const pmk_task& k = c->sched.tasks[i];
-      if (k.op == PMK_OP_ATTN || k.op == PMK_OP_TOKEN || k.op == PMK_OP_COMBINE) continue;
       const unsigned long long* r = &t[((size_t)sp * NT + i) * 8];
+      if (r[2]) (*xcd)[queue_of[i]] = (int)(r[3] >> 32);
+      if (k.op == PMK_OP_ATTN || k.op == PMK_OP_TOKEN || k.op == PMK_OP_COMBINE) continue;
       if (!r[4] || !r[5] || r[5] <= r[4]) continue;
       const double K = k.op == PMK_OP_DOWN ? m.F : k.op == PMK_OP_OPROJ ? m.qdim() : m.H;
       const size_t at = (size_t)k.op * NQ + queue_of[i];
-      // bytes streamed after staging: the tile less what the pre-wait prefetch already holds
-      const double tile = (k.a1 - k.a0) * K * es;
-      bytes[at] += std::max(0.0, tile - (double)kPrefetchBytes);
+      bytes[at] += std::max(0.0, (k.a1 - k.a0) * K * es - (double)kPrefetchBytes);
       ticks[at] += (double)(r[5] - r[4]);
     }
-  RowWeights rw;
-  // only phases whose tiles are several times the prefetch give a usable rate
-  // gate/up only: its per-queue rates can differ reproducibly (by XCD on some boxes); the other
-  // phases measured flat, and re-splitting them only adds noise
-  for (int op : {PMK_OP_GATEUP}) {
-    std::vector<double> w(NQ, 0.0);
-    double mean = 0;
-    int n = 0;
-    for (int q = 0; q < NQ; ++q) {
-      const size_t at = (size_t)op * NQ + q;
-      if (ticks[at] > 0) { w[q] = bytes[at] / ticks[at]; mean += w[q]; ++n; }
-    }
-    if (n < NQ || mean <= 0) continue;  // not every queue measured: keep the even split
-    mean /= n;
-    // half the measured deviation: a CU given fewer rows also streams them faster
-    for (double& x : w) x = std::min(std::max(1.0 + 0.5 * (x / mean - 1.0), 0.5), 2.0);
-    rw.w[op] = w;
+  for (int op = 0; op < 8; ++op) {
+    rate[op].assign(NQ, 0.0);
+    for (int q = 0; q < NQ; ++q)
+      if (ticks[(size_t)op * NQ + q] > 0) rate[op][q] = bytes[(size_t)op * NQ + q] / ticks[(size_t)op * NQ + q];
   }
-  Schedule ns;
-  std::string e = build_schedule(c->m, c->sc, NQ, &ns, &rw);
-  if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
-  s = install_schedule(c, std::move(ns));
+  return PMK_OK;
+}
+
+// Row weights for op from measured rates: per queue, or the mean of each queue's XCD; moved from
+// even toward proportional by `damp`.  Empty when some queue has no rate.
+static std::vector<double> tune_weights(const std::vector<double>& rate, const std::vector<int>& xcd, bool by_xcd,
+                                        double damp) {
+  const int NQ = (int)rate.size();
+  std::vector<double> r = rate;
+  for (int q = 0; q < NQ; ++q)
+    if (!(rate[q] > 0)) return {};
+  if (by_xcd) {
+    std::map<int, std::pair<double, int>> acc;
+    for (int q = 0; q < NQ; ++q) { acc[xcd[q]].first += rate[q]; acc[xcd[q]].second += 1; }
+    for (int q = 0; q < NQ; ++q) r[q] = acc[xcd[q]].first / acc[xcd[q]].second;
+  }
+  double mean = 0;
+  for (double x : r) mean += x;
+  mean /= NQ;
+  std::vector<double> w(NQ);
+  for (int q = 0; q < NQ; ++q) w[q] = std::min(std::max(1.0 + damp * (r[q] / mean - 1.0), 0.5), 2.0);
+  return w;
+}
+
+pmk_status pmk_tune(pmk_ctx* c, int32_t steps, pmk_tune_result* res, void* stream) {
+  pmk_status s = need_device(c);
   if (s != PMK_OK) return s;
-  // keep the new split only if the same steps from the same state now run faster: when the
-  // rates are flat, the measured differences are noise and a re-split only adds imbalance
-  std::vector<unsigned long long> t2;
-  s = traced_run(t2);
+  if (res) std::memset(res, 0, sizeof *res);
+  if (!c->weights || !c->kv_ready) return fail(c, PMK_ERR_NOT_BOUND, "weights and KV state must be loaded first");
+  s = sync_position(c);
   if (s != PMK_OK) return s;
-  const double after_us = traced_step_us(c, t2, steps);
-  if (after_us > 0 && after_us < before_us) {
-    c->rw = rw;
-    if (kept) *kept = 1;
-  } else {
-    Schedule ps;
-    e = build_schedule(c->m, c->sc, NQ, &ps, &c->rw);  // the split in force before this call
+  if (steps <= 0) steps = 32;
+  steps = std::max(4, std::min(steps, kMaxTuneSteps));
+  if ((int64_t)c->pos_host + steps > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "position + steps exceeds max_seq");
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(c, hipSetDevice(c->device));
+  HIPCHK(c, hipStreamSynchronize(st));
+  const int32_t pos0 = c->pos_host;
+  uint32_t tok = 0;
+  HIPCHK(c, hipMemcpy(&tok, c->ws + c->w_ctrl + CTRL_TOKEN * 4, 4, hipMemcpyDeviceToHost));
+  const int32_t token0 = (int32_t)tok;
+  const int NQ = c->sched.n_queues;
+  // the starting point: the schedule in force, from a clean state
+  pmk_schedule_config best_sc = c->sc;
+  RowWeights best_rw = c->rw;
+  {
+    Schedule cur;
+    std::string e = build_schedule(c->m, best_sc, NQ, &cur, &best_rw);
     if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
-    s = install_schedule(c, std::move(ps));
+    s = install_schedule(c, std::move(cur), pos0, token0, st);
     if (s != PMK_OK) return s;
   }
-  c->trace_on = trace_prev;
+  TuneRun ref;
+  s = tune_timed_run(c, steps, pos0, token0, st, &ref);
+  if (s != PMK_OK) return s;
+  double best_us = ref.us;
+  if (res) res->us_before = ref.us;
+  std::string desc;
+  int tried = 0, kept = 0, gated = 0, invalid = 0;
+  // install and time a candidate; keep it if it passes the gate and is faster by more than 0.2%
+  auto attempt = [&](const pmk_schedule_config& sc, const RowWeights& rw, const std::string& what) -> pmk_status {
+    Schedule ns;
+    ++tried;
+    if (!build_schedule(c->m, sc, NQ, &ns, &rw).empty() || !validate_schedule(ns).empty()) { ++invalid; return PMK_OK; }
+    if (install_schedule(c, std::move(ns), pos0, token0, st) != PMK_OK) { ++invalid; c->err.clear(); }
+    else {
+      TuneRun r;
+      pmk_status s2 = tune_timed_run(c, steps, pos0, token0, st, &r);
+      if (s2 != PMK_OK) return s2;
+      // correctness gate against the starting schedule's run from the same state: the same greedy
+      // token at every step, and the same largest logit within 1e-3 (a row split changes only the
+      // grouping of a row's partial sums)
+      bool same = true;
+      for (int i = 0; i < steps; ++i) {
+        const float a = key_value(ref.keys[i]), b = key_value(r.keys[i]);
+        same = same && (uint32_t)ref.keys[i] == (uint32_t)r.keys[i] && std::fabs(a - b) <= 1e-3f * std::max(1.0f, std::fabs(a));
+      }
+      if (!same) ++gated;
+      if (same && r.us < best_us * (1.0 - 0.002)) {
+        best_us = r.us;
+        best_sc = sc;
+        best_rw = rw;
+        ++kept;
+        desc += (desc.empty() ? "" : "; ") + what;
+        return PMK_OK;
+      }
+    }
+    // revert to the best so far
+    Schedule bs;
+    std::string e = build_schedule(c->m, best_sc, NQ, &bs, &best_rw);
+    if (!e.empty()) return fail(c, PMK_ERR_SCHEDULE_INVALID, e);
+    return install_schedule(c, std::move(bs), pos0, token0, st);
+  };
+  // 1. speed-weighted row shares of gate/up, then of the down projection, from measured rates
+  if (c->sc.trace_steps >= 2) {
+    std::vector<double> rate[8];
+    std::vector<int> xcd;
+    s = tune_rates(c, std::min(steps, c->sc.trace_steps), pos0, token0, st, rate, &xcd);
+    if (s != PMK_OK) return s;
+    for (int op : {PMK_OP_GATEUP, PMK_OP_DOWN})
+      for (bool by_xcd : {true, false})
+        for (double damp : {1.0, 0.5}) {
+          std::vector<double> w = tune_weights(rate[op], xcd, by_xcd, damp);
+          if (w.empty()) continue;
+          RowWeights rw = best_rw;
+          rw.w[op] = w;
+          char what[96];
+          std::snprintf(what, sizeof what, "%s rows %s x%.1f", op == PMK_OP_GATEUP ? "gate/up" : "down",
+                        by_xcd ? "per XCD" : "per queue", damp);
+          s = attempt(best_sc, rw, what);
+          if (s != PMK_OK) return s;
+        }
+  }
+  // 2. O-projection rows on the combine queues, combines per kv head, attention splits
+  for (int share : {1, 2, 3}) {
+    if (share == best_sc.combine_o_share) continue;
+    pmk_schedule_config sc = best_sc;
+    sc.combine_o_share = share;
+    s = attempt(sc, best_rw, std::string("combine_o_share ") + std::to_string(share));
+    if (s != PMK_OK) return s;
+  }
+  for (int cp = 1; cp <= c->m.grp(); ++cp) {
+    if (c->m.grp() % cp || cp == c->sched.combine_parts) continue;
+    pmk_schedule_config sc = best_sc;
+    sc.combine_parts = cp;
+    s = attempt(sc, best_rw, std::string("combine_parts ") + std::to_string(cp));
+    if (s != PMK_OK) return s;
+  }
+  for (int frac : {3, 2}) {  // 3/4 and 1/2 of the capacity splits
+    const int S = c->cap_splits * frac / 4;
+    if (S < 1 || S == c->sched.attn_splits) continue;
+    pmk_schedule_config sc = best_sc;
+    sc.attn_splits = S;
+    s = attempt(sc, best_rw, std::string("attn_splits ") + std::to_string(S));
+    if (s != PMK_OK) return s;
+  }
+  c->sc = best_sc;
+  c->rw = best_rw;
+  if (res) {
+    res->tried = tried;
+    res->kept = kept;
+    res->gate_rejected = gated;
+    res->invalid = invalid;
+    res->us_after = best_us;
+    res->chosen = best_sc;
+    res->chosen.combine_parts = c->sched.combine_parts;
+    res->chosen.attn_splits = c->sched.attn_splits;
+    std::snprintf(res->desc, sizeof res->desc, "%s", desc.empty() ? "default" : desc.c_str());
+  }
+  c->pos_host = pos0;
+  c->pos_exact = true;
   return PMK_OK;
 }
 
@@ -1040,9 +1197,9 @@ pmk_status pmk_trace_export(pmk_ctx* c, const char* path) {
       const pmk_task& k = c->sched.tasks[i];
       const unsigned long long t1 = (r[1] >= r[0] && r[1] <= r[2]) ? r[1] : r[0];
       std::fprintf(f, "%s{\"name\":\"wait\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f}", first ? "" : ",\n",
-                   st, r[3], (r[0] - t0) * 0.01, (t1 - r[0]) * 0.01);
-      std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f,\"args\":{\"m4\":%.2f,\"m5\":%.2f,\"m6\":%.2f,\"m7\":%.2f}}",
-                   names[k.op >= 1 && k.op <= 8 ? k.op : 0], k.layer, st, r[3], (t1 - t0) * 0.01, (r[2] - t1) * 0.01,
+                   st, r[3] & 0xffffffffull, (r[0] - t0) * 0.01, (t1 - r[0]) * 0.01);
+      std::fprintf(f, ",\n{\"name\":\"%s L%d\",\"ph\":\"X\",\"pid\":%d,\"tid\":%llu,\"ts\":%.2f,\"dur\":%.2f,\"args\":{\"xcd\":%llu,\"m4\":%.2f,\"m5\":%.2f,\"m6\":%.2f,\"m7\":%.2f}}",
+                   names[k.op >= 1 && k.op <= 8 ? k.op : 0], k.layer, st, r[3] & 0xffffffffull, (t1 - t0) * 0.01, (r[2] - t1) * 0.01, r[3] >> 32,
                    r[4] >= t1 ? (r[4] - t1) * 0.01 : -1.0, r[5] >= t1 ? (r[5] - t1) * 0.01 : -1.0,
                    r[6] >= t1 ? (r[6] - t1) * 0.01 : -1.0, r[7] >= t1 ? (r[7] - t1) * 0.01 : -1.0);
       first = false;

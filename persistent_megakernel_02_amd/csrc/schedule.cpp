@@ -135,15 +135,23 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
     return cp == 1 || o_units(cp, false) <= kOTileUnits || o_units(cp, true) <= kOTileUnits;
   };
   int CP = 1;
-  for (int d = 1; d <= grp; ++d)
-    if (grp % d == 0 && o_fits(d)) {
-      CP = d;
-      if (cbytes / d <= 33 * 1024) break;
-    }
+  if (sc.combine_parts > 0) {
+    if (grp % sc.combine_parts) return "builder: combine_parts must divide the q heads per kv head";
+    CP = sc.combine_parts;
+  } else {
+    for (int d = 1; d <= grp; ++d)
+      if (grp % d == 0 && o_fits(d)) {
+        CP = d;
+        if (cbytes / d <= 33 * 1024) break;
+      }
+  }
   s.combine_parts = CP;
   // with several combines per head group and O tiles that would not fit the queues left, the
-  // combine queues keep half an O-projection share each (a short tile, copied after the combine)
-  const bool o_on_comb = CP > 1 && o_units(CP, false) > kOTileUnits;
+  // combine queues keep half an O-projection share each (a short tile, copied by the combine before
+  // its wait); the ScheduleConfig can ask for none, half or a full share
+  const int share = sc.combine_o_share;
+  const bool o_on_comb = share == 2 || share == 3 || (share == 0 && CP > 1 && o_units(CP, false) > kOTileUnits);
+  const bool o_half = share != 3;
   auto comb_queue = [&](int g, int p) { return (g * S + S - 1 - p % S + n_queues) % n_queues; };
   std::vector<char> comb_q(n_queues, 0);
   for (int g = 0; g < m.nkv; ++g)
@@ -157,7 +165,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   }
   const int n_o = std::min((int)o_queues.size(), m.H);
   std::vector<int> o_bounds;  // row bounds of the O tiles when the combine queues take half shares
-  if (o_on_comb && n_o == (int)o_queues.size()) {
+  if (o_on_comb && o_half && n_o == (int)o_queues.size()) {
     std::vector<double> w(n_o);
     for (int i = 0; i < n_o; ++i) w[i] = comb_q[o_queues[i]] ? 0.5 : 1.0;
     split_weighted(m.H, n_o, w, &o_bounds);

@@ -83,9 +83,9 @@ def test_modes_agree_bitwise_and_chunking(tiny):
 
 @pytest.mark.parametrize("name", ["tiny", "1b"])
 def test_tuned_schedule_keeps_parity(name, tiny):
-    """pmk_tune re-splits the GEMV rows by measured speed, keeps the split only if it runs faster and
-    restores the position and next token: decoding afterwards still matches the oracle, and the
-    modes still agree bitwise."""
+    """pmk_tune searches the schedule knobs and row shares (validated, gated on tokens and largest
+    logits, kept only if faster) and restores the position and next token: decoding afterwards still
+    matches the oracle, and the modes still agree bitwise."""
     import torch
     import persistent_megakernel_02_amd as pmk
     w = synthgen.WORKLOADS[name]
@@ -98,27 +98,24 @@ def test_tuned_schedule_keeps_parity(name, tiny):
     pos = dec.position()
     log(f"{name}: tune at position {pos}")
     h0 = dec.schedule_info().hash
-    k1 = dec.tune(4)
-    h1 = dec.schedule_info().hash
-    k2 = dec.tune(4)
-    h2 = dec.schedule_info().hash
-    # a re-split that did not run faster is undone: the schedule in force before comes back
-    if not k1:
-        assert h1 == h0
-    if not k2:
-        assert h2 == h1
-    log(f"{name}: re-splits kept {k1}, {k2}")
+    r = dec.tune(8)
+    log(f"{name}: {r.tried} candidates, {r.kept} kept [{r.desc.decode()}], {r.gate_rejected} gated, {r.invalid} "
+        f"invalid, {r.us_before:.1f} -> {r.us_after:.1f} us/step")
+    assert r.tried > 0 and r.gate_rejected == 0
+    if r.kept == 0:
+        assert dec.schedule_info().hash == h0
+    else:
+        assert r.us_after < r.us_before
     assert dec.position() == pos
     assert dec.poll_error().code == 0
-    log(f"{name}: schedule hash {h0:#x} -> {dec.schedule_info().hash:#x}")
     steps = 8
     runs = {}
     for mname, m in _modes():
         runs[mname] = gpu_run(w, wts, steps, mode=m, prompt=prompt, dec=dec)
     ref, first_ok = oracle_teacher_forced(w, wts, runs["megakernel"], prompt=prompt)
     check(w, runs["megakernel"], ref, first_ok, f"{name}/tuned")
-    for mname, r in runs.items():
-        assert np.array_equal(r.logits, runs["megakernel"].logits), mname
+    for mname, r2 in runs.items():
+        assert np.array_equal(r2.logits, runs["megakernel"].logits), mname
 
 
 def test_tiny_eos_stops_early(tiny):

@@ -78,7 +78,10 @@ REAL = [("tiny", n, {}) for n in (1, 2, 3, 4, 7, 8, 16, 64, 256)] + \
        [("tiny", 8, dict(attn_splits=s)) for s in (1, 2, 5)] + \
        [("tiny", 8, dict(sync_mode=pmk.PMK_SYNC_COUNTERS))] + \
        [("1b", n, {}) for n in (16, 100, 256)] + [("2b", 256, {}), ("8b", 256, {}), ("8b_fp8", 256, {}),
-                                                  ("8b", 304, dict(attn_splits=16))]
+                                                  ("8b", 304, dict(attn_splits=16))] + \
+       [("8b", 256, dict(combine_parts=cp, combine_o_share=sh)) for cp in (1, 2, 4) for sh in (1, 2, 3)] + \
+       [("1b", 256, dict(combine_parts=4, combine_o_share=3)), ("8b", 256, dict(attn_splits=24)),
+        ("8b", 256, dict(attn_splits=16, combine_o_share=3))]
 
 
 @pytest.mark.parametrize("name,n_cus,kw", REAL)
