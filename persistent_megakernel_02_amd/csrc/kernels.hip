@@ -291,6 +291,36 @@ __device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x)
   }
 }
 
+// chunk_dot with the activations already in registers (the same order of operations, so the same
+// result): x[k] holds elements 4k .. 4k+3 of the chunk
+template <int WDT>
+__device__ __forceinline__ float chunk_dot_regs(u32x4 w, const float4* x) {
+  if constexpr (WDT == WFP8) {
+    float a = 0.f, b = 0.f;
+    f32x2 p;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false); a = fmaf(p.x, x[0].x, a); b = fmaf(p.y, x[0].y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);  a = fmaf(p.x, x[0].z, a); b = fmaf(p.y, x[0].w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false); a = fmaf(p.x, x[1].x, a); b = fmaf(p.y, x[1].y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);  a = fmaf(p.x, x[1].z, a); b = fmaf(p.y, x[1].w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, false); a = fmaf(p.x, x[2].x, a); b = fmaf(p.y, x[2].y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.z, true);  a = fmaf(p.x, x[2].z, a); b = fmaf(p.y, x[2].w, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, false); a = fmaf(p.x, x[3].x, a); b = fmaf(p.y, x[3].y, b);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8(w.w, true);  a = fmaf(p.x, x[3].z, a); b = fmaf(p.y, x[3].w, b);
+    return a + b;
+  } else {
+    float a = 0.f, b = 0.f;
+    a = fmaf(dec16<WDT>((uint16_t)(w.x & 0xffffu)), x[0].x, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.x >> 16)), x[0].y, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.y & 0xffffu)), x[0].z, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.y >> 16)), x[0].w, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.z & 0xffffu)), x[1].x, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.z >> 16)), x[1].y, b);
+    a = fmaf(dec16<WDT>((uint16_t)(w.w & 0xffffu)), x[1].z, a);
+    b = fmaf(dec16<WDT>((uint16_t)(w.w >> 16)), x[1].w, b);
+    return a + b;
+  }
+}
+
 // register ring depth (16-byte weight loads in flight per lane); fp8 slots also carry a block scale
 #ifndef PMK_RING_UNITS
 #define PMK_RING_UNITS 10
@@ -469,7 +499,41 @@ __device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float
   const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const int R = sp.R, KS = sp.KS, si = sp.si, s0 = sp.s0, s1 = sp.s1;
   sync();
-  if (sp.nunits > 0) {
+  // FP8: the activation chunks a lane multiplies are the same for every row of its slices, so with
+  // up to 4 slices per wave they are read from LDS once, into registers (+0.4% on the 8B FP8 decode
+  // in an A/B; for 16-bit weights the same change measured -0.15%, so they keep the LDS reads)
+  constexpr int MAXS = WDT == WFP8 ? 64 / EPL : 0;
+  const int ns = s1 - s0;
+  if (MAXS > 0 && sp.nunits > 0 && ns >= 1 && ns <= MAXS) {
+    constexpr int F4 = EPL / 4;  // float4 per chunk
+    float4 xr[MAXS > 0 ? MAXS : 1][F4];
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k)
+      if (k < ns)
+#pragma unroll
+        for (int f = 0; f < F4; ++f) xr[k][f] = *reinterpret_cast<const float4*>(xs + ((s0 + k) * 64 + lane) * EPL + 4 * f);
+    for (int row = sp.wr0; row < sp.wr1; ++row) {
+      const float* src = pf + (row - r0) * nsl * 256 + lane * 4;
+      float acc = 0.f;
+      u32x4 w[MAXS > 0 ? MAXS : 1];
+#pragma unroll
+      for (int k = 0; k < MAXS; ++k)
+        if (k < ns) w[k] = *reinterpret_cast<const u32x4*>(src + (s0 + k) * 256);
+#pragma unroll
+      for (int k = 0; k < MAXS; ++k)
+        if (k < ns) {
+          const float part = chunk_dot_regs<WDT>(w[k], xr[k]);
+          if constexpr (WDT == WFP8) {
+            const int c = (s0 + k) * 64 + lane;
+            acc = fmaf(part, srow(row)[(c < nch ? c : 0) >> 3], acc);
+          } else {
+            acc += part;
+          }
+        }
+      const float v = wave_sum(acc);
+      if (lane == 0) yp[(row - r0) * KS + si] = v;
+    }
+  } else if (sp.nunits > 0) {
     for (int row = sp.wr0; row < sp.wr1; ++row) {
       const float* src = pf + (row - r0) * nsl * 256 + lane * 4;
       int u = s0;
