@@ -22,8 +22,8 @@ _SRC = os.path.join(_HERE, "pmk_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F16, BF16, E4M3 = 0, 1, 2
-FMT = {"f16": F16, "bf16": BF16, "fp8": E4M3}
+F16, BF16, E4M3, I8, I4 = 0, 1, 2, 3, 4
+FMT = {"f16": F16, "bf16": BF16, "fp8": E4M3, "int8": I8, "int4": I4}
 
 
 def build(force: bool = True) -> str:
@@ -61,6 +61,7 @@ def lib():
         L.orc_rmsnorm.argtypes = [vp, vp, i32, f32, vp]
         L.orc_gemv.argtypes = [i32, vp, vp, i32, i32, vp, vp]
         L.orc_matmul_tokens.argtypes = [i32, vp, vp, i32, i32, vp, i32, vp]
+        L.orc_weight_matrix.argtypes = [i32, vp, vp, i32, i32, vp]
         L.orc_rope.argtypes = [vp, i32, i32, f64]
         L.orc_attend.argtypes = [vp, vp, vp, i32, f32, f32, i32, i32, vp]
         L.orc_silu.argtypes = [f32]
@@ -117,14 +118,41 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return y
 
 
+def _scales(fmt: int, scales: Optional[np.ndarray]):
+    """fp8 block scales as fp32; int8 / int4 group scales stay bf16 bits (uint16)."""
+    if scales is None:
+        return None
+    if fmt in (I8, I4):
+        assert scales.dtype == np.uint16, "integer formats take bf16 scale bits"
+        return np.ascontiguousarray(scales)
+    return np.ascontiguousarray(scales, np.float32)
+
+
+def _cols(fmt: int, W: np.ndarray) -> int:
+    return W.shape[1] * 2 if fmt == I4 else W.shape[1]
+
+
 def gemv(fmt: int, W: np.ndarray, x: np.ndarray, scales: Optional[np.ndarray] = None) -> np.ndarray:
+    """y = W x (fp32, k ascending).  int4 W is [rows][cols / 2] packed bytes; the integer formats
+    round x to binary16 first."""
     W = np.ascontiguousarray(W)
     x = np.ascontiguousarray(x, np.float32)
-    rows, cols = W.shape
+    rows, cols = W.shape[0], _cols(fmt, W)
+    assert x.size == cols
     y = np.empty(rows, np.float32)
-    lib().orc_gemv(fmt, _p(W), _p(None if scales is None else np.ascontiguousarray(scales, np.float32)),
-                   rows, cols, _p(x), _p(y))
+    S = _scales(fmt, scales)
+    lib().orc_gemv(fmt, _p(W), _p(S), rows, cols, _p(x), _p(y))
     return y
+
+
+def weight_matrix(fmt: int, W: np.ndarray, scales: Optional[np.ndarray] = None) -> np.ndarray:
+    """The dequantised weights w(n, k) as fp32 [rows][cols]."""
+    W = np.ascontiguousarray(W)
+    rows, cols = W.shape[0], _cols(fmt, W)
+    out = np.empty((rows, cols), np.float32)
+    S = _scales(fmt, scales)
+    lib().orc_weight_matrix(fmt, _p(W), _p(S), rows, cols, _p(out))
+    return out
 
 
 def rope(u: np.ndarray, pos: int, theta: float) -> np.ndarray:
@@ -170,7 +198,8 @@ class OracleModel:
 
     `weights` is any object with attributes embed, final_norm, lm_head, lm_head_scale,
     layers (list of dicts with wq wk wv wo w_gate w_up w_down attn_norm ffn_norm) and scales
-    (list of dicts of fp8 block scales), and `workload` with the model shape.  The arrays are
+    (list of dicts of fp8 block scales or int8 / int4 group scales), and `workload` with the
+    model shape.  The arrays are
     referenced, not copied: keep them alive while the model lives.
     """
 
@@ -182,7 +211,7 @@ class OracleModel:
         self.w = w
         self._keep = weights
         wfmt = FMT[w.wdtype]
-        efmt = BF16 if w.wdtype == "fp8" else wfmt
+        efmt = BF16 if w.wdtype in ("fp8", "int8", "int4") else wfmt
         self.cfg = _Config(w.layers, w.hidden, w.n_q, w.n_kv, w.head_dim, w.ffn, w.vocab, w.eps, w.theta,
                            wfmt, efmt, FMT[w.kvdtype], max_seq if max_seq is not None else w.max_seq)
         ptrs = []
@@ -190,7 +219,7 @@ class OracleModel:
             ptrs += [_p(d[k]) for k in self.KINDS]
         self._layer = (ctypes.c_void_p * len(ptrs))(*ptrs)
         sc = None
-        if w.wdtype == "fp8":
+        if w.wdtype in ("fp8", "int8", "int4"):
             sptrs = []
             for d in weights.scales:
                 sptrs += [_p(d[k]) for k in self.LIN]

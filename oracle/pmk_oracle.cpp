@@ -10,7 +10,8 @@
 // Self-Retargeting Megakernel Synthesis", Method / Layer 1, names the step's
 // instructions GEMV, attention and RMSNorm for HF Llama-family decoders; "Netra Kernel"
 // summary, details section, names GQA attention over an FP8 KV cache and FP8 E4M3
-// block-scale weights; the rest of the step is the standard Llama decoder):
+// block-scale weights; the AutoMegaKernel explainer's results name weight-only int8 (W8A16)
+// and int4 variants of the same kernels; the rest of the step is the standard Llama decoder):
 //   x = E[tok]; per layer: xn = rmsnorm(x, g1); q,k,v = W xn; rotate-half RoPE on q,k;
 //   append k,v to the cache (rounded to the cache format); grouped-query softmax
 //   attention over cache positions 0..p; x += Wo o; xn = rmsnorm(x, g2);
@@ -26,7 +27,7 @@
 
 namespace {
 
-enum Fmt { F16 = 0, BF16 = 1, E4M3 = 2 };
+enum Fmt { F16 = 0, BF16 = 1, E4M3 = 2, I8 = 3, I4 = 4 };
 
 // ---------------------------------------------------------------------------------------------
 // Storage codecs (IEEE binary16, bfloat16 = upper half of binary32, OCP FP8 E4M3FN)
@@ -133,15 +134,40 @@ void rmsnorm(const float* x, const float* g, int n, float eps, float* y) {
   for (int i = 0; i < n; ++i) y[i] = (x[i] * r) * g[i];
 }
 
-// Dequantised weight element: w(n,k) = dec(W[n][k]) (16-bit) or dec(q[n][k]) * S[n/128][k/128] (fp8).
-inline float weight(int fmt, const void* W, const float* S, int cols, int n, int k) {
+// Weight-only integer formats (W8A16 and W4A16): the code q(n,k) is a two's-complement
+// integer, one signed byte per element (int8) or two per byte with the even column in the low
+// nibble (int4, cols even); every row has one bf16 scale per group of 128 columns.
+inline int int_code(int fmt, const void* W, int cols, int n, int k) {
+  const size_t i = (size_t)n * cols + k;
+  if (fmt == I8) return ((const int8_t*)W)[i];
+  const uint8_t b = ((const uint8_t*)W)[i / 2];
+  const int nib = (k & 1) ? (b >> 4) : (b & 15);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+inline bool is_int(int fmt) { return fmt == I8 || fmt == I4; }
+
+// Dequantised weight element: w(n,k) = dec(W[n][k]) (16-bit), dec(q[n][k]) * S[n/128][k/128]
+// (fp8, fp32 block scales), or q(n,k) * s[n][k/128] (int8 / int4, bf16 group scales).
+inline float weight(int fmt, const void* W, const void* S, int cols, int n, int k) {
+  const int nb = (cols + 127) / 128;
+  if (is_int(fmt)) return (float)int_code(fmt, W, cols, n, k) * dec_bf16(((const uint16_t*)S)[(size_t)n * nb + k / 128]);
   const float w = dec(fmt, W, (size_t)n * cols + k);
   if (fmt != E4M3) return w;
-  return w * S[(size_t)(n / 128) * ((cols + 127) / 128) + k / 128];
+  return w * ((const float*)S)[(size_t)(n / 128) * nb + k / 128];
 }
 
 // Y[t][n] = sum_k w(n,k) * X[t][k] for B tokens, k ascending, fp32 (one sum per (t, n)).
-void matmul_tokens(int fmt, const void* W, const float* S, int rows, int cols, const float* X, int B, float* Y) {
+// The integer weight formats take their activation operand in binary16 (the "A16" of W8A16):
+// every element of X is first rounded to the nearest binary16 value.
+void matmul_tokens(int fmt, const void* W, const void* S, int rows, int cols, const float* Xin, int B, float* Y) {
+  std::vector<float> Xh;
+  const float* X = Xin;
+  if (is_int(fmt)) {
+    Xh.resize((size_t)cols * B);
+    for (size_t i = 0; i < Xh.size(); ++i) Xh[i] = dec_f16(enc_f16(Xin[i]));
+    X = Xh.data();
+  }
   std::vector<float> XT((size_t)cols * B);
   for (int t = 0; t < B; ++t)
     for (int k = 0; k < cols; ++k) XT[(size_t)k * B + t] = X[(size_t)t * cols + k];
@@ -233,21 +259,22 @@ struct orc_config {
   int L, H, nq, nkv, hd, F, V;
   float eps;
   double theta;
-  int wfmt;     // format of the linear weights (0 f16, 1 bf16, 2 e4m3 with 128x128 block scales)
+  int wfmt;     // format of the linear weights (0 f16, 1 bf16, 2 e4m3 with 128x128 block scales,
+                // 3 int8 / 4 int4 with bf16 scales per row and 128-column group)
   int efmt;     // format of the embedding and norm gains (0 f16, 1 bf16)
   int kvfmt;    // format of the KV cache (0 f16, 1 bf16, 2 e4m3 with per (layer, kv head, K|V) scale)
   int max_seq;
 };
 
 // Per layer the 9 tensors wq wk wv wo w_gate w_up w_down attn_norm ffn_norm (canonical [out][in]),
-// and for fp8 the 7 block-scale arrays of the linear tensors.
+// and for fp8 / int8 / int4 the 7 scale arrays of the linear tensors.
 struct orc_weights {
   const void* embed;
   const void* final_norm;
   const void* lm_head;
-  const float* lm_head_scale;
+  const void* lm_head_scale;
   const void* const* layer;        // L * 9
-  const float* const* layer_scale; // L * 7, or NULL
+  const void* const* layer_scale;  // L * 7, or NULL
 };
 
 struct orc_model {
@@ -255,9 +282,9 @@ struct orc_model {
   const void* embed;
   std::vector<float> final_norm;
   const void* lm_head;
-  const float* lm_head_scale;
+  const void* lm_head_scale;
   std::vector<const void*> layer;
-  std::vector<const float*> layer_scale;
+  std::vector<const void*> layer_scale;
   std::vector<std::vector<float>> gains;  // per layer: attn_norm, ffn_norm as fp32
   std::vector<uint8_t> kcache, vcache;    // [L][nkv][max_seq][hd] in the cache format
   std::vector<float> kv_scale;            // [L][nkv][2]
@@ -281,11 +308,17 @@ void orc_encode(int fmt, const float* src, int64_t n, void* dst) {
 // ---- single operations ----
 void orc_rmsnorm(const float* x, const float* g, int n, float eps, float* y) { rmsnorm(x, g, n, eps, y); }
 
-void orc_gemv(int fmt, const void* W, const float* S, int rows, int cols, const float* x, float* y) {
+void orc_gemv(int fmt, const void* W, const void* S, int rows, int cols, const float* x, float* y) {
   matmul_tokens(fmt, W, S, rows, cols, x, 1, y);
 }
 
-void orc_matmul_tokens(int fmt, const void* W, const float* S, int rows, int cols, const float* X, int B, float* Y) {
+// Dequantised weight matrix (any weight format): out[n][k] = w(n,k).
+void orc_weight_matrix(int fmt, const void* W, const void* S, int rows, int cols, float* out) {
+  for (int n = 0; n < rows; ++n)
+    for (int k = 0; k < cols; ++k) out[(size_t)n * cols + k] = weight(fmt, W, S, cols, n, k);
+}
+
+void orc_matmul_tokens(int fmt, const void* W, const void* S, int rows, int cols, const float* X, int B, float* Y) {
   matmul_tokens(fmt, W, S, rows, cols, X, B, Y);
 }
 
@@ -302,6 +335,7 @@ int orc_argmax(const float* v, int n) { return argmax(v, n); }
 // ---- model ----
 orc_model* orc_create(const orc_config* c, const orc_weights* w) {
   if (c->hd % 2 || c->nq % c->nkv) return nullptr;
+  if (c->wfmt == I4 && (c->H % 2 || c->F % 2)) return nullptr;  // int4 rows hold whole bytes
   orc_model* m = new orc_model();
   m->c = *c;
   m->embed = w->embed;
@@ -401,7 +435,7 @@ static int forward_tokens(orc_model* m, const int32_t* toks, int B, float* logit
   const size_t es = fmt_size(c.kvfmt);
   for (int l = 0; l < c.L; ++l) {
     const void* const* W = &m->layer[(size_t)l * 9];
-    const float* const* S = &m->layer_scale[(size_t)l * 7];
+    const void* const* S = &m->layer_scale[(size_t)l * 7];
     for (int t = 0; t < B; ++t) rmsnorm(&x[(size_t)t * H], m->gains[l * 2].data(), H, c.eps, &xn[(size_t)t * H]);
     matmul_tokens(c.wfmt, W[0], S[0], qd, H, xn.data(), B, q.data());
     matmul_tokens(c.wfmt, W[1], S[1], kvd, H, xn.data(), B, k.data());

@@ -47,6 +47,7 @@ def _load():
         lib.sg_uniform_int.argtypes = [u64, u64, u64, u32, vp]
         lib.sg_quant_e4m3_block.argtypes = [vp, i64, i64, vp, vp]
         lib.sg_quant_e4m3_scaled.argtypes = [vp, i64, ctypes.c_float, vp]
+        lib.sg_quant_int_group.argtypes = [vp, i64, i64, i32, vp, vp]
         _lib = lib
     return _lib
 
@@ -76,6 +77,23 @@ def quant_e4m3_block(w_bf16: np.ndarray):
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=np.float32)
     _load().sg_quant_e4m3_block(_ptr(np.ascontiguousarray(w_bf16)), rows, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_int_group(w_bf16: np.ndarray, bits: int):
+    """Symmetric per-row, per-128-column-group integer quantisation of a bf16 matrix.
+
+    Returns (codes, scales): int8 codes as int8 [rows][cols], or int4 codes two per byte (even
+    column in the low nibble) as uint8 [rows][cols // 2]; scales are bf16 bits
+    [rows][ceil(cols / 128)] with s = bf16(max|w| / qmax) and q = clamp(rne(w / s), +-qmax),
+    qmax = 127 or 7.
+    """
+    assert bits in (4, 8)
+    rows, cols = w_bf16.shape
+    assert bits == 8 or cols % 2 == 0
+    q = np.empty((rows, cols if bits == 8 else cols // 2), dtype=np.int8 if bits == 8 else np.uint8)
+    s = np.empty((rows, (cols + 127) // 128), dtype=np.uint16)
+    _load().sg_quant_int_group(_ptr(np.ascontiguousarray(w_bf16)), rows, cols, bits, _ptr(q), _ptr(s))
     return q, s
 
 
@@ -113,8 +131,8 @@ class ModelWeights:
     final_norm: np.ndarray
     lm_head: np.ndarray
     layers: List[Dict[str, np.ndarray]]
-    lm_head_scale: Optional[np.ndarray] = None  # fp8 only
-    scales: List[Dict[str, np.ndarray]] = field(default_factory=list)  # fp8 only, per layer
+    lm_head_scale: Optional[np.ndarray] = None  # fp8 / int8 / int4 only
+    scales: List[Dict[str, np.ndarray]] = field(default_factory=list)  # fp8 / int8 / int4 only, per layer
 
 
 def make_weights(w: "Workload", seed: Optional[int] = None, std: float = 0.02, gain_std: float = 0.0,
@@ -122,7 +140,8 @@ def make_weights(w: "Workload", seed: Optional[int] = None, std: float = 0.02, g
     """Generate the synthetic model of workload w.
 
     Linear and embedding weights ~ N(0, std) in the 16-bit storage format (bf16 for the
-    fp8 workload, then block-quantised).  Norm gains are 1 (gain_std > 0 gives 1 + N(0, gain_std)).
+    fp8, int8 and int4 workloads, whose linear weights are then quantised: fp8 per 128x128
+    block, int8 / int4 per row and 128-column group).  Norm gains are 1 (gain_std > 0 gives 1 + N(0, gain_std)).
     `zero` names linear kinds to set to zero (closed-form test variants).
     """
     seed = w.seed if seed is None else seed
@@ -162,6 +181,14 @@ def make_weights(w: "Workload", seed: Optional[int] = None, std: float = 0.02, g
                 sc[k] = s
             mw.scales.append(sc)
         mw.lm_head, mw.lm_head_scale = quant_e4m3_block(lm)
+    elif w.wdtype in ("int8", "int4"):
+        bits = 8 if w.wdtype == "int8" else 4
+        for d in layers:
+            sc = {}
+            for k in LINEAR_KINDS:
+                d[k], sc[k] = quant_int_group(d[k], bits)
+            mw.scales.append(sc)
+        mw.lm_head, mw.lm_head_scale = quant_int_group(lm, bits)
     return mw
 
 

@@ -172,3 +172,40 @@ void sg_quant_e4m3_scaled(const float* v, int64_t n, float s, uint8_t* q) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) q[i] = sg_to_e4m3((double)v[i] / (double)s);
 }
+
+/* Symmetric weight-only integer quantisation of a bf16 matrix, per row and per group of 128
+ * columns: s = bf16(max |w| / qmax) (1 for an all-zero group), q = clamp(round-half-even(w / s),
+ * -qmax, qmax) with qmax = 127 (bits 8) or 7 (bits 4).  int8 codes are one signed byte each
+ * ([rows][cols]); int4 codes are two per byte, the even column in the low nibble
+ * ([rows][cols / 2], cols even).  Scales are bf16 bits [rows][ceil(cols / 128)]. */
+void sg_quant_int_group(const uint16_t* w, int64_t rows, int64_t cols, int bits, uint8_t* q, uint16_t* scales) {
+  const int64_t ng = (cols + 127) / 128;
+  const double qmax = bits == 8 ? 127.0 : 7.0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < rows; ++r) {
+    if (bits == 4)
+      for (int64_t c = 0; c < cols / 2; ++c) q[r * (cols / 2) + c] = 0;
+    for (int64_t g = 0; g < ng; ++g) {
+      const int64_t c0 = g * 128, c1 = c0 + 128 < cols ? c0 + 128 : cols;
+      float amax = 0.f;
+      for (int64_t c = c0; c < c1; ++c) {
+        const float a = fabsf(sg_bf16_value(w[r * cols + c]));
+        if (a > amax) amax = a;
+      }
+      const uint16_t sb = amax > 0.f ? sg_to_bf16(amax / (float)qmax) : (uint16_t)0x3F80;
+      scales[r * ng + g] = sb;
+      const double s = (double)sg_bf16_value(sb);
+      for (int64_t c = c0; c < c1; ++c) {
+        double v = nearbyint((double)sg_bf16_value(w[r * cols + c]) / s);
+        if (v > qmax) v = qmax;
+        if (v < -qmax) v = -qmax;
+        const int iv = (int)v;
+        if (bits == 8) {
+          q[r * cols + c] = (uint8_t)(int8_t)iv;
+        } else {
+          q[r * (cols / 2) + c / 2] |= (uint8_t)((iv & 15) << (4 * (c & 1)));
+        }
+      }
+    }
+  }
+}

@@ -33,23 +33,45 @@ def round_to(x: np.ndarray, fmt: str, scale: float = 1.0) -> np.ndarray:
     return q.to(torch.float64).numpy() * scale
 
 
+def int_codes(raw: np.ndarray, fmt: str) -> np.ndarray:
+    """Two's-complement integer codes as fp64: int8 bytes, or int4 nibbles (even column low)."""
+    raw = np.ascontiguousarray(raw)
+    if fmt == "int8":
+        return raw.view(np.int8).astype(np.float64)
+    b = raw.view(np.uint8).astype(np.int64)
+    q = np.stack([b & 15, b >> 4], axis=-1).reshape(raw.shape[0], -1)
+    return np.where(q >= 8, q - 16, q).astype(np.float64)
+
+
+def _dequant(raw, S, fmt):
+    if fmt in ("int8", "int4"):
+        q = int_codes(raw, fmt)
+        return q * np.repeat(dec16(S, "bf16"), 128, 1)[:, : q.shape[1]]
+    q = dec_e4m3(raw)
+    S = S.astype(np.float64)
+    return q * np.repeat(np.repeat(S, 128, 0), 128, 1)[: q.shape[0], : q.shape[1]]
+
+
 def linear(weights, layer: int, kind: str) -> np.ndarray:
     w = weights.workload
     raw = weights.layers[layer][kind]
-    if w.wdtype != "fp8":
+    if w.wdtype in ("f16", "bf16"):
         return dec16(raw, w.wdtype)
-    S = weights.scales[layer][kind].astype(np.float64)
-    q = dec_e4m3(raw)
-    return q * np.repeat(np.repeat(S, 128, 0), 128, 1)[: q.shape[0], : q.shape[1]]
+    return _dequant(raw, weights.scales[layer][kind], w.wdtype)
 
 
 def lm_head(weights) -> np.ndarray:
     w = weights.workload
-    if w.wdtype != "fp8":
+    if w.wdtype in ("f16", "bf16"):
         return dec16(weights.lm_head, w.wdtype)
-    q = dec_e4m3(weights.lm_head)
-    S = weights.lm_head_scale.astype(np.float64)
-    return q * np.repeat(np.repeat(S, 128, 0), 128, 1)[: q.shape[0], : q.shape[1]]
+    return _dequant(weights.lm_head, weights.lm_head_scale, w.wdtype)
+
+
+def act(weights, X: np.ndarray) -> np.ndarray:
+    """The activation operand of a linear layer: binary16 for the integer weight formats (A16)."""
+    if weights.workload.wdtype in ("int8", "int4"):
+        return np.asarray(X, np.float64).astype(np.float16).astype(np.float64)
+    return X
 
 
 def _rms(X, g, eps):
@@ -81,7 +103,7 @@ def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=No
     LAST token, used in place of its own rounded k and v.
     """
     w = weights.workload
-    efmt = "bf16" if w.wdtype == "fp8" else w.wdtype
+    efmt = "bf16" if w.wdtype in ("fp8", "int8", "int4") else w.wdtype
     H, hd, nq, nkv = w.hidden, w.head_dim, w.n_q, w.n_kv
     grp = nq // nkv
     P0 = 0 if cached_kv is None else cached_kv[0].shape[2]
@@ -93,9 +115,10 @@ def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=No
         g1 = dec16(weights.layers[l]["attn_norm"], efmt)
         g2 = dec16(weights.layers[l]["ffn_norm"], efmt)
         Xn = _rms(X, g1, w.eps)
-        Q = _rope_rows(Xn @ linear(weights, l, "wq").T, pos, hd, w.theta)
-        K = _rope_rows(Xn @ linear(weights, l, "wk").T, pos, hd, w.theta)
-        Vv = Xn @ linear(weights, l, "wv").T
+        Xa = act(weights, Xn)
+        Q = _rope_rows(Xa @ linear(weights, l, "wq").T, pos, hd, w.theta)
+        K = _rope_rows(Xa @ linear(weights, l, "wk").T, pos, hd, w.theta)
+        Vv = Xa @ linear(weights, l, "wv").T
         K = K.reshape(T, nkv, hd)
         Vv = Vv.reshape(T, nkv, hd)
         if collect_kv is not None:
@@ -124,11 +147,11 @@ def logits_all(weights, tokens, kv_scales=None, cached_kv=None, attn_override=No
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p = p / p.sum(axis=1, keepdims=True)
             O[:, j * hd:(j + 1) * hd] = p @ Vr[:, g]
-        X = X + O @ linear(weights, l, "wo").T
-        Xn = _rms(X, g2, w.eps)
+        X = X + act(weights, O) @ linear(weights, l, "wo").T
+        Xn = act(weights, _rms(X, g2, w.eps))
         G = Xn @ linear(weights, l, "w_gate").T
         U = Xn @ linear(weights, l, "w_up").T
         Hh = G / (1.0 + np.exp(-G)) * U
-        X = X + Hh @ linear(weights, l, "w_down").T
+        X = X + act(weights, Hh) @ linear(weights, l, "w_down").T
     xf = _rms(X[-1], dec16(weights.final_norm, efmt), w.eps)
-    return lm_head(weights) @ xf
+    return lm_head(weights) @ act(weights, xf)

@@ -134,6 +134,97 @@ def test_gemv_within_fp32_error_bound(fmt):
 
 
 # ------------------------------------------------------------------------------------------------
+# weight-only integer formats (W8A16 / W4A16): codes, group scales, binary16 activations
+# ------------------------------------------------------------------------------------------------
+def _bf16_bits(v) -> np.ndarray:
+    return (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_int8_codes_are_twos_complement_bytes():
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    S = _bf16_bits([[1.0, 1.0]])
+    got = oracle.weight_matrix(oracle.I8, codes.view(np.int8), S)
+    assert np.array_equal(got[0], codes[0].view(np.int8).astype(np.float32))
+    assert got[0, 0x80] == -128 and got[0, 0xFF] == -1 and got[0, 0x7F] == 127
+
+
+def test_int4_codes_low_nibble_is_the_even_column():
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)  # 512 columns
+    S = _bf16_bits([[1.0] * 4])
+    got = oracle.weight_matrix(oracle.I4, b, S)[0]
+    lo = (b[0].astype(np.int64) & 15 ^ 8) - 8  # 4-bit two's complement by the xor-subtract identity
+    hi = (b[0].astype(np.int64) >> 4 ^ 8) - 8
+    assert np.array_equal(got[0::2], lo.astype(np.float32))
+    assert np.array_equal(got[1::2], hi.astype(np.float32))
+    # hand-decoded bytes: 0x8F holds (-1, -8), 0x70 holds (0, 7)
+    assert list(got[2 * 0x8F: 2 * 0x8F + 2]) == [-1.0, -8.0]
+    assert list(got[2 * 0x70: 2 * 0x70 + 2]) == [0.0, 7.0]
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_int_group_scales_index_row_and_128_column_group(fmt):
+    rows, cols = 3, 300  # groups of 128, 128 and a ragged 44
+    ng = 3
+    if fmt == "int8":
+        codes = np.ones((rows, cols), np.int8)
+    else:
+        codes = np.full((rows, cols // 2), 0x11, np.uint8)  # +1 in both nibbles
+    S = _bf16_bits([[2.0 ** (3 * r + g) for g in range(ng)] for r in range(rows)])
+    y = oracle.gemv(oracle.FMT[fmt], codes, np.ones(cols, np.float32), S)
+    ref = [128 * 2.0 ** (3 * r) + 128 * 2.0 ** (3 * r + 1) + 44 * 2.0 ** (3 * r + 2) for r in range(rows)]
+    assert list(y) == ref
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_int_gemv_rounds_the_activation_to_binary16(fmt):
+    cols = 256
+    codes = np.ones((1, cols), np.int8) if fmt == "int8" else np.full((1, cols // 2), 0x11, np.uint8)
+    S = _bf16_bits([[1.0, 1.0]])
+    # 1 + 2^-12 is below half a binary16 step at 1 (2^-11): it rounds to 1
+    y = oracle.gemv(oracle.FMT[fmt], codes, np.full(cols, 1 + 2.0 ** -12, np.float32), S)
+    assert y[0] == cols
+    # 1 + 3 * 2^-11 lies halfway between 1 + 2^-10 and 1 + 2^-9: the tie goes to the even 1 + 2^-9
+    y = oracle.gemv(oracle.FMT[fmt], codes, np.full(cols, 1 + 3 * 2.0 ** -11, np.float32), S)
+    assert y[0] == cols * (1 + 2.0 ** -9)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_int_gemv_within_fp32_error_bound(fmt):
+    rows, cols = 200, 640
+    raw = synthgen.normal(12, 3, (rows, cols), 0.02, synthgen.FMT_BF16)
+    q, S = synthgen.quant_int_group(raw, 8 if fmt == "int8" else 4)
+    x = RNG.standard_normal(cols).astype(np.float32)
+    Wd = brute.int_codes(q, fmt) * np.repeat(brute.dec16(S, "bf16"), 128, 1)[:, :cols]
+    x16 = x.astype(np.float16).astype(np.float64)  # numpy's own nearest-even binary16 rounding
+    got = oracle.gemv(oracle.FMT[fmt], q, x, S)
+    ref = Wd @ x16
+    u = 2.0 ** -24
+    gamma = cols * u / (1 - cols * u)  # code * bf16 scale is exact in fp32
+    bound = gamma * (np.abs(Wd) @ np.abs(x16))
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.abs(ref).max() > 10 * bound.max()
+    # the binary16 rounding is visible: unrounded activations give results far outside the oracle's
+    # distance from the rounded reference
+    assert np.abs(Wd @ x.astype(np.float64) - ref).max() > 20 * np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_int_quantiser_reconstructs_each_weight_within_half_a_step(bits):
+    """The generator's group quantiser (shared input data, not oracle arithmetic)."""
+    rows, cols = 64, 300
+    raw = synthgen.normal(13, 4, (rows, cols), 0.02, synthgen.FMT_BF16)
+    q, S = synthgen.quant_int_group(raw, bits)
+    fmt = "int8" if bits == 8 else "int4"
+    s = np.repeat(brute.dec16(S, "bf16"), 128, 1)[:, :cols]
+    w = brute.dec16(raw, "bf16")
+    qmax = 127 if bits == 8 else 7
+    codes = brute.int_codes(q, fmt)
+    assert np.abs(codes).max() == qmax  # the group maximum maps to the largest code
+    # half a step, plus the clamp when bf16 rounded the scale down (|w| / s <= qmax (1 + 2^-8))
+    assert np.all(np.abs(w - codes * s) <= s * (0.5 + qmax * 2.0 ** -8))
+
+
+# ------------------------------------------------------------------------------------------------
 # RMSNorm
 # ------------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("c", [0.003, 0.5, -2.0, 40.0])
@@ -413,6 +504,20 @@ def test_fp8_model_matches_fp64_brute_force():
     assert np.abs(lg - ref).max() < 2e-3 and np.abs(ref).max() > 0.1
     _, lg2 = m.step(tok)
     ref2 = brute.logits_all(wts, list(prompt) + [tok], kv_scales=scales)
+    assert np.abs(lg2 - ref2).max() < 2e-3
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_int_model_matches_fp64_brute_force(fmt):
+    w = TINY.with_(wdtype=fmt, kvdtype="bf16", hidden=256, ffn=384, layers=2)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    m = oracle.OracleModel(wts)
+    prompt = synthgen.make_prompt(w, 8)
+    tok, lg = m.prefill(prompt)
+    ref = brute.logits_all(wts, prompt)
+    assert np.abs(lg - ref).max() < 2e-3 and np.abs(ref).max() > 0.1
+    _, lg2 = m.step(tok)
+    ref2 = brute.logits_all(wts, list(prompt) + [tok])
     assert np.abs(lg2 - ref2).max() < 2e-3
 
 
