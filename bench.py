@@ -291,7 +291,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8-e4m3 (fp32 accumulate)"}[w.wdtype],
+        "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8-e4m3 (fp32 accumulate)",
+                  "int8": "int8 weights, f16 activations (fp32 accumulate)",
+                  "int4": "int4 weights, f16 activations (fp32 accumulate)"}[w.wdtype],
         "data": "synthetic (seeded N(0,0.02) weights, random prompt)",
         "config": {"workload": w.name, "layers": w.layers, "hidden": w.hidden, "heads": [w.n_q, w.n_kv],
                    "head_dim": w.head_dim, "ffn": w.ffn, "vocab": w.vocab, "prompt": P, "decode_steps": K,

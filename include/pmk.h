@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PMK_ABI_VERSION 2
+#define PMK_ABI_VERSION 3
 
 typedef enum {
   PMK_OK = 0,
@@ -62,7 +62,17 @@ typedef enum {
   PMK_ERR_DEVICE = 9            /* the device cannot co-schedule the grid, or is not gfx950 */
 } pmk_status;
 
-typedef enum { PMK_DT_F16 = 0, PMK_DT_BF16 = 1, PMK_DT_FP8_E4M3 = 2 } pmk_dtype;
+/* Storage formats.  INT8 and INT4 are weight-only formats (W8A16 / W4A16; passage: the
+ * AutoMegaKernel explainer, results, which name weight-only int8 and int4 megakernels): symmetric
+ * two's-complement codes with one bf16 scale per row and 128-column group, w = q * s, and the
+ * activation operand of each linear layer taken in binary16. */
+typedef enum {
+  PMK_DT_F16 = 0,
+  PMK_DT_BF16 = 1,
+  PMK_DT_FP8_E4M3 = 2,
+  PMK_DT_INT8 = 3, /* one signed byte per weight */
+  PMK_DT_INT4 = 4  /* two per byte, the even column in the low nibble */
+} pmk_dtype;
 
 typedef enum {
   PMK_MODE_MEGAKERNEL = 0, /* one persistent cooperative launch per decode call */
@@ -80,9 +90,12 @@ typedef enum {
 } pmk_sync_mode;
 
 /* The operation contract.  Supported: no biases, untied embeddings, head_dim in {64, 128},
- * n_q_heads % n_kv_heads == 0, hidden, ffn, n_q_heads*head_dim multiples of 8 (16 for FP8),
- * weight_dtype in {F16, BF16, FP8_E4M3} and kv_dtype in {F16, BF16, FP8_E4M3};
- * FP8 weights use 128x128 fp32 block scales, and their embedding and norm gains are BF16. */
+ * n_q_heads % n_kv_heads == 0, hidden, ffn, n_q_heads*head_dim multiples of 8 (16 for FP8 and
+ * INT8, 32 for INT4), and (weight_dtype, kv_dtype) one of (F16, F16), (BF16, BF16),
+ * (FP8_E4M3, FP8_E4M3), (INT8, BF16), (INT4, BF16).  FP8 weights use 128x128 fp32 block scales;
+ * INT8 / INT4 weights one bf16 scale per row and 128-column group (the last group of a row may be
+ * shorter), and their GEMVs round the activation vector to binary16 and accumulate in fp32.  The
+ * embedding and norm gains of FP8, INT8 and INT4 models are BF16. */
 typedef struct {
   int32_t n_layers;
   int32_t hidden;
@@ -127,21 +140,24 @@ typedef struct {
 } pmk_sizes;
 
 /* Device pointers to the canonical tensors (row-major [out][in] for every linear weight):
- *   embed[V][H], final_norm[H], lm_head[V][H] (+ lm_head_scale[ceil(V/128)][ceil(H/128)] for FP8),
+ *   embed[V][H], final_norm[H], lm_head[V][H] (+ lm_head_scale: [ceil(V/128)][ceil(H/128)] fp32
+ *   for FP8, [V][ceil(H/128)] bf16 for INT8 / INT4),
  *   layers: n_layers * 9 pointers, per layer in order
  *     wq[nq*hd][H], wk[nkv*hd][H], wv[nkv*hd][H], wo[H][nq*hd], w_gate[F][H], w_up[F][H],
  *     w_down[H][F], attn_norm[H], ffn_norm[H]
- *   layer_scales (FP8 weights only, else NULL): n_layers * 7 pointers, the block scales of the
- *     7 linear tensors, each [ceil(out/128)][ceil(in/128)] fp32.
- * 16-bit tensors are raw F16/BF16 bits; FP8 tensors are E4M3FN bytes.  The host arrays of
- * pointers are read during the call only. */
+ *   layer_scales (FP8, INT8 and INT4 weights, else NULL): n_layers * 7 pointers, the scales of
+ *     the 7 linear tensors, each [ceil(out/128)][ceil(in/128)] fp32 (FP8) or [out][ceil(in/128)]
+ *     bf16 bits (INT8 / INT4).
+ * 16-bit tensors are raw F16/BF16 bits; FP8 tensors are E4M3FN bytes; INT8 tensors are int8
+ * [out][in]; INT4 tensors are bytes [out][in/2] (column 2j in the low nibble of byte j, 2j+1 in
+ * the high one).  The host arrays of pointers are read during the call only. */
 typedef struct {
   const void* embed;
   const void* final_norm;
   const void* lm_head;
-  const float* lm_head_scale;
+  const void* lm_head_scale;
   const void* const* layers;
-  const float* const* layer_scales;
+  const void* const* layer_scales;
 } pmk_weight_ptrs;
 
 /* Watchdog / device error record (pmk_poll_error). */
@@ -226,13 +242,15 @@ pmk_status pmk_bind(pmk_ctx* ctx, void* d_arena, void* d_kv, void* d_workspace);
 pmk_status pmk_bind_static_workspace(pmk_ctx* ctx, void* d_arena, void* d_kv);
 
 /* Repack the canonical tensors into the arena (QKV rows concatenated with each RoPE pair made
- * adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table).
+ * adjacent, gate/up rows interleaved, gains widened to fp32, RoPE cos/sin table; INT8 / INT4 codes
+ * re-encoded for the kernels' conversion to binary16: offset binary, int4 nibbles reordered within
+ * each 32-bit word).
  * Passages: [Netra] details (weight layout and FP8 E4M3 block-scale semantics are fixed ahead of
  * time); [AMK] Method (HF Llama-family models are imported into the schedule).
  * src: device pointers to the canonical tensors (pmk_weight_ptrs; the host arrays are read during
  * the call only).  Asynchronous on `stream` (a hipStream_t, NULL = default stream); the sources may
  * be freed once the stream has synchronised.  Errors: PMK_ERR_NOT_BOUND, PMK_ERR_INVALID_ARG
- * (missing pointers or FP8 scales), PMK_ERR_HIP. */
+ * (missing pointers or scales), PMK_ERR_HIP. */
 pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stream);
 
 /* Teacher-forced prefill: runs positions 0..P-1 from d_tokens[P] (device int32), writing the KV
@@ -347,8 +365,10 @@ typedef struct {
  * the hardware, moved fully or half-way from even), the O-projection rows on the combine queues
  * (none, half, full), the combines per kv head and fewer attention splits.  A candidate is kept if
  * it emits the same greedy token at every measured step as the starting schedule, with the same
- * largest logit within 1e-3 (a schedule change only regroups partial sums), and is faster than the
- * best so far by more than 0.2%; otherwise the best schedule is reinstalled.  Rate-based candidates
+ * largest logit within 1e-3 (a schedule change only regroups partial sums; 2e-2 for INT8 / INT4,
+ * whose binary16 operand rounding moves some elements by a whole step when a sum regroups), and is
+ * faster than the best so far by more than 0.2%; otherwise the best schedule is reinstalled.
+ * Rate-based candidates
  * need a context created with trace_steps >= 2.  Every schedule change clears the synchronisation
  * state; the position and next token are restored (KV rows past the position are rewritten by the
  * next decode).  Synchronous on `stream`.  *result may be NULL.  Errors: PMK_ERR_NOT_BOUND,

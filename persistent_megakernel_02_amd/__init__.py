@@ -11,12 +11,13 @@ import ctypes
 from typing import Optional
 
 from . import _lib
-from ._lib import (PMK_DT_BF16, PMK_DT_F16, PMK_DT_FP8_E4M3, PMK_MODE_GRAPH, PMK_MODE_MEGAKERNEL,  # noqa: F401
+from ._lib import (PMK_DT_BF16, PMK_DT_F16, PMK_DT_FP8_E4M3, PMK_DT_INT4, PMK_DT_INT8,  # noqa: F401
+                   PMK_MODE_GRAPH, PMK_MODE_MEGAKERNEL,
                    PMK_MODE_PER_OP, PMK_SYNC_COUNTERS, PMK_SYNC_FLAGS, PmkError, check, load, pmk_device_error,
                    pmk_model_config, pmk_schedule_config, pmk_schedule_info, pmk_sizes, pmk_task, pmk_tune_result,
                    pmk_weight_ptrs)
 
-_DT = {"f16": PMK_DT_F16, "bf16": PMK_DT_BF16, "fp8": PMK_DT_FP8_E4M3}
+_DT = {"f16": PMK_DT_F16, "bf16": PMK_DT_BF16, "fp8": PMK_DT_FP8_E4M3, "int8": PMK_DT_INT8, "int4": PMK_DT_INT4}
 
 
 def model_config(w, max_seq: Optional[int] = None) -> pmk_model_config:

@@ -22,7 +22,7 @@ PMK_ERR_TIMEOUT = 7
 PMK_ERR_NAN = 8
 PMK_ERR_DEVICE = 9
 
-PMK_DT_F16, PMK_DT_BF16, PMK_DT_FP8_E4M3 = 0, 1, 2
+PMK_DT_F16, PMK_DT_BF16, PMK_DT_FP8_E4M3, PMK_DT_INT8, PMK_DT_INT4 = 0, 1, 2, 3, 4
 PMK_MODE_MEGAKERNEL, PMK_MODE_GRAPH, PMK_MODE_PER_OP = 0, 1, 2
 PMK_SYNC_FLAGS, PMK_SYNC_COUNTERS = 0, 1
 PMK_OP_QKV, PMK_OP_ATTN, PMK_OP_OPROJ, PMK_OP_GATEUP, PMK_OP_DOWN, PMK_OP_LMHEAD, PMK_OP_TOKEN = range(1, 8)

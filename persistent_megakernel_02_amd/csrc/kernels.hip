@@ -26,6 +26,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "pmk_device.h"
 
@@ -34,7 +35,7 @@ namespace pmk {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-enum { WF16 = 0, WBF16 = 1, WFP8 = 2 };
+enum { WF16 = 0, WBF16 = 1, WFP8 = 2, WI8 = 3, WI4 = 4 };
 
 // ------------------------------------------------------------------------------------------------
 // coherent (agent scope) accesses
@@ -253,13 +254,81 @@ __device__ __forceinline__ void block_signal(const KParams& P, int ctr, int slot
 // ------------------------------------------------------------------------------------------------
 template <int WDT>
 struct WFmt {
-  static constexpr int EPL = WDT == WFP8 ? 16 : 8;  // elements per 16-byte chunk
-  static constexpr int ES = WDT == WFP8 ? 1 : 2;     // bytes per element
+  static constexpr int EPL = weight_epl(WDT);      // elements per 16-byte chunk
+  static constexpr bool SCALED = WDT >= WFP8;      // a scale per 128-column group of a chunk's row
+  static constexpr bool H16 = weight_is_int(WDT);  // the GEMV's activation vector is staged as binary16
+  static constexpr int CPG = 128 / EPL;            // chunks per 128-column scale group
+  static constexpr int EDT = WDT >= WFP8 ? WBF16 : WDT;  // format of the embedding (and gains)
+  // scale element: fp32 per 128x128 block (fp8), bf16 bits per row and 128-column group (int)
+  using ST = typename std::conditional<WDT == WFP8, float, uint16_t>::type;
+  static __device__ __forceinline__ int64_t row_bytes(int K) { return (int64_t)(K / EPL) * 16; }
 };
 
 template <int WDT>
+__device__ __forceinline__ float scale_value(typename WFmt<WDT>::ST s) {
+  if constexpr (WDT == WFP8) return s;
+  else return __uint_as_float((uint32_t)s << 16);
+}
+
+// The activation elements of chunk c (EPL of them) in the staged vector: fp32, or binary16 pairs
+// packed two to a 32-bit word for the integer formats.
+template <int WDT>
+__device__ __forceinline__ const float* xchunk(const float* xs, int c) {
+  return WFmt<WDT>::H16 ? xs + c * (WFmt<WDT>::EPL / 2) : xs + c * WFmt<WDT>::EPL;
+}
+
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h16x2 as_h2(uint32_t u) { return __builtin_bit_cast(h16x2, u); }
+
+// Integer weight codes (stored offset binary: int8 q + 128 per byte; int4 q + 8 per nibble, the
+// nibbles of each 32-bit word holding columns 0 2 4 6 1 3 5 7 from the low end) -> binary16 pairs
+// of consecutive columns, exactly: a code u placed in the low mantissa bits of 1024.0 (0x6400)
+// is the binary16 value 1024 + u, and one packed add (or fma, for a nibble sitting 4 bits up)
+// removes 1024 and the offset.  Each pair then goes through one v_dot2 (fp32 accumulate) with
+// the matching pair of binary16 activations.
+__device__ __forceinline__ float dot_i8_word(uint32_t w, uint32_t x01, uint32_t x23, float acc) {
+  const h16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const h16x2 lo = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) + bias;  // columns 0, 1
+  const h16x2 hi = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)) + bias;  // columns 2, 3
+  acc = __builtin_amdgcn_fdot2(lo, as_h2(x01), acc, false);
+  return __builtin_amdgcn_fdot2(hi, as_h2(x23), acc, false);
+}
+
+__device__ __forceinline__ float dot_i4_word(uint32_t w, u32x4 x, float acc) {
+  const h16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h16x2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h16x2 b2 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  const h16x2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + b1;                                  // columns 0, 1
+  const h16x2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), m16, b2);   // columns 2, 3
+  const h16x2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + b1;                                 // columns 4, 5
+  const h16x2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), m16, b2);  // columns 6, 7
+  acc = __builtin_amdgcn_fdot2(p0, as_h2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(p1, as_h2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(p2, as_h2(x.z), acc, false);
+  return __builtin_amdgcn_fdot2(p3, as_h2(x.w), acc, false);
+}
+
+template <int WDT>
 __device__ __forceinline__ float chunk_dot(u32x4 w, const float* __restrict__ x) {
-  if constexpr (WDT == WFP8) {
+  if constexpr (WDT == WI8) {  // 16 columns; x: 16 binary16 (two 16-byte LDS reads)
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(x);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(x + 4);
+    float a = 0.f, b = 0.f;
+    a = dot_i8_word(w.x, xa.x, xa.y, a);
+    b = dot_i8_word(w.y, xa.z, xa.w, b);
+    a = dot_i8_word(w.z, xb.x, xb.y, a);
+    b = dot_i8_word(w.w, xb.z, xb.w, b);
+    return a + b;
+  } else if constexpr (WDT == WI4) {  // 32 columns; x: 32 binary16 (four 16-byte LDS reads)
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+    float a = 0.f, b = 0.f;
+    a = dot_i4_word(w.x, xv[0], a);
+    b = dot_i4_word(w.y, xv[1], b);
+    a = dot_i4_word(w.z, xv[2], a);
+    b = dot_i4_word(w.w, xv[3], b);
+    return a + b;
+  } else if constexpr (WDT == WFP8) {
     const float4 x0 = *reinterpret_cast<const float4*>(x);
     const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
     const float4 x2 = *reinterpret_cast<const float4*>(x + 8);
@@ -336,7 +405,9 @@ constexpr int prefetch_depth() { return PMK_PREFETCH_UNITS < ring_depth<WDT>() ?
 
 // Split of one GEMV tile over the 8 waves: KS slices of every row's K times 8/KS groups of rows;
 // KS minimises the busiest wave's cost, units plus row_cost per row (a row ends in a wave-wide
-// reduction; short tiles then still keep all waves streaming).  Wave w takes row group w / KS
+// reduction; short tiles then still keep all waves streaming).  KS never exceeds the row's slice
+// count: every wave of a row group then owns at least one slice, so every partial sum the
+// reduction reads (one per row and slice range) is written.  Wave w takes row group w / KS
 // and slice range w % KS; its units (one 16-byte chunk per lane of one row and one 64-chunk
 // slice) run row by row, slices in order within a row.
 struct TileSplit {
@@ -345,7 +416,7 @@ struct TileSplit {
     R = r1 - r0;
     int best = 0x7fffffff;
     KS = 1;
-    for (int ks = 1; ks <= kWaves; ks <<= 1) {
+    for (int ks = 1; ks <= kWaves && ks <= nsl; ks <<= 1) {
       const int g = kWaves / ks;
       const int cost = ((R + g - 1) / g) * ((nsl + ks - 1) / ks + row_cost);
       if (cost < best) { best = cost; KS = ks; }
@@ -376,7 +447,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
                                           int row_cost = 0) {
   constexpr int EPL = WFmt<WDT>::EPL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
+  const int64_t rb = WFmt<WDT>::row_bytes(K);
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
   const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const int R = sp.R, KS = sp.KS, si = sp.si, wr0 = sp.wr0, wr1 = sp.wr1, s0 = sp.s0, s1 = sp.s1;
@@ -391,24 +462,24 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + (int64_t)r0 * rb), (short)0, (int)((int64_t)R * rb), 0x00020000);
   constexpr uint32_t kOut = (uint32_t)kMaxTileBytes;  // past any tile the validator accepts
-  // The issue cursor (row, slice) moves row by row; the row's byte offset in the tile and (fp8)
-  // its block-scale row are updated when the row changes, not recomputed per unit: the fp8 loops
+  // The issue cursor (row, slice) moves row by row; the row's byte offset in the tile and (scaled
+  // formats) its scale row are updated when the row changes, not recomputed per unit: the fp8 loops
   // run close to the vector-ALU issue limit, and the per-unit index arithmetic was most of it.
   int lrow = wr0, lj = s0;
   uint32_t roff = (uint32_t)((int64_t)(wr0 - r0) * rb);
-  const float* srp = nullptr;
-  if constexpr (WDT == WFP8) srp = srow(wr0);
+  const typename WFmt<WDT>::ST* srp = nullptr;
+  if constexpr (WFmt<WDT>::SCALED) srp = srow(wr0);
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
     const bool ok = lrow < wr1 && c < nch;
     const uint32_t off = ok ? roff + (uint32_t)c * 16u : kOut;
     ring[d] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nontemporal
-    if constexpr (WDT == WFP8) rsc[d] = srp[(c < nch ? c : 0) >> 3];
+    if constexpr (WFmt<WDT>::SCALED) rsc[d] = scale_value<WDT>(srp[(uint32_t)(c < nch ? c : 0) / WFmt<WDT>::CPG]);
     if (++lj == s1) {
       lj = s0;
       ++lrow;
       roff += (uint32_t)rb;
-      if constexpr (WDT == WFP8) srp = srow(lrow < wr1 ? lrow : wr0);
+      if constexpr (WFmt<WDT>::SCALED) srp = srow(lrow < wr1 ? lrow : wr0);
     }
   };
   // kPre units per lane are issued before the dependency wait (when prefetching), the rest of the
@@ -436,8 +507,8 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
         // consume slot d, then refill it: the refill lands in the slot's own registers, so the
         // ring never needs copying (a copy would have to wait for every load in flight)
         if (base + d < nunits) {
-          const float part = chunk_dot<WDT>(ring[d], xs + (cj * 64 + lane) * EPL);
-          if constexpr (WDT == WFP8) acc = fmaf(part, rsc[d], acc);
+          const float part = chunk_dot<WDT>(ring[d], xchunk<WDT>(xs, cj * 64 + lane));
+          if constexpr (WFmt<WDT>::SCALED) acc = fmaf(part, rsc[d], acc);
           else acc += part;
           if (++cj == s1) {
             cj = s0;
@@ -471,7 +542,7 @@ template <int WDT>
 __device__ __forceinline__ void tile_to_lds(const uint8_t* __restrict__ W, int K, int r0, int r1, float* pf,
                                             int row_cost) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rb = (int64_t)K * WFmt<WDT>::ES;
+  const int64_t rb = WFmt<WDT>::row_bytes(K);
   const int nch = K / WFmt<WDT>::EPL, nsl = (nch + 63) >> 6;
   const TileSplit sp(r0, r1, nsl, wave, row_cost);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -540,9 +611,11 @@ __device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float
       float acc = 0.f;
       auto step = [&](const u32x4& w, int j) {
         const int c = j * 64 + lane;
-        const float part = chunk_dot<WDT>(w, xs + c * EPL);
-        if constexpr (WDT == WFP8) acc = fmaf(part, srow(row)[(c < nch ? c : 0) >> 3], acc);
-        else acc += part;
+        const float part = chunk_dot<WDT>(w, xchunk<WDT>(xs, c));
+        if constexpr (WFmt<WDT>::SCALED)
+          acc = fmaf(part, scale_value<WDT>(srow(row)[(uint32_t)(c < nch ? c : 0) / WFmt<WDT>::CPG]), acc);
+        else
+          acc += part;
       };
       int j = s0;
       for (; j + 4 <= s1; j += 4, u += 4) {  // four units' LDS reads in flight
@@ -569,9 +642,21 @@ __device__ __forceinline__ void gemv_rows_lds(int K, int r0, int r1, const float
 // ------------------------------------------------------------------------------------------------
 // input staging (RMSNorm prologue fused into the consuming GEMV)
 // ------------------------------------------------------------------------------------------------
+// Two fp32 values as a binary16 pair (nearest even), the lower element in the low half.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, h16x2));
+}
+
+// Store staged elements i, i+1 of the activation vector: fp32, or one binary16 pair (H16).
+template <bool H16>
+__device__ __forceinline__ void put2(float* xs, int i, float a, float b) {
+  if constexpr (H16) reinterpret_cast<uint32_t*>(xs)[i >> 1] = pack_h2(a, b);
+  else *reinterpret_cast<float2*>(xs + i) = make_float2(a, b);
+}
+
 // Load n fp32 values from a coherent buffer into xs[0..pad) (zeros past n), every load of a
-// batch issued before any is consumed.
-template <int B = 8>
+// batch issued before any is consumed.  H16 stores them as binary16.
+template <bool H16 = false, int B = 8>
 __device__ __forceinline__ void load_vector(const float* src, int n, int pad, float* xs) {
   const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 4);
   for (int base = 0; base < pad; base += B * 4 * kThreads) {
@@ -584,7 +669,13 @@ __device__ __forceinline__ void load_vector(const float* src, int n, int pad, fl
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       const int i = base + (k * kThreads + (int)threadIdx.x) * 4;
-      if (i < pad) *reinterpret_cast<float4*>(xs + i) = as_f4(v[k]);
+      if (i < pad) {
+        const float4 f = as_f4(v[k]);
+        if constexpr (H16)
+          *reinterpret_cast<uint2*>(xs + (i >> 1)) = make_uint2(pack_h2(f.x, f.y), pack_h2(f.z, f.w));
+        else
+          *reinterpret_cast<float4*>(xs + i) = f;
+      }
     }
   }
 }
@@ -593,9 +684,12 @@ __device__ __forceinline__ void load_vector(const float* src, int n, int pad, fl
 // and red[w] = wave w's share of sum(src^2), with one batch of loads and one barrier; the factor
 // 1/sqrt(mean(src^2) + eps) (rms_factor) then scales the GEMV results, since every row's dot
 // product with (src * gain) times that factor is its dot product with the normalised input.
+// With RAW (the integer weight formats) xs holds src itself, and norm_to_h16 then forms the
+// normalised vector (src * r) * gain and rounds it to binary16, the activation operand those
+// formats define.
 // This one stages a 16-bit embedding row (the first layer's input); stage_rmsnorm_tagged stages
 // the tagged residual stream.
-template <int EDT>
+template <int EDT, bool RAW = false>
 __device__ __forceinline__ void stage_rmsnorm_embed(const uint16_t* emb, const float* gain, int H, int pad, float* xs,
                                                     float* red) {
   float ss = 0.f;
@@ -619,7 +713,7 @@ __device__ __forceinline__ void stage_rmsnorm_embed(const uint16_t* emb, const f
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      xs[i + k] = f[k] * g[k];
+      xs[i + k] = RAW ? f[k] : f[k] * g[k];
       ss = fmaf(f[k], f[k], ss);
     }
   }
@@ -633,6 +727,26 @@ __device__ __forceinline__ float rms_factor(const float* red, int H, float eps) 
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t += red[w];
   return 1.0f / sqrtf(t / (float)H + eps);
+}
+
+// Integer weight formats: after an RMSNorm staging with RAW / H16 (xs = src in fp32, red = the wave
+// sums, behind a barrier), xh[0..pad) = binary16((src * r) * gain) with r = 1 / sqrt(mean(src^2) +
+// eps) (zeros past H), the normalised vector in the order of operations of its definition; ends
+// with a barrier.  The GEMV results then need no factor.
+__device__ __forceinline__ void norm_to_h16(const float* xs, const float* gain, int H, int pad, const float* red,
+                                            float eps, float* xh) {
+  const float r = rms_factor(red, H, eps);
+  for (int i = 2 * (int)threadIdx.x; i < pad; i += 2 * kThreads) {
+    float a = 0.f, b = 0.f;
+    if (i < H) {
+      const float2 x = *reinterpret_cast<const float2*>(xs + i);
+      const float2 g = *reinterpret_cast<const float2*>(gain + i);
+      a = (x.x * r) * g.x;
+      b = (x.y * r) * g.y;
+    }
+    reinterpret_cast<uint32_t*>(xh)[i >> 1] = pack_h2(a, b);
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ int pad_len(int n, int epl) {
@@ -658,7 +772,7 @@ struct StepCtx {
 // checked on every retry).  The reads are the wait; the caller's barrier ends it.  With NORM, xs
 // holds src * gain and the return value is this thread's share of sum(src^2) (the gains are
 // loaded before the first read, since they do not depend on the wait).
-template <bool NORM = false>
+template <bool NORM = false, bool H16 = false>
 __device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned long long* src, int n, int pad,
                                               float* xs, int e, bool poll, int cu, int task,
                                               const float* gain = nullptr) {
@@ -704,21 +818,24 @@ __device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned l
       if constexpr (NORM) {
         ss = fmaf(a, a, ss);
         ss = fmaf(b, b, ss);
-        a *= g[k].x;
-        b *= g[k].y;
+        if constexpr (!H16) {  // H16 with NORM: src itself, normalised by norm_to_h16
+          a *= g[k].x;
+          b *= g[k].y;
+        }
       }
-      if (i < pad) *reinterpret_cast<float2*>(xs + i) = make_float2(a, b);
+      if (i < pad) put2<H16 && !NORM>(xs, i, a, b);
     }
   }
   return ss;
 }
 
-// RMSNorm prologue from a tagged vector (as stage_rmsnorm): xs = src * gain, red[w] = wave w's
-// share of sum(src^2), one barrier.
+// RMSNorm prologue from a tagged vector (as stage_rmsnorm): xs = src * gain (H16: src), red[w] =
+// wave w's share of sum(src^2), one barrier.
+template <bool H16 = false>
 __device__ __forceinline__ void stage_rmsnorm_tagged(const KParams& P, const unsigned long long* src, const float* gain,
                                                      int H, int pad, float* xs, float* red, int e, bool poll, int cu,
                                                      int task) {
-  float ss = stage_tagged<true>(P, src, H, pad, xs, e, poll, cu, task, gain);
+  float ss = stage_tagged<true, H16>(P, src, H, pad, xs, e, poll, cu, task, gain);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -788,9 +905,16 @@ __device__ __forceinline__ void maybe_wait(const KParams& P, const pmk_task& t, 
 // ------------------------------------------------------------------------------------------------
 // tasks
 // ------------------------------------------------------------------------------------------------
+// Scale array of linear tensor `which` (q k v o gate up down) of layer l, and the scale row of
+// its (unpacked) row orow: one row per 128 rows for fp8 blocks, one per row for the integer groups.
 template <int WDT>
-__device__ __forceinline__ const float* fp8_rows(const KParams& P, int l, int which) {
-  return P.scales + (int64_t)l * P.sc_layer + P.sc_off[which];
+__device__ __forceinline__ const typename WFmt<WDT>::ST* scale_rows(const KParams& P, int l, int which) {
+  return reinterpret_cast<const typename WFmt<WDT>::ST*>(P.scales) + (int64_t)l * P.sc_layer + P.sc_off[which];
+}
+template <int WDT>
+__device__ __forceinline__ const typename WFmt<WDT>::ST* scale_row(const typename WFmt<WDT>::ST* base, int orow,
+                                                                   int nbc) {
+  return base + (int64_t)(WDT == WFP8 ? orow / 128 : orow) * nbc;
 }
 
 // QKV: RMSNorm(x) -> packed QKV rows [a0, a1) -> RoPE on q/k pairs -> q to the workspace,
@@ -799,7 +923,8 @@ __device__ __forceinline__ const float* fp8_rows(const KParams& P, int l, int wh
 template <int WDT, int KVDT>
 __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                          int cu) {
-  constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
+  constexpr int EDT = WFmt<WDT>::EDT;
+  constexpr bool H16 = WFmt<WDT>::H16;
   const int l = t.layer, H = P.H, hd = P.hd, half = hd / 2;
   const int pad = pad_len(H, WFmt<WDT>::EPL);
   float* xs = lds;
@@ -822,11 +947,12 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
       if (threadIdx.x < 2 * P.nkv) rope[half + threadIdx.x] = make_float2(ks8, 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
-      stage_rmsnorm_embed<EDT>(P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
+      stage_rmsnorm_embed<EDT, H16>(P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
     } else {
-      stage_rmsnorm_tagged(P, P.x + (int64_t)l * H, P.gains + (int64_t)l * 2 * H, H, pad, xs, red, sc.e,
+      stage_rmsnorm_tagged<H16>(P, P.x + (int64_t)l * H, P.gains + (int64_t)l * 2 * H, H, pad, xs, red, sc.e,
                            !sc.per_op, cu, ti);
     }
+    if constexpr (H16) norm_to_h16(xs, P.gains + (int64_t)l * 2 * H, H, pad, red, P.eps, lds + P.xh_off);
     if (poll_x) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
@@ -834,22 +960,24 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
   const int nbc = (H + 127) / 128;
   // scale-array bases taken before the loop (a dynamically indexed kernel argument would be
   // re-read from memory for every weight unit, behind a full wait)
-  const float* const sq = fp8_rows<WDT>(P, l, 0);
-  const float* const sk = fp8_rows<WDT>(P, l, 1);
-  const float* const sv = fp8_rows<WDT>(P, l, 2);
-  auto srow = [=](int r) -> const float* {
-    const float* base;
+  using ST = typename WFmt<WDT>::ST;
+  const ST* const sq = scale_rows<WDT>(P, l, 0);
+  const ST* const sk = scale_rows<WDT>(P, l, 1);
+  const ST* const sv = scale_rows<WDT>(P, l, 2);
+  auto srow = [=](int r) -> const ST* {
+    const ST* base;
     int orow;
     if (r < qrows) { base = sq; orow = r; }
     else if (r < qrows + krows) { base = sk; orow = r - qrows; }
     else { base = sv; orow = r - qrows - krows; }
     const int head = orow / hd, pr = orow % hd;
     const int dim = (pr >> 1) + (pr & 1) * half;
-    return base + (int64_t)((head * hd + dim) / 128) * nbc;
+    return scale_row<WDT>(base, head * hd + dim, nbc);
   };
-  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
+  // integer formats: the GEMV reads the normalised binary16 vector, whose results need no factor
+  gemv_rows<WDT>(W, H, t.a0, t.a1, H16 ? lds + P.xh_off : xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
-  const float rn = rms_factor(red, H, P.eps);
+  const float rn = H16 ? 1.0f : rms_factor(red, H, P.eps);
   const int npairs = (t.a1 - t.a0) >> 1;
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
     const int r = t.a0 + 2 * p;
@@ -985,6 +1113,29 @@ __device__ __forceinline__ void split16(const float* x, u32x4& hi, u32x4& lo) {
   lo = u32x4{o[0], o[1], o[2], o[3]};
 }
 
+// fp32 x[8] as three bf16 vectors with x = hi + mid + lo to ~2^-24 relative (three products).
+// The integer weight formats take this one: their GEMVs round the attention output to binary16,
+// which turns a difference of ~2^-17 in it into a whole binary16 step in some elements, so the
+// attention is computed to fp32 accuracy there.
+__device__ __forceinline__ void split16x3(const float* x, u32x4& hi, u32x4& mid, u32x4& lo) {
+  uint32_t h[4], m[4], o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = x[2 * k], b = x[2 * k + 1];
+    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const float ra = a - __uint_as_float(hb << 16), rb = b - __uint_as_float(hb & 0xFFFF0000u);
+    const uint32_t mb = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
+    h[k] = hb;
+    m[k] = mb;
+    o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                            (f32x2){ra - __uint_as_float(mb << 16), rb - __uint_as_float(mb & 0xFFFF0000u)},
+                                            bf16x2));
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  mid = u32x4{m[0], m[1], m[2], m[3]};
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // 8 FP8 E4M3 values -> 8 bf16 (exact)
 __device__ __forceinline__ u32x4 fp8x8_bf16(u32x2 w) {
   const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
@@ -1040,6 +1191,7 @@ template <int WDT, int KVDT, int HD, int NGW, bool G2LDS, bool COH>
 __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                           int cu) {
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
+  constexpr bool X3 = weight_is_int(WDT) && KVDT == WBF16;  // q and P in three bf16 terms (split16x3)
   constexpr int ROWB = HD * KES;      // K row bytes
   constexpr int NC = HD / 32;         // 32-dim slices of the score product
   constexpr int NT = HD / 16;         // 16-dim tiles of P.V
@@ -1257,7 +1409,14 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[e] = col < grp ? qs[col * HD + 32 * c + 8 * grp4 + e] : 0.f;
       u32x4 qh, ql;
-      split16<KVDT>(qv, qh, ql);
+      if constexpr (X3) {
+        u32x4 qm;
+        split16x3(qv, qh, qm, ql);
+        s0 = mfma16<KVDT>(ka[c], qm, s0);
+        s1 = mfma16<KVDT>(kb[c], qm, s1);
+      } else {
+        split16<KVDT>(qv, qh, ql);
+      }
       s0 = mfma16<KVDT>(ka[c], qh, s0);
       s0 = mfma16<KVDT>(ka[c], ql, s0);
       s1 = mfma16<KVDT>(kb[c], qh, s1);
@@ -1295,7 +1454,14 @@ __device__ __forceinline__ void task_attn(const KParams& P, const pmk_task& t, i
     // ---- P.V: 16 dims x 16 head columns per tile ----
     patch_v(k);
     u32x4 ph, pl;
-    split16<KVDT>(sc8, ph, pl);
+    if constexpr (X3) {
+      u32x4 pm;
+      split16x3(sc8, ph, pm, pl);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma16<KVDT>(vt[tt], pm, acc[tt]);
+    } else {
+      split16<KVDT>(sc8, ph, pl);
+    }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       acc[tt] = mfma16<KVDT>(vt[tt], ph, acc[tt]);
@@ -1418,7 +1584,7 @@ __device__ __forceinline__ void task_combine(const KParams& P, const pmk_task& t
 template <int WDT>
 __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                            int cu, bool tile_copied = false) {
-  constexpr int EDT = WDT == WFP8 ? WBF16 : WDT;
+  constexpr int EDT = WFmt<WDT>::EDT;
   const int l = t.layer, K = P.qdim, R = t.a1 - t.a0;
   // compact LDS layout (o, residual rows, partial sums, results) below the LDS tile area
   float* xs = lds;
@@ -1438,15 +1604,17 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
     for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
       res[i] = l == 0 ? dec16<EDT>(P.embed[(int64_t)tok * P.H + t.a0 + i])
                       : ld_tagged(P, P.x + (int64_t)l * P.H + t.a0 + i, sc.e, !sc.per_op, cu, ti);
-    stage_tagged(P, P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs, sc.e, !sc.per_op, cu, ti);
+    stage_tagged<false, WFmt<WDT>::H16>(P, P.o + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs, sc.e, !sc.per_op,
+                                        cu, ti);
     if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
     __syncthreads();
     if (poll_o) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
-  const float* const so = fp8_rows<WDT>(P, l, 3);
-  auto srow = [=](int r) -> const float* { return so + (int64_t)(r / 128) * nbc; };
+  using ST = typename WFmt<WDT>::ST;
+  const ST* const so = scale_rows<WDT>(P, l, 3);
+  auto srow = [=](int r) -> const ST* { return scale_row<WDT>(so, r, nbc); };
   if (oproj_tile_in_lds(P, t, sc, (K / WFmt<WDT>::EPL + 63) >> 6)) {
     if (!tile_copied) tile_to_lds<WDT>(W, K, t.a0, t.a1, lds + P.pf_off, kOprojRowCost);
     gemv_rows_lds<WDT>(K, t.a0, t.a1, xs, lds + P.pf_off, yp, y, sync, srow, kOprojRowCost);
@@ -1461,7 +1629,8 @@ __device__ __forceinline__ void task_oproj(const KParams& P, const pmk_task& t, 
 template <int WDT>
 __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                             int cu) {
-  const int l = t.layer, H = P.H;
+  constexpr bool H16 = WFmt<WDT>::H16;
+  const int l = t.layer, H = P.H, pad = pad_len(H, WFmt<WDT>::EPL);
   float* xs = lds;
   float* red = lds + P.xs_floats;
   float* yp = lds + P.yp_off;
@@ -1470,19 +1639,21 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
   auto sync = [&]() {
     const bool poll = polls_tags(P, sc);
     if (!poll) maybe_wait(P, t, sc, cu, ti);
-    stage_rmsnorm_tagged(P, P.xm + (int64_t)l * H, P.gains + (int64_t)l * 2 * H + H, H, pad_len(H, WFmt<WDT>::EPL),
-                         xs, red, sc.e, !sc.per_op, cu, ti);
+    stage_rmsnorm_tagged<H16>(P, P.xm + (int64_t)l * H, P.gains + (int64_t)l * 2 * H + H, H, pad, xs, red, sc.e,
+                              !sc.per_op, cu, ti);
+    if constexpr (H16) norm_to_h16(xs, P.gains + (int64_t)l * 2 * H + H, H, pad, red, P.eps, lds + P.xh_off);
     if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
-  const float* const sg = fp8_rows<WDT>(P, l, 4);
-  const float* const su = fp8_rows<WDT>(P, l, 5);
-  auto srow = [=](int r) -> const float* { return ((r & 1) ? su : sg) + (int64_t)((r >> 1) / 128) * nbc; };
-  gemv_rows<WDT>(W, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
+  using ST = typename WFmt<WDT>::ST;
+  const ST* const sg = scale_rows<WDT>(P, l, 4);
+  const ST* const su = scale_rows<WDT>(P, l, 5);
+  auto srow = [=](int r) -> const ST* { return scale_row<WDT>((r & 1) ? su : sg, r >> 1, nbc); };
+  gemv_rows<WDT>(W, H, t.a0, t.a1, H16 ? lds + P.xh_off : xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   const int npairs = (t.a1 - t.a0) >> 1;
-  const float rn = rms_factor(red, H, P.eps);
+  const float rn = H16 ? 1.0f : rms_factor(red, H, P.eps);
   for (int p = threadIdx.x; p < npairs; p += kThreads) {
     const float gte = y[2 * p] * rn, up = y[2 * p + 1] * rn;
     stc(P.h + (int64_t)l * P.F + (t.a0 >> 1) + p, gte / (1.0f + expf(-gte)) * up);
@@ -1506,14 +1677,15 @@ __device__ __forceinline__ void task_down(const KParams& P, const pmk_task& t, i
     if ((int)threadIdx.x < R) rv = ld_tagged(P, P.xm + (int64_t)l * P.H + t.a0 + threadIdx.x, sc.e, !sc.per_op, cu, ti);
     for (int i = threadIdx.x + kThreads; i < R; i += kThreads)
       res[i] = ld_tagged(P, P.xm + (int64_t)l * P.H + t.a0 + i, sc.e, !sc.per_op, cu, ti);
-    load_vector(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
+    load_vector<WFmt<WDT>::H16>(P.h + (int64_t)l * K, K, pad_len(K, WFmt<WDT>::EPL), xs);
     if ((int)threadIdx.x < R) res[threadIdx.x] = rv;
     __syncthreads();
     mark(P, sc, ti, 4);
   };
   const int nbc = (K + 127) / 128;
-  const float* const sd = fp8_rows<WDT>(P, l, 6);
-  auto srow = [=](int r) -> const float* { return sd + (int64_t)(r / 128) * nbc; };
+  using ST = typename WFmt<WDT>::ST;
+  const ST* const sd = scale_rows<WDT>(P, l, 6);
+  auto srow = [=](int r) -> const ST* { return scale_row<WDT>(sd, r, nbc); };
   gemv_rows<WDT>(W, K, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow);
   mark(P, sc, ti, 5);
   for (int i = threadIdx.x; i < R; i += kThreads)
@@ -1540,7 +1712,8 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
 template <int WDT>
 __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                             int cu) {
-  const int H = P.H, R = t.a1 - t.a0;
+  constexpr bool H16 = WFmt<WDT>::H16;
+  const int H = P.H, R = t.a1 - t.a0, pad = pad_len(H, WFmt<WDT>::EPL);
   float* xs = lds;
   float* red = lds + P.xs_floats;
   float* yp = lds + P.yp_off;
@@ -1549,17 +1722,19 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
   auto sync = [&]() {
     const bool poll = polls_tags(P, sc);
     if (!poll) maybe_wait(P, t, sc, cu, ti);
-    stage_rmsnorm_tagged(P, P.x + (int64_t)P.L * H, P.final_gain, H, pad_len(H, WFmt<WDT>::EPL), xs, red, sc.e,
+    stage_rmsnorm_tagged<H16>(P, P.x + (int64_t)P.L * H, P.final_gain, H, pad, xs, red, sc.e,
                          !sc.per_op, cu, ti);
+    if constexpr (H16) norm_to_h16(xs, P.final_gain, H, pad, red, P.eps, lds + P.xh_off);
     if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
   const int nbc = (H + 127) / 128;
-  const float* const sl = P.sc_lm;
-  auto srow = [=](int r) -> const float* { return sl + (int64_t)(r / 128) * nbc; };
-  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, xs, yp, y, P.prefetch != 0, sync, srow, kLmheadRowCost);
+  using ST = typename WFmt<WDT>::ST;
+  const ST* const sl = reinterpret_cast<const ST*>(P.sc_lm);
+  auto srow = [=](int r) -> const ST* { return scale_row<WDT>(sl, r, nbc); };
+  gemv_rows<WDT>(P.lm, H, t.a0, t.a1, H16 ? lds + P.xh_off : xs, yp, y, P.prefetch != 0, sync, srow, kLmheadRowCost);
   mark(P, sc, ti, 5);
-  const float rn = rms_factor(red, H, P.eps);
+  const float rn = H16 ? 1.0f : rms_factor(red, H, P.eps);
   unsigned long long key = 0ull;
   bool nan_seen = false;
   for (int i = threadIdx.x; i < R; i += kThreads) {
@@ -1877,6 +2052,26 @@ __global__ void pmk_repack_gu(uint8_t* dst, const uint8_t* wg, const uint8_t* wu
   for (int i = threadIdx.x; i < rowb / 16; i += blockDim.x) d[i] = s[i];
 }
 
+// Integer weight codes, two's complement as loaded -> the kernels' encoding, in place over n 32-bit
+// words: int8 bytes to offset binary (q + 128); int4 nibbles to offset binary (q + 8) with the
+// nibbles of each word reordered so that positions 0..7 hold columns 0 2 4 6 1 3 5 7.
+__global__ void pmk_int_recode(uint32_t* p, int64_t n, int wdt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = p[i];
+  if (wdt == WI8) {
+    p[i] = w ^ 0x80808080u;
+    return;
+  }
+  uint32_t o = 0;
+#pragma unroll
+  for (int pos = 0; pos < 8; ++pos) {
+    const int col = pos < 4 ? 2 * pos : 2 * (pos - 4) + 1;
+    o |= ((w >> (4 * col)) & 15u) << (4 * pos);
+  }
+  p[i] = o ^ 0x88888888u;
+}
+
 // 16-bit gain -> fp32
 __global__ void pmk_widen(float* dst, const uint16_t* src, int n, int bf16) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1918,6 +2113,8 @@ const void* persistent_kernel(int wdt, int kvdt) {
   if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_persistent<WF16, WF16>;
   if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_persistent<WBF16, WBF16>;
   if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_persistent<WFP8, WFP8>;
+  if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_persistent<WI8, WBF16>;
+  if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_persistent<WI4, WBF16>;
   return nullptr;
 }
 
@@ -1925,6 +2122,8 @@ const void* phase_kernel(int wdt, int kvdt) {
   if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_phase<WF16, WF16>;
   if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_phase<WBF16, WBF16>;
   if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_phase<WFP8, WFP8>;
+  if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_phase<WI8, WBF16>;
+  if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_phase<WI4, WBF16>;
   return nullptr;
 }
 
@@ -1965,6 +2164,13 @@ hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const
 }
 hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st) {
   hipLaunchKernelGGL(pmk_repack_gu, dim3(2 * F), dim3(256), 0, st, dst, (const uint8_t*)wg, (const uint8_t*)wu, rowb);
+  return hipGetLastError();
+}
+hipError_t launch_int_recode(uint8_t* p, int64_t bytes, int wdt, hipStream_t st) {
+  const int64_t n = bytes / 4;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pmk_int_recode, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p),
+                     n, wdt);
   return hipGetLastError();
 }
 hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st) {

@@ -33,6 +33,7 @@ hipError_t launch_repack_qkv(uint8_t* dst, const void* wq, const void* wk, const
                              int64_t rowb, hipStream_t st);
 hipError_t launch_repack_gu(uint8_t* dst, const void* wg, const void* wu, int F, int64_t rowb, hipStream_t st);
 hipError_t launch_widen(float* dst, const void* src, int n, int bf16, hipStream_t st);
+hipError_t launch_int_recode(uint8_t* p, int64_t bytes, int wdt, hipStream_t st);
 hipError_t launch_kv_calib(const KParams& P, int finish, hipStream_t st);
 hipError_t static_workspace_address(int device, void** out);
 }  // namespace pmk
@@ -48,6 +49,15 @@ int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 constexpr int kMaxTuneSteps = 64;  // steps of one measured run of the tuning search
 int64_t nblk(int64_t n) { return (n + 127) / 128; }
 
+// Scale elements of the 7 linear tensors of one layer (q k v o gate up down) and of the LM head:
+// fp8 one per 128x128 block, int8 / int4 one per row and 128-column group.
+void scale_counts(const ModelDims& m, int64_t sz[7]) {
+  const int64_t H = m.H, F = m.F, qd = m.qdim(), kvd = (int64_t)m.nkv * m.hd;
+  const int64_t rows[7] = {qd, kvd, kvd, H, F, F, H}, cols[7] = {H, H, H, qd, H, H, F};
+  for (int i = 0; i < 7; ++i) sz[i] = (m.wdt == PMK_DT_FP8_E4M3 ? nblk(rows[i]) : rows[i]) * nblk(cols[i]);
+}
+int64_t lm_scale_count(const ModelDims& m) { return (m.wdt == PMK_DT_FP8_E4M3 ? nblk(m.V) : m.V) * nblk(m.H); }
+
 struct Phase {
   int first, count;
 };
@@ -62,7 +72,7 @@ struct pmk_ctx {
   DeviceTables tabs;
   int device = -1;
   int n_cus = 0;
-  int wes = 2, kves = 2;
+  int kves = 2;
   pmk_sizes sizes{};
   // arena layout (bytes)
   int64_t a_embed = 0, a_lm = 0, a_layers = 0, layer_bytes = 0, off_qkv = 0, off_o = 0, off_gu = 0, off_d = 0;
@@ -81,7 +91,7 @@ struct pmk_ctx {
   int mode = PMK_MODE_MEGAKERNEL;
   int trace_on = 0;
   int xs_floats = 0;
-  int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0;
+  int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0, xh_off = 0;
   int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_units = 0, attn_g2_off = -1;
   size_t lds_bytes = 0;     // per-op kernels
   size_t lds_bytes_pk = 0;  // persistent kernel (adds the O-projection tile area)
@@ -125,11 +135,14 @@ std::string contract_check(const pmk_model_config& c) {
   if (c.n_q_heads / c.n_kv_heads > 8) return "at most 8 query heads per kv head";
   const bool ok_pair = (c.weight_dtype == PMK_DT_F16 && c.kv_dtype == PMK_DT_F16) ||
                        (c.weight_dtype == PMK_DT_BF16 && c.kv_dtype == PMK_DT_BF16) ||
-                       (c.weight_dtype == PMK_DT_FP8_E4M3 && c.kv_dtype == PMK_DT_FP8_E4M3);
-  if (!ok_pair) return "supported (weight, kv) formats: (f16, f16), (bf16, bf16), (fp8, fp8)";
-  const int epl = c.weight_dtype == PMK_DT_FP8_E4M3 ? 16 : 8;
+                       (c.weight_dtype == PMK_DT_FP8_E4M3 && c.kv_dtype == PMK_DT_FP8_E4M3) ||
+                       (c.weight_dtype == PMK_DT_INT8 && c.kv_dtype == PMK_DT_BF16) ||
+                       (c.weight_dtype == PMK_DT_INT4 && c.kv_dtype == PMK_DT_BF16);
+  if (!ok_pair)
+    return "supported (weight, kv) formats: (f16, f16), (bf16, bf16), (fp8, fp8), (int8, bf16), (int4, bf16)";
+  const int epl = weight_epl(c.weight_dtype);
   if (c.hidden % epl || c.ffn % epl || (c.n_q_heads * c.head_dim) % epl)
-    return "hidden, ffn and n_q_heads*head_dim must be multiples of 8 (16 for fp8 weights)";
+    return "hidden, ffn and n_q_heads*head_dim must be multiples of 8 (16 for fp8 and int8, 32 for int4 weights)";
   const int kves = c.kv_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
   if (c.head_dim * kves < 128) return "a KV row (head_dim * element size) must cover at least 128 bytes";
   if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return "rms_eps and rope_theta must be positive";
@@ -167,30 +180,31 @@ int64_t seqcap_of(const ModelDims& m) { return ((int64_t)m.max_seq + 31) / 32 * 
 
 void compute_layout(pmk_ctx* c) {
   const ModelDims& m = c->m;
-  const int64_t wes = c->wes, H = m.H, F = m.F, V = m.V, qd = m.qdim(), L = m.L;
+  const int64_t H = m.H, F = m.F, V = m.V, qd = m.qdim(), L = m.L;
+  auto rb = [&](int64_t K) { return weight_row_bytes(m.wdt, K); };
   int64_t a = 0;
   c->a_embed = a; a = align256(a + V * H * 2);
-  c->a_lm = a; a = align256(a + V * H * wes);
+  c->a_lm = a; a = align256(a + V * rb(H));
   int64_t lb = 0;
-  c->off_qkv = lb; lb = align256(lb + (int64_t)m.qkv_rows() * H * wes);
-  c->off_o = lb; lb = align256(lb + H * qd * wes);
-  c->off_gu = lb; lb = align256(lb + 2 * F * H * wes);
-  c->off_d = lb; lb = align256(lb + H * F * wes);
+  c->off_qkv = lb; lb = align256(lb + (int64_t)m.qkv_rows() * rb(H));
+  c->off_o = lb; lb = align256(lb + H * rb(qd));
+  c->off_gu = lb; lb = align256(lb + 2 * F * rb(H));
+  c->off_d = lb; lb = align256(lb + H * rb(F));
   c->layer_bytes = lb;
   c->a_layers = a; a = align256(a + L * lb);
   c->a_gains = a; a = align256(a + L * 2 * H * 4);
   c->a_final = a; a = align256(a + H * 4);
   c->a_scales = a;
-  if (m.wdt == PMK_DT_FP8_E4M3) {
-    const int64_t kvd = (int64_t)m.nkv * m.hd;
-    const int64_t sz[7] = {nblk(qd) * nblk(H), nblk(kvd) * nblk(H), nblk(kvd) * nblk(H), nblk(H) * nblk(qd),
-                           nblk(F) * nblk(H),  nblk(F) * nblk(H),   nblk(H) * nblk(F)};
+  if (weight_scale_bytes(m.wdt) > 0) {
+    int64_t sz[7];
+    scale_counts(m, sz);
     int64_t off = 0;
     for (int i = 0; i < 7; ++i) { c->sc_off[i] = off; off += sz[i]; }
     c->sc_layer = off;
-    a = align256(a + L * off * 4);
+    const int es = weight_scale_bytes(m.wdt);
+    a = align256(a + L * off * es);
     c->a_sclm = a;
-    a = align256(a + nblk(V) * nblk(H) * 4);
+    a = align256(a + lm_scale_count(m) * es);
   } else {
     c->sc_layer = 0;
     c->a_sclm = a;
@@ -226,7 +240,7 @@ void compute_layout(pmk_ctx* c) {
   c->sizes.workspace_bytes = w;
 
   // LDS: staged activation vectors, or the attention scratch
-  const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
+  const int epl = weight_epl(m.wdt);
   auto padn = [&](int64_t n) { const int64_t sl = 64 * epl; return (n + sl - 1) / sl * sl; };
   const int64_t grp = m.grp();
   // attention: q [grp][hd], per-wave P.V partials [8][grp][hd], per-wave (max, sum) [8][grp][2]
@@ -244,7 +258,11 @@ void compute_layout(pmk_ctx* c) {
   c->epi_off = c->xs_floats + 64;
   c->yp_off = c->epi_off + c->epi_floats;
   c->y_off = c->yp_off + (int)((kWaves * rmax + 63) / 64 * 64);
-  c->lds_bytes = (size_t)(c->y_off + (rmax + 63) / 64 * 64) * 4;
+  c->xh_off = c->y_off + (int)((rmax + 63) / 64 * 64);
+  // integer weight formats: the normalised vector of an RMSNorm prologue as binary16 (the fp32
+  // source stays in the staging area while it is rounded)
+  const int64_t xh_floats = weight_is_int(m.wdt) ? (padn(H) / 2 + 63) / 64 * 64 : 0;
+  c->lds_bytes = (size_t)(c->xh_off + xh_floats) * 4;
   // OPROJ tasks keep o, their residual rows, partial sums and results in a compact block; the rest
   // of LDS (persistent kernel only) holds the O-projection tile, copied before the task's wait.
   int64_t ormax = 1;
@@ -291,10 +309,10 @@ void fill_params(pmk_ctx* c) {
   P.layer_bytes = c->layer_bytes;
   P.off_qkv = c->off_qkv; P.off_o = c->off_o; P.off_gu = c->off_gu; P.off_d = c->off_d;
   P.lm = A + c->a_lm;
-  P.scales = reinterpret_cast<const float*>(A + c->a_scales);
+  P.scales = A + c->a_scales;
   P.sc_layer = c->sc_layer;
   for (int i = 0; i < 7; ++i) P.sc_off[i] = c->sc_off[i];
-  P.sc_lm = reinterpret_cast<const float*>(A + c->a_sclm);
+  P.sc_lm = A + c->a_sclm;
   P.rope = reinterpret_cast<const float2*>(A + c->a_rope);
   P.kc = c->kv;
   P.vc = c->kv + c->sizes.kv_bytes / 2;
@@ -329,6 +347,7 @@ void fill_params(pmk_ctx* c) {
   P.epi_off = c->epi_off;
   P.yp_off = c->yp_off;
   P.y_off = c->y_off;
+  P.xh_off = c->xh_off;
   P.o_epi_off = c->o_epi_off;
   P.o_yp_off = c->o_yp_off;
   P.o_y_off = c->o_y_off;
@@ -506,7 +525,6 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   c->cfg = *cfg;
   c->sc = defaults(sched);
   c->m = dims_of(*cfg);
-  c->wes = cfg->weight_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
   c->kves = cfg->kv_dtype == PMK_DT_FP8_E4M3 ? 1 : 2;
   c->device = hip_device;
   int n_cus = c->sc.n_cus;
@@ -648,40 +666,47 @@ pmk_status pmk_load_weights(pmk_ctx* c, const pmk_weight_ptrs* w, void* stream) 
   if (s != PMK_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const ModelDims& m = c->m;
-  const bool fp8 = m.wdt == PMK_DT_FP8_E4M3;
+  const int ses = weight_scale_bytes(m.wdt);  // scale element bytes, 0 for unscaled formats
   if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->layers) return fail(c, PMK_ERR_INVALID_ARG, "missing weight pointers");
-  if (fp8 && (!w->lm_head_scale || !w->layer_scales)) return fail(c, PMK_ERR_INVALID_ARG, "fp8 weights need block scales");
-  const int64_t H = m.H, F = m.F, V = m.V, qd = m.qdim(), kvd = (int64_t)m.nkv * m.hd, wes = c->wes;
-  const int gbf16 = (fp8 || m.wdt == PMK_DT_BF16) ? 1 : 0;
+  if (ses && (!w->lm_head_scale || !w->layer_scales))
+    return fail(c, PMK_ERR_INVALID_ARG, "fp8, int8 and int4 weights need their scales");
+  const int64_t H = m.H, F = m.F, V = m.V, qd = m.qdim();
+  auto rb = [&](int64_t K) { return weight_row_bytes(m.wdt, K); };
+  const int gbf16 = m.wdt == PMK_DT_F16 ? 0 : 1;
   for (int l = 0; l < m.L; ++l)
     for (int k = 0; k < 9; ++k)
       if (!w->layers[l * 9 + k]) return fail(c, PMK_ERR_INVALID_ARG, "missing layer weight pointer");
   HIPCHK(c, hipMemcpyAsync(c->arena + c->a_embed, w->embed, V * H * 2, hipMemcpyDeviceToDevice, st));
-  HIPCHK(c, hipMemcpyAsync(c->arena + c->a_lm, w->lm_head, V * H * wes, hipMemcpyDeviceToDevice, st));
+  HIPCHK(c, hipMemcpyAsync(c->arena + c->a_lm, w->lm_head, V * rb(H), hipMemcpyDeviceToDevice, st));
   for (int l = 0; l < m.L; ++l) {
     const void* const* L9 = w->layers + l * 9;
     uint8_t* base = c->arena + c->a_layers + l * c->layer_bytes;
-    HIPCHK(c, launch_repack_qkv(base + c->off_qkv, L9[0], L9[1], L9[2], m.nq, m.nkv, m.hd, H * wes, st));
-    HIPCHK(c, hipMemcpyAsync(base + c->off_o, L9[3], H * qd * wes, hipMemcpyDeviceToDevice, st));
-    HIPCHK(c, launch_repack_gu(base + c->off_gu, L9[4], L9[5], m.F, H * wes, st));
-    HIPCHK(c, hipMemcpyAsync(base + c->off_d, L9[6], H * F * wes, hipMemcpyDeviceToDevice, st));
+    HIPCHK(c, launch_repack_qkv(base + c->off_qkv, L9[0], L9[1], L9[2], m.nq, m.nkv, m.hd, rb(H), st));
+    HIPCHK(c, hipMemcpyAsync(base + c->off_o, L9[3], H * rb(qd), hipMemcpyDeviceToDevice, st));
+    HIPCHK(c, launch_repack_gu(base + c->off_gu, L9[4], L9[5], m.F, rb(H), st));
+    HIPCHK(c, hipMemcpyAsync(base + c->off_d, L9[6], H * rb(F), hipMemcpyDeviceToDevice, st));
     float* g = reinterpret_cast<float*>(c->arena + c->a_gains) + (int64_t)l * 2 * H;
     HIPCHK(c, launch_widen(g, L9[7], (int)H, gbf16, st));
     HIPCHK(c, launch_widen(g + H, L9[8], (int)H, gbf16, st));
-    if (fp8) {
-      const float* const* S7 = w->layer_scales + l * 7;
-      const int64_t sz[7] = {nblk(qd) * nblk(H), nblk(kvd) * nblk(H), nblk(kvd) * nblk(H), nblk(H) * nblk(qd),
-                             nblk(F) * nblk(H),  nblk(F) * nblk(H),   nblk(H) * nblk(F)};
-      float* sb = reinterpret_cast<float*>(c->arena + c->a_scales) + l * c->sc_layer;
+    if (ses) {
+      const void* const* S7 = w->layer_scales + l * 7;
+      int64_t sz[7];
+      scale_counts(m, sz);
+      uint8_t* sb = c->arena + c->a_scales + l * c->sc_layer * ses;
       for (int k = 0; k < 7; ++k) {
-        if (!S7[k]) return fail(c, PMK_ERR_INVALID_ARG, "missing block-scale pointer");
-        HIPCHK(c, hipMemcpyAsync(sb + c->sc_off[k], S7[k], sz[k] * 4, hipMemcpyDeviceToDevice, st));
+        if (!S7[k]) return fail(c, PMK_ERR_INVALID_ARG, "missing scale pointer");
+        HIPCHK(c, hipMemcpyAsync(sb + c->sc_off[k] * ses, S7[k], sz[k] * ses, hipMemcpyDeviceToDevice, st));
       }
     }
   }
   HIPCHK(c, launch_widen(reinterpret_cast<float*>(c->arena + c->a_final), w->final_norm, (int)H, gbf16, st));
-  if (fp8)
-    HIPCHK(c, hipMemcpyAsync(c->arena + c->a_sclm, w->lm_head_scale, nblk(V) * nblk(H) * 4, hipMemcpyDeviceToDevice, st));
+  if (ses)
+    HIPCHK(c, hipMemcpyAsync(c->arena + c->a_sclm, w->lm_head_scale, lm_scale_count(m) * ses, hipMemcpyDeviceToDevice,
+                             st));
+  if (weight_is_int(m.wdt)) {  // every code of the LM head and the layer blocks (padding included)
+    HIPCHK(c, launch_int_recode(c->arena + c->a_lm, V * rb(H), m.wdt, st));
+    HIPCHK(c, launch_int_recode(c->arena + c->a_layers, m.L * c->layer_bytes, m.wdt, st));
+  }
   // RoPE table: angle p * theta^(-2i/hd) in double, cos and sin rounded to fp32
   const int half = m.hd / 2;
   c->rope_host.resize((size_t)m.max_seq * half * 2);
@@ -977,7 +1002,7 @@ static pmk_status tune_rates(pmk_ctx* c, int steps, int32_t pos, int32_t token, 
   xcd->assign(NQ, -1);
   std::vector<double> bytes(8 * (size_t)NQ, 0.0), ticks(8 * (size_t)NQ, 0.0);
   const ModelDims& m = c->m;
-  const double es = m.wdt == PMK_DT_FP8_E4M3 ? 1.0 : 2.0;
+  const double es = weight_bits(m.wdt) / 8.0;
   for (int sp = 1; sp < steps; ++sp)  // the first step also pays the launch
     for (size_t i = 0; i < NT; ++i) {
       const pmk_task& k = c->sched.tasks[i];
@@ -1066,11 +1091,14 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, pmk_tune_result* res, void* strea
       if (s2 != PMK_OK) return s2;
       // correctness gate against the starting schedule's run from the same state: the same greedy
       // token at every step, and the same largest logit within 1e-3 (a row split changes only the
-      // grouping of a row's partial sums)
+      // grouping of a row's partial sums).  The integer weight formats round every GEMV operand to
+      // binary16, where a regrouped fp32 sum moves some elements by a whole binary16 step: 2e-2 there.
+      const float gate_tol = weight_is_int(c->m.wdt) ? 2e-2f : 1e-3f;
       bool same = true;
       for (int i = 0; i < steps; ++i) {
         const float a = key_value(ref.keys[i]), b = key_value(r.keys[i]);
-        same = same && (uint32_t)ref.keys[i] == (uint32_t)r.keys[i] && std::fabs(a - b) <= 1e-3f * std::max(1.0f, std::fabs(a));
+        same = same && (uint32_t)ref.keys[i] == (uint32_t)r.keys[i] &&
+               std::fabs(a - b) <= gate_tol * std::max(1.0f, std::fabs(a));
       }
       if (!same) ++gated;
       if (same && r.us < best_us * (1.0 - 0.002)) {

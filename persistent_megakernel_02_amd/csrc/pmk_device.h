@@ -56,10 +56,11 @@ struct KParams {
   int64_t layer_bytes;
   int64_t off_qkv, off_o, off_gu, off_d;
   const uint8_t* lm;      // [V][H]
-  const float* scales;    // fp8: per layer [q k v o g u d] block-scale arrays, then the LM head's
-  int64_t sc_layer;       // floats per layer
-  int64_t sc_off[7];      // offsets (floats) of the 7 arrays inside a layer
-  const float* sc_lm;
+  const void* scales;     // fp8 / int8 / int4: per layer [q k v o g u d] scale arrays (fp8: fp32 per
+                          // 128x128 block; int: bf16 per row and 128-column group)
+  int64_t sc_layer;       // scale elements per layer
+  int64_t sc_off[7];      // offsets (scale elements) of the 7 arrays inside a layer
+  const void* sc_lm;      // the LM head's scales
   const float2* rope;     // [max_seq][hd/2] (cos, sin)
   // kv cache: K [L][nkv][seqcap][hd], V [L][nkv][seqcap / 32][hd][32]
   uint8_t* kc;
@@ -92,6 +93,7 @@ struct KParams {
   int epi_off;            // LDS float offset of staged epilogue inputs (RoPE row, residual rows)
   int yp_off;             // LDS float offset of per-slice GEMV partial sums [8 * rows]
   int y_off;              // LDS float offset of GEMV row results [rows]
+  int xh_off;             // LDS float offset of the binary16 normalised vector (integer weight formats)
   int o_epi_off, o_yp_off, o_y_off;  // the same three areas for OPROJ tasks, packed below pf_off
   int attn_g2_off;        // LDS float offset of the attention's per-wave second-group buffers (-1: none)
   int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)

@@ -119,7 +119,7 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   // last CP splits), as long as the O-projection tiles of the remaining queues still fit the LDS
   // tile area (~128 KiB).
   const int grp = m.grp();
-  const int epl = m.wdt == PMK_DT_FP8_E4M3 ? 16 : 8;
+  const int epl = weight_epl(m.wdt);
   const int64_t o_slices = ((int64_t)m.qdim() / epl + 63) / 64;
   const int64_t cbytes = (int64_t)S * grp * (m.hd + 4) * 4;
   // O-projection tile rows (in 1 KiB units) that fit the LDS tile area
@@ -560,8 +560,7 @@ std::string validate_schedule(const Schedule& s) {
         return fmt("integrity: task %ld row range [%ld,%ld) splits a row pair", t, k.a0, k.a1);
       // the GEMV addresses a tile with 32-bit offsets below kMaxTileBytes
       const int64_t K = k.op == PMK_OP_DOWN ? m.F : (k.op == PMK_OP_OPROJ ? m.qdim() : m.H);
-      const int64_t es = m.wdt == PMK_DT_FP8_E4M3 ? 1 : 2;
-      if ((int64_t)(k.a1 - k.a0) * K * es > kMaxTileBytes)
+      if ((int64_t)(k.a1 - k.a0) * weight_row_bytes(m.wdt, K) > kMaxTileBytes)
         return fmt("integrity: task %ld weight tile of %ld rows exceeds the GEMV's 32-bit offsets", t, k.a1 - k.a0);
     }
   }

@@ -21,7 +21,13 @@ GAP = 1e-2
 
 
 def tol_for(w) -> float:
-    return 1e-1 if w.wdtype == "fp8" else 2e-2
+    """Logit tolerance: 2e-2 for 16-bit weights and 1e-1 for fp8 (as the workloads state them); 5e-2
+    for the weight-only integer formats, whose binary16 activation rounding turns rounding-order
+    differences of two correct implementations into whole binary16 steps in some elements (the bound
+    is derived where the implementation notes derive the tolerances)."""
+    if w.wdtype == "fp8":
+        return 1e-1
+    return 5e-2 if w.wdtype in ("int8", "int4") else 2e-2
 
 
 def log(*a):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"{n} has no binding"
-    assert lib.pmk_abi_version() == 2
+    assert lib.pmk_abi_version() == 3
 
 
 def create(cfg, sched=None):
@@ -44,6 +44,9 @@ def create(cfg, sched=None):
     (dict(n_kv_heads=3), "multiple"),
     (dict(n_q_heads=32, n_kv_heads=2), "at most 8"),
     (dict(weight_dtype=pmk.PMK_DT_BF16, kv_dtype=pmk.PMK_DT_F16), "formats"),
+    (dict(weight_dtype=pmk.PMK_DT_INT8, kv_dtype=pmk.PMK_DT_FP8_E4M3), "formats"),
+    (dict(weight_dtype=pmk.PMK_DT_INT4, kv_dtype=pmk.PMK_DT_BF16, hidden=272), "32 for int4"),
+    (dict(weight_dtype=pmk.PMK_DT_INT8, kv_dtype=pmk.PMK_DT_BF16, hidden=264), "16 for fp8 and int8"),
     (dict(hidden=260), "multiples"),
     (dict(vocab=0), "positive"),
 ])
@@ -63,7 +66,7 @@ def test_fp8_kv_rows_must_cover_a_cache_line():
 
 def test_sizes_and_device_less_context():
     lib = pmk.load()
-    for name in ("tiny", "8b", "8b_fp8"):
+    for name in ("tiny", "8b", "8b_fp8", "8b_int8", "8b_int4"):
         w = WORKLOADS[name]
         st, ctx, msg = create(pmk.model_config(w))
         assert st == 0, msg
@@ -112,7 +115,10 @@ def test_workload_byte_accounting():
     # and the mean KV bytes over the decode steps, for the workloads' shapes
     expect = {"tiny": (3_427_328, 3_460_608), "1b": (2_077_368_320, 2_096_259_072),
               "2b": (3_742_382_080, 3_803_750_400), "8b": (15_009_857_536, 15_563_571_200),
-              "8b_fp8": (7_507_031_296, 8_052_323_584)}
+              "8b_fp8": (7_507_031_296, 8_052_323_584),
+              # int8 / int4: 7,504,658,432 weights at 1 or 1/2 byte, 58,630,144 bf16 group scales,
+              # 540,672 bytes of gains and embedding row; bf16 KV as in 8b
+              "8b_int8": (7_622_459_392, 8_176_173_056), "8b_int4": (3_870_130_176, 4_423_843_840)}
     for name, (wb, total) in expect.items():
         w = WORKLOADS[name]
         assert w.weight_bytes() == wb
