@@ -284,8 +284,9 @@ __device__ __forceinline__ h16x2 as_h2(uint32_t u) { return __builtin_bit_cast(h
 // nibbles of each 32-bit word holding columns 0 2 4 6 1 3 5 7 from the low end) -> binary16 pairs
 // of consecutive columns, exactly: a code u placed in the low mantissa bits of 1024.0 (0x6400)
 // is the binary16 value 1024 + u, and one packed add (or fma, for a nibble sitting 4 bits up)
-// removes 1024 and the offset.  Each pair then goes through one v_dot2 (fp32 accumulate) with
-// the matching pair of binary16 activations.
+// removes 1024 and the offset.  Each pair then goes through one v_dot2_f32_f16 with the matching
+// pair of binary16 activations: exact products, accumulated in fp32 (measured on gfx950: within 2
+// fp32 ulps of the largest term of the exact sum, as a chain of two fp32 fmas).
 __device__ __forceinline__ float dot_i8_word(uint32_t w, uint32_t x01, uint32_t x23, float acc) {
   const h16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   const h16x2 lo = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) + bias;  // columns 0, 1
@@ -294,15 +295,23 @@ __device__ __forceinline__ float dot_i8_word(uint32_t w, uint32_t x01, uint32_t 
   return __builtin_amdgcn_fdot2(hi, as_h2(x23), acc, false);
 }
 
+// (w & mask) | magic in one instruction (the compiler splits it in two: neither constant fits a
+// 32-bit operand of the three-operand form, so one comes from an SGPR and one from a VGPR)
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
+}
+
 __device__ __forceinline__ float dot_i4_word(uint32_t w, u32x4 x, float acc) {
   const h16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const h16x2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const h16x2 b2 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t w8 = w >> 8;
-  const h16x2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + b1;                                  // columns 0, 1
-  const h16x2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), m16, b2);   // columns 2, 3
-  const h16x2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + b1;                                 // columns 4, 5
-  const h16x2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), m16, b2);  // columns 6, 7
+  const uint32_t magic = 0x64006400u, w8 = w >> 8;
+  const h16x2 p0 = as_h2(and_or(w, 0x000F000Fu, magic)) + b1;                                  // columns 0, 1
+  const h16x2 p1 = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, magic)), m16, b2);   // columns 2, 3
+  const h16x2 p2 = as_h2(and_or(w8, 0x000F000Fu, magic)) + b1;                                 // columns 4, 5
+  const h16x2 p3 = __builtin_elementwise_fma(as_h2(and_or(w8, 0x00F000F0u, magic)), m16, b2);  // columns 6, 7
   acc = __builtin_amdgcn_fdot2(p0, as_h2(x.x), acc, false);
   acc = __builtin_amdgcn_fdot2(p1, as_h2(x.y), acc, false);
   acc = __builtin_amdgcn_fdot2(p2, as_h2(x.z), acc, false);
@@ -684,14 +693,14 @@ __device__ __forceinline__ void load_vector(const float* src, int n, int pad, fl
 // and red[w] = wave w's share of sum(src^2), with one batch of loads and one barrier; the factor
 // 1/sqrt(mean(src^2) + eps) (rms_factor) then scales the GEMV results, since every row's dot
 // product with (src * gain) times that factor is its dot product with the normalised input.
-// With RAW (the integer weight formats) xs holds src itself, and norm_to_h16 then forms the
-// normalised vector (src * r) * gain and rounds it to binary16, the activation operand those
-// formats define.
+// With RAW (the integer weight formats) xs holds src itself and gs the gains, and norm_to_h16 then
+// forms the normalised vector (src * r) * gain and rounds it to binary16, the activation operand
+// those formats define.
 // This one stages a 16-bit embedding row (the first layer's input); stage_rmsnorm_tagged stages
 // the tagged residual stream.
 template <int EDT, bool RAW = false>
 __device__ __forceinline__ void stage_rmsnorm_embed(const uint16_t* emb, const float* gain, int H, int pad, float* xs,
-                                                    float* red) {
+                                                    float* red, float* gs = nullptr) {
   float ss = 0.f;
   for (int i = 8 * threadIdx.x; i < pad; i += 8 * kThreads) {
     float f[8], g[8];
@@ -714,6 +723,7 @@ __device__ __forceinline__ void stage_rmsnorm_embed(const uint16_t* emb, const f
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       xs[i + k] = RAW ? f[k] : f[k] * g[k];
+      if constexpr (RAW) gs[i + k] = g[k];
       ss = fmaf(f[k], f[k], ss);
     }
   }
@@ -729,18 +739,18 @@ __device__ __forceinline__ float rms_factor(const float* red, int H, float eps) 
   return 1.0f / sqrtf(t / (float)H + eps);
 }
 
-// Integer weight formats: after an RMSNorm staging with RAW / H16 (xs = src in fp32, red = the wave
-// sums, behind a barrier), xh[0..pad) = binary16((src * r) * gain) with r = 1 / sqrt(mean(src^2) +
-// eps) (zeros past H), the normalised vector in the order of operations of its definition; ends
-// with a barrier.  The GEMV results then need no factor.
-__device__ __forceinline__ void norm_to_h16(const float* xs, const float* gain, int H, int pad, const float* red,
+// Integer weight formats: after an RMSNorm staging with RAW / H16 (xs = src and gs = the gains in
+// fp32, red = the wave sums, behind a barrier), xh[0..pad) = binary16((src * r) * gain) with r =
+// 1 / sqrt(mean(src^2) + eps) (zeros past H), the normalised vector in the order of operations of
+// its definition; ends with a barrier.  The GEMV results then need no factor.
+__device__ __forceinline__ void norm_to_h16(const float* xs, const float* gs, int H, int pad, const float* red,
                                             float eps, float* xh) {
   const float r = rms_factor(red, H, eps);
   for (int i = 2 * (int)threadIdx.x; i < pad; i += 2 * kThreads) {
     float a = 0.f, b = 0.f;
     if (i < H) {
       const float2 x = *reinterpret_cast<const float2*>(xs + i);
-      const float2 g = *reinterpret_cast<const float2*>(gain + i);
+      const float2 g = *reinterpret_cast<const float2*>(gs + i);
       a = (x.x * r) * g.x;
       b = (x.y * r) * g.y;
     }
@@ -775,7 +785,7 @@ struct StepCtx {
 template <bool NORM = false, bool H16 = false>
 __device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned long long* src, int n, int pad,
                                               float* xs, int e, bool poll, int cu, int task,
-                                              const float* gain = nullptr) {
+                                              const float* gain = nullptr, float* gs = nullptr) {
   constexpr int B = 4;  // 16-byte loads (two values) per thread per batch
   const __amdgpu_buffer_rsrc_t r = coherent_rsrc(src, (uint32_t)n * 8);
   const uint32_t want = (uint32_t)(e + 1);
@@ -818,9 +828,11 @@ __device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned l
       if constexpr (NORM) {
         ss = fmaf(a, a, ss);
         ss = fmaf(b, b, ss);
-        if constexpr (!H16) {  // H16 with NORM: src itself, normalised by norm_to_h16
+        if constexpr (!H16) {  // H16 with NORM: src itself and the gains, normalised by norm_to_h16
           a *= g[k].x;
           b *= g[k].y;
+        } else {
+          if (i < pad) *reinterpret_cast<float2*>(gs + i) = g[k];
         }
       }
       if (i < pad) put2<H16 && !NORM>(xs, i, a, b);
@@ -834,8 +846,8 @@ __device__ __forceinline__ float stage_tagged(const KParams& P, const unsigned l
 template <bool H16 = false>
 __device__ __forceinline__ void stage_rmsnorm_tagged(const KParams& P, const unsigned long long* src, const float* gain,
                                                      int H, int pad, float* xs, float* red, int e, bool poll, int cu,
-                                                     int task) {
-  float ss = stage_tagged<true, H16>(P, src, H, pad, xs, e, poll, cu, task, gain);
+                                                     int task, float* gs = nullptr) {
+  float ss = stage_tagged<true, H16>(P, src, H, pad, xs, e, poll, cu, task, gain, gs);
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -947,12 +959,12 @@ __device__ __forceinline__ void task_qkv(const KParams& P, const pmk_task& t, in
       if (threadIdx.x < 2 * P.nkv) rope[half + threadIdx.x] = make_float2(ks8, 0.f);
     if (l == 0) {
       const int tok = input_token(P, sc);
-      stage_rmsnorm_embed<EDT, H16>(P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red);
+      stage_rmsnorm_embed<EDT, H16>(P.embed + (int64_t)tok * H, P.gains, H, pad, xs, red, lds + P.gs_off);
     } else {
       stage_rmsnorm_tagged<H16>(P, P.x + (int64_t)l * H, P.gains + (int64_t)l * 2 * H, H, pad, xs, red, sc.e,
-                           !sc.per_op, cu, ti);
+                                !sc.per_op, cu, ti, lds + P.gs_off);
     }
-    if constexpr (H16) norm_to_h16(xs, P.gains + (int64_t)l * 2 * H, H, pad, red, P.eps, lds + P.xh_off);
+    if constexpr (H16) norm_to_h16(xs, lds + P.gs_off, H, pad, red, P.eps, lds + P.xh_off);
     if (poll_x) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
@@ -1640,8 +1652,8 @@ __device__ __forceinline__ void task_gateup(const KParams& P, const pmk_task& t,
     const bool poll = polls_tags(P, sc);
     if (!poll) maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm_tagged<H16>(P, P.xm + (int64_t)l * H, P.gains + (int64_t)l * 2 * H + H, H, pad, xs, red, sc.e,
-                              !sc.per_op, cu, ti);
-    if constexpr (H16) norm_to_h16(xs, P.gains + (int64_t)l * 2 * H + H, H, pad, red, P.eps, lds + P.xh_off);
+                              !sc.per_op, cu, ti, lds + P.gs_off);
+    if constexpr (H16) norm_to_h16(xs, lds + P.gs_off, H, pad, red, P.eps, lds + P.xh_off);
     if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };
@@ -1723,8 +1735,8 @@ __device__ __forceinline__ void task_lmhead(const KParams& P, const pmk_task& t,
     const bool poll = polls_tags(P, sc);
     if (!poll) maybe_wait(P, t, sc, cu, ti);
     stage_rmsnorm_tagged<H16>(P, P.x + (int64_t)P.L * H, P.final_gain, H, pad, xs, red, sc.e,
-                         !sc.per_op, cu, ti);
-    if constexpr (H16) norm_to_h16(xs, P.final_gain, H, pad, red, P.eps, lds + P.xh_off);
+                              !sc.per_op, cu, ti, lds + P.gs_off);
+    if constexpr (H16) norm_to_h16(xs, lds + P.gs_off, H, pad, red, P.eps, lds + P.xh_off);
     if (poll) trace_mark(P, sc.s, ti, 1, __builtin_amdgcn_s_memrealtime());
     mark(P, sc, ti, 4);
   };

@@ -91,7 +91,7 @@ struct pmk_ctx {
   int mode = PMK_MODE_MEGAKERNEL;
   int trace_on = 0;
   int xs_floats = 0;
-  int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0, xh_off = 0;
+  int epi_floats = 0, epi_off = 0, yp_off = 0, y_off = 0, xh_off = 0, gs_off = 0;
   int o_epi_off = 0, o_yp_off = 0, o_y_off = 0, pf_off = 0, pf_units = 0, attn_g2_off = -1;
   size_t lds_bytes = 0;     // per-op kernels
   size_t lds_bytes_pk = 0;  // persistent kernel (adds the O-projection tile area)
@@ -260,9 +260,11 @@ void compute_layout(pmk_ctx* c) {
   c->y_off = c->yp_off + (int)((kWaves * rmax + 63) / 64 * 64);
   c->xh_off = c->y_off + (int)((rmax + 63) / 64 * 64);
   // integer weight formats: the normalised vector of an RMSNorm prologue as binary16 (the fp32
-  // source stays in the staging area while it is rounded)
+  // source stays in the staging area while it is rounded), and the prologue's gains in fp32
   const int64_t xh_floats = weight_is_int(m.wdt) ? (padn(H) / 2 + 63) / 64 * 64 : 0;
-  c->lds_bytes = (size_t)(c->xh_off + xh_floats) * 4;
+  const int64_t gs_floats = weight_is_int(m.wdt) ? padn(H) : 0;
+  c->gs_off = c->xh_off + (int)xh_floats;
+  c->lds_bytes = (size_t)(c->gs_off + gs_floats) * 4;
   // OPROJ tasks keep o, their residual rows, partial sums and results in a compact block; the rest
   // of LDS (persistent kernel only) holds the O-projection tile, copied before the task's wait.
   int64_t ormax = 1;
@@ -348,6 +350,7 @@ void fill_params(pmk_ctx* c) {
   P.yp_off = c->yp_off;
   P.y_off = c->y_off;
   P.xh_off = c->xh_off;
+  P.gs_off = c->gs_off;
   P.o_epi_off = c->o_epi_off;
   P.o_yp_off = c->o_yp_off;
   P.o_y_off = c->o_y_off;

@@ -94,6 +94,7 @@ struct KParams {
   int yp_off;             // LDS float offset of per-slice GEMV partial sums [8 * rows]
   int y_off;              // LDS float offset of GEMV row results [rows]
   int xh_off;             // LDS float offset of the binary16 normalised vector (integer weight formats)
+  int gs_off;             // LDS float offset of the staged RMSNorm gains (integer weight formats)
   int o_epi_off, o_yp_off, o_y_off;  // the same three areas for OPROJ tasks, packed below pf_off
   int attn_g2_off;        // LDS float offset of the attention's per-wave second-group buffers (-1: none)
   int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)
