@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PMK_ABI_VERSION 3
+#define PMK_ABI_VERSION 4
 
 typedef enum {
   PMK_OK = 0,
@@ -129,7 +129,12 @@ typedef struct {
                                under ~33 KiB while the O-projection tiles still fit in LDS) */
   int32_t combine_o_share;  /* O-projection rows on the queues that run a COMBINE: 0 automatic, 1 none,
                                2 half a share, 3 a full share */
-  int32_t reserved[6];      /* must be 0 */
+  int32_t prefill_chunk;    /* prompt positions per chunk of the batched prefill (16-bit weights and
+                               cache only): 0 = 256 (or max_seq rounded up to 128 if smaller), a
+                               multiple of 128 up to 1024, or -1 = no batched prefill (every prompt
+                               position runs as a teacher-forced decode step); other formats always
+                               prefill step by step */
+  int32_t reserved[5];      /* must be 0 */
 } pmk_schedule_config;
 
 typedef struct {
@@ -236,8 +241,9 @@ pmk_status pmk_bind(pmk_ctx* ctx, void* d_arena, void* d_kv, void* d_workspace);
  * One context per device at a time: a later pmk_bind_static_workspace on the same device takes the
  * array over, and device calls on the context that held it before then fail with
  * PMK_ERR_NOT_BOUND; calls of two contexts on one device's array that overlap in time race.
- * Errors: PMK_ERR_CAPACITY (the schedule's workspace exceeds the array: larger models or a trace
- * ring need pmk_bind), PMK_ERR_INVALID_ARG, PMK_ERR_NOT_BOUND (device-less context),
+ * Errors: PMK_ERR_CAPACITY (the schedule's workspace exceeds the array: larger models, a trace
+ * ring or the batched prefill's chunk buffers of a large model need pmk_bind, or a context created
+ * with prefill_chunk = -1), PMK_ERR_INVALID_ARG, PMK_ERR_NOT_BOUND (device-less context),
  * PMK_ERR_DEVICE, PMK_ERR_HIP. */
 pmk_status pmk_bind_static_workspace(pmk_ctx* ctx, void* d_arena, void* d_kv);
 

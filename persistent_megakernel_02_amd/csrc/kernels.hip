@@ -1953,6 +1953,369 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 
 // zero flags, counters, control words and the step tags of the attention output; set position
 // and next token
+// ------------------------------------------------------------------------------------------------
+// Batched prefill (16-bit weights and KV cache).  The prompt's positions go through the model in
+// chunks of up to `chunk` tokens; each layer of a chunk is a sequence of grid-wide phases of ONE
+// cooperative launch: RMSNorm (one wave per token), the QKV GEMM with RoPE and the KV append in
+// its epilogue, causal attention (one wave per (q head, 16 queries)), the O GEMM + residual,
+// RMSNorm, the gate/up GEMM + SwiGLU, the down GEMM + residual.  The GEMMs are dense contractions
+// over the chunk's tokens and run on the matrix cores (v_mfma_f32_16x16x32 in the weight format):
+// the weights are the A operand as stored (exact), the fp32 activations the B operand as three
+// 16-bit terms (x = t0 + t1 + t2 to ~2^-24 relative, each product accumulated in fp32), so the
+// results keep fp32 accuracy in a different rounding order.  A phase reads only what earlier
+// phases wrote; phases are separated by a grid barrier (agent-scope fences and one arrival
+// counter), so there is no schedule to validate.
+// ------------------------------------------------------------------------------------------------
+constexpr int kPfRows = 32;    // GEMM tile rows (two 16-row blocks)
+constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
+
+// fp32 x[8] -> three 16-bit terms of format DT per element (nearest even at each step)
+template <int DT>
+__device__ __forceinline__ void split3x8(const float* x, u32x4& t0, u32x4& t1, u32x4& t2) {
+  uint32_t a[4], b[4], c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint16_t h[2], m[2], o[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = x[2 * k + e];
+      h[e] = enc16<DT>(v);
+      const float r = v - dec16<DT>(h[e]);
+      m[e] = enc16<DT>(r);
+      o[e] = enc16<DT>(r - dec16<DT>(m[e]));
+    }
+    a[k] = h[0] | ((uint32_t)h[1] << 16);
+    b[k] = m[0] | ((uint32_t)m[1] << 16);
+    c[k] = o[0] | ((uint32_t)o[1] << 16);
+  }
+  t0 = u32x4{a[0], a[1], a[2], a[3]};
+  t1 = u32x4{b[0], b[1], b[2], b[3]};
+  t2 = u32x4{c[0], c[1], c[2], c[3]};
+}
+
+// Store v as three 16-bit terms at element idx of three planes `plane` elements apart.
+template <int DT>
+__device__ __forceinline__ void put_terms(uint16_t* planes, int64_t plane, int64_t idx, float v) {
+  const uint16_t h = enc16<DT>(v);
+  const float r = v - dec16<DT>(h);
+  const uint16_t m = enc16<DT>(r);
+  planes[idx] = h;
+  planes[plane + idx] = m;
+  planes[2 * plane + idx] = enc16<DT>(r - dec16<DT>(m));
+}
+
+// Grid barrier number `k` (1-based) of the launch: every workgroup arrives once per barrier.  The
+// fences publish this workgroup's stores and make the other workgroups' visible to later loads.
+// The wait is bounded like every other wait (watchdog: the abort word ends all of them).
+__device__ __forceinline__ void pf_barrier(const KParams& P, uint32_t* bar, uint32_t k) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = k * gridDim.x;
+    int64_t spins = 0;
+    uint32_t v = ldc(bar);
+    while (v < target) {
+      if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
+      if (++spins > P.spin_limit) {
+        report_error(P.ctrl, PMK_ERR_TIMEOUT, (int)blockIdx.x, -1, -1, target, v);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = ldc(bar);
+    }
+  }
+  __syncthreads();
+  __threadfence();
+}
+
+// RMSNorm of `ntok` rows of src [chunk][H] (or, with emb, of the embedding rows of the tokens,
+// written to src first) into three-term planes bn: (x * r) * g with r = 1 / sqrt(mean(x^2) + eps).
+// One wave per token.
+template <int DT, int EDT>
+__device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& A, float* src, const int32_t* emb_tok,
+                                           const float* gain, int ntok, int gw, int nw) {
+  const int lane = threadIdx.x & 63, H = P.H;
+  const int64_t plane = (int64_t)A.chunk * H;
+  for (int t = gw; t < ntok; t += nw) {
+    float* x = src + (int64_t)t * H;
+    if (emb_tok) {
+      int tok = emb_tok[t];
+      tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
+      const uint16_t* e = P.embed + (int64_t)tok * H;
+      for (int k = 2 * lane; k < H; k += 128) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(e + k);
+        *reinterpret_cast<float2*>(x + k) = make_float2(dec16<EDT>((uint16_t)(w & 0xffffu)), dec16<EDT>((uint16_t)(w >> 16)));
+      }
+    }
+    float ss = 0.f;
+    for (int k = 2 * lane; k < H; k += 128) {
+      const float2 v = *reinterpret_cast<const float2*>(x + k);
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + P.eps);
+    for (int k = 2 * lane; k < H; k += 128) {
+      const float2 v = *reinterpret_cast<const float2*>(x + k);
+      const float2 g = *reinterpret_cast<const float2*>(gain + k);
+      put_terms<DT>(A.bn, plane, (int64_t)t * H + k, (v.x * r) * g.x);
+      put_terms<DT>(A.bn, plane, (int64_t)t * H + k + 1, (v.y * r) * g.y);
+    }
+  }
+}
+
+// One GEMM tile: rows [row0, row0 + 32) of W ([N][K], 16-bit format DT) against tokens
+// [tok0, tok0 + 128) of the three-term planes B ([3][chunk][K]).  Wave w takes tokens
+// tok0 + 16w .. + 15 and both 16-row blocks; per 32-column step each lane loads 16 bytes of two
+// weight rows and of its token's three terms and issues six matrix-core products.  epi(r, t, v)
+// receives rows r .. r + 3 (r = row0 + 16 rb + 4 (lane / 16), rb = 0, 1) of token
+// t = tok0 + 16 w + lane % 16 (rows past N hold zeros).
+template <int DT, class Epi>
+__device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int row0,
+                                             int tok0, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, kg = lane >> 4;
+  const int rows = N - row0 < kPfRows ? N - row0 : kPfRows;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(W + (int64_t)row0 * K * 2), (short)0, rows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B), (short)0, (int)((int64_t)3 * chunk * K * 2), 0x00020000);
+  constexpr uint32_t kOut = 0x7FFFFFF0u;
+  const int tok = tok0 + 16 * wave + r16;
+  const uint32_t bplane = (uint32_t)chunk * (uint32_t)K * 2u;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const int k = k0 + 8 * kg;
+    const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
+    const uint32_t a0off = ok ? (uint32_t)((r16 * K + k) * 2) : kOut;
+    const uint32_t a1off = ok ? (uint32_t)(((16 + r16) * K + k) * 2) : kOut;
+    const uint32_t boff = (uint32_t)(((int64_t)tok * K + k) * 2);
+    const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(wr, a0off, 0, 0);
+    const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(wr, a1off, 0, 0);
+    const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(br, boff, 0, 0);
+    const u32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(br, boff + bplane, 0, 0);
+    const u32x4 b2 = __builtin_amdgcn_raw_buffer_load_b128(br, boff + 2u * bplane, 0, 0);
+    acc0 = mfma16<DT>(a0, b2, acc0);
+    acc1 = mfma16<DT>(a1, b2, acc1);
+    acc0 = mfma16<DT>(a0, b1, acc0);
+    acc1 = mfma16<DT>(a1, b1, acc1);
+    acc0 = mfma16<DT>(a0, b0, acc0);
+    acc1 = mfma16<DT>(a1, b0, acc1);
+  }
+  epi(row0 + 4 * kg, tok, acc0);
+  epi(row0 + 16 + 4 * kg, tok, acc1);
+}
+
+// Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles spread over the grid.
+template <int DT, class Epi>
+__device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int ntok,
+                                        Epi epi) {
+  const int nr = (N + kPfRows - 1) / kPfRows, nt = (ntok + kPfTokens - 1) / kPfTokens;
+  for (int ti = blockIdx.x; ti < nr * nt; ti += gridDim.x) {
+    const int row0 = (ti / nt) * kPfRows, tok0 = (ti % nt) * kPfTokens;
+    pf_gemm_tile<DT>(W, N, K, B, chunk, row0, tok0, epi);
+  }
+}
+
+// Causal attention of the chunk's queries (positions p0 .. p0 + ntok - 1) over the cache
+// positions 0 .. p0 + ntok - 1 (this chunk's rows were appended by the QKV phase).  One wave per
+// (q head j, block of 16 queries); the same matrix-core layout as the decode attention with the
+// 16 queries of one head as the B columns: scores = K rows (A) x q (B, three terms), online
+// softmax per query, P.V = V^T (A, from the blocked V cache) x P (B, three terms).  The output
+// goes to the three-term planes bo.
+template <int DT, int HD>
+__device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, int l, int p0, int ntok, int gw,
+                                        int nw) {
+  constexpr int NC = HD / 32, NT = HD / 16;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, kg = lane >> 4;
+  const int nqb = (ntok + 15) / 16, ntasks = P.nq * nqb, qd = P.qdim;
+  const int pend = p0 + ntok;  // cache positions [0, pend) are written
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(P.kc);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(P.vc);
+  const int64_t oplane = (int64_t)A.chunk * qd;
+  const float scale = P.attn_scale;
+  for (int task = gw; task < ntasks; task += nw) {
+    const int j = task % P.nq, qb = task / P.nq;
+    const int g = j / P.grp;
+    const int64_t hb = (int64_t)l * P.nkv + g;
+    const int tq = qb * 16 + c16;                  // this lane's query (column)
+    const int tqc = tq < ntok ? tq : ntok - 1;     // padding columns repeat the last query
+    const int qpos = p0 + tqc;
+    const int qlast = p0 + ((qb * 16 + 15) < ntok ? qb * 16 + 15 : ntok - 1);
+    u32x4 qt[NC][3];
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+      float qv[8];
+      const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = src[e];
+      split3x8<DT>(qv, qt[s][0], qt[s][1], qt[s][2]);
+    }
+    float m = -INFINITY, sum = 0.f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb <= qlast; kb += 32) {
+      // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
+      // each lane ends up with the scores of positions kb + 8 kg .. + 7 of its query
+      const int pr0 = kb + 8 * (c16 >> 2) + (c16 & 3);
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NC; ++s) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
+        const u32x4 kb4 = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
+        s0 = mfma16<DT>(ka, qt[s][2], s0);
+        s1 = mfma16<DT>(kb4, qt[s][2], s1);
+        s0 = mfma16<DT>(ka, qt[s][1], s0);
+        s1 = mfma16<DT>(kb4, qt[s][1], s1);
+        s0 = mfma16<DT>(ka, qt[s][0], s0);
+        s1 = mfma16<DT>(kb4, qt[s][0], s1);
+      }
+      const int pv = kb + 8 * kg;  // this lane's 8 positions
+      float sc8[8];
+      float mk = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc8[i] = pv + i <= qpos ? s0[i] * scale : -INFINITY;
+        sc8[4 + i] = pv + 4 + i <= qpos ? s1[i] * scale : -INFINITY;
+        mk = fmaxf(mk, fmaxf(sc8[i], sc8[4 + i]));
+      }
+      const float mn = fmaxf(m, column_max<16>(mk));
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sc8[i] = mn == -INFINITY ? 0.f : expf(sc8[i] - mn);
+        ps += sc8[i];
+      }
+      ps = column_sum<16>(ps);
+      const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+      sum = sum * alpha + ps;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
+      m = mn;
+      u32x4 p0t, p1t, p2t;
+      split3x8<DT>(sc8, p0t, p1t, p2t);
+      const int nv = pend - pv;  // positions of this lane's group that are written (others: zero V)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        u32x4 vt = *reinterpret_cast<const u32x4*>(
+            vc + ((hb * (P.seqcap / 32) + kb / 32) * HD + 16 * tt + c16) * 32 + 8 * kg);
+        if (nv < 8) vt = keep_first(vt, nv < 0 ? 0 : nv);
+        acc[tt] = mfma16<DT>(vt, p2t, acc[tt]);
+        acc[tt] = mfma16<DT>(vt, p1t, acc[tt]);
+        acc[tt] = mfma16<DT>(vt, p0t, acc[tt]);
+      }
+    }
+    if (tq < ntok) {
+      const float inv = 1.0f / sum;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          put_terms<DT>(A.bo, oplane, (int64_t)tq * qd + j * HD + 16 * tt + 4 * kg + i, acc[tt][i] * inv);
+    }
+  }
+}
+
+template <int WDT, int KVDT>
+__global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, PrefillArgs A) {
+  static_assert(WDT == KVDT && (WDT == WF16 || WDT == WBF16), "batched prefill: 16-bit weights and cache");
+  constexpr int DT = WDT;
+  const int H = P.H, qd = P.qdim, F = P.F, hd = P.hd, half = P.hd / 2, chunk = A.chunk;
+  const int qrows = P.qdim, krows = P.nkv * P.hd;
+  // one wave per token (RMSNorm) or per attention task, spread over every wave of the grid
+  const int gw = (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x, nw = kWaves * (int)gridDim.x;
+  uint32_t nbar = 0;
+  for (int p0 = 0; p0 < A.n; p0 += chunk) {
+    const int ntok = A.n - p0 < chunk ? A.n - p0 : chunk;
+    pf_rmsnorm<DT, WDT>(P, A, A.x, A.tokens + p0, P.gains, ntok, gw, nw);
+    pf_barrier(P, A.bar, ++nbar);
+    for (int l = 0; l < P.L; ++l) {
+      const uint8_t* Wl = P.wbase + (int64_t)l * P.layer_bytes;
+      // QKV: rows 2m, 2m + 1 are a RoPE pair (q, k) or two v dims; q to A.q, k and v to the cache
+      pf_gemm<DT>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, [&](int r4, int t, f32x4 v) {
+        if (t >= ntok || r4 >= P.qkv_rows) return;
+        const int pos = p0 + t;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int r = r4 + 2 * pp;
+          float a = v[2 * pp], b = v[2 * pp + 1];
+          int sec, base;
+          if (r < qrows) { sec = 0; base = 0; }
+          else if (r < qrows + krows) { sec = 1; base = qrows; }
+          else { sec = 2; base = qrows + krows; }
+          const int head = (r - base) / hd, i = ((r - base) % hd) >> 1;
+          if (sec < 2) {
+            const float2 cs = P.rope[(int64_t)pos * half + i];
+            const float a2 = a * cs.x - b * cs.y;
+            const float b2 = b * cs.x + a * cs.y;
+            a = a2;
+            b = b2;
+          }
+          if (sec == 0) {
+            float* q = A.q + (int64_t)t * qd + head * hd;
+            q[i] = a;
+            q[i + half] = b;
+            continue;
+          }
+          const int64_t hb = (int64_t)l * P.nkv + head;
+          const int64_t ia = sec == 1 ? (hb * P.seqcap + pos) * hd + i
+                                      : ((hb * (P.seqcap / 32) + pos / 32) * hd + i) * 32 + pos % 32;
+          const int64_t ib = sec == 1 ? ia + half : ia + (int64_t)half * 32;
+          uint16_t* c16 = reinterpret_cast<uint16_t*>(sec == 1 ? P.kc : P.vc);
+          c16[ia] = enc16<KVDT>(a);
+          c16[ib] = enc16<KVDT>(b);
+        }
+      });
+      pf_barrier(P, A.bar, ++nbar);
+      if (hd == 128) pf_attn<DT, 128>(P, A, l, p0, ntok, gw, nw);
+      else pf_attn<DT, 64>(P, A, l, p0, ntok, gw, nw);
+      pf_barrier(P, A.bar, ++nbar);
+      // O projection + residual
+      pf_gemm<DT>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, [&](int r4, int t, f32x4 v) {
+        if (t >= ntok) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r4 + i;
+          if (r < H) A.xm[(int64_t)t * H + r] = A.x[(int64_t)t * H + r] + v[i];
+        }
+      });
+      pf_barrier(P, A.bar, ++nbar);
+      pf_rmsnorm<DT, WDT>(P, A, A.xm, nullptr, P.gains + (int64_t)l * 2 * H + H, ntok, gw, nw);
+      pf_barrier(P, A.bar, ++nbar);
+      // gate/up (interleaved rows 2n, 2n + 1) + SwiGLU
+      const int64_t hplane = (int64_t)chunk * F;
+      pf_gemm<DT>(Wl + P.off_gu, 2 * F, H, A.bn, chunk, ntok, [&](int r4, int t, f32x4 v) {
+        if (t >= ntok) return;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int n = (r4 >> 1) + pp;
+          if (n >= F) continue;
+          const float gte = v[2 * pp], up = v[2 * pp + 1];
+          put_terms<DT>(A.bh, hplane, (int64_t)t * F + n, gte / (1.0f + expf(-gte)) * up);
+        }
+      });
+      pf_barrier(P, A.bar, ++nbar);
+      // down projection + residual
+      pf_gemm<DT>(Wl + P.off_d, H, F, A.bh, chunk, ntok, [&](int r4, int t, f32x4 v) {
+        if (t >= ntok) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r4 + i;
+          if (r < H) A.x[(int64_t)t * H + r] = A.xm[(int64_t)t * H + r] + v[i];
+        }
+      });
+      pf_barrier(P, A.bar, ++nbar);
+      if (l + 1 < P.L) {
+        pf_rmsnorm<DT, WDT>(P, A, A.x, nullptr, P.gains + (int64_t)(l + 1) * 2 * H, ntok, gw, nw);
+        pf_barrier(P, A.bar, ++nbar);
+      }
+    }
+  }
+}
+
 __global__ void pmk_reset(KParams P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x, n = gridDim.x * blockDim.x;
   for (int k = i; k < n_flags; k += n) P.flags[k] = 0u;
@@ -2127,6 +2490,13 @@ const void* persistent_kernel(int wdt, int kvdt) {
   if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_persistent<WFP8, WFP8>;
   if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_persistent<WI8, WBF16>;
   if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_persistent<WI4, WBF16>;
+  return nullptr;
+}
+
+// batched prefill kernel for 16-bit weights and cache, nullptr where the format has none
+const void* prefill_kernel(int wdt, int kvdt) {
+  if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_prefill_batch<WF16, WF16>;
+  if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_prefill_batch<WBF16, WBF16>;
   return nullptr;
 }
 

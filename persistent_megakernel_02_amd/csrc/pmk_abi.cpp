@@ -22,6 +22,7 @@
 namespace pmk {
 const void* persistent_kernel(int wdt, int kvdt);
 const void* phase_kernel(int wdt, int kvdt);
+const void* prefill_kernel(int wdt, int kvdt);
 hipError_t launch_begin_call(const KParams& P, const CallParams& cp, hipStream_t st);
 hipError_t launch_reset(const KParams& P, int n_flags, int n_counters, int pos, int token, const int32_t* d_token,
                         hipStream_t st);
@@ -81,6 +82,9 @@ struct pmk_ctx {
   int64_t w_ctrl = 0, w_call = 0, w_flags = 0, w_counters = 0, w_keys = 0, w_tune = 0, w_kvscale = 0, w_kvamax = 0, w_x = 0,
           w_xm = 0, w_q = 0, w_kvcur = 0, w_part = 0, w_o = 0, w_h = 0, w_trace = 0, w_tasks = 0, w_qoff = 0, w_qtasks = 0,
           w_cprod = 0, w_cflag = 0;
+  // batched prefill: tokens per chunk (0: none) and its chunk buffers
+  int pf_chunk = 0;
+  int64_t w_pfx = 0, w_pfxm = 0, w_pfq = 0, w_pfbn = 0, w_pfbo = 0, w_pfbh = 0, w_pfbar = 0;
   uint8_t* arena = nullptr;
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
@@ -237,6 +241,16 @@ void compute_layout(pmk_ctx* c) {
   c->w_qtasks = w; w = align256(w + NT * 4);
   c->w_cprod = w; w = align256(w + (int64_t)s.counters.size() * 4);
   c->w_cflag = w; w = align256(w + (int64_t)s.counters.size() * 4);
+  if (c->pf_chunk > 0) {
+    const int64_t ch = c->pf_chunk;
+    c->w_pfx = w; w = align256(w + ch * H * 4);
+    c->w_pfxm = w; w = align256(w + ch * H * 4);
+    c->w_pfq = w; w = align256(w + ch * qd * 4);
+    c->w_pfbn = w; w = align256(w + 3 * ch * H * 2);
+    c->w_pfbo = w; w = align256(w + 3 * ch * qd * 2);
+    c->w_pfbh = w; w = align256(w + 3 * ch * F * 2);
+    c->w_pfbar = w; w = align256(w + 4);
+  }
   c->sizes.workspace_bytes = w;
 
   // LDS: staged activation vectors, or the attention scratch
@@ -545,6 +559,18 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
     n_cus = 256;
   }
   c->n_cus = n_cus;
+  {
+    // batched prefill: 16-bit weights and cache only
+    const int ch = c->sc.prefill_chunk;
+    if (ch < -1 || (ch > 0 && (ch % 128 != 0 || ch > 1024))) {
+      delete c;
+      return fail(nullptr, PMK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or a multiple of 128 up to 1024");
+    }
+    const bool fmt16 = (c->m.wdt == PMK_DT_F16 && c->m.kvdt == PMK_DT_F16) ||
+                       (c->m.wdt == PMK_DT_BF16 && c->m.kvdt == PMK_DT_BF16);
+    const int cap = (c->m.max_seq + 127) / 128 * 128;
+    c->pf_chunk = !fmt16 || ch == -1 ? 0 : std::min(ch == 0 ? 256 : ch, cap);
+  }
   std::string e = build_schedule(c->m, c->sc, n_cus, &c->sched);
   if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
   e = validate_schedule(c->sched);
@@ -583,6 +609,11 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
     if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fns[0], kThreads, c->lds_bytes_pk);
     if (he != hipSuccess) { delete c; return fail(nullptr, PMK_ERR_HIP, std::string("kernel setup: ") + hipGetErrorString(he)); }
     if (per_cu < 1) { delete c; return fail(nullptr, PMK_ERR_DEVICE, "the persistent kernel cannot be resident on a CU"); }
+    if (c->pf_chunk > 0) {
+      per_cu = 0;
+      he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel(c->m.wdt, c->m.kvdt), kThreads, 0);
+      if (he != hipSuccess || per_cu < 1) c->pf_chunk = 0;  // step-by-step prefill then
+    }
   }
   *out = c;
   return PMK_OK;
@@ -743,7 +774,34 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     s = set_kv_scales(c, d_kv_scales, st);
     if (s != PMK_OK) return s;
   }
-  s = run_prefill(c, d_tokens, P, 0, st);
+  if (c->pf_chunk > 0 && P >= 2) {
+    // positions 0..P-2 in one launch of the batched prefill, then the last position as a
+    // teacher-forced decode step (its logits give the first token)
+    PrefillArgs a{};
+    a.tokens = d_tokens;
+    a.n = P - 1;
+    a.chunk = c->pf_chunk;
+    a.x = reinterpret_cast<float*>(c->ws + c->w_pfx);
+    a.xm = reinterpret_cast<float*>(c->ws + c->w_pfxm);
+    a.q = reinterpret_cast<float*>(c->ws + c->w_pfq);
+    a.bn = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbn);
+    a.bo = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbo);
+    a.bh = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbh);
+    a.bar = reinterpret_cast<uint32_t*>(c->ws + c->w_pfbar);
+    HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P - 1, 0, d_tokens + P - 1, st));
+    HIPCHK(c, hipMemsetAsync(a.bar, 0, 4, st));
+    void* args[] = {&c->kp, &a};
+    HIPCHK(c, hipLaunchCooperativeKernel(prefill_kernel(c->m.wdt, c->m.kvdt), dim3(c->n_cus), dim3(kThreads), args, 0u,
+                                         st));
+    CallParams cp{};
+    cp.forced = d_tokens + P - 1;
+    cp.n_steps = 1;
+    cp.eos = -1;
+    s = begin_call(c, cp, st);
+    if (s == PMK_OK) s = run_steps(c, 1, st);
+  } else {
+    s = run_prefill(c, d_tokens, P, 0, st);
+  }
   if (s != PMK_OK) return s;
   if (d_first_token) HIPCHK(c, launch_copy_token(c->kp, d_first_token, st));
   c->pos_host = P;

@@ -41,6 +41,20 @@ struct CallParams {
   int32_t calib;  // FP8 KV: record max |k|, |v| per (layer, kv head) while the steps run (scale calibration)
 };
 
+// Batched prefill (16-bit weights and KV cache): chunk buffers in the workspace.
+struct PrefillArgs {
+  const int32_t* tokens;  // prompt tokens (device)
+  int32_t n;              // positions 0..n-1 go through the batched path
+  int32_t chunk;          // tokens per chunk (a multiple of 128)
+  float* x;               // [chunk][H] residual stream
+  float* xm;              // [chunk][H] residual after attention
+  float* q;               // [chunk][qdim] queries after RoPE
+  uint16_t* bn;           // [3][chunk][H] normalised activations as three 16-bit terms
+  uint16_t* bo;           // [3][chunk][qdim] attention output as three terms
+  uint16_t* bh;           // [3][chunk][F] SwiGLU output as three terms
+  uint32_t* bar;          // grid barrier arrivals (zero at launch)
+};
+
 struct KParams {
   // model
   int L, H, nq, nkv, hd, F, V, grp, qkv_rows, qdim, max_seq, S;

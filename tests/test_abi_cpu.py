@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"{n} has no binding"
-    assert lib.pmk_abi_version() == 3
+    assert lib.pmk_abi_version() == 4
 
 
 def create(cfg, sched=None):

@@ -272,6 +272,55 @@ def test_split_combines_match_oracle_and_modes():
         assert np.array_equal(r.logits, runs["megakernel"].logits), name
 
 
+@pytest.mark.parametrize("wdtype", ["f16", "bf16"])
+def test_batched_prefill_rows_against_the_oracle(wdtype):
+    """The batched prefill (chunks of 128 positions: three chunks over a 300-token prompt, the last
+    one ragged; matrix-core GEMMs and causal attention in one launch), checked position by position:
+    the oracle takes the GPU's cache rows of the earlier positions and appends the GPU's row of the
+    position (teacher-forced rounding), and the codes it would itself have appended must be within
+    one rounding of the GPU's.  Then the first token (gap rule) and the decode that follows against
+    the oracle.  The step-by-step prefill of the same prompt (prefill_chunk = -1) is reported beside
+    it: its rows drift apart from the batched ones across positions, as any two correct
+    implementations' do, since each position attends to rows rounded to the cache format."""
+    import torch
+    import oracle
+    import persistent_megakernel_02_amd as pmk
+    from tests.parity import _token_ok
+    w = TINY.with_(name=f"tiny_prefill_{wdtype}", wdtype=wdtype, kvdtype=wdtype, prompt=300, steps=8)
+    wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    out = {}
+    for name, chunk in (("batched", 128), ("stepwise", -1)):
+        dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(prefill_chunk=chunk))
+        dec.load_weights(pmk.DeviceWeights(wts))
+        first = int(dec.prefill(torch.from_numpy(prompt).cuda()).item())
+        torch.cuda.synchronize()
+        assert dec.poll_error().code == 0
+        k, v = (t.cpu().numpy() for t in dec.read_kv(w.prompt))
+        out[name] = (first, k, v)
+        dec.close()
+    first, gk, gv = out["batched"]
+    om = oracle.OracleModel(wts, max_seq=w.max_seq)
+    worst, differ = 0.0, []
+    for p in range(w.prompt):
+        om.load_kv(gk[:, :, :p], gv[:, :, :p], p)
+        _, olg, own_k, own_v = om.step_forced(int(prompt[p]), gk[:, :, p], gv[:, :, p])
+        for g_row, o_row in ((gk[:, :, p], own_k), (gv[:, :, p], own_v)):
+            ex, fr = _kv_excess(g_row, o_row, wdtype)
+            worst = max(worst, float(ex.max()))
+            differ.append(fr)
+    _, sk, sv = out["stepwise"]
+    sdiff = np.mean([_kv_excess(a, b, wdtype)[1] for a, b in ((gk, sk), (gv, sv))])
+    log(f"{w.name}: batched prefill rows against the oracle: {100 * np.mean(differ):.3f}% of codes differ, the "
+        f"largest difference is {worst:.3f} of one rounding; against the step-by-step prefill "
+        f"{100 * sdiff:.2f}% differ; first tokens {first} / {out['stepwise'][0]}")
+    assert worst <= 1.0 and np.mean(differ) <= 0.02
+    assert _token_ok(olg, first)
+    run = gpu_run(w, wts, w.steps, prompt=prompt, sched=pmk.schedule_config(prefill_chunk=128))
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt)
+    check(w, run, ref, first_ok, f"{w.name}/batched prefill")
+
+
 def _check_derived_scales(got, want):
     """Layer 0's k and v are a function of the embedding rows alone, so its calibrated maxima agree
     to rounding order; later layers read a cache rounded to E4M3 at scale 1 during calibration, where

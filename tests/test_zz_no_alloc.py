@@ -64,20 +64,22 @@ def test_a_later_static_bind_takes_the_array_over():
 
 def test_static_bind_rejects_a_workspace_beyond_its_maximum():
     """The maximum is checked before anything else, also without a device: a schedule whose
-    workspace exceeds the static array (the 8B model with a 64-step trace ring) is refused with a
-    clear error; one that fits reaches the device check."""
+    workspace exceeds the static array (the 8B model with a 64-step trace ring, or with the chunk
+    buffers of the batched prefill) is refused with a clear error; one that fits reaches the device
+    check."""
     import persistent_megakernel_02_amd as pmk
     from persistent_megakernel_02_amd import _lib
     lib = pmk.load()
-    for name, trace, want in (("8b", 64, _lib.PMK_ERR_CAPACITY), ("8b", 0, _lib.PMK_ERR_NOT_BOUND),
-                              ("tiny", 0, _lib.PMK_ERR_NOT_BOUND)):
+    for name, trace, chunk, want in (("8b", 64, -1, _lib.PMK_ERR_CAPACITY), ("8b", 0, 0, _lib.PMK_ERR_CAPACITY),
+                                     ("8b", 0, -1, _lib.PMK_ERR_NOT_BOUND), ("tiny", 0, 0, _lib.PMK_ERR_NOT_BOUND)):
         ctx = ctypes.c_void_p()
         st = lib.pmk_create(ctypes.byref(pmk.model_config(WORKLOADS[name])),
-                            ctypes.byref(pmk.schedule_config(trace_steps=trace)), -1, ctypes.byref(ctx))
+                            ctypes.byref(pmk.schedule_config(trace_steps=trace, prefill_chunk=chunk)), -1,
+                            ctypes.byref(ctx))
         assert st == 0
         got = lib.pmk_bind_static_workspace(ctx, 256, 512)
         msg = lib.pmk_last_error(ctx).decode()
         lib.pmk_destroy(ctx)
-        assert got == want, (name, trace, got, msg)
+        assert got == want, (name, trace, chunk, got, msg)
         if want == _lib.PMK_ERR_CAPACITY:
             assert "static workspace holds at most" in msg
