@@ -130,7 +130,7 @@ typedef struct {
   int32_t combine_o_share;  /* O-projection rows on the queues that run a COMBINE: 0 automatic, 1 none,
                                2 half a share, 3 a full share */
   int32_t prefill_chunk;    /* prompt positions per chunk of the batched prefill (16-bit weights and
-                               cache only): 0 = 256 (or max_seq rounded up to 128 if smaller), a
+                               cache only): 0 = 512 (or max_seq rounded up to 128 if smaller), a
                                multiple of 128 up to 1024, or -1 = no batched prefill (every prompt
                                position runs as a teacher-forced decode step); other formats always
                                prefill step by step */

@@ -1966,7 +1966,7 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 // phases wrote; phases are separated by a grid barrier (agent-scope fences and one arrival
 // counter), so there is no schedule to validate.
 // ------------------------------------------------------------------------------------------------
-constexpr int kPfRows = 32;    // GEMM tile rows (two 16-row blocks)
+constexpr int kPfRows = 64;    // GEMM tile rows (four 16-row blocks)
 constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
 
 // fp32 x[8] -> three 16-bit terms of format DT per element (nearest even at each step)
@@ -2065,15 +2065,16 @@ __device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& 
   }
 }
 
-// One GEMM tile: rows [row0, row0 + 32) of W ([N][K], 16-bit format DT) against tokens
+// One GEMM tile: rows [row0, row0 + 64) of W ([N][K], 16-bit format DT) against tokens
 // [tok0, tok0 + 128) of the three-term planes B ([3][chunk][K]).  Wave w takes tokens
-// tok0 + 16w .. + 15 and both 16-row blocks; per 32-column step each lane loads 16 bytes of two
-// weight rows and of its token's three terms and issues six matrix-core products.  epi(r, t, v)
-// receives rows r .. r + 3 (r = row0 + 16 rb + 4 (lane / 16), rb = 0, 1) of token
+// tok0 + 16w .. + 15 and all four 16-row blocks; per 32-column step each lane loads 16 bytes of
+// four weight rows and of its token's three terms and issues twelve matrix-core products.
+// epi(r, t, v) receives rows r .. r + 3 (r = row0 + 16 b + 4 (lane / 16), b = 0..3) of token
 // t = tok0 + 16 w + lane % 16 (rows past N hold zeros).
 template <int DT, class Epi>
 __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int row0,
                                              int tok0, Epi epi) {
+  constexpr int RB = kPfRows / 16;  // 16-row blocks per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, kg = lane >> 4;
   const int rows = N - row0 < kPfRows ? N - row0 : kPfRows;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -2083,27 +2084,42 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
   constexpr uint32_t kOut = 0x7FFFFFF0u;
   const int tok = tok0 + 16 * wave + r16;
   const uint32_t bplane = (uint32_t)chunk * (uint32_t)K * 2u;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const int k = k0 + 8 * kg;
+  const uint32_t bbase = (uint32_t)((int64_t)tok * K * 2);
+  const int nsteps = (K + 31) / 32;
+  // a ring of D steps of fragments in flight per lane (each slot refilled right after it is
+  // consumed; the loads of a step past the end read zeros without touching memory)
+  constexpr int D = 4;
+  u32x4 ra[D][RB], rb[D][3];
+  auto issue = [&](int d, int step) {
+    const int k = step * 32 + 8 * kg;
     const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
-    const uint32_t a0off = ok ? (uint32_t)((r16 * K + k) * 2) : kOut;
-    const uint32_t a1off = ok ? (uint32_t)(((16 + r16) * K + k) * 2) : kOut;
-    const uint32_t boff = (uint32_t)(((int64_t)tok * K + k) * 2);
-    const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(wr, a0off, 0, 0);
-    const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(wr, a1off, 0, 0);
-    const u32x4 b0 = __builtin_amdgcn_raw_buffer_load_b128(br, boff, 0, 0);
-    const u32x4 b1 = __builtin_amdgcn_raw_buffer_load_b128(br, boff + bplane, 0, 0);
-    const u32x4 b2 = __builtin_amdgcn_raw_buffer_load_b128(br, boff + 2u * bplane, 0, 0);
-    acc0 = mfma16<DT>(a0, b2, acc0);
-    acc1 = mfma16<DT>(a1, b2, acc1);
-    acc0 = mfma16<DT>(a0, b1, acc0);
-    acc1 = mfma16<DT>(a1, b1, acc1);
-    acc0 = mfma16<DT>(a0, b0, acc0);
-    acc1 = mfma16<DT>(a1, b0, acc1);
+    const uint32_t ko = (uint32_t)k * 2u;
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+      ra[d][b] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (uint32_t)((16 * b + r16) * K * 2) + ko : kOut, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      rb[d][t] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? bbase + ko + (uint32_t)t * bplane : kOut, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+  f32x4 acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < nsteps; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (base + d < nsteps) {
+#pragma unroll
+        for (int t = 2; t >= 0; --t)
+#pragma unroll
+          for (int b = 0; b < RB; ++b) acc[b] = mfma16<DT>(ra[d][b], rb[d][t], acc[b]);
+      }
+      issue(d, base + d + D);
+    }
   }
-  epi(row0 + 4 * kg, tok, acc0);
-  epi(row0 + 16 + 4 * kg, tok, acc1);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) epi(row0 + 16 * b + 4 * kg, tok, acc[b]);
 }
 
 // Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles spread over the grid.
@@ -2118,23 +2134,25 @@ __device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const ui
 }
 
 // Causal attention of the chunk's queries (positions p0 .. p0 + ntok - 1) over the cache
-// positions 0 .. p0 + ntok - 1 (this chunk's rows were appended by the QKV phase).  One wave per
-// (q head j, block of 16 queries); the same matrix-core layout as the decode attention with the
-// 16 queries of one head as the B columns: scores = K rows (A) x q (B, three terms), online
-// softmax per query, P.V = V^T (A, from the blocked V cache) x P (B, three terms).  The output
-// goes to the three-term planes bo.
+// positions 0 .. p0 + ntok - 1 (this chunk's rows were appended by the QKV phase).  One workgroup
+// per (q head j, block of 16 queries); its eight waves split the key positions, wave w taking the
+// 32-position groups w, w + 8, ... up to the block's last query, with the decode attention's
+// matrix-core layout and the 16 queries of the head as the B columns: scores = K rows (A) x q
+// (B, three terms), online softmax per query, P.V = V^T (A, from the blocked V cache) x P (B,
+// three terms).  The waves' (max, sum, acc) are merged in LDS (lds: 8 x 16 x (hd + 2) floats) and
+// the output goes to the three-term planes bo.
 template <int DT, int HD>
-__device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, int l, int p0, int ntok, int gw,
-                                        int nw) {
-  constexpr int NC = HD / 32, NT = HD / 16;
-  const int lane = threadIdx.x & 63, c16 = lane & 15, kg = lane >> 4;
+__device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, int l, int p0, int ntok, float* lds) {
+  constexpr int NC = HD / 32, NT = HD / 16, REC = HD + 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15, kg = lane >> 4;
   const int nqb = (ntok + 15) / 16, ntasks = P.nq * nqb, qd = P.qdim;
   const int pend = p0 + ntok;  // cache positions [0, pend) are written
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(P.kc);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(P.vc);
   const int64_t oplane = (int64_t)A.chunk * qd;
   const float scale = P.attn_scale;
-  for (int task = gw; task < ntasks; task += nw) {
+  float* rec = lds + (wave * 16 + c16) * REC;  // this lane's column record: acc[HD], m, sum
+  for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
     const int j = task % P.nq, qb = task / P.nq;
     const int g = j / P.grp;
     const int64_t hb = (int64_t)l * P.nkv + g;
@@ -2142,85 +2160,111 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
     const int tqc = tq < ntok ? tq : ntok - 1;     // padding columns repeat the last query
     const int qpos = p0 + tqc;
     const int qlast = p0 + ((qb * 16 + 15) < ntok ? qb * 16 + 15 : ntok - 1);
-    u32x4 qt[NC][3];
-#pragma unroll
-    for (int s = 0; s < NC; ++s) {
-      float qv[8];
-      const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = src[e];
-      split3x8<DT>(qv, qt[s][0], qt[s][1], qt[s][2]);
-    }
     float m = -INFINITY, sum = 0.f;
     f32x4 acc[NT];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb <= qlast; kb += 32) {
-      // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
-      // each lane ends up with the scores of positions kb + 8 kg .. + 7 of its query
-      const int pr0 = kb + 8 * (c16 >> 2) + (c16 & 3);
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if (32 * wave <= qlast) {
+      u32x4 qt[NC][3];
 #pragma unroll
       for (int s = 0; s < NC; ++s) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
-        const u32x4 kb4 = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
-        s0 = mfma16<DT>(ka, qt[s][2], s0);
-        s1 = mfma16<DT>(kb4, qt[s][2], s1);
-        s0 = mfma16<DT>(ka, qt[s][1], s0);
-        s1 = mfma16<DT>(kb4, qt[s][1], s1);
-        s0 = mfma16<DT>(ka, qt[s][0], s0);
-        s1 = mfma16<DT>(kb4, qt[s][0], s1);
+        float qv[8];
+        const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = src[e];
+        split3x8<DT>(qv, qt[s][0], qt[s][1], qt[s][2]);
       }
-      const int pv = kb + 8 * kg;  // this lane's 8 positions
-      float sc8[8];
-      float mk = -INFINITY;
+      for (int kb = 32 * wave; kb <= qlast; kb += 32 * kWaves) {
+        // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
+        // each lane ends up with the scores of positions kb + 8 kg .. + 7 of its query
+        const int pr0 = kb + 8 * (c16 >> 2) + (c16 & 3);
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc8[i] = pv + i <= qpos ? s0[i] * scale : -INFINITY;
-        sc8[4 + i] = pv + 4 + i <= qpos ? s1[i] * scale : -INFINITY;
-        mk = fmaxf(mk, fmaxf(sc8[i], sc8[4 + i]));
-      }
-      const float mn = fmaxf(m, column_max<16>(mk));
-      float ps = 0.f;
+        for (int s = 0; s < NC; ++s) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
+          const u32x4 kb4 = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
+          s0 = mfma16<DT>(ka, qt[s][2], s0);
+          s1 = mfma16<DT>(kb4, qt[s][2], s1);
+          s0 = mfma16<DT>(ka, qt[s][1], s0);
+          s1 = mfma16<DT>(kb4, qt[s][1], s1);
+          s0 = mfma16<DT>(ka, qt[s][0], s0);
+          s1 = mfma16<DT>(kb4, qt[s][0], s1);
+        }
+        const int pv = kb + 8 * kg;  // this lane's 8 positions
+        u32x4 vt[NT];
+        const int nv = pend - pv;  // positions of this lane's group that are written (others: zero V)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sc8[i] = mn == -INFINITY ? 0.f : expf(sc8[i] - mn);
-        ps += sc8[i];
-      }
-      ps = column_sum<16>(ps);
-      const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
-      sum = sum * alpha + ps;
+        for (int tt = 0; tt < NT; ++tt) {
+          vt[tt] = *reinterpret_cast<const u32x4*>(
+              vc + ((hb * (P.seqcap / 32) + kb / 32) * HD + 16 * tt + c16) * 32 + 8 * kg);
+          if (nv < 8) vt[tt] = keep_first(vt[tt], nv < 0 ? 0 : nv);
+        }
+        float sc8[8];
+        float mk = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
+        for (int i = 0; i < 4; ++i) {
+          sc8[i] = pv + i <= qpos ? s0[i] * scale : -INFINITY;
+          sc8[4 + i] = pv + 4 + i <= qpos ? s1[i] * scale : -INFINITY;
+          mk = fmaxf(mk, fmaxf(sc8[i], sc8[4 + i]));
+        }
+        const float mn = fmaxf(m, column_max<16>(mk));
+        float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
-      m = mn;
-      u32x4 p0t, p1t, p2t;
-      split3x8<DT>(sc8, p0t, p1t, p2t);
-      const int nv = pend - pv;  // positions of this lane's group that are written (others: zero V)
+        for (int i = 0; i < 8; ++i) {
+          sc8[i] = mn == -INFINITY ? 0.f : expf(sc8[i] - mn);
+          ps += sc8[i];
+        }
+        ps = column_sum<16>(ps);
+        const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+        sum = sum * alpha + ps;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        u32x4 vt = *reinterpret_cast<const u32x4*>(
-            vc + ((hb * (P.seqcap / 32) + kb / 32) * HD + 16 * tt + c16) * 32 + 8 * kg);
-        if (nv < 8) vt = keep_first(vt, nv < 0 ? 0 : nv);
-        acc[tt] = mfma16<DT>(vt, p2t, acc[tt]);
-        acc[tt] = mfma16<DT>(vt, p1t, acc[tt]);
-        acc[tt] = mfma16<DT>(vt, p0t, acc[tt]);
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
+        m = mn;
+        u32x4 p0t, p1t, p2t;
+        split3x8<DT>(sc8, p0t, p1t, p2t);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          acc[tt] = mfma16<DT>(vt[tt], p2t, acc[tt]);
+          acc[tt] = mfma16<DT>(vt[tt], p1t, acc[tt]);
+          acc[tt] = mfma16<DT>(vt[tt], p0t, acc[tt]);
+        }
       }
     }
-    if (tq < ntok) {
-      const float inv = 1.0f / sum;
+    // merge the eight waves' records in LDS (a wave without positions left m = -inf, sum = 0)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          put_terms<DT>(A.bo, oplane, (int64_t)tq * qd + j * HD + 16 * tt + 4 * kg + i, acc[tt][i] * inv);
+      for (int i = 0; i < 4; ++i) rec[16 * tt + 4 * kg + i] = acc[tt][i];
+    if (kg == 0) {
+      rec[HD] = m;
+      rec[HD + 1] = sum;
     }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * HD; idx += kThreads) {
+      const int c = idx / HD, d = idx % HD, t = qb * 16 + c;
+      if (t >= ntok) continue;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, lds[(w * 16 + c) * REC + HD]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* r = lds + (w * 16 + c) * REC;
+        const float f = r[HD] == -INFINITY ? 0.f : expf(r[HD] - mx);
+        num = fmaf(r[d], f, num);
+        den = fmaf(r[HD + 1], f, den);
+      }
+      put_terms<DT>(A.bo, oplane, (int64_t)t * qd + j * HD + d, num / den);
+    }
+    __syncthreads();
   }
 }
 
 template <int WDT, int KVDT>
 __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, PrefillArgs A) {
+  extern __shared__ float lds_pf[];  // the attention's wave records
   static_assert(WDT == KVDT && (WDT == WF16 || WDT == WBF16), "batched prefill: 16-bit weights and cache");
   constexpr int DT = WDT;
   const int H = P.H, qd = P.qdim, F = P.F, hd = P.hd, half = P.hd / 2, chunk = A.chunk;
@@ -2270,8 +2314,8 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         }
       });
       pf_barrier(P, A.bar, ++nbar);
-      if (hd == 128) pf_attn<DT, 128>(P, A, l, p0, ntok, gw, nw);
-      else pf_attn<DT, 64>(P, A, l, p0, ntok, gw, nw);
+      if (hd == 128) pf_attn<DT, 128>(P, A, l, p0, ntok, lds_pf);
+      else pf_attn<DT, 64>(P, A, l, p0, ntok, lds_pf);
       pf_barrier(P, A.bar, ++nbar);
       // O projection + residual
       pf_gemm<DT>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, [&](int r4, int t, f32x4 v) {

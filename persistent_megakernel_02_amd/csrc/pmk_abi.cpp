@@ -57,6 +57,8 @@ void scale_counts(const ModelDims& m, int64_t sz[7]) {
   const int64_t rows[7] = {qd, kvd, kvd, H, F, F, H}, cols[7] = {H, H, H, qd, H, H, F};
   for (int i = 0; i < 7; ++i) sz[i] = (m.wdt == PMK_DT_FP8_E4M3 ? nblk(rows[i]) : rows[i]) * nblk(cols[i]);
 }
+// LDS of the batched prefill: the attention's eight wave records of 16 queries x (hd + 2) floats
+size_t prefill_lds_bytes(const ModelDims& m) { return (size_t)kWaves * 16 * (m.hd + 2) * 4; }
 int64_t lm_scale_count(const ModelDims& m) { return (m.wdt == PMK_DT_FP8_E4M3 ? nblk(m.V) : m.V) * nblk(m.H); }
 
 struct Phase {
@@ -569,7 +571,7 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
     const bool fmt16 = (c->m.wdt == PMK_DT_F16 && c->m.kvdt == PMK_DT_F16) ||
                        (c->m.wdt == PMK_DT_BF16 && c->m.kvdt == PMK_DT_BF16);
     const int cap = (c->m.max_seq + 127) / 128 * 128;
-    c->pf_chunk = !fmt16 || ch == -1 ? 0 : std::min(ch == 0 ? 256 : ch, cap);
+    c->pf_chunk = !fmt16 || ch == -1 ? 0 : std::min(ch == 0 ? 512 : ch, cap);
   }
   std::string e = build_schedule(c->m, c->sc, n_cus, &c->sched);
   if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
@@ -611,7 +613,10 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
     if (per_cu < 1) { delete c; return fail(nullptr, PMK_ERR_DEVICE, "the persistent kernel cannot be resident on a CU"); }
     if (c->pf_chunk > 0) {
       per_cu = 0;
-      he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prefill_kernel(c->m.wdt, c->m.kvdt), kThreads, 0);
+      const void* pf = prefill_kernel(c->m.wdt, c->m.kvdt);
+      he = hipFuncSetAttribute(pf, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (he == hipSuccess)
+        he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pf, kThreads, prefill_lds_bytes(c->m));
       if (he != hipSuccess || per_cu < 1) c->pf_chunk = 0;  // step-by-step prefill then
     }
   }
@@ -791,8 +796,8 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P - 1, 0, d_tokens + P - 1, st));
     HIPCHK(c, hipMemsetAsync(a.bar, 0, 4, st));
     void* args[] = {&c->kp, &a};
-    HIPCHK(c, hipLaunchCooperativeKernel(prefill_kernel(c->m.wdt, c->m.kvdt), dim3(c->n_cus), dim3(kThreads), args, 0u,
-                                         st));
+    HIPCHK(c, hipLaunchCooperativeKernel(prefill_kernel(c->m.wdt, c->m.kvdt), dim3(c->n_cus), dim3(kThreads), args,
+                                         (unsigned)prefill_lds_bytes(c->m), st));
     CallParams cp{};
     cp.forced = d_tokens + P - 1;
     cp.n_steps = 1;
