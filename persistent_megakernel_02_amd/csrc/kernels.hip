@@ -2004,29 +2004,36 @@ __device__ __forceinline__ void put_terms(uint16_t* planes, int64_t plane, int64
   planes[2 * plane + idx] = enc16<DT>(r - dec16<DT>(m));
 }
 
-// Grid barrier number `k` (1-based) of the launch: every workgroup arrives once per barrier.  The
-// fences publish this workgroup's stores and make the other workgroups' visible to later loads.
-// The wait is bounded like every other wait (watchdog: the abort word ends all of them).
+// Grid barrier number `k` (1-based) of the launch.  Each workgroup owns one flag word (bar[b],
+// zero at launch): it drains its stores, publishes them (agent-scope release) and stores k into
+// its flag; then wave 0 polls all the flags, one coherent load per lane per 64 workgroups, until
+// every one shows k (a single shared counter serialised 256 atomics, ~50 us per barrier).  The
+// acquire fence then makes the other workgroups' stores visible to later loads.  The wait is
+// bounded like every other wait (watchdog: the abort word ends all of them).
 __device__ __forceinline__ void pf_barrier(const KParams& P, uint32_t* bar, uint32_t k) {
-  __threadfence();
+  drain();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = k * gridDim.x;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    stc(&bar[blockIdx.x], k);
+  }
+  if (threadIdx.x < 64) {
+    const int n = (int)gridDim.x;
     int64_t spins = 0;
-    uint32_t v = ldc(bar);
-    while (v < target) {
+    while (true) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // each round reads the flags again
+      bool ok = true;
+      for (int b = (int)threadIdx.x; b < n; b += 64) ok = ok && ldc(&bar[b]) >= k;
+      if (__all(ok)) break;
       if (ldc(&P.ctrl[CTRL_ABORT]) != 0u) break;
       if (++spins > P.spin_limit) {
-        report_error(P.ctrl, PMK_ERR_TIMEOUT, (int)blockIdx.x, -1, -1, target, v);
+        if (threadIdx.x == 0) report_error(P.ctrl, PMK_ERR_TIMEOUT, (int)blockIdx.x, -1, -1, k, 0);
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
-      v = ldc(bar);
     }
   }
   __syncthreads();
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // RMSNorm of `ntok` rows of src [chunk][H] (or, with emb, of the embedding rows of the tokens,

@@ -251,7 +251,7 @@ void compute_layout(pmk_ctx* c) {
     c->w_pfbn = w; w = align256(w + 3 * ch * H * 2);
     c->w_pfbo = w; w = align256(w + 3 * ch * qd * 2);
     c->w_pfbh = w; w = align256(w + 3 * ch * F * 2);
-    c->w_pfbar = w; w = align256(w + 4);
+    c->w_pfbar = w; w = align256(w + (int64_t)std::max(c->n_cus, 1) * 4);  // one barrier flag per workgroup
   }
   c->sizes.workspace_bytes = w;
 
@@ -794,7 +794,7 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     a.bh = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbh);
     a.bar = reinterpret_cast<uint32_t*>(c->ws + c->w_pfbar);
     HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P - 1, 0, d_tokens + P - 1, st));
-    HIPCHK(c, hipMemsetAsync(a.bar, 0, 4, st));
+    HIPCHK(c, hipMemsetAsync(a.bar, 0, (size_t)c->n_cus * 4, st));
     void* args[] = {&c->kp, &a};
     HIPCHK(c, hipLaunchCooperativeKernel(prefill_kernel(c->m.wdt, c->m.kvdt), dim3(c->n_cus), dim3(kThreads), args,
                                          (unsigned)prefill_lds_bytes(c->m), st));

@@ -52,7 +52,7 @@ struct PrefillArgs {
   uint16_t* bn;           // [3][chunk][H] normalised activations as three 16-bit terms
   uint16_t* bo;           // [3][chunk][qdim] attention output as three terms
   uint16_t* bh;           // [3][chunk][F] SwiGLU output as three terms
-  uint32_t* bar;          // grid barrier arrivals (zero at launch)
+  uint32_t* bar;          // grid barrier: one flag word per workgroup (zero at launch)
 };
 
 struct KParams {
