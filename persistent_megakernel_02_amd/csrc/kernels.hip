@@ -1966,7 +1966,6 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 // phases wrote; phases are separated by a grid barrier (agent-scope fences and one arrival
 // counter), so there is no schedule to validate.
 // ------------------------------------------------------------------------------------------------
-constexpr int kPfRows = 64;    // GEMM tile rows (four 16-row blocks)
 constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
 
 // fp32 x[8] -> three 16-bit terms of format DT per element (nearest even at each step)
@@ -2072,18 +2071,19 @@ __device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& 
   }
 }
 
-// One GEMM tile: rows [row0, row0 + 64) of W ([N][K], 16-bit format DT) against tokens
+// One GEMM tile: rows [row0, row0 + MR) of W ([N][K], 16-bit format DT) against tokens
 // [tok0, tok0 + 128) of the three-term planes B ([3][chunk][K]).  Wave w takes tokens
-// tok0 + 16w .. + 15 and all four 16-row blocks; per 32-column step each lane loads 16 bytes of
-// four weight rows and of its token's three terms and issues twelve matrix-core products.
-// epi(r, t, v) receives rows r .. r + 3 (r = row0 + 16 b + 4 (lane / 16), b = 0..3) of token
-// t = tok0 + 16 w + lane % 16 (rows past N hold zeros).
-template <int DT, class Epi>
+// tok0 + 16w .. + 15 and all MR / 16 row blocks; per 32-column step the weight block goes through
+// LDS once for the workgroup, each lane reads its token's three terms (a 4-step register ring) and
+// issues 3 MR / 16 matrix-core products.  epi(r, t, v) receives rows r .. r + 3
+// (r = row0 + 16 b + 4 (lane / 16)) of token t = tok0 + 16 w + lane % 16 (rows past N are zero).
+template <int DT, int MR, class Epi>
 __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int row0,
-                                             int tok0, Epi epi) {
-  constexpr int RB = kPfRows / 16;  // 16-row blocks per tile
+                                             int tok0, float* lds, Epi epi) {
+  constexpr int RB = MR / 16;   // 16-row blocks per tile
+  constexpr int AW = MR >= 128 ? MR / 128 : 1;  // 16-byte A pieces per thread per step (MR x 4 pieces)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, kg = lane >> 4;
-  const int rows = N - row0 < kPfRows ? N - row0 : kPfRows;
+  const int rows = N - row0 < MR ? N - row0 : MR;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + (int64_t)row0 * K * 2), (short)0, rows * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
@@ -2093,50 +2093,81 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
   const uint32_t bplane = (uint32_t)chunk * (uint32_t)K * 2u;
   const uint32_t bbase = (uint32_t)((int64_t)tok * K * 2);
   const int nsteps = (K + 31) / 32;
-  // a ring of D steps of fragments in flight per lane (each slot refilled right after it is
-  // consumed; the loads of a step past the end read zeros without touching memory)
+  // A: the workgroup's MR x 32 weight block of a step goes through LDS (two buffers of MR x 64 bytes,
+  // row-major), each lane loading its pieces one step ahead; a piece is 8 columns (16 bytes) of one
+  // row: piece p = thread + 512 a -> row p / 4, columns 8 (p % 4) ..
+  uint8_t* abuf = reinterpret_cast<uint8_t*>(lds);
+  u32x4 an[AW];
+  auto load_a = [&](int step) {
+#pragma unroll
+    for (int a = 0; a < AW; ++a) {
+      const int p = (int)threadIdx.x + kThreads * a, r = p >> 2, k = step * 32 + 8 * (p & 3);
+      an[a] = __builtin_amdgcn_raw_buffer_load_b128(wr, k < K && p < MR * 4 ? (uint32_t)((r * K + k) * 2) : kOut, 0, 0);
+    }
+  };
+  auto store_a = [&](int step) {
+    uint8_t* dst = abuf + (step & 1) * MR * 64;
+#pragma unroll
+    for (int a = 0; a < AW; ++a) {
+      const int p = (int)threadIdx.x + kThreads * a;
+      if (p < MR * 4) *reinterpret_cast<u32x4*>(dst + p * 16) = an[a];
+    }
+  };
+  // B: a ring of D steps of this lane's three terms in flight (each slot refilled right after it is
+  // consumed; a step past the end reads zeros without touching memory)
   constexpr int D = 4;
-  u32x4 ra[D][RB], rb[D][3];
+  u32x4 rb[D][3];
   auto issue = [&](int d, int step) {
     const int k = step * 32 + 8 * kg;
     const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
     const uint32_t ko = (uint32_t)k * 2u;
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
-      ra[d][b] = __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? (uint32_t)((16 * b + r16) * K * 2) + ko : kOut, 0, 0);
-#pragma unroll
     for (int t = 0; t < 3; ++t)
       rb[d][t] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? bbase + ko + (uint32_t)t * bplane : kOut, 0, 0);
   };
+  load_a(0);
+  store_a(0);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
+  load_a(1);
+  __syncthreads();
   f32x4 acc[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (base + d < nsteps) {
+      const int step = base + d;
+      if (step < nsteps) {
+        const uint8_t* src = abuf + (step & 1) * MR * 64 + r16 * 64 + kg * 16;
 #pragma unroll
-        for (int t = 2; t >= 0; --t)
+        for (int b = 0; b < RB; ++b) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(src + b * 16 * 64);
 #pragma unroll
-          for (int b = 0; b < RB; ++b) acc[b] = mfma16<DT>(ra[d][b], rb[d][t], acc[b]);
+          for (int t = 2; t >= 0; --t) acc[b] = mfma16<DT>(a, rb[d][t], acc[b]);
+        }
       }
-      issue(d, base + d + D);
+      issue(d, step + D);
+      // the next step's A into the other buffer (read by every wave only after the barrier), then
+      // the loads of the step after it
+      if (step + 1 < nsteps) store_a(step + 1);
+      load_a(step + 2);
+      __syncthreads();
     }
   }
 #pragma unroll
   for (int b = 0; b < RB; ++b) epi(row0 + 16 * b + 4 * kg, tok, acc[b]);
 }
 
-// Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles spread over the grid.
-template <int DT, class Epi>
+// Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles of MR rows spread over
+// the grid.
+template <int DT, int MR, class Epi>
 __device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int ntok,
-                                        Epi epi) {
-  const int nr = (N + kPfRows - 1) / kPfRows, nt = (ntok + kPfTokens - 1) / kPfTokens;
+                                        float* lds, Epi epi) {
+  const int nr = (N + MR - 1) / MR, nt = (ntok + kPfTokens - 1) / kPfTokens;
   for (int ti = blockIdx.x; ti < nr * nt; ti += gridDim.x) {
-    const int row0 = (ti / nt) * kPfRows, tok0 = (ti % nt) * kPfTokens;
-    pf_gemm_tile<DT>(W, N, K, B, chunk, row0, tok0, epi);
+    const int row0 = (ti / nt) * MR, tok0 = (ti % nt) * kPfTokens;
+    pf_gemm_tile<DT, MR>(W, N, K, B, chunk, row0, tok0, lds, epi);
   }
 }
 
@@ -2286,7 +2317,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
     for (int l = 0; l < P.L; ++l) {
       const uint8_t* Wl = P.wbase + (int64_t)l * P.layer_bytes;
       // QKV: rows 2m, 2m + 1 are a RoPE pair (q, k) or two v dims; q to A.q, k and v to the cache
-      pf_gemm<DT>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, [&](int r4, int t, f32x4 v) {
+      pf_gemm<DT, 128>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
         if (t >= ntok || r4 >= P.qkv_rows) return;
         const int pos = p0 + t;
 #pragma unroll
@@ -2325,7 +2356,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
       else pf_attn<DT, 64>(P, A, l, p0, ntok, lds_pf);
       pf_barrier(P, A.bar, ++nbar);
       // O projection + residual
-      pf_gemm<DT>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, [&](int r4, int t, f32x4 v) {
+      pf_gemm<DT, 128>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -2338,7 +2369,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
       pf_barrier(P, A.bar, ++nbar);
       // gate/up (interleaved rows 2n, 2n + 1) + SwiGLU
       const int64_t hplane = (int64_t)chunk * F;
-      pf_gemm<DT>(Wl + P.off_gu, 2 * F, H, A.bn, chunk, ntok, [&](int r4, int t, f32x4 v) {
+      pf_gemm<DT, 256>(Wl + P.off_gu, 2 * F, H, A.bn, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
@@ -2350,7 +2381,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
       });
       pf_barrier(P, A.bar, ++nbar);
       // down projection + residual
-      pf_gemm<DT>(Wl + P.off_d, H, F, A.bh, chunk, ntok, [&](int r4, int t, f32x4 v) {
+      pf_gemm<DT, 128>(Wl + P.off_d, H, F, A.bh, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -57,8 +57,11 @@ void scale_counts(const ModelDims& m, int64_t sz[7]) {
   const int64_t rows[7] = {qd, kvd, kvd, H, F, F, H}, cols[7] = {H, H, H, qd, H, H, F};
   for (int i = 0; i < 7; ++i) sz[i] = (m.wdt == PMK_DT_FP8_E4M3 ? nblk(rows[i]) : rows[i]) * nblk(cols[i]);
 }
-// LDS of the batched prefill: the attention's eight wave records of 16 queries x (hd + 2) floats
-size_t prefill_lds_bytes(const ModelDims& m) { return (size_t)kWaves * 16 * (m.hd + 2) * 4; }
+// LDS of the batched prefill: the attention's eight wave records of 16 queries x (hd + 2) floats,
+// or the GEMM's two 256-row x 64-byte weight buffers
+size_t prefill_lds_bytes(const ModelDims& m) {
+  return std::max((size_t)kWaves * 16 * (m.hd + 2) * 4, (size_t)2 * 256 * 64);
+}
 int64_t lm_scale_count(const ModelDims& m) { return (m.wdt == PMK_DT_FP8_E4M3 ? nblk(m.V) : m.V) * nblk(m.H); }
 
 struct Phase {
