@@ -269,9 +269,15 @@ pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stre
  * NULL the library derives them from this prompt: a calibration pass with every scale 1 records the
  * largest |k| and |v| per (layer, kv head), each scale becomes that maximum / 448 in fp32 (1 if the
  * maximum is 0), and the prefill then runs with those scales (read them back with pmk_get_kv_scales).
- * Other KV formats ignore d_kv_scales.  Resets the position and the synchronisation state.
+ * Other KV formats ignore d_kv_scales.  With 16-bit weights and cache (and prefill_chunk != -1)
+ * positions 0..P-2 run batched, in chunks of prefill_chunk tokens, in ONE cooperative launch of
+ * grid-wide phases (RMSNorm, QKV GEMM + RoPE + KV append, causal attention, O GEMM, RMSNorm,
+ * gate/up GEMM + SwiGLU, down GEMM) with the GEMMs on the matrix cores at fp32 accuracy, and the
+ * last position as a teacher-forced decode step; other formats run every position as a
+ * teacher-forced decode step.  Resets the position and the synchronisation state.
  * Asynchronous on `stream`.  Errors: PMK_ERR_NOT_BOUND (no weights), PMK_ERR_INVALID_ARG (NULL
- * tokens, P <= 0), PMK_ERR_CAPACITY (P > max_seq), PMK_ERR_HIP. */
+ * tokens, P <= 0), PMK_ERR_CAPACITY (P > max_seq), PMK_ERR_HIP; a batched-prefill barrier that
+ * exceeds spin_limit polls records PMK_ERR_TIMEOUT for pmk_poll_error. */
 pmk_status pmk_prefill_kv(pmk_ctx* ctx, const int32_t* d_tokens, int32_t P, const float* d_kv_scales,
                           int32_t* d_first_token, void* stream);
 
