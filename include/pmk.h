@@ -129,11 +129,10 @@ typedef struct {
                                under ~33 KiB while the O-projection tiles still fit in LDS) */
   int32_t combine_o_share;  /* O-projection rows on the queues that run a COMBINE: 0 automatic, 1 none,
                                2 half a share, 3 a full share */
-  int32_t prefill_chunk;    /* prompt positions per chunk of the batched prefill (16-bit weights and
-                               cache only): 0 = 512 (or max_seq rounded up to 128 if smaller), a
-                               multiple of 128 up to 1024, or -1 = no batched prefill (every prompt
-                               position runs as a teacher-forced decode step); other formats always
-                               prefill step by step */
+  int32_t prefill_chunk;    /* prompt positions per chunk of the batched prefill: 0 = 512 (or max_seq
+                               rounded up to 128 if smaller), a multiple of 128 up to 1024, or -1 = no
+                               batched prefill (every prompt position runs as a teacher-forced decode
+                               step) */
   int32_t reserved[5];      /* must be 0 */
 } pmk_schedule_config;
 
@@ -269,12 +268,13 @@ pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stre
  * NULL the library derives them from this prompt: a calibration pass with every scale 1 records the
  * largest |k| and |v| per (layer, kv head), each scale becomes that maximum / 448 in fp32 (1 if the
  * maximum is 0), and the prefill then runs with those scales (read them back with pmk_get_kv_scales).
- * Other KV formats ignore d_kv_scales.  With 16-bit weights and cache (and prefill_chunk != -1)
- * positions 0..P-2 run batched, in chunks of prefill_chunk tokens, in ONE cooperative launch of
- * grid-wide phases (RMSNorm, QKV GEMM + RoPE + KV append, causal attention, O GEMM, RMSNorm,
- * gate/up GEMM + SwiGLU, down GEMM) with the GEMMs on the matrix cores at fp32 accuracy, and the
- * last position as a teacher-forced decode step; other formats run every position as a
- * teacher-forced decode step.  Resets the position and the synchronisation state.
+ * Other KV formats ignore d_kv_scales.  Unless prefill_chunk is -1, positions 0..P-2 run batched,
+ * in chunks of prefill_chunk tokens, in ONE cooperative launch of grid-wide phases (RMSNorm, QKV
+ * GEMM + RoPE + KV append, causal attention, O GEMM, RMSNorm, gate/up GEMM + SwiGLU, down GEMM)
+ * with the GEMMs on the matrix cores (fp32-accurate activations; binary16 ones for INT8 / INT4, as
+ * the format defines), and the last position as a teacher-forced decode step; with -1 every
+ * position runs as a teacher-forced decode step.  Resets the position and the synchronisation
+ * state.
  * Asynchronous on `stream`.  Errors: PMK_ERR_NOT_BOUND (no weights), PMK_ERR_INVALID_ARG (NULL
  * tokens, P <= 0), PMK_ERR_CAPACITY (P > max_seq), PMK_ERR_HIP; a batched-prefill barrier that
  * exceeds spin_limit polls records PMK_ERR_TIMEOUT for pmk_poll_error. */

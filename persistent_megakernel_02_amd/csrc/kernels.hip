@@ -1954,19 +1954,28 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 // zero flags, counters, control words and the step tags of the attention output; set position
 // and next token
 // ------------------------------------------------------------------------------------------------
-// Batched prefill (16-bit weights and KV cache).  The prompt's positions go through the model in
-// chunks of up to `chunk` tokens; each layer of a chunk is a sequence of grid-wide phases of ONE
-// cooperative launch: RMSNorm (one wave per token), the QKV GEMM with RoPE and the KV append in
-// its epilogue, causal attention (one wave per (q head, 16 queries)), the O GEMM + residual,
-// RMSNorm, the gate/up GEMM + SwiGLU, the down GEMM + residual.  The GEMMs are dense contractions
-// over the chunk's tokens and run on the matrix cores (v_mfma_f32_16x16x32 in the weight format):
-// the weights are the A operand as stored (exact), the fp32 activations the B operand as three
-// 16-bit terms (x = t0 + t1 + t2 to ~2^-24 relative, each product accumulated in fp32), so the
-// results keep fp32 accuracy in a different rounding order.  A phase reads only what earlier
-// phases wrote; phases are separated by a grid barrier (agent-scope fences and one arrival
-// counter), so there is no schedule to validate.
+// Batched prefill.  The prompt's positions go through the model in chunks of up to `chunk`
+// tokens; each layer of a chunk is a sequence of grid-wide phases of ONE cooperative launch:
+// RMSNorm (one wave per token), the QKV GEMM with RoPE and the KV append in its epilogue, causal
+// attention, the O GEMM + residual, RMSNorm, the gate/up GEMM + SwiGLU, the down GEMM + residual.
+// The GEMMs are dense contractions over the chunk's tokens and run on the matrix cores
+// (v_mfma_f32_16x16x32): the weights are the A operand, converted exactly to a 16-bit format where
+// they are not one (FP8 -> bf16, int8 / int4 codes -> binary16) and scaled per 128-column group
+// after the products (FP8 block scales, integer group scales); the activations are the B operand,
+// as three 16-bit terms (x = t0 + t1 + t2 to ~2^-24, each product accumulated in fp32: fp32
+// accuracy in another rounding order) or, for the integer formats, as the one binary16 value the
+// format defines.  A phase reads only what earlier phases wrote; phases are separated by a grid
+// barrier, so there is no schedule to validate.
 // ------------------------------------------------------------------------------------------------
 constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
+
+template <int WDT>
+struct PfFmt {
+  static constexpr bool INT = weight_is_int(WDT);
+  static constexpr int ADT = WDT == WF16 || INT ? WF16 : WBF16;  // matrix-core operand format
+  static constexpr int NTERM = INT ? 1 : 3;                       // activation terms
+  static constexpr bool SCALED = WDT >= WFP8;
+};
 
 // fp32 x[8] -> three 16-bit terms of format DT per element (nearest even at each step)
 template <int DT>
@@ -1992,15 +2001,18 @@ __device__ __forceinline__ void split3x8(const float* x, u32x4& t0, u32x4& t1, u
   t2 = u32x4{c[0], c[1], c[2], c[3]};
 }
 
-// Store v as three 16-bit terms at element idx of three planes `plane` elements apart.
-template <int DT>
+// Store v as NT 16-bit terms of format DT at element idx of NT planes `plane` elements apart (one
+// term: v rounded to DT, the binary16 activation of the integer formats).
+template <int DT, int NT>
 __device__ __forceinline__ void put_terms(uint16_t* planes, int64_t plane, int64_t idx, float v) {
   const uint16_t h = enc16<DT>(v);
-  const float r = v - dec16<DT>(h);
-  const uint16_t m = enc16<DT>(r);
   planes[idx] = h;
-  planes[plane + idx] = m;
-  planes[2 * plane + idx] = enc16<DT>(r - dec16<DT>(m));
+  if constexpr (NT == 3) {
+    const float r = v - dec16<DT>(h);
+    const uint16_t m = enc16<DT>(r);
+    planes[plane + idx] = m;
+    planes[2 * plane + idx] = enc16<DT>(r - dec16<DT>(m));
+  }
 }
 
 // Grid barrier number `k` (1-based) of the launch.  Each workgroup owns one flag word (bar[b],
@@ -2035,10 +2047,10 @@ __device__ __forceinline__ void pf_barrier(const KParams& P, uint32_t* bar, uint
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// RMSNorm of `ntok` rows of src [chunk][H] (or, with emb, of the embedding rows of the tokens,
-// written to src first) into three-term planes bn: (x * r) * g with r = 1 / sqrt(mean(x^2) + eps).
-// One wave per token.
-template <int DT, int EDT>
+// RMSNorm of `ntok` rows of src [chunk][H] (or, with emb_tok, of the embedding rows of those tokens,
+// written to src first) into the activation planes bn: (x * r) * g with r = 1 / sqrt(mean(x^2) +
+// eps), as NT terms of format DT.  One wave per token.
+template <int DT, int NT, int EDT>
 __device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& A, float* src, const int32_t* emb_tok,
                                            const float* gain, int ntok, int gw, int nw) {
   const int lane = threadIdx.x & 63, H = P.H;
@@ -2065,44 +2077,80 @@ __device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& 
     for (int k = 2 * lane; k < H; k += 128) {
       const float2 v = *reinterpret_cast<const float2*>(x + k);
       const float2 g = *reinterpret_cast<const float2*>(gain + k);
-      put_terms<DT>(A.bn, plane, (int64_t)t * H + k, (v.x * r) * g.x);
-      put_terms<DT>(A.bn, plane, (int64_t)t * H + k + 1, (v.y * r) * g.y);
+      put_terms<DT, NT>(A.bn, plane, (int64_t)t * H + k, (v.x * r) * g.x);
+      put_terms<DT, NT>(A.bn, plane, (int64_t)t * H + k + 1, (v.y * r) * g.y);
     }
   }
 }
 
-// One GEMM tile: rows [row0, row0 + MR) of W ([N][K], 16-bit format DT) against tokens
-// [tok0, tok0 + 128) of the three-term planes B ([3][chunk][K]).  Wave w takes tokens
+// 8 columns of one weight row as 8 exact 16-bit matrix-core operands (format PfFmt::ADT), from
+// their bytes in the arena: 16-bit formats as stored; FP8 E4M3 to bf16; int8 / int4 codes (offset
+// binary, int4 nibbles of the word in the order 0 2 4 6 1 3 5 7) to binary16.
+template <int WDT>
+__device__ __forceinline__ u32x4 pf_load_a8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (WDT == WF16 || WDT == WBF16) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  } else if constexpr (WDT == WFP8) {
+    return fp8x8_bf16(__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  } else if constexpr (WDT == WI8) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const h16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    auto cv = [&](uint32_t v, uint32_t sel) {
+      return __builtin_bit_cast(uint32_t, as_h2(__builtin_amdgcn_perm(0x64646464u, v, sel)) + bias);
+    };
+    return u32x4{cv(w.x, 0x04010400u), cv(w.x, 0x04030402u), cv(w.y, 0x04010400u), cv(w.y, 0x04030402u)};
+  } else {
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    const h16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h16x2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h16x2 b2 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t magic = 0x64006400u, w8 = w >> 8;
+    const h16x2 p0 = as_h2(and_or(w, 0x000F000Fu, magic)) + b1;
+    const h16x2 p1 = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, magic)), m16, b2);
+    const h16x2 p2 = as_h2(and_or(w8, 0x000F000Fu, magic)) + b1;
+    const h16x2 p3 = __builtin_elementwise_fma(as_h2(and_or(w8, 0x00F000F0u, magic)), m16, b2);
+    return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+                 __builtin_bit_cast(uint32_t, p3)};
+  }
+}
+
+// One GEMM tile: rows [row0, row0 + MR) of W ([N][K] in format WDT) against tokens
+// [tok0, tok0 + 128) of the activation planes B ([NTERM][chunk][K]).  Wave w takes tokens
 // tok0 + 16w .. + 15 and all MR / 16 row blocks; per 32-column step the weight block goes through
-// LDS once for the workgroup, each lane reads its token's three terms (a 4-step register ring) and
-// issues 3 MR / 16 matrix-core products.  epi(r, t, v) receives rows r .. r + 3
-// (r = row0 + 16 b + 4 (lane / 16)) of token t = tok0 + 16 w + lane % 16 (rows past N are zero).
-template <int DT, int MR, class Epi>
+// LDS once for the workgroup (converted to 16-bit operands on the way), each lane reads its
+// token's terms (a 4-step register ring) and issues NTERM MR / 16 matrix-core products.  Scaled
+// formats accumulate each 128-column group apart and add it times scale(row, group).
+// epi(r, t, v) receives rows r .. r + 3 (r = row0 + 16 b + 4 (lane / 16)) of token
+// t = tok0 + 16 w + lane % 16 (rows past N are garbage the epilogues skip).
+template <int WDT, int MR, class ScaleF, class Epi>
 __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int row0,
-                                             int tok0, float* lds, Epi epi) {
-  constexpr int RB = MR / 16;   // 16-row blocks per tile
-  constexpr int AW = MR >= 128 ? MR / 128 : 1;  // 16-byte A pieces per thread per step (MR x 4 pieces)
+                                             int tok0, float* lds, ScaleF scale, Epi epi) {
+  using F = PfFmt<WDT>;
+  constexpr int RB = MR / 16;                   // 16-row blocks per tile
+  constexpr int AW = MR >= 128 ? MR / 128 : 1;  // 8-column A pieces per thread per step (MR x 4 pieces)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, kg = lane >> 4;
   const int rows = N - row0 < MR ? N - row0 : MR;
+  const int64_t rbytes = weight_row_bytes(WDT, K);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(W + (int64_t)row0 * K * 2), (short)0, rows * K * 2, 0x00020000);
+      const_cast<uint8_t*>(W + (int64_t)row0 * rbytes), (short)0, (int)(rows * rbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(B), (short)0, (int)((int64_t)3 * chunk * K * 2), 0x00020000);
+      const_cast<uint16_t*>(B), (short)0, (int)((int64_t)F::NTERM * chunk * K * 2), 0x00020000);
   constexpr uint32_t kOut = 0x7FFFFFF0u;
   const int tok = tok0 + 16 * wave + r16;
   const uint32_t bplane = (uint32_t)chunk * (uint32_t)K * 2u;
   const uint32_t bbase = (uint32_t)((int64_t)tok * K * 2);
   const int nsteps = (K + 31) / 32;
-  // A: the workgroup's MR x 32 weight block of a step goes through LDS (two buffers of MR x 64 bytes,
-  // row-major), each lane loading its pieces one step ahead; a piece is 8 columns (16 bytes) of one
-  // row: piece p = thread + 512 a -> row p / 4, columns 8 (p % 4) ..
+  // A: the workgroup's MR x 32 block of a step goes through LDS (two buffers of MR x 64 bytes of
+  // 16-bit operands, row-major), each thread loading its pieces one step ahead; piece
+  // p = thread + 512 a -> row p / 4, columns 8 (p % 4) ..
   uint8_t* abuf = reinterpret_cast<uint8_t*>(lds);
   u32x4 an[AW];
   auto load_a = [&](int step) {
 #pragma unroll
     for (int a = 0; a < AW; ++a) {
       const int p = (int)threadIdx.x + kThreads * a, r = p >> 2, k = step * 32 + 8 * (p & 3);
-      an[a] = __builtin_amdgcn_raw_buffer_load_b128(wr, k < K && p < MR * 4 ? (uint32_t)((r * K + k) * 2) : kOut, 0, 0);
+      const uint32_t off = (uint32_t)(r * rbytes + (int64_t)k * weight_bits(WDT) / 8);
+      an[a] = pf_load_a8<WDT>(wr, k < K && p < MR * 4 ? off : kOut);
     }
   };
   auto store_a = [&](int step) {
@@ -2113,16 +2161,16 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
       if (p < MR * 4) *reinterpret_cast<u32x4*>(dst + p * 16) = an[a];
     }
   };
-  // B: a ring of D steps of this lane's three terms in flight (each slot refilled right after it is
+  // B: a ring of D steps of this lane's terms in flight (each slot refilled right after it is
   // consumed; a step past the end reads zeros without touching memory)
   constexpr int D = 4;
-  u32x4 rb[D][3];
+  u32x4 rb[D][F::NTERM];
   auto issue = [&](int d, int step) {
     const int k = step * 32 + 8 * kg;
     const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
     const uint32_t ko = (uint32_t)k * 2u;
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < F::NTERM; ++t)
       rb[d][t] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? bbase + ko + (uint32_t)t * bplane : kOut, 0, 0);
   };
   load_a(0);
@@ -2131,9 +2179,11 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
   for (int d = 0; d < D; ++d) issue(d, d);
   load_a(1);
   __syncthreads();
-  f32x4 acc[RB];
+  f32x4 acc[RB], accg[F::SCALED ? RB : 1];
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < (F::SCALED ? RB : 1); ++b) accg[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -2143,8 +2193,20 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(src + b * 16 * 64);
+          f32x4& c = F::SCALED ? accg[b] : acc[b];
 #pragma unroll
-          for (int t = 2; t >= 0; --t) acc[b] = mfma16<DT>(a, rb[d][t], acc[b]);
+          for (int t = F::NTERM - 1; t >= 0; --t) c = mfma16<F::ADT>(a, rb[d][t], c);
+        }
+        if constexpr (F::SCALED) {
+          if ((step & 3) == 3 || step == nsteps - 1) {  // end of a 128-column group
+            const int g = step >> 2;
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(accg[b][i], scale(row0 + 16 * b + 4 * kg + i, g), acc[b][i]);
+              accg[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+          }
         }
       }
       issue(d, step + D);
@@ -2161,14 +2223,21 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
 
 // Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles of MR rows spread over
 // the grid.
-template <int DT, int MR, class Epi>
+template <int WDT, int MR, class ScaleF, class Epi>
 __device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int ntok,
-                                        float* lds, Epi epi) {
+                                        float* lds, ScaleF scale, Epi epi) {
   const int nr = (N + MR - 1) / MR, nt = (ntok + kPfTokens - 1) / kPfTokens;
   for (int ti = blockIdx.x; ti < nr * nt; ti += gridDim.x) {
     const int row0 = (ti / nt) * MR, tok0 = (ti % nt) * kPfTokens;
-    pf_gemm_tile<DT, MR>(W, N, K, B, chunk, row0, tok0, lds, epi);
+    pf_gemm_tile<WDT, MR>(W, N, K, B, chunk, row0, tok0, lds, scale, epi);
   }
+}
+
+// 8 cache elements (K row piece or V^T piece) as 16-bit matrix-core operands: FP8 to bf16 (exact).
+template <int KVDT>
+__device__ __forceinline__ u32x4 pf_kv8(const uint8_t* base, int64_t elem) {
+  if constexpr (KVDT == WFP8) return fp8x8_bf16(*reinterpret_cast<const u32x2*>(base + elem));
+  else return *reinterpret_cast<const u32x4*>(base + elem * 2);
 }
 
 // Causal attention of the chunk's queries (positions p0 .. p0 + ntok - 1) over the cache
@@ -2177,23 +2246,29 @@ __device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const ui
 // 32-position groups w, w + 8, ... up to the block's last query, with the decode attention's
 // matrix-core layout and the 16 queries of the head as the B columns: scores = K rows (A) x q
 // (B, three terms), online softmax per query, P.V = V^T (A, from the blocked V cache) x P (B,
-// three terms).  The waves' (max, sum, acc) are merged in LDS (lds: 8 x 16 x (hd + 2) floats) and
-// the output goes to the three-term planes bo.
-template <int DT, int HD>
+// three terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
+// output).  The waves' (max, sum, acc) are merged in LDS (8 x 16 x (hd + 2) floats) and the output
+// goes to the activation planes bo as ONT terms of format ODT.
+template <int KVDT, int ODT, int ONT, int HD>
 __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, int l, int p0, int ntok, float* lds) {
+  constexpr int KDT = KVDT == WF16 ? WF16 : WBF16;  // operand format of the cache values
+  constexpr int KES = KVDT == WFP8 ? 1 : 2;
   constexpr int NC = HD / 32, NT = HD / 16, REC = HD + 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15, kg = lane >> 4;
   const int nqb = (ntok + 15) / 16, ntasks = P.nq * nqb, qd = P.qdim;
   const int pend = p0 + ntok;  // cache positions [0, pend) are written
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(P.kc);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(P.vc);
   const int64_t oplane = (int64_t)A.chunk * qd;
-  const float scale = P.attn_scale;
   float* rec = lds + (wave * 16 + c16) * REC;  // this lane's column record: acc[HD], m, sum
   for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
     const int j = task % P.nq, qb = task / P.nq;
     const int g = j / P.grp;
     const int64_t hb = (int64_t)l * P.nkv + g;
+    float kscale = 1.f, vscale = 1.f;
+    if constexpr (KVDT == WFP8) {
+      kscale = P.kv_scale[hb * 2];
+      vscale = P.kv_scale[hb * 2 + 1];
+    }
+    const float scale = kscale * P.attn_scale;
     const int tq = qb * 16 + c16;                  // this lane's query (column)
     const int tqc = tq < ntok ? tq : ntok - 1;     // padding columns repeat the last query
     const int qpos = p0 + tqc;
@@ -2210,7 +2285,7 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
         const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = src[e];
-        split3x8<DT>(qv, qt[s][0], qt[s][1], qt[s][2]);
+        split3x8<KDT>(qv, qt[s][0], qt[s][1], qt[s][2]);
       }
       for (int kb = 32 * wave; kb <= qlast; kb += 32 * kWaves) {
         // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
@@ -2219,22 +2294,21 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NC; ++s) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
-          const u32x4 kb4 = *reinterpret_cast<const u32x4*>(kc + (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
-          s0 = mfma16<DT>(ka, qt[s][2], s0);
-          s1 = mfma16<DT>(kb4, qt[s][2], s1);
-          s0 = mfma16<DT>(ka, qt[s][1], s0);
-          s1 = mfma16<DT>(kb4, qt[s][1], s1);
-          s0 = mfma16<DT>(ka, qt[s][0], s0);
-          s1 = mfma16<DT>(kb4, qt[s][0], s1);
+          const u32x4 ka = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
+          const u32x4 kb4 = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
+          s0 = mfma16<KDT>(ka, qt[s][2], s0);
+          s1 = mfma16<KDT>(kb4, qt[s][2], s1);
+          s0 = mfma16<KDT>(ka, qt[s][1], s0);
+          s1 = mfma16<KDT>(kb4, qt[s][1], s1);
+          s0 = mfma16<KDT>(ka, qt[s][0], s0);
+          s1 = mfma16<KDT>(kb4, qt[s][0], s1);
         }
         const int pv = kb + 8 * kg;  // this lane's 8 positions
         u32x4 vt[NT];
         const int nv = pend - pv;  // positions of this lane's group that are written (others: zero V)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          vt[tt] = *reinterpret_cast<const u32x4*>(
-              vc + ((hb * (P.seqcap / 32) + kb / 32) * HD + 16 * tt + c16) * 32 + 8 * kg);
+          vt[tt] = pf_kv8<KVDT>(P.vc, ((hb * (P.seqcap / 32) + kb / 32) * HD + 16 * tt + c16) * 32 + 8 * kg);
           if (nv < 8) vt[tt] = keep_first(vt[tt], nv < 0 ? 0 : nv);
         }
         float sc8[8];
@@ -2261,12 +2335,12 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
           for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
         m = mn;
         u32x4 p0t, p1t, p2t;
-        split3x8<DT>(sc8, p0t, p1t, p2t);
+        split3x8<KDT>(sc8, p0t, p1t, p2t);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          acc[tt] = mfma16<DT>(vt[tt], p2t, acc[tt]);
-          acc[tt] = mfma16<DT>(vt[tt], p1t, acc[tt]);
-          acc[tt] = mfma16<DT>(vt[tt], p0t, acc[tt]);
+          acc[tt] = mfma16<KDT>(vt[tt], p2t, acc[tt]);
+          acc[tt] = mfma16<KDT>(vt[tt], p1t, acc[tt]);
+          acc[tt] = mfma16<KDT>(vt[tt], p0t, acc[tt]);
         }
       }
     }
@@ -2294,7 +2368,7 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
         num = fmaf(r[d], f, num);
         den = fmaf(r[HD + 1], f, den);
       }
-      put_terms<DT>(A.bo, oplane, (int64_t)t * qd + j * HD + d, num / den);
+      put_terms<ODT, ONT>(A.bo, oplane, (int64_t)t * qd + j * HD + d, num / den * vscale);
     }
     __syncthreads();
   }
@@ -2302,22 +2376,40 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
 
 template <int WDT, int KVDT>
 __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, PrefillArgs A) {
-  extern __shared__ float lds_pf[];  // the attention's wave records
-  static_assert(WDT == KVDT && (WDT == WF16 || WDT == WBF16), "batched prefill: 16-bit weights and cache");
-  constexpr int DT = WDT;
-  const int H = P.H, qd = P.qdim, F = P.F, hd = P.hd, half = P.hd / 2, chunk = A.chunk;
+  extern __shared__ float lds_pf[];  // the attention's wave records, or the GEMM's weight blocks
+  using F = PfFmt<WDT>;
+  constexpr int ADT = F::ADT, NT = F::NTERM, EDT = WFmt<WDT>::EDT;
+  using ST = typename WFmt<WDT>::ST;
+  const int H = P.H, qd = P.qdim, F_ = P.F, hd = P.hd, half = P.hd / 2, chunk = A.chunk;
   const int qrows = P.qdim, krows = P.nkv * P.hd;
-  // one wave per token (RMSNorm) or per attention task, spread over every wave of the grid
+  // one wave per token (RMSNorm) spread over every wave of the grid
   const int gw = (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x, nw = kWaves * (int)gridDim.x;
   uint32_t nbar = 0;
   for (int p0 = 0; p0 < A.n; p0 += chunk) {
     const int ntok = A.n - p0 < chunk ? A.n - p0 : chunk;
-    pf_rmsnorm<DT, WDT>(P, A, A.x, A.tokens + p0, P.gains, ntok, gw, nw);
+    pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, A.tokens + p0, P.gains, ntok, gw, nw);
     pf_barrier(P, A.bar, ++nbar);
     for (int l = 0; l < P.L; ++l) {
       const uint8_t* Wl = P.wbase + (int64_t)l * P.layer_bytes;
+      // scale of (packed) row r, 128-column group g of each linear tensor (unscaled formats: unused)
+      const int nbh = (H + 127) / 128, nbq = (qd + 127) / 128, nbf = (F_ + 127) / 128;
+      const ST* const sq = scale_rows<WDT>(P, l, 0);
+      const ST* const sk = scale_rows<WDT>(P, l, 1);
+      const ST* const sv = scale_rows<WDT>(P, l, 2);
+      auto s_qkv = [&](int r, int g) -> float {
+        if constexpr (!F::SCALED) return 1.f;
+        else {
+          const ST* base;
+          int orow;
+          if (r < qrows) { base = sq; orow = r; }
+          else if (r < qrows + krows) { base = sk; orow = r - qrows; }
+          else { base = sv; orow = r - qrows - krows; }
+          const int head = orow / hd, pr = orow % hd;
+          return scale_value<WDT>(scale_row<WDT>(base, head * hd + (pr >> 1) + (pr & 1) * half, nbh)[g]);
+        }
+      };
       // QKV: rows 2m, 2m + 1 are a RoPE pair (q, k) or two v dims; q to A.q, k and v to the cache
-      pf_gemm<DT, 128>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
+      pf_gemm<WDT, 128>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, lds_pf, s_qkv, [&](int r4, int t, f32x4 v) {
         if (t >= ntok || r4 >= P.qkv_rows) return;
         const int pos = p0 + t;
 #pragma unroll
@@ -2346,17 +2438,32 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
           const int64_t ia = sec == 1 ? (hb * P.seqcap + pos) * hd + i
                                       : ((hb * (P.seqcap / 32) + pos / 32) * hd + i) * 32 + pos % 32;
           const int64_t ib = sec == 1 ? ia + half : ia + (int64_t)half * 32;
-          uint16_t* c16 = reinterpret_cast<uint16_t*>(sec == 1 ? P.kc : P.vc);
-          c16[ia] = enc16<KVDT>(a);
-          c16[ib] = enc16<KVDT>(b);
+          if constexpr (KVDT == WFP8) {
+            if (A.calib)
+              __hip_atomic_fetch_max(&P.kv_amax[hb * 2 + (sec - 1)], __float_as_uint(fmaxf(fabsf(a), fabsf(b))),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float s8 = P.kv_scale[hb * 2 + (sec - 1)];
+            uint8_t* c8 = sec == 1 ? P.kc : P.vc;
+            c8[ia] = enc_e4m3(a / s8);
+            c8[ib] = enc_e4m3(b / s8);
+          } else {
+            uint16_t* c16 = reinterpret_cast<uint16_t*>(sec == 1 ? P.kc : P.vc);
+            c16[ia] = enc16<KVDT>(a);
+            c16[ib] = enc16<KVDT>(b);
+          }
         }
       });
       pf_barrier(P, A.bar, ++nbar);
-      if (hd == 128) pf_attn<DT, 128>(P, A, l, p0, ntok, lds_pf);
-      else pf_attn<DT, 64>(P, A, l, p0, ntok, lds_pf);
+      if (hd == 128) pf_attn<KVDT, ADT, NT, 128>(P, A, l, p0, ntok, lds_pf);
+      else pf_attn<KVDT, ADT, NT, 64>(P, A, l, p0, ntok, lds_pf);
       pf_barrier(P, A.bar, ++nbar);
       // O projection + residual
-      pf_gemm<DT, 128>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
+      const ST* const so = scale_rows<WDT>(P, l, 3);
+      auto s_o = [&](int r, int g) -> float {
+        if constexpr (!F::SCALED) return 1.f;
+        else return scale_value<WDT>(scale_row<WDT>(so, r, nbq)[g]);
+      };
+      pf_gemm<WDT, 128>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, lds_pf, s_o, [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -2365,23 +2472,36 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         }
       });
       pf_barrier(P, A.bar, ++nbar);
-      pf_rmsnorm<DT, WDT>(P, A, A.xm, nullptr, P.gains + (int64_t)l * 2 * H + H, ntok, gw, nw);
+      pf_rmsnorm<ADT, NT, EDT>(P, A, A.xm, nullptr, P.gains + (int64_t)l * 2 * H + H, ntok, gw, nw);
       pf_barrier(P, A.bar, ++nbar);
       // gate/up (interleaved rows 2n, 2n + 1) + SwiGLU
-      const int64_t hplane = (int64_t)chunk * F;
-      pf_gemm<DT, 256>(Wl + P.off_gu, 2 * F, H, A.bn, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
+      const int64_t hplane = (int64_t)chunk * F_;
+      const ST* const sg = scale_rows<WDT>(P, l, 4);
+      const ST* const su = scale_rows<WDT>(P, l, 5);
+      auto s_gu = [&](int r, int g) -> float {
+        if constexpr (!F::SCALED) return 1.f;
+        else return scale_value<WDT>(scale_row<WDT>((r & 1) ? su : sg, r >> 1, nbh)[g]);
+      };
+      // 256-row tiles (128 where the per-group accumulators of a scaled format would not fit)
+      pf_gemm<WDT, F::SCALED ? 128 : 256>(Wl + P.off_gu, 2 * F_, H, A.bn, chunk, ntok, lds_pf, s_gu,
+                                          [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int n = (r4 >> 1) + pp;
-          if (n >= F) continue;
+          if (n >= F_) continue;
           const float gte = v[2 * pp], up = v[2 * pp + 1];
-          put_terms<DT>(A.bh, hplane, (int64_t)t * F + n, gte / (1.0f + expf(-gte)) * up);
+          put_terms<ADT, NT>(A.bh, hplane, (int64_t)t * F_ + n, gte / (1.0f + expf(-gte)) * up);
         }
       });
       pf_barrier(P, A.bar, ++nbar);
       // down projection + residual
-      pf_gemm<DT, 128>(Wl + P.off_d, H, F, A.bh, chunk, ntok, lds_pf, [&](int r4, int t, f32x4 v) {
+      const ST* const sd = scale_rows<WDT>(P, l, 6);
+      auto s_d = [&](int r, int g) -> float {
+        if constexpr (!F::SCALED) return 1.f;
+        else return scale_value<WDT>(scale_row<WDT>(sd, r, nbf)[g]);
+      };
+      pf_gemm<WDT, 128>(Wl + P.off_d, H, F_, A.bh, chunk, ntok, lds_pf, s_d, [&](int r4, int t, f32x4 v) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -2391,7 +2511,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
       });
       pf_barrier(P, A.bar, ++nbar);
       if (l + 1 < P.L) {
-        pf_rmsnorm<DT, WDT>(P, A, A.x, nullptr, P.gains + (int64_t)(l + 1) * 2 * H, ntok, gw, nw);
+        pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, nullptr, P.gains + (int64_t)(l + 1) * 2 * H, ntok, gw, nw);
         pf_barrier(P, A.bar, ++nbar);
       }
     }
@@ -2575,10 +2695,13 @@ const void* persistent_kernel(int wdt, int kvdt) {
   return nullptr;
 }
 
-// batched prefill kernel for 16-bit weights and cache, nullptr where the format has none
+// batched prefill kernel of a (weight, KV) format pair
 const void* prefill_kernel(int wdt, int kvdt) {
   if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_prefill_batch<WF16, WF16>;
   if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_prefill_batch<WBF16, WBF16>;
+  if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_prefill_batch<WFP8, WFP8>;
+  if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_prefill_batch<WI8, WBF16>;
+  if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_prefill_batch<WI4, WBF16>;
   return nullptr;
 }
 

@@ -565,16 +565,14 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   }
   c->n_cus = n_cus;
   {
-    // batched prefill: 16-bit weights and cache only
+    // batched prefill: tokens per chunk
     const int ch = c->sc.prefill_chunk;
     if (ch < -1 || (ch > 0 && (ch % 128 != 0 || ch > 1024))) {
       delete c;
       return fail(nullptr, PMK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or a multiple of 128 up to 1024");
     }
-    const bool fmt16 = (c->m.wdt == PMK_DT_F16 && c->m.kvdt == PMK_DT_F16) ||
-                       (c->m.wdt == PMK_DT_BF16 && c->m.kvdt == PMK_DT_BF16);
     const int cap = (c->m.max_seq + 127) / 128 * 128;
-    c->pf_chunk = !fmt16 || ch == -1 ? 0 : std::min(ch == 0 ? 512 : ch, cap);
+    c->pf_chunk = ch == -1 ? 0 : std::min(ch == 0 ? 512 : ch, cap);
   }
   std::string e = build_schedule(c->m, c->sc, n_cus, &c->sched);
   if (!e.empty()) { delete c; return fail(nullptr, PMK_ERR_SCHEDULE_INVALID, e); }
@@ -771,20 +769,10 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
   if (!d_tokens || P <= 0) return fail(c, PMK_ERR_INVALID_ARG, "prefill needs P > 0 device tokens");
   if (P > c->m.max_seq) return fail(c, PMK_ERR_CAPACITY, "prompt longer than max_seq");
   hipStream_t st = (hipStream_t)stream;
-  if (c->m.kvdt == PMK_DT_FP8_E4M3 && !d_kv_scales) {
-    // static scales from this prompt: a calibration pass with every scale 1 records max |k|, |v|
-    // per (layer, kv head); each scale becomes that maximum / 448; then the real prefill
-    HIPCHK(c, launch_kv_calib(c->kp, 0, st));
-    s = run_prefill(c, d_tokens, P, 1, st);
-    if (s != PMK_OK) return s;
-    HIPCHK(c, launch_kv_calib(c->kp, 1, st));
-  } else {
-    s = set_kv_scales(c, d_kv_scales, st);
-    if (s != PMK_OK) return s;
-  }
-  if (c->pf_chunk > 0 && P >= 2) {
-    // positions 0..P-2 in one launch of the batched prefill, then the last position as a
-    // teacher-forced decode step (its logits give the first token)
+  // one prefill pass: batched (positions 0..P-2 in one launch, then the last position as a
+  // teacher-forced decode step, whose logits give the first token) or step by step
+  auto pass = [&](int calib) -> pmk_status {
+    if (c->pf_chunk <= 0 || P < 2) return run_prefill(c, d_tokens, P, calib, st);
     PrefillArgs a{};
     a.tokens = d_tokens;
     a.n = P - 1;
@@ -796,6 +784,7 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     a.bo = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbo);
     a.bh = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbh);
     a.bar = reinterpret_cast<uint32_t*>(c->ws + c->w_pfbar);
+    a.calib = calib;
     HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P - 1, 0, d_tokens + P - 1, st));
     HIPCHK(c, hipMemsetAsync(a.bar, 0, (size_t)c->n_cus * 4, st));
     void* args[] = {&c->kp, &a};
@@ -805,11 +794,23 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     cp.forced = d_tokens + P - 1;
     cp.n_steps = 1;
     cp.eos = -1;
-    s = begin_call(c, cp, st);
-    if (s == PMK_OK) s = run_steps(c, 1, st);
+    cp.calib = calib;
+    pmk_status r = begin_call(c, cp, st);
+    if (r == PMK_OK) r = run_steps(c, 1, st);
+    return r;
+  };
+  if (c->m.kvdt == PMK_DT_FP8_E4M3 && !d_kv_scales) {
+    // static scales from this prompt: a calibration pass with every scale 1 records max |k|, |v|
+    // per (layer, kv head); each scale becomes that maximum / 448; then the real prefill
+    HIPCHK(c, launch_kv_calib(c->kp, 0, st));
+    s = pass(1);
+    if (s != PMK_OK) return s;
+    HIPCHK(c, launch_kv_calib(c->kp, 1, st));
   } else {
-    s = run_prefill(c, d_tokens, P, 0, st);
+    s = set_kv_scales(c, d_kv_scales, st);
+    if (s != PMK_OK) return s;
   }
+  s = pass(0);
   if (s != PMK_OK) return s;
   if (d_first_token) HIPCHK(c, launch_copy_token(c->kp, d_first_token, st));
   c->pos_host = P;

@@ -41,7 +41,7 @@ struct CallParams {
   int32_t calib;  // FP8 KV: record max |k|, |v| per (layer, kv head) while the steps run (scale calibration)
 };
 
-// Batched prefill (16-bit weights and KV cache): chunk buffers in the workspace.
+// Batched prefill: chunk buffers in the workspace.
 struct PrefillArgs {
   const int32_t* tokens;  // prompt tokens (device)
   int32_t n;              // positions 0..n-1 go through the batched path
@@ -49,10 +49,12 @@ struct PrefillArgs {
   float* x;               // [chunk][H] residual stream
   float* xm;              // [chunk][H] residual after attention
   float* q;               // [chunk][qdim] queries after RoPE
-  uint16_t* bn;           // [3][chunk][H] normalised activations as three 16-bit terms
-  uint16_t* bo;           // [3][chunk][qdim] attention output as three terms
-  uint16_t* bh;           // [3][chunk][F] SwiGLU output as three terms
+  uint16_t* bn;           // [terms][chunk][H] normalised activations (three 16-bit terms, or the
+                          // one binary16 value of the integer formats)
+  uint16_t* bo;           // [terms][chunk][qdim] attention output
+  uint16_t* bh;           // [terms][chunk][F] SwiGLU output
   uint32_t* bar;          // grid barrier: one flag word per workgroup (zero at launch)
+  int32_t calib;          // FP8 KV scale calibration: record max |k|, |v| of every appended row
 };
 
 struct KParams {

@@ -272,8 +272,17 @@ def test_split_combines_match_oracle_and_modes():
         assert np.array_equal(r.logits, runs["megakernel"].logits), name
 
 
-@pytest.mark.parametrize("wdtype", ["f16", "bf16"])
-def test_batched_prefill_rows_against_the_oracle(wdtype):
+_PREFILL_FORMATS = {
+    "f16": dict(wdtype="f16", kvdtype="f16"),
+    "bf16": dict(wdtype="bf16", kvdtype="bf16"),
+    "fp8": dict(wdtype="fp8", kvdtype="fp8", n_q=4, n_kv=2, head_dim=128, hidden=512, ffn=1024),
+    "int8": dict(wdtype="int8", kvdtype="bf16", ffn=672),
+    "int4": dict(wdtype="int4", kvdtype="bf16", ffn=672),
+}
+
+
+@pytest.mark.parametrize("fmt", list(_PREFILL_FORMATS))
+def test_batched_prefill_rows_against_the_oracle(fmt):
     """The batched prefill (chunks of 128 positions: three chunks over a 300-token prompt, the last
     one ragged; matrix-core GEMMs and causal attention in one launch), checked position by position:
     the oracle takes the GPU's cache rows of the earlier positions and appends the GPU's row of the
@@ -281,19 +290,24 @@ def test_batched_prefill_rows_against_the_oracle(wdtype):
     one rounding of the GPU's.  Then the first token (gap rule) and the decode that follows against
     the oracle.  The step-by-step prefill of the same prompt (prefill_chunk = -1) is reported beside
     it: its rows drift apart from the batched ones across positions, as any two correct
-    implementations' do, since each position attends to rows rounded to the cache format."""
+    implementations' do, since each position attends to rows rounded to the cache format.  Integer
+    formats round every GEMM operand to binary16, where two correct implementations differ by whole
+    binary16 steps in some elements (the format's tolerance note): their rows are reported, and the
+    first token and the logits are checked."""
     import torch
     import oracle
     import persistent_megakernel_02_amd as pmk
     from tests.parity import _token_ok
-    w = TINY.with_(name=f"tiny_prefill_{wdtype}", wdtype=wdtype, kvdtype=wdtype, prompt=300, steps=8)
+    w = TINY.with_(name=f"tiny_prefill_{fmt}", prompt=300, steps=8, **_PREFILL_FORMATS[fmt])
     wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
     prompt = synthgen.make_prompt(w)
+    scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32) if w.kvdtype == "fp8" else None
     out = {}
     for name, chunk in (("batched", 128), ("stepwise", -1)):
         dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(prefill_chunk=chunk))
         dec.load_weights(pmk.DeviceWeights(wts))
-        first = int(dec.prefill(torch.from_numpy(prompt).cuda()).item())
+        ks = torch.from_numpy(scales).cuda() if scales is not None else None
+        first = int(dec.prefill(torch.from_numpy(prompt).cuda(), ks).item())
         torch.cuda.synchronize()
         assert dec.poll_error().code == 0
         k, v = (t.cpu().numpy() for t in dec.read_kv(w.prompt))
@@ -301,24 +315,61 @@ def test_batched_prefill_rows_against_the_oracle(wdtype):
         dec.close()
     first, gk, gv = out["batched"]
     om = oracle.OracleModel(wts, max_seq=w.max_seq)
+    if scales is not None:
+        om.set_kv_scales(scales)
     worst, differ = 0.0, []
     for p in range(w.prompt):
         om.load_kv(gk[:, :, :p], gv[:, :, :p], p)
         _, olg, own_k, own_v = om.step_forced(int(prompt[p]), gk[:, :, p], gv[:, :, p])
         for g_row, o_row in ((gk[:, :, p], own_k), (gv[:, :, p], own_v)):
-            ex, fr = _kv_excess(g_row, o_row, wdtype)
+            ex, fr = _kv_excess(g_row, o_row, w.kvdtype)
             worst = max(worst, float(ex.max()))
             differ.append(fr)
     _, sk, sv = out["stepwise"]
-    sdiff = np.mean([_kv_excess(a, b, wdtype)[1] for a, b in ((gk, sk), (gv, sv))])
+    sdiff = np.mean([_kv_excess(a, b, w.kvdtype)[1] for a, b in ((gk, sk), (gv, sv))])
     log(f"{w.name}: batched prefill rows against the oracle: {100 * np.mean(differ):.3f}% of codes differ, the "
         f"largest difference is {worst:.3f} of one rounding; against the step-by-step prefill "
         f"{100 * sdiff:.2f}% differ; first tokens {first} / {out['stepwise'][0]}")
+    if fmt not in ("int8", "int4"):
+        assert worst <= 1.0 and np.mean(differ) <= 0.02
+    assert _token_ok(olg, first)
+    run = gpu_run(w, wts, w.steps, prompt=prompt, kv_scales=scales, sched=pmk.schedule_config(prefill_chunk=128))
+    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt, kv_scales=scales)
+    check(w, run, ref, first_ok, f"{w.name}/batched prefill")
+
+
+@pytest.mark.parametrize("P", [1, 2, 129, 257])
+def test_batched_prefill_edge_lengths(P):
+    """Prompt lengths at the batched prefill's edges (chunks of 128 positions): one token (no batched
+    part), two (a one-token chunk), 129 and 257 (the batched positions fill whole chunks and the
+    last position runs as a decode step): every position's rows against the oracle with teacher-
+    forced rounding, the first token by the gap rule."""
+    import torch
+    import oracle
+    import persistent_megakernel_02_amd as pmk
+    from tests.parity import _token_ok
+    w = TINY.with_(name=f"tiny_prefill_{P}", prompt=P, steps=4)
+    wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
+    prompt = synthgen.make_prompt(w)
+    dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(prefill_chunk=128))
+    dec.load_weights(pmk.DeviceWeights(wts))
+    first = int(dec.prefill(torch.from_numpy(prompt).cuda()).item())
+    torch.cuda.synchronize()
+    assert dec.poll_error().code == 0
+    gk, gv = (t.cpu().numpy() for t in dec.read_kv(P))
+    dec.close()
+    om = oracle.OracleModel(wts, max_seq=w.max_seq)
+    worst, differ = 0.0, []
+    for p in range(P):
+        om.load_kv(gk[:, :, :p], gv[:, :, :p], p)
+        _, olg, own_k, own_v = om.step_forced(int(prompt[p]), gk[:, :, p], gv[:, :, p])
+        for g_row, o_row in ((gk[:, :, p], own_k), (gv[:, :, p], own_v)):
+            ex, fr = _kv_excess(g_row, o_row, w.kvdtype)
+            worst = max(worst, float(ex.max()))
+            differ.append(fr)
+    log(f"{w.name}: {100 * np.mean(differ):.3f}% of codes differ, the largest difference is {worst:.3f} of one rounding")
     assert worst <= 1.0 and np.mean(differ) <= 0.02
     assert _token_ok(olg, first)
-    run = gpu_run(w, wts, w.steps, prompt=prompt, sched=pmk.schedule_config(prefill_chunk=128))
-    ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt)
-    check(w, run, ref, first_ok, f"{w.name}/batched prefill")
 
 
 def _check_derived_scales(got, want):
