@@ -1956,62 +1956,70 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 // ------------------------------------------------------------------------------------------------
 // Batched prefill.  The prompt's positions go through the model in chunks of up to `chunk`
 // tokens; each layer of a chunk is a sequence of grid-wide phases of ONE cooperative launch:
-// RMSNorm (one wave per token), the QKV GEMM with RoPE and the KV append in its epilogue, causal
+// RMSNorm (four waves per token), the QKV GEMM with RoPE and the KV append in its epilogue, causal
 // attention, the O GEMM + residual, RMSNorm, the gate/up GEMM + SwiGLU, the down GEMM + residual.
 // The GEMMs are dense contractions over the chunk's tokens and run on the matrix cores
 // (v_mfma_f32_16x16x32): the weights are the A operand, converted exactly to a 16-bit format where
 // they are not one (FP8 -> bf16, int8 / int4 codes -> binary16) and scaled per 128-column group
 // after the products (FP8 block scales, integer group scales); the activations are the B operand,
-// as three 16-bit terms (x = t0 + t1 + t2 to ~2^-24, each product accumulated in fp32: fp32
-// accuracy in another rounding order) or, for the integer formats, as the one binary16 value the
-// format defines.  A phase reads only what earlier phases wrote; phases are separated by a grid
+// as two 16-bit terms (x = t0 + t1 to within 2^-18 |x| for bf16 terms, 2^-22 for binary16; each
+// product accumulated in fp32: about the rounding an fp32 dot product of a few thousand terms
+// accumulates anyway) or, for the integer formats, as the one binary16 value the format defines.  A phase reads only what earlier phases wrote; phases are separated by a grid
 // barrier, so there is no schedule to validate.
 // ------------------------------------------------------------------------------------------------
 constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
+// 16-bit terms of an fp32 activation operand (GEMM inputs, attention q and probabilities) for the
+// 16-bit and FP8 weight formats
+constexpr int kPfTerms = 2;
+
+// Element (t, k) of an activation plane of K columns (the GEMMs' B operand): 16-token blocks of
+// 8-column groups of 16 tokens x 8 columns, so that a wave's operand load of one step (16 tokens x
+// 32 columns) is one contiguous KiB
+__device__ __forceinline__ int64_t pf_b_index(int t, int k, int K) {
+  return ((((int64_t)(t >> 4) * (K >> 3)) + (k >> 3)) << 7) + ((t & 15) << 3) + (k & 7);
+}
 
 template <int WDT>
 struct PfFmt {
   static constexpr bool INT = weight_is_int(WDT);
   static constexpr int ADT = WDT == WF16 || INT ? WF16 : WBF16;  // matrix-core operand format
-  static constexpr int NTERM = INT ? 1 : 3;                       // activation terms
+  static constexpr int NTERM = INT ? 1 : kPfTerms;                // activation terms
   static constexpr bool SCALED = WDT >= WFP8;
 };
 
-// fp32 x[8] -> three 16-bit terms of format DT per element (nearest even at each step)
-template <int DT>
-__device__ __forceinline__ void split3x8(const float* x, u32x4& t0, u32x4& t1, u32x4& t2) {
-  uint32_t a[4], b[4], c[4];
+// fp32 x[8] -> NT 16-bit terms of format DT per element (nearest even at each step): term 0 is x
+// rounded, term 1 the rounded remainder
+template <int DT, int NT>
+__device__ __forceinline__ void split_terms8(const float* x, u32x4 (&t)[NT]) {
+  uint32_t w[NT][4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint16_t h[2], m[2], o[2];
+    uint16_t h[NT][2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float v = x[2 * k + e];
-      h[e] = enc16<DT>(v);
-      const float r = v - dec16<DT>(h[e]);
-      m[e] = enc16<DT>(r);
-      o[e] = enc16<DT>(r - dec16<DT>(m[e]));
+      float r = x[2 * k + e];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        h[n][e] = enc16<DT>(r);
+        if (n + 1 < NT) r -= dec16<DT>(h[n][e]);
+      }
     }
-    a[k] = h[0] | ((uint32_t)h[1] << 16);
-    b[k] = m[0] | ((uint32_t)m[1] << 16);
-    c[k] = o[0] | ((uint32_t)o[1] << 16);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) w[n][k] = h[n][0] | ((uint32_t)h[n][1] << 16);
   }
-  t0 = u32x4{a[0], a[1], a[2], a[3]};
-  t1 = u32x4{b[0], b[1], b[2], b[3]};
-  t2 = u32x4{c[0], c[1], c[2], c[3]};
+#pragma unroll
+  for (int n = 0; n < NT; ++n) t[n] = u32x4{w[n][0], w[n][1], w[n][2], w[n][3]};
 }
 
 // Store v as NT 16-bit terms of format DT at element idx of NT planes `plane` elements apart (one
 // term: v rounded to DT, the binary16 activation of the integer formats).
 template <int DT, int NT>
 __device__ __forceinline__ void put_terms(uint16_t* planes, int64_t plane, int64_t idx, float v) {
-  const uint16_t h = enc16<DT>(v);
-  planes[idx] = h;
-  if constexpr (NT == 3) {
-    const float r = v - dec16<DT>(h);
-    const uint16_t m = enc16<DT>(r);
-    planes[plane + idx] = m;
-    planes[2 * plane + idx] = enc16<DT>(r - dec16<DT>(m));
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint16_t h = enc16<DT>(v);
+    planes[n * plane + idx] = h;
+    if (n + 1 < NT) v -= dec16<DT>(h);
   }
 }
 
@@ -2051,34 +2059,57 @@ __device__ __forceinline__ void pf_barrier(const KParams& P, uint32_t* bar, uint
 // written to src first) into the activation planes bn: (x * r) * g with r = 1 / sqrt(mean(x^2) +
 // eps), as NT terms of format DT.  One wave per token.
 template <int DT, int NT, int EDT>
-__device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& A, float* src, const int32_t* emb_tok,
-                                           const float* gain, int ntok, int gw, int nw) {
-  const int lane = threadIdx.x & 63, H = P.H;
+__device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& A, float* src, const float* add,
+                                           const int32_t* emb_tok, const float* gain, int ntok, float* red) {
+  // four waves per token (a quarter of the columns each; their sums of squares meet in LDS), two
+  // tokens per workgroup and round
+  constexpr int WPT = 4, TPR = kWaves / WPT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = wave % WPT, H = P.H, Hq = H / WPT;
   const int64_t plane = (int64_t)A.chunk * H;
-  for (int t = gw; t < ntok; t += nw) {
+  for (int t0 = (int)blockIdx.x * TPR; t0 < ntok; t0 += (int)gridDim.x * TPR) {
+    const int t = t0 + wave / WPT;
+    const bool ok = t < ntok;
     float* x = src + (int64_t)t * H;
-    if (emb_tok) {
-      int tok = emb_tok[t];
-      tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
-      const uint16_t* e = P.embed + (int64_t)tok * H;
-      for (int k = 2 * lane; k < H; k += 128) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(e + k);
-        *reinterpret_cast<float2*>(x + k) = make_float2(dec16<EDT>((uint16_t)(w & 0xffffu)), dec16<EDT>((uint16_t)(w >> 16)));
+    // a projection computed in two K-halves: the residual stream is the sum of both planes (stored
+    // back, for the residual the next GEMM's epilogue adds)
+    const float* x2 = add ? add + (int64_t)t * H : nullptr;
+    float ss = 0.f;
+    if (ok) {
+      if (emb_tok) {
+        int tok = emb_tok[t];
+        tok = tok < 0 ? 0 : (tok >= P.V ? P.V - 1 : tok);
+        const uint16_t* e = P.embed + (int64_t)tok * H;
+        for (int k = sub * Hq + 2 * lane; k < (sub + 1) * Hq; k += 128) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(e + k);
+          *reinterpret_cast<float2*>(x + k) = make_float2(dec16<EDT>((uint16_t)(w & 0xffffu)),
+                                                          dec16<EDT>((uint16_t)(w >> 16)));
+        }
+      }
+      for (int k = sub * Hq + 2 * lane; k < (sub + 1) * Hq; k += 128) {
+        float2 v = *reinterpret_cast<const float2*>(x + k);
+        if (x2) {
+          const float2 u = *reinterpret_cast<const float2*>(x2 + k);
+          v = make_float2(v.x + u.x, v.y + u.y);
+          *reinterpret_cast<float2*>(x + k) = v;
+        }
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
       }
     }
-    float ss = 0.f;
-    for (int k = 2 * lane; k < H; k += 128) {
-      const float2 v = *reinterpret_cast<const float2*>(x + k);
-      ss = fmaf(v.x, v.x, ss);
-      ss = fmaf(v.y, v.y, ss);
-    }
     ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)H + P.eps);
-    for (int k = 2 * lane; k < H; k += 128) {
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) tot += red[(wave / WPT) * WPT + q];
+    __syncthreads();  // red is written again in the next round
+    if (!ok) continue;
+    const float r = 1.0f / sqrtf(tot / (float)H + P.eps);
+    for (int k = sub * Hq + 2 * lane; k < (sub + 1) * Hq; k += 128) {
       const float2 v = *reinterpret_cast<const float2*>(x + k);
       const float2 g = *reinterpret_cast<const float2*>(gain + k);
-      put_terms<DT, NT>(A.bn, plane, (int64_t)t * H + k, (v.x * r) * g.x);
-      put_terms<DT, NT>(A.bn, plane, (int64_t)t * H + k + 1, (v.y * r) * g.y);
+      put_terms<DT, NT>(A.bn, plane, pf_b_index(t, k, H), (v.x * r) * g.x);
+      put_terms<DT, NT>(A.bn, plane, pf_b_index(t, k + 1, H), (v.y * r) * g.y);
     }
   }
 }
@@ -2086,21 +2117,46 @@ __device__ __forceinline__ void pf_rmsnorm(const KParams& P, const PrefillArgs& 
 // 8 columns of one weight row as 8 exact 16-bit matrix-core operands (format PfFmt::ADT), from
 // their bytes in the arena: 16-bit formats as stored; FP8 E4M3 to bf16; int8 / int4 codes (offset
 // binary, int4 nibbles of the word in the order 0 2 4 6 1 3 5 7) to binary16.
+// A weight piece of 8 columns as loaded (16 B of a 16-bit format, 8 B of FP8 or int8, 4 B of
+// int4), and its conversion to eight 16-bit matrix-core operands (done when the piece is stored to
+// LDS, so a load in flight holds only the raw bytes)
 template <int WDT>
-__device__ __forceinline__ u32x4 pf_load_a8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+struct PfRaw {
+  using T = u32x4;
+};
+template <>
+struct PfRaw<WFP8> {
+  using T = u32x2;
+};
+template <>
+struct PfRaw<WI8> {
+  using T = u32x2;
+};
+template <>
+struct PfRaw<WI4> {
+  using T = uint32_t;
+};
+
+template <int WDT>
+__device__ __forceinline__ typename PfRaw<WDT>::T pf_load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (WDT == WF16 || WDT == WBF16) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  else if constexpr (WDT == WFP8 || WDT == WI8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+template <int WDT>
+__device__ __forceinline__ u32x4 pf_a16(typename PfRaw<WDT>::T w) {
   if constexpr (WDT == WF16 || WDT == WBF16) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return w;
   } else if constexpr (WDT == WFP8) {
-    return fp8x8_bf16(__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return fp8x8_bf16(w);
   } else if constexpr (WDT == WI8) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     const h16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     auto cv = [&](uint32_t v, uint32_t sel) {
       return __builtin_bit_cast(uint32_t, as_h2(__builtin_amdgcn_perm(0x64646464u, v, sel)) + bias);
     };
     return u32x4{cv(w.x, 0x04010400u), cv(w.x, 0x04030402u), cv(w.y, 0x04010400u), cv(w.y, 0x04030402u)};
   } else {
-    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     const h16x2 b1 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h16x2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h16x2 b2 = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -2114,122 +2170,192 @@ __device__ __forceinline__ u32x4 pf_load_a8(__amdgpu_buffer_rsrc_t r, uint32_t o
   }
 }
 
+// Byte offset of the 16-byte piece (row, 8-column group kg) of a step's A block in LDS: rows of 64
+// bytes, the four pieces of a row permuted by row bits 1..3.  The matrix-core operand reads take one
+// kg for 16 consecutive rows of a block, and the stores four kg of consecutive rows: both then fall
+// on distinct banks in every group of 8 (or 16) lanes, where the plain row-major order put four of
+// every eight lanes' reads on the same banks.
+__device__ __forceinline__ uint32_t pf_a_offset(int row, int kg) {
+  return (uint32_t)row * 64u + (uint32_t)((kg ^ ((row >> 1) & 3) ^ ((row >> 3) & 1)) * 16);
+}
+
+// Steps of weight loads in flight ahead of the LDS store (raw pieces in registers; it divides the
+// activation ring's depth): two, one for the scaled formats, whose per-group accumulators leave no
+// registers for more
+template <int WDT>
+constexpr int pf_a_depth() { return WDT >= WFP8 ? 1 : 2; }
+
 // One GEMM tile: rows [row0, row0 + MR) of W ([N][K] in format WDT) against tokens
-// [tok0, tok0 + 128) of the activation planes B ([NTERM][chunk][K]).  Wave w takes tokens
-// tok0 + 16w .. + 15 and all MR / 16 row blocks; per 32-column step the weight block goes through
-// LDS once for the workgroup (converted to 16-bit operands on the way), each lane reads its
-// token's terms (a 4-step register ring) and issues NTERM MR / 16 matrix-core products.  Scaled
-// formats accumulate each 128-column group apart and add it times scale(row, group).
-// epi(r, t, v) receives rows r .. r + 3 (r = row0 + 16 b + 4 (lane / 16)) of token
-// t = tok0 + 16 w + lane % 16 (rows past N are garbage the epilogues skip).
+// [tok0, tok0 + 128) of the activation planes B ([NTERM] planes of chunk x K, layout pf_b_index),
+// over the 32-column steps [step0, step1).  Wave w takes tile rows (w / 4) MR / 2 .. + MR / 2 - 1
+// and tokens tok0 + 32 (w % 4) .. + 31 (two 16-token column blocks): per step it reads MR / 2 rows
+// of the weight block from LDS (half of what a wave taking all rows would) and its tokens' terms
+// from global memory (a 4-step register ring).  The weight block of a step goes through LDS once
+// for the workgroup (converted to 16-bit operands on the way, three buffers) and each wave reads its
+// operands of the next step while its matrix-core products of this step run.  Scaled formats
+// accumulate each 128-column group apart and add it times scale(row, group).
+// epi(r, t, v, ks) receives rows r .. r + 3 (r = a 16-row block's first row + 4 (lane / 16)) of token
+// t (its 16-token block's first token + lane % 16); rows past N are garbage the epilogues skip.
 template <int WDT, int MR, class ScaleF, class Epi>
 __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int row0,
-                                             int tok0, float* lds, ScaleF scale, Epi epi) {
+                                             int tok0, int step0, int step1, int ks, float* lds, ScaleF scale,
+                                             Epi epi) {
   using F = PfFmt<WDT>;
-  constexpr int RB = MR / 16;                   // 16-row blocks per tile
+  constexpr int NT = F::NTERM;
+  constexpr int RB = MR / 32;                   // 16-row blocks per wave
   constexpr int AW = MR >= 128 ? MR / 128 : 1;  // 8-column A pieces per thread per step (MR x 4 pieces)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r16 = lane & 15, kg = lane >> 4;
+  const int wrow = (wave >> 2) * (MR / 2);      // the wave's first tile row
+  const int tb0 = (tok0 >> 4) + 2 * (wave & 3);  // the wave's two 16-token blocks
   const int rows = N - row0 < MR ? N - row0 : MR;
   const int64_t rbytes = weight_row_bytes(WDT, K);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + (int64_t)row0 * rbytes), (short)0, (int)(rows * rbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(B), (short)0, (int)((int64_t)F::NTERM * chunk * K * 2), 0x00020000);
+      const_cast<uint16_t*>(B), (short)0, (int)((int64_t)NT * chunk * K * 2), 0x00020000);
   constexpr uint32_t kOut = 0x7FFFFFF0u;
-  const int tok = tok0 + 16 * wave + r16;
   const uint32_t bplane = (uint32_t)chunk * (uint32_t)K * 2u;
-  const uint32_t bbase = (uint32_t)((int64_t)tok * K * 2);
-  const int nsteps = (K + 31) / 32;
-  // A: the workgroup's MR x 32 block of a step goes through LDS (two buffers of MR x 64 bytes of
-  // 16-bit operands, row-major), each thread loading its pieces one step ahead; piece
-  // p = thread + 512 a -> row p / 4, columns 8 (p % 4) ..
+  const uint32_t bblk = (uint32_t)K * 32u;                 // bytes of a 16-token block
+  const uint32_t bbase = (uint32_t)tb0 * bblk + (uint32_t)r16 * 16u;
+  const int nsteps = step1 - step0, kofs = 32 * step0;  // this tile's columns: [kofs, 32 step1)
+  // A: each thread's pieces of a step are loaded DA steps before they are stored (raw bytes in a
+  // register ring, slot = step % DA), converted on the store two steps ahead of their use; step s
+  // goes to LDS buffer s % 3 (MR x 64 bytes, pf_a_offset), which is read one step ahead of its use,
+  // so the buffer written at a step was last read two barriers earlier.
+  // Piece p = thread + 512 a -> row p / 4, columns 8 (p % 4) ..
+  constexpr int DA = pf_a_depth<WDT>();
+  using RawT = typename PfRaw<WDT>::T;
   uint8_t* abuf = reinterpret_cast<uint8_t*>(lds);
-  u32x4 an[AW];
-  auto load_a = [&](int step) {
+  RawT ar[DA][AW];
+  auto load_a = [&](int slot, int step) {
 #pragma unroll
     for (int a = 0; a < AW; ++a) {
-      const int p = (int)threadIdx.x + kThreads * a, r = p >> 2, k = step * 32 + 8 * (p & 3);
+      const int p = (int)threadIdx.x + kThreads * a, r = p >> 2, k = kofs + step * 32 + 8 * (p & 3);
       const uint32_t off = (uint32_t)(r * rbytes + (int64_t)k * weight_bits(WDT) / 8);
-      an[a] = pf_load_a8<WDT>(wr, k < K && p < MR * 4 ? off : kOut);
+      ar[slot][a] = pf_load_raw<WDT>(wr, k < K && p < MR * 4 ? off : kOut);
     }
   };
-  auto store_a = [&](int step) {
-    uint8_t* dst = abuf + (step & 1) * MR * 64;
+  auto store_a = [&](int slot, int step) {
+    uint8_t* dst = abuf + (step % 3) * MR * 64;
 #pragma unroll
     for (int a = 0; a < AW; ++a) {
       const int p = (int)threadIdx.x + kThreads * a;
-      if (p < MR * 4) *reinterpret_cast<u32x4*>(dst + p * 16) = an[a];
+      if (p < MR * 4) *reinterpret_cast<u32x4*>(dst + pf_a_offset(p >> 2, p & 3)) = pf_a16<WDT>(ar[slot][a]);
     }
   };
-  // B: a ring of D steps of this lane's terms in flight (each slot refilled right after it is
-  // consumed; a step past the end reads zeros without touching memory)
-  constexpr int D = 4;
-  u32x4 rb[D][F::NTERM];
-  auto issue = [&](int d, int step) {
-    const int k = step * 32 + 8 * kg;
-    const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
-    const uint32_t ko = (uint32_t)k * 2u;
+  // the wave's operands of one step: RB 16-row blocks
+  u32x4 ao[2][RB];
+  auto read_a = [&](int buf, int step) {
+    const uint8_t* src = abuf + (step % 3) * MR * 64 + wrow * 64 + pf_a_offset(r16, kg);
 #pragma unroll
-    for (int t = 0; t < F::NTERM; ++t)
-      rb[d][t] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? bbase + ko + (uint32_t)t * bplane : kOut, 0, 0);
+    for (int b = 0; b < RB; ++b) ao[buf][b] = *reinterpret_cast<const u32x4*>(src + b * 16 * 64);
   };
-  load_a(0);
-  store_a(0);
+  // B: a ring of D steps of this lane's terms (two token blocks) in flight; a step past the end
+  // reads zeros without touching memory
+#ifndef PMK_PF_B_DEPTH
+#define PMK_PF_B_DEPTH 2
+#endif
+  constexpr int D = PMK_PF_B_DEPTH;
+  static_assert(D % DA == 0 && D % 2 == 0, "the rings' slots follow the step");
+  u32x4 rb[D][2][NT];
+  auto issue = [&](int d, int step) {
+    const int k = kofs + step * 32 + 8 * kg;
+    const bool ok = k < K;  // K is a multiple of 8: a lane's 8 columns are all in or all out
+    const uint32_t ko = bbase + (uint32_t)(k >> 3) * 256u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        rb[d][c][t] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? ko + (uint32_t)c * bblk + (uint32_t)t * bplane : kOut,
+                                                            0, 0);
+  };
+#pragma unroll
+  for (int s = 0; s < DA; ++s) load_a(s, s);
+  store_a(0, 0);
+  load_a(0, DA);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, d);
-  load_a(1);
+  store_a(1 % DA, 1);
+  load_a(1 % DA, 1 + DA);
   __syncthreads();
-  f32x4 acc[RB], accg[F::SCALED ? RB : 1];
+  read_a(0, 0);
+  f32x4 acc[RB][2], accg[F::SCALED ? RB : 1][2];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < RB; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int b = 0; b < (F::SCALED ? RB : 1); ++b) accg[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < (F::SCALED ? RB : 1); ++b) accg[b][0] = accg[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int step = base + d;
       if (step < nsteps) {
-        const uint8_t* src = abuf + (step & 1) * MR * 64 + r16 * 64 + kg * 16;
+        if (step + 1 < nsteps) read_a((d + 1) & 1, step + 1);
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(src + b * 16 * 64);
-          f32x4& c = F::SCALED ? accg[b] : acc[b];
+        for (int b = 0; b < RB; ++b)
 #pragma unroll
-          for (int t = F::NTERM - 1; t >= 0; --t) c = mfma16<F::ADT>(a, rb[d][t], c);
-        }
+          for (int c = 0; c < 2; ++c) {
+            f32x4& cc = F::SCALED ? accg[b][c] : acc[b][c];
+#pragma unroll
+            for (int t = NT - 1; t >= 0; --t) cc = mfma16<F::ADT>(ao[d & 1][b], rb[d][c][t], cc);
+          }
         if constexpr (F::SCALED) {
-          if ((step & 3) == 3 || step == nsteps - 1) {  // end of a 128-column group
-            const int g = step >> 2;
+          if ((step & 3) == 3 || step == nsteps - 1) {  // end of a 128-column group (step0 % 4 == 0)
+            const int g = (step0 + step) >> 2;
 #pragma unroll
-            for (int b = 0; b < RB; ++b) {
+            for (int b = 0; b < RB; ++b)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[b][i] = fmaf(accg[b][i], scale(row0 + 16 * b + 4 * kg + i, g), acc[b][i]);
-              accg[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+              for (int i = 0; i < 4; ++i) {
+                const float sv = scale(row0 + wrow + 16 * b + 4 * kg + i, g);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                  acc[b][c][i] = fmaf(accg[b][c][i], sv, acc[b][c][i]);
+                  accg[b][c][i] = 0.f;
+                }
+              }
           }
         }
       }
       issue(d, step + D);
-      // the next step's A into the other buffer (read by every wave only after the barrier), then
-      // the loads of the step after it
-      if (step + 1 < nsteps) store_a(step + 1);
-      load_a(step + 2);
+      // step + 2's weights into the buffer read two barriers ago, then their slot refilled with the
+      // loads DA steps after them
+      if (step + 2 < nsteps) store_a((d + 2) % DA, step + 2);
+      load_a((d + 2) % DA, step + 2 + DA);
       __syncthreads();
     }
   }
 #pragma unroll
-  for (int b = 0; b < RB; ++b) epi(row0 + 16 * b + 4 * kg, tok, acc[b]);
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) epi(row0 + wrow + 16 * b + 4 * kg, (tb0 + c) * 16 + r16, acc[b][c], ks);
 }
 
-// Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok), tiles of MR rows spread over
+// K-halves of a GEMM phase: 2 where its tiles would fill at most half the grid and K has at least
+// eight 32-column steps (the halves split at a 128-column group boundary), else 1
+__device__ __forceinline__ int pf_ksplit(int N, int K, int MR, int ntok) {
+  const int tiles = ((N + MR - 1) / MR) * ((ntok + kPfTokens - 1) / kPfTokens);
+  return 2 * tiles <= (int)gridDim.x && (((K + 31) / 32 / 2) & ~3) > 0 ? 2 : 1;
+}
+
+// Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok) x ksplit K-parts (epi gets the
+// part's index: part 1 of two adds its products to a plane of its own), tiles of MR rows spread over
 // the grid.
 template <int WDT, int MR, class ScaleF, class Epi>
 __device__ __forceinline__ void pf_gemm(const uint8_t* W, int N, int K, const uint16_t* B, int chunk, int ntok,
-                                        float* lds, ScaleF scale, Epi epi) {
-  const int nr = (N + MR - 1) / MR, nt = (ntok + kPfTokens - 1) / kPfTokens;
-  for (int ti = blockIdx.x; ti < nr * nt; ti += gridDim.x) {
-    const int row0 = (ti / nt) * MR, tok0 = (ti % nt) * kPfTokens;
-    pf_gemm_tile<WDT, MR>(W, N, K, B, chunk, row0, tok0, lds, scale, epi);
+                                        int ksplit, float* lds, ScaleF scale, Epi epi) {
+  const int nr = (N + MR - 1) / MR, nt = (ntok + kPfTokens - 1) / kPfTokens, total = nr * nt * ksplit;
+  const int ns = (K + 31) / 32, mid = ksplit == 2 ? ((ns / 2) & ~3) : ns;
+  // workgroup b runs on XCD b % 8: each round of G tiles gives XCD x the consecutive tiles
+  // x G / 8 .. (x + 1) G / 8 - 1, so the token tiles of a row block (and K-part) share its weight
+  // reads in one L2
+  const int G = (int)gridDim.x, rounds = (total + G - 1) / G;
+  for (int k = 0; k < rounds; ++k) {
+    const int b = (int)blockIdx.x;
+    const int ti = k * G + ((G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b);
+    if (ti >= total) continue;
+    const int part = ti / (nr * nt), rt = ti % (nr * nt);
+    const int row0 = (rt / nt) * MR, tok0 = (rt % nt) * kPfTokens;
+    pf_gemm_tile<WDT, MR>(W, N, K, B, chunk, row0, tok0, part == 0 ? 0 : mid, part == 0 ? mid : ns, part, lds,
+                          scale, epi);
   }
 }
 
@@ -2245,8 +2371,8 @@ __device__ __forceinline__ u32x4 pf_kv8(const uint8_t* base, int64_t elem) {
 // per (q head j, block of 16 queries); its eight waves split the key positions, wave w taking the
 // 32-position groups w, w + 8, ... up to the block's last query, with the decode attention's
 // matrix-core layout and the 16 queries of the head as the B columns: scores = K rows (A) x q
-// (B, three terms), online softmax per query, P.V = V^T (A, from the blocked V cache) x P (B,
-// three terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
+// (B, two terms), online softmax per query, P.V = V^T (A, from the blocked V cache) x P (B,
+// two terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
 // output).  The waves' (max, sum, acc) are merged in LDS (8 x 16 x (hd + 2) floats) and the output
 // goes to the activation planes bo as ONT terms of format ODT.
 template <int KVDT, int ODT, int ONT, int HD>
@@ -2278,14 +2404,14 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (32 * wave <= qlast) {
-      u32x4 qt[NC][3];
+      u32x4 qt[NC][kPfTerms];
 #pragma unroll
       for (int s = 0; s < NC; ++s) {
         float qv[8];
         const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = src[e];
-        split3x8<KDT>(qv, qt[s][0], qt[s][1], qt[s][2]);
+        split_terms8<KDT, kPfTerms>(qv, qt[s]);
       }
       for (int kb = 32 * wave; kb <= qlast; kb += 32 * kWaves) {
         // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
@@ -2296,12 +2422,11 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
         for (int s = 0; s < NC; ++s) {
           const u32x4 ka = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
           const u32x4 kb4 = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
-          s0 = mfma16<KDT>(ka, qt[s][2], s0);
-          s1 = mfma16<KDT>(kb4, qt[s][2], s1);
-          s0 = mfma16<KDT>(ka, qt[s][1], s0);
-          s1 = mfma16<KDT>(kb4, qt[s][1], s1);
-          s0 = mfma16<KDT>(ka, qt[s][0], s0);
-          s1 = mfma16<KDT>(kb4, qt[s][0], s1);
+#pragma unroll
+          for (int n = kPfTerms - 1; n >= 0; --n) {
+            s0 = mfma16<KDT>(ka, qt[s][n], s0);
+            s1 = mfma16<KDT>(kb4, qt[s][n], s1);
+          }
         }
         const int pv = kb + 8 * kg;  // this lane's 8 positions
         u32x4 vt[NT];
@@ -2334,14 +2459,12 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
         m = mn;
-        u32x4 p0t, p1t, p2t;
-        split3x8<KDT>(sc8, p0t, p1t, p2t);
+        u32x4 pt[kPfTerms];
+        split_terms8<KDT, kPfTerms>(sc8, pt);
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          acc[tt] = mfma16<KDT>(vt[tt], p2t, acc[tt]);
-          acc[tt] = mfma16<KDT>(vt[tt], p1t, acc[tt]);
-          acc[tt] = mfma16<KDT>(vt[tt], p0t, acc[tt]);
-        }
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int n = kPfTerms - 1; n >= 0; --n) acc[tt] = mfma16<KDT>(vt[tt], pt[n], acc[tt]);
       }
     }
     // merge the eight waves' records in LDS (a wave without positions left m = -inf, sum = 0)
@@ -2368,7 +2491,7 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
         num = fmaf(r[d], f, num);
         den = fmaf(r[HD + 1], f, den);
       }
-      put_terms<ODT, ONT>(A.bo, oplane, (int64_t)t * qd + j * HD + d, num / den * vscale);
+      put_terms<ODT, ONT>(A.bo, oplane, pf_b_index(t, j * HD + d, qd), num / den * vscale);
     }
     __syncthreads();
   }
@@ -2382,12 +2505,13 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
   using ST = typename WFmt<WDT>::ST;
   const int H = P.H, qd = P.qdim, F_ = P.F, hd = P.hd, half = P.hd / 2, chunk = A.chunk;
   const int qrows = P.qdim, krows = P.nkv * P.hd;
-  // one wave per token (RMSNorm) spread over every wave of the grid
-  const int gw = (int)(threadIdx.x >> 6) * (int)gridDim.x + (int)blockIdx.x, nw = kWaves * (int)gridDim.x;
   uint32_t nbar = 0;
   for (int p0 = 0; p0 < A.n; p0 += chunk) {
     const int ntok = A.n - p0 < chunk ? A.n - p0 : chunk;
-    pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, A.tokens + p0, P.gains, ntok, gw, nw);
+    pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, nullptr, A.tokens + p0, P.gains, ntok, lds_pf);
+    // K-halves of the O and down projections for this chunk (their partial planes are summed by
+    // the RMSNorm that reads them)
+    const int ks_o = pf_ksplit(H, qd, 128, ntok), ks_d = pf_ksplit(H, F_, 128, ntok);
     pf_barrier(P, A.bar, ++nbar);
     for (int l = 0; l < P.L; ++l) {
       const uint8_t* Wl = P.wbase + (int64_t)l * P.layer_bytes;
@@ -2409,8 +2533,12 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         }
       };
       // QKV: rows 2m, 2m + 1 are a RoPE pair (q, k) or two v dims; q to A.q, k and v to the cache
-      pf_gemm<WDT, 128>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, lds_pf, s_qkv, [&](int r4, int t, f32x4 v) {
-        if (t >= ntok || r4 >= P.qkv_rows) return;
+      pf_gemm<WDT, 128>(Wl + P.off_qkv, P.qkv_rows, H, A.bn, chunk, ntok, 1, lds_pf, s_qkv,
+                        [&](int r4, int t, f32x4 v, int) {
+        // the 16 rows of this lane's block lie in one section and one head (sections and heads are
+        // multiples of 16 rows), so the calibration's max reduces over the wave first
+        float amax = 0.f;
+        if (t < ntok && r4 < P.qkv_rows) {
         const int pos = p0 + t;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
@@ -2439,9 +2567,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
                                       : ((hb * (P.seqcap / 32) + pos / 32) * hd + i) * 32 + pos % 32;
           const int64_t ib = sec == 1 ? ia + half : ia + (int64_t)half * 32;
           if constexpr (KVDT == WFP8) {
-            if (A.calib)
-              __hip_atomic_fetch_max(&P.kv_amax[hb * 2 + (sec - 1)], __float_as_uint(fmaxf(fabsf(a), fabsf(b))),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            amax = fmaxf(amax, fmaxf(fabsf(a), fabsf(b)));
             const float s8 = P.kv_scale[hb * 2 + (sec - 1)];
             uint8_t* c8 = sec == 1 ? P.kc : P.vc;
             c8[ia] = enc_e4m3(a / s8);
@@ -2450,6 +2576,18 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
             uint16_t* c16 = reinterpret_cast<uint16_t*>(sec == 1 ? P.kc : P.vc);
             c16[ia] = enc16<KVDT>(a);
             c16[ib] = enc16<KVDT>(b);
+          }
+        }
+        }
+        if constexpr (KVDT == WFP8) {
+          const int rb = r4 & ~15;  // the block's first row (the same on every lane)
+          if (A.calib && rb >= qrows && rb < P.qkv_rows) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+            const int sec = rb < qrows + krows ? 1 : 2, head = (rb - (sec == 1 ? qrows : qrows + krows)) / hd;
+            if ((threadIdx.x & 63) == 0)
+              __hip_atomic_fetch_max(&P.kv_amax[((int64_t)l * P.nkv + head) * 2 + (sec - 1)], __float_as_uint(amax),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       });
@@ -2463,16 +2601,20 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         if constexpr (!F::SCALED) return 1.f;
         else return scale_value<WDT>(scale_row<WDT>(so, r, nbq)[g]);
       };
-      pf_gemm<WDT, 128>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, lds_pf, s_o, [&](int r4, int t, f32x4 v) {
+      pf_gemm<WDT, 128>(Wl + P.off_o, H, qd, A.bo, chunk, ntok, ks_o, lds_pf, s_o, [&](int r4, int t, f32x4 v, int ks) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = r4 + i;
-          if (r < H) A.xm[(int64_t)t * H + r] = A.x[(int64_t)t * H + r] + v[i];
+          if (r >= H) continue;
+          const int64_t e = (int64_t)t * H + r;
+          if (ks == 0) A.xm[e] = A.x[e] + v[i];
+          else A.xm2[e] = v[i];
         }
       });
       pf_barrier(P, A.bar, ++nbar);
-      pf_rmsnorm<ADT, NT, EDT>(P, A, A.xm, nullptr, P.gains + (int64_t)l * 2 * H + H, ntok, gw, nw);
+      pf_rmsnorm<ADT, NT, EDT>(P, A, A.xm, ks_o == 2 ? A.xm2 : nullptr, nullptr, P.gains + (int64_t)l * 2 * H + H,
+                               ntok, lds_pf);
       pf_barrier(P, A.bar, ++nbar);
       // gate/up (interleaved rows 2n, 2n + 1) + SwiGLU
       const int64_t hplane = (int64_t)chunk * F_;
@@ -2483,15 +2625,15 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         else return scale_value<WDT>(scale_row<WDT>((r & 1) ? su : sg, r >> 1, nbh)[g]);
       };
       // 256-row tiles (128 where the per-group accumulators of a scaled format would not fit)
-      pf_gemm<WDT, F::SCALED ? 128 : 256>(Wl + P.off_gu, 2 * F_, H, A.bn, chunk, ntok, lds_pf, s_gu,
-                                          [&](int r4, int t, f32x4 v) {
+      pf_gemm<WDT, F::SCALED ? 128 : 256>(Wl + P.off_gu, 2 * F_, H, A.bn, chunk, ntok, 1, lds_pf, s_gu,
+                                          [&](int r4, int t, f32x4 v, int) {
         if (t >= ntok) return;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int n = (r4 >> 1) + pp;
           if (n >= F_) continue;
           const float gte = v[2 * pp], up = v[2 * pp + 1];
-          put_terms<ADT, NT>(A.bh, hplane, (int64_t)t * F_ + n, gte / (1.0f + expf(-gte)) * up);
+          put_terms<ADT, NT>(A.bh, hplane, pf_b_index(t, n, F_), gte / (1.0f + expf(-gte)) * up);
         }
       });
       pf_barrier(P, A.bar, ++nbar);
@@ -2501,17 +2643,21 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
         if constexpr (!F::SCALED) return 1.f;
         else return scale_value<WDT>(scale_row<WDT>(sd, r, nbf)[g]);
       };
-      pf_gemm<WDT, 128>(Wl + P.off_d, H, F_, A.bh, chunk, ntok, lds_pf, s_d, [&](int r4, int t, f32x4 v) {
+      pf_gemm<WDT, 128>(Wl + P.off_d, H, F_, A.bh, chunk, ntok, ks_d, lds_pf, s_d, [&](int r4, int t, f32x4 v, int ks) {
         if (t >= ntok) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = r4 + i;
-          if (r < H) A.x[(int64_t)t * H + r] = A.xm[(int64_t)t * H + r] + v[i];
+          if (r >= H) continue;
+          const int64_t e = (int64_t)t * H + r;
+          if (ks == 0) A.x[e] = A.xm[e] + v[i];
+          else A.x2[e] = v[i];
         }
       });
       pf_barrier(P, A.bar, ++nbar);
       if (l + 1 < P.L) {
-        pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, nullptr, P.gains + (int64_t)(l + 1) * 2 * H, ntok, gw, nw);
+        pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, ks_d == 2 ? A.x2 : nullptr, nullptr, P.gains + (int64_t)(l + 1) * 2 * H,
+                                 ntok, lds_pf);
         pf_barrier(P, A.bar, ++nbar);
       }
     }

@@ -60,7 +60,8 @@ void scale_counts(const ModelDims& m, int64_t sz[7]) {
 // LDS of the batched prefill: the attention's eight wave records of 16 queries x (hd + 2) floats,
 // or the GEMM's two 256-row x 64-byte weight buffers
 size_t prefill_lds_bytes(const ModelDims& m) {
-  return std::max((size_t)kWaves * 16 * (m.hd + 2) * 4, (size_t)2 * 256 * 64);
+  // the attention's wave records, or three weight blocks of a 256-row GEMM tile
+  return std::max((size_t)kWaves * 16 * (m.hd + 2) * 4, (size_t)3 * 256 * 64);
 }
 int64_t lm_scale_count(const ModelDims& m) { return (m.wdt == PMK_DT_FP8_E4M3 ? nblk(m.V) : m.V) * nblk(m.H); }
 
@@ -89,7 +90,7 @@ struct pmk_ctx {
           w_cprod = 0, w_cflag = 0;
   // batched prefill: tokens per chunk (0: none) and its chunk buffers
   int pf_chunk = 0;
-  int64_t w_pfx = 0, w_pfxm = 0, w_pfq = 0, w_pfbn = 0, w_pfbo = 0, w_pfbh = 0, w_pfbar = 0;
+  int64_t w_pfx = 0, w_pfxm = 0, w_pfx2 = 0, w_pfxm2 = 0, w_pfq = 0, w_pfbn = 0, w_pfbo = 0, w_pfbh = 0, w_pfbar = 0;
   uint8_t* arena = nullptr;
   uint8_t* kv = nullptr;
   uint8_t* ws = nullptr;
@@ -251,9 +252,11 @@ void compute_layout(pmk_ctx* c) {
     c->w_pfx = w; w = align256(w + ch * H * 4);
     c->w_pfxm = w; w = align256(w + ch * H * 4);
     c->w_pfq = w; w = align256(w + ch * qd * 4);
-    c->w_pfbn = w; w = align256(w + 3 * ch * H * 2);
-    c->w_pfbo = w; w = align256(w + 3 * ch * qd * 2);
-    c->w_pfbh = w; w = align256(w + 3 * ch * F * 2);
+    c->w_pfx2 = w; w = align256(w + ch * H * 4);
+    c->w_pfxm2 = w; w = align256(w + ch * H * 4);
+    c->w_pfbn = w; w = align256(w + 2 * ch * H * 2);  // two 16-bit terms per activation
+    c->w_pfbo = w; w = align256(w + 2 * ch * qd * 2);
+    c->w_pfbh = w; w = align256(w + 2 * ch * F * 2);
     c->w_pfbar = w; w = align256(w + (int64_t)std::max(c->n_cus, 1) * 4);  // one barrier flag per workgroup
   }
   c->sizes.workspace_bytes = w;
@@ -779,6 +782,8 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     a.chunk = c->pf_chunk;
     a.x = reinterpret_cast<float*>(c->ws + c->w_pfx);
     a.xm = reinterpret_cast<float*>(c->ws + c->w_pfxm);
+    a.x2 = reinterpret_cast<float*>(c->ws + c->w_pfx2);
+    a.xm2 = reinterpret_cast<float*>(c->ws + c->w_pfxm2);
     a.q = reinterpret_cast<float*>(c->ws + c->w_pfq);
     a.bn = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbn);
     a.bo = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbo);

@@ -48,8 +48,10 @@ struct PrefillArgs {
   int32_t chunk;          // tokens per chunk (a multiple of 128)
   float* x;               // [chunk][H] residual stream
   float* xm;              // [chunk][H] residual after attention
+  float* x2;              // [chunk][H] second K-half of the down projection (x = x + x2 at the next RMSNorm)
+  float* xm2;             // [chunk][H] second K-half of the O projection (xm = xm + xm2 at the RMSNorm)
   float* q;               // [chunk][qdim] queries after RoPE
-  uint16_t* bn;           // [terms][chunk][H] normalised activations (three 16-bit terms, or the
+  uint16_t* bn;           // [terms][chunk][H] normalised activations (two 16-bit terms, or the
                           // one binary16 value of the integer formats)
   uint16_t* bo;           // [terms][chunk][qdim] attention output
   uint16_t* bh;           // [terms][chunk][F] SwiGLU output
