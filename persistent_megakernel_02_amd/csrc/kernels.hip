@@ -1969,7 +1969,8 @@ __global__ void pmk_begin_call(KParams P, CallParams cp) {
 // ------------------------------------------------------------------------------------------------
 constexpr int kPfTokens = 128;  // GEMM tile tokens (16 per wave)
 // 16-bit terms of an fp32 activation operand (GEMM inputs, attention q and probabilities) for the
-// 16-bit and FP8 weight formats
+// 16-bit and FP8 weight formats (the integer formats take one binary16 term in the GEMMs and three
+// in the attention)
 constexpr int kPfTerms = 2;
 
 // Element (t, k) of an activation plane of K columns (the GEMMs' B operand): 16-token blocks of
@@ -2371,8 +2372,8 @@ __device__ __forceinline__ u32x4 pf_kv8(const uint8_t* base, int64_t elem) {
 // per (q head j, block of 16 queries); its eight waves split the key positions, wave w taking the
 // 32-position groups w, w + 8, ... up to the block's last query, with the decode attention's
 // matrix-core layout and the 16 queries of the head as the B columns: scores = K rows (A) x q
-// (B, two terms), online softmax per query, P.V = V^T (A, from the blocked V cache) x P (B,
-// two terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
+// (B, two 16-bit terms; three for the integer formats), online softmax per query, P.V = V^T (A,
+// from the blocked V cache) x P (B, the same terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
 // output).  The waves' (max, sum, acc) are merged in LDS (8 x 16 x (hd + 2) floats) and the output
 // goes to the activation planes bo as ONT terms of format ODT.
 template <int KVDT, int ODT, int ONT, int HD>
@@ -2380,6 +2381,10 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
   constexpr int KDT = KVDT == WF16 ? WF16 : WBF16;  // operand format of the cache values
   constexpr int KES = KVDT == WFP8 ? 1 : 2;
   constexpr int NC = HD / 32, NT = HD / 16, REC = HD + 2;
+  // q and P as 16-bit terms: three where the output is rounded to one binary16 term (the integer
+  // formats' A16 operand of the O projection, whose rounding turns a two-term error into whole
+  // binary16 steps in some elements), else two
+  constexpr int QT = ONT == 1 ? 3 : kPfTerms;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c16 = lane & 15, kg = lane >> 4;
   const int nqb = (ntok + 15) / 16, ntasks = P.nq * nqb, qd = P.qdim;
   const int pend = p0 + ntok;  // cache positions [0, pend) are written
@@ -2404,14 +2409,14 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (32 * wave <= qlast) {
-      u32x4 qt[NC][kPfTerms];
+      u32x4 qt[NC][QT];
 #pragma unroll
       for (int s = 0; s < NC; ++s) {
         float qv[8];
         const float* src = A.q + (int64_t)tqc * qd + j * HD + 32 * s + 8 * kg;
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = src[e];
-        split_terms8<KDT, kPfTerms>(qv, qt[s]);
+        split_terms8<KDT, QT>(qv, qt[s]);
       }
       for (int kb = 32 * wave; kb <= qlast; kb += 32 * kWaves) {
         // A rows: block 0 row r -> position kb + 8 (r / 4) + r % 4, block 1 the same + 4, so that
@@ -2423,7 +2428,7 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
           const u32x4 ka = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0) * HD + 32 * s + 8 * kg);
           const u32x4 kb4 = pf_kv8<KVDT>(P.kc, (hb * P.seqcap + pr0 + 4) * HD + 32 * s + 8 * kg);
 #pragma unroll
-          for (int n = kPfTerms - 1; n >= 0; --n) {
+          for (int n = QT - 1; n >= 0; --n) {
             s0 = mfma16<KDT>(ka, qt[s][n], s0);
             s1 = mfma16<KDT>(kb4, qt[s][n], s1);
           }
@@ -2459,12 +2464,12 @@ __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[tt][i] *= alpha;
         m = mn;
-        u32x4 pt[kPfTerms];
-        split_terms8<KDT, kPfTerms>(sc8, pt);
+        u32x4 pt[QT];
+        split_terms8<KDT, QT>(sc8, pt);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-          for (int n = kPfTerms - 1; n >= 0; --n) acc[tt] = mfma16<KDT>(vt[tt], pt[n], acc[tt]);
+          for (int n = QT - 1; n >= 0; --n) acc[tt] = mfma16<KDT>(vt[tt], pt[n], acc[tt]);
       }
     }
     // merge the eight waves' records in LDS (a wave without positions left m = -inf, sum = 0)
