@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PMK_ABI_VERSION 4
+#define PMK_ABI_VERSION 5
 
 typedef enum {
   PMK_OK = 0,
@@ -133,7 +133,10 @@ typedef struct {
                                rounded up to 128 if smaller), a multiple of 128 up to 1024, or -1 = no
                                batched prefill (every prompt position runs as a teacher-forced decode
                                step) */
-  int32_t reserved[5];      /* must be 0 */
+  int32_t prefill_ksplit;   /* K-halves of the batched prefill's O and down projections: 0 automatic (two
+                               where their tiles would fill at most half the grid), 1 never, 2 always
+                               (where K has at least eight 32-column steps) */
+  int32_t reserved[4];      /* must be 0 */
 } pmk_schedule_config;
 
 typedef struct {

@@ -2330,11 +2330,13 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
     for (int c = 0; c < 2; ++c) epi(row0 + wrow + 16 * b + 4 * kg, (tb0 + c) * 16 + r16, acc[b][c], ks);
 }
 
-// K-halves of a GEMM phase: 2 where its tiles would fill at most half the grid and K has at least
-// eight 32-column steps (the halves split at a 128-column group boundary), else 1
-__device__ __forceinline__ int pf_ksplit(int N, int K, int MR, int ntok) {
+// K-halves of a GEMM phase: 2 where K has at least eight 32-column steps (the halves split at a
+// 128-column group boundary) and `mode` asks for it (2) or, automatic (0), its tiles would fill at
+// most half the grid; else 1
+__device__ __forceinline__ int pf_ksplit(int N, int K, int MR, int ntok, int mode) {
   const int tiles = ((N + MR - 1) / MR) * ((ntok + kPfTokens - 1) / kPfTokens);
-  return 2 * tiles <= (int)gridDim.x && (((K + 31) / 32 / 2) & ~3) > 0 ? 2 : 1;
+  const bool can = (((K + 31) / 32 / 2) & ~3) > 0;
+  return can && (mode == 2 || (mode == 0 && 2 * tiles <= (int)gridDim.x)) ? 2 : 1;
 }
 
 // Run the tiles of one GEMM phase: rows [0, N) x tokens [0, ntok) x ksplit K-parts (epi gets the
@@ -2516,7 +2518,7 @@ __global__ void __launch_bounds__(kThreads, 1) pmk_prefill_batch(KParams P, Pref
     pf_rmsnorm<ADT, NT, EDT>(P, A, A.x, nullptr, A.tokens + p0, P.gains, ntok, lds_pf);
     // K-halves of the O and down projections for this chunk (their partial planes are summed by
     // the RMSNorm that reads them)
-    const int ks_o = pf_ksplit(H, qd, 128, ntok), ks_d = pf_ksplit(H, F_, 128, ntok);
+    const int ks_o = pf_ksplit(H, qd, 128, ntok, A.ksplit), ks_d = pf_ksplit(H, F_, 128, ntok, A.ksplit);
     pf_barrier(P, A.bar, ++nbar);
     for (int l = 0; l < P.L; ++l) {
       const uint8_t* Wl = P.wbase + (int64_t)l * P.layer_bytes;

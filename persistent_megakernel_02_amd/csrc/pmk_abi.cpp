@@ -574,6 +574,10 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
       delete c;
       return fail(nullptr, PMK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or a multiple of 128 up to 1024");
     }
+    if (c->sc.prefill_ksplit < 0 || c->sc.prefill_ksplit > 2) {
+      delete c;
+      return fail(nullptr, PMK_ERR_INVALID_ARG, "prefill_ksplit must be 0, 1 or 2");
+    }
     const int cap = (c->m.max_seq + 127) / 128 * 128;
     c->pf_chunk = ch == -1 ? 0 : std::min(ch == 0 ? 512 : ch, cap);
   }
@@ -790,6 +794,7 @@ pmk_status pmk_prefill_kv(pmk_ctx* c, const int32_t* d_tokens, int32_t P, const 
     a.bh = reinterpret_cast<uint16_t*>(c->ws + c->w_pfbh);
     a.bar = reinterpret_cast<uint32_t*>(c->ws + c->w_pfbar);
     a.calib = calib;
+    a.ksplit = c->sc.prefill_ksplit;
     HIPCHK(c, launch_reset(c->kp, c->sched.n_flags, (int)c->sched.counters.size(), P - 1, 0, d_tokens + P - 1, st));
     HIPCHK(c, hipMemsetAsync(a.bar, 0, (size_t)c->n_cus * 4, st));
     void* args[] = {&c->kp, &a};

@@ -57,6 +57,7 @@ struct PrefillArgs {
   uint16_t* bh;           // [terms][chunk][F] SwiGLU output
   uint32_t* bar;          // grid barrier: one flag word per workgroup (zero at launch)
   int32_t calib;          // FP8 KV scale calibration: record max |k|, |v| of every appended row
+  int32_t ksplit;         // K-halves of the O and down projections: 0 automatic, 1 never, 2 always
 };
 
 struct KParams {

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"{n} has no binding"
-    assert lib.pmk_abi_version() == 4
+    assert lib.pmk_abi_version() == 5
 
 
 def create(cfg, sched=None):
@@ -108,6 +108,15 @@ def test_null_and_bad_arguments():
     assert lib.pmk_set_trace(ctx, 1) == _lib.PMK_ERR_INVALID_ARG  # no trace buffer in this schedule
     assert lib.pmk_status_str(_lib.PMK_ERR_CAPACITY) == b"KV capacity exceeded"
     lib.pmk_destroy(ctx)
+    cfg = pmk.model_config(WORKLOADS["tiny"])
+    for bad in (dict(prefill_chunk=100), dict(prefill_chunk=2048), dict(prefill_chunk=-2), dict(prefill_ksplit=3),
+                dict(prefill_ksplit=-1)):
+        st, _, msg = create(cfg, pmk.schedule_config(**bad))
+        assert st == _lib.PMK_ERR_INVALID_ARG and "prefill" in msg, (bad, st, msg)
+    for good in (dict(prefill_ksplit=1), dict(prefill_ksplit=2), dict(prefill_chunk=-1)):
+        st, ctx, msg = create(cfg, pmk.schedule_config(**good))
+        assert st == 0, (good, msg)
+        lib.pmk_destroy(ctx)
 
 
 def test_workload_byte_accounting():

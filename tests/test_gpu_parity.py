@@ -281,8 +281,9 @@ _PREFILL_FORMATS = {
 }
 
 
-@pytest.mark.parametrize("fmt", list(_PREFILL_FORMATS))
-def test_batched_prefill_rows_against_the_oracle(fmt):
+@pytest.mark.parametrize("fmt,ksplit", [(f, 0) for f in _PREFILL_FORMATS] + [("bf16", 1), ("fp8", 1), ("int4", 1)],
+                         ids=[f for f in _PREFILL_FORMATS] + ["bf16-whole-K", "fp8-whole-K", "int4-whole-K"])
+def test_batched_prefill_rows_against_the_oracle(fmt, ksplit):
     """The batched prefill (chunks of 128 positions: three chunks over a 300-token prompt, the last
     one ragged; matrix-core GEMMs and causal attention in one launch), checked position by position:
     the oracle takes the GPU's cache rows of the earlier positions and appends the GPU's row of the
@@ -293,18 +294,21 @@ def test_batched_prefill_rows_against_the_oracle(fmt):
     implementations' do, since each position attends to rows rounded to the cache format.  Integer
     formats round every GEMM operand to binary16, where two correct implementations differ by whole
     binary16 steps in some elements (the format's tolerance note): their rows are reported, and the
-    first token and the logits are checked."""
+    first token and the logits are checked.  The O and down projections run as two K-halves at
+    these sizes (prefill_ksplit 0, automatic); the whole-K cases (prefill_ksplit 1) check the
+    unsplit path on the same prompts."""
     import torch
     import oracle
     import persistent_megakernel_02_amd as pmk
     from tests.parity import _token_ok
-    w = TINY.with_(name=f"tiny_prefill_{fmt}", prompt=300, steps=8, **_PREFILL_FORMATS[fmt])
+    w = TINY.with_(name=f"tiny_prefill_{fmt}{'_wholek' if ksplit == 1 else ''}", prompt=300, steps=8,
+                   **_PREFILL_FORMATS[fmt])
     wts = synthgen.make_weights(w, std=0.05, gain_std=0.1)
     prompt = synthgen.make_prompt(w)
     scales = np.full((w.layers, w.n_kv, 2), 4.0 / 448.0, np.float32) if w.kvdtype == "fp8" else None
     out = {}
     for name, chunk in (("batched", 128), ("stepwise", -1)):
-        dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(prefill_chunk=chunk))
+        dec = pmk.Decoder(pmk.model_config(w), 0, pmk.schedule_config(prefill_chunk=chunk, prefill_ksplit=ksplit))
         dec.load_weights(pmk.DeviceWeights(wts))
         ks = torch.from_numpy(scales).cuda() if scales is not None else None
         first = int(dec.prefill(torch.from_numpy(prompt).cuda(), ks).item())
@@ -333,7 +337,8 @@ def test_batched_prefill_rows_against_the_oracle(fmt):
     if fmt not in ("int8", "int4"):
         assert worst <= 1.0 and np.mean(differ) <= 0.02
     assert _token_ok(olg, first)
-    run = gpu_run(w, wts, w.steps, prompt=prompt, kv_scales=scales, sched=pmk.schedule_config(prefill_chunk=128))
+    run = gpu_run(w, wts, w.steps, prompt=prompt, kv_scales=scales,
+                  sched=pmk.schedule_config(prefill_chunk=128, prefill_ksplit=ksplit))
     ref, first_ok = oracle_teacher_forced(w, wts, run, prompt=prompt, kv_scales=scales)
     check(w, run, ref, first_ok, f"{w.name}/batched prefill")
 
