@@ -477,7 +477,9 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   int lrow = wr0, lj = s0;
   uint32_t roff = (uint32_t)((int64_t)(wr0 - r0) * rb);
   const typename WFmt<WDT>::ST* srp = nullptr;
-  if constexpr (WFmt<WDT>::SCALED) srp = srow(wr0);
+  // a wave without rows reads the tile's first row's scales (a row that exists) for its zero units
+  const int srow0 = wr0 < wr1 ? wr0 : r0;
+  if constexpr (WFmt<WDT>::SCALED) srp = srow(srow0);
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
     const bool ok = lrow < wr1 && c < nch;
@@ -488,7 +490,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
       lj = s0;
       ++lrow;
       roff += (uint32_t)rb;
-      if constexpr (WFmt<WDT>::SCALED) srp = srow(lrow < wr1 ? lrow : wr0);
+      if constexpr (WFmt<WDT>::SCALED) srp = srow(lrow < wr1 ? lrow : srow0);
     }
   };
   // kPre units per lane are issued before the dependency wait (when prefetching), the rest of the
