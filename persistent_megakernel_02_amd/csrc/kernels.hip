@@ -2293,14 +2293,17 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
       const int step = base + d;
       if (step < nsteps) {
         if (step + 1 < nsteps) read_a((d + 1) & 1, step + 1);
+        // the low terms first (each accumulator sums its products smallest first), all of a term's
+        // products before the next term's: consecutive products never share an accumulator
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
+        for (int t = NT - 1; t >= 0; --t)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            f32x4& cc = F::SCALED ? accg[b][c] : acc[b][c];
+          for (int b = 0; b < RB; ++b)
 #pragma unroll
-            for (int t = NT - 1; t >= 0; --t) cc = mfma16<F::ADT>(ao[d & 1][b], rb[d][c][t], cc);
-          }
+            for (int c = 0; c < 2; ++c) {
+              f32x4& cc = F::SCALED ? accg[b][c] : acc[b][c];
+              cc = mfma16<F::ADT>(ao[d & 1][b], rb[d][c][t], cc);
+            }
         if constexpr (F::SCALED) {
           if ((step & 3) == 3 || step == nsteps - 1) {  // end of a 128-column group (step0 % 4 == 0)
             const int g = (step0 + step) >> 2;
