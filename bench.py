@@ -317,10 +317,3 @@ def main():
 
 if __name__ == "__main__":
     main()
-    # Everything is released above.  Skip the interpreter's exit handlers: after cooperative
-    # launches the HIP runtime's own exit-time teardown segfaults inside exit() when rocprofv3 has
-    # already finalized (a process that loads the library and launches only ordinary kernels exits
-    # 0 under the profiler; this one, after its results are written, did not).
-    sys.stdout.flush()
-    sys.stderr.flush()
-    os._exit(0)
