@@ -274,8 +274,9 @@ pmk_status pmk_load_weights(pmk_ctx* ctx, const pmk_weight_ptrs* src, void* stre
  * Other KV formats ignore d_kv_scales.  Unless prefill_chunk is -1, positions 0..P-2 run batched,
  * in chunks of prefill_chunk tokens, in ONE cooperative launch of grid-wide phases (RMSNorm, QKV
  * GEMM + RoPE + KV append, causal attention, O GEMM, RMSNorm, gate/up GEMM + SwiGLU, down GEMM)
- * with the GEMMs on the matrix cores (fp32-accurate activations; binary16 ones for INT8 / INT4, as
- * the format defines), and the last position as a teacher-forced decode step; with -1 every
+ * with the GEMMs on the matrix cores (activations as two 16-bit terms, within 2^-18 of fp32;
+ * binary16 ones for INT8 / INT4, as the format defines; the O and down projections in two
+ * K-halves as prefill_ksplit says), and the last position as a teacher-forced decode step; with -1 every
  * position runs as a teacher-forced decode step.  Resets the position and the synchronisation
  * state.
  * Asynchronous on `stream`.  Errors: PMK_ERR_NOT_BOUND (no weights), PMK_ERR_INVALID_ARG (NULL
