@@ -2193,7 +2193,7 @@ constexpr int pf_a_depth() { return WDT >= WFP8 ? 1 : 2; }
 // over the 32-column steps [step0, step1).  Wave w takes tile rows (w / 4) MR / 2 .. + MR / 2 - 1
 // and tokens tok0 + 32 (w % 4) .. + 31 (two 16-token column blocks): per step it reads MR / 2 rows
 // of the weight block from LDS (half of what a wave taking all rows would) and its tokens' terms
-// from global memory (a 4-step register ring).  The weight block of a step goes through LDS once
+// from global memory (a 2-step register ring).  The weight block of a step goes through LDS once
 // for the workgroup (converted to 16-bit operands on the way, three buffers) and each wave reads its
 // operands of the next step while its matrix-core products of this step run.  Scaled formats
 // accumulate each 128-column group apart and add it times scale(row, group).
@@ -2255,10 +2255,7 @@ __device__ __forceinline__ void pf_gemm_tile(const uint8_t* W, int N, int K, con
   };
   // B: a ring of D steps of this lane's terms (two token blocks) in flight; a step past the end
   // reads zeros without touching memory
-#ifndef PMK_PF_B_DEPTH
-#define PMK_PF_B_DEPTH 2
-#endif
-  constexpr int D = PMK_PF_B_DEPTH;
+  constexpr int D = 2;  // 4 measured slower: the registers it takes spill elsewhere in the kernel
   static_assert(D % DA == 0 && D % 2 == 0, "the rings' slots follow the step");
   u32x4 rb[D][2][NT];
   auto issue = [&](int d, int step) {
@@ -2380,9 +2377,10 @@ __device__ __forceinline__ u32x4 pf_kv8(const uint8_t* base, int64_t elem) {
 // 32-position groups w, w + 8, ... up to the block's last query, with the decode attention's
 // matrix-core layout and the 16 queries of the head as the B columns: scores = K rows (A) x q
 // (B, two 16-bit terms; three for the integer formats), online softmax per query, P.V = V^T (A,
-// from the blocked V cache) x P (B, the same terms); an FP8 cache is read as bf16 operands and scaled (K on the scores, V on the
-// output).  The waves' (max, sum, acc) are merged in LDS (8 x 16 x (hd + 2) floats) and the output
-// goes to the activation planes bo as ONT terms of format ODT.
+// from the blocked V cache) x P (B, the same terms); an FP8 cache is read as bf16 operands and
+// scaled (K on the scores, V on the output).  The waves' (max, sum, acc) are merged in LDS
+// (8 x 16 x (hd + 2) floats) and the output goes to the activation planes bo as ONT terms of
+// format ODT.
 template <int KVDT, int ODT, int ONT, int HD>
 __device__ __forceinline__ void pf_attn(const KParams& P, const PrefillArgs& A, int l, int p0, int ntok, float* lds) {
   constexpr int KDT = KVDT == WF16 ? WF16 : WBF16;  // operand format of the cache values

@@ -58,9 +58,8 @@ void scale_counts(const ModelDims& m, int64_t sz[7]) {
   for (int i = 0; i < 7; ++i) sz[i] = (m.wdt == PMK_DT_FP8_E4M3 ? nblk(rows[i]) : rows[i]) * nblk(cols[i]);
 }
 // LDS of the batched prefill: the attention's eight wave records of 16 queries x (hd + 2) floats,
-// or the GEMM's two 256-row x 64-byte weight buffers
+// or the GEMM's three 256-row x 64-byte weight buffers
 size_t prefill_lds_bytes(const ModelDims& m) {
-  // the attention's wave records, or three weight blocks of a 256-row GEMM tile
   return std::max((size_t)kWaves * 16 * (m.hd + 2) * 4, (size_t)3 * 256 * 64);
 }
 int64_t lm_scale_count(const ModelDims& m) { return (m.wdt == PMK_DT_FP8_E4M3 ? nblk(m.V) : m.V) * nblk(m.H); }
