@@ -425,10 +425,11 @@ struct TileSplit {
     R = r1 - r0;
     int best = 0x7fffffff;
     KS = 1;
-    for (int ks = 1; ks <= kWaves && ks <= nsl; ks <<= 1) {
+#pragma unroll
+    for (int ks = 1; ks <= kWaves; ks <<= 1) {
       const int g = kWaves / ks;
       const int cost = ((R + g - 1) / g) * ((nsl + ks - 1) / ks + row_cost);
-      if (cost < best) { best = cost; KS = ks; }
+      if (ks <= nsl && cost < best) { best = cost; KS = ks; }
     }
     const int G = kWaves / KS;
     gi = wave / KS;
@@ -480,9 +481,15 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
   // a wave without rows reads the tile's first row's scales (a row that exists) for its zero units
   const int srow0 = wr0 < wr1 ? wr0 : r0;
   if constexpr (WFmt<WDT>::SCALED) srp = srow(srow0);
+  // The chunk count lives in a vector register: the issue's compare then needs no scalar register.
+  // The scalar file of this kernel is full, and without this the count was reloaded from a spill
+  // slot at every unit (8B decode 324 -> 337 tok/s in an A/B; pinning the row stride the same way
+  // as well moved other values into spills and was slower).
+  int nch_v = nch;
+  asm volatile("" : "+v"(nch_v));
   auto issue = [&](int d) {
     const int c = lj * 64 + lane;
-    const bool ok = lrow < wr1 && c < nch;
+    const bool ok = lrow < wr1 && c < nch_v;
     const uint32_t off = ok ? roff + (uint32_t)c * 16u : kOut;
     ring[d] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);  // nontemporal
     if constexpr (WFmt<WDT>::SCALED) rsc[d] = scale_value<WDT>(srp[(uint32_t)(c < nch ? c : 0) / WFmt<WDT>::CPG]);
