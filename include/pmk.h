@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PMK_ABI_VERSION 5
+#define PMK_ABI_VERSION 6
 
 typedef enum {
   PMK_OK = 0,
@@ -136,7 +136,11 @@ typedef struct {
   int32_t prefill_ksplit;   /* K-halves of the batched prefill's O and down projections: 0 automatic (two
                                where their tiles would fill at most half the grid), 1 never, 2 always
                                (where K has at least eight 32-column steps) */
-  int32_t reserved[4];      /* must be 0 */
+  int32_t combine_o_copy;   /* a COMBINE copies the O-projection tile of its queue's next task to LDS
+                               before its own wait: 0 automatic (when an attention split holds at least
+                               128 positions, where the copy hides behind the longer wait), 1 never,
+                               2 always */
+  int32_t reserved[3];      /* must be 0 */
 } pmk_schedule_config;
 
 typedef struct {

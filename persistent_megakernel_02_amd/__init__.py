@@ -31,9 +31,9 @@ def model_config(w, max_seq: Optional[int] = None) -> pmk_model_config:
 def schedule_config(n_cus: int = 0, sync_mode: int = PMK_SYNC_FLAGS, attn_splits: int = 0, prefetch: int = 0,
                     trace_steps: int = 0, spin_limit: int = 0, combine_parts: int = 0,
                     combine_o_share: int = 0, prefill_chunk: int = 0,
-                    prefill_ksplit: int = 0) -> pmk_schedule_config:
+                    prefill_ksplit: int = 0, combine_o_copy: int = 0) -> pmk_schedule_config:
     return pmk_schedule_config(n_cus, sync_mode, attn_splits, prefetch, trace_steps, spin_limit, combine_parts,
-                               combine_o_share, prefill_chunk, prefill_ksplit)
+                               combine_o_share, prefill_chunk, prefill_ksplit, combine_o_copy)
 
 
 def _stream(stream=None) -> int:

@@ -40,8 +40,8 @@ class pmk_model_config(ctypes.Structure):
 
 class pmk_schedule_config(ctypes.Structure):
     _fields_ = [("n_cus", i32), ("sync_mode", i32), ("attn_splits", i32), ("prefetch", i32), ("trace_steps", i32),
-                ("spin_limit", i64), ("combine_parts", i32), ("combine_o_share", i32), ("prefill_chunk", i32), ("prefill_ksplit", i32),
-                ("reserved", i32 * 4)]
+                ("spin_limit", i64), ("combine_parts", i32), ("combine_o_share", i32), ("prefill_chunk", i32), ("prefill_ksplit", i32), ("combine_o_copy", i32),
+                ("reserved", i32 * 3)]
 
 
 class pmk_sizes(ctypes.Structure):

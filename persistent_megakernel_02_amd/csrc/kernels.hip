@@ -1817,20 +1817,17 @@ __device__ __forceinline__ void attn_hd(const KParams& P, const pmk_task& t, int
 // An O-projection task that follows a COMBINE on the same queue has its LDS tile copied by the
 // combine, before the combine's wait: the combine uses no LDS, and otherwise the copy would start
 // only once the combine ends, which put those queues' O projections last on the chip's critical path.
+// Both tasks evaluate the same predicate on their own (no state is carried from one task to the
+// next): the combine to issue the copy, the O projection to skip its own.
 template <int WDT>
-__device__ __forceinline__ bool copy_next_oproj_tile(const KParams& P, const StepCtx& sc, int next_ti, int layer,
-                                                     float* lds) {
-  if (next_ti < 0) return false;
-  const pmk_task tn = P.tasks[next_ti];
-  const int K = P.qdim, nsl = (K / WFmt<WDT>::EPL + 63) >> 6;
-  if (tn.op != PMK_OP_OPROJ || tn.layer != layer || !oproj_tile_in_lds(P, tn, sc, nsl)) return false;
-  tile_to_lds<WDT>(P.wbase + (int64_t)layer * P.layer_bytes + P.off_o, K, tn.a0, tn.a1, lds + P.pf_off, kOprojRowCost);
-  return true;
+__device__ __forceinline__ bool combine_copies_tile(const KParams& P, const StepCtx& sc, const pmk_task& o, int layer) {
+  const int nsl = (P.qdim / WFmt<WDT>::EPL + 63) >> 6;
+  return P.o_copy && o.op == PMK_OP_OPROJ && o.layer == layer && oproj_tile_in_lds(P, o, sc, nsl);
 }
 
 template <int WDT, int KVDT>
 __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
-                                         int cu, int next_ti = -1, int* otile = nullptr) {
+                                         int cu, int qi = -1, int q0 = 0, int q1 = 0) {
   switch (t.op) {
     case PMK_OP_QKV: task_qkv<WDT, KVDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_ATTN: {
@@ -1854,14 +1851,24 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
       break;
     }
     case PMK_OP_COMBINE:
-      if (otile && copy_next_oproj_tile<WDT>(P, sc, next_ti, t.layer, lds)) *otile = next_ti;
+      if (qi >= 0 && qi + 1 < q1) {
+        const pmk_task tn = P.tasks[P.qtasks[qi + 1]];
+        if (combine_copies_tile<WDT>(P, sc, tn, t.layer))
+          tile_to_lds<WDT>(P.wbase + (int64_t)t.layer * P.layer_bytes + P.off_o, P.qdim, tn.a0, tn.a1, lds + P.pf_off,
+                           kOprojRowCost);
+      }
       if (P.hd == 128) task_combine<128>(P, t, ti, sc, cu);
       else task_combine<64>(P, t, ti, sc, cu);
       break;
-    case PMK_OP_OPROJ:
-      task_oproj<WDT>(P, t, ti, sc, lds, cu, otile && *otile == ti);
-      if (otile) *otile = -1;
+    case PMK_OP_OPROJ: {
+      bool copied = false;
+      if (qi > q0) {
+        const pmk_task tp = P.tasks[P.qtasks[qi - 1]];
+        copied = tp.op == PMK_OP_COMBINE && combine_copies_tile<WDT>(P, sc, t, tp.layer);
+      }
+      task_oproj<WDT>(P, t, ti, sc, lds, cu, copied);
       break;
+    }
     case PMK_OP_GATEUP: task_gateup<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_DOWN: task_down<WDT>(P, t, ti, sc, lds, cu); break;
     case PMK_OP_LMHEAD: task_lmhead<WDT>(P, t, ti, sc, lds, cu); break;
@@ -1904,12 +1911,11 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
     if (sc.tok >= P.V) sc.tok = P.V - 1;
     sc.per_op = false;
     sc.calib = cp.calib != 0;
-    int otile = -1;  // task whose O-projection tile this CU has already copied to LDS
     for (int qi = q0; qi < q1; ++qi) {
       const int ti = P.qtasks[qi];
       const pmk_task t = P.tasks[ti];
       trace_mark(P, s, ti, 0, __builtin_amdgcn_s_memrealtime());
-      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu, qi + 1 < q1 ? P.qtasks[qi + 1] : -1, &otile);
+      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu, qi, q0, q1);
       trace_mark(P, s, ti, 2, __builtin_amdgcn_s_memrealtime());
       trace_mark(P, s, ti, 3, who);
     }

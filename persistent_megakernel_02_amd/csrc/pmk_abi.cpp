@@ -321,6 +321,7 @@ void fill_params(pmk_ctx* c) {
   P = KParams{};
   P.L = m.L; P.H = m.H; P.nq = m.nq; P.nkv = m.nkv; P.hd = m.hd; P.F = m.F; P.V = m.V;
   P.grp = m.grp(); P.qkv_rows = m.qkv_rows(); P.qdim = m.qdim(); P.max_seq = m.max_seq; P.S = c->sched.attn_splits;
+  P.o_copy = c->sched.o_copy;
   P.seqcap = (int)seqcap_of(m);
   P.wdt = m.wdt; P.kvdt = m.kvdt; P.eps = m.eps;
   P.attn_scale = (float)(1.0 / std::sqrt((double)m.hd));
@@ -576,6 +577,10 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
     if (c->sc.prefill_ksplit < 0 || c->sc.prefill_ksplit > 2) {
       delete c;
       return fail(nullptr, PMK_ERR_INVALID_ARG, "prefill_ksplit must be 0, 1 or 2");
+    }
+    if (c->sc.combine_o_copy < 0 || c->sc.combine_o_copy > 2) {
+      delete c;
+      return fail(nullptr, PMK_ERR_INVALID_ARG, "combine_o_copy must be 0, 1 or 2");
     }
     const int cap = (c->m.max_seq + 127) / 128 * 128;
     c->pf_chunk = ch == -1 ? 0 : std::min(ch == 0 ? 512 : ch, cap);
@@ -1221,6 +1226,12 @@ pmk_status pmk_tune(pmk_ctx* c, int32_t steps, pmk_tune_result* res, void* strea
     pmk_schedule_config sc = best_sc;
     sc.combine_o_share = share;
     s = attempt(sc, best_rw, std::string("combine_o_share ") + std::to_string(share));
+    if (s != PMK_OK) return s;
+  }
+  {
+    pmk_schedule_config sc = best_sc;
+    sc.combine_o_copy = c->sched.o_copy ? 1 : 2;
+    s = attempt(sc, best_rw, std::string("combine_o_copy ") + std::to_string(sc.combine_o_copy));
     if (s != PMK_OK) return s;
   }
   for (int cp = 1; cp <= c->m.grp(); ++cp) {

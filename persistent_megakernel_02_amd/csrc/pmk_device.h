@@ -118,6 +118,7 @@ struct KParams {
   int attn_g2_off;        // LDS float offset of the attention's per-wave second-group buffers (-1: none)
   int pf_off;             // LDS float offset of the O-projection weight tile (copied before the task's wait)
   int pf_units;           // 1 KiB units in that area (0: the copy is off)
+  int32_t o_copy;  // a COMBINE copies its queue's next O-projection tile to LDS before its wait
 };
 
 }  // namespace pmk

@@ -100,6 +100,11 @@ std::string build_schedule(const ModelDims& m, const pmk_schedule_config& sc, in
   const int max_chunk = attn_max_chunk(m);
   S = std::max(S, (m.max_seq + max_chunk - 1) / max_chunk);
   s.attn_splits = S;
+  // the combine's early copy of the next O-projection tile: it hides behind the combine's wait when
+  // the splits are long (8B class, 4096+ positions in 32 splits: +1 %), and delays the combine's
+  // polls when they are short (~1B and 2B, 32 and 64 positions per split: -4 %)
+  if (sc.combine_o_copy < 0 || sc.combine_o_copy > 2) return "builder: combine_o_copy must be 0, 1 or 2";
+  s.o_copy = sc.combine_o_copy == 2 || (sc.combine_o_copy == 0 && (m.max_seq + S - 1) / S >= 128) ? 1 : 0;
   s.queues.assign(n_queues, {});
 
   auto add_counter = [&](int producers, int phase, int layer) {
@@ -928,6 +933,7 @@ uint64_t schedule_hash(const Schedule& s) {
   mix(&s.n_queues, sizeof(int));
   mix(&s.attn_splits, sizeof(int));
   mix(&s.sync_mode, sizeof(int));
+  mix(&s.o_copy, sizeof(int));
   for (auto& t : s.tasks) mix(&t, sizeof(t));
   for (auto& q : s.queues) {
     int n = (int)q.size();

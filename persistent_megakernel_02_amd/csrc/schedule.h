@@ -36,6 +36,7 @@ struct Schedule {
   int n_queues = 0;
   int attn_splits = 1;
   int combine_parts = 1;  // COMBINE tasks per kv head (each over a range of its q heads)
+  int o_copy = 0;         // a COMBINE copies its queue's next O-projection tile to LDS before its wait
   int sync_mode = PMK_SYNC_FLAGS;
   std::vector<pmk_task> tasks;
   std::vector<std::vector<int32_t>> queues;  // task indices per queue, in program order (one step)

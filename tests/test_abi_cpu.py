@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"{n} has no binding"
-    assert lib.pmk_abi_version() == 5
+    assert lib.pmk_abi_version() == 6
 
 
 def create(cfg, sched=None):
@@ -110,10 +110,12 @@ def test_null_and_bad_arguments():
     lib.pmk_destroy(ctx)
     cfg = pmk.model_config(WORKLOADS["tiny"])
     for bad in (dict(prefill_chunk=100), dict(prefill_chunk=2048), dict(prefill_chunk=-2), dict(prefill_ksplit=3),
-                dict(prefill_ksplit=-1)):
+                dict(prefill_ksplit=-1), dict(combine_o_copy=3), dict(combine_o_copy=-1)):
         st, _, msg = create(cfg, pmk.schedule_config(**bad))
-        assert st == _lib.PMK_ERR_INVALID_ARG and "prefill" in msg, (bad, st, msg)
-    for good in (dict(prefill_ksplit=1), dict(prefill_ksplit=2), dict(prefill_chunk=-1)):
+        name = next(iter(bad))
+        assert st == _lib.PMK_ERR_INVALID_ARG and name in msg, (bad, st, msg)
+    for good in (dict(prefill_ksplit=1), dict(prefill_ksplit=2), dict(prefill_chunk=-1), dict(combine_o_copy=1),
+                 dict(combine_o_copy=2)):
         st, ctx, msg = create(cfg, pmk.schedule_config(**good))
         assert st == 0, (good, msg)
         lib.pmk_destroy(ctx)

@@ -272,6 +272,24 @@ def test_split_combines_match_oracle_and_modes():
         assert np.array_equal(r.logits, runs["megakernel"].logits), name
 
 
+@pytest.mark.gpu
+def test_combine_o_copy_is_bitwise_neutral():
+    """The combine's early copy of its queue's next O-projection tile into LDS (combine_o_copy 2)
+    only moves a weight load earlier: the decode with it and without it (1) gives the same tokens
+    and logits bit for bit, and both match the oracle."""
+    import persistent_megakernel_02_amd as pmk
+    w = TINY.with_(name="tiny_o_copy", n_q=8, n_kv=2, prompt=2016, steps=12)
+    wts = synthgen.make_weights(w, gain_std=0.1)
+    k, v, _ = synthgen.make_kv(w, w.prompt)
+    nxt = int(synthgen.make_prompt(w, 1)[0])
+    runs = {oc: gpu_run(w, wts, w.steps, kv=(k, v, w.prompt), next_token=nxt,
+                        sched=pmk.schedule_config(attn_splits=16, combine_o_copy=oc)) for oc in (1, 2)}
+    assert np.array_equal(runs[1].tokens, runs[2].tokens)
+    assert np.array_equal(runs[1].logits, runs[2].logits)
+    ref, _ = oracle_teacher_forced(w, wts, runs[2], kv=(k, v, w.prompt))
+    check(w, runs[2], ref, True, "tiny/combine O-tile copy")
+
+
 _PREFILL_FORMATS = {
     "f16": dict(wdtype="f16", kvdtype="f16"),
     "bf16": dict(wdtype="bf16", kvdtype="bf16"),
