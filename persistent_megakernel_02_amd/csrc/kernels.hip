@@ -1825,7 +1825,7 @@ __device__ __forceinline__ bool combine_copies_tile(const KParams& P, const Step
   return P.o_copy && o.op == PMK_OP_OPROJ && o.layer == layer && oproj_tile_in_lds(P, o, sc, nsl);
 }
 
-template <int WDT, int KVDT>
+template <int WDT, int KVDT, bool OCOPY = false>
 __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, int ti, const StepCtx& sc, float* lds,
                                          int cu, int qi = -1, int q0 = 0, int q1 = 0) {
   switch (t.op) {
@@ -1851,7 +1851,7 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
       break;
     }
     case PMK_OP_COMBINE:
-      if (qi >= 0 && qi + 1 < q1) {
+      if (OCOPY && qi >= 0 && qi + 1 < q1) {
         const pmk_task tn = P.tasks[P.qtasks[qi + 1]];
         if (combine_copies_tile<WDT>(P, sc, tn, t.layer))
           tile_to_lds<WDT>(P.wbase + (int64_t)t.layer * P.layer_bytes + P.off_o, P.qdim, tn.a0, tn.a1, lds + P.pf_off,
@@ -1862,7 +1862,7 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
       break;
     case PMK_OP_OPROJ: {
       bool copied = false;
-      if (qi > q0) {
+      if (OCOPY && qi > q0) {
         const pmk_task tp = P.tasks[P.qtasks[qi - 1]];
         copied = tp.op == PMK_OP_COMBINE && combine_copies_tile<WDT>(P, sc, t, tp.layer);
       }
@@ -1881,7 +1881,10 @@ __device__ __forceinline__ void run_task(const KParams& P, const pmk_task& t, in
 // ------------------------------------------------------------------------------------------------
 // the persistent kernel: one workgroup per CU, n steps of this CU's queue
 // ------------------------------------------------------------------------------------------------
-template <int WDT, int KVDT>
+// OCOPY: the instance whose COMBINE tasks copy the next O-projection tile early (schedules with
+// o_copy set); the other instance has none of that code, which the register allocation of the
+// rest of the kernel also benefits from
+template <int WDT, int KVDT, bool OCOPY>
 __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
   extern __shared__ float lds[];
   const int cu = blockIdx.x;
@@ -1915,7 +1918,7 @@ __global__ __launch_bounds__(kThreads, 1) void pmk_persistent(KParams P) {
       const int ti = P.qtasks[qi];
       const pmk_task t = P.tasks[ti];
       trace_mark(P, s, ti, 0, __builtin_amdgcn_s_memrealtime());
-      run_task<WDT, KVDT>(P, t, ti, sc, lds, cu, qi, q0, q1);
+      run_task<WDT, KVDT, OCOPY>(P, t, ti, sc, lds, cu, qi, q0, q1);
       trace_mark(P, s, ti, 2, __builtin_amdgcn_s_memrealtime());
       trace_mark(P, s, ti, 3, who);
     }
@@ -2855,13 +2858,17 @@ hipError_t static_workspace_address(int device, void** out) {
 typedef void (*KernelFn)(KParams);
 typedef void (*PhaseFn)(KParams, int);
 
-const void* persistent_kernel(int wdt, int kvdt) {
-  if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_persistent<WF16, WF16>;
-  if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_persistent<WBF16, WBF16>;
-  if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_persistent<WFP8, WFP8>;
-  if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_persistent<WI8, WBF16>;
-  if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_persistent<WI4, WBF16>;
+template <bool OCOPY>
+static const void* persistent_instance(int wdt, int kvdt) {
+  if (wdt == WF16 && kvdt == WF16) return (const void*)pmk_persistent<WF16, WF16, OCOPY>;
+  if (wdt == WBF16 && kvdt == WBF16) return (const void*)pmk_persistent<WBF16, WBF16, OCOPY>;
+  if (wdt == WFP8 && kvdt == WFP8) return (const void*)pmk_persistent<WFP8, WFP8, OCOPY>;
+  if (wdt == WI8 && kvdt == WBF16) return (const void*)pmk_persistent<WI8, WBF16, OCOPY>;
+  if (wdt == WI4 && kvdt == WBF16) return (const void*)pmk_persistent<WI4, WBF16, OCOPY>;
   return nullptr;
+}
+const void* persistent_kernel(int wdt, int kvdt, int o_copy) {
+  return o_copy ? persistent_instance<true>(wdt, kvdt) : persistent_instance<false>(wdt, kvdt);
 }
 
 // batched prefill kernel of a (weight, KV) format pair

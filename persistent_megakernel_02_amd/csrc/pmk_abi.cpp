@@ -20,7 +20,7 @@
 #include "schedule.h"
 
 namespace pmk {
-const void* persistent_kernel(int wdt, int kvdt);
+const void* persistent_kernel(int wdt, int kvdt, int o_copy);
 const void* phase_kernel(int wdt, int kvdt);
 const void* prefill_kernel(int wdt, int kvdt);
 hipError_t launch_begin_call(const KParams& P, const CallParams& cp, hipStream_t st);
@@ -430,7 +430,7 @@ pmk_status sync_position(pmk_ctx* c) {
 }
 
 pmk_status launch_persistent(pmk_ctx* c, hipStream_t st) {
-  const void* fn = persistent_kernel(c->m.wdt, c->m.kvdt);
+  const void* fn = persistent_kernel(c->m.wdt, c->m.kvdt, c->sched.o_copy);
   void* args[] = {&c->kp};
   HIPCHK(c, hipLaunchCooperativeKernel(fn, dim3(c->n_cus), dim3(kThreads), args, (unsigned)c->lds_bytes_pk, st));
   return PMK_OK;
@@ -614,7 +614,8 @@ pmk_status pmk_create(const pmk_model_config* cfg, const pmk_schedule_config* sc
   compute_phases(c);
   if (hip_device >= 0) {
     hipError_t he = hipSetDevice(hip_device);
-    const void* fns[2] = {persistent_kernel(c->m.wdt, c->m.kvdt), phase_kernel(c->m.wdt, c->m.kvdt)};
+    const void* fns[3] = {persistent_kernel(c->m.wdt, c->m.kvdt, c->sched.o_copy), phase_kernel(c->m.wdt, c->m.kvdt),
+                          persistent_kernel(c->m.wdt, c->m.kvdt, !c->sched.o_copy)};
     // the attribute is an upper bound shared by every context: allow all of a CU's LDS
     for (const void* fn : fns) {
       if (he == hipSuccess) he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
