@@ -456,7 +456,12 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ W, int K, 
                                           float* yp, float* y, bool prefetch, Sync sync, ScaleRow srow,
                                           int row_cost = 0) {
   constexpr int EPL = WFmt<WDT>::EPL;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // int4 takes the wave index as a scalar: the split, the issue cursor and the unit branches are
+  // then scalar, ~87 vector instructions per unit instead of ~108, for a loop that is vector-ALU
+  // bound (8B int4 482 -> 500 tok/s in an A/B).  For the other formats the scalar cursor costs
+  // reloads from the full scalar file instead and runs no faster (bf16, int8) or slower (fp8).
+  const int wave = WDT == WI4 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int64_t rb = WFmt<WDT>::row_bytes(K);
   const int nch = K / EPL, nsl = (nch + 63) >> 6;
   const TileSplit sp(r0, r1, nsl, wave, row_cost);
