@@ -1162,12 +1162,14 @@ __device__ __forceinline__ void split16x3(const float* x, u32x4& hi, u32x4& mid,
   lo = u32x4{o[0], o[1], o[2], o[3]};
 }
 
-// 8 FP8 E4M3 values -> 8 bf16 (exact)
+// 8 FP8 E4M3 values -> 8 bf16 (exact: every E4M3 value is a bf16 value).  gfx950's scaled
+// conversion with scale 1 writes a bf16 pair in one instruction (checked on the device against the
+// upper halves of the fp32 conversion for every pair of finite codes); converting to fp32 and
+// packing took two per pair (8B FP8 prefill of 8192 tokens 1269 -> 1223 ms).
 __device__ __forceinline__ u32x4 fp8x8_bf16(u32x2 w) {
-  const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
-  const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false), f3 = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
-  auto hi16 = [](f32x2 f) { return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u); };
-  return u32x4{hi16(f0), hi16(f1), hi16(f2), hi16(f3)};
+#define PMK_FP8_BF16(v, hi) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, hi))
+  return u32x4{PMK_FP8_BF16(w.x, false), PMK_FP8_BF16(w.x, true), PMK_FP8_BF16(w.y, false), PMK_FP8_BF16(w.y, true)};
+#undef PMK_FP8_BF16
 }
 
 // KV cache element loads through a buffer resource (out of range: zeros): 8 elements per lane as
